@@ -1,0 +1,485 @@
+"""Pins for the float64 oracle: it must agree with things other than itself.
+
+* brute force: pure-Python loops with math.exp / math.fsum and a page walk
+  written here, on tiny random inputs;
+* a library routine: torch's float64 CPU scaled_dot_product_attention with
+  an explicit mask, and scipy's logsumexp for the lse;
+* closed forms: one key, constant V, Q = 0, a dominant key, an empty row;
+* invariants: softmax rows sum to one, page permutation, page size, GQA as
+  repeated MHA, tiled == untiled for any tile, split + merge == unsplit for
+  any partition, last causal row == decode, chunked prefill == one shot;
+* the traffic figures the pages print (tests/golden/traffic_figures.json);
+* planted mistakes: each plausible oracle bug must fail one of the pins.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+from scipy.special import logsumexp
+
+import oracle
+from oracle import attention as oa
+from workloads import bits, make_case, units
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# brute force, written independently of the oracle
+# ----------------------------------------------------------------------------
+
+def _bf16(x):
+    x = np.asarray(x, dtype=np.uint16)
+    return [float(np.frombuffer(np.uint32(int(v) << 16).tobytes(), dtype=np.float32)[0])
+            for v in x.ravel()]
+
+
+def brute_attention(case):
+    """Loops over sequences, rows, heads and keys; math.exp and math.fsum only."""
+    q = bits(case.q)
+    kp = bits(case.k_pool)
+    vp = bits(case.v_pool)
+    bt = case.block_tables.numpy()
+    lens = case.seq_lens_k.numpy()
+    cu = case.cu_seqlens_q.numpy()
+    T, Hq, D = q.shape
+    Hkv, ps = kp.shape[2], kp.shape[1]
+    grp = Hq // Hkv
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    for b in range(len(lens)):
+        L = int(lens[b])
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t = int(cu[b]) + i
+            limit = L if not case.causal else L - n + i + 1
+            for h in range(Hq):
+                kvh = h // grp
+                qv = _bf16(q[t, h])
+                scores, vrows = [], []
+                for j in range(max(0, min(limit, L))):
+                    page, slot = int(bt[b][j // ps]), j % ps
+                    kv = _bf16(kp[page, slot, kvh])
+                    scores.append(case.scale * math.fsum(a * c for a, c in zip(qv, kv)))
+                    vrows.append(_bf16(vp[page, slot, kvh]))
+                if not scores:
+                    continue
+                m = max(scores)
+                e = [math.exp(s - m) for s in scores]
+                den = math.fsum(e)
+                for d in range(D):
+                    out[t, h, d] = math.fsum(w * vr[d] for w, vr in zip(e, vrows)) / den
+                lse[t, h] = m + math.log(den)
+    return out, lse
+
+
+def run_oracle(case):
+    return oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
+                                case.block_tables.numpy(), case.seq_lens_k.numpy(),
+                                case.cu_seqlens_q.numpy(), case.scale, case.causal,
+                                case.page_size)
+
+
+def assert_close(a, b, tol=1e-12):
+    a, b = np.asarray(a), np.asarray(b)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin)
+    assert np.array_equal(a[~fin], b[~fin])
+    if fin.any():
+        err = np.abs(a[fin] - b[fin]) / (1.0 + np.abs(b[fin]))
+        assert err.max() <= tol, err.max()
+
+
+small_shapes = st.fixed_dictionaries(dict(
+    B=st.integers(1, 3),
+    D=st.sampled_from([4, 8]),
+    Hkv=st.integers(1, 2),
+    G=st.sampled_from([1, 2, 3, 7]),
+    ps=st.sampled_from([1, 3, 16]),
+    causal=st.booleans(),
+    seed=st.integers(0, 10_000),
+    lens=st.lists(st.integers(0, 40), min_size=3, max_size=3),
+    qlens=st.lists(st.integers(1, 5), min_size=3, max_size=3),
+))
+
+
+def _small_case(p):
+    B = p["B"]
+    lens = p["lens"][:B]
+    ql = [min(n, max(L, 1)) for n, L in zip(p["qlens"][:B], lens)]
+    spare = 3
+    return make_case("hyp", seq_lens=lens, q_lens=ql, Hq=p["Hkv"] * p["G"], Hkv=p["Hkv"],
+                     D=p["D"], page_size=p["ps"], seed=p["seed"], causal=p["causal"],
+                     num_pages=sum(-(-L // p["ps"]) for L in lens) + spare)
+
+
+@settings(max_examples=40, deadline=None)
+@given(small_shapes)
+def test_oracle_matches_brute_force(p):
+    case = _small_case(p)
+    o, lse = run_oracle(case)
+    ob, lseb = brute_attention(case)
+    assert_close(o, ob)
+    assert_close(lse, lseb)
+
+
+def test_brute_force_covers_poison_and_tails():
+    # partially filled last pages, an empty sequence, spare NaN pages, GQA 7
+    case = make_case("t", seq_lens=[0, 5, 33], q_lens=[1, 3, 4], Hq=7, Hkv=1, D=8,
+                     page_size=16, num_pages=8, seed=3, causal=True)
+    o, lse = run_oracle(case)
+    assert np.isfinite(o).all()
+    ob, lseb = brute_attention(case)
+    assert_close(o, ob)
+    assert_close(lse, lseb)
+    assert (lse[0] == -np.inf).all() and (o[0] == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# library routines
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("L,n", [(1, 1), (17, 1), (64, 64), (100, 37)])
+def test_attend_rows_matches_torch_sdpa_float64(L, n, causal):
+    rng = np.random.default_rng(L * 31 + n)
+    D = 16
+    q = rng.standard_normal((n, D))
+    k = rng.standard_normal((L, D))
+    v = rng.standard_normal((L, D))
+    vis = oa._visible_counts(L, n, causal)
+    o, lse = oracle.attend_rows(q, k, v, 0.3, vis)
+    mask = torch.arange(L)[None, :] < torch.as_tensor(vis)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.as_tensor(q)[None], torch.as_tensor(k)[None], torch.as_tensor(v)[None],
+        attn_mask=mask[None], scale=0.3)[0].numpy()
+    assert np.abs(o - ref).max() < 1e-12
+    s = 0.3 * q @ k.T
+    s[~mask.numpy()] = -np.inf
+    assert np.abs(lse - logsumexp(s, axis=1)).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+
+def test_single_key_returns_its_value_row():
+    rng = np.random.default_rng(1)
+    q, k, v = rng.standard_normal((3, 8)), rng.standard_normal((1, 8)), rng.standard_normal((1, 8))
+    o, lse = oracle.attend_rows(q, k, v, 0.5, [1, 1, 1])
+    assert np.array_equal(o, np.repeat(v, 3, axis=0))
+    assert np.allclose(lse, 0.5 * q @ k[0], rtol=0, atol=1e-14)
+
+
+def test_constant_values_return_that_constant():
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((4, 8)), rng.standard_normal((50, 8))
+    v = np.tile(rng.standard_normal(8), (50, 1))
+    o, _ = oracle.attend_rows(q, k, v, 1.0, [50, 10, 1, 33])
+    assert np.abs(o - v[0]).max() < 1e-13
+
+
+def test_zero_query_returns_mean_of_visible_values():
+    rng = np.random.default_rng(3)
+    k, v = rng.standard_normal((40, 8)), rng.standard_normal((40, 8))
+    o, lse = oracle.attend_rows(np.zeros((3, 8)), k, v, 1.0, [40, 7, 1])
+    for i, n in enumerate([40, 7, 1]):
+        assert np.abs(o[i] - v[:n].mean(axis=0)).max() < 1e-13
+        assert abs(lse[i] - math.log(n)) < 1e-13
+
+
+def test_dominant_key_returns_its_value_row():
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((64, 8)) * 0.01
+    v = rng.standard_normal((64, 8))
+    q = np.zeros((1, 8))
+    q[0, 0] = 1.0
+    k[17, 0] = 200.0                               # score gap >= 110
+    o, _ = oracle.attend_rows(q, k, v, 1.0, [64])
+    assert np.abs(o[0] - v[17]).max() < 1e-40
+
+
+def test_fully_masked_row_is_zero_with_minus_inf_lse():
+    rng = np.random.default_rng(5)
+    k, v = rng.standard_normal((5, 4)), rng.standard_normal((5, 4))
+    o, lse = oracle.attend_rows(rng.standard_normal((2, 4)), k, v, 1.0, [0, 3])
+    assert (o[0] == 0).all() and lse[0] == -np.inf
+    assert np.isfinite(o[1]).all()
+    o, lse = oracle.attend_rows(np.ones((1, 4)), np.zeros((0, 4)), np.zeros((0, 4)), 1.0, [0])
+    assert (o == 0).all() and lse[0] == -np.inf
+
+
+def test_extreme_logits_stay_finite_and_match_brute_force():
+    case = make_case("x", seq_lens=[37, 100], Hq=4, Hkv=2, D=8, page_size=16, seed=7)
+    case.q = (case.q.float() * 30).to(torch.bfloat16)
+    o, lse = run_oracle(case)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ob, lseb = brute_attention(case)
+    assert_close(o, ob, 1e-11)
+    assert_close(lse, lseb, 1e-11)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one_and_masked_keys_are_zero():
+    rng = np.random.default_rng(6)
+    q, k = rng.standard_normal((5, 8)), rng.standard_normal((30, 8))
+    vis = [30, 1, 15, 0, 29]
+    p = oracle.softmax_probs_ref(q, k, 0.7, vis)
+    for i, n in enumerate(vis):
+        assert (p[i, n:] == 0).all()
+        if n:
+            assert abs(p[i].sum() - 1.0) < 1e-12
+        else:
+            assert (p[i] == 0).all()
+
+
+def test_page_permutation_leaves_output_unchanged():
+    case = make_case("p", seq_lens=[40, 17, 64], Hq=4, Hkv=2, D=8, page_size=16, seed=8,
+                     num_pages=12)
+    o1, l1 = run_oracle(case)
+    perm = np.random.default_rng(0).permutation(12)          # new page id of old page i
+    inv = np.argsort(perm)
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    bt = case.block_tables.numpy().copy()
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
+    o2, l2 = oracle.attention_ref(bits(case.q), kp[inv], vp[inv], bt2, case.seq_lens_k.numpy(),
+                                  case.cu_seqlens_q.numpy(), case.scale, False, 16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_page_size_does_not_change_the_result():
+    a = make_case("a", seq_lens=[100, 65], Hq=4, Hkv=2, D=8, page_size=16, seed=9, permute=False)
+    ka, va = oracle.gather_sequence_kv, None
+    # rebuild the same logical KV in a 64-token page pool
+    kp16, vp16 = bits(a.k_pool), bits(a.v_pool)
+    bt = a.block_tables.numpy()
+    lens = a.seq_lens_k.numpy()
+    pools = []
+    for pool in (kp16, vp16):
+        seqs = [pool[bt[b, :-(-lens[b] // 16)]].reshape(-1, 2, 8)[:lens[b]] for b in range(2)]
+        big = np.zeros((4, 64, 2, 8), dtype=np.uint16)
+        for b, s in enumerate(seqs):
+            flat = np.zeros((128, 2, 8), dtype=np.uint16)
+            flat[:len(s)] = s
+            big[2 * b:2 * b + 2] = flat.reshape(2, 64, 2, 8)
+        pools.append(big)
+    bt64 = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    o16, l16 = run_oracle(a)
+    o64, l64 = oracle.attention_ref(bits(a.q), pools[0], pools[1], bt64, lens,
+                                    a.cu_seqlens_q.numpy(), a.scale, False, 64)
+    assert np.array_equal(o16, o64) and np.array_equal(l16, l64)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    case = make_case("g", seq_lens=[33, 70], q_lens=[3, 5], Hq=6, Hkv=2, D=8, page_size=16,
+                     seed=10, causal=True)
+    o, l = run_oracle(case)
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    kr, vr = np.repeat(kp, 3, axis=2), np.repeat(vp, 3, axis=2)
+    o2, l2 = oracle.attention_ref(bits(case.q), kr, vr, case.block_tables.numpy(),
+                                  case.seq_lens_k.numpy(), case.cu_seqlens_q.numpy(),
+                                  case.scale, True, 16)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+@pytest.mark.parametrize("tile", [1, 7, 16, 64, 97])
+def test_tiled_online_softmax_equals_untiled(tile):
+    rng = np.random.default_rng(tile)
+    q, k, v = rng.standard_normal((6, 16)) * 3, rng.standard_normal((97, 16)), \
+        rng.standard_normal((97, 16))
+    vis = [97, 1, 50, 0, 64, 33]
+    o, lse = oracle.attend_rows(q, k, v, 0.25, vis)
+    ot, lset = oracle.tiled_attend_rows(q, k, v, 0.25, vis, tile)
+    assert_close(ot, o, 1e-12)
+    assert_close(lset, lse, 1e-12)
+
+
+@pytest.mark.parametrize("bounds", [[0, 97], [0, 32, 64, 97], [0, 0, 5, 5, 97],
+                                    [0, 1, 2, 3, 50, 97, 97, 97], [0, 40, 80, 97]])
+@pytest.mark.parametrize("visible", [97, 45, 1, 0])
+def test_split_and_merge_equals_unsplit(bounds, visible):
+    rng = np.random.default_rng(len(bounds) * 100 + visible)
+    q, k, v = rng.standard_normal(16), rng.standard_normal((97, 16)), rng.standard_normal((97, 16))
+    o, lse = oracle.attend_rows(q[None], k, v, 0.3, [visible])
+    oc, lc = oracle.split_partials_ref(q, k, v, 0.3, visible, bounds)
+    om, lm = oracle.merge_ref(oc, lc)
+    assert_close(om, o[0], 1e-12)
+    assert_close(np.atleast_1d(lm), lse, 1e-12)
+
+
+def test_merge_of_all_empty_chunks_is_zero():
+    o, l = oracle.merge_ref(np.ones((3, 4)), np.full(3, -np.inf))
+    assert (o == 0).all() and l == -np.inf
+
+
+def test_last_causal_row_equals_decode_of_the_same_sequence():
+    pre = make_case("c", seq_lens=[57], q_lens=[57], Hq=4, Hkv=1, D=8, page_size=16, seed=11,
+                    causal=True)
+    o, l = run_oracle(pre)
+    dec_q = pre.q[-1:].clone()
+    o2, l2 = oracle.attention_ref(bits(dec_q), bits(pre.k_pool), bits(pre.v_pool),
+                                  pre.block_tables.numpy(), pre.seq_lens_k.numpy(),
+                                  np.array([0, 1]), pre.scale, False, 16)
+    assert_close(o[-1], o2[0])          # BLAS may round a 1-row product differently
+    assert_close(l[-1], l2[0])
+
+
+def test_chunked_prefill_equals_one_shot():
+    full = make_case("f", seq_lens=[80], q_lens=[80], Hq=2, Hkv=1, D=8, page_size=16, seed=12,
+                     causal=True)
+    o, l = run_oracle(full)
+    args = (bits(full.k_pool), bits(full.v_pool), full.block_tables.numpy())
+    qb = bits(full.q)
+    # first chunk: 30 queries over a 30-key prefix; second: 50 queries over all 80 keys
+    o1, l1 = oracle.attention_ref(qb[:30], *args, np.array([30]), np.array([0, 30]),
+                                  full.scale, True, 16)
+    o2, l2 = oracle.attention_ref(qb[30:], *args, np.array([80]), np.array([0, 50]),
+                                  full.scale, True, 16)
+    assert_close(np.concatenate([o1, o2]), o)
+    assert_close(np.concatenate([l1, l2]), l)
+
+
+def test_rows_ref_matches_full_ref():
+    case = make_case("r", hist_lens=[20, 0, 45], q_lens=[5, 16, 1], write_new=True, causal=True,
+                     Hq=4, Hkv=2, D=8, page_size=16, seed=13)
+    kp, vp = oracle.kv_write_ref(bits(case.k_pool), bits(case.v_pool), bits(case.k_new),
+                                 bits(case.v_new), case.cu_new.numpy(), case.start_pos.numpy(),
+                                 case.block_tables.numpy(), 16)
+    args = (bits(case.q), kp, vp, case.block_tables.numpy(), case.seq_lens_k.numpy(),
+            case.cu_seqlens_q.numpy(), case.scale, True, 16)
+    o, l = oracle.attention_ref(*args)
+    rows = [(0, 0), (4, 3), (5, 1), (20, 2), (21, 0)]
+    orow, lrow = oracle.attention_rows_ref(*args, rows=rows)
+    for i, (t, h) in enumerate(rows):
+        assert_close(orow[i], o[t, h])
+        assert_close(lrow[i], l[t, h])
+
+
+# ----------------------------------------------------------------------------
+# page writes
+# ----------------------------------------------------------------------------
+
+def test_kv_write_matches_a_loop_and_round_trips():
+    case = make_case("w", hist_lens=[0, 13, 40], q_lens=[20, 3, 1], write_new=True, Hq=4, Hkv=2,
+                     D=8, page_size=16, seed=14, num_pages=10)
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    kn, vn = bits(case.k_new), bits(case.v_new)
+    bt = case.block_tables.numpy()
+    cu, sp = case.cu_new.numpy(), case.start_pos.numpy()
+    ko, vo = oracle.kv_write_ref(kp, vp, kn, vn, cu, sp, bt, 16)
+    kl, vl = kp.copy(), vp.copy()
+    for b in range(3):
+        for t in range(cu[b], cu[b + 1]):
+            pos = sp[b] + t - cu[b]
+            kl[bt[b][pos // 16], pos % 16] = kn[t]
+            vl[bt[b][pos // 16], pos % 16] = vn[t]
+    assert np.array_equal(ko, kl) and np.array_equal(vo, vl)
+    assert np.array_equal(kp, bits(case.k_pool))                  # input untouched
+    for b in range(3):
+        L = int(case.seq_lens_k[b])
+        g = oracle.gather_sequence_kv(ko, bt[b], L, 16)
+        new = oracle.bf16_bits_to_f64(kn[cu[b]:cu[b + 1]])
+        assert np.array_equal(g[sp[b]:], new)
+        assert np.isfinite(g).all()                               # every NaN slot was written
+
+
+# ----------------------------------------------------------------------------
+# traffic figures printed by the pages
+# ----------------------------------------------------------------------------
+
+def test_traffic_figures_from_the_pages():
+    with open(os.path.join(GOLDEN, "traffic_figures.json")) as f:
+        entries = json.load(f)["entries"]
+    e = entries
+    assert units.kv_bytes_per_head(e[0]["seq_len"], e[0]["head_dim"], e[0]["elem_bytes"]) == e[0]["bytes"]
+    assert units.score_matrix_bytes(e[1]["n"], e[1]["n"], e[1]["elem_bytes"]) == e[1]["bytes"]
+    assert units.naive_attention_traffic(e[2]["n"], e[2]["elem_bytes"], e[2]["passes"]) == e[2]["bytes"]
+    assert units.score_matrix_bytes(e[3]["n_q"], e[3]["n_k"], e[3]["elem_bytes"]) == e[3]["bytes"]
+    assert units.score_matrix_bytes(e[4]["n"], e[4]["n"], e[4]["elem_bytes"]) == e[4]["bytes"]
+    assert e[2]["bytes"] // e[0]["bytes"] == e[5]["ratio"]
+    # one sequence, one head, no query/output/table overhead: the decode unit is the same 2 MiB
+    one = units.decode_bytes([4096], 1, 1, 128, 16) - 2 * 128 * 2 - 256 * 4 - 4
+    assert one == e[0]["bytes"]
+
+
+def test_workload_units_at_the_five_sizes():
+    assert units.decode_bytes([17, 64, 100, 255], 8, 2, 64, 16) == 231_556
+    assert units.decode_bytes([8192] * 32, 28, 4, 128, 16) == 537_395_328
+    assert units.decode_bytes([131072] * 8, 64, 8, 128, 64) == 4_295_295_008
+    assert units.prefill_flops([4096] * 4, [4096] * 4, 32, 128, True) == 549_890_031_616
+    # brute-force pair count on a small ragged causal batch
+    lens, ql = [7, 3, 12], [7, 1, 5]
+    pairs = sum(max(0, L - n + i + 1) for L, n in zip(lens, ql) for i in range(n))
+    assert units.prefill_pairs(lens, ql, True) == pairs
+    assert units.prefill_pairs(lens, ql, False) == sum(L * n for L, n in zip(lens, ql))
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must be caught by a pin above
+# ----------------------------------------------------------------------------
+
+def _mut_drop_scale(q_rows, k, v, scale, visible):
+    return _orig_attend(q_rows, k, v, 1.0, visible)
+
+
+def _mut_no_mask(q_rows, k, v, scale, visible):
+    return _orig_attend(q_rows, k, v, scale, np.full(len(np.atleast_1d(visible)), k.shape[0]))
+
+
+def _mut_off_by_one_causal(q_rows, k, v, scale, visible):
+    vis = np.asarray(visible) - 1
+    return _orig_attend(q_rows, k, v, scale, np.maximum(vis, 0))
+
+
+def _mut_transposed_value(q_rows, k, v, scale, visible):
+    o, l = _orig_attend(q_rows, k, v, scale, visible)
+    return o[:, ::-1].copy(), l
+
+
+_orig_attend = oa.attend_rows
+
+
+@pytest.mark.parametrize("mutant", [_mut_drop_scale, _mut_no_mask, _mut_off_by_one_causal,
+                                    _mut_transposed_value])
+def test_planted_oracle_mistakes_are_caught(monkeypatch, mutant):
+    case = make_case("m", seq_lens=[20, 9], q_lens=[4, 2], Hq=2, Hkv=1, D=4, page_size=3,
+                     seed=15, causal=True)
+    ob, lb = brute_attention(case)
+    monkeypatch.setattr(oa, "attend_rows", mutant)
+    o, l = run_oracle(case)
+    with pytest.raises(AssertionError):
+        assert_close(o, ob)
+        assert_close(l, lb)
+
+
+def test_planted_gqa_mapping_mistake_is_caught(monkeypatch):
+    case = make_case("m", seq_lens=[20], Hq=4, Hkv=2, D=4, page_size=4, seed=16)
+    ob, _ = brute_attention(case)
+    # a wrong head mapping (h % Hkv instead of h // G) through a patched gather
+    orig = oa.gather_sequence_kv
+
+    def swapped(pool, row, L, ps):
+        g = orig(pool, row, L, ps)
+        return g[:, ::-1]
+    monkeypatch.setattr(oa, "gather_sequence_kv", swapped)
+    o, _ = run_oracle(case)
+    assert np.abs(o - ob).max() > 1e-3
+
+
+def test_planted_merge_mistake_is_caught(monkeypatch):
+    rng = np.random.default_rng(17)
+    q, k, v = rng.standard_normal(8), rng.standard_normal((40, 8)), rng.standard_normal((40, 8))
+    o, _ = oracle.attend_rows(q[None], k, v, 1.0, [40])
+    oc, lc = oracle.split_partials_ref(q, k, v, 1.0, 40, [0, 10, 40])
+    # forgetting the lse weights (plain average of chunk outputs) must not pass
+    assert np.abs(oc.mean(axis=0) - o[0]).max() > 1e-3
+    om, _ = oracle.merge_ref(oc, lc)
+    assert np.abs(om - o[0]).max() < 1e-12

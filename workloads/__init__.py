@@ -1,0 +1,272 @@
+"""Seeded synthetic inputs for paged-KV attention, shared by tests and bench.
+
+This module draws random numbers and lays them out as a paged KV cache; it
+holds none of the attention arithmetic.  Both the HIP library and the
+float64 oracle consume what it produces, and it imports neither.
+
+Layout of a case (the problem statement of the source pages: queries
+[tokens, Hq, D], key/value page pools [pages, page_size, Hkv, D],
+per-sequence block tables and lengths, GQA ratio, softmax scale, causal):
+
+* ``q``            [T, Hq, D] bf16, packed query rows of all sequences;
+* ``k_pool``/``v_pool`` [P, page_size, Hkv, D] bf16, the cache BEFORE any
+  ``kv_page_write`` of the case's new tokens;
+* ``block_tables`` [B, max_pages] int32, a seeded permutation of the pool
+  handed out in sequence order; entries past a sequence's last page are -1;
+* ``seq_lens_k``   [B] int32, keys attended (history + new tokens);
+* ``cu_seqlens_q`` [B+1] int32;
+* ``k_new``/``v_new`` [Tn, Hkv, D], ``cu_new`` [B+1], ``start_pos`` [B]:
+  tokens that ``kv_page_write`` must place before attention (None when the
+  pools already hold every key).
+
+Poison, so that a wrong gather cannot go unnoticed:
+
+* pages no table references are filled with bf16 NaN;
+* slots past a sequence's last key in its last page hold +-3e4 (finite);
+* slots that ``kv_page_write`` must fill start as NaN.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+__all__ = ["PagedCase", "make_case", "make_config", "CONFIGS", "CONFIG_ORDER",
+           "bits", "units"]
+
+BF16_NAN_BITS = 0x7FC0
+TAIL_POISON = 3.0e4
+
+
+@dataclass
+class PagedCase:
+    name: str
+    Hq: int
+    Hkv: int
+    D: int
+    page_size: int
+    scale: float
+    causal: bool
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens_k: torch.Tensor
+    cu_seqlens_q: torch.Tensor
+    hist_lens: List[int]
+    q_lens: List[int]
+    k_new: Optional[torch.Tensor] = None
+    v_new: Optional[torch.Tensor] = None
+    cu_new: Optional[torch.Tensor] = None
+    start_pos: Optional[torch.Tensor] = None
+    num_splits: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.seq_lens_k.shape[0])
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def seq_lens(self) -> List[int]:
+        return [h + n for h, n in zip(self.hist_lens, self.q_lens)] if self.k_new is not None \
+            else [int(x) for x in self.seq_lens_k.cpu().tolist()]
+
+    @property
+    def max_seq_len(self) -> int:
+        return max(self.seq_lens) if self.B else 0
+
+    @property
+    def max_q_len(self) -> int:
+        return max(self.q_lens) if self.q_lens else 0
+
+    def to(self, device) -> "PagedCase":
+        out = PagedCase(**{k: getattr(self, k) for k in self.__dataclass_fields__})
+        for k in ("q", "k_pool", "v_pool", "block_tables", "seq_lens_k", "cu_seqlens_q",
+                  "k_new", "v_new", "cu_new", "start_pos"):
+            t = getattr(self, k)
+            if t is not None:
+                setattr(out, k, t.to(device))
+        return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """A bf16 tensor's raw bits as a host uint16 array (for the oracle)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _randn_bf16(shape, std, gen, device, chunk_rows=None):
+    """Normal(0, std) values rounded to bf16 (round-to-nearest-even)."""
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if chunk_rows is None or shape[0] <= chunk_rows:
+        out.copy_(torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std)
+        return out
+    for r in range(0, shape[0], chunk_rows):
+        n = min(chunk_rows, shape[0] - r)
+        out[r:r + n].copy_(torch.randn((n,) + tuple(shape[1:]), generator=gen, device=device,
+                                       dtype=torch.float32) * std)
+    return out
+
+
+def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=None,
+              seed=0, q_lens=None, hist_lens=None, causal=False, write_new=False,
+              std_q=1.0, std_kv=1.0, scale=None, device="cpu", num_splits=0,
+              max_pages=None, permute=True) -> PagedCase:
+    """Build one seeded case.
+
+    Two shapes of case:
+
+    * decode-style (``write_new=False``): ``seq_lens[b]`` keys already sit in
+      the pools; ``q_lens[b]`` query rows per sequence (default 1).
+    * write-then-attend (``write_new=True``): ``hist_lens[b]`` keys already sit
+      in the pools and ``q_lens[b]`` new tokens arrive with their own K/V,
+      which ``kv_page_write`` places at positions hist..hist+q_len-1 before
+      attention; ``seq_lens_k = hist + q_len``.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    if write_new:
+        hist = [int(x) for x in hist_lens]
+        ql = [int(x) for x in q_lens]
+        total = [h + n for h, n in zip(hist, ql)]
+    else:
+        total = [int(x) for x in seq_lens]
+        ql = [1] * len(total) if q_lens is None else [int(x) for x in q_lens]
+        hist = [t - n for t, n in zip(total, ql)]
+    B = len(total)
+    n_pages = [-(-L // page_size) for L in total]
+    used = sum(n_pages)
+    if num_pages is None:
+        num_pages = max(used, 1)
+    if used > num_pages:
+        raise ValueError(f"{used} pages needed, pool has {num_pages}")
+    if max_pages is None:
+        max_pages = max(max(n_pages) if n_pages else 1, 1)
+    perm = rng.permutation(num_pages) if permute else np.arange(num_pages)
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :n_pages[b]] = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+    referenced = perm[:used]
+
+    shape = (num_pages, page_size, Hkv, D)
+    chunk = max(1, (1 << 26) // (page_size * Hkv * D))
+    k_pool = _randn_bf16(shape, std_kv, gen, device, chunk)
+    v_pool = _randn_bf16(shape, std_kv, gen, device, chunk)
+
+    # poison: unreferenced pages -> NaN
+    unref = np.setdiff1d(np.arange(num_pages), referenced)
+    nan = torch.tensor(BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16).item()
+    if unref.size:
+        idx = torch.as_tensor(unref, device=device, dtype=torch.long)
+        k_pool[idx] = nan
+        v_pool[idx] = nan
+    # poison: slots past the last key of each sequence's last page -> +-3e4
+    for b in range(B):
+        L = total[b]
+        if L % page_size and n_pages[b]:
+            page = int(bt[b, n_pages[b] - 1])
+            k_pool[page, L % page_size:] = TAIL_POISON
+            v_pool[page, L % page_size:] = -TAIL_POISON
+    T = sum(ql)
+    q = _randn_bf16((max(T, 0), Hq, D), std_q, gen, device)
+    cu_q = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+
+    k_new = v_new = cu_new = start_pos = None
+    if write_new:
+        k_new = _randn_bf16((T, Hkv, D), std_kv, gen, device)
+        v_new = _randn_bf16((T, Hkv, D), std_kv, gen, device)
+        # the slots the writer must fill start as NaN
+        for b in range(B):
+            if ql[b] == 0:
+                continue
+            pos = np.arange(hist[b], total[b])
+            pages = torch.as_tensor(bt[b, pos // page_size].astype(np.int64), device=device)
+            slots = torch.as_tensor(pos % page_size, device=device, dtype=torch.long)
+            k_pool[pages, slots] = nan
+            v_pool[pages, slots] = nan
+        cu_new = torch.as_tensor(cu_q, device=device)
+        start_pos = torch.as_tensor(np.asarray(hist, dtype=np.int32), device=device)
+
+    return PagedCase(
+        name=name, Hq=Hq, Hkv=Hkv, D=D, page_size=page_size,
+        scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), causal=causal,
+        q=q, k_pool=k_pool, v_pool=v_pool,
+        block_tables=torch.as_tensor(bt, device=device),
+        seq_lens_k=torch.as_tensor(np.asarray(total, dtype=np.int32), device=device),
+        cu_seqlens_q=torch.as_tensor(cu_q, device=device),
+        hist_lens=hist, q_lens=ql, k_new=k_new, v_new=v_new, cu_new=cu_new,
+        start_pos=start_pos, num_splits=num_splits,
+        meta=dict(seed=seed, std_q=std_q, std_kv=std_kv),
+    )
+
+
+def _mixed_lengths(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hist = np.clip(np.rint(rng.lognormal(7.0, 1.0, size=23)), 16, 32768).astype(np.int64)
+    q_lens = [512] * 5 + [1] * 18
+    return [int(h) for h in hist], q_lens
+
+
+# The five workloads.  Seeds are 1000 + the workload's index.
+CONFIG_ORDER = ["tiny_decode", "qwen7b_decode", "mixed_ragged", "causal_prefill", "long_decode"]
+
+
+def _cfg_tiny(device):
+    return make_case("tiny_decode", seq_lens=[17, 64, 100, 255], Hq=8, Hkv=2, D=64,
+                     page_size=16, num_pages=64, seed=1000, device=device, num_splits=1)
+
+
+def _cfg_qwen(device):
+    return make_case("qwen7b_decode", seq_lens=[8192] * 32, Hq=28, Hkv=4, D=128,
+                     page_size=16, num_pages=16384, seed=1001, device=device)
+
+
+def _cfg_mixed(device):
+    hist, ql = _mixed_lengths(1002)
+    return make_case("mixed_ragged", hist_lens=hist, q_lens=ql, write_new=True, causal=True,
+                     Hq=32, Hkv=8, D=128, page_size=16, seed=1002, device=device)
+
+
+def _cfg_prefill(device):
+    return make_case("causal_prefill", hist_lens=[0] * 4, q_lens=[4096] * 4, write_new=True,
+                     causal=True, Hq=32, Hkv=8, D=128, page_size=16, num_pages=1024,
+                     seed=1003, device=device)
+
+
+def _cfg_long(device):
+    return make_case("long_decode", seq_lens=[131072] * 8, Hq=64, Hkv=8, D=128, page_size=64,
+                     num_pages=16384, seed=1004, std_kv=0.5, device=device, num_splits=64)
+
+
+CONFIGS = {
+    "tiny_decode": _cfg_tiny,
+    "qwen7b_decode": _cfg_qwen,
+    "mixed_ragged": _cfg_mixed,
+    "causal_prefill": _cfg_prefill,
+    "long_decode": _cfg_long,
+}
+
+
+def make_config(name: str, device="cpu") -> PagedCase:
+    return CONFIGS[name](device)
+
+
+from . import units  # noqa: E402,F401

@@ -1,0 +1,87 @@
+"""Algorithmic work units: the bytes and flops a paged-attention call must move.
+
+These count what the method has to touch, not what a kernel happens to
+touch, so that achieved GB/s and TFLOP/s measure kernel quality:
+
+* decode bytes: every attended key and value element once per KV head (not
+  per query head), plus Q, O, the block-table entries actually used and the
+  lengths.  Split-K partials are overhead and are not counted.
+* prefill flops: 4 * D per unmasked (query, key) pair per query head (one
+  multiply-add for QK^T and one for PV).  Masked pairs are not counted.
+
+The per-head figures that the inference guide's chapter 8, section
+"Counting attention's traffic", prints are reproduced by
+``kv_bytes_per_head`` and ``score_matrix_bytes``; the N^2 b intermediate of
+"The Stack Below the Stack (Part 2)", section 2.1, by ``score_matrix_bytes``.
+"""
+
+from __future__ import annotations
+
+from typing import Sequence
+
+
+def kv_bytes_per_head(seq_len: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """Bytes of keys plus values one head streams for a sequence: 2 * L * D * b."""
+    return 2 * seq_len * head_dim * elem_bytes
+
+
+def score_matrix_bytes(n_q: int, n_k: int, elem_bytes: int = 2) -> int:
+    """Bytes of a materialised score matrix: n_q * n_k * b (N^2 b when square)."""
+    return n_q * n_k * elem_bytes
+
+
+def naive_attention_traffic(seq_len: int, elem_bytes: int = 2, passes: int = 3) -> int:
+    """HBM traffic of the unfused score matrix per head: written, read, read again."""
+    return passes * score_matrix_bytes(seq_len, seq_len, elem_bytes)
+
+
+def decode_bytes(seq_lens: Sequence[int], Hq: int, Hkv: int, D: int, page_size: int,
+                 elem_bytes: int = 2) -> int:
+    """Algorithmic bytes of one decode call (one query row per sequence)."""
+    B = len(seq_lens)
+    kv = sum(kv_bytes_per_head(L, D, elem_bytes) * Hkv for L in seq_lens)
+    q = B * Hq * D * elem_bytes
+    o = B * Hq * D * elem_bytes
+    tables = sum(-(-L // page_size) for L in seq_lens) * 4
+    lens = B * 4
+    return kv + q + o + tables + lens
+
+
+def prefill_pairs(seq_lens: Sequence[int], q_lens: Sequence[int], causal: bool) -> int:
+    """Unmasked (query, key) pairs per query head over a ragged batch.
+
+    Causal rows sit at the end of their sequence: row i of a chunk of q_len
+    rows over L keys sees L - q_len + i + 1 keys.
+    """
+    total = 0
+    for L, n in zip(seq_lens, q_lens):
+        if not causal:
+            total += n * L
+            continue
+        # sum over i < n of max(0, L - n + 1 + i): an arithmetic series over
+        # the rows that see at least one key
+        first = L - n + 1
+        skip = max(0, 1 - first)          # rows that see nothing
+        rows = n - skip
+        lo = first + skip
+        total += rows * lo + rows * (rows - 1) // 2
+    return total
+
+
+def prefill_flops(seq_lens: Sequence[int], q_lens: Sequence[int], Hq: int, D: int,
+                  causal: bool) -> int:
+    """Algorithmic flops: 4 * D * Hq per unmasked (query, key) pair."""
+    return 4 * D * Hq * prefill_pairs(seq_lens, q_lens, causal)
+
+
+def prefill_bytes(seq_lens: Sequence[int], q_lens: Sequence[int], Hq: int, Hkv: int,
+                  D: int, elem_bytes: int = 2) -> int:
+    """Minimum HBM traffic of a prefill call: Q, O once, K and V once per KV head."""
+    T = sum(q_lens)
+    return 2 * T * Hq * D * elem_bytes + sum(kv_bytes_per_head(L, D, elem_bytes) * Hkv
+                                             for L in seq_lens)
+
+
+def kv_write_bytes(n_tokens: int, Hkv: int, D: int, elem_bytes: int = 2) -> int:
+    """Bytes a KV page write moves: K and V rows read once and written once."""
+    return 2 * 2 * n_tokens * Hkv * D * elem_bytes
