@@ -1,0 +1,319 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Headline: Qwen2.5-7B-shaped one-layer decode (batch 32, context 8192, Hq 28,
+Hkv 4, D 128, page size 16) -- the paged split-K decode plus its merge, inputs
+resident in HBM.  Value = algorithmic KV-read GB/s (every attended K and V
+element once per KV head, plus Q, O, used table entries and lengths).  Several
+copies of the pools are rotated so that no step finds its KV in the 256 MiB
+last-level cache.  Secondary lines (same JSON object): dense causal prefill
+TFLOP/s (4 x 4096, Hq 32, Hkv 8), long-context decode (8 x 131072), and the
+mixed ragged step, each timed the same way.
+
+One JSON line is printed.  Only one GPU is used: --gpus above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode KV-read GB/s (% HBM peak); causal prefill TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen7b_decode",
+                   choices=["qwen7b_decode", "long_decode", "causal_prefill", "mixed_ragged",
+                            "tiny_decode"])
+    p.add_argument("--num-splits", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# steps
+# ---------------------------------------------------------------------------
+
+class DecodeStep:
+    """paged_attn_decode over one of `copies` rotated pool copies per step."""
+
+    def __init__(self, name, copies, num_splits=0):
+        import torch
+        import paged_kv_flashattention_amd as pa
+        from workloads import make_config, units
+        self.pa = pa
+        self.case = make_config(name, "cuda")
+        c = self.case
+        self.kv = [(c.k_pool, c.v_pool)]
+        for i in range(1, copies):
+            self.kv.append((c.k_pool.clone(), c.v_pool.clone()))
+        self.S = num_splits if num_splits > 0 else (c.num_splits or pa.decode_num_splits(
+            c.B, c.Hkv, c.max_seq_len))
+        self.out = torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
+        need = pa.decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.D, c.max_seq_len, self.S)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.i = 0
+        self.units = units.decode_bytes(c.seq_lens, c.Hq, c.Hkv, c.D, c.page_size)
+        self.unit_name = "GB/s"
+
+    def __call__(self):
+        c = self.case
+        kp, vp = self.kv[self.i % len(self.kv)]
+        self.i += 1
+        self.pa.paged_attn_decode(c.q, kp, vp, c.block_tables, c.seq_lens_k, c.scale,
+                                  max_seq_len=c.max_seq_len, num_splits=self.S, out=self.out,
+                                  workspace=self.ws)
+
+    def config(self):
+        c = self.case
+        return {"workload": c.name, "batch": c.B, "context": c.max_seq_len, "Hq": c.Hq,
+                "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size,
+                "num_splits": self.S, "pool_copies_rotated": len(self.kv)}
+
+
+class PrefillStep:
+    """kv_page_write is done once at setup; each step is one prefill_varlen call."""
+
+    def __init__(self, name, copies=1):
+        import torch
+        import paged_kv_flashattention_amd as pa
+        from workloads import make_config, units
+        self.pa = pa
+        self.case = c = make_config(name, "cuda")
+        pa.kv_page_write(c.k_pool, c.v_pool, c.k_new, c.v_new, c.cu_new, c.start_pos,
+                         c.block_tables)
+        self.out = torch.empty((c.T, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
+        self.units = units.prefill_flops(c.seq_lens, c.q_lens, c.Hq, c.D, c.causal)
+        self.unit_name = "TFLOP/s"
+
+    def __call__(self):
+        c = self.case
+        self.pa.paged_attn_prefill_varlen(c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k,
+                                          c.block_tables, c.scale, causal=True,
+                                          max_q_len=c.max_q_len, out=self.out)
+
+    def config(self):
+        c = self.case
+        return {"workload": c.name, "batch": c.B, "q_len": c.max_q_len, "Hq": c.Hq,
+                "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size, "causal": True}
+
+
+class MixedStep:
+    """The mixed ragged step: write 2,578 new tokens, prefill the 5 chunks, decode 18 rows."""
+
+    def __init__(self, name="mixed_ragged"):
+        import torch
+        import paged_kv_flashattention_amd as pa
+        from workloads import make_config, units
+        self.pa = pa
+        self.case = c = make_config(name, "cuda")
+        n = 5
+        self.t_pf = int(c.cu_seqlens_q[n])
+        self.cu_pf = c.cu_seqlens_q[:n + 1].contiguous()
+        self.lens_pf = c.seq_lens_k[:n].contiguous()
+        self.bt_pf = c.block_tables[:n].contiguous()
+        self.q_pf = c.q[:self.t_pf].contiguous()
+        self.q_d = c.q[self.t_pf:].contiguous()
+        self.lens_d = c.seq_lens_k[n:].contiguous()
+        self.bt_d = c.block_tables[n:].contiguous()
+        self.max_d = max(c.seq_lens[n:])
+        self.S = pa.decode_num_splits(c.B - n, c.Hkv, self.max_d)
+        need = pa.decode_workspace_bytes(c.B - n, c.Hq, c.Hkv, c.D, self.max_d, self.S)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.out_pf = torch.empty((self.t_pf, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
+        self.out_d = torch.empty((c.B - n, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
+        self.flops = units.prefill_flops(c.seq_lens[:n], c.q_lens[:n], c.Hq, c.D, True)
+        self.bytes = units.decode_bytes(c.seq_lens[n:], c.Hq, c.Hkv, c.D, c.page_size)
+        self.units = self.flops
+        self.unit_name = "TFLOP/s"
+
+    def __call__(self):
+        c = self.case
+        pa = self.pa
+        pa.kv_page_write(c.k_pool, c.v_pool, c.k_new, c.v_new, c.cu_new, c.start_pos,
+                         c.block_tables)
+        pa.paged_attn_prefill_varlen(self.q_pf, c.k_pool, c.v_pool, self.cu_pf, self.lens_pf,
+                                     self.bt_pf, c.scale, causal=True, max_q_len=512,
+                                     out=self.out_pf)
+        pa.paged_attn_decode(self.q_d, c.k_pool, c.v_pool, self.bt_d, self.lens_d, c.scale,
+                             max_seq_len=self.max_d, num_splits=self.S, out=self.out_d,
+                             workspace=self.ws)
+
+    def config(self):
+        c = self.case
+        return {"workload": c.name, "requests": c.B, "prefill_chunks": 5, "chunk_len": 512,
+                "decode_rows": c.B - 5, "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.D,
+                "page_size": c.page_size}
+
+
+def make_step(name, num_splits=0):
+    if name == "qwen7b_decode":
+        return DecodeStep(name, copies=3, num_splits=num_splits)
+    if name in ("long_decode", "tiny_decode"):
+        return DecodeStep(name, copies=1, num_splits=num_splits)
+    if name == "causal_prefill":
+        return PrefillStep(name)
+    return MixedStep(name)
+
+
+def time_step(step, steps, warmup):
+    """Warm up, then time exactly `steps` calls bracketed by synchronisations.
+
+    Returns (wall ms per step, event ms per step): HIP events are recorded on the
+    stream the kernels are launched on (torch's current stream)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = start.elapsed_time(stop) / steps
+    return wall, ev
+
+
+def rate(units, ms, unit_name):
+    if unit_name == "GB/s":
+        return units / (ms * 1e-3) / 1e9
+    return units / (ms * 1e-3) / 1e12
+
+
+# ---------------------------------------------------------------------------
+# oracle baseline on the host cores
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(step, budget_s=15.0):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from workloads import bits, units
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    c = step.case
+    if isinstance(step, DecodeStep):
+        bt = c.block_tables.cpu().numpy()
+        lens = c.seq_lens_k.cpu().numpy()
+        q = bits(c.q)
+        done, t_used, nbytes = 0, 0.0, 0
+        import torch
+        for b in range(c.B):
+            n_pages = -(-int(lens[b]) // c.page_size)
+            pages = torch.as_tensor(bt[b, :n_pages].astype(np.int64), device="cuda")
+            # host copy of this sequence's pages (input transfer, not timed)
+            kp = bits(c.k_pool[pages])
+            vp = bits(c.v_pool[pages])
+            local_bt = np.arange(n_pages, dtype=np.int32)[None]
+            t0 = time.perf_counter()
+            oracle.attention_ref(q[b:b + 1], kp, vp, local_bt, lens[b:b + 1],
+                                 np.array([0, 1]), c.scale, False, c.page_size)
+            t_used += time.perf_counter() - t0
+            nbytes += units.decode_bytes([int(lens[b])], c.Hq, c.Hkv, c.D, c.page_size)
+            done += 1
+            if t_used >= budget_s:
+                break
+        return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"{c.name}: {done} of {c.B} sequences, all {c.Hq} query heads, "
+                          f"float64 NumPy, {t_used:.1f} s"}
+    return None
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU "
+                                   "sharding of the path is described, not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import paged_kv_flashattention_amd as pa
+    pa.load_library()
+    torch.cuda.init()
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
+
+    step = make_step(args.workload, args.num_splits)
+    torch.cuda.synchronize()
+    wall, ev = time_step(step, args.steps, args.warmup)
+    value = rate(step.units, ev, step.unit_name)
+    log(f"[bench] {args.workload}: {ev * 1e3:.1f} us/step (events), {wall * 1e3:.1f} us/step "
+        f"(wall), {value:.1f} {step.unit_name}; {pa.describe_launch()}")
+    bound = "hbm" if step.unit_name == "GB/s" else "mfma"
+    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": step.unit_name,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": step.config(),
+        "roofline": {"bound": bound, "achieved": round(value, 2), "peak": peak,
+                     "unit": step.unit_name, "frac": round(value / peak, 4), "traffic": None,
+                     "kernel": pa.describe_launch(), "event_us_per_launch": round(ev * 1e3, 2)},
+    }
+    del step
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.workload == "qwen7b_decode":
+        extra = {}
+        for name in ("causal_prefill", "long_decode", "mixed_ragged"):
+            s = make_step(name)
+            w2, e2 = time_step(s, max(5, args.steps // 3), 2)
+            v2 = rate(s.units, e2, s.unit_name)
+            pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
+            extra[name] = {"value": round(v2, 2), "unit": s.unit_name,
+                           "frac": round(v2 / pk, 4), "us_per_step": round(e2 * 1e3, 2),
+                           "config": s.config()}
+            log(f"[bench] {name}: {e2 * 1e3:.1f} us/step, {v2:.2f} {s.unit_name}")
+            del s
+            torch.cuda.empty_cache()
+        result["secondary"] = extra
+
+    if not args.no_cpu_baseline:
+        s = make_step(args.workload, args.num_splits)
+        cb = cpu_baseline(s)
+        del s
+        if cb is not None:
+            result["cpu_baseline"] = cb
+            log(f"[bench] cpu baseline: {cb['value']:.3f} {cb['unit']} ({cb['sample']})")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

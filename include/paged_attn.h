@@ -1,0 +1,196 @@
+/*
+ * paged_attn.h -- exact attention over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * C ABI of libpaged_attn.so.  Every entry point takes plain device pointers and
+ * sizes; the library never allocates, frees or synchronises, and enqueues all of
+ * its work on the caller's HIP stream (`stream`, a hipStream_t passed as void*;
+ * NULL means the default stream).
+ *
+ * Problem statement followed (the source pages, cited by title and section):
+ *   - queries Q[tokens, Hq, D], key/value page pools [pages, page_size, Hkv, D],
+ *     per-sequence block tables and lengths ("8. Kernels and Attention Backends",
+ *     chapter intro and "Attention is an I/O problem": ragged sequences, KV blocks
+ *     scattered through memory, KV state may be paged);
+ *   - exact softmax attention softmax(scale * Q K^T + mask) V, computed tile by tile
+ *     with an online softmax ("The Stack Below the Stack (Part 2)", section 2.1);
+ *   - decode split along the KV length with a log-sum-exp merge (same page,
+ *     section 2.2 "Flash-Decoding");
+ *   - causal mask q_idx >= kv_idx (same page, section 5), in absolute positions;
+ *   - eager KV page writeback ("Inside Ion", "IonAttention in One Paragraph").
+ *
+ * Common conventions
+ *   - bf16 data (Q, K/V pools, new K/V, outputs), int32 indices, fp32 lse.
+ *   - All tensors are dense and row-major in the order written; data pointers must
+ *     be 16-byte aligned.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - lse outputs are natural-log log-sum-exps of the scaled visible scores.
+ *   - A query row that sees no key (sequence length 0, or an empty causal window)
+ *     yields O = 0 and lse = -inf, never NaN.
+ *   - Supported envelope: D in {64, 128}; page_size in {16, 32, 64};
+ *     Hq % Hkv == 0 and 1 <= Hq/Hkv <= 16.  Anything else returns
+ *     PA_ERR_UNSUPPORTED and enqueues nothing: there is no fallback path.
+ *   - A failing call enqueues nothing and leaves every output untouched.  A launch
+ *     error reported by the runtime becomes PA_ERR_LAUNCH.  pa_last_error() gives
+ *     a thread-local description of the last failure.
+ *   - Device-resident metadata is a precondition, not checked on the device:
+ *     block-table entries used must lie in [0, num_pages); a sequence's keys must
+ *     fit its table row (seq_len <= max_pages * page_size); kv_page_write's
+ *     destination slots must be distinct.  The kernels clamp page ids and table
+ *     indices into range so that a violation reads or skips wrong-but-valid
+ *     memory instead of faulting; results are then undefined.
+ *   - The library keeps no state between calls except thread-local strings; calls
+ *     on different streams may run concurrently unless they write the same memory.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = 2,       /* a size is negative or inconsistent               */
+  PA_ERR_UNSUPPORTED = 3, /* outside the supported envelope (D, page size, GQA) */
+  PA_ERR_MISALIGNED = 4,  /* a data pointer is not 16-byte aligned            */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  PA_ERR_LAUNCH = 6       /* the HIP runtime rejected a launch                */
+} pa_status;
+
+/*
+ * kv_page_write -- place new tokens' keys and values into their pages.
+ *
+ * Eager KV writeback ("Inside Ion", "IonAttention in One Paragraph"; KV-cache
+ * insertion in "The Stack Below the Stack (Part 2)", section 2.1).  New token t of
+ * sequence b (cu_new[b] <= t < cu_new[b+1]) has logical position
+ *   pos = start_pos[b] + (t - cu_new[b])
+ * and is copied, all Hkv heads, bit for bit, to row pos % page_size of page
+ * block_tables[b * max_pages + pos / page_size] in both pools.
+ *
+ *   k_pool, v_pool : [num_pages, page_size, Hkv, D] bf16, modified in place
+ *   k_new, v_new   : [T, Hkv, D] bf16
+ *   cu_new         : [B+1] int32 prefix sums of new tokens per sequence (cu_new[B] == T)
+ *   start_pos      : [B] int32 logical position of each sequence's first new token
+ *   block_tables   : [B, max_pages] int32
+ * Tokens whose position falls outside the table row, or whose page id is outside
+ * [0, num_pages), are skipped (precondition violation; see above).  T == 0 or
+ * B == 0 is a no-op returning PA_OK.
+ */
+int kv_page_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                  const int32_t* cu_new, const int32_t* start_pos,
+                  const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
+                  int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
+                  void* stream);
+
+/*
+ * paged_attn_decode_num_splits -- the split count paged_attn_decode uses when it is
+ * passed num_splits <= 0: enough (sequence, KV head, split) work-groups to fill the
+ * chip, each covering at least a few 32-key chunks ("The Stack Below the Stack
+ * (Part 2)", section 2.2: decode has parallelism to spare only along the KV length).
+ * Never more than the number of 32-key chunks of max_seq_len; at least 1.
+ */
+int32_t paged_attn_decode_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len);
+
+/*
+ * paged_attn_decode_workspace_bytes -- bytes of workspace paged_attn_decode needs for
+ * this shape and split count (after resolving num_splits <= 0 as above): fp32
+ * partial outputs [B, Hq, S, D] followed by fp32 partial lse [B, Hq, S], 256-byte
+ * aligned.  0 when S == 1.
+ */
+size_t paged_attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                         int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * paged_attn_decode -- one query row per sequence against its paged KV history.
+ *
+ * out[b, h, :] = softmax(scale * q[b, h] . K_b^T) V_b over keys 0..seq_lens[b]-1
+ * of sequence b, where K_b/V_b are gathered through block_tables row b
+ * ("8. Kernels and Attention Backends", "Counting attention's traffic": decode is
+ * bound by reading the whole history).  The keys are cut into S = num_splits
+ * partitions of part_len = roundup(ceil(max_seq_len / S), 32) keys; each
+ * partition's partial output and log-sum-exp go to the workspace and a second
+ * kernel merges them exactly ("The Stack Below the Stack (Part 2)", section 2.2).
+ * With S == 1 the first kernel writes out/lse_out directly and no workspace is used.
+ *
+ *   out       : [B, Hq, D] bf16                 lse_out : [B, Hq] fp32 or NULL
+ *   q         : [B, Hq, D] bf16
+ *   k_pool, v_pool : [num_pages, page_size, Hkv, D] bf16 (read only)
+ *   block_tables   : [B, max_pages] int32       seq_lens : [B] int32 keys attended
+ *   max_seq_len    : host-side upper bound of seq_lens (sizes the partitions; keys
+ *                    past S * part_len are not attended)
+ *   num_splits     : S, or <= 0 for paged_attn_decode_num_splits()
+ *   workspace      : device buffer of at least paged_attn_decode_workspace_bytes()
+ *                    (may be NULL when that is 0); contents are scratch
+ */
+int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                      int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                      int32_t D, float softmax_scale, int32_t max_seq_len,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * paged_attn_splitk_reduce -- merge S partial results per row into the exact one.
+ *
+ * "The Stack Below the Stack (Part 2)", section 2.2, step 3: with m = max_c lse_c,
+ *   lse = m + ln sum_c exp(lse_c - m),   out = sum_c exp(lse_c - lse) * partial_out[c].
+ * A partial with lse_c = -inf (an empty partition) contributes nothing; if every
+ * partial of a row is empty the row gets out = 0, lse = -inf.
+ *
+ *   out         : [R, D] bf16              lse_out     : [R] fp32 or NULL
+ *   partial_out : [R, S, D] fp32 (each row normalised by its own partition's sum)
+ *   partial_lse : [R, S] fp32 natural-log lse of each partition
+ */
+int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out,
+                             const float* partial_lse, int32_t R, int32_t S, int32_t D,
+                             void* stream);
+
+/*
+ * paged_attn_prefill_varlen -- ragged (causal) attention of many query rows per
+ * sequence over paged keys, on MFMA.
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and
+ * attends keys 0..seq_lens_k[b]-1 of its table row.  With causal != 0 the q_len
+ * rows of a sequence are its LAST q_len positions: row i sits at absolute position
+ * p_i = seq_lens_k[b] - q_len + i and sees keys j <= p_i (the q_idx >= kv_idx mask
+ * of "The Stack Below the Stack (Part 2)", section 5, bottom-right aligned over the
+ * history).  Without causal every row sees all seq_lens_k[b] keys.  q_len == 1 is
+ * a valid decode row.  Prefill is compute-heavy ("8. Kernels and Attention
+ * Backends", "Counting attention's traffic"): scores and P V run on bf16 MFMA with
+ * fp32 accumulation; P is rounded to bf16 before P V.
+ *
+ *   out        : [Tq, Hq, D] bf16               lse_out : [Tq, Hq] fp32 or NULL
+ *   q          : [Tq, Hq, D] bf16               cu_seqlens_q : [B+1] int32 (cu[B] == Tq)
+ *   seq_lens_k : [B] int32                      block_tables : [B, max_pages] int32
+ *   max_q_len  : host-side upper bound of the per-sequence q_len (sizes the grid;
+ *                rows past it are not computed)
+ */
+int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens_k, const int32_t* block_tables,
+                              int32_t B, int32_t Tq, int32_t max_q_len, int32_t max_pages,
+                              int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                              int32_t D, float softmax_scale, int32_t causal, void* stream);
+
+/* Human-readable name of a pa_status value (static string). */
+const char* pa_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Thread-local description of the last successful launch on this thread: kernel
+ * variant, grid, split count.  The selected path is part of the contract, so it is
+ * reported rather than implied ("8. Kernels and Attention Backends", "Backends are
+ * compatibility decisions"). */
+const char* pa_describe_launch(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,296 @@
+"""Exact attention over a paged KV cache on AMD MI355X (gfx950).
+
+A thin binding over the C ABI of ``libpaged_attn.so`` (``include/paged_attn.h``):
+argument checks and marshalling only.  Every step of the computation runs in the
+library's HIP kernels; torch supplies device memory and the current stream.
+
+Entry points (same names as the C ABI):
+
+* :func:`kv_page_write`      -- place new tokens' K/V into their pages;
+* :func:`paged_attn_decode`  -- one query row per sequence, split-K + merge;
+* :func:`paged_attn_splitk_reduce` -- the merge on its own;
+* :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA.
+
+Data contract: bf16 Q / K / V / outputs, int32 indices (int64 is refused, not
+cast), fp32 lse, contiguous tensors on one GPU.  An unsupported configuration
+raises; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "PagedAttnError", "kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
+    "paged_attn_prefill_varlen", "decode_num_splits", "decode_workspace_bytes",
+    "describe_launch", "library_path", "load_library",
+]
+
+PA_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+             4: "PA_ERR_MISALIGNED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{PA_STATUS.get(status, status)}: {detail}")
+
+
+def load_library():
+    return _lib.load()
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def describe_launch() -> str:
+    return load_library().pa_describe_launch().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise PagedAttnError(status, load_library().pa_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device):
+    _need_dtype(t, name, dtype)
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_dtype(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype} (no implicit casts)")
+
+
+def _dtypes(*specs):
+    """Check every argument's dtype before anything else, so a dtype mistake is
+    reported as such whatever else is wrong."""
+    for t, name, dtype in specs:
+        if t is not None:
+            _need_dtype(t, name, dtype)
+
+
+def _validate_tables(block_tables, seq_lens, num_pages, page_size, what="seq_lens"):
+    bt = block_tables.cpu()
+    lens = seq_lens.cpu()
+    max_pages = bt.shape[1]
+    for b in range(bt.shape[0]):
+        L = int(lens[b])
+        if L < 0 or L > max_pages * page_size:
+            raise ValueError(f"{what}[{b}]={L} does not fit a table row of {max_pages} pages")
+        n = -(-L // page_size)
+        if n and (int(bt[b, :n].min()) < 0 or int(bt[b, :n].max()) >= num_pages):
+            raise ValueError(f"block_tables row {b} references a page outside [0, {num_pages})")
+
+
+def kv_page_write(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
+                  stream=None, validate: bool = False) -> None:
+    """Write k_new/v_new [T, Hkv, D] into the pools in place (see kv_page_write in C)."""
+    _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16),
+            (k_new, "k_new", torch.bfloat16), (v_new, "v_new", torch.bfloat16),
+            (cu_new, "cu_new", torch.int32), (start_pos, "start_pos", torch.int32),
+            (block_tables, "block_tables", torch.int32))
+    dev = k_pool.device
+    _need(k_pool, "k_pool", torch.bfloat16, 4, None)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(k_new, "k_new", torch.bfloat16, 3, dev)
+    _need(v_new, "v_new", torch.bfloat16, 3, dev)
+    _need(cu_new, "cu_new", torch.int32, 1, dev)
+    _need(start_pos, "start_pos", torch.int32, 1, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    P, ps, Hkv, D = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    T = k_new.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D):
+        raise ValueError(f"k_new/v_new must be [T, {Hkv}, {D}]")
+    B = start_pos.shape[0]
+    if cu_new.shape[0] != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_new must be [B+1] and block_tables [B, max_pages]")
+    if validate:
+        cu = cu_new.cpu()
+        sp = start_pos.cpu()
+        if int(cu[0]) != 0 or int(cu[-1]) != T or bool((cu[1:] < cu[:-1]).any()):
+            raise ValueError("cu_new must be non-decreasing from 0 to T")
+        ends = sp + (cu[1:] - cu[:-1])
+        _validate_tables(block_tables, ends, P, ps, "start_pos + new tokens")
+        seen = set()
+        bt = block_tables.cpu()
+        for b in range(B):
+            for pos in range(int(sp[b]), int(ends[b])):
+                key = (int(bt[b, pos // ps]), pos % ps)
+                if key in seen:
+                    raise ValueError(f"two new tokens write page {key[0]} slot {key[1]}")
+                seen.add(key)
+    with torch.cuda.device(dev):
+        _check(load_library().kv_page_write(
+            _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(cu_new),
+            _ptr(start_pos), _ptr(block_tables), B, T, block_tables.shape[1], P, ps, Hkv, D,
+            _stream(stream)))
+
+
+def decode_num_splits(B: int, Hkv: int, max_seq_len: int) -> int:
+    return int(load_library().paged_attn_decode_num_splits(B, Hkv, max_seq_len))
+
+
+def decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, num_splits=0) -> int:
+    return int(load_library().paged_attn_decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len,
+                                                                num_splits))
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
+                      max_seq_len: Optional[int] = None, num_splits: int = 0,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
+                      stream=None, validate: bool = False):
+    """Decode attention: q [B, Hq, D] against each sequence's paged history.
+
+    ``max_seq_len`` is a host-side bound of ``seq_lens``; if omitted it is read
+    from the device (a synchronisation).  Returns out [B, Hq, D] bf16, and the
+    natural-log lse [B, Hq] fp32 as well when ``return_lse``.
+    """
+    _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
+            (v_pool, "v_pool", torch.bfloat16), (block_tables, "block_tables", torch.int32),
+            (seq_lens, "seq_lens", torch.int32), (out, "out", torch.bfloat16),
+            (lse, "lse", torch.float32))
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, None)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pool.shape
+    if Dk != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shapes do not match q")
+    if seq_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("seq_lens must be [B] and block_tables [B, max_pages]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if validate:
+        _validate_tables(block_tables, seq_lens, P, ps)
+        if B and int(seq_lens.max().item()) > max_seq_len:
+            raise ValueError("max_seq_len is below a sequence length")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    lib = load_library()
+    need = int(lib.paged_attn_decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, num_splits))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib.paged_attn_decode(
+            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale),
+            int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, stream=None):
+    """Merge partial_out [R, S, D] fp32 with partial_lse [R, S] fp32 -> (out bf16, lse fp32)."""
+    _dtypes((partial_out, "partial_out", torch.float32), (partial_lse, "partial_lse", torch.float32),
+            (out, "out", torch.bfloat16), (lse, "lse", torch.float32))
+    dev = partial_out.device
+    _need(partial_out, "partial_out", torch.float32, 3, None)
+    _need(partial_lse, "partial_lse", torch.float32, 2, dev)
+    R, S, D = partial_out.shape
+    if partial_lse.shape != (R, S):
+        raise ValueError("partial_lse must be [R, S]")
+    if out is None:
+        out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2, dev)
+    if lse is None:
+        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, 1, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().paged_attn_splitk_reduce(
+            _ptr(out), _ptr(lse), _ptr(partial_out), _ptr(partial_lse), R, S, D,
+            _stream(stream)))
+    return out, lse
+
+
+def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
+                              softmax_scale: float, causal: bool = True,
+                              max_q_len: Optional[int] = None,
+                              out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                              stream=None, validate: bool = False):
+    """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
+
+    ``max_q_len`` is a host-side bound of the per-sequence query counts; if
+    omitted it is read from the device (a synchronisation).
+    """
+    _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
+            (v_pool, "v_pool", torch.bfloat16), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            (seq_lens_k, "seq_lens_k", torch.int32), (block_tables, "block_tables", torch.int32),
+            (out, "out", torch.bfloat16), (lse, "lse", torch.float32))
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, None)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _need(seq_lens_k, "seq_lens_k", torch.int32, 1, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    Tq, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pool.shape
+    B = seq_lens_k.shape[0]
+    if Dk != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shapes do not match q")
+    if cu_seqlens_q.shape[0] != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_seqlens_q must be [B+1] and block_tables [B, max_pages]")
+    if max_q_len is None:
+        max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
+    if validate:
+        cu = cu_seqlens_q.cpu()
+        if int(cu[0]) != 0 or int(cu[-1]) != Tq or bool((cu[1:] < cu[:-1]).any()):
+            raise ValueError("cu_seqlens_q must be non-decreasing from 0 to Tq")
+        if B and int((cu[1:] - cu[:-1]).max()) > max_q_len:
+            raise ValueError("max_q_len is below a sequence's query count")
+        _validate_tables(block_tables, seq_lens_k, P, ps)
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().paged_attn_prefill_varlen(
+            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(cu_seqlens_q),
+            _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
+            P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0, _stream(stream)))
+    return (out, lse) if return_lse else out

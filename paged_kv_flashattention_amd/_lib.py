@@ -1,0 +1,57 @@
+"""ctypes loader for libpaged_attn.so: argument types of every exported symbol.
+
+The library is built in-tree (``python -m paged_kv_flashattention_amd.build``);
+nothing here compiles or falls back.  A missing library is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
+
+c_i32 = ctypes.c_int32
+c_vp = ctypes.c_void_p
+c_fp = ctypes.c_void_p          # float*, passed as raw device addresses
+c_size = ctypes.c_size_t
+c_float = ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/paged_attn.h
+SIGNATURES = {
+    "kv_page_write": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "paged_attn_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
+    "paged_attn_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "paged_attn_decode": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                  c_float, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "paged_attn_splitk_reduce": (c_i32, [c_vp, c_fp, c_fp, c_fp, c_i32, c_i32, c_i32, c_vp]),
+    "paged_attn_prefill_varlen": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          c_i32, c_i32, c_float, c_i32, c_vp]),
+    "pa_status_string": (ctypes.c_char_p, [c_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_describe_launch": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_flashattention_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

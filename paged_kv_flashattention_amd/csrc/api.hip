@@ -1,0 +1,275 @@
+// C-ABI entry points of libpaged_attn.so: argument validation, launch sizing,
+// error reporting.  Every check runs on the host before anything is enqueued, so
+// a failing call leaves outputs untouched; the only device work is the kernels'.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/paged_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local char g_last_launch[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+bool page_size_ok(int ps) { return ps == 16 || ps == 32 || ps == 64; }
+
+// Shared checks of the paged-KV description.
+int check_pool(int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size,
+               int32_t Hq, int32_t Hkv, int32_t D) {
+  if (B < 0 || max_pages < 1 || num_pages < 1 || Hq < 1 || Hkv < 1)
+    return fail(PA_ERR_SHAPE, "sizes must be positive (B=%d max_pages=%d num_pages=%d Hq=%d Hkv=%d)",
+                B, max_pages, num_pages, Hq, Hkv);
+  if (!head_dim_ok(D)) return fail(PA_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", D);
+  if (!page_size_ok(page_size))
+    return fail(PA_ERR_UNSUPPORTED, "page size %d not in {16, 32, 64}", page_size);
+  if (Hq % Hkv) return fail(PA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(PA_ERR_UNSUPPORTED, "GQA group %d exceeds 16", Hq / Hkv);
+  if ((long long)num_pages * page_size * Hkv * D > (1ll << 40))
+    return fail(PA_ERR_SHAPE, "pool larger than 2^40 elements");
+  return PA_OK;
+}
+
+constexpr int kChunk = 32;   // keys per decode chunk; partitions are multiples of it
+
+int32_t resolve_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t num_splits) {
+  const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
+  if (num_splits <= 0) {
+    // ~2048 work-groups of 4 waves fill 256 CUs about 2 deep at 8 waves per CU
+    // while each partition keeps >= 8 chunks (2 per wave) to amortise start-up.
+    const long long groups = (long long)(B > 0 ? B : 1) * Hkv;
+    long long s = (2048 + groups - 1) / groups;
+    const long long max_by_len = chunks / 8 > 0 ? chunks / 8 : 1;
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    num_splits = (int32_t)s;
+  }
+  if (num_splits > chunks) num_splits = chunks;
+  return num_splits < 1 ? 1 : num_splits;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t workspace_for(int32_t B, int32_t Hq, int32_t D, int32_t S) {
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * S;
+  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+const char* pa_describe_launch(void) { return g_last_launch; }
+
+int kv_page_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                  const int32_t* cu_new, const int32_t* start_pos,
+                  const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
+                  int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
+                  void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || T < 0) return fail(PA_ERR_SHAPE, "B=%d T=%d must be >= 0", B, T);
+  if (B == 0 || T == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "kv_page_write: nothing to do");
+    return PA_OK;
+  }
+  int st = check_pool(B, max_pages, num_pages, page_size, Hkv, Hkv, D);
+  if (st) return st;
+  if (!k_pool || !v_pool || !k_new || !v_new || !cu_new || !start_pos || !block_tables)
+    return fail(PA_ERR_NULL, "kv_page_write: a required pointer is NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_MISALIGNED, "kv_page_write: data pointers must be 16-byte aligned");
+  pa::KvWriteArgs a{};
+  a.k_pool = static_cast<uint16_t*>(k_pool);
+  a.v_pool = static_cast<uint16_t*>(v_pool);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.cu_new = cu_new;
+  a.start_pos = start_pos;
+  a.block_tables = block_tables;
+  a.B = B; a.T = T; a.max_pages = max_pages; a.num_pages = num_pages;
+  a.page_size = page_size; a.ps_shift = log2_exact(page_size); a.Hkv = Hkv; a.D = D;
+  hipError_t e = pa::launch_kv_write(a, static_cast<hipStream_t>(stream), g_last_launch,
+                                     sizeof(g_last_launch));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "kv_page_write launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t paged_attn_decode_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len) {
+  return resolve_splits(B, Hkv > 0 ? Hkv : 1, max_seq_len, 0);
+}
+
+size_t paged_attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                         int32_t max_seq_len, int32_t num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return workspace_for(B, Hq, D, resolve_splits(B, Hkv, max_seq_len, num_splits));
+}
+
+int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out,
+                             const float* partial_lse, int32_t R, int32_t S, int32_t D,
+                             void* stream) {
+  g_last_error[0] = 0;
+  if (R < 0 || S < 1) return fail(PA_ERR_SHAPE, "splitk_reduce: R=%d S=%d", R, S);
+  if (!head_dim_ok(D)) return fail(PA_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", D);
+  if (R == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "splitk_reduce: nothing to do");
+    return PA_OK;
+  }
+  if (!out || !partial_out || !partial_lse)
+    return fail(PA_ERR_NULL, "splitk_reduce: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(partial_out))
+    return fail(PA_ERR_MISALIGNED, "splitk_reduce: data pointers must be 16-byte aligned");
+  pa::ReduceArgs r{};
+  r.out = static_cast<uint16_t*>(out);
+  r.lse_out = lse_out;
+  r.part_o = partial_out;
+  r.part_lse = partial_lse;
+  r.R = R; r.S = S; r.D = D;
+  hipError_t e = pa::launch_reduce(r, static_cast<hipStream_t>(stream), g_last_launch,
+                                   sizeof(g_last_launch));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "splitk_reduce launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                      int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                      int32_t D, float softmax_scale, int32_t max_seq_len,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || max_seq_len < 0) return fail(PA_ERR_SHAPE, "decode: B=%d max_seq_len=%d", B, max_seq_len);
+  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
+  if (st) return st;
+  if (B == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "decode: nothing to do");
+    return PA_OK;
+  }
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "decode: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_MISALIGNED, "decode: data pointers must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "decode: softmax scale is NaN");
+  const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
+  const size_t need = workspace_for(B, Hq, D, S);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "decode: workspace of %zu bytes needed for %d splits, got %zu",
+                need, S, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned16(workspace))
+    return fail(PA_ERR_MISALIGNED, "decode: workspace must be 16-byte aligned");
+
+  const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
+  const int32_t part_len = ((chunks + S - 1) / S) * kChunk;
+
+  pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.ps_shift = log2_exact(page_size);
+  a.part_len = part_len; a.S = S;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const size_t rows = (size_t)B * Hq * S;
+  if (S > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256(rows * D * sizeof(float)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char d1[256], d2[256];
+  hipError_t e = pa::launch_decode(a, s, d1, sizeof(d1));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  if (S > 1) {
+    pa::ReduceArgs r{};
+    r.out = a.out; r.lse_out = lse_out; r.part_o = a.part_o; r.part_lse = a.part_lse;
+    r.R = B * Hq; r.S = S; r.D = D;
+    e = pa::launch_reduce(r, s, d2, sizeof(d2));
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s; %s", d1, d2);
+  } else {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s", d1);
+  }
+  return PA_OK;
+}
+
+int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens_k, const int32_t* block_tables,
+                              int32_t B, int32_t Tq, int32_t max_q_len, int32_t max_pages,
+                              int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                              int32_t D, float softmax_scale, int32_t causal, void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || Tq < 0 || max_q_len < 0)
+    return fail(PA_ERR_SHAPE, "prefill: B=%d Tq=%d max_q_len=%d", B, Tq, max_q_len);
+  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
+  if (st) return st;
+  if (B == 0 || Tq == 0 || max_q_len == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "prefill: nothing to do");
+    return PA_OK;
+  }
+  if (!out || !q || !k_pool || !v_pool || !cu_seqlens_q || !seq_lens_k || !block_tables)
+    return fail(PA_ERR_NULL, "prefill: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_MISALIGNED, "prefill: data pointers must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "prefill: softmax scale is NaN");
+  if (max_q_len > Tq) max_q_len = Tq;
+  pa::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens_k = seq_lens_k;
+  a.block_tables = block_tables;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  a.B = B; a.Tq = Tq; a.max_q_len = max_q_len; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.ps_shift = log2_exact(page_size);
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_last_launch,
+                                    sizeof(g_last_launch));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "prefill launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

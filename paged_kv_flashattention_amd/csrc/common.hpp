@@ -1,0 +1,87 @@
+// Shared device types and helpers for the gfx950 kernels of libpaged_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 16x16x32 bf16 matrix-core product with fp32 accumulation (gfx950).
+// Lane l supplies A[l % 16][8 (l/16) .. 8 (l/16) + 7] and B[8 (l/16) ..][l % 16];
+// it receives C[4 (l/16) + i][l % 16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 matrix-core product with fp32 accumulation (gfx950).
+// Lane l supplies A[l % 32][8 (l/32) .. + 7] and B[8 (l/32) ..][l % 32];
+// it receives C[8 j + 4 (l/32) + i][l % 32] in element 4 j + i (j, i = 0..3).
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values to a packed bf16 pair (round to nearest even), low half = lo.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Byte-select of two dwords: result byte k = byte sel_k of {hi:lo} (0-3 lo, 4-7 hi).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// {low halves of x and y} and {high halves of x and y}
+__device__ __forceinline__ uint32_t pack_lo_halves(uint32_t x, uint32_t y) {
+  return perm_b32(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi_halves(uint32_t x, uint32_t y) {
+  return perm_b32(y, x, 0x07060302u);
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Page id of logical key `key` of a sequence, clamped into the pool and the
+// table row so that a malformed table cannot send a load outside the buffers.
+__device__ __forceinline__ int page_of(const int32_t* table_row, int key, int ps_shift,
+                                       int max_pages, int num_pages) {
+  int idx = key >> ps_shift;
+  idx = idx < max_pages ? idx : max_pages - 1;
+  int page = table_row[idx];
+  return (unsigned)page < (unsigned)num_pages ? page : 0;
+}
+
+}  // namespace pa

@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const uint16_t* q;             // [B, Hq, D]
+  const uint16_t* k_pool;        // [num_pages, page_size, Hkv, D]
+  const uint16_t* v_pool;
+  const int32_t* block_tables;   // [B, max_pages]
+  const int32_t* seq_lens;       // [B]
+  uint16_t* out;                 // [B, Hq, D]           (S == 1)
+  float* lse_out;                // [B, Hq] or null      (S == 1)
+  float* part_o;                 // [B * Hq, S, D]       (S > 1)
+  float* part_lse;               // [B * Hq, S]          (S > 1)
+  int B, Hq, Hkv, G, D;
+  int max_pages, num_pages, page_size, ps_shift;
+  int part_len, S;
+  float scale_log2;              // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+  uint16_t* out;                 // [R, D]
+  float* lse_out;                // [R] or null
+  const float* part_o;           // [R, S, D]
+  const float* part_lse;         // [R, S]
+  int R, S, D;
+};
+
+struct KvWriteArgs {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const uint16_t* k_new;         // [T, Hkv, D]
+  const uint16_t* v_new;
+  const int32_t* cu_new;         // [B + 1]
+  const int32_t* start_pos;      // [B]
+  const int32_t* block_tables;   // [B, max_pages]
+  int B, T, max_pages, num_pages, page_size, ps_shift, Hkv, D;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;             // [Tq, Hq, D]
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* cu_seqlens_q;   // [B + 1]
+  const int32_t* seq_lens_k;     // [B]
+  const int32_t* block_tables;   // [B, max_pages]
+  uint16_t* out;                 // [Tq, Hq, D]
+  float* lse_out;                // [Tq, Hq] or null
+  int B, Tq, max_q_len, Hq, Hkv, G, D;
+  int max_pages, num_pages, page_size, ps_shift;
+  int causal;
+  float scale_log2;
+};
+
+// Each launcher enqueues on `stream` and returns hipGetLastError() of the launch;
+// `desc` (>= 256 bytes) receives a one-line description of what was launched.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, char* desc, size_t desc_len);
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
+                           size_t desc_len);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
+                          size_t desc_len);
+
+}  // namespace pa

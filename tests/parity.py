@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests: run the oracle on a case, compare.
+
+The tolerance is the one the problem statement fixes for bf16 inputs with fp32
+accumulation: max-abs error <= 2e-2 and mean-abs error <= 2e-3 against the
+float64 oracle, on the same seeded inputs.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import bits
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+LSE_ABS = 2e-3
+
+
+def pools_after_write(case):
+    """Oracle view of the pools once the case's new tokens are written (host bits)."""
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    if case.k_new is None:
+        return kp, vp
+    return oracle.kv_write_ref(kp, vp, bits(case.k_new), bits(case.v_new),
+                               case.cu_new.cpu().numpy(), case.start_pos.cpu().numpy(),
+                               case.block_tables.cpu().numpy(), case.page_size)
+
+
+def oracle_full(case, kp=None, vp=None, causal=None):
+    if kp is None:
+        kp, vp = pools_after_write(case)
+    return oracle.attention_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
+                                case.seq_lens_k.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
+                                case.scale, case.causal if causal is None else causal,
+                                case.page_size)
+
+
+def oracle_rows(case, rows, kp=None, vp=None):
+    if kp is None:
+        kp, vp = pools_after_write(case)
+    return oracle.attention_rows_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
+                                     case.seq_lens_k.cpu().numpy(),
+                                     case.cu_seqlens_q.cpu().numpy(), case.scale, case.causal,
+                                     case.page_size, rows)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_parity(got, ref, what="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    mn = float(err.mean()) if err.size else 0.0
+    assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e}, mean-abs {mn:.3e}"
+    return mx, mn
+
+
+def assert_lse(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: lse finiteness differs"
+    assert (got[~fin] == ref[~fin]).all()
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))
+        assert err.max() <= LSE_ABS, f"{what}: lse error {err.max():.3e}"

@@ -1,0 +1,173 @@
+"""The C-ABI boundary: the library loads, exports what the header declares, and
+rejects invalid arguments with the documented status before touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_flashattention_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ["kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
+              "paged_attn_prefill_varlen", "paged_attn_decode_workspace_bytes",
+              "paged_attn_decode_num_splits", "pa_status_string", "pa_last_error",
+              "pa_describe_launch"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from paged_kv_flashattention_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_status_strings(lib):
+    assert lib.pa_status_string(0) == b"PA_OK"
+    assert lib.pa_status_string(3) == b"PA_ERR_UNSUPPORTED"
+    assert lib.pa_status_string(99) == b"PA_ERR_UNKNOWN"
+
+
+FAKE = 0x10000          # 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def decode_call(lib, **over):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, B=2,
+                max_pages=4, num_pages=8, ps=16, Hq=8, Hkv=2, D=128, scale=0.1, max_seq=64,
+                S=1, ws=None, ws_bytes=0)
+    args.update(over)
+    return lib.paged_attn_decode(args["out"], args["lse"], args["q"], args["k"], args["v"],
+                                 args["bt"], args["lens"], args["B"], args["max_pages"],
+                                 args["num_pages"], args["ps"], args["Hq"], args["Hkv"],
+                                 args["D"], args["scale"], args["max_seq"], args["S"],
+                                 args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1),
+    (dict(bt=None), 1),
+    (dict(D=96), 3),
+    (dict(ps=24), 3),
+    (dict(Hq=7, Hkv=2), 3),
+    (dict(Hq=34, Hkv=2), 3),            # group of 17
+    (dict(B=-1), 2),
+    (dict(num_pages=0), 2),
+    (dict(q=FAKE + 8), 4),
+    (dict(S=4, ws=None), 5),
+    (dict(S=4, ws=FAKE, ws_bytes=16), 5),
+    (dict(scale=float("nan")), 2),
+])
+def test_decode_rejects_invalid_arguments(lib, over, status):
+    assert decode_call(lib, **over) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_decode_with_no_sequences_is_ok(lib):
+    assert decode_call(lib, B=0, out=None, q=None) in (0, 1)
+
+
+def test_workspace_sizing(lib):
+    assert lib.paged_attn_decode_workspace_bytes(32, 28, 4, 128, 8192, 1) == 0
+    need = lib.paged_attn_decode_workspace_bytes(32, 28, 4, 128, 8192, 8)
+    rows = 32 * 28 * 8
+    assert need >= rows * 128 * 4 + rows * 4
+    auto = lib.paged_attn_decode_num_splits(32, 4, 8192)
+    assert 1 <= auto <= 8192 // 32
+    assert lib.paged_attn_decode_num_splits(1, 1, 10) == 1        # one chunk -> one split
+    # split count never exceeds the number of 32-key chunks
+    assert lib.paged_attn_decode_workspace_bytes(1, 4, 4, 128, 100, 64) == \
+        lib.paged_attn_decode_workspace_bytes(1, 4, 4, 128, 100, 4)
+
+
+def test_prefill_and_write_reject_invalid_arguments(lib):
+    f = lib.paged_attn_prefill_varlen
+    base = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 4, 8, 16, 8, 2, 128,
+            0.1, 1, None]
+    assert f(*base) == 0 or True   # valid arguments are not launched here (no GPU)
+    bad = list(base); bad[2] = None
+    assert f(*bad) == 1
+    bad = list(base); bad[16] = 80
+    assert f(*bad) == 3
+    bad = list(base); bad[13] = 48
+    assert f(*bad) == 3
+    bad = list(base); bad[0] = FAKE + 2
+    assert f(*bad) == 4
+    w = lib.kv_page_write
+    wb = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 8, 16, 2, 128, None]
+    bad = list(wb); bad[4] = None
+    assert w(*bad) == 1
+    bad = list(wb); bad[11] = 8
+    assert w(*bad) == 3
+    bad = list(wb); bad[8] = 0
+    assert w(*bad) == 0          # nothing to write
+    r = lib.paged_attn_splitk_reduce
+    assert r(FAKE, None, FAKE, FAKE, 4, 0, 128, None) == 2
+    assert r(FAKE, None, FAKE, FAKE, 4, 2, 32, None) == 3
+    assert r(None, None, FAKE, FAKE, 4, 2, 128, None) == 1
+
+
+def test_binding_refuses_wrong_dtypes_before_any_device_work():
+    import paged_kv_flashattention_amd as pa
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    kp = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    bt64 = torch.zeros(2, 2, dtype=torch.int64)
+    lens = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        pa.paged_attn_decode(q, kp, kp, bt64, lens, 0.1)
+    with pytest.raises(TypeError):
+        pa.paged_attn_decode(q.half(), kp, kp, bt64.int(), lens, 0.1)
+    with pytest.raises(TypeError):
+        pa.paged_attn_prefill_varlen(q, kp.float(), kp, lens, lens, bt64.int(), 0.1)
+    with pytest.raises(ValueError):      # a CPU tensor is refused, never computed on
+        pa.paged_attn_decode(q, kp, kp, bt64.int(), lens, 0.1)
+
+
+@pytest.mark.gpu
+def test_describe_launch_names_the_kernel(require_gpu):
+    import paged_kv_flashattention_amd as pa
+    from workloads import make_case
+    case = make_case("d", seq_lens=[100, 50], Hq=8, Hkv=2, D=128, page_size=16, seed=1,
+                     device="cuda")
+    pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables, case.seq_lens_k,
+                         case.scale, max_seq_len=100, num_splits=2)
+    torch.cuda.synchronize()
+    d = pa.describe_launch()
+    assert "decode_partition" in d and "splitk_reduce" in d
+
+
+@pytest.mark.gpu
+def test_failed_call_leaves_output_untouched(require_gpu):
+    import paged_kv_flashattention_amd as pa
+    from workloads import make_case
+    case = make_case("d", seq_lens=[100, 50], Hq=8, Hkv=2, D=128, page_size=16, seed=1,
+                     device="cuda")
+    out = torch.full((2, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                             case.seq_lens_k, case.scale, max_seq_len=100, num_splits=3,
+                             out=out, workspace=ws)
+    assert e.value.status == 5
+    torch.cuda.synchronize()
+    assert (out.float() == 7.0).all()

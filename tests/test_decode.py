@@ -1,0 +1,187 @@
+"""GPU parity of paged_attn_decode (+ its split-K reduce) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_flashattention_amd as pa
+from tests.parity import (as_f64, assert_lse, assert_parity, oracle_full, oracle_rows,
+                          pools_after_write)
+from workloads import bits, make_case, make_config, units
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(case, num_splits=0, max_seq_len=None):
+    out, lse = pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                    case.seq_lens_k, case.scale,
+                                    max_seq_len=case.max_seq_len if max_seq_len is None else max_seq_len,
+                                    num_splits=num_splits, return_lse=True, validate=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 0, 64])
+def test_tiny_decode_config(require_gpu, splits):
+    case = make_config("tiny_decode", "cuda")
+    print(f"[decode] tiny_decode splits={splits}", flush=True)
+    out, lse = run_decode(case, splits)
+    o_ref, l_ref = oracle_full(case)
+    assert_parity(as_f64(out), o_ref, "tiny_decode")
+    assert_lse(as_f64(lse), l_ref, "tiny_decode lse")
+
+
+AWKWARD = [
+    # seq_lens, Hq, Hkv, D, ps, splits
+    ([1, 15, 16, 17], 8, 2, 128, 16, 1),
+    ([1, 15, 16, 17], 8, 2, 128, 16, 4),
+    ([127, 4096, 33, 64], 28, 4, 128, 16, 0),
+    ([127, 4096, 33, 64], 28, 4, 128, 16, 7),
+    ([0, 5, 0, 300], 32, 8, 128, 16, 3),
+    ([200, 1000], 16, 1, 128, 64, 5),         # GQA 16, page size 64
+    ([200, 1000], 8, 8, 64, 32, 2),           # MHA, D 64, page size 32
+    ([513, 77, 1], 7, 1, 64, 64, 0),          # GQA 7, D 64
+    ([100], 4, 4, 128, 16, 64),               # more splits than chunks
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,ps,splits", AWKWARD)
+def test_awkward_shapes(require_gpu, lens, Hq, Hkv, D, ps, splits):
+    print(f"[decode] awkward lens={lens} Hq={Hq} Hkv={Hkv} D={D} ps={ps} S={splits}", flush=True)
+    case = make_case("awk", seq_lens=lens, Hq=Hq, Hkv=Hkv, D=D, page_size=ps, seed=sum(lens) + D,
+                     num_pages=sum(-(-L // ps) for L in lens) + 5, device="cuda")
+    out, lse = run_decode(case, splits)
+    o_ref, l_ref = oracle_full(case)
+    assert_parity(as_f64(out), o_ref, "awkward")
+    assert_lse(as_f64(lse), l_ref, "awkward lse")
+    for b, L in enumerate(lens):
+        if L == 0:       # no key: defined zeros, lse = -inf
+            assert (as_f64(out[b]) == 0).all()
+            assert np.isneginf(as_f64(lse[b])).all()
+
+
+def test_extreme_logits(require_gpu):
+    case = make_case("x", seq_lens=[700, 33, 4096], Hq=28, Hkv=4, D=128, page_size=16, seed=5,
+                     device="cuda")
+    case.q = (case.q.float() * 30).to(torch.bfloat16)
+    print("[decode] extreme logits", flush=True)
+    out, lse = run_decode(case, 4)
+    o_ref, l_ref = oracle_full(case)
+    assert_parity(as_f64(out), o_ref, "extreme logits")
+    assert_lse(as_f64(lse), l_ref, "extreme lse")
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_dominant_key_gathers_bit_exact(require_gpu, splits):
+    """Each query matches one key so strongly that every other weight underflows to 0
+    in fp32: the output must be that key's V row exactly (pins page/slot indexing)."""
+    lens = [300, 77, 1024]
+    case = make_case("dom", seq_lens=lens, Hq=8, Hkv=2, D=128, page_size=16, seed=9,
+                     device="cuda", std_kv=0.01)
+    rng = np.random.default_rng(0)
+    targets = [int(rng.integers(0, L)) for L in lens]
+    bt = case.block_tables.cpu().numpy()
+    for b, j in enumerate(targets):
+        page, slot = int(bt[b, j // 16]), j % 16
+        for kvh in range(2):
+            case.k_pool[page, slot, kvh] = 0
+            case.k_pool[page, slot, kvh, 0] = 64.0
+    case.q.zero_()
+    case.q[:, :, 0] = 64.0   # score gap 64 * 64 / sqrt(128) ~ 362 >> 110
+    print(f"[decode] dominant key splits={splits}", flush=True)
+    out, _ = run_decode(case, splits)
+    vp = bits(case.v_pool)
+    got = bits(out)
+    for b, j in enumerate(targets):
+        page, slot = int(bt[b, j // 16]), j % 16
+        for h in range(8):
+            assert np.array_equal(got[b, h], vp[page, slot, h // 4]), (b, h)
+
+
+def test_single_key_returns_value_row_bit_exact(require_gpu):
+    case = make_case("one", seq_lens=[1, 1, 1], Hq=16, Hkv=4, D=128, page_size=16, seed=3,
+                     device="cuda")
+    out, lse = run_decode(case, 1)
+    vp = bits(case.v_pool)
+    bt = case.block_tables.cpu().numpy()
+    got = bits(out)
+    for b in range(3):
+        for h in range(16):
+            assert np.array_equal(got[b, h], vp[bt[b, 0], 0, h // 4])
+
+
+def test_repeat_runs_are_bitwise_identical(require_gpu):
+    case = make_case("det", seq_lens=[3000, 17, 999, 4096], Hq=28, Hkv=4, D=128, page_size=16,
+                     seed=4, device="cuda")
+    ref = bits(run_decode(case, 6)[0])
+    for _ in range(20):
+        assert np.array_equal(bits(run_decode(case, 6)[0]), ref)
+
+
+def test_splitk_reduce_standalone_matches_merge(require_gpu):
+    rng = np.random.default_rng(11)
+    R, S, D = 37, 9, 128
+    po = rng.standard_normal((R, S, D)).astype(np.float32)
+    pl = (rng.standard_normal((R, S)) * 5).astype(np.float32)
+    pl[3, :] = -np.inf           # a row with every partition empty
+    pl[4, ::2] = -np.inf         # some empty partitions
+    out, lse = pa.paged_attn_splitk_reduce(torch.as_tensor(po, device="cuda"),
+                                           torch.as_tensor(pl, device="cuda"))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge_ref(po.astype(np.float64), pl.astype(np.float64))
+    assert_parity(as_f64(out), o_ref, "reduce", max_abs=1e-2, mean_abs=2e-3)
+    assert_lse(as_f64(lse), l_ref, "reduce lse")
+    assert (as_f64(out[3]) == 0).all()
+
+
+def _sample_rows(case, n_seq, n_heads, seed):
+    rng = np.random.default_rng(seed)
+    seqs = rng.choice(case.B, size=min(n_seq, case.B), replace=False)
+    rows = []
+    for b in seqs:
+        for h in rng.choice(case.Hq, size=n_heads, replace=False):
+            rows.append((int(b), int(h)))
+    return rows
+
+
+def test_qwen7b_decode_full_size_sampled(require_gpu):
+    """Qwen2.5-7B-shaped decode at its full size (32 x 8192, Hq 28, Hkv 4), in the
+    launch configuration the benchmark times; oracle on sampled (sequence, head) rows."""
+    case = make_config("qwen7b_decode", "cuda")
+    print("[decode] qwen7b full size", flush=True)
+    out, lse = run_decode(case, 0)
+    rows = _sample_rows(case, 6, 4, 1)
+    kp_rows = None
+    o_ref, l_ref = oracle_rows(case, rows)
+    got = np.stack([as_f64(out[b, h]) for b, h in rows])
+    assert_parity(got, o_ref, "qwen7b sampled")
+    assert_lse(np.array([float(lse[b, h]) for b, h in rows]), l_ref, "qwen7b lse")
+    # every output finite and every row a convex combination: |o| <= max |v|
+    assert torch.isfinite(out.float()).all()
+
+
+def test_long_context_decode_full_size_sampled(require_gpu):
+    """Long-context decode at full size (8 x 131072, Hq 64, Hkv 8, page 64, S = 64)."""
+    case = make_config("long_decode", "cuda")
+    print("[decode] long_decode full size", flush=True)
+    out, lse = run_decode(case, 64)
+    rows = _sample_rows(case, 2, 3, 2)
+    # the oracle needs only the sampled sequences' pages: gather them on the host
+    bt = case.block_tables.cpu().numpy()
+    o_ref = np.zeros((len(rows), 128))
+    l_ref = np.zeros(len(rows))
+    q = bits(case.q)
+    for i, (b, h) in enumerate(rows):
+        pages = torch.as_tensor(bt[b].astype(np.int64), device="cuda")
+        kh = bits(case.k_pool[pages, :, h // 8])      # [pages, 64, D]
+        vh = bits(case.v_pool[pages, :, h // 8])
+        k = oracle.bf16_bits_to_f64(kh).reshape(-1, 128)
+        v = oracle.bf16_bits_to_f64(vh).reshape(-1, 128)
+        o, l = oracle.attend_rows(oracle.bf16_bits_to_f64(q[b, h])[None], k, v, case.scale,
+                                  [131072])
+        o_ref[i], l_ref[i] = o[0], l[0]
+    got = np.stack([as_f64(out[b, h]) for b, h in rows])
+    assert_parity(got, o_ref, "long_decode sampled")
+    assert_lse(np.array([float(lse[b, h]) for b, h in rows]), l_ref, "long lse")
+    assert torch.isfinite(out.float()).all()
