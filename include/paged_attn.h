@@ -98,8 +98,8 @@ int32_t paged_attn_decode_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len
 /*
  * paged_attn_decode_workspace_bytes -- bytes of workspace paged_attn_decode needs for
  * this shape and split count (after resolving num_splits <= 0 as above): fp32
- * partial outputs [B, Hq, S, D] followed by fp32 partial lse [B, Hq, S], 256-byte
- * aligned.  0 when S == 1.
+ * partial outputs [B, Hq, S, D] followed by fp32 partial lse [B, Hq, S], each region
+ * 256-byte aligned.  0 when S == 1.  Split counts are capped at 65535.
  */
 size_t paged_attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                          int32_t max_seq_len, int32_t num_splits);
@@ -124,7 +124,8 @@ size_t paged_attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int
  *                    past S * part_len are not attended)
  *   num_splits     : S, or <= 0 for paged_attn_decode_num_splits()
  *   workspace      : device buffer of at least paged_attn_decode_workspace_bytes()
- *                    (may be NULL when that is 0); contents are scratch
+ *                    (may be NULL when that is 0); contents are scratch.  Calls that
+ *                    share a workspace must not run concurrently.
  */
 int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_tables,
@@ -133,6 +134,29 @@ int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_po
                       int32_t D, float softmax_scale, int32_t max_seq_len,
                       int32_t num_splits, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * paged_attn_decode_partials -- the first phase of paged_attn_decode on its own:
+ * per-partition results, to be merged later by paged_attn_splitk_reduce (possibly
+ * after gathering partials of the same rows computed elsewhere, e.g. on other GPUs
+ * holding other parts of the KV history; the merge is associative).
+ *
+ * Same arguments and partitioning as paged_attn_decode, with num_splits >= 1 given
+ * explicitly (it must not exceed the number of 32-key chunks of max_seq_len).  For
+ * row r = b * Hq + h and partition c (keys [c * part_len, (c+1) * part_len) of the
+ * sequence), partial_out[r, c, :] is the attention output over that partition alone
+ * and partial_lse[r, c] its natural-log log-sum-exp ("The Stack Below the Stack
+ * (Part 2)", section 2.2, step 2); an empty partition gives 0 and -inf.
+ *
+ *   partial_out : [B * Hq, S, D] fp32 (16-byte aligned)   partial_lse : [B * Hq, S] fp32
+ */
+int paged_attn_decode_partials(float* partial_out, float* partial_lse, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t B, int32_t max_pages, int32_t num_pages,
+                               int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                               float softmax_scale, int32_t max_seq_len, int32_t num_splits,
+                               void* stream);
 
 /*
  * paged_attn_splitk_reduce -- merge S partial results per row into the exact one.

@@ -8,6 +8,7 @@ Entry points (same names as the C ABI):
 
 * :func:`kv_page_write`      -- place new tokens' K/V into their pages;
 * :func:`paged_attn_decode`  -- one query row per sequence, split-K + merge;
+* :func:`paged_attn_decode_partials` -- decode's per-partition results only;
 * :func:`paged_attn_splitk_reduce` -- the merge on its own;
 * :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA.
 
@@ -26,7 +27,8 @@ import torch
 from . import _lib
 
 __all__ = [
-    "PagedAttnError", "kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
+    "PagedAttnError", "kv_page_write", "paged_attn_decode", "paged_attn_decode_partials",
+    "paged_attn_splitk_reduce",
     "paged_attn_prefill_varlen", "decode_num_splits", "decode_workspace_bytes",
     "describe_launch", "library_path", "load_library",
 ]
@@ -161,6 +163,7 @@ def decode_num_splits(B: int, Hkv: int, max_seq_len: int) -> int:
 
 
 def decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, num_splits=0) -> int:
+    """Workspace bytes for paged_attn_decode (scratch; no initialisation needed)."""
     return int(load_library().paged_attn_decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len,
                                                                 num_splits))
 
@@ -217,6 +220,44 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale),
             int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def paged_attn_decode_partials(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
+                               num_splits: int, max_seq_len: Optional[int] = None,
+                               partial_out: Optional[torch.Tensor] = None,
+                               partial_lse: Optional[torch.Tensor] = None, stream=None):
+    """Per-partition decode results: partial_out [B*Hq, S, D] fp32, partial_lse [B*Hq, S]."""
+    _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
+            (v_pool, "v_pool", torch.bfloat16), (block_tables, "block_tables", torch.int32),
+            (seq_lens, "seq_lens", torch.int32), (partial_out, "partial_out", torch.float32),
+            (partial_lse, "partial_lse", torch.float32))
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, None)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pool.shape
+    if Dk != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shapes do not match q")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    S = int(num_splits)
+    if partial_out is None:
+        partial_out = torch.empty((B * Hq, S, D), dtype=torch.float32, device=dev)
+    _need(partial_out, "partial_out", torch.float32, 3, dev)
+    if partial_lse is None:
+        partial_lse = torch.empty((B * Hq, S), dtype=torch.float32, device=dev)
+    _need(partial_lse, "partial_lse", torch.float32, 2, dev)
+    if tuple(partial_out.shape) != (B * Hq, S, D) or tuple(partial_lse.shape) != (B * Hq, S):
+        raise ValueError("partials must be [B*Hq, S, D] and [B*Hq, S]")
+    with torch.cuda.device(dev):
+        _check(load_library().paged_attn_decode_partials(
+            _ptr(partial_out), _ptr(partial_lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D,
+            float(softmax_scale), int(max_seq_len), S, _stream(stream)))
+    return partial_out, partial_lse
 
 
 def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, stream=None):

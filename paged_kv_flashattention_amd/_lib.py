@@ -27,6 +27,9 @@ SIGNATURES = {
     "paged_attn_decode": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                   c_float, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "paged_attn_decode_partials": (c_i32, [c_fp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           c_float, c_i32, c_i32, c_vp]),
     "paged_attn_splitk_reduce": (c_i32, [c_vp, c_fp, c_fp, c_fp, c_i32, c_i32, c_i32, c_vp]),
     "paged_attn_prefill_varlen": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,

@@ -50,30 +50,70 @@ int check_pool(int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_siz
 }
 
 constexpr int kChunk = 32;   // keys per decode chunk; partitions are multiples of it
+constexpr int32_t kMaxSplits = 65535;   // arrival counts are 16-bit
 
 int32_t resolve_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t num_splits) {
   const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   if (num_splits <= 0) {
-    // ~2048 work-groups of 4 waves fill 256 CUs about 2 deep at 8 waves per CU
-    // while each partition keeps >= 8 chunks (2 per wave) to amortise start-up.
+    // About one work-group per CU (256 on MI355X), each streaming one long
+    // partition, measured fastest; partitions keep >= 8 chunks.
     const long long groups = (long long)(B > 0 ? B : 1) * Hkv;
-    long long s = (2048 + groups - 1) / groups;
+    long long s = (256 + groups / 2) / groups;
     const long long max_by_len = chunks / 8 > 0 ? chunks / 8 : 1;
     if (s > max_by_len) s = max_by_len;
     if (s < 1) s = 1;
     num_splits = (int32_t)s;
   }
   if (num_splits > chunks) num_splits = chunks;
+  if (num_splits > kMaxSplits) num_splits = kMaxSplits;
   return num_splits < 1 ? 1 : num_splits;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Split-K workspace: fp32 partial outputs [B, Hq, S, D] then fp32 partial lse
+// [B, Hq, S].
 size_t workspace_for(int32_t B, int32_t Hq, int32_t D, int32_t S) {
   if (S <= 1) return 0;
   const size_t rows = (size_t)B * Hq * S;
   return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
 }
+
+// Checks and argument packing shared by paged_attn_decode and
+// paged_attn_decode_partials.  `what` names the entry point in messages.
+int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* k_pool,
+                const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
+                int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
+                int32_t num_splits) {
+  if (B < 0 || max_seq_len < 0)
+    return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
+  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
+  if (st) return st;
+  if (B > 0) {
+    if (!q || !k_pool || !v_pool || !block_tables || !seq_lens)
+      return fail(PA_ERR_NULL, "%s: a required pointer is NULL", what);
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+      return fail(PA_ERR_MISALIGNED, "%s: data pointers must be 16-byte aligned", what);
+  }
+  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "%s: softmax scale is NaN", what);
+  const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
+  const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
+  a = pa::DecodeArgs{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.ps_shift = log2_exact(page_size);
+  a.S = S;
+  a.part_len = ((chunks + S - 1) / S) * kChunk;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return PA_OK;
+}
+
 
 }  // namespace
 
@@ -172,47 +212,31 @@ int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_po
                       int32_t num_splits, void* workspace, size_t workspace_bytes,
                       void* stream) {
   g_last_error[0] = 0;
-  if (B < 0 || max_seq_len < 0) return fail(PA_ERR_SHAPE, "decode: B=%d max_seq_len=%d", B, max_seq_len);
-  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
+  pa::DecodeArgs a;
+  int st = decode_args(a, "decode", q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
+                       num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                       num_splits);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "decode: nothing to do");
     return PA_OK;
   }
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
-    return fail(PA_ERR_NULL, "decode: a required pointer is NULL");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(PA_ERR_MISALIGNED, "decode: data pointers must be 16-byte aligned");
-  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "decode: softmax scale is NaN");
-  const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
+  if (!out) return fail(PA_ERR_NULL, "decode: out is NULL");
+  if (!aligned16(out)) return fail(PA_ERR_MISALIGNED, "decode: out must be 16-byte aligned");
+  const int32_t S = a.S;
   const size_t need = workspace_for(B, Hq, D, S);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "decode: workspace of %zu bytes needed for %d splits, got %zu",
                 need, S, workspace ? workspace_bytes : (size_t)0);
   if (need && !aligned16(workspace))
     return fail(PA_ERR_MISALIGNED, "decode: workspace must be 16-byte aligned");
-
-  const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
-  const int32_t part_len = ((chunks + S - 1) / S) * kChunk;
-
-  pa::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_pool = static_cast<const uint16_t*>(k_pool);
-  a.v_pool = static_cast<const uint16_t*>(v_pool);
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
   a.lse_out = lse_out;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
-  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
-  a.ps_shift = log2_exact(page_size);
-  a.part_len = part_len; a.S = S;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
   const size_t rows = (size_t)B * Hq * S;
   if (S > 1) {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align256(rows * D * sizeof(float)));
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + align256(rows * D * sizeof(float)));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char d1[256], d2[256];
@@ -228,6 +252,41 @@ int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_po
   } else {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s", d1);
   }
+  return PA_OK;
+}
+
+int paged_attn_decode_partials(float* partial_out, float* partial_lse, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t B, int32_t max_pages, int32_t num_pages,
+                               int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                               float softmax_scale, int32_t max_seq_len, int32_t num_splits,
+                               void* stream) {
+  g_last_error[0] = 0;
+  pa::DecodeArgs a;
+  if (num_splits < 1) return fail(PA_ERR_SHAPE, "decode_partials: num_splits=%d < 1", num_splits);
+  int st = decode_args(a, "decode_partials", q, k_pool, v_pool, block_tables, seq_lens, B,
+                       max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                       num_splits);
+  if (st) return st;
+  if (a.S != num_splits)
+    return fail(PA_ERR_SHAPE, "decode_partials: %d splits exceed the %d 32-key chunks of max_seq_len",
+                num_splits, a.S);
+  if (B == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "decode_partials: nothing to do");
+    return PA_OK;
+  }
+  if (!partial_out || !partial_lse) return fail(PA_ERR_NULL, "decode_partials: NULL partials");
+  if (!aligned16(partial_out))
+    return fail(PA_ERR_MISALIGNED, "decode_partials: partial_out must be 16-byte aligned");
+  // the partition kernel writes partials whenever S > 1; with S == 1 route the
+  // single partition through the same path by presenting it as split 0 of 1
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.force_partials = 1;
+  hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream), g_last_launch,
+                                   sizeof(g_last_launch));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode_partials launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -73,6 +73,14 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
+// Streaming loads for data read exactly once (decode's K/V): non-temporal, so
+// they do not displace reusable lines in the caches.
+__device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld8_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 // Page id of logical key `key` of a sequence, clamped into the pool and the
 // table row so that a malformed table cannot send a load outside the buffers.
@@ -83,5 +91,41 @@ __device__ __forceinline__ int page_of(const int32_t* table_row, int key, int ps
   int page = table_row[idx];
   return (unsigned)page < (unsigned)num_pages ? page : 0;
 }
+
+// A window of 64 consecutive block-table entries of one sequence, held one per
+// lane, plus the next 64 already in flight.  Page lookups are made with a
+// wave-uniform table index (readlane, so the page id lands in a scalar register)
+// and must not decrease from call to call; crossing the window end shifts it
+// and fetches the following 64 entries.  Entries are clamped into the table row
+// and page ids into the pool.
+struct PageWindow {
+  const int32_t* row;
+  int max_pages, num_pages;
+  int base;       // table index held by lane 0 of `cur` (multiple of 64)
+  int cur, nxt;
+
+  __device__ __forceinline__ int fetch(int idx) const {
+    idx = idx < max_pages ? idx : max_pages - 1;
+    return row[idx];
+  }
+  __device__ __forceinline__ void init(const int32_t* r, int max_p, int num_p, int first_idx,
+                                       int lane) {
+    row = r;
+    max_pages = max_p;
+    num_pages = num_p;
+    base = first_idx & ~63;
+    cur = fetch(base + lane);
+    nxt = fetch(base + 64 + lane);
+  }
+  __device__ __forceinline__ int page(int idx, int lane) {
+    while (idx >= base + 64) {
+      base += 64;
+      cur = nxt;
+      nxt = fetch(base + 64 + lane);
+    }
+    const int p = __builtin_amdgcn_readlane(cur, idx - base);
+    return (unsigned)p < (unsigned)num_pages ? p : 0;
+  }
+};
 
 }  // namespace pa

@@ -1,8 +1,8 @@
 // Split-K paged decode attention for gfx950.
 //
 // One work-group of W waves owns one (sequence b, KV head, partition) triple.
-// The partition's keys are walked in 32-key chunks, chunk c going to wave c % W;
-// each wave streams its chunks straight from the page pools into registers
+// The partition's keys are walked in 32-key chunks, each wave taking a contiguous
+// run of them; each wave streams its chunks straight from the page pools into registers
 // (16-byte loads, next chunk in flight while the current one computes), so the
 // kernel reads every attended K/V byte exactly once -- decode is bound by those
 // reads ("8. Kernels and Attention Backends", "Counting attention's traffic").
@@ -19,8 +19,10 @@
 //
 // At the end the W waves merge through LDS and the work-group writes either the
 // final bf16 output (one partition) or the partition's normalised partial output
-// and natural-log lse for the split-K reduce ("The Stack Below the Stack (Part 2)",
-// section 2.2).
+// and natural-log lse, which the split-K reduce kernel merges ("The Stack Below the
+// Stack (Part 2)", section 2.2: a second kernel combines the chunks).  Merging in
+// the last-arriving work-group instead was measured slower on MI355X: the partials
+// must then bypass the per-XCD L2 caches.
 #include <stdio.h>
 
 #include "common.hpp"
@@ -35,39 +37,111 @@ struct DecodeChunk {
   uint32_t v[8][D / 32];     // V rows of the lane's 8 keys, d in [D/16 * n, D/16 * (n+1))
 };
 
+// Loads of one 32-key chunk (keys c0 .. c0+31, c0 a multiple of 32); pg0 / pg1 are
+// the wave-uniform pages holding keys c0 and c0+16.  K and V are issued separately
+// so that each can be refilled as soon as its registers are consumed.
 template <int D>
-__device__ __forceinline__ void decode_load_chunk(DecodeChunk<D>& c, const uint16_t* kbase,
-                                                  const uint16_t* vbase, const int32_t* bt,
-                                                  int c0, const DecodeArgs& a, int n, int g) {
+__device__ __forceinline__ void decode_load_k(DecodeChunk<D>& c, const uint16_t* kbase,
+                                              int pg0, int pg1, int c0, const DecodeArgs& a,
+                                              int n, int g) {
   const int psm = a.page_size - 1;
-  const size_t rs = (size_t)a.Hkv * D;
-  const int pg0 = page_of(bt, c0, a.ps_shift, a.max_pages, a.num_pages);
-  const int pg1 = page_of(bt, c0 + 16, a.ps_shift, a.max_pages, a.num_pages);
-  const size_t base0 = (size_t)pg0 * a.page_size;
-  const size_t base1 = (size_t)pg1 * a.page_size;
-  const uint16_t* ka = kbase + (base0 + ((c0 + n) & psm)) * rs + (D / 4) * g;
-  const uint16_t* kb = kbase + (base1 + ((c0 + 16 + n) & psm)) * rs + (D / 4) * g;
+  const int rs = a.Hkv * D;                        // elements between consecutive slots
+  const size_t page_elems = (size_t)a.page_size * rs;
+  const uint16_t* ka = kbase + (size_t)pg0 * page_elems + ((c0 + n) & psm) * rs + (D / 4) * g;
+  const uint16_t* kb = kbase + (size_t)pg1 * page_elems + ((c0 + 16 + n) & psm) * rs +
+                       (D / 4) * g;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
+#ifdef PA_DECODE_K_NT
+    c.ka[kk] = ld16_nt(ka + 8 * kk);
+    c.kb[kk] = ld16_nt(kb + 8 * kk);
+#else
     c.ka[kk] = ld16(ka + 8 * kk);
     c.kb[kk] = ld16(kb + 8 * kk);
+#endif
   }
+}
+
+// K of a chunk in whole-row order: instruction i covers rows RPI*i .. RPI*i+RPI-1
+// (RPI = 512 / D rows of D bf16), each row read by D/8 consecutive lanes, so every
+// load instruction consumes whole cache lines and can stream past the caches.
+// The rows are then regrouped through LDS into the MFMA operand layout.
+template <int D>
+struct KRows {
+  static constexpr int LPR = D / 8;          // lanes per row (16 B each)
+  static constexpr int RPI = 64 / LPR;       // rows per load instruction
+  static constexpr int NI = 32 / RPI;        // load instructions per 32-key chunk
+  static constexpr int LROW = D + 8;         // LDS row pitch (bf16), 16 B pad
+  u32x4 r[NI];
+};
+
+template <int D>
+__device__ __forceinline__ void decode_load_k_rows(KRows<D>& k, const uint16_t* kbase, int pg0,
+                                                   int pg1, int c0, const DecodeArgs& a,
+                                                   int lane) {
+  const int psm = a.page_size - 1;
+  const int rs = a.Hkv * D;
+  const size_t page_elems = (size_t)a.page_size * rs;
+  const int sub = lane / KRows<D>::LPR;
+  const int off = (lane % KRows<D>::LPR) * 8;
+#pragma unroll
+  for (int i = 0; i < KRows<D>::NI; ++i) {
+    const int row = KRows<D>::RPI * i + sub;           // key c0 + row
+    const int pg = row < 16 ? pg0 : pg1;
+    const uint16_t* p = kbase + (size_t)pg * page_elems + ((c0 + row) & psm) * rs + off;
+    k.r[i] = ld16_nt(p);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void decode_k_to_lds(const KRows<D>& k, uint16_t* kl, int lane) {
+  const int sub = lane / KRows<D>::LPR;
+  const int off = (lane % KRows<D>::LPR) * 8;
+#pragma unroll
+  for (int i = 0; i < KRows<D>::NI; ++i)
+    *reinterpret_cast<u32x4*>(kl + (KRows<D>::RPI * i + sub) * KRows<D>::LROW + off) = k.r[i];
+}
+
+template <int D>
+__device__ __forceinline__ void decode_k_from_lds(DecodeChunk<D>& c, const uint16_t* kl, int n,
+                                                  int g) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    c.ka[kk] = *reinterpret_cast<const u32x4*>(kl + n * KRows<D>::LROW + (D / 4) * g + 8 * kk);
+    c.kb[kk] =
+        *reinterpret_cast<const u32x4*>(kl + (16 + n) * KRows<D>::LROW + (D / 4) * g + 8 * kk);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void decode_load_v(DecodeChunk<D>& c, const uint16_t* vbase,
+                                              int pg0, int pg1, int c0, const DecodeArgs& a,
+                                              int n, int g) {
   constexpr int DPL = D / 16;
-  const uint16_t* va = vbase + (base0 + ((c0 + 4 * g) & psm)) * rs + DPL * n;
-  const uint16_t* vb = vbase + (base1 + ((c0 + 16 + 4 * g) & psm)) * rs + DPL * n;
+  const int psm = a.page_size - 1;
+  const int rs = a.Hkv * D;
+  const size_t page_elems = (size_t)a.page_size * rs;
+  const uint16_t* va = vbase + (size_t)pg0 * page_elems + ((c0 + 4 * g) & psm) * rs + DPL * n;
+  const uint16_t* vb = vbase + (size_t)pg1 * page_elems + ((c0 + 16 + 4 * g) & psm) * rs +
+                       DPL * n;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (D == 128) {
+#ifdef PA_DECODE_V_REGULAR
       u32x4 x = ld16(va + i * rs);
       u32x4 y = ld16(vb + i * rs);
+#else
+      u32x4 x = ld16_nt(va + i * rs);
+      u32x4 y = ld16_nt(vb + i * rs);
+#endif
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         c.v[i][w] = x[w];
         c.v[4 + i][w] = y[w];
       }
     } else {
-      u32x2 x = ld8(va + i * rs);
-      u32x2 y = ld8(vb + i * rs);
+      u32x2 x = ld8_nt(va + i * rs);
+      u32x2 y = ld8_nt(vb + i * rs);
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         c.v[i][w] = x[w];
@@ -81,7 +155,7 @@ template <int D, int W>
 __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) {
   constexpr int DPL = D / 16;   // d values per lane per V row = MFMA d-tiles
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;      // head column (S^T, O^T) / K row within a tile
   const int g = lane >> 4;      // k-group of the MFMA operands
   const int kvh = blockIdx.x;
@@ -111,88 +185,115 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     }
   }
 
+  // per-wave staging of one chunk's K rows
+  __shared__ __align__(16) uint16_t k_lds_all[W][32 * KRows<D>::LROW];
+  uint16_t* k_lds = k_lds_all[wave];
+
   float m_run = kNegInf;     // running max (log2 domain) of head n
   float l_run = 0.f;         // this lane's share of the running sum
   f32x4 acc[DPL];
 #pragma unroll
   for (int t = 0; t < DPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](DecodeChunk<D>& c, int c0) {
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-    f32x4 sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      sa = mfma16x16x32(c.ka[kk], qb[kk], sa);
-      sb = mfma16x16x32(c.kb[kk], qb[kk], sb);
+  // Each wave owns a contiguous run of chunks and keeps one chunk in registers.
+  // The next chunk's K loads are issued as soon as this chunk's scores are formed
+  // and its V loads as soon as P V has consumed the V registers, so every wave
+  // keeps a chunk's worth of loads in flight while it computes; several waves per
+  // SIMD cover the rest of the memory latency.  The next chunk index is clamped to
+  // the wave's last chunk (a repeat of cached addresses) so the loads are issued
+  // unconditionally.  Page ids come from a register window over the table row.
+  const int per = (n_chunks + W - 1) / W;
+  int c = min(n_chunks, wave * per);
+  const int c_hi = min(n_chunks, c + per);
+  // Outer loop: one register window of 64 table entries per pass (lane j holds
+  // entry base + j); the inner loop over the chunks it covers issues no other loads.
+  while (c < c_hi) {
+    const int base = (k_begin + 32 * c) >> a.ps_shift;
+    const int tab = bt[min(base + lane, a.max_pages - 1)];
+    const int c_end = min(c_hi, (((base + 64) << a.ps_shift) - k_begin) >> 5);
+    auto page = [&](int key) {
+      const int pg = __builtin_amdgcn_readlane(tab, (key >> a.ps_shift) - base);
+      return (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+    };
+    DecodeChunk<D> ch;
+    KRows<D> kr;
+    {
+      const int c0 = k_begin + 32 * c;
+      const int p0 = page(c0), p1 = page(c0 + 16);
+      decode_load_k_rows<D>(kr, kbase, p0, p1, c0, a, lane);
+      // K before V: the first scores then wait only for the K loads
+      __builtin_amdgcn_sched_barrier(0);
+      decode_load_v<D>(ch, vbase, p0, p1, c0, a, n, g);
     }
-    float s[8];
+    for (; c < c_end; ++c) {
+      const int c0 = k_begin + 32 * c;
+      const int c0n = k_begin + 32 * min(c + 1, c_end - 1);
+      const int pn0 = page(c0n);
+      const int pn1 = page(c0n + 16);
+
+      // this chunk's K rows -> LDS; the next chunk's K loads reuse the registers
+      decode_k_to_lds<D>(kr, k_lds, lane);
+      decode_load_k_rows<D>(kr, kbase, pn0, pn1, c0n, a, lane);
+      decode_k_from_lds<D>(ch, k_lds, n, g);
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sa[i] * a.scale_log2;
-      s[4 + i] = sb[i] * a.scale_log2;
-    }
-    if (c0 + 32 > k_end) {     // last chunk: keys past the end get -inf, their V rows 0
+      for (int kk = 0; kk < D / 32; ++kk) {
+        sa = mfma16x16x32(ch.ka[kk], qb[kk], sa);
+        sb = mfma16x16x32(ch.kb[kk], qb[kk], sb);
+      }
+
+      float s[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = c0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-        if (key >= k_end) {
-          s[j] = kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sa[i] * a.scale_log2;
+        s[4 + i] = sb[i] * a.scale_log2;
+      }
+      if (c0 + 32 > k_end) {   // last chunk: keys past the end get -inf, their V rows 0
 #pragma unroll
-          for (int w = 0; w < D / 32; ++w) c.v[j][w] = 0u;
+        for (int j = 0; j < 8; ++j) {
+          const int key = c0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+          if (key >= k_end) {
+            s[j] = kNegInf;
+#pragma unroll
+            for (int w = 0; w < D / 32; ++w) ch.v[j][w] = 0u;
+          }
         }
       }
-    }
-    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mt = wave_max_xor16_32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float p[8];
-    float ps = 0.f;
+      float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mt = wave_max_xor16_32(mt);
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      float p[8];
+      float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(s[j] - m_use);
-      ps += p[j];
-    }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
-    const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) {
-      const int w = t >> 1;
-      u32x4 va;
-      if ((t & 1) == 0) {
-        va = u32x4{pack_lo_halves(c.v[0][w], c.v[1][w]), pack_lo_halves(c.v[2][w], c.v[3][w]),
-                   pack_lo_halves(c.v[4][w], c.v[5][w]), pack_lo_halves(c.v[6][w], c.v[7][w])};
-      } else {
-        va = u32x4{pack_hi_halves(c.v[0][w], c.v[1][w]), pack_hi_halves(c.v[2][w], c.v[3][w]),
-                   pack_hi_halves(c.v[4][w], c.v[5][w]), pack_hi_halves(c.v[6][w], c.v[7][w])};
+      for (int j = 0; j < 8; ++j) {
+        p[j] = exp2f(s[j] - m_use);
+        psum += p[j];
       }
-      acc[t] = mfma16x16x32(va, pb, acc[t]);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
+      const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) {
+        const int w = t >> 1;
+        u32x4 va;
+        if ((t & 1) == 0) {
+          va = u32x4{pack_lo_halves(ch.v[0][w], ch.v[1][w]), pack_lo_halves(ch.v[2][w], ch.v[3][w]),
+                     pack_lo_halves(ch.v[4][w], ch.v[5][w]), pack_lo_halves(ch.v[6][w], ch.v[7][w])};
+        } else {
+          va = u32x4{pack_hi_halves(ch.v[0][w], ch.v[1][w]), pack_hi_halves(ch.v[2][w], ch.v[3][w]),
+                     pack_hi_halves(ch.v[4][w], ch.v[5][w]), pack_hi_halves(ch.v[6][w], ch.v[7][w])};
+        }
+        acc[t] = mfma16x16x32(va, pb, acc[t]);
+      }
+      decode_load_v<D>(ch, vbase, pn0, pn1, c0n, a, n, g);
     }
-  };
-
-  // Software pipeline over this wave's chunks: two register buffers, the next
-  // chunk's loads issued before the current chunk is consumed.
-  DecodeChunk<D> c_a, c_b;
-  int c = wave;
-  if (c < n_chunks) decode_load_chunk<D>(c_a, kbase, vbase, bt, k_begin + 32 * c, a, n, g);
-  while (c < n_chunks) {
-    const int c_next = c + W;
-    if (c_next < n_chunks)
-      decode_load_chunk<D>(c_b, kbase, vbase, bt, k_begin + 32 * c_next, a, n, g);
-    compute(c_a, k_begin + 32 * c);
-    c = c_next;
-    if (c >= n_chunks) break;
-    const int c_next2 = c + W;
-    if (c_next2 < n_chunks)
-      decode_load_chunk<D>(c_a, kbase, vbase, bt, k_begin + 32 * c_next2, a, n, g);
-    compute(c_b, k_begin + 32 * c);
-    c = c_next2;
   }
 
   float l_tot = wave_sum_xor16_32(l_run);
@@ -232,12 +333,13 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     m_fin = M;
   }
 
-  if (!head_ok) return;
   const bool live = l_tot > 0.f;
   const float inv = live ? 1.f / l_tot : 0.f;
   const float lse = live ? (m_fin + __log2f(l_tot)) * kLn2 : kNegInf;
-  // lane holds d = DPL * (4 g + i) + t for i = 0..3, t = 0..DPL-1
-  if (a.S == 1) {
+  // lane holds d = DPL * (4 g + i) + t for i = 0..3, t = 0..DPL-1, i.e. the
+  // DPL * 4 consecutive values starting at d = DPL * 4 * g
+  if (a.S == 1 && !a.force_partials) {
+    if (!head_ok) return;
     uint16_t* op = a.out + ((size_t)b * a.Hq + h) * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -257,21 +359,25 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       }
     }
     if (g == 0 && a.lse_out) a.lse_out[(size_t)b * a.Hq + h] = lse;
-  } else {
-    const size_t row = ((size_t)b * a.Hq + h) * a.S + split;
-    float* op = a.part_o + row * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = DPL * (4 * g + i);
-#pragma unroll
-      for (int t4 = 0; t4 < DPL / 4; ++t4) {
-        f32x4 w = {acc[4 * t4][i] * inv, acc[4 * t4 + 1][i] * inv, acc[4 * t4 + 2][i] * inv,
-                   acc[4 * t4 + 3][i] * inv};
-        *reinterpret_cast<f32x4*>(op + d0 + 4 * t4) = w;
-      }
-    }
-    if (g == 0) a.part_lse[row] = lse;
+    return;
   }
+
+  // Split-K: this partition's normalised output and natural-log lse, merged by
+  // the split-K reduce kernel.
+  if (!head_ok) return;
+  const size_t row = ((size_t)b * a.Hq + h) * a.S + split;
+  float* op = a.part_o + row * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d0 = DPL * (4 * g + i);
+#pragma unroll
+    for (int t4 = 0; t4 < DPL / 4; ++t4) {
+      f32x4 w = {acc[4 * t4][i] * inv, acc[4 * t4 + 1][i] * inv, acc[4 * t4 + 2][i] * inv,
+                 acc[4 * t4 + 3][i] * inv};
+      *reinterpret_cast<f32x4*>(op + d0 + 4 * t4) = w;
+    }
+  }
+  if (g == 0) a.part_lse[row] = lse;
 }
 
 template <int D, int W>
@@ -281,17 +387,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-static constexpr int kDecodeWaves = 4;
+// Waves per work-group: long partitions are split over 4 waves, shorter ones over
+// 2 (measured on MI355X: fewer, longer streams per CU read HBM faster).
+static int decode_waves(int part_len) { return part_len >= 8192 ? 4 : 2; }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len) {
+  const int W = decode_waves(a.part_len);
   hipError_t e;
   if (a.D == 128)
-    e = launch_decode_t<128, kDecodeWaves>(a, stream);
+    e = W == 4 ? launch_decode_t<128, 4>(a, stream) : launch_decode_t<128, 2>(a, stream);
   else
-    e = launch_decode_t<64, kDecodeWaves>(a, stream);
+    e = W == 4 ? launch_decode_t<64, 4>(a, stream) : launch_decode_t<64, 2>(a, stream);
   snprintf(desc, desc_len,
            "decode_partition<D=%d,W=%d> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
-           kDecodeWaves, a.Hkv, a.S, a.B, 64 * kDecodeWaves, a.part_len, a.S);
+           W, a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
   return e;
 }
 

@@ -17,6 +17,7 @@ struct DecodeArgs {
   float* lse_out;                // [B, Hq] or null      (S == 1)
   float* part_o;                 // [B * Hq, S, D]       (S > 1)
   float* part_lse;               // [B * Hq, S]          (S > 1)
+  int force_partials;            // write partials even when S == 1
   int B, Hq, Hkv, G, D;
   int max_pages, num_pages, page_size, ps_shift;
   int part_len, S;

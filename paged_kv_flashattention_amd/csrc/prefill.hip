@@ -55,39 +55,43 @@ struct PfStage {
   uint32_t v[4][D / 32];           // V: 4 key rows x D/16 values
 };
 
+// Global loads of one 64-key tile for this thread.  Wave w stages keys
+// k0 + 16 w .. k0 + 16 w + 15, which share one page (`page`, wave-uniform); the
+// loads are unconditional (page and slot are always inside the pool) and rows past
+// the sequence end are zeroed afterwards.
 template <int D>
 __device__ __forceinline__ void pf_load_tile(PfStage<D>& st, const PrefillArgs& a,
                                              const uint16_t* kbase, const uint16_t* vbase,
-                                             const int32_t* bt, int k0, int L, int tid) {
+                                             int page, int k0, int L, int tid) {
   const int psm = a.page_size - 1;
-  const size_t rs = (size_t)a.Hkv * D;
+  const int rs = a.Hkv * D;
+  const size_t page_off = (size_t)page * a.page_size * rs;
   // K: thread -> key tid/4, d range [(tid%4) * D/4, +D/4)
   {
     const int key = k0 + (tid >> 2);
-    const int page = page_of(bt, key, a.ps_shift, a.max_pages, a.num_pages);
-    const uint16_t* p = kbase + ((size_t)page * a.page_size + (key & psm)) * rs +
-                        (tid & 3) * (D / 4);
+    const uint16_t* p = kbase + page_off + (key & psm) * rs + (tid & 3) * (D / 4);
     const bool ok = key < L;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) st.k[c] = ok ? ld16(p + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < D / 32; ++c) {
+      const u32x4 x = ld16(p + 8 * c);
+      st.k[c] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   // V: thread -> keys 4 (tid/16) .. +3, d range [(tid%16) * D/16, +D/16)
   {
     const int key0 = k0 + 4 * (tid >> 4);
-    const int page = page_of(bt, key0, a.ps_shift, a.max_pages, a.num_pages);
-    const uint16_t* p = vbase + ((size_t)page * a.page_size + (key0 & psm)) * rs +
-                        (tid & 15) * (D / 16);
+    const uint16_t* p = vbase + page_off + (key0 & psm) * rs + (tid & 15) * (D / 16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool ok = key0 + r < L;
       if constexpr (D == 128) {
-        const u32x4 x = ok ? ld16(p + r * rs) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 x = ld16(p + r * rs);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) st.v[r][w] = x[w];
+        for (int w = 0; w < 4; ++w) st.v[r][w] = ok ? x[w] : 0u;
       } else {
-        const u32x2 x = ok ? ld8(p + r * rs) : u32x2{0u, 0u};
+        const u32x2 x = ld8(p + r * rs);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) st.v[r][w] = x[w];
+        for (int w = 0; w < 2; ++w) st.v[r][w] = ok ? x[w] : 0u;
       }
     }
   }
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;         // query column of S^T / O^T
   const int hh = lane >> 5;          // k-half of the MFMA operands
   const int h = blockIdx.x;          // query head
@@ -140,7 +144,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int cap = a.max_pages * a.page_size;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int kvh = h / a.G;
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
   const uint16_t* kbase = a.k_pool + (size_t)kvh * D;
   const uint16_t* vbase = a.v_pool + (size_t)kvh * D;
 
@@ -175,83 +178,103 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
+  // Block-table window: lane j holds the page of this wave's 16 keys of tile
+  // base_t + j, so the 64 tiles of a window need no further table reads; the
+  // tile loop runs one window at a time.
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
+  int base_t = 0;
+  int tab = 0;
+  auto load_tab = [&](int first_tile) {
+    int idx = ((first_tile + lane) * kPfBN + 16 * wave) >> a.ps_shift;
+    idx = idx < a.max_pages ? idx : a.max_pages - 1;
+    return bt[idx];
+  };
+  auto tile_page = [&](int kt) {
+    const int pg = __builtin_amdgcn_readlane(tab, kt - base_t);
+    return (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+  };
+
   PfStage<D> st;
-  if (n_tiles > 0) {
-    pf_load_tile<D>(st, a, kbase, vbase, bt, 0, L, tid);
-    pf_store_tile<D>(st, pf_lds, tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const uint16_t* cur = pf_lds + (kt & 1) * PfLds<D>::STAGE;
-    const bool more = kt + 1 < n_tiles;
-    if (more) pf_load_tile<D>(st, a, kbase, vbase, bt, (kt + 1) * kPfBN, L, tid);
-
-#pragma unroll
-    for (int kb = 0; kb < kPfBN / 32; ++kb) {
-      const int kb0 = kt * kPfBN + kb * 32;
-      const bool skip = kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len;
-      if (skip) continue;
-      // S^T = K Q^T
-      f32x16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      const uint16_t* kl = cur + (kb * 32 + col) * PfLds<D>::KROW + 8 * hh;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + 16 * kk);
-        s = mfma32x32x16(ka, qb[kk], s);
-      }
-      // scale to log2 units; mask keys past the end and (causal) above the diagonal
-      const bool need_mask = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] *= a.scale_log2;
-      if (need_mask) {
-        const int lim = a.causal ? min(L - 1, my_pos) : L - 1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb0 + 8 * j + 4 * hh + i;
-            if (key > lim) s[4 * j + i] = kNegInf;
-          }
-      }
-      float mt = s[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] = exp2f(s[e] - m_use);
-        psum += s[e];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-      const u32x4 pb0 = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
-                         pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
-      const u32x4 pb1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
-                         pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
-      // O^T += V^T P^T
-      const uint16_t* vl = cur + PfLds<D>::K_ELEMS + col * PfLds<D>::VROW + kb * 32 + 8 * hh;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const uint16_t* vrow = vl + 32 * t * PfLds<D>::VROW;
-        const u32x4 va0 = *reinterpret_cast<const u32x4*>(vrow);
-        const u32x4 va1 = *reinterpret_cast<const u32x4*>(vrow + 16);
-        acc[t] = mfma32x32x16(va0, pb0, acc[t]);
-        acc[t] = mfma32x32x16(va1, pb1, acc[t]);
-      }
-    }
-    if (more) {
-      pf_store_tile<D>(st, pf_lds + ((kt + 1) & 1) * PfLds<D>::STAGE, tid);
-    }
+  while (base_t < n_tiles) {
+    tab = load_tab(base_t);
+    const int win_end = min(n_tiles, base_t + 64);
+    // stage the window's first tile
+    pf_load_tile<D>(st, a, kbase, vbase, tile_page(base_t), base_t * kPfBN, L, tid);
+    pf_store_tile<D>(st, pf_lds + (base_t & 1) * PfLds<D>::STAGE, tid);
     __syncthreads();
+
+    for (int kt = base_t; kt < win_end; ++kt) {
+      const uint16_t* cur = pf_lds + (kt & 1) * PfLds<D>::STAGE;
+      // next tile's loads in flight during this tile's math (clamped to the window:
+      // the window's last iteration stages a repeat that nobody reads)
+      const int nt = min(kt + 1, win_end - 1);
+      pf_load_tile<D>(st, a, kbase, vbase, tile_page(nt), nt * kPfBN, L, tid);
+
+#pragma unroll
+      for (int kb = 0; kb < kPfBN / 32; ++kb) {
+        const int kb0 = kt * kPfBN + kb * 32;
+        const bool skip = kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len;
+        if (skip) continue;
+        // S^T = K Q^T
+        f32x16 s;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        const uint16_t* kl = cur + (kb * 32 + col) * PfLds<D>::KROW + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + 16 * kk);
+          s = mfma32x32x16(ka, qb[kk], s);
+        }
+        // scale to log2 units; mask keys past the end and (causal) above the diagonal
+        const bool need_mask = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] *= a.scale_log2;
+        if (need_mask) {
+          const int lim = a.causal ? min(L - 1, my_pos) : L - 1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kb0 + 8 * j + 4 * hh + i;
+              if (key > lim) s[4 * j + i] = kNegInf;
+            }
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[e] = exp2f(s[e] - m_use);
+          psum += s[e];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+        const u32x4 pb0 = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
+                           pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
+        const u32x4 pb1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
+                           pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
+        // O^T += V^T P^T
+        const uint16_t* vl = cur + PfLds<D>::K_ELEMS + col * PfLds<D>::VROW + kb * 32 + 8 * hh;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const uint16_t* vrow = vl + 32 * t * PfLds<D>::VROW;
+          const u32x4 va0 = *reinterpret_cast<const u32x4*>(vrow);
+          const u32x4 va1 = *reinterpret_cast<const u32x4*>(vrow + 16);
+          acc[t] = mfma32x32x16(va0, pb0, acc[t]);
+          acc[t] = mfma32x32x16(va1, pb1, acc[t]);
+        }
+      }
+      pf_store_tile<D>(st, pf_lds + ((kt + 1) & 1) * PfLds<D>::STAGE, tid);
+      __syncthreads();
+    }
+    base_t = win_end;
   }
 
   if (!row_ok) return;

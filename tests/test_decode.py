@@ -185,3 +185,93 @@ def test_long_context_decode_full_size_sampled(require_gpu):
     assert_parity(got, o_ref, "long_decode sampled")
     assert_lse(np.array([float(lse[b, h]) for b, h in rows]), l_ref, "long lse")
     assert torch.isfinite(out.float()).all()
+
+
+def test_workspace_is_scratch_and_reusable(require_gpu):
+    """A workspace full of garbage, reused across calls with different split counts and
+    batch shapes, gives the oracle's result every time."""
+    cases = [make_case("ws", seq_lens=lens, Hq=28, Hkv=4, D=128, page_size=16, seed=40 + i,
+                       device="cuda")
+             for i, lens in enumerate([[3000, 17, 999, 4096], [8192] * 3, [77]])]
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device="cuda")   # garbage
+    refs = [oracle_full(c)[0] for c in cases]
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            for S in (2, 5, 16):
+                out = pa.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                           c.seq_lens_k, c.scale, max_seq_len=c.max_seq_len,
+                                           num_splits=S, workspace=ws)
+                torch.cuda.synchronize()
+                assert_parity(as_f64(out), refs[i], f"case {i} S={S} rep {rep}")
+
+
+def test_graph_replays_match_eager(require_gpu):
+    """A captured split-K decode (partition + merge launches) replayed several times,
+    with eager work and synchronisations between replays, matches the eager result on
+    every replay."""
+    case = make_case("g", seq_lens=[5000, 3000, 8192, 100], Hq=28, Hkv=4, D=128, page_size=16,
+                     seed=50, device="cuda")
+    S = 4
+    need = pa.decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, 8192, S)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, case.Hq, case.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device="cuda")
+    args = (case.q, case.k_pool, case.v_pool, case.block_tables, case.seq_lens_k, case.scale)
+    pa.paged_attn_decode(*args, max_seq_len=8192, num_splits=S, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = bits(out).copy(), lse.cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pa.paged_attn_decode(*args, max_seq_len=8192, num_splits=S, out=out, lse=lse,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), ref_o), rep
+        assert np.array_equal(lse.cpu().numpy(), ref_l), rep
+        # eager work with the same workspace between replays
+        pa.paged_attn_decode(*args, max_seq_len=8192, num_splits=3, workspace=ws)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("lens,S", [([3000, 17, 999, 4096], 4), ([100, 0, 64], 3), ([8192], 1)])
+def test_partials_match_oracle_chunks_and_merge_to_decode(require_gpu, lens, S):
+    """decode_partials gives each partition's own attention and lse (the oracle's
+    per-chunk partials over the same boundaries), and reducing them reproduces
+    paged_attn_decode bit for bit."""
+    case = make_case("parts", seq_lens=lens, Hq=28, Hkv=4, D=128, page_size=16, seed=60 + S,
+                     device="cuda")
+    max_len = max(lens)
+    po, pl = pa.paged_attn_decode_partials(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                           case.seq_lens_k, case.scale, num_splits=S,
+                                           max_seq_len=max_len)
+    torch.cuda.synchronize()
+    chunks = -(-max_len // 32)
+    part_len = -(-chunks // S) * 32
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    bt = case.block_tables.cpu().numpy()
+    q = oracle.bf16_bits_to_f64(bits(case.q))
+    got_o, got_l = po.cpu().numpy(), pl.cpu().numpy()
+    for b, L in enumerate(lens):
+        k = oracle.gather_sequence_kv(kp, bt[b], L, 16)
+        v = oracle.gather_sequence_kv(vp, bt[b], L, 16)
+        bounds = [min(c * part_len, L) for c in range(S)] + [L]
+        for h in range(28):
+            oc, lc = oracle.split_partials_ref(q[b, h], k[:, h // 7], v[:, h // 7], case.scale,
+                                               L, bounds)
+            r = b * 28 + h
+            assert_parity(got_o[r], oc, f"partials b={b} h={h}", max_abs=2e-3, mean_abs=2e-4)
+            assert_lse(got_l[r], lc, f"partial lse b={b} h={h}")
+    out_r, lse_r = pa.paged_attn_splitk_reduce(po, pl)
+    out_d, lse_d = pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                        case.seq_lens_k, case.scale, max_seq_len=max_len,
+                                        num_splits=S, return_lse=True)
+    torch.cuda.synchronize()
+    if S > 1:
+        assert np.array_equal(bits(out_r.view(case.B, 28, 128)), bits(out_d))
+        assert np.array_equal(lse_r.view(case.B, 28).cpu().numpy(), lse_d.cpu().numpy())

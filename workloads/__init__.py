@@ -65,6 +65,7 @@ class PagedCase:
     start_pos: Optional[torch.Tensor] = None
     num_splits: int = 0
     meta: dict = field(default_factory=dict)
+    host_seq_lens: Optional[List[int]] = None     # keys attended, kept on the host
 
     @property
     def B(self) -> int:
@@ -84,8 +85,9 @@ class PagedCase:
 
     @property
     def seq_lens(self) -> List[int]:
-        return [h + n for h, n in zip(self.hist_lens, self.q_lens)] if self.k_new is not None \
-            else [int(x) for x in self.seq_lens_k.cpu().tolist()]
+        if self.host_seq_lens is not None:
+            return list(self.host_seq_lens)
+        return [int(x) for x in self.seq_lens_k.cpu().tolist()]
 
     @property
     def max_seq_len(self) -> int:
@@ -214,7 +216,7 @@ def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=No
         cu_seqlens_q=torch.as_tensor(cu_q, device=device),
         hist_lens=hist, q_lens=ql, k_new=k_new, v_new=v_new, cu_new=cu_new,
         start_pos=start_pos, num_splits=num_splits,
-        meta=dict(seed=seed, std_q=std_q, std_kv=std_kv),
+        meta=dict(seed=seed, std_q=std_q, std_kv=std_kv), host_seq_lens=list(total),
     )
 
 
