@@ -23,6 +23,7 @@
  *   - All tensors are dense and row-major in the order written; data pointers must
  *     be 16-byte aligned.
  *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - softmax_scale must be positive and finite (PA_ERR_SHAPE otherwise).
  *   - lse outputs are natural-log log-sum-exps of the scaled visible scores.
  *   - A query row that sees no key (sequence length 0, or an empty causal window)
  *     yields O = 0 and lse = -inf, never NaN.

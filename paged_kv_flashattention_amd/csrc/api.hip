@@ -96,7 +96,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
       return fail(PA_ERR_MISALIGNED, "%s: data pointers must be 16-byte aligned", what);
   }
-  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "%s: softmax scale is NaN", what);
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
+    return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
   const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
   const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   a = pa::DecodeArgs{};
@@ -309,7 +310,8 @@ int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const vo
     return fail(PA_ERR_NULL, "prefill: a required pointer is NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PA_ERR_MISALIGNED, "prefill: data pointers must be 16-byte aligned");
-  if (!(softmax_scale == softmax_scale)) return fail(PA_ERR_SHAPE, "prefill: softmax scale is NaN");
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
+    return fail(PA_ERR_SHAPE, "prefill: softmax scale must be positive and finite");
   if (max_q_len > Tq) max_q_len = Tq;
   pa::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);

@@ -265,12 +265,12 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       mt = wave_max_xor16_32(mt);
       const float m_new = fmaxf(m_run, mt);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       float p[8];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = exp2f(s[j] - m_use);
+        p[j] = __builtin_amdgcn_exp2f(s[j] - m_use);
         psum += p[j];
       }
       l_run = l_run * alpha + psum;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     for (int t = 0; t < DPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float e = exp2f(sm_m[w][n] - M_use);
+      const float e = __builtin_amdgcn_exp2f(sm_m[w][n] - M_use);
       Lsum += e * sm_l[w][n];
 #pragma unroll
       for (int t = 0; t < DPL; ++t)

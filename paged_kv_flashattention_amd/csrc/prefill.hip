@@ -31,102 +31,97 @@ constexpr int kPfWaves = 4;
 constexpr int kPfBM = 32 * kPfWaves;   // query rows per work-group
 constexpr int kPfBN = 64;              // keys per LDS tile
 constexpr int kPfThreads = 64 * kPfWaves;
+constexpr float kRescaleSlack = 8.f;   // log2 headroom before the reference moves
 
+// LDS tile: K and V rows of 64 keys, row-major [key][D] with no padding; the
+// 16-byte chunks of row r are stored permuted (chunk c at c ^ chunk_swz(r)) so
+// that both the K operand reads (16 consecutive rows, one chunk) and the
+// transposing V reads (4 consecutive rows, two chunks) hit distinct LDS banks.
 template <int D>
 struct PfLds {
-  static constexpr int KROW = D + 8;          // bf16 per K row (16 B pad)
-  static constexpr int VROW = kPfBN + 8;      // bf16 per V^T row (16 B pad)
-  static constexpr int K_ELEMS = kPfBN * KROW;
-  static constexpr int V_ELEMS = D * VROW;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);
+  static constexpr int TILE = kPfBN * D;          // bf16 elements of K (or V) per tile
+  static constexpr int STAGE = 2 * TILE;          // K then V
+  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);   // two stages
 };
 
-// Position of key offset o (0..63) of a tile among the V^T columns.
-__device__ __forceinline__ int vt_col(int o) {
-  const int grp = (o >> 2) & 3;
-  const int swapped = grp == 1 ? 2 : (grp == 2 ? 1 : grp);
-  return (o & ~15) | (swapped << 2) | (o & 3);
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  return (r >> 1) & 7;
 }
 
-template <int D>
-struct PfStage {
-  u32x4 k[D / 32];                 // K: one key row, D/4 values
-  uint32_t v[4][D / 32];           // V: 4 key rows x D/16 values
-};
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// lds_wave_base + 16 i (gfx950 global_load_lds_dwordx4).  Completion is tracked by
+// the vector-memory counter only, so waits are explicit (vmcnt_wait).
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)gsrc,
+      (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
 
-// Global loads of one 64-key tile for this thread.  Wave w stages keys
-// k0 + 16 w .. k0 + 16 w + 15, which share one page (`page`, wave-uniform); the
-// loads are unconditional (page and slot are always inside the pool) and rows past
-// the sequence end are zeroed afterwards.
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier that the compiler may not move memory operations across
+// (the hardware barrier alone; the waits it needs are issued explicitly).
+__device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
+
+// Transposing 8-byte LDS read: within each 16-lane group, lane j receives element
+// (j % 4) of the 8-byte rows that lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4 point at.
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// DMA loads of one 64-key tile into one LDS stage.  Wave w fills rows 16 w ..
+// 16 w + 15 of K and of V (keys k0 + 16 w .., all in one page `page`); each load
+// instruction covers RPI = 512 / D rows, lane i fetching the global chunk that
+// belongs at LDS position i of the permuted layout.
 template <int D>
-__device__ __forceinline__ void pf_load_tile(PfStage<D>& st, const PrefillArgs& a,
-                                             const uint16_t* kbase, const uint16_t* vbase,
-                                             int page, int k0, int L, int tid) {
+__device__ __forceinline__ void pf_issue_tile(uint16_t* stage, const PrefillArgs& a,
+                                              const uint16_t* kbase, const uint16_t* vbase,
+                                              int page, int k0, int wave, int lane) {
+  constexpr int LPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPI = 64 / LPR;            // rows per instruction
   const int psm = a.page_size - 1;
   const int rs = a.Hkv * D;
   const size_t page_off = (size_t)page * a.page_size * rs;
-  // K: thread -> key tid/4, d range [(tid%4) * D/4, +D/4)
-  {
-    const int key = k0 + (tid >> 2);
-    const uint16_t* p = kbase + page_off + (key & psm) * rs + (tid & 3) * (D / 4);
-    const bool ok = key < L;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const u32x4 x = ld16(p + 8 * c);
-      st.k[c] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // V: thread -> keys 4 (tid/16) .. +3, d range [(tid%16) * D/16, +D/16)
-  {
-    const int key0 = k0 + 4 * (tid >> 4);
-    const uint16_t* p = vbase + page_off + (key0 & psm) * rs + (tid & 15) * (D / 16);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = key0 + r < L;
-      if constexpr (D == 128) {
-        const u32x4 x = ld16(p + r * rs);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) st.v[r][w] = ok ? x[w] : 0u;
-      } else {
-        const u32x2 x = ld8(p + r * rs);
-#pragma unroll
-        for (int w = 0; w < 2; ++w) st.v[r][w] = ok ? x[w] : 0u;
-      }
-    }
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int r = 16 * wave + RPI * i + lane / LPR;          // tile row = key - k0
+    const int c = (lane % LPR) ^ chunk_swz<D>(r);            // global chunk for this slot
+    const size_t src = page_off + (size_t)((k0 + r) & psm) * rs + c * 8;
+    uint16_t* dst = stage + (16 * wave + RPI * i) * D;       // wave-uniform
+    dma16(kbase + src, dst);
+    dma16(vbase + src, dst + PfLds<D>::TILE);
   }
 }
 
+// Zero this wave's V rows at or past the sequence end (the last tile only): they
+// hold other data, and P = 0 times NaN would not be 0.
 template <int D>
-__device__ __forceinline__ void pf_store_tile(const PfStage<D>& st, uint16_t* lds, int tid) {
-  uint16_t* kl = lds;
-  uint16_t* vl = lds + PfLds<D>::K_ELEMS;
-  {
-    uint16_t* p = kl + (tid >> 2) * PfLds<D>::KROW + (tid & 3) * (D / 4);
+__device__ __forceinline__ void pf_zero_tail(uint16_t* stage, int k0, int L, int wave, int lane) {
+  constexpr int LPR = D / 8;
+  constexpr int RPI = 64 / LPR;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) *reinterpret_cast<u32x4*>(p + 8 * c) = st.k[c];
-  }
-  {
-    // 4 keys x D/16 d values -> for each d, 4 keys (8 bytes) at the key group's column
-    const int col = vt_col(4 * (tid >> 4));
-    const int d0 = (tid & 15) * (D / 16);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const int w = t >> 1;
-      u32x2 pr;
-      if ((t & 1) == 0) {
-        pr = u32x2{pack_lo_halves(st.v[0][w], st.v[1][w]), pack_lo_halves(st.v[2][w], st.v[3][w])};
-      } else {
-        pr = u32x2{pack_hi_halves(st.v[0][w], st.v[1][w]), pack_hi_halves(st.v[2][w], st.v[3][w])};
-      }
-      *reinterpret_cast<u32x2*>(vl + (d0 + t) * PfLds<D>::VROW + col) = pr;
-    }
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int r = 16 * wave + RPI * i + lane / LPR;
+    if (k0 + r >= L)
+      *reinterpret_cast<u32x4*>(stage + PfLds<D>::TILE + r * D + (lane % LPR) * 8) =
+          u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
+  constexpr int NDMA = 2 * (16 * D / 512);  // DMA instructions per wave per tile
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,42 +189,58 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     return (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
   };
 
-  PfStage<D> st;
   while (base_t < n_tiles) {
     tab = load_tab(base_t);
     const int win_end = min(n_tiles, base_t + 64);
-    // stage the window's first tile
-    pf_load_tile<D>(st, a, kbase, vbase, tile_page(base_t), base_t * kPfBN, L, tid);
-    pf_store_tile<D>(st, pf_lds + (base_t & 1) * PfLds<D>::STAGE, tid);
-    __syncthreads();
+    // every wave has finished reading both stages before they are refilled
+    block_sync();
+    pf_issue_tile<D>(pf_lds + (base_t & 1) * PfLds<D>::STAGE, a, kbase, vbase,
+                     tile_page(base_t), base_t * kPfBN, wave, lane);
 
     for (int kt = base_t; kt < win_end; ++kt) {
-      const uint16_t* cur = pf_lds + (kt & 1) * PfLds<D>::STAGE;
-      // next tile's loads in flight during this tile's math (clamped to the window:
+      uint16_t* cur = pf_lds + (kt & 1) * PfLds<D>::STAGE;
+      // next tile's DMA in flight during this tile's math (clamped to the window:
       // the window's last iteration stages a repeat that nobody reads)
       const int nt = min(kt + 1, win_end - 1);
-      pf_load_tile<D>(st, a, kbase, vbase, tile_page(nt), nt * kPfBN, L, tid);
+      pf_issue_tile<D>(pf_lds + ((kt + 1) & 1) * PfLds<D>::STAGE, a, kbase, vbase,
+                       tile_page(nt), nt * kPfBN, wave, lane);
+      vmcnt_wait<NDMA>();                 // this wave's loads of tile kt have landed
+      if (kt * kPfBN + kPfBN > L) {
+        pf_zero_tail<D>(cur, kt * kPfBN, L, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in LDS
+      }
+      block_sync();                        // ... and every other wave's
 
+      // scores of both 32-key blocks first, so that the softmax of the first block
+      // overlaps the matrix cores working on the second
+      f32x16 sblk[kPfBN / 32];
+      bool act[kPfBN / 32];
 #pragma unroll
       for (int kb = 0; kb < kPfBN / 32; ++kb) {
         const int kb0 = kt * kPfBN + kb * 32;
-        const bool skip = kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len;
-        if (skip) continue;
-        // S^T = K Q^T
-        f32x16 s;
+        act[kb] = !(kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
-        const uint16_t* kl = cur + (kb * 32 + col) * PfLds<D>::KROW + 8 * hh;
+        for (int e = 0; e < 16; ++e) sblk[kb][e] = 0.f;
+        if (!act[kb]) continue;
+        const int row = kb * 32 + col;
+        const uint16_t* kl = cur + row * D;
+        const int sw = chunk_swz<D>(row);
+        u32x4 ka[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + 16 * kk);
-          s = mfma32x32x16(ka, qb[kk], s);
-        }
-        // scale to log2 units; mask keys past the end and (causal) above the diagonal
+        for (int kk = 0; kk < D / 16; ++kk)
+          ka[kk] = *reinterpret_cast<const u32x4*>(kl + (((2 * kk + hh) ^ sw) << 3));
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) sblk[kb] = mfma32x32x16(ka[kk], qb[kk], sblk[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kPfBN / 32; ++kb) {
+        if (!act[kb]) continue;
+        const int kb0 = kt * kPfBN + kb * 32;
+        f32x16& s = sblk[kb];
+        // Keys past the end and (causal) above the diagonal get -inf; only blocks
+        // that touch the boundary need it.
         const bool need_mask = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] *= a.scale_log2;
-        if (need_mask) {
+        if (__builtin_expect(need_mask, 0)) {
           const int lim = a.causal ? min(L - 1, my_pos) : L - 1;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -239,41 +250,67 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
               if (key > lim) s[4 * j + i] = kNegInf;
             }
         }
-        float mt = s[0];
+        // Online softmax in log2 units with a lazily moved reference: the running
+        // reference m_ref only moves (rescaling l and the accumulator) when a row's
+        // scaled maximum exceeds it by more than kRescaleSlack, so P stays below
+        // 2^kRescaleSlack and the result is unchanged -- the final normalisation
+        // uses the same reference ("The Stack Below the Stack (Part 2)", 2.1 and 2.3).
+        float mt = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, s[e]), s[e + 1]);
+        mt = fmaxf(mt, s[15]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.scale_log2;
+        const bool grow = mt > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mt : m_run;
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+          m_run = m_new;
+        }
+        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          s[e] = exp2f(s[e] - m_use);
+          s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.scale_log2, neg_m));
           psum += s[e];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+        l_run += psum;
+        // P^T operand halves: keys 16u + 4 hh + (0..3) and 16u + 8 + 4 hh + (0..3)
         const u32x4 pb0 = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
                            pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
         const u32x4 pb1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
                            pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
-        // O^T += V^T P^T
-        const uint16_t* vl = cur + PfLds<D>::K_ELEMS + col * PfLds<D>::VROW + kb * 32 + 8 * hh;
+        // O^T += V^T P^T; the V^T operand (8 keys of one d per lane) comes from two
+        // transposing reads of row-major V: in each 16-lane group, lane i points at
+        // key row key0 + i/4, columns d0 + 4 (i % 4) .. + 3.
+        const int g16 = lane & 15;
+        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const uint16_t* vrow = vl + 32 * t * PfLds<D>::VROW;
-          const u32x4 va0 = *reinterpret_cast<const u32x4*>(vrow);
-          const u32x4 va1 = *reinterpret_cast<const u32x4*>(vrow + 16);
-          acc[t] = mfma32x32x16(va0, pb0, acc[t]);
-          acc[t] = mfma32x32x16(va1, pb1, acc[t]);
+          const int dd = 32 * t + dsub;                      // first d of this lane's row piece
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            u32x2 lo, hi;
+            {
+              const int row = kb * 32 + 16 * u + 4 * hh + (g16 >> 2);
+              lo = ds_read_tr16(cur + PfLds<D>::TILE + row * D +
+                                ((((dd >> 3) ^ chunk_swz<D>(row))) << 3) + (dd & 7));
+            }
+            {
+              const int row = kb * 32 + 16 * u + 8 + 4 * hh + (g16 >> 2);
+              hi = ds_read_tr16(cur + PfLds<D>::TILE + row * D +
+                                ((((dd >> 3) ^ chunk_swz<D>(row))) << 3) + (dd & 7));
+            }
+            const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+            acc[t] = mfma32x32x16(va, u == 0 ? pb0 : pb1, acc[t]);
+          }
         }
       }
-      pf_store_tile<D>(st, pf_lds + ((kt + 1) & 1) * PfLds<D>::STAGE, tid);
-      __syncthreads();
+      block_sync();                        // stage kt is free for tile kt + 2
     }
+    vmcnt_wait<0>();                       // no DMA outstanding into a reused stage
     base_t = win_end;
   }
 
@@ -317,8 +354,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
     e = launch_prefill_t<64>(a, stream, n_qt);
   }
   snprintf(desc, desc_len,
-           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16> grid=(%d,%d,%d) block=%d lds=%zu", a.D,
-           kPfBM, kPfBN, a.Hq, a.B, n_qt, kPfThreads,
+           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=(%d,%d,%d) block=%d lds=%zu",
+           a.D, kPfBM, kPfBN, a.Hq, a.B, n_qt, kPfThreads,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;
 }

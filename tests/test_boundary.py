@@ -77,6 +77,9 @@ def decode_call(lib, **over):
     (dict(S=4, ws=None), 5),
     (dict(S=4, ws=FAKE, ws_bytes=16), 5),
     (dict(scale=float("nan")), 2),
+    (dict(scale=0.0), 2),
+    (dict(scale=-0.1), 2),
+    (dict(scale=float("inf")), 2),
 ])
 def test_decode_rejects_invalid_arguments(lib, over, status):
     assert decode_call(lib, **over) == status
