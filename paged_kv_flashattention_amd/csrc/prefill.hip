@@ -1,20 +1,18 @@
 // Ragged causal prefill over paged K/V on gfx950 matrix cores.
 //
 // Work-group = 4 waves = 128 consecutive query rows of one query head of one
-// sequence; each wave owns 32 rows.  Keys are walked in 64-key tiles gathered
-// through the block table into LDS (double buffered: the next tile's global
-// loads are in flight while the current tile is consumed).  Per 32-key block a
-// wave computes
+// sequence; each wave owns 32 rows.  Keys are walked in 64-key tiles that the
+// waves copy from the page pool straight into LDS (global_load_lds, through the
+// block table; double buffered, so the next tile is in flight while the current
+// one is consumed).  Per 32-key block a wave computes
 //   S^T[32 keys x 32 queries] = K Q^T           32x32x16 bf16 MFMA, fp32 accumulate
 //   running max / running sum per query         ("The Stack Below the Stack (Part 2)",
 //                                                 section 2.1, online softmax)
 //   O^T[D x 32 queries] += V^T P^T               P rounded to bf16
 // Keys sit on the MFMA's M side so that every per-query statistic lives in lane %
-// 32 and the S^T accumulator is already laid out as the P^T operand; V is stored
-// transposed in LDS (V^T[d][key], transposed in registers while staging) so the
-// V^T operand is one 16-byte LDS read.  Within each group of 16 keys the V^T
-// columns hold keys in the order 0-3, 8-11, 4-7, 12-15: the order in which the
-// S^T accumulator hands P^T its keys.
+// 32 and the S^T accumulator is already laid out as the P^T operand.  K and V are
+// both stored row-major; the V^T operand comes from transposing LDS reads
+// (ds_read_b64_tr_b16).
 //
 // Causal rows are the LAST q_len positions of their sequence (query row i at
 // absolute position seq_len - q_len + i sees keys j <= that position); key
@@ -34,9 +32,12 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom before the reference moves
 
 // LDS tile: K and V rows of 64 keys, row-major [key][D] with no padding; the
-// 16-byte chunks of row r are stored permuted (chunk c at c ^ chunk_swz(r)) so
-// that both the K operand reads (16 consecutive rows, one chunk) and the
-// transposing V reads (4 consecutive rows, two chunks) hit distinct LDS banks.
+// 16-byte chunks of row r are stored permuted (chunk c at c ^ chunk_swz(r)).  The
+// LDS serves 256 bytes (all 64 banks) per clock: a K operand read covers one chunk
+// of 16 consecutive rows per clock, a transposing V read four chunks of 4
+// consecutive rows per 32 lanes, and the permutation keeps both on distinct banks
+// (for D = 128 a row spans all banks, so rows r .. r + 3 must differ in the
+// permutation's upper two bits; for D = 64 two rows share a bank line).
 template <int D>
 struct PfLds {
   static constexpr int TILE = kPfBN * D;          // bf16 elements of K (or V) per tile
@@ -46,17 +47,22 @@ struct PfLds {
 
 template <int D>
 __device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  return (r >> 1) & 7;
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
-// lds_wave_base + 16 i (gfx950 global_load_lds_dwordx4).  Completion is tracked by
-// the vector-memory counter only, so waits are explicit (vmcnt_wait).
+// lds_wave_base + 16 i (gfx950 global_load_lds_dwordx4, LDS base in M0).  Written
+// as inline assembly so that the compiler, which cannot tell which LDS reads such
+// a load may feed, does not wait for every outstanding one before each LDS read;
+// completion is waited for explicitly (vmcnt_wait) before the barrier that
+// publishes a tile.
 __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(
-      (const __attribute__((address_space(1))) void*)gsrc,
-      (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "m0", "memory");
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -211,8 +217,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
       block_sync();                        // ... and every other wave's
 
-      // scores of both 32-key blocks first, so that the softmax of the first block
-      // overlaps the matrix cores working on the second
+      // Scores of both 32-key blocks, their two MFMA chains interleaved and each K
+      // fragment read one step ahead, so the softmax of the first block overlaps
+      // the matrix cores' work on the second.  A block wholly outside this wave's
+      // causal window is computed anyway and then ignored.
       f32x16 sblk[kPfBN / 32];
       bool act[kPfBN / 32];
 #pragma unroll
@@ -221,16 +229,33 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         act[kb] = !(kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len);
 #pragma unroll
         for (int e = 0; e < 16; ++e) sblk[kb][e] = 0.f;
-        if (!act[kb]) continue;
-        const int row = kb * 32 + col;
-        const uint16_t* kl = cur + row * D;
-        const int sw = chunk_swz<D>(row);
-        u32x4 ka[D / 16];
+      }
+      if (act[0] || act[1]) {
+        const uint16_t* kl0 = cur + col * D;
+        const uint16_t* kl1 = cur + (32 + col) * D;
+        const int sw0 = chunk_swz<D>(col), sw1 = chunk_swz<D>(32 + col);
+        auto kfrag = [&](const uint16_t* kl, int sw, int kk) {
+          return *reinterpret_cast<const u32x4*>(kl + (((2 * kk + hh) ^ sw) << 3));
+        };
+        u32x4 n0 = kfrag(kl0, sw0, 0), n1 = kfrag(kl1, sw1, 0);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          ka[kk] = *reinterpret_cast<const u32x4*>(kl + (((2 * kk + hh) ^ sw) << 3));
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const u32x4 f0 = n0, f1 = n1;
+          if (kk + 1 < D / 16) {
+            n0 = kfrag(kl0, sw0, kk + 1);
+            n1 = kfrag(kl1, sw1, kk + 1);
+          }
+          sblk[0] = mfma32x32x16(f0, qb[kk], sblk[0]);
+          sblk[1] = mfma32x32x16(f1, qb[kk], sblk[1]);
+        }
+        // Scheduling order: the fragment reads run two MFMA pairs ahead of their use.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 LDS reads
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) sblk[kb] = mfma32x32x16(ka[kk], qb[kk], sblk[kb]);
+        for (int i = 0; i < D / 16 - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
 #pragma unroll
       for (int kb = 0; kb < kPfBN / 32; ++kb) {
@@ -259,7 +284,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, s[e]), s[e + 1]);
         mt = fmaxf(mt, s[15]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.scale_log2;
+        mt = xor32_max(mt) * a.scale_log2;
         const bool grow = mt > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(grow)) {
           const float m_new = grow ? mt : m_run;
@@ -282,31 +307,35 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
                            pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
         const u32x4 pb1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
                            pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
-        // O^T += V^T P^T; the V^T operand (8 keys of one d per lane) comes from two
-        // transposing reads of row-major V: in each 16-lane group, lane i points at
-        // key row key0 + i/4, columns d0 + 4 (i % 4) .. + 3.
+        // The V^T operand (8 keys of one d per lane) comes from two transposing
+        // reads of row-major V: in each 16-lane group, lane i points at key row
+        // key0 + i/4, columns d0 + 4 (i % 4) .. + 3.
         const int g16 = lane & 15;
         const int dsub = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+        auto vfrag = [&](int t, int u) {
+          const int dd = 32 * t + dsub;                      // first d of this lane's piece
+          const int r0 = kb * 32 + 16 * u + 4 * hh + (g16 >> 2);
+          const int r1 = r0 + 8;
+          const u32x2 lo = ds_read_tr16(cur + PfLds<D>::TILE + r0 * D +
+                                        (((dd >> 3) ^ chunk_swz<D>(r0)) << 3) + (dd & 7));
+          const u32x2 hi = ds_read_tr16(cur + PfLds<D>::TILE + r1 * D +
+                                        (((dd >> 3) ^ chunk_swz<D>(r1)) << 3) + (dd & 7));
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        // O^T += V^T P^T over the block's two 16-key halves; the four d-tiles are
+        // independent accumulators, so each half issues four MFMAs back to back.
+        u32x4 vnext = vfrag(0, 0);
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const int dd = 32 * t + dsub;                      // first d of this lane's row piece
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            u32x2 lo, hi;
-            {
-              const int row = kb * 32 + 16 * u + 4 * hh + (g16 >> 2);
-              lo = ds_read_tr16(cur + PfLds<D>::TILE + row * D +
-                                ((((dd >> 3) ^ chunk_swz<D>(row))) << 3) + (dd & 7));
+          for (int t = 0; t < D / 32; ++t) {
+            const u32x4 va = vnext;
+            if (u * (D / 32) + t + 1 < 2 * (D / 32)) {
+              const int n = u * (D / 32) + t + 1;
+              vnext = vfrag(n % (D / 32), n / (D / 32));
             }
-            {
-              const int row = kb * 32 + 16 * u + 8 + 4 * hh + (g16 >> 2);
-              hi = ds_read_tr16(cur + PfLds<D>::TILE + row * D +
-                                ((((dd >> 3) ^ chunk_swz<D>(row))) << 3) + (dd & 7));
-            }
-            const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
             acc[t] = mfma32x32x16(va, u == 0 ? pb0 : pb1, acc[t]);
           }
-        }
       }
       block_sync();                        // stage kt is free for tile kt + 2
     }
@@ -315,7 +344,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   const bool live = l_tot > 0.f;
   const float inv = live ? 1.f / l_tot : 0.f;
   uint16_t* op = a.out + ((size_t)(t0 + my_row) * a.Hq + h) * D;
