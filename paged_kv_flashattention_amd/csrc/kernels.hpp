@@ -56,6 +56,8 @@ struct PrefillArgs {
   int max_pages, num_pages, page_size, ps_shift;
   int causal;
   float scale_log2;
+  int n_qt;                      // query tiles per sequence (of the longest)
+  int xcd_groups;                // (sequence, KV head) groups per XCD, or 0: plain order
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError() of the launch;

@@ -31,37 +31,41 @@ constexpr int kPfBN = 64;              // keys per LDS tile
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom before the reference moves
 
-// LDS tile: K and V rows of 64 keys, row-major [key][D] with no padding; the
-// 16-byte chunks of row r are stored permuted (chunk c at c ^ chunk_swz(r)).  The
-// LDS serves 256 bytes (all 64 banks) per clock: a K operand read covers one chunk
-// of 16 consecutive rows per clock, a transposing V read four chunks of 4
-// consecutive rows per 32 lanes, and the permutation keeps both on distinct banks
-// (for D = 128 a row spans all banks, so rows r .. r + 3 must differ in the
-// permutation's upper two bits; for D = 64 two rows share a bank line).
+// LDS tiles of 64 keys.  Each wave's 16 rows (keys 16 w .. 16 w + 15, one run of
+// one page) form a region of 16 x D bf16 stored chunk-major: the 16-byte chunk c
+// (columns 8 c .. 8 c + 7) of the region's rows sits in the 256-byte line c, one
+// slot per row.  The LDS serves 256 bytes (all 64 banks) per clock.
+//   K: row s of the region in slot s.  A K operand read (one chunk of 16
+//      consecutive rows per 16 lanes) covers one whole line.
+//   V: row s in slot (s + 4 c) mod 16 of line c.  A transposing V read (per 32
+//      lanes: 4 consecutive rows x 4 consecutive chunks, 8 bytes each) then hits
+//      16 distinct slots of 4 lines.
+// Both layouts make every operand address a fixed per-lane offset plus a
+// compile-time constant; the DMA (one 1024-byte run of 64 slots per instruction)
+// fetches, per lane, whichever global chunk belongs in its slot.
 template <int D>
 struct PfLds {
-  static constexpr int TILE = kPfBN * D;          // bf16 elements of K (or V) per tile
-  static constexpr int STAGE = 2 * TILE;          // K then V
-  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);   // two stages
+  static constexpr int TILE = kPfBN * D;          // bf16 elements of one K or V tile
+  static constexpr int REGION = 16 * D;           // one wave's 16 rows
+  static constexpr int K_STAGES = 2;              // K of tiles t and t + 1
+  static constexpr int V_STAGES = 3;              // V of tiles t - 1 .. t + 1
+  static constexpr int V0 = K_STAGES * TILE;      // first V stage
+  static constexpr size_t BYTES = (size_t)(K_STAGES + V_STAGES) * TILE * sizeof(uint16_t);
 };
 
-template <int D>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
-// lds_wave_base + 16 i (gfx950 global_load_lds_dwordx4, LDS base in M0).  Written
-// as inline assembly so that the compiler, which cannot tell which LDS reads such
-// a load may feed, does not wait for every outstanding one before each LDS read;
-// completion is waited for explicitly (vmcnt_wait) before the barrier that
-// publishes a tile.
-__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
+// 16 bytes per lane from global memory straight into LDS: lane i reads
+// sbase + voff_i (a wave-uniform base address in SGPRs plus a 32-bit per-lane byte
+// offset) and its bytes land at lds_wave_base + 16 i (gfx950
+// global_load_lds_dwordx4, LDS base in M0).  Written as inline assembly so that
+// the compiler, which cannot tell which LDS reads such a load may feed, does not
+// wait for every outstanding one before each LDS read; completion is waited for
+// explicitly (vmcnt_wait) before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff,
+                                      uint16_t* lds_wave_base) {
   const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gsrc), "s"(lds)
+               : "v"(voff), "s"(sbase), "s"(lds)
                : "m0", "memory");
 }
 
@@ -76,6 +80,26 @@ __device__ __forceinline__ void vmcnt_wait() {
 // (the hardware barrier alone; the waits it needs are issued explicitly).
 __device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
 
+// max(a, b, c) in one instruction.  The scores compared here come from MFMA
+// accumulators and cannot be signalling NaNs, so the quieting that fmaxf needs
+// before each comparison is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Keeps a value computed where it is written: later passes may not sink its
+// computation past this point (used to hold vector work between MFMAs).
+__device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+
+// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+
 // Transposing 8-byte LDS read: within each 16-lane group, lane j receives element
 // (j % 4) of the 8-byte rows that lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4 point at.
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
@@ -85,41 +109,37 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// DMA loads of one 64-key tile into one LDS stage.  Wave w fills rows 16 w ..
-// 16 w + 15 of K and of V (keys k0 + 16 w .., all in one page `page`); each load
-// instruction covers RPI = 512 / D rows, lane i fetching the global chunk that
-// belongs at LDS position i of the permuted layout.
+// DMA loads of one 64-key tile into LDS (K into kst, V into vst).  Wave w fills
+// its region (keys k0 + 16 w .., all in one page, which starts its 16-row run at
+// in-page row (16 w) & (page_size - 1) since tiles start on page boundaries) with
+// D / 32 load instructions per matrix.  The per-lane byte offsets koff / voff
+// (row and chunk within the run of the slot the lane fills) are fixed for the
+// whole kernel, so a tile costs only scalar address arithmetic.
 template <int D>
-__device__ __forceinline__ void pf_issue_tile(uint16_t* stage, const PrefillArgs& a,
+__device__ __forceinline__ void pf_issue_tile(uint16_t* kst, uint16_t* vst,
                                               const uint16_t* kbase, const uint16_t* vbase,
-                                              int page, int k0, int wave, int lane) {
-  constexpr int LPR = D / 8;               // 16-byte chunks per row
-  constexpr int RPI = 64 / LPR;            // rows per instruction
-  const int psm = a.page_size - 1;
-  const int rs = a.Hkv * D;
-  const size_t page_off = (size_t)page * a.page_size * rs;
+                                              size_t page_row0, int rs, const uint32_t* koff,
+                                              const uint32_t* voff, int wave) {
+  const size_t base = page_row0 * rs;
 #pragma unroll
-  for (int i = 0; i < 16 / RPI; ++i) {
-    const int r = 16 * wave + RPI * i + lane / LPR;          // tile row = key - k0
-    const int c = (lane % LPR) ^ chunk_swz<D>(r);            // global chunk for this slot
-    const size_t src = page_off + (size_t)((k0 + r) & psm) * rs + c * 8;
-    uint16_t* dst = stage + (16 * wave + RPI * i) * D;       // wave-uniform
-    dma16(kbase + src, dst);
-    dma16(vbase + src, dst + PfLds<D>::TILE);
+  for (int j = 0; j < D / 32; ++j) {
+    const int slot0 = wave * PfLds<D>::REGION + 512 * j;      // wave-uniform
+    dma16(kbase + base, koff[j], kst + slot0);
+    dma16(vbase + base, voff[j], vst + slot0);
   }
 }
 
 // Zero this wave's V rows at or past the sequence end (the last tile only): they
-// hold other data, and P = 0 times NaN would not be 0.
+// hold other data, and P = 0 times NaN would not be 0.  Lane i of pass j owns
+// slot 64 j + i of the region, as in the DMA.
 template <int D>
-__device__ __forceinline__ void pf_zero_tail(uint16_t* stage, int k0, int L, int wave, int lane) {
-  constexpr int LPR = D / 8;
-  constexpr int RPI = 64 / LPR;
+__device__ __forceinline__ void pf_zero_tail(uint16_t* vst, int k0, int L, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 16 / RPI; ++i) {
-    const int r = 16 * wave + RPI * i + lane / LPR;
-    if (k0 + r >= L)
-      *reinterpret_cast<u32x4*>(stage + PfLds<D>::TILE + r * D + (lane % LPR) * 8) =
+  for (int j = 0; j < D / 32; ++j) {
+    const int c = 4 * j + (lane >> 4);
+    const int row = ((lane & 15) - 4 * c) & 15;
+    if (k0 + 16 * wave + row >= L)
+      *reinterpret_cast<u32x4*>(vst + wave * PfLds<D>::REGION + 512 * j + 8 * lane) =
           u32x4{0u, 0u, 0u, 0u};
   }
 }
@@ -127,15 +147,37 @@ __device__ __forceinline__ void pf_zero_tail(uint16_t* stage, int k0, int L, int
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
-  constexpr int NDMA = 2 * (16 * D / 512);  // DMA instructions per wave per tile
+  using L_ = PfLds<D>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;         // query column of S^T / O^T
   const int hh = lane >> 5;          // k-half of the MFMA operands
-  const int h = blockIdx.x;          // query head
-  const int b = blockIdx.y;
-  const int qt = gridDim.z - 1 - blockIdx.z;   // heaviest tiles first
+  const int g16 = lane & 15;
+  // Work-group -> (query head h, sequence b, query tile qt).  Work-groups are
+  // handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2; with
+  // xcd_groups set, every (sequence, KV head) group lives on one XCD, so its K/V
+  // tiles are fetched into one L2 and shared there by the group's query heads and
+  // tiles.  Either way the heaviest query tiles (most keys) start first.
+  int h, b, qt;
+  {
+    const int p = blockIdx.x;
+    if (a.xcd_groups) {
+      const int k = p >> 3;
+      const int level = a.xcd_groups * a.G;      // work-groups per query-tile level
+      const int rank = k / level;
+      const int rem = k - rank * level;
+      const int g = (p & 7) + 8 * (rem / a.G);
+      b = g / a.Hkv;
+      h = (g - b * a.Hkv) * a.G + rem % a.G;
+      qt = a.n_qt - 1 - rank;
+    } else {
+      h = p % a.Hq;
+      const int r = p / a.Hq;
+      b = r % a.B;
+      qt = a.n_qt - 1 - r / a.B;
+    }
+  }
 
   const int t0 = a.cu_seqlens_q[b];
   const int q_len = a.cu_seqlens_q[b + 1] - t0;
@@ -160,8 +202,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int my_row = r_w + col;
   const bool row_ok = my_row < q_len && t0 + my_row < a.Tq;
   const int my_pos = shift + my_row;          // causal: keys <= my_pos are visible
-  const int w_pos_max = shift + min(r_w + 31, q_len - 1);
   const int w_pos_min = shift + r_w;
+  const int lim = a.causal ? min(L - 1, my_pos) : L - 1;   // last visible key
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
   u32x4 qb[D / 16];
@@ -169,6 +211,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     const uint16_t* qp = a.q + ((size_t)(t0 + (row_ok ? my_row : 0)) * a.Hq + h) * D + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qb[kk] = row_ok ? ld16(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Fixed per-lane LDS offsets (elements within a tile).  K operand of step kk
+  // of block kb: row 32 kb + col, chunk 2 kk + hh, at k_lane + 32 kb D + 256 kk.
+  // V^T operand of d-tile t, 16-key half u of block kb: two transposing reads,
+  // rows 8 j + 4 hh + g16 / 4 of region 2 kb + u, columns 32 t + dsub .., at
+  // v_lane[j] + (2 kb + u) 16 D + 512 t.
+  const uint32_t k_lane = (col >> 4) * PfLds<D>::REGION + hh * 128 + (col & 15) * 8;
+  uint32_t v_lane[2];
+  {
+    const int e = 2 * ((lane >> 4) & 1) + ((g16 & 3) >> 1);   // chunk within 4
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      v_lane[j] = e * 128 + (((8 * j + 4 * hh + (g16 >> 2) + 4 * e) & 15) << 3) + 4 * (g16 & 1);
   }
 
   float m_run = kNegInf;
@@ -180,8 +236,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
   // Block-table window: lane j holds the page of this wave's 16 keys of tile
-  // base_t + j, so the 64 tiles of a window need no further table reads; the
-  // tile loop runs one window at a time.
+  // base_t + j; it is reloaded every 64 tiles.
   const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
   int base_t = 0;
   int tab = 0;
@@ -190,157 +245,223 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     idx = idx < a.max_pages ? idx : a.max_pages - 1;
     return bt[idx];
   };
-  auto tile_page = [&](int kt) {
-    const int pg = __builtin_amdgcn_readlane(tab, kt - base_t);
-    return (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+  const int run0 = (16 * wave) & (a.page_size - 1);
+  const int rs = a.Hkv * D;
+  // the global chunk each lane's DMA slot receives: slot 64 j + lane = line c,
+  // slot s; K holds row s there, V row (s - 4 c) mod 16
+  uint32_t k_dma[D / 32], v_dma[D / 32];
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int c = 4 * j + (lane >> 4), sl = lane & 15;
+    k_dma[j] = (uint32_t)(sl * rs + c * 8) * 2u;
+    v_dma[j] = (uint32_t)((((sl - 4 * c) & 15) * rs) + c * 8) * 2u;
+  }
+  auto kst = [&](int kt) { return pf_lds + (kt & 1) * L_::TILE; };
+  auto vst = [&](int vs) { return pf_lds + L_::V0 + vs * L_::TILE; };
+  // DMA of tile n (tiles are issued in increasing order) into V stage vs
+  auto issue = [&](int n, int vs) {
+    if (n - base_t >= 64) {
+      base_t += 64;
+      tab = load_tab(base_t);
+    }
+    int pg = __builtin_amdgcn_readlane(tab, n - base_t);
+    pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+    pf_issue_tile<D>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
+                     k_dma, v_dma, wave);
+  };
+  // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
+  auto publish = [&](int n, int vs) {
+    vmcnt_wait<0>();
+    if (n * kPfBN + kPfBN > L) {
+      pf_zero_tail<D>(vst(vs), n * kPfBN, L, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in LDS
+    }
+    block_sync();
   };
 
-  while (base_t < n_tiles) {
-    tab = load_tab(base_t);
-    const int win_end = min(n_tiles, base_t + 64);
-    // every wave has finished reading both stages before they are refilled
-    block_sync();
-    pf_issue_tile<D>(pf_lds + (base_t & 1) * PfLds<D>::STAGE, a, kbase, vbase,
-                     tile_page(base_t), base_t * kPfBN, wave, lane);
-
-    for (int kt = base_t; kt < win_end; ++kt) {
-      uint16_t* cur = pf_lds + (kt & 1) * PfLds<D>::STAGE;
-      // next tile's DMA in flight during this tile's math (clamped to the window:
-      // the window's last iteration stages a repeat that nobody reads)
-      const int nt = min(kt + 1, win_end - 1);
-      pf_issue_tile<D>(pf_lds + ((kt + 1) & 1) * PfLds<D>::STAGE, a, kbase, vbase,
-                       tile_page(nt), nt * kPfBN, wave, lane);
-      vmcnt_wait<NDMA>();                 // this wave's loads of tile kt have landed
-      if (kt * kPfBN + kPfBN > L) {
-        pf_zero_tail<D>(cur, kt * kPfBN, L, wave, lane);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in LDS
-      }
-      block_sync();                        // ... and every other wave's
-
-      // Scores of both 32-key blocks, their two MFMA chains interleaved and each K
-      // fragment read one step ahead, so the softmax of the first block overlaps
-      // the matrix cores' work on the second.  A block wholly outside this wave's
-      // causal window is computed anyway and then ignored.
-      f32x16 sblk[kPfBN / 32];
-      bool act[kPfBN / 32];
+  // ---- the per-block steps ----
+  // S^T of the 32 keys of block kb of a K tile
+  auto qk = [&](const uint16_t* kt_lds, int kb) {
+    const uint16_t* kl = kt_lds + k_lane + kb * 32 * D;
+    f32x16 sc;
 #pragma unroll
-      for (int kb = 0; kb < kPfBN / 32; ++kb) {
-        const int kb0 = kt * kPfBN + kb * 32;
-        act[kb] = !(kb0 >= L || (a.causal && kb0 > w_pos_max) || r_w >= q_len);
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sblk[kb][e] = 0.f;
-      }
-      if (act[0] || act[1]) {
-        const uint16_t* kl0 = cur + col * D;
-        const uint16_t* kl1 = cur + (32 + col) * D;
-        const int sw0 = chunk_swz<D>(col), sw1 = chunk_swz<D>(32 + col);
-        auto kfrag = [&](const uint16_t* kl, int sw, int kk) {
-          return *reinterpret_cast<const u32x4*>(kl + (((2 * kk + hh) ^ sw) << 3));
-        };
-        u32x4 n0 = kfrag(kl0, sw0, 0), n1 = kfrag(kl1, sw1, 0);
+    for (int kk = 0; kk < D / 16; ++kk)
+      sc = mfma32x32x16(*reinterpret_cast<const u32x4*>(kl + 256 * kk), qb[kk], sc);
+    return sc;
+  };
+  // scaled row maximum of a block (log2 units)
+  auto rowmax = [&](const f32x16& sc) {
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const u32x4 f0 = n0, f1 = n1;
-          if (kk + 1 < D / 16) {
-            n0 = kfrag(kl0, sw0, kk + 1);
-            n1 = kfrag(kl1, sw1, kk + 1);
-          }
-          sblk[0] = mfma32x32x16(f0, qb[kk], sblk[0]);
-          sblk[1] = mfma32x32x16(f1, qb[kk], sblk[1]);
-        }
-        // Scheduling order: the fragment reads run two MFMA pairs ahead of their use.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 LDS reads
+    for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, sc[e]), sc[e + 1]);
+    mt = fmaxf(mt, sc[15]);
+    return xor32_max(mt) * a.scale_log2;
+  };
+  // -inf for keys past the end and (causal) above the diagonal; returns the row
+  // maximum, recomputed when the block needed a mask
+  auto mask = [&](f32x16& sc, int kb0, float mt) {
+    const bool need = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
+    if (__builtin_expect(need, 0)) {
 #pragma unroll
-        for (int i = 0; i < D / 16 - 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int kb = 0; kb < kPfBN / 32; ++kb) {
-        if (!act[kb]) continue;
-        const int kb0 = kt * kPfBN + kb * 32;
-        f32x16& s = sblk[kb];
-        // Keys past the end and (causal) above the diagonal get -inf; only blocks
-        // that touch the boundary need it.
-        const bool need_mask = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
-        if (__builtin_expect(need_mask, 0)) {
-          const int lim = a.causal ? min(L - 1, my_pos) : L - 1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kb0 + 8 * j + 4 * hh + i;
-              if (key > lim) s[4 * j + i] = kNegInf;
-            }
-        }
-        // Online softmax in log2 units with a lazily moved reference: the running
-        // reference m_ref only moves (rescaling l and the accumulator) when a row's
-        // scaled maximum exceeds it by more than kRescaleSlack, so P stays below
-        // 2^kRescaleSlack and the result is unchanged -- the final normalisation
-        // uses the same reference ("The Stack Below the Stack (Part 2)", 2.1 and 2.3).
-        float mt = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-        for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, s[e]), s[e + 1]);
-        mt = fmaxf(mt, s[15]);
-        mt = xor32_max(mt) * a.scale_log2;
-        const bool grow = mt > m_run + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float m_new = grow ? mt : m_run;
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-          l_run *= alpha;
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-          m_run = m_new;
-        }
-        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.scale_log2, neg_m));
-          psum += s[e];
-        }
-        l_run += psum;
-        // P^T operand halves: keys 16u + 4 hh + (0..3) and 16u + 8 + 4 hh + (0..3)
-        const u32x4 pb0 = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
-                           pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
-        const u32x4 pb1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
-                           pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
-        // The V^T operand (8 keys of one d per lane) comes from two transposing
-        // reads of row-major V: in each 16-lane group, lane i points at key row
-        // key0 + i/4, columns d0 + 4 (i % 4) .. + 3.
-        const int g16 = lane & 15;
-        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
-        auto vfrag = [&](int t, int u) {
-          const int dd = 32 * t + dsub;                      // first d of this lane's piece
-          const int r0 = kb * 32 + 16 * u + 4 * hh + (g16 >> 2);
-          const int r1 = r0 + 8;
-          const u32x2 lo = ds_read_tr16(cur + PfLds<D>::TILE + r0 * D +
-                                        (((dd >> 3) ^ chunk_swz<D>(r0)) << 3) + (dd & 7));
-          const u32x2 hi = ds_read_tr16(cur + PfLds<D>::TILE + r1 * D +
-                                        (((dd >> 3) ^ chunk_swz<D>(r1)) << 3) + (dd & 7));
-          return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
-        // O^T += V^T P^T over the block's two 16-key halves; the four d-tiles are
-        // independent accumulators, so each half issues four MFMAs back to back.
-        u32x4 vnext = vfrag(0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) {
-            const u32x4 va = vnext;
-            if (u * (D / 32) + t + 1 < 2 * (D / 32)) {
-              const int n = u * (D / 32) + t + 1;
-              vnext = vfrag(n % (D / 32), n / (D / 32));
-            }
-            acc[t] = mfma32x32x16(va, u == 0 ? pb0 : pb1, acc[t]);
-          }
-      }
-      block_sync();                        // stage kt is free for tile kt + 2
+        for (int i = 0; i < 4; ++i)
+          if (kb0 + 8 * j + 4 * hh + i > lim) sc[4 * j + i] = kNegInf;
+      mt = rowmax(sc);
     }
-    vmcnt_wait<0>();                       // no DMA outstanding into a reused stage
-    base_t = win_end;
+    return mt;
+  };
+  // Online softmax in log2 units with a lazily moved reference: the running
+  // reference m_run only moves (rescaling l and the accumulator) when a row's
+  // scaled maximum exceeds it by more than kRescaleSlack, so P stays below
+  // 2^kRescaleSlack and the result is unchanged -- the final normalisation uses
+  // the same reference ("The Stack Below the Stack (Part 2)", 2.1 and 2.3).
+  auto decide = [&](float mt) {
+    const bool grow = mt > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // P^T operand halves (keys 16 u + 4 hh + 0..3 and 16 u + 8 + 4 hh + 0..3)
+  auto probs = [&](const f32x16& sc, u32x4& pb0, u32x4& pb1) {
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m));
+    pb0 = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                pack_bf16x2(p[6], p[7])};
+    pb1 = u32x4{pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]),
+                pack_bf16x2(p[12], p[13]), pack_bf16x2(p[14], p[15])};
+  };
+  // the row sum takes the same bf16-rounded P that multiplies V
+  auto rowsum = [&](const u32x4& pb0, const u32x4& pb1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_run = sum_bf16x2(pb0[i], l_run);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_run = sum_bf16x2(pb1[i], l_run);
+  };
+  // O^T += V^T P^T over block kb of a V tile
+  auto pv = [&](const uint16_t* vt_lds, int kb, const u32x4& pb0, const u32x4& pb1) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t* vl = vt_lds + (2 * kb + u) * PfLds<D>::REGION;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const u32x2 lo = ds_read_tr16(vl + v_lane[0] + 512 * t);
+        const u32x2 hi = ds_read_tr16(vl + v_lane[1] + 512 * t);
+        acc[t] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, u == 0 ? pb0 : pb1, acc[t]);
+      }
+    }
+  };
+
+  // One pipeline step: exponentiate the pending block (its reference already
+  // decided) and accumulate its P V from V tile vp (block kbp), while computing the
+  // scores of the next block from K tile kq (block kbq) and their raw row maximum.
+  // The instruction order is written out: each MFMA is followed by the vector work
+  // that does not depend on it, so the matrix cores and the vector ALU of one wave
+  // overlap; operand reads run two MFMAs ahead.  sched_barrier keeps the compiler
+  // from regrouping the chunks.
+  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, const uint16_t* vp, int kbp,
+                  float& mt_next) {
+    constexpr int NK = D / 16;                 // QK MFMAs
+    constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
+    constexpr int NV = 2 * (D / 32);           // PV MFMAs
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    const uint16_t* kl = kq + k_lane + kbq * 32 * D;
+    u32x4 kf[NK];
+    kf[0] = *reinterpret_cast<const u32x4*>(kl);
+    kf[1] = *reinterpret_cast<const u32x4*>(kl + 256);
+    f32x16 sn;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+    // P^T operand, packed as it is produced: pw[0..3] is the half for keys 16 u +
+    // 4 hh + 0..3 with u = 0, pw[4..7] the half with u = 1
+    uint32_t pw[8];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      if (i + 2 < NK) kf[i + 2] = *reinterpret_cast<const u32x4*>(kl + 256 * (i + 2));
+      sn = mfma32x32x16(kf[i], qb[i], sn);
+#pragma unroll
+      for (int e = EPK * i; e < EPK * (i + 1); e += 2)
+        pw[e / 2] =
+            pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], a.scale_log2, neg_m)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], a.scale_log2, neg_m)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const u32x4 pb0 = {pw[0], pw[1], pw[2], pw[3]};
+    const u32x4 pb1 = {pw[4], pw[5], pw[6], pw[7]};
+    // O^T += V^T P^T: MFMA i covers d-tile i % (D / 32) of 16-key half i / (D / 32)
+    auto vfrag = [&](int i) {
+      const uint16_t* vl =
+          vp + (2 * kbp + i / (D / 32)) * PfLds<D>::REGION + 512 * (i % (D / 32));
+      const u32x2 lo = ds_read_tr16(vl + v_lane[0]);
+      const u32x2 hi = ds_read_tr16(vl + v_lane[1]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vf[NV];
+    vf[0] = vfrag(0);
+    vf[1] = vfrag(1);
+    float mt = kNegInf;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i + 2 < NV) vf[i + 2] = vfrag(i + 2);
+      const int t = i % (D / 32);
+      acc[t] = mfma32x32x16(vf[i], i < D / 32 ? pb0 : pb1, acc[t]);
+      // the row sum takes the same bf16-rounded P that multiplies V; the 8 packed
+      // pairs and the 16 scores of the new block are spread over the NV chunks
+#pragma unroll
+      for (int w = (8 / NV) * i; w < (8 / NV) * (i + 1); ++w) l_run = sum_bf16x2(pw[w], l_run);
+#pragma unroll
+      for (int e = (16 / NV) * i; e < (16 / NV) * (i + 1); e += 2)
+        mt = max3(mt, sn[e], sn[e + 1]);
+      pin(l_run);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mt_next = xor32_max(mt) * a.scale_log2;
+    s_pend = sn;
+  };
+
+  // Software pipeline over 32-key blocks: while the matrix cores compute S of
+  // block i + 1 and then O += P V of block i, the vector unit exponentiates block
+  // i and reduces block i + 1.  K of tiles t, t + 1 and V of tiles t - 1 .. t + 1
+  // are resident, so one barrier per tile suffices.
+  if (n_tiles > 0) {
+    tab = load_tab(0);
+    int vs_cur = 0;                       // V stage of tile kt
+    issue(0, 0);
+    publish(0, 0);
+    if (n_tiles > 1) issue(1, 1);
+    f32x16 s_pend = qk(kst(0), 0);        // block 0: scores, mask, reference
+    decide(mask(s_pend, 0, rowmax(s_pend)));
+    float mt;
+    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+      const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
+      // block 2 kt (pending) -> block 2 kt + 1
+      step(s_pend, kst(kt), 1, vst(vs_cur), 0, mt);
+      decide(mask(s_pend, kt * kPfBN + 32, mt));
+      // block 2 kt + 1 -> block 2 kt + 2 (first of the next tile)
+      publish(kt + 1, vs_next);
+      if (kt + 2 < n_tiles) issue(kt + 2, vs_next == 2 ? 0 : vs_next + 1);
+      step(s_pend, kst(kt + 1), 0, vst(vs_cur), 1, mt);
+      decide(mask(s_pend, (kt + 1) * kPfBN, mt));
+      vs_cur = vs_next;
+    }
+    step(s_pend, kst(n_tiles - 1), 1, vst(vs_cur), 0, mt);
+    decide(mask(s_pend, (n_tiles - 1) * kPfBN + 32, mt));
+    u32x4 p0, p1;
+    probs(s_pend, p0, p1);
+    pv(vst(vs_cur), 1, p0, p1);
+    rowsum(p0, p1);
   }
 
   if (!row_ok) return;
@@ -362,15 +483,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int D>
-static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream, int n_qt) {
-  dim3 grid(a.Hq, a.B, n_qt);
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  dim3 grid(a.Hq * a.B * a.n_qt);
   hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kPfThreads), PfLds<D>::BYTES, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
+hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
                           size_t desc_len) {
-  const int n_qt = (a.max_q_len + kPfBM - 1) / kPfBM;
+  PrefillArgs a = a_in;
+  a.n_qt = (a.max_q_len + kPfBM - 1) / kPfBM;
+  const int groups = a.B * a.Hkv;
+  a.xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
   if (a.D == 128) {
     // more than 64 KiB of dynamic LDS must be requested once per process
@@ -378,13 +502,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
         reinterpret_cast<const void*>(prefill_kernel<128>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<128>::BYTES);
     if (attr != hipSuccess) return attr;
-    e = launch_prefill_t<128>(a, stream, n_qt);
+    e = launch_prefill_t<128>(a, stream);
   } else {
-    e = launch_prefill_t<64>(a, stream, n_qt);
+    e = launch_prefill_t<64>(a, stream);
   }
   snprintf(desc, desc_len,
-           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=(%d,%d,%d) block=%d lds=%zu",
-           a.D, kPfBM, kPfBN, a.Hq, a.B, n_qt, kPfThreads,
+           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=%d (%d heads x %d seqs x %d "
+           "q-tiles, %s) block=%d lds=%zu",
+           a.D, kPfBM, kPfBN, a.Hq * a.B * a.n_qt, a.Hq, a.B, a.n_qt,
+           a.xcd_groups ? "KV groups per XCD" : "head-major", kPfThreads,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;
 }
