@@ -194,8 +194,10 @@ int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out
  *   seq_lens_k : [B] int32                      block_tables : [B, max_pages] int32
  *   max_q_len  : host-side upper bound of the per-sequence q_len (sizes the grid;
  *                rows past it are not computed)
- * One launch covers Hq * B * ceil(max_q_len / 128) work-groups of 256 threads;
- * more than 2^32 - 1 threads in total is refused with PA_ERR_SHAPE.
+ * One launch covers Hq * B * ceil(max_q_len / R) work-groups of 2 R threads
+ * (R = 128 query rows, or 256 when max_q_len >= 1024); when
+ * Hq * B * (ceil(max_q_len / 128) + 1) * 256 exceeds 2^32 - 1 the call is refused
+ * with PA_ERR_SHAPE.
  */
 int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const void* k_pool,
                               const void* v_pool, const int32_t* cu_seqlens_q,

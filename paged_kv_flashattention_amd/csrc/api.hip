@@ -313,9 +313,9 @@ int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const vo
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
     return fail(PA_ERR_SHAPE, "prefill: softmax scale must be positive and finite");
   if (max_q_len > Tq) max_q_len = Tq;
-  // one work-group per (query head, sequence, 128-row query tile); the launch
-  // holds at most 2^32 - 1 work-items
-  if ((long long)Hq * B * ((max_q_len + 127) / 128) * 256 > 0xffffffffll)
+  // one work-group per (query head, sequence, 128- or 256-row query tile); the
+  // launch holds at most 2^32 - 1 work-items
+  if ((long long)Hq * B * ((max_q_len + 127) / 128 + 1) * 256 > 0xffffffffll)
     return fail(PA_ERR_SHAPE, "prefill: %d heads x %d sequences x %d query rows is too many "
                 "work-groups for one launch", Hq, B, max_q_len);
   pa::PrefillArgs a{};

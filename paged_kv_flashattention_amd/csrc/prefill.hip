@@ -25,11 +25,12 @@
 
 namespace pa {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfBM = 32 * kPfWaves;   // query rows per work-group
 constexpr int kPfBN = 64;              // keys per LDS tile
-constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom before the reference moves
+constexpr float kSumLimit = 256.f;     // 2^kRescaleSlack: bound on a lane's block row sum
+#ifndef PF_W8_MIN
+#define PF_W8_MIN 1024
+#endif
 
 // LDS tiles of 64 keys.  Each wave's 16 rows (keys 16 w .. 16 w + 15, one run of
 // one page) form a region of 16 x D bf16 stored chunk-major: the 16-byte chunk c
@@ -109,45 +110,62 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// DMA loads of one 64-key tile into LDS (K into kst, V into vst).  Wave w fills
-// its region (keys k0 + 16 w .., all in one page, which starts its 16-row run at
-// in-page row (16 w) & (page_size - 1) since tiles start on page boundaries) with
-// D / 32 load instructions per matrix.  The per-lane byte offsets koff / voff
-// (row and chunk within the run of the slot the lane fills) are fixed for the
-// whole kernel, so a tile costs only scalar address arithmetic.
-template <int D>
+// How the W waves of a work-group split the DMA of a 64-key tile: the tile has
+// four 16-row regions of D / 8 lines; wave w fills lines line0 .. line0 + LPW - 1
+// of region w * 4 / W, with LPW / 4 load instructions per matrix (each covers four
+// lines of 16 slots).  The 16 rows of a region are keys k0 + 16 r .., all in one
+// page, which starts the run at in-page row (16 r) & (page_size - 1) since tiles
+// start on page boundaries.
+template <int D, int W>
+struct PfDma {
+  static constexpr int LPW = (D / 8) * 4 / W;     // lines per wave
+  static constexpr int NJ = LPW / 4;              // load instructions per matrix
+  static __device__ __forceinline__ int region(int wave) { return wave * 4 / W; }
+  static __device__ __forceinline__ int line0(int wave) { return (wave % (W / 4)) * LPW; }
+};
+
+// DMA loads of one 64-key tile into LDS (K into kst, V into vst).  The per-lane
+// byte offsets koff / voff (row and chunk within the run of the slot the lane
+// fills) are fixed for the whole kernel, so a tile costs only scalar address
+// arithmetic.
+template <int D, int W>
 __device__ __forceinline__ void pf_issue_tile(uint16_t* kst, uint16_t* vst,
                                               const uint16_t* kbase, const uint16_t* vbase,
                                               size_t page_row0, int rs, const uint32_t* koff,
                                               const uint32_t* voff, int wave) {
+  using M = PfDma<D, W>;
   const size_t base = page_row0 * rs;
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int slot0 = wave * PfLds<D>::REGION + 512 * j;      // wave-uniform
+  for (int j = 0; j < M::NJ; ++j) {
+    const int slot0 = M::region(wave) * PfLds<D>::REGION + 128 * (M::line0(wave) + 4 * j);
     dma16(kbase + base, koff[j], kst + slot0);
     dma16(vbase + base, voff[j], vst + slot0);
   }
 }
 
-// Zero this wave's V rows at or past the sequence end (the last tile only): they
-// hold other data, and P = 0 times NaN would not be 0.  Lane i of pass j owns
-// slot 64 j + i of the region, as in the DMA.
-template <int D>
+// Zero this wave's V slots whose rows are at or past the sequence end (the last
+// tile only): they hold other data, and P = 0 times NaN would not be 0.  The
+// slots are the ones this wave's DMA fills.
+template <int D, int W>
 __device__ __forceinline__ void pf_zero_tail(uint16_t* vst, int k0, int L, int wave, int lane) {
+  using M = PfDma<D, W>;
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int c = 4 * j + (lane >> 4);
+  for (int j = 0; j < M::NJ; ++j) {
+    const int c = M::line0(wave) + 4 * j + (lane >> 4);
     const int row = ((lane & 15) - 4 * c) & 15;
-    if (k0 + 16 * wave + row >= L)
-      *reinterpret_cast<u32x4*>(vst + wave * PfLds<D>::REGION + 512 * j + 8 * lane) =
-          u32x4{0u, 0u, 0u, 0u};
+    if (k0 + 16 * M::region(wave) + row >= L)
+      *reinterpret_cast<u32x4*>(vst + M::region(wave) * PfLds<D>::REGION + 128 * c +
+                                8 * (lane & 15)) = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
+// W waves (32 W query rows) per work-group; 8 W waves per CU.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
+  using M_ = PfDma<D, W>;
+  constexpr int kPfBM = 32 * W;       // query rows per work-group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -241,18 +259,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   int base_t = 0;
   int tab = 0;
   auto load_tab = [&](int first_tile) {
-    int idx = ((first_tile + lane) * kPfBN + 16 * wave) >> a.ps_shift;
+    int idx = ((first_tile + lane) * kPfBN + 16 * M_::region(wave)) >> a.ps_shift;
     idx = idx < a.max_pages ? idx : a.max_pages - 1;
     return bt[idx];
   };
-  const int run0 = (16 * wave) & (a.page_size - 1);
+  const int run0 = (16 * M_::region(wave)) & (a.page_size - 1);
   const int rs = a.Hkv * D;
   // the global chunk each lane's DMA slot receives: slot 64 j + lane = line c,
   // slot s; K holds row s there, V row (s - 4 c) mod 16
-  uint32_t k_dma[D / 32], v_dma[D / 32];
+  uint32_t k_dma[M_::NJ], v_dma[M_::NJ];
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int c = 4 * j + (lane >> 4), sl = lane & 15;
+  for (int j = 0; j < M_::NJ; ++j) {
+    const int c = M_::line0(wave) + 4 * j + (lane >> 4), sl = lane & 15;
     k_dma[j] = (uint32_t)(sl * rs + c * 8) * 2u;
     v_dma[j] = (uint32_t)((((sl - 4 * c) & 15) * rs) + c * 8) * 2u;
   }
@@ -266,14 +284,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     int pg = __builtin_amdgcn_readlane(tab, n - base_t);
     pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
-    pf_issue_tile<D>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
+    pf_issue_tile<D, W>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
                      k_dma, v_dma, wave);
   };
   // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
   auto publish = [&](int n, int vs) {
     vmcnt_wait<0>();
     if (n * kPfBN + kPfBN > L) {
-      pf_zero_tail<D>(vst(vs), n * kPfBN, L, wave, lane);
+      pf_zero_tail<D, W>(vst(vs), n * kPfBN, L, wave, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in LDS
     }
     block_sync();
@@ -299,9 +317,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     mt = fmaxf(mt, sc[15]);
     return xor32_max(mt) * a.scale_log2;
   };
-  // -inf for keys past the end and (causal) above the diagonal; returns the row
-  // maximum, recomputed when the block needed a mask
-  auto mask = [&](f32x16& sc, int kb0, float mt) {
+  // -inf for keys past the end and (causal) above the diagonal; only blocks that
+  // touch the boundary need it
+  auto mask = [&](f32x16& sc, int kb0) {
     const bool need = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
     if (__builtin_expect(need, 0)) {
 #pragma unroll
@@ -309,9 +327,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (kb0 + 8 * j + 4 * hh + i > lim) sc[4 * j + i] = kNegInf;
-      mt = rowmax(sc);
     }
-    return mt;
   };
   // Online softmax in log2 units with a lazily moved reference: the running
   // reference m_run only moves (rescaling l and the accumulator) when a row's
@@ -329,25 +345,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
       m_run = m_new;
     }
   };
-  // P^T operand halves (keys 16 u + 4 hh + 0..3 and 16 u + 8 + 4 hh + 0..3)
-  auto probs = [&](const f32x16& sc, u32x4& pb0, u32x4& pb1) {
-    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-    float p[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m));
-    pb0 = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                pack_bf16x2(p[6], p[7])};
-    pb1 = u32x4{pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]),
-                pack_bf16x2(p[12], p[13]), pack_bf16x2(p[14], p[15])};
-  };
-  // the row sum takes the same bf16-rounded P that multiplies V
-  auto rowsum = [&](const u32x4& pb0, const u32x4& pb1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l_run = sum_bf16x2(pb0[i], l_run);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l_run = sum_bf16x2(pb1[i], l_run);
-  };
   // O^T += V^T P^T over block kb of a V tile
   auto pv = [&](const uint16_t* vt_lds, int kb, const u32x4& pb0, const u32x4& pb1) {
 #pragma unroll
@@ -362,15 +359,48 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // One pipeline step: exponentiate the pending block (its reference already
-  // decided) and accumulate its P V from V tile vp (block kbp), while computing the
-  // scores of the next block from K tile kq (block kbq) and their raw row maximum.
-  // The instruction order is written out: each MFMA is followed by the vector work
-  // that does not depend on it, so the matrix cores and the vector ALU of one wave
-  // overlap; operand reads run two MFMAs ahead.  sched_barrier keeps the compiler
-  // from regrouping the chunks.
-  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, const uint16_t* vp, int kbp,
-                  float& mt_next) {
+  // exp2(s * scale_log2 - m_run) of a block, packed to the P^T operand layout
+  // (pw[0..3]: keys 16 u + 4 hh + 0..3 with u = 0, pw[4..7] with u = 1), and the
+  // lane's share of the block's row sum, taken on the same bf16-rounded P that
+  // multiplies V
+  auto exps = [&](const f32x16& sc, uint32_t* pw, float& ps) {
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      pw[e / 2] =
+          pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], a.scale_log2, neg_m)));
+      ps = sum_bf16x2(pw[e / 2], ps);
+    }
+  };
+  // The reference m_run is only checked after the fact: a block is exponentiated
+  // against the current reference, and only when some lane's partial row sum
+  // exceeds 2^kRescaleSlack (so P may have grown past that) does the wave take
+  // the row maximum, move the reference, rescale l and the accumulator and redo
+  // the block.  The accepted P are therefore bounded by 2^kRescaleSlack and the
+  // result is the same as with an exact running maximum ("The Stack Below the
+  // Stack (Part 2)", 2.1 and 2.3: any common reference gives the same quotient).
+  auto settle = [&](const f32x16& sc, uint32_t* pw, float& ps) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit) || m_run == kNegInf), 0)) {
+      const float m_new = fmaxf(m_run, rowmax(sc));
+      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+      m_run = m_new;
+      exps(sc, pw, ps);
+    }
+    l_run += ps;
+  };
+  // One pipeline step: exponentiate the pending block against the current
+  // reference and accumulate its P V from V tile vp (block kbp), while computing
+  // the scores of the next block from K tile kq (block kbq).  The instruction
+  // order is written out: each MFMA is followed by the vector work that does not
+  // depend on it, so the matrix cores and the vector ALU of one wave overlap;
+  // operand reads run two MFMAs ahead.  sched_barrier keeps the compiler from
+  // regrouping the chunks.
+  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, const uint16_t* vp, int kbp) {
     constexpr int NK = D / 16;                 // QK MFMAs
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
     constexpr int NV = 2 * (D / 32);           // PV MFMAs
@@ -382,9 +412,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     f32x16 sn;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
-    // P^T operand, packed as it is produced: pw[0..3] is the half for keys 16 u +
-    // 4 hh + 0..3 with u = 0, pw[4..7] the half with u = 1
     uint32_t pw[8];
+    float ps = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -395,8 +424,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         pw[e / 2] =
             pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], a.scale_log2, neg_m)),
                         __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], a.scale_log2, neg_m)));
+      // row sum of the pairs packed one chunk earlier
+      if (i > 0) {
+#pragma unroll
+        for (int e = EPK * (i - 1); e < EPK * i; e += 2) ps = sum_bf16x2(pw[e / 2], ps);
+      }
+      pin(ps);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int e = EPK * (NK - 1); e < 16; e += 2) ps = sum_bf16x2(pw[e / 2], ps);
+    settle(s_pend, pw, ps);
     const u32x4 pb0 = {pw[0], pw[1], pw[2], pw[3]};
     const u32x4 pb1 = {pw[4], pw[5], pw[6], pw[7]};
     // O^T += V^T P^T: MFMA i covers d-tile i % (D / 32) of 16-key half i / (D / 32)
@@ -410,58 +448,49 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     u32x4 vf[NV];
     vf[0] = vfrag(0);
     vf[1] = vfrag(1);
-    float mt = kNegInf;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       if (i + 2 < NV) vf[i + 2] = vfrag(i + 2);
       const int t = i % (D / 32);
       acc[t] = mfma32x32x16(vf[i], i < D / 32 ? pb0 : pb1, acc[t]);
-      // the row sum takes the same bf16-rounded P that multiplies V; the 8 packed
-      // pairs and the 16 scores of the new block are spread over the NV chunks
-#pragma unroll
-      for (int w = (8 / NV) * i; w < (8 / NV) * (i + 1); ++w) l_run = sum_bf16x2(pw[w], l_run);
-#pragma unroll
-      for (int e = (16 / NV) * i; e < (16 / NV) * (i + 1); e += 2)
-        mt = max3(mt, sn[e], sn[e + 1]);
-      pin(l_run);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mt_next = xor32_max(mt) * a.scale_log2;
     s_pend = sn;
   };
 
   // Software pipeline over 32-key blocks: while the matrix cores compute S of
   // block i + 1 and then O += P V of block i, the vector unit exponentiates block
-  // i and reduces block i + 1.  K of tiles t, t + 1 and V of tiles t - 1 .. t + 1
-  // are resident, so one barrier per tile suffices.
+  // i.  K of tiles t, t + 1 and V of tiles t - 1 .. t + 1 are resident, so one
+  // barrier per tile suffices.
   if (n_tiles > 0) {
     tab = load_tab(0);
     int vs_cur = 0;                       // V stage of tile kt
     issue(0, 0);
     publish(0, 0);
     if (n_tiles > 1) issue(1, 1);
-    f32x16 s_pend = qk(kst(0), 0);        // block 0: scores, mask, reference
-    decide(mask(s_pend, 0, rowmax(s_pend)));
-    float mt;
+    f32x16 s_pend = qk(kst(0), 0);        // block 0: scores, mask, first reference
+    mask(s_pend, 0);
+    decide(rowmax(s_pend));
     for (int kt = 0; kt + 1 < n_tiles; ++kt) {
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // block 2 kt (pending) -> block 2 kt + 1
-      step(s_pend, kst(kt), 1, vst(vs_cur), 0, mt);
-      decide(mask(s_pend, kt * kPfBN + 32, mt));
+      step(s_pend, kst(kt), 1, vst(vs_cur), 0);
+      mask(s_pend, kt * kPfBN + 32);
       // block 2 kt + 1 -> block 2 kt + 2 (first of the next tile)
       publish(kt + 1, vs_next);
       if (kt + 2 < n_tiles) issue(kt + 2, vs_next == 2 ? 0 : vs_next + 1);
-      step(s_pend, kst(kt + 1), 0, vst(vs_cur), 1, mt);
-      decide(mask(s_pend, (kt + 1) * kPfBN, mt));
+      step(s_pend, kst(kt + 1), 0, vst(vs_cur), 1);
+      mask(s_pend, (kt + 1) * kPfBN);
       vs_cur = vs_next;
     }
-    step(s_pend, kst(n_tiles - 1), 1, vst(vs_cur), 0, mt);
-    decide(mask(s_pend, (n_tiles - 1) * kPfBN + 32, mt));
-    u32x4 p0, p1;
-    probs(s_pend, p0, p1);
-    pv(vst(vs_cur), 1, p0, p1);
-    rowsum(p0, p1);
+    step(s_pend, kst(n_tiles - 1), 1, vst(vs_cur), 0);
+    mask(s_pend, (n_tiles - 1) * kPfBN + 32);
+    uint32_t pw[8];
+    float ps;
+    exps(s_pend, pw, ps);
+    settle(s_pend, pw, ps);
+    pv(vst(vs_cur), 1, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
   }
 
   if (!row_ok) return;
@@ -482,35 +511,40 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     a.lse_out[(size_t)(t0 + my_row) * a.Hq + h] = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
 }
 
-template <int D>
+template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  // more than 64 KiB of dynamic LDS must be requested once per process
+  static const hipError_t attr = PfLds<D>::BYTES > 65536
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
+      : hipSuccess;
+  if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt);
-  hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kPfThreads), PfLds<D>::BYTES, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, W>), grid, dim3(64 * W), PfLds<D>::BYTES, stream, a);
   return hipGetLastError();
 }
+
+// Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
+// longest query run fills them, else 4.
+int prefill_waves(int max_q_len) { return max_q_len >= PF_W8_MIN ? 8 : 4; }
 
 hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
                           size_t desc_len) {
   PrefillArgs a = a_in;
-  a.n_qt = (a.max_q_len + kPfBM - 1) / kPfBM;
+  const int W = prefill_waves(a.max_q_len);
+  a.n_qt = (a.max_q_len + 32 * W - 1) / (32 * W);
   const int groups = a.B * a.Hkv;
   a.xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
-  if (a.D == 128) {
-    // more than 64 KiB of dynamic LDS must be requested once per process
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(prefill_kernel<128>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<128>::BYTES);
-    if (attr != hipSuccess) return attr;
-    e = launch_prefill_t<128>(a, stream);
-  } else {
-    e = launch_prefill_t<64>(a, stream);
-  }
+  if (a.D == 128)
+    e = W == 8 ? launch_prefill_t<128, 8>(a, stream) : launch_prefill_t<128, 4>(a, stream);
+  else
+    e = W == 8 ? launch_prefill_t<64, 8>(a, stream) : launch_prefill_t<64, 4>(a, stream);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=%d (%d heads x %d seqs x %d "
            "q-tiles, %s) block=%d lds=%zu",
-           a.D, kPfBM, kPfBN, a.Hq * a.B * a.n_qt, a.Hq, a.B, a.n_qt,
-           a.xcd_groups ? "KV groups per XCD" : "head-major", kPfThreads,
+           a.D, 32 * W, kPfBN, a.Hq * a.B * a.n_qt, a.Hq, a.B, a.n_qt,
+           a.xcd_groups ? "KV groups per XCD" : "head-major", 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;
 }

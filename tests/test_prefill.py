@@ -37,6 +37,10 @@ CASES = [
     ([17, 0], [50, 130], 8, 8, 64, 32, True),              # MHA, D 64, page 32
     ([300, 0, 7], [40, 129, 1], 8, 2, 128, 16, False),     # non-causal
     ([0, 0], [1, 2], 4, 2, 64, 16, False),
+    # max_q_len >= 1024: 256-row work-groups (8 waves), ragged last tiles
+    ([0, 0], [1100, 300], 4, 2, 64, 16, True),
+    ([500, 0], [1030, 260], 8, 2, 128, 32, True),
+    ([0], [1024], 4, 4, 128, 64, False),
 ]
 
 
