@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--traffic-pass", action="store_true",
+                   help="run only a 1 GiB device copy and a few partition-kernel launches, "
+                        "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE collection")
     return p.parse_args()
 
 
@@ -242,6 +245,58 @@ def rate(units, ms, unit_name):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from rocprofv3 counters
+# ---------------------------------------------------------------------------
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_qwen7b_decode_traffic.json")
+DECODE_SOURCES = ["decode.hip", "common.hpp", "kernels.hpp"]
+COPY_BYTES = 1 << 30           # the calibration copy reads and writes this many bytes
+
+
+def decode_source_digest():
+    """sha256 over the sources the partition kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "paged_kv_flashattention_amd", "csrc")
+    for f in DECODE_SOURCES:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per partition-kernel launch (FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter's reading for a copy of known size), as recorded from the
+    counter runs -- or None when the kernel's sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != decode_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def traffic_pass(steps):
+    """What the counter runs profile: a plain device copy of COPY_BYTES (the
+    calibration), then `steps` launches of the decode partition kernel over the
+    rotated pool copies, exactly as dominant_kernel_ms launches them."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    step = make_step("qwen7b_decode", 0)
+    step.dominant_kernel_ms(steps)
+    log(f"[bench] traffic pass: copy of {COPY_BYTES} bytes, {steps} partition launches; "
+        f"sources {decode_source_digest()[:16]}")
+
+
+# ---------------------------------------------------------------------------
 # oracle baseline on the host cores
 # ---------------------------------------------------------------------------
 
@@ -298,6 +353,10 @@ def main():
     torch.cuda.init()
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
 
+    if args.traffic_pass:
+        traffic_pass(args.steps)
+        return
+
     step = make_step(args.workload, args.num_splits)
     torch.cuda.synchronize()
     wall, ev = time_step(step, args.steps, args.warmup)
@@ -325,7 +384,8 @@ def main():
         "data": "synthetic",
         "config": step.config(),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": step.unit_name, "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": step.unit_name, "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic() if args.workload == "qwen7b_decode" else None,
                      "kernel": "decode_partition_kernel" if bound == "hbm" else "prefill_kernel",
                      "kernel_us_per_launch": round(kern_ms * 1e3, 2),
                      "step_us": round(ev * 1e3, 2)},
