@@ -387,17 +387,25 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Waves per work-group: long partitions are split over 4 waves, shorter ones over
-// 2 (measured on MI355X: fewer, longer streams per CU read HBM faster).
-static int decode_waves(int part_len) { return part_len >= 8192 ? 4 : 2; }
+// Waves per work-group: enough waves in the whole grid (about two per CU, 512 on
+// MI355X) and no more, so that each wave streams as long a run of keys as
+// possible (measured on MI355X: fewer, longer streams read HBM faster; one
+// wave per CU is too few).
+static int decode_waves(const DecodeArgs& a) {
+  const long long groups = (long long)a.Hkv * a.S * a.B;
+  return groups >= 512 ? 1 : (groups >= 256 ? 2 : 4);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream, int W) {
+  if (W == 4) return launch_decode_t<D, 4>(a, stream);
+  if (W == 2) return launch_decode_t<D, 2>(a, stream);
+  return launch_decode_t<D, 1>(a, stream);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len) {
-  const int W = decode_waves(a.part_len);
-  hipError_t e;
-  if (a.D == 128)
-    e = W == 4 ? launch_decode_t<128, 4>(a, stream) : launch_decode_t<128, 2>(a, stream);
-  else
-    e = W == 4 ? launch_decode_t<64, 4>(a, stream) : launch_decode_t<64, 2>(a, stream);
+  const int W = decode_waves(a);
+  hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W) : launch_decode_d<64>(a, stream, W);
   snprintf(desc, desc_len,
            "decode_partition<D=%d,W=%d> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
            W, a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);

@@ -43,6 +43,11 @@ AWKWARD = [
     ([200, 1000], 8, 8, 64, 32, 2),           # MHA, D 64, page size 32
     ([513, 77, 1], 7, 1, 64, 64, 0),          # GQA 7, D 64
     ([100], 4, 4, 128, 16, 64),               # more splits than chunks
+    # >= 512 work-groups (one wave each) and 256 (two waves each)
+    ([(37 * i) % 701 for i in range(64)], 16, 8, 128, 16, 1),
+    ([(37 * i) % 701 for i in range(64)], 16, 8, 128, 16, 2),
+    ([(53 * i) % 509 for i in range(64)], 8, 8, 64, 16, 2),
+    ([(91 * i) % 1201 for i in range(32)], 32, 8, 64, 32, 1),
 ]
 
 
