@@ -37,31 +37,6 @@ struct DecodeChunk {
   uint32_t v[8][D / 32];     // V rows of the lane's 8 keys, d in [D/16 * n, D/16 * (n+1))
 };
 
-// Loads of one 32-key chunk (keys c0 .. c0+31, c0 a multiple of 32); pg0 / pg1 are
-// the wave-uniform pages holding keys c0 and c0+16.  K and V are issued separately
-// so that each can be refilled as soon as its registers are consumed.
-template <int D>
-__device__ __forceinline__ void decode_load_k(DecodeChunk<D>& c, const uint16_t* kbase,
-                                              int pg0, int pg1, int c0, const DecodeArgs& a,
-                                              int n, int g) {
-  const int psm = a.page_size - 1;
-  const int rs = a.Hkv * D;                        // elements between consecutive slots
-  const size_t page_elems = (size_t)a.page_size * rs;
-  const uint16_t* ka = kbase + (size_t)pg0 * page_elems + ((c0 + n) & psm) * rs + (D / 4) * g;
-  const uint16_t* kb = kbase + (size_t)pg1 * page_elems + ((c0 + 16 + n) & psm) * rs +
-                       (D / 4) * g;
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-#ifdef PA_DECODE_K_NT
-    c.ka[kk] = ld16_nt(ka + 8 * kk);
-    c.kb[kk] = ld16_nt(kb + 8 * kk);
-#else
-    c.ka[kk] = ld16(ka + 8 * kk);
-    c.kb[kk] = ld16(kb + 8 * kk);
-#endif
-  }
-}
-
 // K of a chunk in whole-row order: instruction i covers rows RPI*i .. RPI*i+RPI-1
 // (RPI = 512 / D rows of D bf16), each row read by D/8 consecutive lanes, so every
 // load instruction consumes whole cache lines and can stream past the caches.
@@ -127,13 +102,8 @@ __device__ __forceinline__ void decode_load_v(DecodeChunk<D>& c, const uint16_t*
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (D == 128) {
-#ifdef PA_DECODE_V_REGULAR
-      u32x4 x = ld16(va + i * rs);
-      u32x4 y = ld16(vb + i * rs);
-#else
       u32x4 x = ld16_nt(va + i * rs);
       u32x4 y = ld16_nt(vb + i * rs);
-#endif
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         c.v[i][w] = x[w];
