@@ -156,7 +156,12 @@ class PrefillStep:
 
 
 class MixedStep:
-    """The mixed ragged step: write 2,578 new tokens, prefill the 5 chunks, decode 18 rows."""
+    """The mixed ragged step: write 2,578 new tokens, prefill the 5 chunks, decode 18 rows.
+
+    The prefill chunks and the decode rows read disjoint outputs and both only read
+    the pools after the write, so the decode runs on a second stream (default
+    priority) after the write and overlaps the prefill; the step ends when both
+    have finished (the launch stream waits for the second one)."""
 
     def __init__(self, name="mixed_ragged"):
         import torch
@@ -183,18 +188,24 @@ class MixedStep:
         self.bytes = units.decode_bytes(c.seq_lens[n:], c.Hq, c.Hkv, c.D, c.page_size)
         self.units = self.flops
         self.unit_name = "TFLOP/s"
+        self.side = torch.cuda.Stream()
 
     def __call__(self):
+        import torch
         c = self.case
         pa = self.pa
+        main = torch.cuda.current_stream()
         pa.kv_page_write(c.k_pool, c.v_pool, c.k_new, c.v_new, c.cu_new, c.start_pos,
                          c.block_tables)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            pa.paged_attn_decode(self.q_d, c.k_pool, c.v_pool, self.bt_d, self.lens_d, c.scale,
+                                 max_seq_len=self.max_d, num_splits=self.S, out=self.out_d,
+                                 workspace=self.ws)
         pa.paged_attn_prefill_varlen(self.q_pf, c.k_pool, c.v_pool, self.cu_pf, self.lens_pf,
                                      self.bt_pf, c.scale, causal=True, max_q_len=512,
                                      out=self.out_pf)
-        pa.paged_attn_decode(self.q_d, c.k_pool, c.v_pool, self.bt_d, self.lens_d, c.scale,
-                             max_seq_len=self.max_d, num_splits=self.S, out=self.out_d,
-                             workspace=self.ws)
+        main.wait_stream(self.side)
 
     def config(self):
         c = self.case
