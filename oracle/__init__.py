@@ -18,9 +18,12 @@ pages are cited by title and section:
 * "Inside Ion: Custom Attention Kernels for NVIDIA Grace" (cumuluslabs.io),
   "IonAttention in One Paragraph" (paged KV, eager KV writeback).
 
-Parity status: every function below is pinned by ``tests/test_oracle.py``
-(brute force, a library routine, closed forms and invariants).  No function
-is "parity unpinned".
+``oracle/fp8.py`` adds the FP8 (E4M3) page format: decode, a nearest-value
+encoder, the pool quantiser and the quantising page write.
+
+Parity status: every function below is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_fp8.py`` (brute force, a library routine, closed forms and
+invariants).  No function is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -34,4 +37,12 @@ from .attention import (  # noqa: F401
     split_partials_ref,
     merge_ref,
     kv_write_ref,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_ref,
+    dequantize_pool,
+    kv_write_fp8_ref,
 )

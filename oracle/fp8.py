@@ -1,0 +1,108 @@
+"""FP8 (E4M3) key/value pages: the quantiser and its inverse, on the CPU.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+The pages name FP8 quantisation as a fusion target at KV-cache insertion
+("The Stack Below the Stack (Part 2)", section 2.1, the fused inverse-RoPE plus
+FP8 quantisation kernel) and FP8 KV as one ingredient of a serving recipe (the
+same page, its closing "Part 3" pointer).  They fix neither the format nor the
+scaling.  Readings used here (restated in the design notes):
+
+F1  Format: the OCP 8-bit E4M3 ("fn") encoding -- 1 sign bit, 4 exponent bits
+    with bias 7, 3 mantissa bits, subnormals, no infinities, the two codes
+    S.1111.111 are NaN; largest finite magnitude 448 (1.75 * 2^8), smallest
+    normal 2^-6, smallest subnormal 2^-9.
+F2  Scaling: one float32 scale per pool (k_scale for K, v_scale for V), given
+    by the caller.  A stored code c stands for decode(c) * scale.
+F3  Quantisation: y = float32(x) * float32(1 / scale) in float32 arithmetic,
+    clamped to [-448, 448], then rounded to the nearest E4M3 value, ties to the
+    even code (the IEEE default rounding).
+
+The encoder below is written as the definition: it searches the table of every
+finite E4M3 value for the nearest one, so no bit trick has to be trusted.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import bf16_bits_to_f64
+
+__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_ref", "kv_write_fp8_ref",
+           "dequantize_pool"]
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code (uint8) as float64 (F1)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, subnormal, normal)
+    val = np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+    return sign * val
+
+
+# all non-negative finite codes in increasing value order (code order is value order)
+_POS_CODES = np.arange(0x7F, dtype=np.uint8)            # 0x00 .. 0x7E
+_POS_VALUES = e4m3_decode(_POS_CODES)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each finite value with |x| <= 448, ties to the even
+    code (F3).  NaN maps to 0x7F; magnitudes above 448 are an error (the
+    quantiser clamps before encoding)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x[~np.isnan(x)]) > E4M3_MAX):
+        raise ValueError("e4m3_encode: |x| > 448 (clamp first)")
+    a = np.abs(np.nan_to_num(x, nan=0.0))
+    hi = np.searchsorted(_POS_VALUES, a, side="left")     # first value >= a
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    code = np.where(a == _POS_VALUES[hi], _POS_CODES[hi], code).astype(np.uint8)
+    code = np.where(np.signbit(x) & (code != 0), code | 0x80, code).astype(np.uint8)
+    code = np.where(np.signbit(x) & (code == 0), np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_ref(x, scale: float) -> np.ndarray:
+    """E4M3 codes of bf16 values x (uint16 bit patterns or floats) under a pool
+    scale (F2, F3)."""
+    xf = bf16_bits_to_f64(x).astype(np.float32)
+    inv = np.float32(1.0) / np.float32(scale)
+    y = (xf * inv).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(y.astype(np.float64))
+
+
+def dequantize_pool(codes, scale: float) -> np.ndarray:
+    """float64 values a code pool stands for: decode(c) * scale (F2)."""
+    return e4m3_decode(codes) * float(np.float32(scale))
+
+
+def kv_write_fp8_ref(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
+                     page_size: int, k_scale: float, v_scale: float):
+    """The page write of "Inside Ion", "IonAttention in One Paragraph" (token t of
+    sequence b goes to page block_tables[b][pos // page_size], slot pos % page_size)
+    with the quantisation fused in ("The Stack Below the Stack (Part 2)", 2.1).
+    Pools are uint8 code arrays [P, page_size, Hkv, D]; returns new arrays."""
+    kp = np.array(k_pool, dtype=np.uint8, copy=True)
+    vp = np.array(v_pool, dtype=np.uint8, copy=True)
+    kq = quantize_ref(k_new, k_scale)
+    vq = quantize_ref(v_new, v_scale)
+    cu = np.asarray(cu_new)
+    for b in range(len(cu) - 1):
+        for t in range(int(cu[b]), int(cu[b + 1])):
+            pos = int(start_pos[b]) + (t - int(cu[b]))
+            page = int(block_tables[b][pos // page_size])
+            kp[page, pos % page_size] = kq[t]
+            vp[page, pos % page_size] = vq[t]
+    return kp, vp
