@@ -88,6 +88,41 @@ int kv_page_write(void* k_pool, void* v_pool, const void* k_new, const void* v_n
                   void* stream);
 
 /*
+ * FP8 key/value pages.
+ *
+ * Quantising the KV cache to FP8 at insertion is named as a fusion target and as
+ * part of a serving recipe ("The Stack Below the Stack (Part 2)", section 2.1 and
+ * its closing pointer to Part 3); the pages fix no format or scaling, so this
+ * library defines them:
+ *   - a code is one byte in the OCP 8-bit E4M3 ("fn") format: sign, 4 exponent
+ *     bits with bias 7, 3 mantissa bits, subnormals, no infinities, largest
+ *     finite magnitude 448, codes 0x7F/0xFF are NaN;
+ *   - each pool has one float32 scale (k_scale for K, v_scale for V): code c
+ *     stands for decode(c) * scale;
+ *   - quantisation computes y = x * (1 / scale) in float32 (the reciprocal taken
+ *     once, in float32), clamps y to [-448, 448] and rounds to the nearest E4M3
+ *     value, ties to even.  NaN inputs give unspecified codes.
+ * FP8 pools have the bf16 pools' shape [num_pages, page_size, Hkv, D], one byte
+ * per element (uint8 storage), and the same 16-byte alignment rule.
+ */
+
+/*
+ * kv_page_write_fp8 -- kv_page_write with the quantisation fused in: token t's
+ * keys are written as the E4M3 codes of k_new[t] under k_scale, its values under
+ * v_scale, at the same place kv_page_write would put them.
+ *
+ *   k_pool, v_pool   : [num_pages, page_size, Hkv, D] uint8 E4M3 codes, modified in place
+ *   k_new, v_new     : [T, Hkv, D] bf16
+ *   k_scale, v_scale : positive finite float32 (PA_ERR_SHAPE otherwise)
+ * Every other argument, precondition and status is kv_page_write's.
+ */
+int kv_page_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                      const int32_t* cu_new, const int32_t* start_pos,
+                      const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
+                      int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
+                      float k_scale, float v_scale, void* stream);
+
+/*
  * paged_attn_decode_num_splits -- the split count paged_attn_decode uses when it is
  * passed num_splits <= 0: enough (sequence, KV head, split) work-groups to fill the
  * chip, each covering at least a few 32-key chunks ("The Stack Below the Stack
@@ -135,6 +170,28 @@ int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_po
                       int32_t D, float softmax_scale, int32_t max_seq_len,
                       int32_t num_splits, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * paged_attn_decode_fp8 -- paged_attn_decode over FP8 E4M3 pools (format above):
+ * the attention of q against keys decode(k_code) * k_scale and values
+ * decode(v_code) * v_scale.  The codes are widened to bf16 exactly on their way to
+ * the same MFMA path; k_scale folds into the softmax scale and v_scale into the
+ * final normalisation, so lse_out is the log-sum-exp of the scaled scores against
+ * the dequantised keys.
+ *
+ *   k_pool, v_pool   : [num_pages, page_size, Hkv, D] uint8 E4M3 codes (read only)
+ *   k_scale, v_scale : positive finite float32, with softmax_scale * k_scale finite
+ *                      (PA_ERR_SHAPE otherwise)
+ * Every other argument, the split-K workspace (same size as paged_attn_decode's)
+ * and every status are paged_attn_decode's.
+ */
+int paged_attn_decode_fp8(void* out, float* lse_out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                          int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                          int32_t D, float softmax_scale, float k_scale, float v_scale,
+                          int32_t max_seq_len, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_decode_partials -- the first phase of paged_attn_decode on its own:

@@ -7,13 +7,16 @@ library's HIP kernels; torch supplies device memory and the current stream.
 Entry points (same names as the C ABI):
 
 * :func:`kv_page_write`      -- place new tokens' K/V into their pages;
+* :func:`kv_page_write_fp8`  -- the same, quantising into FP8 E4M3 pools;
 * :func:`paged_attn_decode`  -- one query row per sequence, split-K + merge;
+* :func:`paged_attn_decode_fp8` -- decode over FP8 E4M3 pools with per-pool scales;
 * :func:`paged_attn_decode_partials` -- decode's per-partition results only;
 * :func:`paged_attn_splitk_reduce` -- the merge on its own;
 * :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA.
 
 Data contract: bf16 Q / K / V / outputs, int32 indices (int64 is refused, not
-cast), fp32 lse, contiguous tensors on one GPU.  An unsupported configuration
+cast), fp32 lse, contiguous tensors on one GPU.  FP8 pools are uint8 (or
+torch.float8_e4m3fn) tensors of E4M3 codes with one float32 scale per pool.  An unsupported configuration
 raises; there is no fallback path.
 """
 
@@ -27,7 +30,8 @@ import torch
 from . import _lib
 
 __all__ = [
-    "PagedAttnError", "kv_page_write", "paged_attn_decode", "paged_attn_decode_partials",
+    "PagedAttnError", "kv_page_write", "kv_page_write_fp8", "paged_attn_decode",
+    "paged_attn_decode_fp8", "paged_attn_decode_partials",
     "paged_attn_splitk_reduce",
     "paged_attn_prefill_varlen", "decode_num_splits", "decode_workspace_bytes",
     "describe_launch", "library_path", "load_library",
@@ -91,6 +95,35 @@ def _need_dtype(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype} (no implicit casts)")
 
 
+FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _need_fp8_dtype(t, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in FP8_POOL_DTYPES:
+        raise TypeError(f"{name} must hold E4M3 codes as uint8 or float8_e4m3fn, got {t.dtype}")
+
+
+def _need_fp8_pool(t, name: str, device):
+    _need_fp8_dtype(t, name)
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _scales(k_scale, v_scale):
+    ks, vs = float(k_scale), float(v_scale)
+    if not (0.0 < ks < float("inf") and 0.0 < vs < float("inf")):
+        raise ValueError(f"k_scale and v_scale must be positive and finite, got {ks}, {vs}")
+    return ks, vs
+
+
 def _dtypes(*specs):
     """Check every argument's dtype before anything else, so a dtype mistake is
     reported as such whatever else is wrong."""
@@ -115,13 +148,36 @@ def _validate_tables(block_tables, seq_lens, num_pages, page_size, what="seq_len
 def kv_page_write(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
                   stream=None, validate: bool = False) -> None:
     """Write k_new/v_new [T, Hkv, D] into the pools in place (see kv_page_write in C)."""
-    _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16),
-            (k_new, "k_new", torch.bfloat16), (v_new, "v_new", torch.bfloat16),
+    _kv_write(None, k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables, stream,
+              validate)
+
+
+def kv_page_write_fp8(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
+                      k_scale: float, v_scale: float, stream=None,
+                      validate: bool = False) -> None:
+    """Quantise k_new/v_new [T, Hkv, D] bf16 to E4M3 codes under the pool scales and
+    write them into the uint8 pools in place (see kv_page_write_fp8 in C)."""
+    _kv_write(_scales(k_scale, v_scale), k_pool, v_pool, k_new, v_new, cu_new, start_pos,
+              block_tables, stream, validate)
+
+
+def _kv_write(scales, k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables, stream,
+              validate):
+    if scales is None:
+        _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
+    else:
+        _need_fp8_dtype(k_pool, "k_pool")
+        _need_fp8_dtype(v_pool, "v_pool")
+    _dtypes((k_new, "k_new", torch.bfloat16), (v_new, "v_new", torch.bfloat16),
             (cu_new, "cu_new", torch.int32), (start_pos, "start_pos", torch.int32),
             (block_tables, "block_tables", torch.int32))
     dev = k_pool.device
-    _need(k_pool, "k_pool", torch.bfloat16, 4, None)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    if scales is None:
+        _need(k_pool, "k_pool", torch.bfloat16, 4, None)
+        _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    else:
+        _need_fp8_pool(k_pool, "k_pool", None)
+        _need_fp8_pool(v_pool, "v_pool", dev)
     _need(k_new, "k_new", torch.bfloat16, 3, dev)
     _need(v_new, "v_new", torch.bfloat16, 3, dev)
     _need(cu_new, "cu_new", torch.int32, 1, dev)
@@ -151,11 +207,14 @@ def kv_page_write(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
                 if key in seen:
                     raise ValueError(f"two new tokens write page {key[0]} slot {key[1]}")
                 seen.add(key)
+    args = (_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(cu_new),
+            _ptr(start_pos), _ptr(block_tables), B, T, block_tables.shape[1], P, ps, Hkv, D)
+    lib = load_library()
     with torch.cuda.device(dev):
-        _check(load_library().kv_page_write(
-            _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(cu_new),
-            _ptr(start_pos), _ptr(block_tables), B, T, block_tables.shape[1], P, ps, Hkv, D,
-            _stream(stream)))
+        if scales is None:
+            _check(lib.kv_page_write(*args, _stream(stream)))
+        else:
+            _check(lib.kv_page_write_fp8(*args, scales[0], scales[1], _stream(stream)))
 
 
 def decode_num_splits(B: int, Hkv: int, max_seq_len: int) -> int:
@@ -179,14 +238,42 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
     from the device (a synchronisation).  Returns out [B, Hq, D] bf16, and the
     natural-log lse [B, Hq] fp32 as well when ``return_lse``.
     """
-    _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
-            (v_pool, "v_pool", torch.bfloat16), (block_tables, "block_tables", torch.int32),
+    return _decode(None, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
+                   num_splits, out, lse, workspace, return_lse, stream, validate)
+
+
+def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
+                          k_scale: float, v_scale: float, max_seq_len: Optional[int] = None,
+                          num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
+                          stream=None, validate: bool = False):
+    """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
+    decode(code) * k_scale, values for decode(code) * v_scale.  Arguments and
+    results are paged_attn_decode's."""
+    return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
+                   softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
+                   stream, validate)
+
+
+def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
+            num_splits, out, lse, workspace, return_lse, stream, validate):
+    if scales is None:
+        _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
+    else:
+        _need_fp8_dtype(k_pool, "k_pool")
+        _need_fp8_dtype(v_pool, "v_pool")
+    _dtypes((q, "q", torch.bfloat16), (block_tables, "block_tables", torch.int32),
             (seq_lens, "seq_lens", torch.int32), (out, "out", torch.bfloat16),
             (lse, "lse", torch.float32))
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, None)
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    if scales is None:
+        _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+        _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    else:
+        _need_fp8_pool(k_pool, "k_pool", dev)
+        _need_fp8_pool(v_pool, "v_pool", dev)
     _need(block_tables, "block_tables", torch.int32, 2, dev)
     _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, Hq, D = q.shape
@@ -214,11 +301,14 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    head = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
+    tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
-        _check(lib.paged_attn_decode(
-            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-            _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale),
-            int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream)))
+        if scales is None:
+            _check(lib.paged_attn_decode(*head, *tail))
+        else:
+            _check(lib.paged_attn_decode_fp8(*head, scales[0], scales[1], *tail))
     return (out, lse) if return_lse else out
 
 

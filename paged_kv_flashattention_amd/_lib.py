@@ -22,11 +22,18 @@ c_float = ctypes.c_float
 SIGNATURES = {
     "kv_page_write": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "kv_page_write_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                  c_float, c_float, c_vp]),
     "paged_attn_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
     "paged_attn_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "paged_attn_decode": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                   c_float, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "paged_attn_decode_fp8": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                      c_float, c_float, c_float, c_i32, c_i32, c_vp, c_size,
+                                      c_vp]),
     "paged_attn_decode_partials": (c_i32, [c_fp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_float, c_i32, c_i32, c_vp]),

@@ -69,6 +69,10 @@ int32_t resolve_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t num_
   return num_splits < 1 ? 1 : num_splits;
 }
 
+bool scales_ok(float k_scale, float v_scale) {
+  return k_scale > 0.f && k_scale <= 3.0e38f && v_scale > 0.f && v_scale <= 3.0e38f;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-K workspace: fp32 partial outputs [B, Hq, S, D] then fp32 partial lse
@@ -85,7 +89,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
-                int32_t num_splits) {
+                int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
+                float v_scale = 1.f) {
   if (B < 0 || max_seq_len < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
@@ -98,6 +103,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   }
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
+  if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
+    return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
   const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   a = pa::DecodeArgs{};
@@ -111,10 +118,106 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.ps_shift = log2_exact(page_size);
   a.S = S;
   a.part_len = ((chunks + S - 1) / S) * kChunk;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  // FP8 pools: scores use the codes, so k_scale folds into the softmax scale and
+  // v_scale into the final normalisation
+  a.scale_log2 = softmax_scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.v_scale = fp8 ? v_scale : 1.f;
   return PA_OK;
 }
 
+
+// Checks and launch shared by the bf16 and FP8 page writes.
+int kv_write_impl(const char* what, void* k_pool, void* v_pool, const void* k_new,
+                  const void* v_new, const int32_t* cu_new, const int32_t* start_pos,
+                  const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
+                  int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D, bool fp8,
+                  float k_scale, float v_scale, void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || T < 0) return fail(PA_ERR_SHAPE, "%s: B=%d T=%d must be >= 0", what, B, T);
+  if (fp8 && !scales_ok(k_scale, v_scale))
+    return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
+  if (B == 0 || T == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
+    return PA_OK;
+  }
+  int st = check_pool(B, max_pages, num_pages, page_size, Hkv, Hkv, D);
+  if (st) return st;
+  if (!k_pool || !v_pool || !k_new || !v_new || !cu_new || !start_pos || !block_tables)
+    return fail(PA_ERR_NULL, "%s: a required pointer is NULL", what);
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_MISALIGNED, "%s: data pointers must be 16-byte aligned", what);
+  pa::KvWriteArgs a{};
+  a.k_pool = static_cast<uint16_t*>(k_pool);
+  a.v_pool = static_cast<uint16_t*>(v_pool);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.cu_new = cu_new;
+  a.start_pos = start_pos;
+  a.block_tables = block_tables;
+  a.B = B; a.T = T; a.max_pages = max_pages; a.num_pages = num_pages;
+  a.page_size = page_size; a.ps_shift = log2_exact(page_size); a.Hkv = Hkv; a.D = D;
+  a.fp8 = fp8 ? 1 : 0;
+  // the reciprocal is taken once, in float32, as the quantiser's definition does
+  a.k_inv = fp8 ? 1.0f / k_scale : 1.f;
+  a.v_inv = fp8 ? 1.0f / v_scale : 1.f;
+  hipError_t e = pa::launch_kv_write(a, static_cast<hipStream_t>(stream), g_last_launch,
+                                     sizeof(g_last_launch));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
+// Checks, workspace carving and the partition + reduce launches shared by the
+// bf16 and FP8 decode entry points.
+int decode_impl(const char* what, void* out, float* lse_out, const void* q, const void* k_pool,
+                const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
+                int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
+                int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
+                float k_scale, float v_scale, void* stream) {
+  g_last_error[0] = 0;
+  pa::DecodeArgs a;
+  int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
+                       num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                       num_splits, fp8, k_scale, v_scale);
+  if (st) return st;
+  if (B == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
+    return PA_OK;
+  }
+  if (!out) return fail(PA_ERR_NULL, "%s: out is NULL", what);
+  if (!aligned16(out)) return fail(PA_ERR_MISALIGNED, "%s: out must be 16-byte aligned", what);
+  const int32_t S = a.S;
+  const size_t need = workspace_for(B, Hq, D, S);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu",
+                what, need, S, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned16(workspace))
+    return fail(PA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", what);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  const size_t rows = (size_t)B * Hq * S;
+  if (S > 1) {
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + align256(rows * D * sizeof(float)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char d1[256], d2[256];
+  hipError_t e = pa::launch_decode(a, s, d1, sizeof(d1));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
+  if (S > 1) {
+    pa::ReduceArgs r{};
+    r.out = a.out; r.lse_out = lse_out; r.part_o = a.part_o; r.part_lse = a.part_lse;
+    r.R = B * Hq; r.S = S; r.D = D;
+    e = pa::launch_reduce(r, s, d2, sizeof(d2));
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s; %s", d1, d2);
+  } else {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s", d1);
+  }
+  return PA_OK;
+}
 
 }  // namespace
 
@@ -141,32 +244,43 @@ int kv_page_write(void* k_pool, void* v_pool, const void* k_new, const void* v_n
                   const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
                   int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
                   void* stream) {
-  g_last_error[0] = 0;
-  if (B < 0 || T < 0) return fail(PA_ERR_SHAPE, "B=%d T=%d must be >= 0", B, T);
-  if (B == 0 || T == 0) {
-    snprintf(g_last_launch, sizeof(g_last_launch), "kv_page_write: nothing to do");
-    return PA_OK;
-  }
-  int st = check_pool(B, max_pages, num_pages, page_size, Hkv, Hkv, D);
-  if (st) return st;
-  if (!k_pool || !v_pool || !k_new || !v_new || !cu_new || !start_pos || !block_tables)
-    return fail(PA_ERR_NULL, "kv_page_write: a required pointer is NULL");
-  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
-    return fail(PA_ERR_MISALIGNED, "kv_page_write: data pointers must be 16-byte aligned");
-  pa::KvWriteArgs a{};
-  a.k_pool = static_cast<uint16_t*>(k_pool);
-  a.v_pool = static_cast<uint16_t*>(v_pool);
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.cu_new = cu_new;
-  a.start_pos = start_pos;
-  a.block_tables = block_tables;
-  a.B = B; a.T = T; a.max_pages = max_pages; a.num_pages = num_pages;
-  a.page_size = page_size; a.ps_shift = log2_exact(page_size); a.Hkv = Hkv; a.D = D;
-  hipError_t e = pa::launch_kv_write(a, static_cast<hipStream_t>(stream), g_last_launch,
-                                     sizeof(g_last_launch));
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "kv_page_write launch: %s", hipGetErrorString(e));
-  return PA_OK;
+  return kv_write_impl("kv_page_write", k_pool, v_pool, k_new, v_new, cu_new, start_pos,
+                       block_tables, B, T, max_pages, num_pages, page_size, Hkv, D, false, 1.f,
+                       1.f, stream);
+}
+
+int kv_page_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                      const int32_t* cu_new, const int32_t* start_pos,
+                      const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
+                      int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
+                      float k_scale, float v_scale, void* stream) {
+  return kv_write_impl("kv_page_write_fp8", k_pool, v_pool, k_new, v_new, cu_new, start_pos,
+                       block_tables, B, T, max_pages, num_pages, page_size, Hkv, D, true,
+                       k_scale, v_scale, stream);
+}
+
+int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                      int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                      int32_t D, float softmax_scale, int32_t max_seq_len,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl("decode", out, lse_out, q, k_pool, v_pool, block_tables, seq_lens, B,
+                     max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                     num_splits, workspace, workspace_bytes, false, 1.f, 1.f, stream);
+}
+
+int paged_attn_decode_fp8(void* out, float* lse_out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                          int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                          int32_t D, float softmax_scale, float k_scale, float v_scale,
+                          int32_t max_seq_len, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_impl("decode_fp8", out, lse_out, q, k_pool, v_pool, block_tables, seq_lens, B,
+                     max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                     num_splits, workspace, workspace_bytes, true, k_scale, v_scale, stream);
 }
 
 int32_t paged_attn_decode_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len) {
@@ -202,57 +316,6 @@ int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out
   hipError_t e = pa::launch_reduce(r, static_cast<hipStream_t>(stream), g_last_launch,
                                    sizeof(g_last_launch));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "splitk_reduce launch: %s", hipGetErrorString(e));
-  return PA_OK;
-}
-
-int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
-                      const void* v_pool, const int32_t* block_tables,
-                      const int32_t* seq_lens, int32_t B, int32_t max_pages,
-                      int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
-                      int32_t D, float softmax_scale, int32_t max_seq_len,
-                      int32_t num_splits, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  g_last_error[0] = 0;
-  pa::DecodeArgs a;
-  int st = decode_args(a, "decode", q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
-                       num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
-                       num_splits);
-  if (st) return st;
-  if (B == 0) {
-    snprintf(g_last_launch, sizeof(g_last_launch), "decode: nothing to do");
-    return PA_OK;
-  }
-  if (!out) return fail(PA_ERR_NULL, "decode: out is NULL");
-  if (!aligned16(out)) return fail(PA_ERR_MISALIGNED, "decode: out must be 16-byte aligned");
-  const int32_t S = a.S;
-  const size_t need = workspace_for(B, Hq, D, S);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(PA_ERR_WORKSPACE, "decode: workspace of %zu bytes needed for %d splits, got %zu",
-                need, S, workspace ? workspace_bytes : (size_t)0);
-  if (need && !aligned16(workspace))
-    return fail(PA_ERR_MISALIGNED, "decode: workspace must be 16-byte aligned");
-  a.out = static_cast<uint16_t*>(out);
-  a.lse_out = lse_out;
-  const size_t rows = (size_t)B * Hq * S;
-  if (S > 1) {
-    char* ws = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(ws);
-    a.part_lse = reinterpret_cast<float*>(ws + align256(rows * D * sizeof(float)));
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char d1[256], d2[256];
-  hipError_t e = pa::launch_decode(a, s, d1, sizeof(d1));
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
-  if (S > 1) {
-    pa::ReduceArgs r{};
-    r.out = a.out; r.lse_out = lse_out; r.part_o = a.part_o; r.part_lse = a.part_lse;
-    r.R = B * Hq; r.S = S; r.D = D;
-    e = pa::launch_reduce(r, s, d2, sizeof(d2));
-    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch: %s", hipGetErrorString(e));
-    snprintf(g_last_launch, sizeof(g_last_launch), "%s; %s", d1, d2);
-  } else {
-    snprintf(g_last_launch, sizeof(g_last_launch), "%s", d1);
-  }
   return PA_OK;
 }
 

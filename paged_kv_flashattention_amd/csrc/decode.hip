@@ -50,6 +50,59 @@ struct KRows {
   u32x4 r[NI];
 };
 
+// FP8 pools: a row is D bytes, read 16 bytes (16 codes) per lane, RPI8 rows per
+// instruction; the codes are widened to bf16 (exactly: every E4M3 value is a bf16
+// value) on their way into the same LDS tile.
+template <int D>
+struct KRows8 {
+  static constexpr int LPR = D / 16;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int NI = 32 / RPI;
+};
+
+template <int D>
+__device__ __forceinline__ void decode_load_k_rows8(KRows<D>& k, const uint8_t* kbase, int pg0,
+                                                    int pg1, int c0, const DecodeArgs& a,
+                                                    int lane) {
+  using R = KRows8<D>;
+  const int psm = a.page_size - 1;
+  const int rs = a.Hkv * D;
+  const size_t page_elems = (size_t)a.page_size * rs;
+  const int sub = lane / R::LPR;
+  const int off = (lane % R::LPR) * 16;
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const int row = R::RPI * i + sub;
+    const int pg = row < 16 ? pg0 : pg1;
+    k.r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        kbase + (size_t)pg * page_elems + ((c0 + row) & psm) * rs + off));
+  }
+}
+
+// four E4M3 codes (bytes 0..3) -> two packed bf16 pairs (bytes 0,1 and 2,3)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
+  return u32x2{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+template <int D>
+__device__ __forceinline__ void decode_k8_to_lds(const KRows<D>& k, uint16_t* kl, int lane) {
+  using R = KRows8<D>;
+  const int sub = lane / R::LPR;
+  const int off = (lane % R::LPR) * 16;
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const u32x2 w0 = fp8x4_to_bf16(k.r[i][0]), w1 = fp8x4_to_bf16(k.r[i][1]);
+    const u32x2 w2 = fp8x4_to_bf16(k.r[i][2]), w3 = fp8x4_to_bf16(k.r[i][3]);
+    const u32x4 a = {w0[0], w0[1], w1[0], w1[1]};
+    const u32x4 b = {w2[0], w2[1], w3[0], w3[1]};
+    uint16_t* p = kl + (R::RPI * i + sub) * KRows<D>::LROW + off;
+    *reinterpret_cast<u32x4*>(p) = a;
+    *reinterpret_cast<u32x4*>(p + 8) = b;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void decode_load_k_rows(KRows<D>& k, const uint16_t* kbase, int pg0,
                                                    int pg1, int c0, const DecodeArgs& a,
@@ -121,7 +174,39 @@ __device__ __forceinline__ void decode_load_v(DecodeChunk<D>& c, const uint16_t*
   }
 }
 
-template <int D, int W>
+// FP8 V: the lane's D/16 codes of each of its 8 key rows, widened to bf16 pairs
+// in the layout decode_load_v produces.
+template <int D>
+__device__ __forceinline__ void decode_load_v8(DecodeChunk<D>& c, const uint8_t* vbase,
+                                               int pg0, int pg1, int c0, const DecodeArgs& a,
+                                               int n, int g) {
+  constexpr int DPL = D / 16;
+  const int psm = a.page_size - 1;
+  const int rs = a.Hkv * D;
+  const size_t page_elems = (size_t)a.page_size * rs;
+  const uint8_t* va = vbase + (size_t)pg0 * page_elems + ((c0 + 4 * g) & psm) * rs + DPL * n;
+  const uint8_t* vb = vbase + (size_t)pg1 * page_elems + ((c0 + 16 + 4 * g) & psm) * rs +
+                      DPL * n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (D == 128) {
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(va + i * rs));
+      const u32x2 y = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + i * rs));
+      const u32x2 x0 = fp8x4_to_bf16(x[0]), x1 = fp8x4_to_bf16(x[1]);
+      const u32x2 y0 = fp8x4_to_bf16(y[0]), y1 = fp8x4_to_bf16(y[1]);
+      c.v[i][0] = x0[0]; c.v[i][1] = x0[1]; c.v[i][2] = x1[0]; c.v[i][3] = x1[1];
+      c.v[4 + i][0] = y0[0]; c.v[4 + i][1] = y0[1]; c.v[4 + i][2] = y1[0]; c.v[4 + i][3] = y1[1];
+    } else {
+      const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(va + i * rs));
+      const uint32_t y = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vb + i * rs));
+      const u32x2 x0 = fp8x4_to_bf16(x), y0 = fp8x4_to_bf16(y);
+      c.v[i][0] = x0[0]; c.v[i][1] = x0[1];
+      c.v[4 + i][0] = y0[0]; c.v[4 + i][1] = y0[1];
+    }
+  }
+}
+
+template <int D, int W, bool F8>
 __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) {
   constexpr int DPL = D / 16;   // d values per lane per V row = MFMA d-tiles
   const int lane = threadIdx.x & 63;
@@ -142,6 +227,16 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
   const uint16_t* kbase = a.k_pool + (size_t)kvh * D;
   const uint16_t* vbase = a.v_pool + (size_t)kvh * D;
+  const uint8_t* kbase8 = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * D;
+  const uint8_t* vbase8 = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * D;
+  auto load_k = [&](KRows<D>& kr, int p0, int p1, int c0) {
+    if constexpr (F8) decode_load_k_rows8<D>(kr, kbase8, p0, p1, c0, a, lane);
+    else decode_load_k_rows<D>(kr, kbase, p0, p1, c0, a, lane);
+  };
+  auto load_v = [&](DecodeChunk<D>& ch, int p0, int p1, int c0) {
+    if constexpr (F8) decode_load_v8<D>(ch, vbase8, p0, p1, c0, a, n, g);
+    else decode_load_v<D>(ch, vbase, p0, p1, c0, a, n, g);
+  };
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[head n][D/4 * g + 8 kk + j].
   const bool head_ok = n < a.G;
@@ -190,10 +285,10 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     {
       const int c0 = k_begin + 32 * c;
       const int p0 = page(c0), p1 = page(c0 + 16);
-      decode_load_k_rows<D>(kr, kbase, p0, p1, c0, a, lane);
+      load_k(kr, p0, p1, c0);
       // K before V: the first scores then wait only for the K loads
       __builtin_amdgcn_sched_barrier(0);
-      decode_load_v<D>(ch, vbase, p0, p1, c0, a, n, g);
+      load_v(ch, p0, p1, c0);
     }
     for (; c < c_end; ++c) {
       const int c0 = k_begin + 32 * c;
@@ -202,8 +297,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       const int pn1 = page(c0n + 16);
 
       // this chunk's K rows -> LDS; the next chunk's K loads reuse the registers
-      decode_k_to_lds<D>(kr, k_lds, lane);
-      decode_load_k_rows<D>(kr, kbase, pn0, pn1, c0n, a, lane);
+      if constexpr (F8) decode_k8_to_lds<D>(kr, k_lds, lane);
+      else decode_k_to_lds<D>(kr, k_lds, lane);
+      load_k(kr, pn0, pn1, c0n);
       decode_k_from_lds<D>(ch, k_lds, n, g);
       f32x4 sa = {0.f, 0.f, 0.f, 0.f};
       f32x4 sb = {0.f, 0.f, 0.f, 0.f};
@@ -262,7 +358,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
         }
         acc[t] = mfma16x16x32(va, pb, acc[t]);
       }
-      decode_load_v<D>(ch, vbase, pn0, pn1, c0n, a, n, g);
+      load_v(ch, pn0, pn1, c0n);
     }
   }
 
@@ -304,7 +400,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   }
 
   const bool live = l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
+  const float inv = live ? a.v_scale / l_tot : 0.f;
   const float lse = live ? (m_fin + __log2f(l_tot)) * kLn2 : kNegInf;
   // lane holds d = DPL * (4 g + i) + t for i = 0..3, t = 0..DPL-1, i.e. the
   // DPL * 4 consecutive values starting at d = DPL * 4 * g
@@ -353,7 +449,10 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
 template <int D, int W>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.Hkv, a.S, a.B);
-  hipLaunchKernelGGL((decode_partition_kernel<D, W>), grid, dim3(64 * W), 0, stream, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((decode_partition_kernel<D, W, true>), grid, dim3(64 * W), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, W, false>), grid, dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -377,8 +476,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, si
   const int W = decode_waves(a);
   hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W) : launch_decode_d<64>(a, stream, W);
   snprintf(desc, desc_len,
-           "decode_partition<D=%d,W=%d> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
-           W, a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
+           "decode_partition<D=%d,W=%d,%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
+           W, a.kv_fp8 ? "fp8-e4m3" : "bf16", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
   return e;
 }
 

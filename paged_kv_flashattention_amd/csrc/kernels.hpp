@@ -21,7 +21,9 @@ struct DecodeArgs {
   int B, Hq, Hkv, G, D;
   int max_pages, num_pages, page_size, ps_shift;
   int part_len, S;
-  float scale_log2;              // softmax scale * log2(e)
+  float scale_log2;              // softmax scale * log2(e) (* k_scale for FP8 pools)
+  int kv_fp8;                    // pools hold FP8 E4M3 codes (uint8) instead of bf16
+  float v_scale;                 // value of one V code unit (1 for bf16 pools)
 };
 
 struct ReduceArgs {
@@ -41,6 +43,8 @@ struct KvWriteArgs {
   const int32_t* start_pos;      // [B]
   const int32_t* block_tables;   // [B, max_pages]
   int B, T, max_pages, num_pages, page_size, ps_shift, Hkv, D;
+  int fp8;                       // quantise into FP8 E4M3 pools (uint8 codes)
+  float k_inv, v_inv;            // 1 / k_scale, 1 / v_scale (float32)
 };
 
 struct PrefillArgs {

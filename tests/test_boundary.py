@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ["kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
-              "paged_attn_prefill_varlen", "paged_attn_decode_workspace_bytes",
+              "paged_attn_prefill_varlen", "kv_page_write_fp8", "paged_attn_decode_fp8", "paged_attn_decode_workspace_bytes",
               "paged_attn_decode_num_splits", "pa_status_string", "pa_last_error",
               "pa_describe_launch"]:
         assert n in names
@@ -130,6 +130,46 @@ def test_prefill_and_write_reject_invalid_arguments(lib):
     assert r(None, None, FAKE, FAKE, 4, 2, 128, None) == 1
 
 
+def decode_fp8_call(lib, ks=0.01, vs=0.02, **over):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, B=2,
+                max_pages=4, num_pages=8, ps=16, Hq=8, Hkv=2, D=128, scale=0.1, max_seq=64,
+                S=1, ws=None, ws_bytes=0)
+    args.update(over)
+    return lib.paged_attn_decode_fp8(args["out"], args["lse"], args["q"], args["k"], args["v"],
+                                     args["bt"], args["lens"], args["B"], args["max_pages"],
+                                     args["num_pages"], args["ps"], args["Hq"], args["Hkv"],
+                                     args["D"], args["scale"], ks, vs, args["max_seq"],
+                                     args["S"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("ks,vs,over,status", [
+    (0.0, 0.02, {}, 2),
+    (0.01, -1.0, {}, 2),
+    (float("nan"), 0.02, {}, 2),
+    (0.01, float("inf"), {}, 2),
+    (3.0e38, 0.02, dict(scale=10.0), 2),        # softmax_scale * k_scale overflows
+    (0.01, 0.02, dict(k=None), 1),
+    (0.01, 0.02, dict(D=96), 3),
+    (0.01, 0.02, dict(v=FAKE + 4), 4),
+    (0.01, 0.02, dict(S=4, ws=FAKE, ws_bytes=16), 5),
+])
+def test_decode_fp8_rejects_invalid_arguments(lib, ks, vs, over, status):
+    assert decode_fp8_call(lib, ks, vs, **over) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_write_fp8_rejects_invalid_arguments(lib):
+    w = lib.kv_page_write_fp8
+    wb = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 8, 16, 2, 128, 0.5, 0.25, None]
+    for i, v, st in [(14, 0.0, 2), (15, float("nan"), 2), (15, -2.0, 2), (14, float("inf"), 2),
+                     (4, None, 1), (11, 8, 3), (1, FAKE + 8, 4)]:
+        bad = list(wb); bad[i] = v
+        assert w(*bad) == st, (i, v)
+    bad = list(wb); bad[8] = 0
+    assert w(*bad) == 0          # nothing to write
+    assert b"nothing" in lib.pa_describe_launch()
+
+
 def test_binding_refuses_wrong_dtypes_before_any_device_work():
     import paged_kv_flashattention_amd as pa
     q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
@@ -144,6 +184,19 @@ def test_binding_refuses_wrong_dtypes_before_any_device_work():
         pa.paged_attn_prefill_varlen(q, kp.float(), kp, lens, lens, bt64.int(), 0.1)
     with pytest.raises(ValueError):      # a CPU tensor is refused, never computed on
         pa.paged_attn_decode(q, kp, kp, bt64.int(), lens, 0.1)
+    with pytest.raises(TypeError):       # FP8 entry points take code pools only
+        pa.paged_attn_decode_fp8(q, kp, kp, bt64.int(), lens, 0.1, 0.01, 0.01)
+    k8 = torch.zeros(4, 16, 2, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):      # scales are checked before anything else runs
+        pa.paged_attn_decode_fp8(q, k8, k8, bt64.int(), lens, 0.1, 0.0, 0.01)
+    with pytest.raises(ValueError):
+        pa.paged_attn_decode_fp8(q, k8, k8, bt64.int(), lens, 0.1, 0.01, 0.01)   # CPU pools
+    kn = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    cu = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        pa.kv_page_write_fp8(kp, kp, kn, kn, cu, lens, bt64.int(), 0.1, 0.1)
+    with pytest.raises(TypeError):
+        pa.kv_page_write_fp8(k8, k8, kn.float(), kn, cu, lens, bt64.int(), 0.1, 0.1)
 
 
 @pytest.mark.gpu

@@ -36,7 +36,7 @@ import numpy as np
 import torch
 
 __all__ = ["PagedCase", "make_case", "make_config", "CONFIGS", "CONFIG_ORDER",
-           "bits", "units"]
+           "bits", "units", "random_e4m3_codes"]
 
 BF16_NAN_BITS = 0x7FC0
 TAIL_POISON = 3.0e4
@@ -123,6 +123,22 @@ def _randn_bf16(shape, std, gen, device, chunk_rows=None):
         out[r:r + n].copy_(torch.randn((n,) + tuple(shape[1:]), generator=gen, device=device,
                                        dtype=torch.float32) * std)
     return out
+
+
+def random_e4m3_codes(shape, seed: int, device="cpu", exp_lo: int = 4,
+                      exp_hi: int = 10) -> torch.Tensor:
+    """Seeded random bytes shaped like FP8 E4M3 codes, as uint8: a random sign bit,
+    a 4-bit exponent field drawn uniformly from [exp_lo, exp_hi] and a random 3-bit
+    mantissa field.  With the default window every code is a finite normal number
+    and none is a NaN code (those need the exponent field 15).  Used for FP8 pools
+    too large to build from float data on the host."""
+    if not (0 <= exp_lo <= exp_hi <= 14):
+        raise ValueError("exponent window must lie in [0, 14]")
+    gen = torch.Generator(device=device).manual_seed(seed)
+    e = torch.randint(exp_lo, exp_hi + 1, shape, generator=gen, device=device, dtype=torch.int32)
+    m = torch.randint(0, 8, shape, generator=gen, device=device, dtype=torch.int32)
+    s = torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int32)
+    return ((s << 7) | (e << 3) | m).to(torch.uint8)
 
 
 def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=None,
