@@ -7,7 +7,8 @@ Hkv 4, D 128, page size 16) -- the paged split-K decode plus its merge, inputs
 resident in HBM.  Value = algorithmic KV-read GB/s (every attended K and V
 element once per KV head, plus Q, O, used table entries and lengths).  Several
 copies of the pools are rotated so that no step finds its KV in the 256 MiB
-last-level cache.  Secondary lines (same JSON object): dense causal prefill
+last-level cache.  Secondary lines (same JSON object): the same decode over
+FP8 E4M3 pools (bytes counted at one per K/V element), dense causal prefill
 TFLOP/s (4 x 4096, Hq 32, Hkv 8), long-context decode (8 x 131072), and the
 mixed ragged step, each timed the same way.
 
@@ -42,7 +43,7 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen7b_decode",
-                   choices=["qwen7b_decode", "long_decode", "causal_prefill", "mixed_ragged",
+                   choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_decode", "causal_prefill", "mixed_ragged",
                             "tiny_decode"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -114,6 +115,48 @@ class DecodeStep:
         return {"workload": c.name, "batch": c.B, "context": c.max_seq_len, "Hq": c.Hq,
                 "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size,
                 "num_splits": self.S, "pool_copies_rotated": len(self.kv)}
+
+
+class Fp8DecodeStep(DecodeStep):
+    """The same decode over FP8 E4M3 pools: seeded random codes of the same shape
+    (one byte per element), per-pool scales, rotated copies as above."""
+
+    K_SCALE, V_SCALE = 0.02, 0.05
+
+    def __init__(self, name, copies, num_splits=0):
+        super().__init__(name, 1, num_splits)
+        from workloads import random_e4m3_codes, units
+        c = self.case
+        shape = tuple(c.k_pool.shape)
+        c.k_pool = c.v_pool = None
+        self.kv = [(random_e4m3_codes(shape, 8000 + 2 * i, "cuda"),
+                    random_e4m3_codes(shape, 8001 + 2 * i, "cuda")) for i in range(copies)]
+        self.units = units.decode_bytes(c.seq_lens, c.Hq, c.Hkv, c.D, c.page_size,
+                                        kv_elem_bytes=1)
+
+    def __call__(self):
+        c = self.case
+        kp, vp = self.kv[self.i % len(self.kv)]
+        self.i += 1
+        self.pa.paged_attn_decode_fp8(c.q, kp, vp, c.block_tables, c.seq_lens_k, c.scale,
+                                      self.K_SCALE, self.V_SCALE, max_seq_len=c.max_seq_len,
+                                      num_splits=self.S, out=self.out, workspace=self.ws)
+
+    def dominant_kernel_ms(self, launches):
+        """No partials-only entry point exists for FP8 pools: time whole calls
+        (partition kernel plus the few-microsecond merge)."""
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(launches):
+            self()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / launches
+
+    def config(self):
+        return dict(super().config(), kv_format="fp8-e4m3")
 
 
 class PrefillStep:
@@ -215,6 +258,8 @@ class MixedStep:
 
 
 def make_step(name, num_splits=0):
+    if name == "qwen7b_decode_fp8":
+        return Fp8DecodeStep("qwen7b_decode", copies=3, num_splits=num_splits)
     if name == "qwen7b_decode":
         return DecodeStep(name, copies=3, num_splits=num_splits)
     if name == "long_decode":
@@ -325,7 +370,7 @@ def cpu_baseline(step, min_s=10.0, budget_s=15.0):
     except Exception:
         cores = 1
     c = step.case
-    if not isinstance(step, DecodeStep):
+    if not isinstance(step, DecodeStep) or isinstance(step, Fp8DecodeStep):
         return None
     import torch
     bt = c.block_tables.cpu().numpy()
@@ -416,7 +461,8 @@ def main():
         # the other workloads, same timing; the long-context decode both with the 64
         # partitions it is stated with and with the library's own split choice
         extra = {}
-        for label, name, splits in (("causal_prefill", "causal_prefill", 0),
+        for label, name, splits in (("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
+                                    ("causal_prefill", "causal_prefill", 0),
                                     ("long_decode", "long_decode", 64),
                                     ("long_decode_auto_splits", "long_decode", -1),
                                     ("mixed_ragged", "mixed_ragged", 0)):

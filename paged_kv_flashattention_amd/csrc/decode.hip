@@ -35,6 +35,7 @@ struct DecodeChunk {
   u32x4 ka[D / 32];          // K row (chunk key l%16), d in [D/4 * g, D/4 * (g+1))
   u32x4 kb[D / 32];          // K row (chunk key 16 + l%16), same d range
   uint32_t v[8][D / 32];     // V rows of the lane's 8 keys, d in [D/16 * n, D/16 * (n+1))
+  uint32_t v8[8][D / 64];    // FP8 pools: the same values as raw E4M3 codes
 };
 
 // K of a chunk in whole-row order: instruction i covers rows RPI*i .. RPI*i+RPI-1
@@ -174,8 +175,9 @@ __device__ __forceinline__ void decode_load_v(DecodeChunk<D>& c, const uint16_t*
   }
 }
 
-// FP8 V: the lane's D/16 codes of each of its 8 key rows, widened to bf16 pairs
-// in the layout decode_load_v produces.
+// FP8 V: the lane's D/16 codes of each of its 8 key rows, kept as codes until
+// P V needs them (widening them here would make the wave wait for the loads at
+// once instead of one chunk later).
 template <int D>
 __device__ __forceinline__ void decode_load_v8(DecodeChunk<D>& c, const uint8_t* vbase,
                                                int pg0, int pg1, int c0, const DecodeArgs& a,
@@ -192,18 +194,26 @@ __device__ __forceinline__ void decode_load_v8(DecodeChunk<D>& c, const uint8_t*
     if constexpr (D == 128) {
       const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(va + i * rs));
       const u32x2 y = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + i * rs));
-      const u32x2 x0 = fp8x4_to_bf16(x[0]), x1 = fp8x4_to_bf16(x[1]);
-      const u32x2 y0 = fp8x4_to_bf16(y[0]), y1 = fp8x4_to_bf16(y[1]);
-      c.v[i][0] = x0[0]; c.v[i][1] = x0[1]; c.v[i][2] = x1[0]; c.v[i][3] = x1[1];
-      c.v[4 + i][0] = y0[0]; c.v[4 + i][1] = y0[1]; c.v[4 + i][2] = y1[0]; c.v[4 + i][3] = y1[1];
+      c.v8[i][0] = x[0]; c.v8[i][1] = x[1];
+      c.v8[4 + i][0] = y[0]; c.v8[4 + i][1] = y[1];
     } else {
-      const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(va + i * rs));
-      const uint32_t y = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vb + i * rs));
-      const u32x2 x0 = fp8x4_to_bf16(x), y0 = fp8x4_to_bf16(y);
-      c.v[i][0] = x0[0]; c.v[i][1] = x0[1];
-      c.v[4 + i][0] = y0[0]; c.v[4 + i][1] = y0[1];
+      c.v8[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(va + i * rs));
+      c.v8[4 + i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vb + i * rs));
     }
   }
+}
+
+// The codes widened to bf16 pairs in the layout decode_load_v produces.
+template <int D>
+__device__ __forceinline__ void decode_widen_v8(DecodeChunk<D>& c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      const u32x2 r = fp8x4_to_bf16(c.v8[j][w]);
+      c.v[j][2 * w] = r[0];
+      c.v[j][2 * w + 1] = r[1];
+    }
 }
 
 template <int D, int W, bool F8>
@@ -308,6 +318,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
         sa = mfma16x16x32(ch.ka[kk], qb[kk], sa);
         sb = mfma16x16x32(ch.kb[kk], qb[kk], sb);
       }
+
+      if constexpr (F8) decode_widen_v8<D>(ch);
 
       float s[8];
 #pragma unroll
@@ -459,10 +471,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 // Waves per work-group: enough waves in the whole grid (about two per CU, 512 on
 // MI355X) and no more, so that each wave streams as long a run of keys as
 // possible (measured on MI355X: fewer, longer streams read HBM faster; one
-// wave per CU is too few).
+// wave per CU is too few).  A wave over FP8 pools moves half the bytes per chunk
+// for the same work, so it takes twice the waves (about four per CU) to keep as
+// many bytes in flight.
 static int decode_waves(const DecodeArgs& a) {
   const long long groups = (long long)a.Hkv * a.S * a.B;
-  return groups >= 512 ? 1 : (groups >= 256 ? 2 : 4);
+  const long long target = a.kv_fp8 ? 1024 : 512;
+  return groups >= target ? 1 : (2 * groups >= target ? 2 : 4);
 }
 
 template <int D>

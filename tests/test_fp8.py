@@ -146,8 +146,10 @@ DECODE = [
     ([0, 5, 0, 300], 32, 8, 128, 16, 3),
     ([200, 1000], 16, 1, 128, 64, 5),
     ([513, 77, 1], 7, 1, 64, 64, 0),
-    ([(37 * i) % 701 for i in range(64)], 16, 8, 128, 16, 1),     # one wave per work-group
-    ([(53 * i) % 509 for i in range(64)], 8, 8, 64, 16, 2),       # two waves per work-group
+    # FP8 pools take one wave per work-group from 1024 work-groups, two from 512
+    ([(37 * i) % 701 for i in range(64)], 16, 8, 128, 16, 1),     # 512: two waves
+    ([(37 * i) % 701 for i in range(64)], 16, 8, 128, 16, 2),     # 1024: one wave
+    ([(53 * i) % 509 for i in range(64)], 8, 8, 64, 16, 2),       # 1024: one wave, D 64
 ]
 
 

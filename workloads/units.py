@@ -17,7 +17,7 @@ The per-head figures that the inference guide's chapter 8, section
 
 from __future__ import annotations
 
-from typing import Sequence
+from typing import Optional, Sequence
 
 
 def kv_bytes_per_head(seq_len: int, head_dim: int, elem_bytes: int = 2) -> int:
@@ -36,10 +36,13 @@ def naive_attention_traffic(seq_len: int, elem_bytes: int = 2, passes: int = 3) 
 
 
 def decode_bytes(seq_lens: Sequence[int], Hq: int, Hkv: int, D: int, page_size: int,
-                 elem_bytes: int = 2) -> int:
-    """Algorithmic bytes of one decode call (one query row per sequence)."""
+                 elem_bytes: int = 2, kv_elem_bytes: Optional[int] = None) -> int:
+    """Algorithmic bytes of one decode call (one query row per sequence).  Q and O
+    take elem_bytes per element, the K/V pools kv_elem_bytes (1 for FP8 pools;
+    elem_bytes when not given)."""
     B = len(seq_lens)
-    kv = sum(kv_bytes_per_head(L, D, elem_bytes) * Hkv for L in seq_lens)
+    kvb = elem_bytes if kv_elem_bytes is None else kv_elem_bytes
+    kv = sum(kv_bytes_per_head(L, D, kvb) * Hkv for L in seq_lens)
     q = B * Hq * D * elem_bytes
     o = B * Hq * D * elem_bytes
     tables = sum(-(-L // page_size) for L in seq_lens) * 4
