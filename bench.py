@@ -9,8 +9,9 @@ element once per KV head, plus Q, O, used table entries and lengths).  Several
 copies of the pools are rotated so that no step finds its KV in the 256 MiB
 last-level cache.  Secondary lines (same JSON object): the same decode over
 FP8 E4M3 pools (bytes counted at one per K/V element), dense causal prefill
-TFLOP/s (4 x 4096, Hq 32, Hkv 8), long-context decode (8 x 131072), and the
-mixed ragged step, each timed the same way.
+TFLOP/s (4 x 4096, Hq 32, Hkv 8), long-context decode (8 x 131072), a 512-token
+prefill chunk over a 32,768-token history (key-split prefill), and the mixed
+ragged step, each timed the same way.
 
 One JSON line is printed.  Only one GPU is used: --gpus above 1 is refused.
 """
@@ -43,7 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen7b_decode",
-                   choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_decode", "causal_prefill", "mixed_ragged",
+                   choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
+                            "long_decode", "causal_prefill", "mixed_ragged",
                             "tiny_decode"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,9 +162,11 @@ class Fp8DecodeStep(DecodeStep):
 
 
 class PrefillStep:
-    """kv_page_write is done once at setup; each step is one prefill_varlen call."""
+    """kv_page_write is done once at setup; each step is one prefill_varlen call (with
+    `splitk`, one prefill_varlen_splitk call with the library's key-part count: the
+    prefill kernel, then the merge of the split tiles)."""
 
-    def __init__(self, name, copies=1):
+    def __init__(self, name, splitk=False):
         import torch
         import paged_kv_flashattention_amd as pa
         from workloads import make_config, units
@@ -173,9 +177,19 @@ class PrefillStep:
         self.out = torch.empty((c.T, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
         self.units = units.prefill_flops(c.seq_lens, c.q_lens, c.Hq, c.D, c.causal)
         self.unit_name = "TFLOP/s"
+        self.S = pa.prefill_num_splits(c.B, c.Hq, c.max_q_len) if splitk else 1
+        need = pa.prefill_workspace_bytes(c.B, c.T, c.max_q_len, c.Hq, c.D, self.S)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.splitk = splitk
 
     def __call__(self):
         c = self.case
+        if self.splitk:
+            self.pa.paged_attn_prefill_varlen_splitk(
+                c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
+                causal=True, max_q_len=c.max_q_len, num_splits=self.S, out=self.out,
+                workspace=self.ws)
+            return
         self.pa.paged_attn_prefill_varlen(c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k,
                                           c.block_tables, c.scale, causal=True,
                                           max_q_len=c.max_q_len, out=self.out)
@@ -194,8 +208,11 @@ class PrefillStep:
 
     def config(self):
         c = self.case
-        return {"workload": c.name, "batch": c.B, "q_len": c.max_q_len, "Hq": c.Hq,
-                "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size, "causal": True}
+        cfg = {"workload": c.name, "batch": c.B, "q_len": c.max_q_len, "Hq": c.Hq,
+               "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size, "causal": True}
+        if self.splitk:
+            cfg.update(history=max(c.seq_lens) - c.max_q_len, key_parts=self.S)
+        return cfg
 
 
 class MixedStep:
@@ -269,6 +286,8 @@ def make_step(name, num_splits=0):
         return DecodeStep(name, copies=1, num_splits=num_splits)
     if name == "causal_prefill":
         return PrefillStep(name)
+    if name == "long_history_chunk":
+        return PrefillStep(name, splitk=True)
     return MixedStep(name)
 
 
@@ -465,6 +484,7 @@ def main():
                                     ("causal_prefill", "causal_prefill", 0),
                                     ("long_decode", "long_decode", 64),
                                     ("long_decode_auto_splits", "long_decode", -1),
+                                    ("long_history_chunk", "long_history_chunk", 0),
                                     ("mixed_ragged", "mixed_ragged", 0)):
             if splits < 0:
                 from workloads import make_config

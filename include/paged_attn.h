@@ -263,6 +263,55 @@ int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const vo
                               int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
                               int32_t D, float softmax_scale, int32_t causal, void* stream);
 
+/*
+ * paged_attn_prefill_varlen_splitk -- paged_attn_prefill_varlen with long key
+ * ranges cut into parts, so that a batch whose sequences differ widely in length
+ * (a long history next to short ones) does not wait on a few long work-groups.
+ *
+ * Each query tile (R rows as above) of sequence b needs the keys up to its last
+ * row's position (all seq_lens_k[b] keys without causal): n tiles of 64 keys.
+ * With S = num_splits > 1 those tiles are cut into P = min(S, max(1, n / 16))
+ * parts of consecutive tiles (so a part spans at least 1,024 keys); each part is
+ * computed by its own work-group into the workspace (partial output and natural-log
+ * lse, as paged_attn_decode_partials does for decode), and a second kernel merges
+ * the parts of every split row exactly ("The Stack Below the Stack (Part 2)",
+ * section 2.2: the log-sum-exp merge is exact for any partition of the keys).
+ * Rows of tiles with P == 1 are written directly.  The result equals
+ * paged_attn_prefill_varlen's up to rounding; with S == 1 it is the same launch.
+ *
+ *   num_splits : S (at most 16), or <= 0 for paged_attn_prefill_num_splits()
+ *   workspace  : device buffer of at least paged_attn_prefill_workspace_bytes()
+ *                (may be NULL when that is 0); contents are scratch.  Calls that share
+ *                a workspace must not run concurrently.
+ * Every other argument and status is paged_attn_prefill_varlen's; the launch bound
+ * on work-items includes the factor S.
+ */
+int paged_attn_prefill_varlen_splitk(void* out, float* lse_out, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                     const int32_t* block_tables, int32_t B, int32_t Tq,
+                                     int32_t max_q_len, int32_t max_pages, int32_t num_pages,
+                                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                                     float softmax_scale, int32_t causal, int32_t num_splits,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_prefill_num_splits -- the key-part count paged_attn_prefill_varlen_splitk
+ * uses for num_splits <= 0: 1 while the launch fills every work-group slot of MI355X
+ * (256 CUs; one 256-row or two 128-row work-groups per CU), else enough parts for
+ * one work-group per slot, at most 8.  Depends only on host scalars.
+ */
+int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len);
+
+/*
+ * paged_attn_prefill_workspace_bytes -- workspace bytes of paged_attn_prefill_varlen_splitk
+ * for this shape and num_splits (after resolving num_splits <= 0 as above): fp32
+ * partial outputs [Tq * Hq, S, D] followed by fp32 partial lse [Tq * Hq, S], each
+ * region 256-byte aligned.  0 when S == 1.
+ */
+size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len, int32_t Hq,
+                                          int32_t D, int32_t num_splits);
+
 /* Human-readable name of a pa_status value (static string). */
 const char* pa_status_string(int status);
 

@@ -12,7 +12,9 @@ Entry points (same names as the C ABI):
 * :func:`paged_attn_decode_fp8` -- decode over FP8 E4M3 pools with per-pool scales;
 * :func:`paged_attn_decode_partials` -- decode's per-partition results only;
 * :func:`paged_attn_splitk_reduce` -- the merge on its own;
-* :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA.
+* :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA;
+* :func:`paged_attn_prefill_varlen_splitk` -- the same with long key ranges cut
+  into parts computed by separate work-groups and merged.
 
 Data contract: bf16 Q / K / V / outputs, int32 indices (int64 is refused, not
 cast), fp32 lse, contiguous tensors on one GPU.  FP8 pools are uint8 (or
@@ -33,7 +35,8 @@ __all__ = [
     "PagedAttnError", "kv_page_write", "kv_page_write_fp8", "paged_attn_decode",
     "paged_attn_decode_fp8", "paged_attn_decode_partials",
     "paged_attn_splitk_reduce",
-    "paged_attn_prefill_varlen", "decode_num_splits", "decode_workspace_bytes",
+    "paged_attn_prefill_varlen", "paged_attn_prefill_varlen_splitk", "prefill_num_splits",
+    "prefill_workspace_bytes", "decode_num_splits", "decode_workspace_bytes",
     "describe_launch", "library_path", "load_library",
 ]
 
@@ -384,6 +387,37 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
     omitted it is read from the device (a synchronisation).
     """
+    return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
+                    softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate)
+
+
+def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:
+    return int(load_library().paged_attn_prefill_num_splits(B, Hq, max_q_len))
+
+
+def prefill_workspace_bytes(B, Tq, max_q_len, Hq, D, num_splits=0) -> int:
+    """Workspace bytes for paged_attn_prefill_varlen_splitk (scratch)."""
+    return int(load_library().paged_attn_prefill_workspace_bytes(B, Tq, max_q_len, Hq, D,
+                                                                 num_splits))
+
+
+def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
+                                     softmax_scale: float, causal: bool = True,
+                                     max_q_len: Optional[int] = None, num_splits: int = 0,
+                                     out: Optional[torch.Tensor] = None,
+                                     lse: Optional[torch.Tensor] = None,
+                                     workspace: Optional[torch.Tensor] = None,
+                                     return_lse: bool = False, stream=None,
+                                     validate: bool = False):
+    """Ragged prefill with long key ranges cut into at most ``num_splits`` parts
+    (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C."""
+    return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
+                    block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
+                    validate)
+
+
+def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
+             causal, max_q_len, out, lse, return_lse, stream, validate):
     _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
             (v_pool, "v_pool", torch.bfloat16), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
             (seq_lens_k, "seq_lens_k", torch.int32), (block_tables, "block_tables", torch.int32),
@@ -419,9 +453,23 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
         lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2, dev)
-    with torch.cuda.device(dev):
-        _check(load_library().paged_attn_prefill_varlen(
-            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(cu_seqlens_q),
+    lib = load_library()
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(cu_seqlens_q),
             _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
-            P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0, _stream(stream)))
+            P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0)
+    if split is not None:
+        num_splits, workspace = split
+        need = int(lib.paged_attn_prefill_workspace_bytes(B, Tq, int(max_q_len), Hq, D,
+                                                          num_splits))
+        if workspace is not None:
+            _need(workspace, "workspace", torch.uint8, 1, dev)
+        elif need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel()
+    with torch.cuda.device(dev):
+        if split is None:
+            _check(lib.paged_attn_prefill_varlen(*args, _stream(stream)))
+        else:
+            _check(lib.paged_attn_prefill_varlen_splitk(*args, num_splits, _ptr(workspace),
+                                                        ws_bytes, _stream(stream)))
     return (out, lse) if return_lse else out

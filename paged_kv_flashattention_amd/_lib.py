@@ -41,6 +41,12 @@ SIGNATURES = {
     "paged_attn_prefill_varlen": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                           c_i32, c_i32, c_float, c_i32, c_vp]),
+    "paged_attn_prefill_varlen_splitk": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                 c_i32, c_i32, c_i32, c_float, c_i32, c_i32,
+                                                 c_vp, c_size, c_vp]),
+    "paged_attn_prefill_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
+    "paged_attn_prefill_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_status_string": (ctypes.c_char_p, [c_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_describe_launch": (ctypes.c_char_p, []),

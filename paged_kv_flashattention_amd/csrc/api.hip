@@ -219,6 +219,106 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
   return PA_OK;
 }
 
+constexpr int32_t kPrefillMaxSplits = 16;      // the merge kernel's part limit
+constexpr int kPrefillPartMinTiles = 16;       // 64-key tiles per key-range part at least
+
+// Key-range parts per prefill query tile when the caller passes num_splits <= 0:
+// none while the launch fills every work-group slot of the chip (256 CUs; one
+// 8-wave or two 4-wave work-groups per CU) -- measured on MI355X, splitting a
+// launch that already fills the chip gains less than the partial-result traffic
+// and the merge cost -- else enough parts for one work-group per slot, at most 8.
+int32_t resolve_prefill_splits(int32_t B, int32_t Hq, int32_t max_q_len, int32_t num_splits) {
+  if (num_splits > 0) return num_splits < kPrefillMaxSplits ? num_splits : kPrefillMaxSplits;
+  if (B <= 0 || Hq <= 0 || max_q_len <= 0) return 1;
+  const int W = pa::prefill_waves(max_q_len);
+  const long long n_qt = (max_q_len + 32 * W - 1) / (32 * W);
+  const long long wgs = (long long)Hq * B * n_qt;
+  const long long slots = 256ll * (8 / W);
+  if (wgs >= slots) return 1;
+  const long long s = (slots + wgs - 1) / wgs;
+  return (int32_t)(s < 8 ? s : 8);
+}
+
+// Key-split workspace: fp32 partial outputs [Tq * Hq, S, D], then fp32 partial lse
+// [Tq * Hq, S].
+size_t prefill_workspace_for(int32_t Tq, int32_t Hq, int32_t D, int32_t S) {
+  if (S <= 1 || Tq <= 0) return 0;
+  const size_t rows = (size_t)Tq * Hq * S;
+  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Checks and launches shared by the prefill entry points; S == 1 is the plain
+// one-pass prefill.
+int prefill_impl(const char* what, void* out, float* lse_out, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                 const int32_t* block_tables, int32_t B, int32_t Tq, int32_t max_q_len,
+                 int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
+                 int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || Tq < 0 || max_q_len < 0)
+    return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d", what, B, Tq, max_q_len);
+  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
+  if (st) return st;
+  if (B == 0 || Tq == 0 || max_q_len == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
+    return PA_OK;
+  }
+  if (!out || !q || !k_pool || !v_pool || !cu_seqlens_q || !seq_lens_k || !block_tables)
+    return fail(PA_ERR_NULL, "%s: a required pointer is NULL", what);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_MISALIGNED, "%s: data pointers must be 16-byte aligned", what);
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
+    return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
+  if (max_q_len > Tq) max_q_len = Tq;
+  const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits);
+  // one work-group per (query head, sequence, 128- or 256-row query tile, key
+  // part); the launch holds at most 2^32 - 1 work-items
+  if ((long long)Hq * B * ((max_q_len + 127) / 128 + 1) * 256 * S > 0xffffffffll)
+    return fail(PA_ERR_SHAPE, "%s: %d heads x %d sequences x %d query rows x %d key parts is "
+                "too many work-groups for one launch", what, Hq, B, max_q_len, S);
+  const size_t need = prefill_workspace_for(Tq, Hq, D, S);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d key parts, got %zu",
+                what, need, S, workspace ? workspace_bytes : (size_t)0);
+  if (need && !aligned16(workspace))
+    return fail(PA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", what);
+  pa::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens_k = seq_lens_k;
+  a.block_tables = block_tables;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  a.B = B; a.Tq = Tq; a.max_q_len = max_q_len; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.ps_shift = log2_exact(page_size);
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.S = S;
+  a.part_min = kPrefillPartMinTiles;
+  if (S > 1) {
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + align256((size_t)Tq * Hq * S * D * sizeof(float)));
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char d1[320], d2[256];
+  hipError_t e = pa::launch_prefill(a, hs, d1, sizeof(d1));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
+  if (S > 1) {
+    e = pa::launch_prefill_merge(a, hs, d2, sizeof(d2));
+    if (e != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "%s merge launch: %s", what, hipGetErrorString(e));
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s; %s", d1, d2);
+  } else {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s", d1);
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,45 +460,34 @@ int paged_attn_prefill_varlen(void* out, float* lse_out, const void* q, const vo
                               int32_t B, int32_t Tq, int32_t max_q_len, int32_t max_pages,
                               int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
                               int32_t D, float softmax_scale, int32_t causal, void* stream) {
-  g_last_error[0] = 0;
-  if (B < 0 || Tq < 0 || max_q_len < 0)
-    return fail(PA_ERR_SHAPE, "prefill: B=%d Tq=%d max_q_len=%d", B, Tq, max_q_len);
-  int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
-  if (st) return st;
-  if (B == 0 || Tq == 0 || max_q_len == 0) {
-    snprintf(g_last_launch, sizeof(g_last_launch), "prefill: nothing to do");
-    return PA_OK;
-  }
-  if (!out || !q || !k_pool || !v_pool || !cu_seqlens_q || !seq_lens_k || !block_tables)
-    return fail(PA_ERR_NULL, "prefill: a required pointer is NULL");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(PA_ERR_MISALIGNED, "prefill: data pointers must be 16-byte aligned");
-  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
-    return fail(PA_ERR_SHAPE, "prefill: softmax scale must be positive and finite");
+  return prefill_impl("prefill", out, lse_out, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
+                      block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
+                      D, softmax_scale, causal, 1, nullptr, 0, stream);
+}
+
+int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len) {
+  return resolve_prefill_splits(B, Hq, max_q_len, 0);
+}
+
+size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len, int32_t Hq,
+                                          int32_t D, int32_t num_splits) {
+  if (B <= 0 || Tq <= 0 || max_q_len <= 0 || Hq <= 0 || D <= 0) return 0;
   if (max_q_len > Tq) max_q_len = Tq;
-  // one work-group per (query head, sequence, 128- or 256-row query tile); the
-  // launch holds at most 2^32 - 1 work-items
-  if ((long long)Hq * B * ((max_q_len + 127) / 128 + 1) * 256 > 0xffffffffll)
-    return fail(PA_ERR_SHAPE, "prefill: %d heads x %d sequences x %d query rows is too many "
-                "work-groups for one launch", Hq, B, max_q_len);
-  pa::PrefillArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_pool = static_cast<const uint16_t*>(k_pool);
-  a.v_pool = static_cast<const uint16_t*>(v_pool);
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.seq_lens_k = seq_lens_k;
-  a.block_tables = block_tables;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse_out = lse_out;
-  a.B = B; a.Tq = Tq; a.max_q_len = max_q_len; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
-  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
-  a.ps_shift = log2_exact(page_size);
-  a.causal = causal ? 1 : 0;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_last_launch,
-                                    sizeof(g_last_launch));
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "prefill launch: %s", hipGetErrorString(e));
-  return PA_OK;
+  return prefill_workspace_for(Tq, Hq, D, resolve_prefill_splits(B, Hq, max_q_len, num_splits));
+}
+
+int paged_attn_prefill_varlen_splitk(void* out, float* lse_out, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                     const int32_t* block_tables, int32_t B, int32_t Tq,
+                                     int32_t max_q_len, int32_t max_pages, int32_t num_pages,
+                                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                                     float softmax_scale, int32_t causal, int32_t num_splits,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl("prefill_splitk", out, lse_out, q, k_pool, v_pool, cu_seqlens_q,
+                      seq_lens_k, block_tables, B, Tq, max_q_len, max_pages, num_pages,
+                      page_size, Hq, Hkv, D, softmax_scale, causal, num_splits, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -62,6 +62,10 @@ struct PrefillArgs {
   float scale_log2;
   int n_qt;                      // query tiles per sequence (of the longest)
   int xcd_groups;                // (sequence, KV head) groups per XCD, or 0: plain order
+  int S;                         // key-range parts per query tile at most (1: no split)
+  int part_min;                  // 64-key tiles per part at least
+  float* part_o;                 // [Tq * Hq, S, D] partial outputs        (S > 1)
+  float* part_lse;               // [Tq * Hq, S] partial natural-log lse   (S > 1)
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError() of the launch;
@@ -72,5 +76,10 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
                            size_t desc_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
                           size_t desc_len);
+// with S > 1: merges the rows whose query tile was split (after launch_prefill)
+hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream, char* desc,
+                                size_t desc_len);
+// waves per prefill work-group (32 query rows each) for the longest query run
+int prefill_waves(int max_q_len);
 
 }  // namespace pa

@@ -32,6 +32,28 @@ constexpr float kSumLimit = 256.f;     // 2^kRescaleSlack: bound on a lane's blo
 #define PF_W8_MIN 1024
 #endif
 
+// The key tiles a query tile needs and how many parts they are cut into.  A
+// query tile of rows r0 .. r0 + rows - 1 of a sequence with L keys and q_len query
+// rows needs keys 0 .. k_lim - 1 (causal: up to its last row's position).  With
+// key splitting on (S > 1) the n tiles are cut into min(S, n / part_min) parts of
+// consecutive tiles (at least one), each computed by its own work-group; the
+// prefill merge recomputes the same count for every row.
+struct PfTiles {
+  int n;       // 64-key tiles
+  int parts;   // key-range parts
+};
+
+__device__ __forceinline__ PfTiles pf_tiles(const PrefillArgs& a, int L, int q_len, int r0,
+                                            int bm) {
+  const int rows = min(bm, q_len - r0);
+  int k_lim = L;
+  if (a.causal) k_lim = min(L, max(0, L - q_len + r0 + rows));
+  PfTiles t;
+  t.n = (k_lim + kPfBN - 1) / kPfBN;
+  t.parts = a.S > 1 ? max(1, min(a.S, t.n / a.part_min)) : 1;
+  return t;
+}
+
 // LDS tiles of 64 keys.  Each wave's 16 rows (keys 16 w .. 16 w + 15, one run of
 // one page) form a region of 16 x D bf16 stored chunk-major: the 16-byte chunk c
 // (columns 8 c .. 8 c + 7) of the region's rows sits in the 256-byte line c, one
@@ -172,19 +194,22 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int col = lane & 31;         // query column of S^T / O^T
   const int hh = lane >> 5;          // k-half of the MFMA operands
   const int g16 = lane & 15;
-  // Work-group -> (query head h, sequence b, query tile qt).  Work-groups are
-  // handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2; with
+  // Work-group -> (query head h, sequence b, query tile qt, key part).  Work-groups
+  // are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2; with
   // xcd_groups set, every (sequence, KV head) group lives on one XCD, so its K/V
   // tiles are fetched into one L2 and shared there by the group's query heads and
-  // tiles.  Either way the heaviest query tiles (most keys) start first.
-  int h, b, qt;
+  // tiles.  Either way the heaviest query tiles (most keys) start first, all their
+  // key parts together, and every XCD keeps its share of the unsplit work.
+  int h, b, qt, part;
   {
     const int p = blockIdx.x;
     if (a.xcd_groups) {
       const int k = p >> 3;
-      const int level = a.xcd_groups * a.G;      // work-groups per query-tile level
-      const int rank = k / level;
-      const int rem = k - rank * level;
+      const int level = a.xcd_groups * a.G;      // work-groups per (tile level, part)
+      const int r2 = k / level;
+      const int rem = k - r2 * level;
+      const int rank = r2 / a.S;
+      part = r2 - rank * a.S;
       const int g = (p & 7) + 8 * (rem / a.G);
       b = g / a.Hkv;
       h = (g - b * a.Hkv) * a.G + rem % a.G;
@@ -193,7 +218,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       h = p % a.Hq;
       const int r = p / a.Hq;
       b = r % a.B;
-      qt = a.n_qt - 1 - r / a.B;
+      const int r2 = r / a.B;
+      const int rank = r2 / a.S;
+      part = r2 - rank * a.S;
+      qt = a.n_qt - 1 - rank;
     }
   }
 
@@ -208,12 +236,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const uint16_t* kbase = a.k_pool + (size_t)kvh * D;
   const uint16_t* vbase = a.v_pool + (size_t)kvh * D;
 
-  // absolute position of this work-group's last row; keys past it are never needed
-  const int rows_wg = min(kPfBM, q_len - r_wg);
+  // keys past this work-group's last row are never needed; with key splitting this
+  // work-group covers tiles tile_lo .. tile_hi - 1 of them
   const int shift = L - q_len;                 // position of row r is shift + r
-  int k_lim = L;
-  if (a.causal) k_lim = min(L, max(0, shift + r_wg + rows_wg));
-  const int n_tiles = (k_lim + kPfBN - 1) / kPfBN;
+  const PfTiles tw = pf_tiles(a, L, q_len, r_wg, kPfBM);
+  if (part >= tw.parts) return;
+  const int tile_lo = part * tw.n / tw.parts;
+  const int tile_hi = (part + 1) * tw.n / tw.parts;
 
   // this wave's rows and the position bound of its rows
   const int r_w = r_wg + 32 * wave;
@@ -463,29 +492,30 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // block i + 1 and then O += P V of block i, the vector unit exponentiates block
   // i.  K of tiles t, t + 1 and V of tiles t - 1 .. t + 1 are resident, so one
   // barrier per tile suffices.
-  if (n_tiles > 0) {
-    tab = load_tab(0);
+  if (tile_hi > tile_lo) {
+    base_t = tile_lo;
+    tab = load_tab(tile_lo);
     int vs_cur = 0;                       // V stage of tile kt
-    issue(0, 0);
-    publish(0, 0);
-    if (n_tiles > 1) issue(1, 1);
-    f32x16 s_pend = qk(kst(0), 0);        // block 0: scores, mask, first reference
-    mask(s_pend, 0);
+    issue(tile_lo, 0);
+    publish(tile_lo, 0);
+    if (tile_hi - tile_lo > 1) issue(tile_lo + 1, 1);
+    f32x16 s_pend = qk(kst(tile_lo), 0);  // first block: scores, mask, first reference
+    mask(s_pend, tile_lo * kPfBN);
     decide(rowmax(s_pend));
-    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+    for (int kt = tile_lo; kt + 1 < tile_hi; ++kt) {
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // block 2 kt (pending) -> block 2 kt + 1
       step(s_pend, kst(kt), 1, vst(vs_cur), 0);
       mask(s_pend, kt * kPfBN + 32);
       // block 2 kt + 1 -> block 2 kt + 2 (first of the next tile)
       publish(kt + 1, vs_next);
-      if (kt + 2 < n_tiles) issue(kt + 2, vs_next == 2 ? 0 : vs_next + 1);
+      if (kt + 2 < tile_hi) issue(kt + 2, vs_next == 2 ? 0 : vs_next + 1);
       step(s_pend, kst(kt + 1), 0, vst(vs_cur), 1);
       mask(s_pend, (kt + 1) * kPfBN);
       vs_cur = vs_next;
     }
-    step(s_pend, kst(n_tiles - 1), 1, vst(vs_cur), 0);
-    mask(s_pend, (n_tiles - 1) * kPfBN + 32);
+    step(s_pend, kst(tile_hi - 1), 1, vst(vs_cur), 0);
+    mask(s_pend, (tile_hi - 1) * kPfBN + 32);
     uint32_t pw[8];
     float ps;
     exps(s_pend, pw, ps);
@@ -497,6 +527,21 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const float l_tot = xor32_sum(l_run);
   const bool live = l_tot > 0.f;
   const float inv = live ? 1.f / l_tot : 0.f;
+  const float lse = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  if (tw.parts > 1) {
+    // this part's normalised output and lse, merged by the prefill merge kernel
+    const size_t prow = ((size_t)(t0 + my_row) * a.Hq + h) * a.S + part;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(po + 32 * t + 8 * j + 4 * hh) =
+            f32x4{acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv, acc[t][4 * j + 2] * inv,
+                  acc[t][4 * j + 3] * inv};
+    if (hh == 0) a.part_lse[prow] = lse;
+    return;
+  }
   uint16_t* op = a.out + ((size_t)(t0 + my_row) * a.Hq + h) * D;
   // lane holds O^T[32 t + 8 j + 4 hh + i][col]
 #pragma unroll
@@ -507,8 +552,70 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
                        pack_bf16x2(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
       *reinterpret_cast<u32x2*>(op + 32 * t + 8 * j + 4 * hh) = w;
     }
-  if (hh == 0 && a.lse_out)
-    a.lse_out[(size_t)(t0 + my_row) * a.Hq + h] = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  if (hh == 0 && a.lse_out) a.lse_out[(size_t)(t0 + my_row) * a.Hq + h] = lse;
+}
+
+// Merge of the query tiles that were cut into key-range parts ("The Stack Below
+// the Stack (Part 2)", section 2.2, step 3: with m the largest part lse, weights
+// exp(lse_c - m), lse = m + ln sum).  A work-group covers 256 / (D / 4) rows of one
+// (query head, sequence, query tile); each thread merges 4 output columns of one
+// row, with all of its loads issued before any is used, so the merge costs about
+// two memory round trips.  Work-groups of tiles with one part (written by the
+// prefill kernel) return at once.
+constexpr int kMergeThreads = 256;
+constexpr int kMaxParts = 16;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs a, int bm) {
+  constexpr int CH = D / 4;                  // 4-column chunks per row
+  constexpr int RPB = kMergeThreads / CH;    // rows per work-group
+  const int rblocks = bm / RPB;
+  const int p = blockIdx.x / rblocks;
+  const int rb = blockIdx.x - p * rblocks;
+  const int h = p % a.Hq;
+  const int r = p / a.Hq;
+  const int b = r % a.B;
+  const int qt = r / a.B;
+  const int t0 = a.cu_seqlens_q[b];
+  const int q_len = a.cu_seqlens_q[b + 1] - t0;
+  const int r_wg = qt * bm;
+  if (r_wg >= q_len) return;
+  int L = a.seq_lens_k[b];
+  const int cap = a.max_pages * a.page_size;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const PfTiles tw = pf_tiles(a, L, q_len, r_wg, bm);
+  if (tw.parts <= 1) return;
+  const int row = r_wg + rb * RPB + threadIdx.x / CH;
+  const int c = threadIdx.x % CH;
+  if (row >= q_len || t0 + row >= a.Tq) return;
+  const size_t orow = (size_t)(t0 + row) * a.Hq + h;
+  const size_t prow = orow * a.S;
+  float lse[kMaxParts];
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k) lse[k] = k < tw.parts ? a.part_lse[prow + k] : kNegInf;
+  f32x4 o[kMaxParts];
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k)
+    if (k < tw.parts) o[k] = *reinterpret_cast<const f32x4*>(a.part_o + (prow + k) * D + 4 * c);
+  float m = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k) m = fmaxf(m, lse[k]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k)
+      if (k < tw.parts) {
+        const float w = __expf(lse[k] - m);
+        tot += w;
+        acc += w * o[k];
+      }
+  }
+  const bool live = tot > 0.f;
+  const float inv = live ? 1.f / tot : 0.f;
+  *reinterpret_cast<u32x2*>(a.out + orow * D + 4 * c) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
 template <int D, int W>
@@ -519,7 +626,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
       : hipSuccess;
   if (attr != hipSuccess) return attr;
-  dim3 grid(a.Hq * a.B * a.n_qt);
+  dim3 grid(a.Hq * a.B * a.n_qt * a.S);
   hipLaunchKernelGGL((prefill_kernel<D, W>), grid, dim3(64 * W), PfLds<D>::BYTES, stream, a);
   return hipGetLastError();
 }
@@ -528,13 +635,36 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 // longest query run fills them, else 4.
 int prefill_waves(int max_q_len) { return max_q_len >= PF_W8_MIN ? 8 : 4; }
 
-hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
-                          size_t desc_len) {
+static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
   PrefillArgs a = a_in;
-  const int W = prefill_waves(a.max_q_len);
   a.n_qt = (a.max_q_len + 32 * W - 1) / (32 * W);
   const int groups = a.B * a.Hkv;
   a.xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
+  if (a.S < 1) a.S = 1;
+  return a;
+}
+
+hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, char* desc,
+                                size_t desc_len) {
+  const int W = prefill_waves(a_in.max_q_len);
+  const PrefillArgs a = prefill_shape(a_in, W);
+  const int rows_per_wg = kMergeThreads / (a.D / 4);
+  dim3 grid(a.Hq * a.B * a.n_qt * (32 * W / rows_per_wg));
+  if (a.D == 128)
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a,
+                       32 * W);
+  else
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, a,
+                       32 * W);
+  snprintf(desc, desc_len, "prefill_merge<D=%d> grid=%u (query tiles x heads x %d-row blocks) "
+           "parts<=%d", a.D, grid.x, rows_per_wg, a.S);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
+                          size_t desc_len) {
+  const int W = prefill_waves(a_in.max_q_len);
+  const PrefillArgs a = prefill_shape(a_in, W);
   hipError_t e;
   if (a.D == 128)
     e = W == 8 ? launch_prefill_t<128, 8>(a, stream) : launch_prefill_t<128, 4>(a, stream);
@@ -542,8 +672,8 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
     e = W == 8 ? launch_prefill_t<64, 8>(a, stream) : launch_prefill_t<64, 4>(a, stream);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=%d (%d heads x %d seqs x %d "
-           "q-tiles, %s) block=%d lds=%zu",
-           a.D, 32 * W, kPfBN, a.Hq * a.B * a.n_qt, a.Hq, a.B, a.n_qt,
+           "q-tiles x %d key parts, %s) block=%d lds=%zu",
+           a.D, 32 * W, kPfBN, a.Hq * a.B * a.n_qt * a.S, a.Hq, a.B, a.n_qt, a.S,
            a.xcd_groups ? "KV groups per XCD" : "head-major", 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;

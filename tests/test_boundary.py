@@ -30,7 +30,9 @@ def declared_functions():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ["kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
-              "paged_attn_prefill_varlen", "kv_page_write_fp8", "paged_attn_decode_fp8", "paged_attn_decode_workspace_bytes",
+              "paged_attn_prefill_varlen", "kv_page_write_fp8", "paged_attn_decode_fp8",
+              "paged_attn_prefill_varlen_splitk", "paged_attn_prefill_num_splits",
+              "paged_attn_prefill_workspace_bytes", "paged_attn_decode_workspace_bytes",
               "paged_attn_decode_num_splits", "pa_status_string", "pa_last_error",
               "pa_describe_launch"]:
         assert n in names
@@ -168,6 +170,32 @@ def test_write_fp8_rejects_invalid_arguments(lib):
     bad = list(wb); bad[8] = 0
     assert w(*bad) == 0          # nothing to write
     assert b"nothing" in lib.pa_describe_launch()
+
+
+def test_prefill_splitk_sizing_and_rejections(lib):
+    n = lib.paged_attn_prefill_num_splits
+    assert n(4, 32, 4096) == 1          # 2048 work-groups of 256 rows fill the chip
+    assert n(5, 32, 512) == 1           # 640 work-groups of 128 rows fill 512 slots
+    assert n(1, 32, 512) == 4           # 128 work-groups: one per slot with 4 parts
+    assert n(1, 1, 100) == 8            # at most 8 automatically
+    wb = lib.paged_attn_prefill_workspace_bytes
+    assert wb(1, 512, 512, 32, 128, 1) == 0
+    need = wb(1, 512, 512, 32, 128, 4)
+    assert need >= 512 * 32 * 4 * 129 * 4
+    assert wb(1, 512, 512, 32, 128, 0) == need          # auto resolves to the same 4
+    assert wb(1, 512, 512, 32, 128, 99) == wb(1, 512, 512, 32, 128, 16)   # capped at 16
+    f = lib.paged_attn_prefill_varlen_splitk
+    base = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 512, 2100, 2100, 16, 32, 8,
+            128, 0.1, 1, 4, None, 0, None]
+    assert f(*base) == 5                                  # workspace missing
+    bad = list(base); bad[20] = FAKE; bad[21] = 16
+    assert f(*bad) == 5                                   # workspace too small
+    bad = list(base); bad[20] = FAKE + 4; bad[21] = need
+    assert f(*bad) == 4                                   # workspace misaligned
+    bad = list(base); bad[16] = 96
+    assert f(*bad) == 3
+    bad = list(base); bad[9] = 0
+    assert f(*bad) == 0 and b"nothing" in lib.pa_describe_launch()
 
 
 def test_binding_refuses_wrong_dtypes_before_any_device_work():

@@ -102,20 +102,110 @@ def test_causal_prefill_full_size_sampled(require_gpu):
     assert torch.isfinite(out.float()).all()
 
 
-def test_mixed_ragged_step_full_size(require_gpu):
+def run_prefill_splitk(case, splits, causal=None, workspace=None):
+    out, lse = pa.paged_attn_prefill_varlen_splitk(
+        case.q, case.k_pool, case.v_pool, case.cu_seqlens_q, case.seq_lens_k, case.block_tables,
+        case.scale, causal=case.causal if causal is None else causal, max_q_len=case.max_q_len,
+        num_splits=splits, workspace=workspace, return_lse=True, validate=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+SPLIT_CASES = [
+    # hist, q_lens, Hq, Hkv, D, ps, causal, splits
+    ([4113, 214, 0], [512, 512, 40], 8, 2, 128, 16, True, 3),     # one long history
+    ([3000, 0], [100, 1], 4, 1, 128, 16, True, 0),                # automatic: 8 parts at most
+    ([2500, 9], [300, 20], 8, 8, 64, 32, False, 4),               # non-causal, D 64
+    ([1500, 2200], [1100, 64], 4, 2, 128, 64, True, 2),           # 256-row work-groups
+    ([0], [3000], 4, 2, 128, 16, True, 16),                       # no history, 16 parts at most
+    ([5000], [1], 8, 1, 128, 16, True, 5),                        # a decode row, GQA 8
+]
+
+
+@pytest.mark.parametrize("hist,ql,Hq,Hkv,D,ps,causal,splits", SPLIT_CASES)
+def test_prefill_splitk_parity(require_gpu, hist, ql, Hq, Hkv, D, ps, causal, splits):
+    print(f"[prefill splitk] hist={hist} q={ql} Hq={Hq} Hkv={Hkv} D={D} ps={ps} "
+          f"causal={causal} S={splits}", flush=True)
+    case = make_case("pfs", hist_lens=hist, q_lens=ql, write_new=True, causal=causal, Hq=Hq,
+                     Hkv=Hkv, D=D, page_size=ps, seed=sum(hist) + sum(ql) + Hq, device="cuda",
+                     num_pages=sum(-(-(h + n) // ps) for h, n in zip(hist, ql)) + 2)
+    kp, vp = pools_after_write(case)
+    write(case)
+    out, lse = run_prefill_splitk(case, splits)
+    desc = pa.describe_launch()
+    assert "prefill_merge" in desc, desc          # some tile was split
+    o_ref, l_ref = oracle_full(case, kp, vp)
+    assert_parity(as_f64(out), o_ref, "prefill splitk")
+    assert_lse(as_f64(lse), l_ref, "prefill splitk lse")
+
+
+def test_prefill_splitk_unsplit_tiles_are_bitwise_the_plain_prefill(require_gpu):
+    """One part per tile (S = 1, or tiles shorter than two parts) is the plain launch."""
+    case = make_case("pfb", hist_lens=[700, 0, 31], q_lens=[129, 300, 5], write_new=True,
+                     causal=True, Hq=8, Hkv=2, D=128, page_size=16, seed=12, device="cuda")
+    write(case)
+    ref, lref = run_prefill(case)
+    for splits in (1, 4):
+        out, lse = run_prefill_splitk(case, splits)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), splits
+        assert torch.equal(lse, lref), splits
+
+
+def test_prefill_splitk_workspace_is_scratch(require_gpu):
+    """A garbage-filled workspace, reused by two calls of different shapes, gives the
+    oracle's result both times."""
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
+    for i, (hist, ql) in enumerate([([4000, 10], [64, 3]), ([2100], [700])]):
+        case = make_case("pfw", hist_lens=hist, q_lens=ql, write_new=True, causal=True, Hq=8,
+                         Hkv=2, D=128, page_size=16, seed=30 + i, device="cuda")
+        kp, vp = pools_after_write(case)
+        write(case)
+        out, lse = run_prefill_splitk(case, 4, workspace=ws)
+        o_ref, l_ref = oracle_full(case, kp, vp)
+        assert_parity(as_f64(out), o_ref, f"prefill splitk ws {i}")
+        assert_lse(as_f64(lse), l_ref, f"prefill splitk ws lse {i}")
+
+
+def test_long_history_chunk_full_size_sampled(require_gpu):
+    """A 512-token chunk over a 32,768-token history (Hq 32, Hkv 8), with the library's
+    own key-part count as the benchmark runs it; the oracle checks sampled rows."""
+    case = make_config("long_history_chunk", "cuda")
+    print("[prefill splitk] long_history_chunk full size", flush=True)
+    kp, vp = pools_after_write(case)
+    write(case)
+    assert pa.prefill_num_splits(1, 32, 512) > 1
+    out, lse = run_prefill_splitk(case, 0)
+    assert "prefill_merge" in pa.describe_launch()
+    rng = np.random.default_rng(8)
+    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, 512, 24), rng.integers(0, 32, 24))]
+    rows += [(0, 0), (511, 31), (255, 16), (256, 1)]
+    o_ref, l_ref = oracle_rows(case, rows, kp, vp)
+    got = np.stack([as_f64(out[t, h]) for t, h in rows])
+    assert_parity(got, o_ref, "long_history_chunk sampled")
+    assert_lse(np.array([float(lse[t, h]) for t, h in rows]), l_ref, "long_history_chunk lse")
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("splitk", [False, True])
+def test_mixed_ragged_step_full_size(require_gpu, splitk):
     """The mixed step: write all 2,578 new tokens, prefill the five 512-token chunks over
-    their history, decode the 18 single-token requests, all on the same pools."""
+    their history (in one pass, or with long key ranges split and merged), decode the
+    18 single-token requests, all on the same pools."""
     case = make_config("mixed_ragged", "cuda")
-    print("[mixed] mixed_ragged full size", flush=True)
+    print(f"[mixed] mixed_ragged full size, splitk={splitk}", flush=True)
     kp, vp = pools_after_write(case)
     write(case)
     n_pf = 5
     cu = case.cu_seqlens_q
     t_pf = int(cu[n_pf])
-    out_p, lse_p = pa.paged_attn_prefill_varlen(
+    extra = dict(num_splits=4) if splitk else {}
+    prefill = pa.paged_attn_prefill_varlen_splitk if splitk else pa.paged_attn_prefill_varlen
+    out_p, lse_p = prefill(
         case.q[:t_pf], case.k_pool, case.v_pool, cu[:n_pf + 1].contiguous(),
         case.seq_lens_k[:n_pf].contiguous(), case.block_tables[:n_pf].contiguous(), case.scale,
-        causal=True, max_q_len=512, return_lse=True, validate=True)
+        causal=True, max_q_len=512, return_lse=True, validate=True, **extra)
+    if splitk:
+        assert "prefill_merge" in pa.describe_launch()
     out_d, lse_d = pa.paged_attn_decode(
         case.q[t_pf:].contiguous(), case.k_pool, case.v_pool,
         case.block_tables[n_pf:].contiguous(), case.seq_lens_k[n_pf:].contiguous(), case.scale,
@@ -123,7 +213,7 @@ def test_mixed_ragged_step_full_size(require_gpu):
     torch.cuda.synchronize()
     rng = np.random.default_rng(6)
     rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, t_pf, 40), rng.integers(0, 32, 40))]
-    rows += [(511, 0), (512, 31), (t_pf - 1, 3)]
+    rows += [(511, 0), (512, 31), (t_pf - 1, 3), (1024, 0), (1300, 7), (1535, 31)]
     rows += [(t, h) for t in range(t_pf, case.T) for h in (0, 13, 31)]
     o_ref, l_ref = oracle_rows(case, rows, kp, vp)
     got = np.stack([as_f64(out_p[t, h]) if t < t_pf else as_f64(out_d[t - t_pf, h])

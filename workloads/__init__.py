@@ -274,12 +274,20 @@ def _cfg_long(device):
                      num_pages=16384, seed=1004, std_kv=0.5, device=device, num_splits=64)
 
 
+def _cfg_long_chunk(device):
+    # one 512-token prefill chunk over a 32,768-token history (chunked prefill of a
+    # long prompt): only 128 query tiles, the case key splitting is for
+    return make_case("long_history_chunk", hist_lens=[32768], q_lens=[512], write_new=True,
+                     causal=True, Hq=32, Hkv=8, D=128, page_size=16, seed=1005, device=device)
+
+
 CONFIGS = {
     "tiny_decode": _cfg_tiny,
     "qwen7b_decode": _cfg_qwen,
     "mixed_ragged": _cfg_mixed,
     "causal_prefill": _cfg_prefill,
     "long_decode": _cfg_long,
+    "long_history_chunk": _cfg_long_chunk,
 }
 
 
