@@ -25,6 +25,13 @@ R2  Causal alignment: a chunk of q_len queries sits at the END of its
 R3  A row with no visible key returns O = 0 and lse = -inf ("Test the kernel
     at three levels": a fully masked row must give a defined value, not the
     NaN of a zero denominator).
+R4  Sliding window: the pages list sliding windows among the masks a serving
+    backend must support ("8. Kernels and Attention Backends", "Attention is an
+    I/O problem"; FlexAttention mask functions in "The Stack Below the Stack
+    (Part 2)", section 5) without fixing the predicate.  With window w > 0 a
+    query at absolute position p sees key j only if p - w < j (its last w
+    positions, itself included), on top of the causal condition when causal;
+    without causal only this lower bound applies.  w = 0 means no window.
 """
 
 from __future__ import annotations
@@ -81,11 +88,12 @@ def gather_sequence_kv(pool, table_row, seq_len: int, page_size: int) -> np.ndar
     return dense[:seq_len]
 
 
-def attend_rows(q_rows, k, v, scale: float, visible):
+def attend_rows(q_rows, k, v, scale: float, visible, first=None):
     """Plain softmax attention for a set of query rows against one key head.
 
     ``q_rows`` [n, D], ``k``/``v`` [L, D], ``visible`` [n] = number of leading
-    keys each row may see.  Returns (O [n, D], lse [n]) in float64.
+    keys each row may see; ``first`` [n] (optional) = index of the first key
+    each row may see (R4; default 0).  Returns (O [n, D], lse [n]) in float64.
 
     This is the definition the tiled method must reproduce exactly ("8.
     Kernels and Attention Backends", "Attention is an I/O problem": scores
@@ -105,6 +113,9 @@ def attend_rows(q_rows, k, v, scale: float, visible):
         return out, lse
     s = scale * (q_rows @ k.T)                                   # [n, L]
     mask = np.arange(L)[None, :] >= visible[:, None]
+    if first is not None:
+        first = np.asarray(first, dtype=np.int64).reshape(n)
+        mask |= np.arange(L)[None, :] < first[:, None]
     s = np.where(mask, -np.inf, s)
     m = s.max(axis=1)
     live = np.isfinite(m)
@@ -130,8 +141,18 @@ def _visible_counts(seq_len: int, q_len: int, causal: bool) -> np.ndarray:
     return np.clip(vis, 0, seq_len)
 
 
+def _first_visible(seq_len: int, q_len: int, window: int) -> np.ndarray:
+    """Index of the first key each of the q_len rows may see under a sliding
+    window (R4): row i at absolute position p = seq_len - q_len + i sees keys
+    j > p - window, so the first is max(0, p - window + 1); 0 without a window."""
+    if window <= 0:
+        return np.zeros(q_len, dtype=np.int64)
+    pos = seq_len - q_len + np.arange(q_len, dtype=np.int64)
+    return np.maximum(0, pos - window + 1)
+
+
 def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
-                  scale: float, causal: bool, page_size: int):
+                  scale: float, causal: bool, page_size: int, window: int = 0):
     """Exact attention of every query row; returns (O [T, Hq, D], lse [T, Hq]).
 
     Streams one (sequence, key head) at a time so that memory stays bounded
@@ -157,16 +178,17 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
         kb = gather_sequence_kv(k_pool, block_tables[b], L, page_size)
         vb = gather_sequence_kv(v_pool, block_tables[b], L, page_size)
         vis = _visible_counts(L, t1 - t0, causal)
+        first = _first_visible(L, t1 - t0, window)
         for h in range(Hq):
             kvh = h // G                                                # R1
-            o, ls = attend_rows(q[t0:t1, h], kb[:, kvh], vb[:, kvh], scale, vis)
+            o, ls = attend_rows(q[t0:t1, h], kb[:, kvh], vb[:, kvh], scale, vis, first)
             out[t0:t1, h] = o
             lse[t0:t1, h] = ls
     return out, lse
 
 
 def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
-                       scale: float, causal: bool, page_size: int, rows):
+                       scale: float, causal: bool, page_size: int, rows, window: int = 0):
     """Same as :func:`attention_ref` for selected (token, head) pairs only.
 
     Used at full workload sizes, where the oracle computes sampled outputs one
@@ -189,12 +211,14 @@ def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q
         L = int(lens[b])
         q_len = int(cu[b + 1] - cu[b])
         vis_all = _visible_counts(L, q_len, causal)
+        first_all = _first_visible(L, q_len, window)
         kb = gather_sequence_kv(k_pool, block_tables[b], L, page_size)
         vb = gather_sequence_kv(v_pool, block_tables[b], L, page_size)
         for i, t, h in items:
             kvh = h // G
+            i0 = t - int(cu[b])
             o, ls = attend_rows(q[t:t + 1, h], kb[:, kvh], vb[:, kvh], scale,
-                                vis_all[t - int(cu[b]):t - int(cu[b]) + 1])
+                                vis_all[i0:i0 + 1], first_all[i0:i0 + 1])
             out[i], lse[i] = o[0], ls[0]
     return out, lse
 

@@ -34,7 +34,7 @@ def oracle_full(case, kp=None, vp=None, causal=None):
     return oracle.attention_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
                                 case.seq_lens_k.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
                                 case.scale, case.causal if causal is None else causal,
-                                case.page_size)
+                                case.page_size, case.window)
 
 
 def oracle_rows(case, rows, kp=None, vp=None):
@@ -43,7 +43,7 @@ def oracle_rows(case, rows, kp=None, vp=None):
     return oracle.attention_rows_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
                                      case.seq_lens_k.cpu().numpy(),
                                      case.cu_seqlens_q.cpu().numpy(), case.scale, case.causal,
-                                     case.page_size, rows)
+                                     case.page_size, rows, case.window)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:

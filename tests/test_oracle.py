@@ -39,8 +39,10 @@ def _bf16(x):
             for v in x.ravel()]
 
 
-def brute_attention(case):
-    """Loops over sequences, rows, heads and keys; math.exp and math.fsum only."""
+def brute_attention(case, window=None):
+    """Loops over sequences, rows, heads and keys; math.exp and math.fsum only.
+    With a sliding window w > 0 the row at position p takes keys j > p - w only."""
+    w = case.window if window is None else window
     q = bits(case.q)
     kp = bits(case.k_pool)
     vp = bits(case.v_pool)
@@ -58,11 +60,15 @@ def brute_attention(case):
         for i in range(n):
             t = int(cu[b]) + i
             limit = L if not case.causal else L - n + i + 1
+            pos = L - n + i
+            start = pos - w + 1 if w > 0 else 0
             for h in range(Hq):
                 kvh = h // grp
                 qv = _bf16(q[t, h])
                 scores, vrows = [], []
                 for j in range(max(0, min(limit, L))):
+                    if j < start:
+                        continue
                     page, slot = int(bt[b][j // ps]), j % ps
                     kv = _bf16(kp[page, slot, kvh])
                     scores.append(case.scale * math.fsum(a * c for a, c in zip(qv, kv)))
@@ -78,11 +84,11 @@ def brute_attention(case):
     return out, lse
 
 
-def run_oracle(case):
+def run_oracle(case, window=None):
     return oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
                                 case.block_tables.numpy(), case.seq_lens_k.numpy(),
                                 case.cu_seqlens_q.numpy(), case.scale, case.causal,
-                                case.page_size)
+                                case.page_size, case.window if window is None else window)
 
 
 def assert_close(a, b, tol=1e-12):
@@ -105,6 +111,7 @@ small_shapes = st.fixed_dictionaries(dict(
     seed=st.integers(0, 10_000),
     lens=st.lists(st.integers(0, 40), min_size=3, max_size=3),
     qlens=st.lists(st.integers(1, 5), min_size=3, max_size=3),
+    window=st.sampled_from([0, 0, 1, 2, 5, 17]),
 ))
 
 
@@ -115,7 +122,8 @@ def _small_case(p):
     spare = 3
     return make_case("hyp", seq_lens=lens, q_lens=ql, Hq=p["Hkv"] * p["G"], Hkv=p["Hkv"],
                      D=p["D"], page_size=p["ps"], seed=p["seed"], causal=p["causal"],
-                     num_pages=sum(-(-L // p["ps"]) for L in lens) + spare)
+                     num_pages=sum(-(-L // p["ps"]) for L in lens) + spare,
+                     window=p["window"])
 
 
 @settings(max_examples=40, deadline=None)
@@ -426,21 +434,21 @@ def test_workload_units_at_the_five_sizes():
 # planted mistakes: each must be caught by a pin above
 # ----------------------------------------------------------------------------
 
-def _mut_drop_scale(q_rows, k, v, scale, visible):
-    return _orig_attend(q_rows, k, v, 1.0, visible)
+def _mut_drop_scale(q_rows, k, v, scale, visible, first=None):
+    return _orig_attend(q_rows, k, v, 1.0, visible, first)
 
 
-def _mut_no_mask(q_rows, k, v, scale, visible):
+def _mut_no_mask(q_rows, k, v, scale, visible, first=None):
     return _orig_attend(q_rows, k, v, scale, np.full(len(np.atleast_1d(visible)), k.shape[0]))
 
 
-def _mut_off_by_one_causal(q_rows, k, v, scale, visible):
+def _mut_off_by_one_causal(q_rows, k, v, scale, visible, first=None):
     vis = np.asarray(visible) - 1
-    return _orig_attend(q_rows, k, v, scale, np.maximum(vis, 0))
+    return _orig_attend(q_rows, k, v, scale, np.maximum(vis, 0), first)
 
 
-def _mut_transposed_value(q_rows, k, v, scale, visible):
-    o, l = _orig_attend(q_rows, k, v, scale, visible)
+def _mut_transposed_value(q_rows, k, v, scale, visible, first=None):
+    o, l = _orig_attend(q_rows, k, v, scale, visible, first)
     return o[:, ::-1].copy(), l
 
 
@@ -483,3 +491,79 @@ def test_planted_merge_mistake_is_caught(monkeypatch):
     assert np.abs(oc.mean(axis=0) - o[0]).max() > 1e-3
     om, _ = oracle.merge_ref(oc, lc)
     assert np.abs(om - o[0]).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# sliding window (R4)
+# ----------------------------------------------------------------------------
+
+def _window_case(window, causal=True, seed=31):
+    return make_case("win", seq_lens=[40, 7, 23], q_lens=[6, 7, 1], Hq=4, Hkv=2, D=8,
+                     page_size=3, seed=seed, causal=causal, window=window)
+
+
+def test_window_of_one_returns_each_rows_own_value_row():
+    """Causal window 1: a row sees only the key at its own position, so O is that
+    key's value row exactly and lse is its scaled score."""
+    case = _window_case(1)
+    o, lse = run_oracle(case)
+    q, kp, vp = bits(case.q), bits(case.k_pool), bits(case.v_pool)
+    bt, cu = case.block_tables.numpy(), case.cu_seqlens_q.numpy()
+    for b, L in enumerate(case.seq_lens):
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            pos = L - n + i
+            page, slot = int(bt[b][pos // 3]), pos % 3
+            for h in range(4):
+                kv = oracle.bf16_bits_to_f64(kp[page, slot, h // 2])
+                vv = oracle.bf16_bits_to_f64(vp[page, slot, h // 2])
+                qv = oracle.bf16_bits_to_f64(q[int(cu[b]) + i, h])
+                assert np.array_equal(o[int(cu[b]) + i, h], vv)
+                assert abs(lse[int(cu[b]) + i, h] - case.scale * float(qv @ kv)) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_covering_every_key_changes_nothing(causal):
+    case = _window_case(0, causal)
+    o0, l0 = run_oracle(case)
+    o1, l1 = run_oracle(case, window=41)       # longer than every sequence
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("window,causal", [(1, True), (4, True), (9, False), (40, True)])
+def test_window_matches_brute_force(window, causal):
+    case = _window_case(window, causal)
+    o, l = run_oracle(case)
+    ob, lb = brute_attention(case)
+    assert_close(o, ob)
+    assert_close(l, lb)
+
+
+def test_window_equals_attention_over_the_sliced_keys():
+    """A windowed row is plain attention over keys p - w + 1 .. p (no mask at all)."""
+    case = _window_case(5)
+    o, _ = run_oracle(case)
+    q, bt = bits(case.q), case.block_tables.numpy()
+    L, n = case.seq_lens[0], 6
+    k = oa.gather_sequence_kv(bits(case.k_pool), bt[0], L, 3)[:, 1]
+    v = oa.gather_sequence_kv(bits(case.v_pool), bt[0], L, 3)[:, 1]
+    for i in range(n):
+        pos = L - n + i
+        lo = max(0, pos - 4)
+        qi = oracle.bf16_bits_to_f64(q[i, 2])[None]
+        os_, _ = oracle.attend_rows(qi, k[lo:pos + 1], v[lo:pos + 1], case.scale, [pos + 1 - lo])
+        assert np.abs(os_[0] - o[i, 2]).max() < 1e-12
+
+
+@pytest.mark.parametrize("mutant", ["off_by_one", "ignored"])
+def test_planted_window_mistakes_are_caught(monkeypatch, mutant):
+    case = _window_case(4)
+    ob, lb = brute_attention(case)
+    real = oa._first_visible
+    if mutant == "off_by_one":
+        monkeypatch.setattr(oa, "_first_visible",
+                            lambda L, n, w: np.maximum(0, real(L, n, w) - 1))
+    else:
+        monkeypatch.setattr(oa, "_first_visible", lambda L, n, w: real(L, n, 0))
+    o, _ = run_oracle(case)
+    assert np.abs(o - ob).max() > 1e-6

@@ -64,6 +64,7 @@ class PagedCase:
     cu_new: Optional[torch.Tensor] = None
     start_pos: Optional[torch.Tensor] = None
     num_splits: int = 0
+    window: int = 0                               # sliding window (0: none)
     meta: dict = field(default_factory=dict)
     host_seq_lens: Optional[List[int]] = None     # keys attended, kept on the host
 
@@ -144,7 +145,7 @@ def random_e4m3_codes(shape, seed: int, device="cpu", exp_lo: int = 4,
 def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=None,
               seed=0, q_lens=None, hist_lens=None, causal=False, write_new=False,
               std_q=1.0, std_kv=1.0, scale=None, device="cpu", num_splits=0,
-              max_pages=None, permute=True) -> PagedCase:
+              max_pages=None, permute=True, window=0) -> PagedCase:
     """Build one seeded case.
 
     Two shapes of case:
@@ -231,7 +232,7 @@ def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=No
         seq_lens_k=torch.as_tensor(np.asarray(total, dtype=np.int32), device=device),
         cu_seqlens_q=torch.as_tensor(cu_q, device=device),
         hist_lens=hist, q_lens=ql, k_new=k_new, v_new=v_new, cu_new=cu_new,
-        start_pos=start_pos, num_splits=num_splits,
+        start_pos=start_pos, num_splits=num_splits, window=int(window),
         meta=dict(seed=seed, std_q=std_q, std_kv=std_kv), host_seq_lens=list(total),
     )
 
