@@ -312,6 +312,74 @@ int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len);
 size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len, int32_t Hq,
                                           int32_t D, int32_t num_splits);
 
+/*
+ * Sliding-window attention and the general entry points.
+ *
+ * The pages list sliding windows among the masks a serving backend must support
+ * ("8. Kernels and Attention Backends", "Attention is an I/O problem"; sliding-window
+ * and document masks as FlexAttention mask functions in "The Stack Below the Stack
+ * (Part 2)", section 5) without fixing the predicate.  This library's: with
+ * window_left = w > 0 a query at absolute position p sees key j only if p - w < j
+ * (its last w positions, itself included), on top of the causal bound when causal;
+ * without causal only this lower bound applies.  A decode row sits at position
+ * seq_len - 1, so it sees keys seq_len - w .. seq_len - 1.  w = 0: no window.
+ * Document masks need no option: every sequence of a ragged batch is one document.
+ *
+ * The _ex entry points take every option of an operation in one struct; the
+ * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
+ * negative window PA_ERR_SHAPE.
+ */
+typedef struct {
+  int32_t num_splits;   /* as paged_attn_decode's (<= 0: the library's choice)            */
+  int32_t window_left;  /* 0, or w > 0: keys seq_len - w .. seq_len - 1 only              */
+  int32_t kv_fp8;       /* 0: bf16 pools; 1: E4M3 code pools (paged_attn_decode_fp8)      */
+  float k_scale;        /* kv_fp8 only                                                    */
+  float v_scale;        /* kv_fp8 only                                                    */
+} pa_decode_opts;
+
+typedef struct {
+  int32_t causal;       /* as paged_attn_prefill_varlen's                                 */
+  int32_t window_left;  /* 0, or w > 0: row at position p sees keys j > p - w only        */
+  int32_t num_splits;   /* key parts as paged_attn_prefill_varlen_splitk's: 1 plain,
+                           <= 0 the library's choice (may need a workspace)               */
+} pa_prefill_opts;
+
+/*
+ * paged_attn_decode_ex -- paged_attn_decode / paged_attn_decode_fp8 with options.
+ * With a window every row walks at most window_left + 31 keys (its first key rounded
+ * down to a 32-key chunk), and the split count and workspace are sized for
+ * min(max_seq_len, window_left + 31): use paged_attn_decode_ex_workspace_bytes.
+ */
+int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                         int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                         int32_t D, float softmax_scale, int32_t max_seq_len,
+                         const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes of paged_attn_decode_ex for these options (0 for NULL opts). */
+size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t max_seq_len, const pa_decode_opts* opts);
+
+/*
+ * paged_attn_prefill_ex -- paged_attn_prefill_varlen(_splitk) with options.  With a
+ * window, a query tile starts at the 64-key tile holding its first row's lower
+ * bound, so key tiles wholly below every row's window are never read.
+ */
+int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_k, const int32_t* block_tables, int32_t B,
+                          int32_t Tq, int32_t max_q_len, int32_t max_pages, int32_t num_pages,
+                          int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                          float softmax_scale, const pa_prefill_opts* opts, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of paged_attn_prefill_ex for these options (0 for NULL opts). */
+size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,
+                                             int32_t Hq, int32_t D,
+                                             const pa_prefill_opts* opts);
+
 /* Human-readable name of a pa_status value (static string). */
 const char* pa_status_string(int status);
 

@@ -18,6 +18,22 @@ c_fp = ctypes.c_void_p          # float*, passed as raw device addresses
 c_size = ctypes.c_size_t
 c_float = ctypes.c_float
 
+class DecodeOpts(ctypes.Structure):
+    """pa_decode_opts"""
+    _fields_ = [("num_splits", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+class PrefillOpts(ctypes.Structure):
+    """pa_prefill_opts"""
+    _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32)]
+
+
+c_dopts = ctypes.POINTER(DecodeOpts)
+c_popts = ctypes.POINTER(PrefillOpts)
+
 # name -> (restype, argtypes); mirrors include/paged_attn.h
 SIGNATURES = {
     "kv_page_write": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -47,6 +63,16 @@ SIGNATURES = {
                                                  c_vp, c_size, c_vp]),
     "paged_attn_prefill_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
     "paged_attn_prefill_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "paged_attn_decode_ex": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_float, c_i32, c_dopts, c_vp, c_size, c_vp]),
+    "paged_attn_decode_ex_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                      c_dopts]),
+    "paged_attn_prefill_ex": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                      c_i32, c_float, c_popts, c_vp, c_size, c_vp]),
+    "paged_attn_prefill_ex_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                       c_popts]),
     "pa_status_string": (ctypes.c_char_p, [c_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_describe_launch": (ctypes.c_char_p, []),

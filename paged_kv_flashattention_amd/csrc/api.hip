@@ -69,6 +69,14 @@ int32_t resolve_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t num_
   return num_splits < 1 ? 1 : num_splits;
 }
 
+// Keys a decode row walks at most: max_seq_len, or with a sliding window of w keys
+// at most w + 31 (the window's start is rounded down to a 32-key chunk).
+int32_t effective_len(int32_t max_seq_len, int32_t window) {
+  if (window <= 0) return max_seq_len;
+  const long long w = (long long)window + kChunk - 1;
+  return w < max_seq_len ? (int32_t)w : max_seq_len;
+}
+
 bool scales_ok(float k_scale, float v_scale) {
   return k_scale > 0.f && k_scale <= 3.0e38f && v_scale > 0.f && v_scale <= 3.0e38f;
 }
@@ -90,8 +98,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
-                float v_scale = 1.f) {
-  if (B < 0 || max_seq_len < 0)
+                float v_scale = 1.f, int32_t window = 0) {
+  if (B < 0 || max_seq_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
   if (st) return st;
@@ -105,8 +113,11 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
-  const int32_t S = resolve_splits(B, Hkv, max_seq_len, num_splits);
-  const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
+  // with a window every row walks at most window + 31 keys (its lower bound rounded
+  // down to a 32-key chunk): partitions are sized for that
+  const int32_t len = effective_len(max_seq_len, window);
+  const int32_t S = resolve_splits(B, Hkv, len, num_splits);
+  const int32_t chunks = len > 0 ? (len + kChunk - 1) / kChunk : 1;
   a = pa::DecodeArgs{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -123,6 +134,7 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.scale_log2 = softmax_scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
   a.kv_fp8 = fp8 ? 1 : 0;
   a.v_scale = fp8 ? v_scale : 1.f;
+  a.window = window;
   return PA_OK;
 }
 
@@ -174,12 +186,12 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
-                float k_scale, float v_scale, void* stream) {
+                float k_scale, float v_scale, void* stream, int32_t window = 0) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
                        num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
-                       num_splits, fp8, k_scale, v_scale);
+                       num_splits, fp8, k_scale, v_scale, window);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
@@ -254,10 +266,11 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  const int32_t* block_tables, int32_t B, int32_t Tq, int32_t max_q_len,
                  int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0) {
   g_last_error[0] = 0;
-  if (B < 0 || Tq < 0 || max_q_len < 0)
-    return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d", what, B, Tq, max_q_len);
+  if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
+    return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
+                window);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
   if (st) return st;
   if (B == 0 || Tq == 0 || max_q_len == 0) {
@@ -297,6 +310,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.ps_shift = log2_exact(page_size);
   a.causal = causal ? 1 : 0;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.window = window;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -488,6 +502,53 @@ int paged_attn_prefill_varlen_splitk(void* out, float* lse_out, const void* q,
                       seq_lens_k, block_tables, B, Tq, max_q_len, max_pages, num_pages,
                       page_size, Hq, Hkv, D, softmax_scale, causal, num_splits, workspace,
                       workspace_bytes, stream);
+}
+
+int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                         int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                         int32_t D, float softmax_scale, int32_t max_seq_len,
+                         const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error[0] = 0;
+  if (!opts) return fail(PA_ERR_NULL, "decode_ex: opts is NULL");
+  if (opts->kv_fp8 != 0 && opts->kv_fp8 != 1)
+    return fail(PA_ERR_UNSUPPORTED, "decode_ex: kv_fp8=%d", opts->kv_fp8);
+  return decode_impl("decode_ex", out, lse_out, q, k_pool, v_pool, block_tables, seq_lens, B,
+                     max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                     opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
+                     opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
+                     stream, opts->window_left);
+}
+
+size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t max_seq_len, const pa_decode_opts* opts) {
+  if (!opts || B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || opts->window_left < 0) return 0;
+  const int32_t len = effective_len(max_seq_len, opts->window_left);
+  return workspace_for(B, Hq, D, resolve_splits(B, Hkv, len, opts->num_splits));
+}
+
+int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_k, const int32_t* block_tables, int32_t B,
+                          int32_t Tq, int32_t max_q_len, int32_t max_pages, int32_t num_pages,
+                          int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                          float softmax_scale, const pa_prefill_opts* opts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!opts) return fail(PA_ERR_NULL, "prefill_ex: opts is NULL");
+  return prefill_impl("prefill_ex", out, lse_out, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
+                      block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
+                      D, softmax_scale, opts->causal, opts->num_splits, workspace,
+                      workspace_bytes, stream, opts->window_left);
+}
+
+size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,
+                                             int32_t Hq, int32_t D,
+                                             const pa_prefill_opts* opts) {
+  if (!opts) return 0;
+  return paged_attn_prefill_workspace_bytes(B, Tq, max_q_len, Hq, D, opts->num_splits);
 }
 
 }  // extern "C"

@@ -230,7 +230,11 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   int L = a.seq_lens[b];
   const int cap = a.max_pages * a.page_size;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int k_begin = split * a.part_len;
+  // sliding window: the row (position L - 1) sees keys lo .. L - 1; the walk starts
+  // at lo rounded down to a chunk, so chunks keep their page alignment, and the keys
+  // below lo are masked
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const int k_begin = (lo & ~31) + split * a.part_len;
   const int k_end = min(L, k_begin + a.part_len);
   const int n_chunks = k_end > k_begin ? (k_end - k_begin + 31) >> 5 : 0;
 
@@ -327,7 +331,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
         s[i] = sa[i] * a.scale_log2;
         s[4 + i] = sb[i] * a.scale_log2;
       }
-      if (c0 + 32 > k_end) {   // last chunk: keys past the end get -inf, their V rows 0
+      if (c0 + 32 > k_end || c0 < lo) {
+        // keys past the end get -inf and V rows 0 (they may hold anything); keys
+        // below the window get -inf (their V rows are real data)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = c0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
@@ -335,6 +341,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
             s[j] = kNegInf;
 #pragma unroll
             for (int w = 0; w < D / 32; ++w) ch.v[j][w] = 0u;
+          } else if (key < lo) {
+            s[j] = kNegInf;
           }
         }
       }

@@ -18,6 +18,7 @@
 // absolute position seq_len - q_len + i sees keys j <= that position); key
 // blocks wholly above a wave's rows are skipped, and only blocks that cross the
 // diagonal are masked.  Work-groups with the most keys are dispatched first.
+#include <limits.h>
 #include <stdio.h>
 
 #include "common.hpp"
@@ -34,12 +35,14 @@ constexpr float kSumLimit = 256.f;     // 2^kRescaleSlack: bound on a lane's blo
 
 // The key tiles a query tile needs and how many parts they are cut into.  A
 // query tile of rows r0 .. r0 + rows - 1 of a sequence with L keys and q_len query
-// rows needs keys 0 .. k_lim - 1 (causal: up to its last row's position).  With
-// key splitting on (S > 1) the n tiles are cut into min(S, n / part_min) parts of
-// consecutive tiles (at least one), each computed by its own work-group; the
-// prefill merge recomputes the same count for every row.
+// rows needs keys up to k_lim - 1 (causal: up to its last row's position) and,
+// with a sliding window, from its first row's lower bound on: tiles first .. n - 1.
+// With key splitting on (S > 1) those tiles are cut into min(S, count / part_min)
+// parts of consecutive tiles (at least one), each computed by its own work-group;
+// the prefill merge recomputes the same count for every row.
 struct PfTiles {
-  int n;       // 64-key tiles
+  int first;   // first 64-key tile
+  int n;       // one past the last tile
   int parts;   // key-range parts
 };
 
@@ -50,7 +53,9 @@ __device__ __forceinline__ PfTiles pf_tiles(const PrefillArgs& a, int L, int q_l
   if (a.causal) k_lim = min(L, max(0, L - q_len + r0 + rows));
   PfTiles t;
   t.n = (k_lim + kPfBN - 1) / kPfBN;
-  t.parts = a.S > 1 ? max(1, min(a.S, t.n / a.part_min)) : 1;
+  const int k_lo = a.window > 0 ? max(0, L - q_len + r0 - a.window + 1) : 0;
+  t.first = min(k_lo / kPfBN, t.n);
+  t.parts = a.S > 1 ? max(1, min(a.S, (t.n - t.first) / a.part_min)) : 1;
   return t;
 }
 
@@ -182,7 +187,7 @@ __device__ __forceinline__ void pf_zero_tail(uint16_t* vst, int k0, int L, int w
 }
 
 // W waves (32 W query rows) per work-group; 8 W waves per CU.
-template <int D, int W>
+template <int D, int W, bool WIN>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
@@ -241,8 +246,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int shift = L - q_len;                 // position of row r is shift + r
   const PfTiles tw = pf_tiles(a, L, q_len, r_wg, kPfBM);
   if (part >= tw.parts) return;
-  const int tile_lo = part * tw.n / tw.parts;
-  const int tile_hi = (part + 1) * tw.n / tw.parts;
+  const int tile_lo = tw.first + part * (tw.n - tw.first) / tw.parts;
+  const int tile_hi = tw.first + (part + 1) * (tw.n - tw.first) / tw.parts;
 
   // this wave's rows and the position bound of its rows
   const int r_w = r_wg + 32 * wave;
@@ -251,6 +256,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int my_pos = shift + my_row;          // causal: keys <= my_pos are visible
   const int w_pos_min = shift + r_w;
   const int lim = a.causal ? min(L - 1, my_pos) : L - 1;   // last visible key
+  // sliding window: first visible key of this row, and the largest of the wave's
+  const int lo_row = WIN ? my_pos - a.window + 1 : INT_MIN;
+  const int w_lo_max = WIN ? shift + r_w + 31 - a.window + 1 : INT_MIN;
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
   u32x4 qb[D / 16];
@@ -346,16 +354,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     mt = fmaxf(mt, sc[15]);
     return xor32_max(mt) * a.scale_log2;
   };
-  // -inf for keys past the end and (causal) above the diagonal; only blocks that
-  // touch the boundary need it
+  // -inf for keys past the end, (causal) above the diagonal and (window) below a
+  // row's window; only blocks that touch one of these boundaries need it
   auto mask = [&](f32x16& sc, int kb0) {
-    const bool need = (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min);
+    const bool need =
+        (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (WIN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kb0 + 8 * j + 4 * hh + i > lim) sc[4 * j + i] = kNegInf;
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb0 + 8 * j + 4 * hh + i;
+          if (key > lim || (WIN && key < lo_row)) sc[4 * j + i] = kNegInf;
+        }
     }
   };
   // Online softmax in log2 units with a lazily moved reference: the running
@@ -618,17 +629,25 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
-template <int D, int W>
-static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+template <int D, int W, bool WIN>
+static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
   // more than 64 KiB of dynamic LDS must be requested once per process
   static const hipError_t attr = PfLds<D>::BYTES > 65536
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W>),
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, WIN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
       : hipSuccess;
   if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
-  hipLaunchKernelGGL((prefill_kernel<D, W>), grid, dim3(64 * W), PfLds<D>::BYTES, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, W, WIN>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
+                     a);
   return hipGetLastError();
+}
+
+// the sliding-window bound is compiled only into the windowed variant
+template <int D, int W>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  return a.window > 0 ? launch_prefill_w<D, W, true>(a, stream)
+                      : launch_prefill_w<D, W, false>(a, stream);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the

@@ -32,7 +32,9 @@ def test_header_declares_the_four_operations():
     for n in ["kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
               "paged_attn_prefill_varlen", "kv_page_write_fp8", "paged_attn_decode_fp8",
               "paged_attn_prefill_varlen_splitk", "paged_attn_prefill_num_splits",
-              "paged_attn_prefill_workspace_bytes", "paged_attn_decode_workspace_bytes",
+              "paged_attn_prefill_workspace_bytes", "paged_attn_decode_ex",
+              "paged_attn_decode_ex_workspace_bytes", "paged_attn_prefill_ex",
+              "paged_attn_prefill_ex_workspace_bytes", "paged_attn_decode_workspace_bytes",
               "paged_attn_decode_num_splits", "pa_status_string", "pa_last_error",
               "pa_describe_launch"]:
         assert n in names
@@ -196,6 +198,46 @@ def test_prefill_splitk_sizing_and_rejections(lib):
     assert f(*bad) == 3
     bad = list(base); bad[9] = 0
     assert f(*bad) == 0 and b"nothing" in lib.pa_describe_launch()
+
+
+def test_options_entry_points_check_their_options(lib):
+    from paged_kv_flashattention_amd import _lib
+    d = lib.paged_attn_decode_ex
+    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 16, 8, 2, 128, 0.1, 64]
+    assert d(*args, None, None, 0, None) == 1                         # NULL opts
+    bad = _lib.DecodeOpts(1, -3, 0, 1.0, 1.0)
+    assert d(*args, ctypes.byref(bad), None, 0, None) == 2            # negative window
+    bad = _lib.DecodeOpts(1, 0, 2, 1.0, 1.0)
+    assert d(*args, ctypes.byref(bad), None, 0, None) == 3            # unknown pool format
+    bad = _lib.DecodeOpts(1, 0, 1, 0.0, 1.0)
+    assert d(*args, ctypes.byref(bad), None, 0, None) == 2            # FP8 scale 0
+    wb = lib.paged_attn_decode_ex_workspace_bytes
+    plain = _lib.DecodeOpts(8, 0, 0, 1.0, 1.0)
+    win = _lib.DecodeOpts(8, 100, 0, 1.0, 1.0)
+    assert wb(32, 28, 4, 128, 8192, ctypes.byref(plain)) == \
+        lib.paged_attn_decode_workspace_bytes(32, 28, 4, 128, 8192, 8)
+    # a 100-key window walks at most 131 keys: 5 chunks, so at most 5 splits
+    assert wb(32, 28, 4, 128, 8192, ctypes.byref(win)) == \
+        lib.paged_attn_decode_workspace_bytes(32, 28, 4, 128, 8192, 5)
+    assert wb(32, 28, 4, 128, 8192, None) == 0
+    p = lib.paged_attn_prefill_ex
+    pargs = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 4, 8, 16, 8, 2, 128, 0.1]
+    assert p(*pargs, None, None, 0, None) == 1
+    bad = _lib.PrefillOpts(1, -1, 1)
+    assert p(*pargs, ctypes.byref(bad), None, 0, None) == 2
+    assert lib.paged_attn_prefill_ex_workspace_bytes(1, 512, 512, 32, 128, None) == 0
+    po = _lib.PrefillOpts(1, 64, 4)
+    assert lib.paged_attn_prefill_ex_workspace_bytes(1, 512, 512, 32, 128, ctypes.byref(po)) == \
+        lib.paged_attn_prefill_workspace_bytes(1, 512, 512, 32, 128, 4)
+
+
+def test_binding_refuses_a_negative_window():
+    import paged_kv_flashattention_amd as pa
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    kp = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.paged_attn_decode(q, kp, kp, torch.zeros(2, 2, dtype=torch.int32),
+                             torch.zeros(2, dtype=torch.int32), 0.1, window_left=-1)
 
 
 def test_binding_refuses_wrong_dtypes_before_any_device_work():
