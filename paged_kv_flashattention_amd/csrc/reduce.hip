@@ -67,16 +67,75 @@ __global__ __launch_bounds__(64 * kReduceRowsPerBlock) void splitk_reduce_kernel
   if (lane == 0 && a.lse_out) a.lse_out[r] = live ? m + __logf(tot) : kNegInf;
 }
 
+// Few partitions (S <= SMAX, the common case): every load of a row -- its S lse
+// values and S partial outputs -- is issued before any is used, so a row costs
+// one memory round trip instead of a chain of dependent ones.  Each thread owns 4
+// consecutive output columns of one row (D / 4 threads per row).
+constexpr int kReduceFewThreads = 256;
+
+template <int D, int SMAX>
+__global__ __launch_bounds__(kReduceFewThreads) void splitk_reduce_few_kernel(ReduceArgs a) {
+  constexpr int CH = D / 4;
+  const long long i = (long long)blockIdx.x * kReduceFewThreads + threadIdx.x;
+  const int r = (int)(i / CH);
+  const int c = (int)(i - (long long)r * CH);
+  if (r >= a.R) return;
+  const float* lse_row = a.part_lse + (size_t)r * a.S;
+  const float* o_row = a.part_o + (size_t)r * a.S * D + 4 * c;
+  float lse[SMAX];
+  f32x4 o[SMAX];
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k) lse[k] = k < a.S ? lse_row[k] : kNegInf;
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k)
+    if (k < a.S) o[k] = *reinterpret_cast<const f32x4*>(o_row + (size_t)k * D);
+  float m = kNegInf;
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k) m = fmaxf(m, lse[k]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k)
+      if (k < a.S) {
+        const float w = __expf(lse[k] - m);
+        tot += w;
+        acc += w * o[k];
+      }
+  }
+  const bool live = tot > 0.f;
+  const float inv = live ? 1.f / tot : 0.f;
+  *reinterpret_cast<u32x2*>(a.out + (size_t)r * D + 4 * c) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (c == 0 && a.lse_out) a.lse_out[r] = live ? m + __logf(tot) : kNegInf;
+}
+
+template <int D>
+static void launch_reduce_d(const ReduceArgs& a, hipStream_t stream, unsigned& blocks,
+                            bool& few) {
+  few = a.S <= 8;
+  if (few) {
+    blocks = (unsigned)(((long long)a.R * (D / 4) + kReduceFewThreads - 1) / kReduceFewThreads);
+    if (a.S <= 4)
+      hipLaunchKernelGGL((splitk_reduce_few_kernel<D, 4>), dim3(blocks), dim3(kReduceFewThreads),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((splitk_reduce_few_kernel<D, 8>), dim3(blocks), dim3(kReduceFewThreads),
+                         0, stream, a);
+    return;
+  }
+  blocks = (a.R + kReduceRowsPerBlock - 1) / kReduceRowsPerBlock;
+  hipLaunchKernelGGL(splitk_reduce_kernel<D>, dim3(blocks), dim3(64 * kReduceRowsPerBlock), 0,
+                     stream, a);
+}
+
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, char* desc, size_t desc_len) {
-  dim3 grid((a.R + kReduceRowsPerBlock - 1) / kReduceRowsPerBlock);
-  if (a.D == 128)
-    hipLaunchKernelGGL(splitk_reduce_kernel<128>, grid, dim3(64 * kReduceRowsPerBlock), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<64>, grid, dim3(64 * kReduceRowsPerBlock), 0,
-                       stream, a);
-  snprintf(desc, desc_len, "splitk_reduce<D=%d> grid=%d rows=%d splits=%d", a.D, grid.x, a.R,
-           a.S);
+  unsigned blocks = 0;
+  bool few = false;
+  if (a.D == 128) launch_reduce_d<128>(a, stream, blocks, few);
+  else launch_reduce_d<64>(a, stream, blocks, few);
+  snprintf(desc, desc_len, "splitk_reduce%s<D=%d> grid=%u rows=%d splits=%d", few ? "_few" : "",
+           a.D, blocks, a.R, a.S);
   return hipGetLastError();
 }
 
