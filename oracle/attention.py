@@ -32,6 +32,12 @@ R4  Sliding window: the pages list sliding windows among the masks a serving
     query at absolute position p sees key j only if p - w < j (its last w
     positions, itself included), on top of the causal condition when causal;
     without causal only this lower bound applies.  w = 0 means no window.
+R5  ALiBi: "The Stack Below the Stack (Part 2)", section 5, names ALiBi among the
+    score modifications a FlexAttention function expresses, without a formula.
+    Reading: with one slope per query head (given by the caller), the score of
+    query h at absolute position p against key j becomes
+    scale * q . k + slope_h * (j - p), i.e. a linear penalty on the distance to
+    earlier keys for positive slopes.  No slopes means no bias.
 """
 
 from __future__ import annotations
@@ -88,12 +94,15 @@ def gather_sequence_kv(pool, table_row, seq_len: int, page_size: int) -> np.ndar
     return dense[:seq_len]
 
 
-def attend_rows(q_rows, k, v, scale: float, visible, first=None):
+def attend_rows(q_rows, k, v, scale: float, visible, first=None, slope: float = 0.0,
+                pos=None):
     """Plain softmax attention for a set of query rows against one key head.
 
     ``q_rows`` [n, D], ``k``/``v`` [L, D], ``visible`` [n] = number of leading
     keys each row may see; ``first`` [n] (optional) = index of the first key
-    each row may see (R4; default 0).  Returns (O [n, D], lse [n]) in float64.
+    each row may see (R4; default 0); ``slope`` with ``pos`` [n] (the rows'
+    absolute positions) adds slope * (j - pos_i) to every score (R5).  Returns
+    (O [n, D], lse [n]) in float64.
 
     This is the definition the tiled method must reproduce exactly ("8.
     Kernels and Attention Backends", "Attention is an I/O problem": scores
@@ -112,6 +121,9 @@ def attend_rows(q_rows, k, v, scale: float, visible, first=None):
     if n == 0 or L == 0:
         return out, lse
     s = scale * (q_rows @ k.T)                                   # [n, L]
+    if slope != 0.0:
+        pos = np.asarray(pos, dtype=np.float64).reshape(n)
+        s = s + float(slope) * (np.arange(L, dtype=np.float64)[None, :] - pos[:, None])
     mask = np.arange(L)[None, :] >= visible[:, None]
     if first is not None:
         first = np.asarray(first, dtype=np.int64).reshape(n)
@@ -152,7 +164,7 @@ def _first_visible(seq_len: int, q_len: int, window: int) -> np.ndarray:
 
 
 def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
-                  scale: float, causal: bool, page_size: int, window: int = 0):
+                  scale: float, causal: bool, page_size: int, window: int = 0, alibi=None):
     """Exact attention of every query row; returns (O [T, Hq, D], lse [T, Hq]).
 
     Streams one (sequence, key head) at a time so that memory stays bounded
@@ -179,16 +191,20 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
         vb = gather_sequence_kv(v_pool, block_tables[b], L, page_size)
         vis = _visible_counts(L, t1 - t0, causal)
         first = _first_visible(L, t1 - t0, window)
+        pos = L - (t1 - t0) + np.arange(t1 - t0)                        # R2
         for h in range(Hq):
             kvh = h // G                                                # R1
-            o, ls = attend_rows(q[t0:t1, h], kb[:, kvh], vb[:, kvh], scale, vis, first)
+            slope = 0.0 if alibi is None else float(alibi[h])          # R5
+            o, ls = attend_rows(q[t0:t1, h], kb[:, kvh], vb[:, kvh], scale, vis, first,
+                                slope, pos)
             out[t0:t1, h] = o
             lse[t0:t1, h] = ls
     return out, lse
 
 
 def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
-                       scale: float, causal: bool, page_size: int, rows, window: int = 0):
+                       scale: float, causal: bool, page_size: int, rows, window: int = 0,
+                       alibi=None):
     """Same as :func:`attention_ref` for selected (token, head) pairs only.
 
     Used at full workload sizes, where the oracle computes sampled outputs one
@@ -217,8 +233,10 @@ def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q
         for i, t, h in items:
             kvh = h // G
             i0 = t - int(cu[b])
+            slope = 0.0 if alibi is None else float(alibi[h])
             o, ls = attend_rows(q[t:t + 1, h], kb[:, kvh], vb[:, kvh], scale,
-                                vis_all[i0:i0 + 1], first_all[i0:i0 + 1])
+                                vis_all[i0:i0 + 1], first_all[i0:i0 + 1], slope,
+                                [L - q_len + i0])
             out[i], lse[i] = o[0], ls[0]
     return out, lse
 

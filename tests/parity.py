@@ -28,22 +28,22 @@ def pools_after_write(case):
                                case.block_tables.cpu().numpy(), case.page_size)
 
 
-def oracle_full(case, kp=None, vp=None, causal=None):
+def oracle_full(case, kp=None, vp=None, causal=None, alibi=None):
     if kp is None:
         kp, vp = pools_after_write(case)
     return oracle.attention_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
                                 case.seq_lens_k.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
                                 case.scale, case.causal if causal is None else causal,
-                                case.page_size, case.window)
+                                case.page_size, case.window, alibi)
 
 
-def oracle_rows(case, rows, kp=None, vp=None):
+def oracle_rows(case, rows, kp=None, vp=None, alibi=None):
     if kp is None:
         kp, vp = pools_after_write(case)
     return oracle.attention_rows_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
                                      case.seq_lens_k.cpu().numpy(),
                                      case.cu_seqlens_q.cpu().numpy(), case.scale, case.causal,
-                                     case.page_size, rows, case.window)
+                                     case.page_size, rows, case.window, alibi)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:

@@ -39,9 +39,10 @@ def _bf16(x):
             for v in x.ravel()]
 
 
-def brute_attention(case, window=None):
+def brute_attention(case, window=None, alibi=None):
     """Loops over sequences, rows, heads and keys; math.exp and math.fsum only.
-    With a sliding window w > 0 the row at position p takes keys j > p - w only."""
+    With a sliding window w > 0 the row at position p takes keys j > p - w only;
+    with ALiBi slopes the score of key j gets slope_h * (j - p) added."""
     w = case.window if window is None else window
     q = bits(case.q)
     kp = bits(case.k_pool)
@@ -71,7 +72,8 @@ def brute_attention(case, window=None):
                         continue
                     page, slot = int(bt[b][j // ps]), j % ps
                     kv = _bf16(kp[page, slot, kvh])
-                    scores.append(case.scale * math.fsum(a * c for a, c in zip(qv, kv)))
+                    bias = 0.0 if alibi is None else float(alibi[h]) * (j - pos)
+                    scores.append(case.scale * math.fsum(a * c for a, c in zip(qv, kv)) + bias)
                     vrows.append(_bf16(vp[page, slot, kvh]))
                 if not scores:
                     continue
@@ -84,11 +86,12 @@ def brute_attention(case, window=None):
     return out, lse
 
 
-def run_oracle(case, window=None):
+def run_oracle(case, window=None, alibi=None):
     return oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
                                 case.block_tables.numpy(), case.seq_lens_k.numpy(),
                                 case.cu_seqlens_q.numpy(), case.scale, case.causal,
-                                case.page_size, case.window if window is None else window)
+                                case.page_size, case.window if window is None else window,
+                                alibi)
 
 
 def assert_close(a, b, tol=1e-12):
@@ -434,21 +437,21 @@ def test_workload_units_at_the_five_sizes():
 # planted mistakes: each must be caught by a pin above
 # ----------------------------------------------------------------------------
 
-def _mut_drop_scale(q_rows, k, v, scale, visible, first=None):
-    return _orig_attend(q_rows, k, v, 1.0, visible, first)
+def _mut_drop_scale(q_rows, k, v, scale, visible, *rest):
+    return _orig_attend(q_rows, k, v, 1.0, visible, *rest)
 
 
-def _mut_no_mask(q_rows, k, v, scale, visible, first=None):
+def _mut_no_mask(q_rows, k, v, scale, visible, *rest):
     return _orig_attend(q_rows, k, v, scale, np.full(len(np.atleast_1d(visible)), k.shape[0]))
 
 
-def _mut_off_by_one_causal(q_rows, k, v, scale, visible, first=None):
+def _mut_off_by_one_causal(q_rows, k, v, scale, visible, *rest):
     vis = np.asarray(visible) - 1
-    return _orig_attend(q_rows, k, v, scale, np.maximum(vis, 0), first)
+    return _orig_attend(q_rows, k, v, scale, np.maximum(vis, 0), *rest)
 
 
-def _mut_transposed_value(q_rows, k, v, scale, visible, first=None):
-    o, l = _orig_attend(q_rows, k, v, scale, visible, first)
+def _mut_transposed_value(q_rows, k, v, scale, visible, *rest):
+    o, l = _orig_attend(q_rows, k, v, scale, visible, *rest)
     return o[:, ::-1].copy(), l
 
 
@@ -566,4 +569,68 @@ def test_planted_window_mistakes_are_caught(monkeypatch, mutant):
     else:
         monkeypatch.setattr(oa, "_first_visible", lambda L, n, w: real(L, n, 0))
     o, _ = run_oracle(case)
+    assert np.abs(o - ob).max() > 1e-6
+
+
+# ----------------------------------------------------------------------------
+# ALiBi (R5)
+# ----------------------------------------------------------------------------
+
+SLOPES = np.array([0.5, 0.25, 0.125, 0.0625])
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 9)])
+def test_alibi_matches_brute_force(causal, window):
+    case = _window_case(window, causal, seed=44)
+    o, l = run_oracle(case, alibi=SLOPES)
+    ob, lb = brute_attention(case, alibi=SLOPES)
+    assert_close(o, ob)
+    assert_close(l, lb)
+
+
+def test_alibi_with_zero_query_gives_geometric_weights():
+    """q = 0: every score is the bias alone, so a causal row at position p weights key
+    j by exp(-s (p - j)) / sum_i exp(-s (p - i)), a geometric series in closed form."""
+    case = make_case("ag", seq_lens=[30], q_lens=[1], Hq=2, Hkv=1, D=4, page_size=4, seed=2,
+                     causal=True)
+    case.q = torch.zeros_like(case.q)
+    slopes = np.array([0.3, 1.1])
+    o, lse = run_oracle(case, alibi=slopes)
+    v = oa.gather_sequence_kv(bits(case.v_pool), case.block_tables.numpy()[0], 30, 4)[:, 0]
+    for h, s_ in enumerate(slopes):
+        r = math.exp(-s_)
+        w = np.array([r ** (29 - j) for j in range(30)])
+        den = (1 - r ** 30) / (1 - r)                      # sum of r^k, k = 0..29
+        assert abs(w.sum() - den) < 1e-12
+        assert np.abs(o[0, h] - (w @ v) / den).max() < 1e-12
+        assert abs(lse[0, h] - math.log(den)) < 1e-12
+
+
+def test_alibi_is_a_shift_of_a_position_independent_bias():
+    """slope * (j - p) differs from slope * j by a per-row constant: the same O, and
+    lse lower by slope * p."""
+    case = _window_case(0, True, seed=45)
+    o1, l1 = run_oracle(case, alibi=SLOPES)
+    q, kp, vp, bt = bits(case.q), bits(case.k_pool), bits(case.v_pool), case.block_tables.numpy()
+    cu = case.cu_seqlens_q.numpy()
+    for b, L in enumerate(case.seq_lens):
+        n = int(cu[b + 1] - cu[b])
+        k = oa.gather_sequence_kv(kp, bt[b], L, 3)
+        v = oa.gather_sequence_kv(vp, bt[b], L, 3)
+        for h in range(4):
+            rows = oracle.bf16_bits_to_f64(q[int(cu[b]):int(cu[b]) + n, h])
+            vis = L - n + np.arange(n) + 1
+            o0, l0 = oracle.attend_rows(rows, k[:, h // 2], v[:, h // 2], case.scale, vis, None,
+                                        SLOPES[h], np.zeros(n))
+            pos = L - n + np.arange(n)
+            assert np.abs(o0 - o1[int(cu[b]):int(cu[b]) + n, h]).max() < 1e-12
+            assert np.abs(l0 - SLOPES[h] * pos - l1[int(cu[b]):int(cu[b]) + n, h]).max() < 1e-9
+
+
+@pytest.mark.parametrize("mutant", ["sign", "scaled"])
+def test_planted_alibi_mistakes_are_caught(mutant):
+    case = _window_case(0, True, seed=46)
+    ob, _ = brute_attention(case, alibi=SLOPES)
+    wrong = -SLOPES if mutant == "sign" else SLOPES * case.scale
+    o, _ = run_oracle(case, alibi=wrong)
     assert np.abs(o - ob).max() > 1e-6
