@@ -325,6 +325,13 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * seq_len - 1, so it sees keys seq_len - w .. seq_len - 1.  w = 0: no window.
  * Document masks need no option: every sequence of a ragged batch is one document.
  *
+ * ALiBi: the same section names ALiBi among the score modifications, again without
+ * a formula.  This library's: with alibi_slopes (device float32 [Hq], one slope per
+ * query head, 4-byte aligned) the score of query head h at absolute position p
+ * against key j becomes softmax_scale * q . k + slope_h * (j - p); NULL: no bias.
+ * lse outputs include the bias.  The bias composes with the causal bound and the
+ * window.
+ *
  * The _ex entry points take every option of an operation in one struct; the
  * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
  * negative window PA_ERR_SHAPE.
@@ -335,6 +342,7 @@ typedef struct {
   int32_t kv_fp8;       /* 0: bf16 pools; 1: E4M3 code pools (paged_attn_decode_fp8)      */
   float k_scale;        /* kv_fp8 only                                                    */
   float v_scale;        /* kv_fp8 only                                                    */
+  const float* alibi_slopes;  /* NULL, or device [Hq] float32 slopes (ALiBi above)        */
 } pa_decode_opts;
 
 typedef struct {
@@ -342,6 +350,7 @@ typedef struct {
   int32_t window_left;  /* 0, or w > 0: row at position p sees keys j > p - w only        */
   int32_t num_splits;   /* key parts as paged_attn_prefill_varlen_splitk's: 1 plain,
                            <= 0 the library's choice (may need a workspace)               */
+  const float* alibi_slopes;  /* NULL, or device [Hq] float32 slopes (ALiBi above)        */
 } pa_prefill_opts;
 
 /*
@@ -365,7 +374,9 @@ size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, 
 /*
  * paged_attn_prefill_ex -- paged_attn_prefill_varlen(_splitk) with options.  With a
  * window, a query tile starts at the 64-key tile holding its first row's lower
- * bound, so key tiles wholly below every row's window are never read.
+ * bound, so key tiles wholly below every row's window are never read.  A window or
+ * ALiBi selects a kernel variant with those steps compiled in (two more vector
+ * operations per score for ALiBi); without them the plain kernel runs.
  */
 int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* cu_seqlens_q,

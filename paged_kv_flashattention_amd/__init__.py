@@ -234,16 +234,19 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
                       max_seq_len: Optional[int] = None, num_splits: int = 0,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
-                      stream=None, validate: bool = False, window_left: int = 0):
+                      stream=None, validate: bool = False, window_left: int = 0,
+                      alibi_slopes: Optional[torch.Tensor] = None):
     """Decode attention: q [B, Hq, D] against each sequence's paged history.
 
     ``max_seq_len`` is a host-side bound of ``seq_lens``; if omitted it is read
     from the device (a synchronisation).  Returns out [B, Hq, D] bf16, and the
     natural-log lse [B, Hq] fp32 as well when ``return_lse``.  ``window_left`` = w > 0
-    restricts each row to its last w keys (sliding window; see paged_attn_decode_ex).
+    restricts each row to its last w keys (sliding window; see paged_attn_decode_ex);
+    ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
     """
     return _decode(None, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
-                   num_splits, out, lse, workspace, return_lse, stream, validate, window_left)
+                   num_splits, out, lse, workspace, return_lse, stream, validate, window_left,
+                   alibi_slopes)
 
 
 def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
@@ -251,13 +254,14 @@ def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_sca
                           num_splits: int = 0, out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
-                          stream=None, validate: bool = False, window_left: int = 0):
+                          stream=None, validate: bool = False, window_left: int = 0,
+                          alibi_slopes: Optional[torch.Tensor] = None):
     """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
     decode(code) * k_scale, values for decode(code) * v_scale.  Arguments and
     results are paged_attn_decode's."""
     return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
                    softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
-                   stream, validate, window_left)
+                   stream, validate, window_left, alibi_slopes)
 
 
 def _window(window_left) -> int:
@@ -267,8 +271,20 @@ def _window(window_left) -> int:
     return w
 
 
+def _alibi(slopes, Hq, dev):
+    """Device pointer of an ALiBi slope vector (float32 [Hq]), or None."""
+    if slopes is None:
+        return None
+    _need_dtype(slopes, "alibi_slopes", torch.float32)
+    _need(slopes, "alibi_slopes", torch.float32, 1, dev)
+    if slopes.shape[0] != Hq:
+        raise ValueError(f"alibi_slopes must have Hq={Hq} entries, got {slopes.shape[0]}")
+    return slopes.data_ptr()
+
+
 def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
-            num_splits, out, lse, workspace, return_lse, stream, validate, window_left=0):
+            num_splits, out, lse, workspace, return_lse, stream, validate, window_left=0,
+            alibi_slopes=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -309,8 +325,9 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
     if lse is not None:
         _need(lse, "lse", torch.float32, 2, dev)
     lib = load_library()
+    alibi_ptr = _alibi(alibi_slopes, Hq, dev)
     opts = _lib.DecodeOpts(int(num_splits), window_left, 0 if scales is None else 1,
-                           *(scales if scales is not None else (1.0, 1.0)))
+                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
     if need and workspace is None:
@@ -320,7 +337,7 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
-        if window_left:
+        if window_left or alibi_ptr is not None:
             _check(lib.paged_attn_decode_ex(*head, int(max_seq_len), ctypes.byref(opts),
                                             *tail[2:]))
         elif scales is None:
@@ -396,16 +413,18 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                               max_q_len: Optional[int] = None,
                               out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = False,
-                              stream=None, validate: bool = False, window_left: int = 0):
+                              stream=None, validate: bool = False, window_left: int = 0,
+                              alibi_slopes: Optional[torch.Tensor] = None):
     """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
 
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
     omitted it is read from the device (a synchronisation).  ``window_left`` = w > 0
-    restricts the row at position p to keys j > p - w (sliding window).
+    restricts the row at position p to keys j > p - w (sliding window);
+    ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
     """
     return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
                     softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate,
-                    window_left)
+                    window_left, alibi_slopes)
 
 
 def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:
@@ -425,16 +444,18 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
                                      lse: Optional[torch.Tensor] = None,
                                      workspace: Optional[torch.Tensor] = None,
                                      return_lse: bool = False, stream=None,
-                                     validate: bool = False, window_left: int = 0):
+                                     validate: bool = False, window_left: int = 0,
+                                     alibi_slopes: Optional[torch.Tensor] = None):
     """Ragged prefill with long key ranges cut into at most ``num_splits`` parts
     (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
-                    validate, window_left)
+                    validate, window_left, alibi_slopes)
 
 
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
-             causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0):
+             causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
+             alibi_slopes=None):
     window_left = _window(window_left)
     _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
             (v_pool, "v_pool", torch.bfloat16), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
@@ -475,7 +496,9 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
     args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(cu_seqlens_q),
             _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
             P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0)
-    if window_left and split is None:
+    alibi_ptr = _alibi(alibi_slopes, Hq, dev)
+    general = bool(window_left) or alibi_ptr is not None
+    if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
         num_splits, workspace = split
@@ -489,8 +512,8 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
     with torch.cuda.device(dev):
         if split is None:
             _check(lib.paged_attn_prefill_varlen(*args, _stream(stream)))
-        elif window_left:
-            opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits)
+        elif general:
+            opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

@@ -22,13 +22,13 @@ class DecodeOpts(ctypes.Structure):
     """pa_decode_opts"""
     _fields_ = [("num_splits", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
 
 
 class PrefillOpts(ctypes.Structure):
     """pa_prefill_opts"""
     _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)

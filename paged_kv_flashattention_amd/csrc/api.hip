@@ -98,7 +98,7 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
-                float v_scale = 1.f, int32_t window = 0) {
+                float v_scale = 1.f, int32_t window = 0, const float* alibi = nullptr) {
   if (B < 0 || max_seq_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
@@ -111,6 +111,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   }
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
+  if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u))
+    return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   // with a window every row walks at most window + 31 keys (its lower bound rounded
@@ -135,6 +137,7 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.kv_fp8 = fp8 ? 1 : 0;
   a.v_scale = fp8 ? v_scale : 1.f;
   a.window = window;
+  a.alibi = alibi;
   return PA_OK;
 }
 
@@ -186,12 +189,13 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
-                float k_scale, float v_scale, void* stream, int32_t window = 0) {
+                float k_scale, float v_scale, void* stream, int32_t window = 0,
+                const float* alibi = nullptr) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
                        num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
-                       num_splits, fp8, k_scale, v_scale, window);
+                       num_splits, fp8, k_scale, v_scale, window, alibi);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
@@ -266,7 +270,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  const int32_t* block_tables, int32_t B, int32_t Tq, int32_t max_q_len,
                  int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
-                 void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0) {
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
+                 const float* alibi = nullptr) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -283,6 +288,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     return fail(PA_ERR_MISALIGNED, "%s: data pointers must be 16-byte aligned", what);
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
+  if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u))
+    return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
   if (max_q_len > Tq) max_q_len = Tq;
   const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits);
   // one work-group per (query head, sequence, 128- or 256-row query tile, key
@@ -311,6 +318,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.causal = causal ? 1 : 0;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.window = window;
+  a.alibi = alibi;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -519,7 +527,7 @@ int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k
                      max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
                      opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
                      opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
-                     stream, opts->window_left);
+                     stream, opts->window_left, opts->alibi_slopes);
 }
 
 size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -541,7 +549,7 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
   return prefill_impl("prefill_ex", out, lse_out, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                       block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
-                      workspace_bytes, stream, opts->window_left);
+                      workspace_bytes, stream, opts->window_left, opts->alibi_slopes);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

@@ -255,6 +255,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[head n][D/4 * g + 8 kk + j].
   const bool head_ok = n < a.G;
   const int h = kvh * a.G + n;
+  // ALiBi: this head's slope in log2 units (the row sits at position L - 1)
+  const float slope = a.alibi && head_ok ? a.alibi[h] * kLog2e : 0.f;
   u32x4 qb[D / 32];
   {
     const uint16_t* qp = a.q + ((size_t)b * a.Hq + (head_ok ? h : 0)) * D + (D / 4) * g;
@@ -330,6 +332,13 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       for (int i = 0; i < 4; ++i) {
         s[i] = sa[i] * a.scale_log2;
         s[4 + i] = sb[i] * a.scale_log2;
+      }
+      if (a.alibi) {
+        // score of key c0 + 4 g + o (o = j, or 12 + j for the second half) gets
+        // slope * (key - (L - 1))
+        const float fb = (float)(c0 + 4 * g - (L - 1));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] = fmaf(slope, fb + (float)(j < 4 ? j : 12 + j), s[j]);
       }
       if (c0 + 32 > k_end || c0 < lo) {
         // keys past the end get -inf and V rows 0 (they may hold anything); keys

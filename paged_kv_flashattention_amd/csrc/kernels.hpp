@@ -25,6 +25,7 @@ struct DecodeArgs {
   int kv_fp8;                    // pools hold FP8 E4M3 codes (uint8) instead of bf16
   float v_scale;                 // value of one V code unit (1 for bf16 pools)
   int window;                    // sliding window: keys j >= seq_len - window only (0: none)
+  const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
 };
 
 struct ReduceArgs {
@@ -64,6 +65,7 @@ struct PrefillArgs {
   int n_qt;                      // query tiles per sequence (of the longest)
   int xcd_groups;                // (sequence, KV head) groups per XCD, or 0: plain order
   int window;                    // sliding window: position p sees keys j > p - window (0: none)
+  const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
   int S;                         // key-range parts per query tile at most (1: no split)
   int part_min;                  // 64-key tiles per part at least
   float* part_o;                 // [Tq * Hq, S, D] partial outputs        (S > 1)

@@ -46,6 +46,7 @@ struct PfTiles {
   int parts;   // key-range parts
 };
 
+template <bool GEN>
 __device__ __forceinline__ PfTiles pf_tiles(const PrefillArgs& a, int L, int q_len, int r0,
                                             int bm) {
   const int rows = min(bm, q_len - r0);
@@ -53,7 +54,8 @@ __device__ __forceinline__ PfTiles pf_tiles(const PrefillArgs& a, int L, int q_l
   if (a.causal) k_lim = min(L, max(0, L - q_len + r0 + rows));
   PfTiles t;
   t.n = (k_lim + kPfBN - 1) / kPfBN;
-  const int k_lo = a.window > 0 ? max(0, L - q_len + r0 - a.window + 1) : 0;
+  // only the general variant (window, ALiBi) sees a window
+  const int k_lo = GEN && a.window > 0 ? max(0, L - q_len + r0 - a.window + 1) : 0;
   t.first = min(k_lo / kPfBN, t.n);
   t.parts = a.S > 1 ? max(1, min(a.S, (t.n - t.first) / a.part_min)) : 1;
   return t;
@@ -187,7 +189,7 @@ __device__ __forceinline__ void pf_zero_tail(uint16_t* vst, int k0, int L, int w
 }
 
 // W waves (32 W query rows) per work-group; 8 W waves per CU.
-template <int D, int W, bool WIN>
+template <int D, int W, bool GEN>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // keys past this work-group's last row are never needed; with key splitting this
   // work-group covers tiles tile_lo .. tile_hi - 1 of them
   const int shift = L - q_len;                 // position of row r is shift + r
-  const PfTiles tw = pf_tiles(a, L, q_len, r_wg, kPfBM);
+  const PfTiles tw = pf_tiles<GEN>(a, L, q_len, r_wg, kPfBM);
   if (part >= tw.parts) return;
   const int tile_lo = tw.first + part * (tw.n - tw.first) / tw.parts;
   const int tile_hi = tw.first + (part + 1) * (tw.n - tw.first) / tw.parts;
@@ -257,8 +259,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int w_pos_min = shift + r_w;
   const int lim = a.causal ? min(L - 1, my_pos) : L - 1;   // last visible key
   // sliding window: first visible key of this row, and the largest of the wave's
-  const int lo_row = WIN ? my_pos - a.window + 1 : INT_MIN;
-  const int w_lo_max = WIN ? shift + r_w + 31 - a.window + 1 : INT_MIN;
+  const int lo_row = GEN && a.window > 0 ? my_pos - a.window + 1 : INT_MIN;
+  const int w_lo_max = GEN && a.window > 0 ? shift + r_w + 31 - a.window + 1 : INT_MIN;
+  // ALiBi: the head's slope in raw score units (scores are scaled later), and the
+  // distance of this lane's first key in a block from its row, less kb0
+  const float slope_raw = GEN && a.alibi ? a.alibi[h] * kLog2e / a.scale_log2 : 0.f;
+  const int dist0 = 4 * hh - my_pos;
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
   u32x4 qb[D / 16];
@@ -354,18 +360,28 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     mt = fmaxf(mt, sc[15]);
     return xor32_max(mt) * a.scale_log2;
   };
-  // -inf for keys past the end, (causal) above the diagonal and (window) below a
-  // row's window; only blocks that touch one of these boundaries need it
+  // ALiBi bias (general variant), then -inf for keys past the end, (causal) above
+  // the diagonal and (window) below a row's window; only blocks that touch one of
+  // these boundaries need the second part.  Called once per block, right after its
+  // scores are formed.
   auto mask = [&](f32x16& sc, int kb0) {
+    if (GEN && a.alibi) {
+      const float fb = (float)(kb0 + dist0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * j + i] = fmaf(slope_raw, fb + (float)(8 * j + i), sc[4 * j + i]);
+    }
     const bool need =
-        (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (WIN && kb0 < w_lo_max);
+        (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (GEN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb0 + 8 * j + 4 * hh + i;
-          if (key > lim || (WIN && key < lo_row)) sc[4 * j + i] = kNegInf;
+          if (key > lim || (GEN && key < lo_row)) sc[4 * j + i] = kNegInf;
         }
     }
   };
@@ -594,7 +610,8 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   int L = a.seq_lens_k[b];
   const int cap = a.max_pages * a.page_size;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const PfTiles tw = pf_tiles(a, L, q_len, r_wg, bm);
+  const PfTiles tw = a.window > 0 ? pf_tiles<true>(a, L, q_len, r_wg, bm)
+                                   : pf_tiles<false>(a, L, q_len, r_wg, bm);
   if (tw.parts <= 1) return;
   const int row = r_wg + rb * RPB + threadIdx.x / CH;
   const int c = threadIdx.x % CH;
@@ -629,25 +646,26 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
-template <int D, int W, bool WIN>
+template <int D, int W, bool GEN>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
   // more than 64 KiB of dynamic LDS must be requested once per process
   static const hipError_t attr = PfLds<D>::BYTES > 65536
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, WIN>),
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
       : hipSuccess;
   if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
-  hipLaunchKernelGGL((prefill_kernel<D, W, WIN>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, W, GEN>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
                      a);
   return hipGetLastError();
 }
 
-// the sliding-window bound is compiled only into the windowed variant
+// the sliding-window bound and the ALiBi bias are compiled only into the general
+// variant
 template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  return a.window > 0 ? launch_prefill_w<D, W, true>(a, stream)
-                      : launch_prefill_w<D, W, false>(a, stream);
+  return a.window > 0 || a.alibi ? launch_prefill_w<D, W, true>(a, stream)
+                                 : launch_prefill_w<D, W, false>(a, stream);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
