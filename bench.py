@@ -13,6 +13,10 @@ TFLOP/s (4 x 4096, Hq 32, Hkv 8), long-context decode (8 x 131072), a 512-token
 prefill chunk over a 32,768-token history (key-split prefill), and the mixed
 ragged step, each timed the same way.
 
+For the HBM-bound headline the roofline object also carries the bandwidth of a
+plain streaming read of a 4 GiB buffer measured on the same GPU (libpa_stream.so)
+and the dominant kernel's fraction of it.
+
 One JSON line is printed.  Only one GPU is used: --gpus above 1 is refused.
 """
 
@@ -372,6 +376,46 @@ def traffic_pass(steps):
 
 
 # ---------------------------------------------------------------------------
+# the box's streaming-read bandwidth (reference for the HBM-bound kernels)
+# ---------------------------------------------------------------------------
+
+STREAM_BYTES = 4 << 30
+
+
+def stream_read_gbs(iters=10):
+    """Best GB/s of a plain streaming read of a 4 GiB buffer (libpa_stream.so, built
+    with the library), over a few grid sizes; HIP events on the launch stream."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "paged_kv_flashattention_amd", "libpa_stream.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.pa_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p]
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    best = (0.0, 0)
+    for blocks in (16384, 65536, 131072, 262144):
+        sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        for _ in range(2):
+            if fn(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), blocks, s):
+                raise RuntimeError("pa_stream_read rejected its arguments")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), blocks, s)
+        b.record()
+        torch.cuda.synchronize()
+        gbs = STREAM_BYTES / (a.elapsed_time(b) / iters * 1e-3) / 1e9
+        best = max(best, (gbs, blocks))
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+# ---------------------------------------------------------------------------
 # oracle baseline on the host cores
 # ---------------------------------------------------------------------------
 
@@ -475,6 +519,13 @@ def main():
     }
     del step
     torch.cuda.empty_cache()
+    if bound == "hbm":
+        read_gbs, read_blocks = stream_read_gbs()
+        result["roofline"]["measured_read_GBs"] = round(read_gbs, 1)
+        result["roofline"]["frac_of_measured_read"] = round(achieved / read_gbs, 4)
+        log(f"[bench] streaming read of {STREAM_BYTES >> 30} GiB: {read_gbs:.1f} GB/s "
+            f"({read_blocks} work-groups); the dominant kernel reaches "
+            f"{achieved / read_gbs:.1%} of it")
 
     if not args.no_secondary and args.workload == "qwen7b_decode":
         # the other workloads, same timing; the long-context decode both with the 64

@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "reduce.hip", "prefill.hip"]
+# the benchmark's streaming-read reference kernel, in a library of its own
+STREAM_SOURCE = "stream_read.hip"
+STREAM_LIB_PATH = os.path.join(HERE, "libpa_stream.so")
 
 ARCH = "gfx950"
 
@@ -53,11 +56,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, path):
+    tmp = path + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, path)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libpaged_attn.so; returns its path."""
+    """Compile every HIP source and link libpaged_attn.so (and the benchmark's
+    libpa_stream.so); returns the path of libpaged_attn.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    srcs = SOURCES + [STREAM_SOURCE]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[-1:], STREAM_LIB_PATH)
+    objs = objs[:-1]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
