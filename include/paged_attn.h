@@ -351,6 +351,9 @@ typedef struct {
   int32_t num_splits;   /* key parts as paged_attn_prefill_varlen_splitk's: 1 plain,
                            <= 0 the library's choice (may need a workspace)               */
   const float* alibi_slopes;  /* NULL, or device [Hq] float32 slopes (ALiBi above)        */
+  int32_t kv_fp8;       /* 0: bf16 pools; 1: E4M3 code pools (format above)               */
+  float k_scale;        /* kv_fp8 only                                                    */
+  float v_scale;        /* kv_fp8 only                                                    */
 } pa_prefill_opts;
 
 /*
@@ -376,7 +379,11 @@ size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, 
  * window, a query tile starts at the 64-key tile holding its first row's lower
  * bound, so key tiles wholly below every row's window are never read.  A window or
  * ALiBi selects a kernel variant with those steps compiled in (two more vector
- * operations per score for ALiBi); without them the plain kernel runs.
+ * operations per score for ALiBi); without them the plain kernel runs.  With
+ * kv_fp8 the pools hold E4M3 codes: each tile's codes are loaded into registers and
+ * widened to bf16 (exactly) into the same LDS tile the bf16 path fills, k_scale
+ * folds into the softmax scale and v_scale into the final normalisation, as in
+ * paged_attn_decode_fp8.
  */
 int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* cu_seqlens_q,

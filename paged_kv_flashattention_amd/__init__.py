@@ -14,7 +14,8 @@ Entry points (same names as the C ABI):
 * :func:`paged_attn_splitk_reduce` -- the merge on its own;
 * :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA;
 * :func:`paged_attn_prefill_varlen_splitk` -- the same with long key ranges cut
-  into parts computed by separate work-groups and merged.
+  into parts computed by separate work-groups and merged;
+* :func:`paged_attn_prefill_varlen_fp8` -- prefill over FP8 E4M3 pools.
 
 Data contract: bf16 Q / K / V / outputs, int32 indices (int64 is refused, not
 cast), fp32 lse, contiguous tensors on one GPU.  FP8 pools are uint8 (or
@@ -35,7 +36,8 @@ __all__ = [
     "PagedAttnError", "kv_page_write", "kv_page_write_fp8", "paged_attn_decode",
     "paged_attn_decode_fp8", "paged_attn_decode_partials",
     "paged_attn_splitk_reduce",
-    "paged_attn_prefill_varlen", "paged_attn_prefill_varlen_splitk", "prefill_num_splits",
+    "paged_attn_prefill_varlen", "paged_attn_prefill_varlen_splitk",
+    "paged_attn_prefill_varlen_fp8", "prefill_num_splits",
     "prefill_workspace_bytes", "decode_num_splits", "decode_workspace_bytes",
     "describe_launch", "library_path", "load_library",
 ]
@@ -427,6 +429,23 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                     window_left, alibi_slopes)
 
 
+def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
+                                  softmax_scale: float, k_scale: float, v_scale: float,
+                                  causal: bool = True, max_q_len: Optional[int] = None,
+                                  num_splits: int = 1, out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  return_lse: bool = False, stream=None,
+                                  validate: bool = False, window_left: int = 0,
+                                  alibi_slopes: Optional[torch.Tensor] = None):
+    """Ragged prefill over FP8 E4M3 pools (uint8 codes; keys stand for decode(code) *
+    k_scale, values for decode(code) * v_scale), through paged_attn_prefill_ex.
+    ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass)."""
+    return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
+                    block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
+                    validate, window_left, alibi_slopes, _scales(k_scale, v_scale))
+
+
 def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:
     return int(load_library().paged_attn_prefill_num_splits(B, Hq, max_q_len))
 
@@ -455,16 +474,24 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
 
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
              causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
-             alibi_slopes=None):
+             alibi_slopes=None, scales=None):
     window_left = _window(window_left)
-    _dtypes((q, "q", torch.bfloat16), (k_pool, "k_pool", torch.bfloat16),
-            (v_pool, "v_pool", torch.bfloat16), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
+    if scales is None:
+        _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
+    else:
+        _need_fp8_dtype(k_pool, "k_pool")
+        _need_fp8_dtype(v_pool, "v_pool")
+    _dtypes((q, "q", torch.bfloat16), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
             (seq_lens_k, "seq_lens_k", torch.int32), (block_tables, "block_tables", torch.int32),
             (out, "out", torch.bfloat16), (lse, "lse", torch.float32))
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, None)
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    if scales is None:
+        _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+        _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    else:
+        _need_fp8_pool(k_pool, "k_pool", dev)
+        _need_fp8_pool(v_pool, "v_pool", dev)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
     _need(seq_lens_k, "seq_lens_k", torch.int32, 1, dev)
     _need(block_tables, "block_tables", torch.int32, 2, dev)
@@ -497,7 +524,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
             P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0)
     alibi_ptr = _alibi(alibi_slopes, Hq, dev)
-    general = bool(window_left) or alibi_ptr is not None
+    general = bool(window_left) or alibi_ptr is not None or scales is not None
     if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
@@ -513,7 +540,9 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         if split is None:
             _check(lib.paged_attn_prefill_varlen(*args, _stream(stream)))
         elif general:
-            opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr)
+            ks, vs = scales if scales is not None else (1.0, 1.0)
+            opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
+                                    0 if scales is None else 1, ks, vs)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

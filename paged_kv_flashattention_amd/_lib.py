@@ -28,7 +28,9 @@ class DecodeOpts(ctypes.Structure):
 class PrefillOpts(ctypes.Structure):
     """pa_prefill_opts"""
     _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p)]
+                ("num_splits", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p),
+                ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)

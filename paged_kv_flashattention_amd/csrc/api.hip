@@ -271,7 +271,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
-                 const float* alibi = nullptr) {
+                 const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
+                 float v_scale = 1.f) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -290,6 +291,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
   if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u))
     return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
+  if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
+    return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   if (max_q_len > Tq) max_q_len = Tq;
   const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits);
   // one work-group per (query head, sequence, 128- or 256-row query tile, key
@@ -316,9 +319,13 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
   a.ps_shift = log2_exact(page_size);
   a.causal = causal ? 1 : 0;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  // FP8 pools: scores use the codes, so k_scale folds into the softmax scale and
+  // v_scale into the final normalisation
+  a.scale_log2 = softmax_scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
   a.window = window;
   a.alibi = alibi;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.v_scale = fp8 ? v_scale : 1.f;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -546,10 +553,13 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                           size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   if (!opts) return fail(PA_ERR_NULL, "prefill_ex: opts is NULL");
+  if (opts->kv_fp8 != 0 && opts->kv_fp8 != 1)
+    return fail(PA_ERR_UNSUPPORTED, "prefill_ex: kv_fp8=%d", opts->kv_fp8);
   return prefill_impl("prefill_ex", out, lse_out, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                       block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
-                      workspace_bytes, stream, opts->window_left, opts->alibi_slopes);
+                      workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
+                      opts->kv_fp8 == 1, opts->k_scale, opts->v_scale);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

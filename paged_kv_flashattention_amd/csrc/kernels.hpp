@@ -66,6 +66,8 @@ struct PrefillArgs {
   int xcd_groups;                // (sequence, KV head) groups per XCD, or 0: plain order
   int window;                    // sliding window: position p sees keys j > p - window (0: none)
   const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
+  int kv_fp8;                    // pools hold FP8 E4M3 codes (uint8) instead of bf16
+  float v_scale;                 // value of one V code unit (1 for bf16 pools)
   int S;                         // key-range parts per query tile at most (1: no split)
   int part_min;                  // 64-key tiles per part at least
   float* part_o;                 // [Tq * Hq, S, D] partial outputs        (S > 1)

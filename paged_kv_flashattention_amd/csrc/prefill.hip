@@ -188,8 +188,17 @@ __device__ __forceinline__ void pf_zero_tail(uint16_t* vst, int k0, int L, int w
   }
 }
 
-// W waves (32 W query rows) per work-group; 8 W waves per CU.
-template <int D, int W, bool GEN>
+// Four E4M3 codes (bytes 0..3) -> two packed bf16 pairs, exactly (every E4M3 value
+// is a bf16 value).
+__device__ __forceinline__ u32x2 pf_fp8x4_to_bf16(uint32_t w) {
+  return u32x2{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+// W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
+// variant (sliding window, ALiBi); F8: FP8 E4M3 pools (general variant only).
+template <int D, int W, bool GEN, bool F8>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
@@ -319,6 +328,16 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   }
   auto kst = [&](int kt) { return pf_lds + (kt & 1) * L_::TILE; };
   auto vst = [&](int vs) { return pf_lds + L_::V0 + vs * L_::TILE; };
+  // FP8 pools: each wave covers the pieces (16 consecutive codes of one row) of its
+  // region, row-major so that a row's pieces are neighbouring lanes; they are
+  // loaded into registers one tile ahead, like the DMA, and widened to bf16 into the
+  // tile's slots when the tile is published.
+  constexpr int F8_PPR = D / 16;                  // pieces per row
+  constexpr int F8_IPW = 4 * D / W;               // pieces per wave per matrix
+  constexpr int F8_NP = F8 ? (F8_IPW + 63) / 64 : 1;
+  const uint8_t* kbase8 = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * D;
+  const uint8_t* vbase8 = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * D;
+  u32x4 k8[F8_NP], v8[F8_NP];
   // DMA of tile n (tiles are issued in increasing order) into V stage vs
   auto issue = [&](int n, int vs) {
     if (n - base_t >= 64) {
@@ -327,13 +346,55 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     }
     int pg = __builtin_amdgcn_readlane(tab, n - base_t);
     pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
-    pf_issue_tile<D, W>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
-                     k_dma, v_dma, wave);
+    if constexpr (F8) {
+      const size_t base = ((size_t)pg * a.page_size + run0) * rs;
+#pragma unroll
+      for (int k = 0; k < F8_NP; ++k) {
+        const int i = lane + 64 * k;
+        if (F8_IPW % 64 == 0 || i < F8_IPW) {
+          const int piece = (wave % (W / 4)) * F8_IPW + i;
+          const size_t off = base + (size_t)(piece / F8_PPR) * rs + 16 * (piece % F8_PPR);
+          k8[k] = *reinterpret_cast<const u32x4*>(kbase8 + off);
+          v8[k] = *reinterpret_cast<const u32x4*>(vbase8 + off);
+        }
+      }
+    } else {
+      pf_issue_tile<D, W>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
+                          k_dma, v_dma, wave);
+    }
   };
   // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
   auto publish = [&](int n, int vs) {
     vmcnt_wait<0>();
-    if (n * kPfBN + kPfBN > L) {
+    if constexpr (F8) {
+      uint16_t* kr = kst(n) + M_::region(wave) * PfLds<D>::REGION;
+      uint16_t* vr = vst(vs) + M_::region(wave) * PfLds<D>::REGION;
+      const int row0 = n * kPfBN + 16 * M_::region(wave);
+#pragma unroll
+      for (int k = 0; k < F8_NP; ++k) {
+        const int i = lane + 64 * k;
+        if (F8_IPW % 64 == 0 || i < F8_IPW) {
+          const int piece = (wave % (W / 4)) * F8_IPW + i;
+          const int sl = piece / F8_PPR, c = 2 * (piece % F8_PPR);
+          const u32x2 k0 = pf_fp8x4_to_bf16(k8[k][0]), k1 = pf_fp8x4_to_bf16(k8[k][1]);
+          const u32x2 k2 = pf_fp8x4_to_bf16(k8[k][2]), k3 = pf_fp8x4_to_bf16(k8[k][3]);
+          *reinterpret_cast<u32x4*>(kr + 128 * c + 8 * sl) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+          *reinterpret_cast<u32x4*>(kr + 128 * (c + 1) + 8 * sl) =
+              u32x4{k2[0], k2[1], k3[0], k3[1]};
+          // V rows at or past the sequence end are zeroed (P = 0 times NaN is not 0)
+          u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+          if (row0 + sl < L) {
+            const u32x2 v0 = pf_fp8x4_to_bf16(v8[k][0]), v1 = pf_fp8x4_to_bf16(v8[k][1]);
+            const u32x2 v2 = pf_fp8x4_to_bf16(v8[k][2]), v3 = pf_fp8x4_to_bf16(v8[k][3]);
+            va = u32x4{v0[0], v0[1], v1[0], v1[1]};
+            vb = u32x4{v2[0], v2[1], v3[0], v3[1]};
+          }
+          *reinterpret_cast<u32x4*>(vr + 128 * c + 8 * ((sl + 4 * c) & 15)) = va;
+          *reinterpret_cast<u32x4*>(vr + 128 * (c + 1) + 8 * ((sl + 4 * (c + 1)) & 15)) = vb;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the tile is in LDS
+    } else if (n * kPfBN + kPfBN > L) {
       pf_zero_tail<D, W>(vst(vs), n * kPfBN, L, wave, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in LDS
     }
@@ -553,7 +614,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   if (!row_ok) return;
   const float l_tot = xor32_sum(l_run);
   const bool live = l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
+  const float inv = live ? (F8 ? a.v_scale : 1.f) / l_tot : 0.f;
   const float lse = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
   if (tw.parts > 1) {
     // this part's normalised output and lse, merged by the prefill merge kernel
@@ -646,16 +707,16 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
-template <int D, int W, bool GEN>
+template <int D, int W, bool GEN, bool F8>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
   // more than 64 KiB of dynamic LDS must be requested once per process
   static const hipError_t attr = PfLds<D>::BYTES > 65536
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN>),
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
       : hipSuccess;
   if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
-  hipLaunchKernelGGL((prefill_kernel<D, W, GEN>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, W, GEN, F8>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
                      a);
   return hipGetLastError();
 }
@@ -664,8 +725,9 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
 // variant
 template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  return a.window > 0 || a.alibi ? launch_prefill_w<D, W, true>(a, stream)
-                                 : launch_prefill_w<D, W, false>(a, stream);
+  if (a.kv_fp8) return launch_prefill_w<D, W, true, true>(a, stream);
+  return a.window > 0 || a.alibi ? launch_prefill_w<D, W, true, false>(a, stream)
+                                 : launch_prefill_w<D, W, false, false>(a, stream);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
@@ -708,9 +770,10 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
   else
     e = W == 8 ? launch_prefill_t<64, 8>(a, stream) : launch_prefill_t<64, 4>(a, stream);
   snprintf(desc, desc_len,
-           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,lds-dma> grid=%d (%d heads x %d seqs x %d "
+           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s) block=%d lds=%zu",
-           a.D, 32 * W, kPfBN, a.Hq * a.B * a.n_qt * a.S, a.Hq, a.B, a.n_qt, a.S,
+           a.D, 32 * W, kPfBN, a.kv_fp8 ? "fp8-e4m3-widened" : "lds-dma",
+           a.Hq * a.B * a.n_qt * a.S, a.Hq, a.B, a.n_qt, a.S,
            a.xcd_groups ? "KV groups per XCD" : "head-major", 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;

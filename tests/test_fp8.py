@@ -14,7 +14,8 @@ import torch
 
 from oracle import fp8 as of
 import paged_kv_flashattention_amd as pa
-from tests.parity import as_f64, assert_lse, assert_parity, oracle_full, oracle_rows
+from tests.parity import (as_f64, assert_lse, assert_parity, oracle_full, oracle_rows,
+                          pools_after_write)
 from workloads import bits, make_case, make_config, random_e4m3_codes
 
 pytestmark = pytest.mark.gpu
@@ -270,3 +271,136 @@ def test_fp8_write_then_decode_round_trip(require_gpu):
     o_ref, l_ref = oracle_full(dcase, of.dequantize_pool(k_ref, ks), of.dequantize_pool(v_ref, vs))
     assert_parity(as_f64(out), o_ref, "fp8 write+decode")
     assert_lse(as_f64(lse), l_ref, "fp8 write+decode lse")
+
+
+# ---------------------------------------------------------------------------
+# prefill over FP8 pools
+# ---------------------------------------------------------------------------
+
+def _pool_codes(case, kp_bits, vp_bits):
+    """E4M3 codes of the case's pools (after its page write) at amax/448 scales."""
+    kx = torch.from_numpy(kp_bits.view(np.int16)).view(torch.bfloat16)
+    vx = torch.from_numpy(vp_bits.view(np.int16)).view(torch.bfloat16)
+    ks, vs = amax_scale(kx), amax_scale(vx)
+    return of.quantize_ref(kp_bits, ks), of.quantize_ref(vp_bits, vs), ks, vs
+
+
+PREFILL = [
+    # hist, q_lens, Hq, Hkv, D, ps, causal, splits, window, alibi
+    ([0, 0], [127, 300], 8, 2, 128, 16, True, 1, 0, False),
+    ([200, 31, 0], [129, 1, 64], 8, 2, 128, 16, True, 1, 0, False),
+    ([17, 0], [50, 130], 8, 8, 64, 32, True, 1, 0, False),          # D 64, 4 waves
+    ([0, 0], [1100, 300], 4, 2, 64, 16, True, 1, 0, False),         # D 64, 8 waves
+    ([500, 0], [1030, 260], 8, 2, 128, 64, True, 1, 0, False),      # D 128, 8 waves
+    ([300, 0, 7], [40, 129, 1], 8, 2, 128, 16, False, 1, 0, False),
+    ([1000, 0], [100, 257], 28, 4, 128, 16, True, 1, 200, True),    # window and ALiBi
+    ([4113, 214], [512, 40], 8, 2, 128, 16, True, 4, 0, False),     # key parts
+]
+
+
+@pytest.mark.parametrize("hist,ql,Hq,Hkv,D,ps,causal,splits,window,alibi", PREFILL)
+def test_fp8_prefill_parity(require_gpu, hist, ql, Hq, Hkv, D, ps, causal, splits, window,
+                            alibi):
+    print(f"[fp8 prefill] hist={hist} q={ql} Hq={Hq} Hkv={Hkv} D={D} ps={ps} causal={causal} "
+          f"S={splits} w={window} alibi={alibi}", flush=True)
+    case = make_case("p8", hist_lens=hist, q_lens=ql, write_new=True, causal=causal, Hq=Hq,
+                     Hkv=Hkv, D=D, page_size=ps, seed=sum(ql) + D + 88, device="cuda",
+                     num_pages=sum(-(-(h + n) // ps) for h, n in zip(hist, ql)) + 2,
+                     window=window)
+    kp, vp = pools_after_write(case)
+    kc, vc, ks, vs = _pool_codes(case, kp, vp)
+    sl = (torch.tensor(2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq), dtype=torch.float32,
+                       device="cuda") if alibi else None)
+    out, lse = pa.paged_attn_prefill_varlen_fp8(
+        case.q, to_gpu_codes(kc), to_gpu_codes(vc), case.cu_seqlens_q, case.seq_lens_k,
+        case.block_tables, case.scale, ks, vs, causal=causal, max_q_len=case.max_q_len,
+        num_splits=splits, return_lse=True, validate=True, window_left=window,
+        alibi_slopes=sl)
+    torch.cuda.synchronize()
+    assert "fp8" in pa.describe_launch()
+    o_ref, l_ref = oracle_full(case, of.dequantize_pool(kc, ks), of.dequantize_pool(vc, vs),
+                               alibi=None if sl is None else sl.cpu().numpy().astype(np.float64))
+    assert_parity(as_f64(out), o_ref, "fp8 prefill")
+    assert_lse(as_f64(lse), l_ref, "fp8 prefill lse")
+
+
+@pytest.mark.parametrize("q_lens", [[129, 300], [1100, 64]])
+def test_unit_scale_fp8_prefill_equals_bf16_prefill_bitwise(require_gpu, q_lens):
+    """Unit scales: the widened codes are the bf16 values a bf16 pool would hold, and
+    both paths run the same general kernel from there."""
+    case = make_case("p8u", seq_lens=[300 + q_lens[0], q_lens[1]], q_lens=q_lens, causal=True,
+                     Hq=8, Hkv=2, D=128, page_size=16, seed=19, device="cuda")
+    shape = tuple(case.k_pool.shape)
+    kc = random_e4m3_codes(shape, 31, "cuda", 2, 8)
+    vc = random_e4m3_codes(shape, 32, "cuda", 2, 8)
+    as_bf16 = lambda c: torch.from_numpy(                                       # noqa: E731
+        of.e4m3_decode(c.cpu().numpy()).astype(np.float32)).to(torch.bfloat16).cuda()
+    args = (case.q,)
+    rest = (case.cu_seqlens_q, case.seq_lens_k, case.block_tables, case.scale)
+    o8, l8 = pa.paged_attn_prefill_varlen_fp8(*args, kc, vc, *rest, 1.0, 1.0, causal=True,
+                                              max_q_len=max(q_lens), return_lse=True)
+    big = 1 << 30                      # a window longer than everything: the general kernel
+    o16, l16 = pa.paged_attn_prefill_varlen(*args, as_bf16(kc), as_bf16(vc), *rest, causal=True,
+                                            max_q_len=max(q_lens), return_lse=True,
+                                            window_left=big)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(l8, l16)
+
+
+def test_fp8_causal_prefill_full_size_sampled(require_gpu):
+    """Dense causal prefill (4 x 4096, Hq 32, Hkv 8) over FP8 pools of seeded random codes;
+    the oracle dequantises only the pages the sampled rows need."""
+    case = make_config("causal_prefill", "cuda")
+    shape = tuple(case.k_pool.shape)
+    case.k_pool = case.v_pool = None
+    kc = random_e4m3_codes(shape, 1003 * 8 + 1, "cuda")
+    vc = random_e4m3_codes(shape, 1003 * 8 + 2, "cuda")
+    ks, vs = 0.02, 0.05
+    print("[fp8 prefill] causal_prefill full size", flush=True)
+    out, lse = pa.paged_attn_prefill_varlen_fp8(case.q, kc, vc, case.cu_seqlens_q,
+                                                case.seq_lens_k, case.block_tables, case.scale,
+                                                ks, vs, causal=True, max_q_len=4096,
+                                                return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(14)
+    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, case.T, 32), rng.integers(0, 32, 32))]
+    rows += [(0, 0), (4095, 31), (case.T - 1, 17)]
+    bt = case.block_tables.cpu().numpy()
+    kd = np.zeros(shape)
+    vd = np.zeros(shape)
+    for b in sorted({t // 4096 for t, _ in rows}):
+        pages = bt[b, :256].astype(np.int64)
+        idx = torch.as_tensor(pages, device="cuda")
+        kd[pages] = of.dequantize_pool(kc[idx].cpu().numpy(), ks)
+        vd[pages] = of.dequantize_pool(vc[idx].cpu().numpy(), vs)
+    o_ref, l_ref = oracle_rows(case, rows, kd, vd)
+    got = np.stack([as_f64(out[t, h]) for t, h in rows])
+    assert_parity(got, o_ref, "fp8 causal_prefill sampled")
+    assert_lse(np.array([float(lse[t, h]) for t, h in rows]), l_ref, "fp8 prefill lse")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_fp8_write_then_prefill_round_trip(require_gpu):
+    """The quantising page write feeds the FP8 prefill: a ragged batch of chunks over
+    their history, all in FP8 pools."""
+    case = make_case("wp8", hist_lens=[0, 0, 0], q_lens=[37, 300, 129], write_new=True,
+                     causal=True, Hq=16, Hkv=4, D=128, page_size=16, seed=78, device="cuda")
+    ks, vs = amax_scale(case.k_new), amax_scale(case.v_new)
+    shape = tuple(case.k_pool.shape)
+    kp = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    vp = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    write_fp8(case, kp, vp, ks, vs)
+    print("[fp8 prefill] write then prefill", flush=True)
+    out, lse = pa.paged_attn_prefill_varlen_fp8(case.q, kp, vp, case.cu_seqlens_q,
+                                                case.seq_lens_k, case.block_tables, case.scale,
+                                                ks, vs, causal=True, max_q_len=300,
+                                                return_lse=True)
+    torch.cuda.synchronize()
+    zeros = np.zeros(shape, np.uint8)
+    k_ref, v_ref = of.kv_write_fp8_ref(zeros, zeros, bits(case.k_new), bits(case.v_new),
+                                       case.cu_new.cpu().numpy(), case.start_pos.cpu().numpy(),
+                                       case.block_tables.cpu().numpy(), 16, ks, vs)
+    o_ref, l_ref = oracle_full(case, of.dequantize_pool(k_ref, ks), of.dequantize_pool(v_ref, vs))
+    assert_parity(as_f64(out), o_ref, "fp8 write+prefill")
+    assert_lse(as_f64(lse), l_ref, "fp8 write+prefill lse")
