@@ -197,8 +197,9 @@ __device__ __forceinline__ u32x2 pf_fp8x4_to_bf16(uint32_t w) {
 }
 
 // W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
-// variant (sliding window, ALiBi); F8: FP8 E4M3 pools (general variant only).
-template <int D, int W, bool GEN, bool F8>
+// variant (sliding window, ALiBi); F8: FP8 E4M3 pools and REV: key tiles walked
+// downwards (ALiBi), both in the general variant only.
+template <int D, int W, bool GEN, bool F8, bool REV>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
@@ -270,10 +271,20 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // sliding window: first visible key of this row, and the largest of the wave's
   const int lo_row = GEN && a.window > 0 ? my_pos - a.window + 1 : INT_MIN;
   const int w_lo_max = GEN && a.window > 0 ? shift + r_w + 31 - a.window + 1 : INT_MIN;
-  // ALiBi: the head's slope in raw score units (scores are scaled later), and the
-  // distance of this lane's first key in a block from its row, less kb0
-  const float slope_raw = GEN && a.alibi ? a.alibi[h] * kLog2e / a.scale_log2 : 0.f;
-  const int dist0 = 4 * hh - my_pos;
+  // ALiBi, slope_h * (key - row position), in two parts that cost nothing per score:
+  // the key's offset within its block (8 j + 4 hh + i for element 4 j + i) is the
+  // same for every block, so it is the initial value of the score accumulator
+  // (raw units; the scores are scaled later); the block start less the row's
+  // position is one value per block and row, added with the softmax reference
+  // (log2 units, `boff`, set when a block's scores are masked).
+  const float slope_log2 = GEN && a.alibi ? a.alibi[h] * kLog2e : 0.f;
+  f32x16 ebias;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ebias[4 * j + i] = GEN ? slope_log2 / a.scale_log2 * (float)(8 * j + 4 * hh + i) : 0.f;
+  float boff = 0.f;
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
   u32x4 qb[D / 16];
@@ -340,8 +351,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   u32x4 k8[F8_NP], v8[F8_NP];
   // DMA of tile n (tiles are issued in increasing order) into V stage vs
   auto issue = [&](int n, int vs) {
-    if (n - base_t >= 64) {
-      base_t += 64;
+    if (REV ? n < base_t : n - base_t >= 64) {
+      base_t = REV ? max(0, n - 63) : base_t + 64;
       tab = load_tab(base_t);
     }
     int pg = __builtin_amdgcn_readlane(tab, n - base_t);
@@ -405,9 +416,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // S^T of the 32 keys of block kb of a K tile
   auto qk = [&](const uint16_t* kt_lds, int kb) {
     const uint16_t* kl = kt_lds + k_lane + kb * 32 * D;
-    f32x16 sc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+    f32x16 sc = ebias;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       sc = mfma32x32x16(*reinterpret_cast<const u32x4*>(kl + 256 * kk), qb[kk], sc);
@@ -419,21 +428,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, sc[e]), sc[e + 1]);
     mt = fmaxf(mt, sc[15]);
-    return xor32_max(mt) * a.scale_log2;
+    const float r = xor32_max(mt) * a.scale_log2;
+    return GEN ? r + boff : r;
   };
-  // ALiBi bias (general variant), then -inf for keys past the end, (causal) above
-  // the diagonal and (window) below a row's window; only blocks that touch one of
-  // these boundaries need the second part.  Called once per block, right after its
-  // scores are formed.
+  // The block's ALiBi offset (general variant), then -inf for keys past the end,
+  // (causal) above the diagonal and (window) below a row's window; only blocks that
+  // touch one of these boundaries need the second part.  Called once per block,
+  // right after its scores are formed and before they are used.
   auto mask = [&](f32x16& sc, int kb0) {
-    if (GEN && a.alibi) {
-      const float fb = (float)(kb0 + dist0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[4 * j + i] = fmaf(slope_raw, fb + (float)(8 * j + i), sc[4 * j + i]);
-    }
+    if (GEN) boff = slope_log2 * (float)(kb0 - my_pos);
     const bool need =
         (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (GEN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
@@ -481,7 +484,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // lane's share of the block's row sum, taken on the same bf16-rounded P that
   // multiplies V
   auto exps = [&](const f32x16& sc, uint32_t* pw, float& ps) {
-    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
+    const float neg_m = GEN ? neg_m0 + boff : neg_m0;
     ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
@@ -521,14 +525,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     constexpr int NK = D / 16;                 // QK MFMAs
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
     constexpr int NV = 2 * (D / 32);           // PV MFMAs
-    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
+    const float neg_m = GEN ? neg_m0 + boff : neg_m0;
     const uint16_t* kl = kq + k_lane + kbq * 32 * D;
     u32x4 kf[NK];
     kf[0] = *reinterpret_cast<const u32x4*>(kl);
     kf[1] = *reinterpret_cast<const u32x4*>(kl + 256);
-    f32x16 sn;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+    f32x16 sn = ebias;
     uint32_t pw[8];
     float ps = 0.f;
     __builtin_amdgcn_sched_barrier(0);
@@ -580,35 +583,45 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // block i + 1 and then O += P V of block i, the vector unit exponentiates block
   // i.  K of tiles t, t + 1 and V of tiles t - 1 .. t + 1 are resident, so one
   // barrier per tile suffices.
-  if (tile_hi > tile_lo) {
-    base_t = tile_lo;
-    tab = load_tab(tile_lo);
-    int vs_cur = 0;                       // V stage of tile kt
-    issue(tile_lo, 0);
-    publish(tile_lo, 0);
-    if (tile_hi - tile_lo > 1) issue(tile_lo + 1, 1);
-    f32x16 s_pend = qk(kst(tile_lo), 0);  // first block: scores, mask, first reference
-    mask(s_pend, tile_lo * kPfBN);
+  // Key tiles are walked upwards, or (REV) from the last one down: with ALiBi the
+  // scores grow towards a row's own position, so walking down sets the softmax
+  // reference at the first block instead of moving it at nearly every block.  B0, B1:
+  // the first and second 32-key block of a tile in walk order.
+  constexpr int B0 = REV ? 1 : 0, B1 = 1 - B0;
+  auto tile_at = [&](int u) { return REV ? tile_hi - 1 - u : tile_lo + u; };
+  const int nt = tile_hi - tile_lo;
+  if (nt > 0) {
+    base_t = REV ? max(0, tile_hi - 64) : tile_lo;
+    tab = load_tab(base_t);
+    int vs_cur = 0;                       // V stage of the walk's current tile
+    issue(tile_at(0), 0);
+    publish(tile_at(0), 0);
+    if (nt > 1) issue(tile_at(1), 1);
+    // first block: scores, mask, first reference
+    f32x16 s_pend = qk(kst(tile_at(0)), B0);
+    mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
     decide(rowmax(s_pend));
-    for (int kt = tile_lo; kt + 1 < tile_hi; ++kt) {
+    for (int u = 0; u + 1 < nt; ++u) {
+      const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
-      // block 2 kt (pending) -> block 2 kt + 1
-      step(s_pend, kst(kt), 1, vst(vs_cur), 0);
-      mask(s_pend, kt * kPfBN + 32);
-      // block 2 kt + 1 -> block 2 kt + 2 (first of the next tile)
-      publish(kt + 1, vs_next);
-      if (kt + 2 < tile_hi) issue(kt + 2, vs_next == 2 ? 0 : vs_next + 1);
-      step(s_pend, kst(kt + 1), 0, vst(vs_cur), 1);
-      mask(s_pend, (kt + 1) * kPfBN);
+      // first block of tile kt (pending) -> its second block
+      step(s_pend, kst(kt), B1, vst(vs_cur), B0);
+      mask(s_pend, kt * kPfBN + 32 * B1);
+      // second block of tile kt -> first block of tile kn
+      publish(kn, vs_next);
+      if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
+      step(s_pend, kst(kn), B0, vst(vs_cur), B1);
+      mask(s_pend, kn * kPfBN + 32 * B0);
       vs_cur = vs_next;
     }
-    step(s_pend, kst(tile_hi - 1), 1, vst(vs_cur), 0);
-    mask(s_pend, (tile_hi - 1) * kPfBN + 32);
+    const int kl = tile_at(nt - 1);
+    step(s_pend, kst(kl), B1, vst(vs_cur), B0);
+    mask(s_pend, kl * kPfBN + 32 * B1);
     uint32_t pw[8];
     float ps;
     exps(s_pend, pw, ps);
     settle(s_pend, pw, ps);
-    pv(vst(vs_cur), 1, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    pv(vst(vs_cur), B1, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
   }
 
   if (!row_ok) return;
@@ -707,16 +720,16 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
-template <int D, int W, bool GEN, bool F8>
+template <int D, int W, bool GEN, bool F8, bool REV>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
   // more than 64 KiB of dynamic LDS must be requested once per process
   static const hipError_t attr = PfLds<D>::BYTES > 65536
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8>),
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
       : hipSuccess;
   if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
-  hipLaunchKernelGGL((prefill_kernel<D, W, GEN, F8>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, W, GEN, F8, REV>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
                      a);
   return hipGetLastError();
 }
@@ -725,9 +738,12 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
 // variant
 template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  if (a.kv_fp8) return launch_prefill_w<D, W, true, true>(a, stream);
-  return a.window > 0 || a.alibi ? launch_prefill_w<D, W, true, false>(a, stream)
-                                 : launch_prefill_w<D, W, false, false>(a, stream);
+  if (a.kv_fp8)
+    return a.alibi ? launch_prefill_w<D, W, true, true, true>(a, stream)
+                   : launch_prefill_w<D, W, true, true, false>(a, stream);
+  if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream);
+  return a.window > 0 ? launch_prefill_w<D, W, true, false, false>(a, stream)
+                      : launch_prefill_w<D, W, false, false, false>(a, stream);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the

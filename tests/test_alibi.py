@@ -121,9 +121,11 @@ def test_alibi_prefill_parity(require_gpu, hist, ql, Hq, Hkv, D, ps, causal, win
     assert_lse(as_f64(lse), l_ref, "alibi prefill lse")
 
 
-def test_zero_slopes_give_the_plain_kernels_bits(require_gpu):
-    """slope 0 adds exactly 0 to every score: decode and prefill through the general
-    path equal the plain launches bit for bit."""
+def test_zero_slopes_give_the_plain_results(require_gpu):
+    """slope 0 adds exactly 0 to every score: decode equals the plain launch bit for
+    bit; prefill with ALiBi walks the key tiles downwards, so its softmax reference
+    and hence the bf16 rounding of P differ from the plain launch's: the two agree
+    within half the parity tolerance."""
     case = make_case("az", hist_lens=[300, 0], q_lens=[70, 129], write_new=True, causal=True,
                      Hq=8, Hkv=2, D=128, page_size=16, seed=6, device="cuda")
     write(case)
@@ -134,7 +136,9 @@ def test_zero_slopes_give_the_plain_kernels_bits(require_gpu):
     b, lb = pa.paged_attn_prefill_varlen(*args, causal=True, max_q_len=129, return_lse=True,
                                          alibi_slopes=z)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+    assert_parity(as_f64(b), as_f64(a), "zero slopes vs plain", max_abs=1e-2, mean_abs=1e-3)
+    la64 = as_f64(la)
+    assert (np.abs(la64 - as_f64(lb)) <= 1e-3 * np.maximum(1.0, np.abs(la64))).all()
     d = make_case("azd", seq_lens=[700, 33, 129], Hq=8, Hkv=2, D=128, page_size=16, seed=7,
                   device="cuda")
     dargs = (d.q, d.k_pool, d.v_pool, d.block_tables, d.seq_lens_k, d.scale)
