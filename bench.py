@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen7b_decode",
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
-                            "long_decode", "causal_prefill", "mixed_ragged",
-                            "tiny_decode"])
+                            "long_decode", "causal_prefill", "causal_prefill_fp8",
+                            "mixed_ragged", "tiny_decode"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
@@ -95,26 +95,21 @@ class DecodeStep:
         self.i += 1
         self.pa.paged_attn_decode(c.q, kp, vp, c.block_tables, c.seq_lens_k, c.scale,
                                   max_seq_len=c.max_seq_len, num_splits=self.S, out=self.out,
-                                  workspace=self.ws)
+                                  workspace=self.ws, kernel_events=next_events(self))
 
-    def dominant_kernel_ms(self, launches):
-        """Average duration of the partition kernel alone: `launches` back-to-back
-        paged_attn_decode_partials calls (same inputs, same rotation) between HIP
-        events on the launch stream."""
-        import torch
+    def partials(self):
         c = self.case
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for j in range(launches):
-            kp, vp = self.kv[j % len(self.kv)]
-            self.pa.paged_attn_decode_partials(c.q, kp, vp, c.block_tables, c.seq_lens_k,
-                                               c.scale, num_splits=self.S,
-                                               max_seq_len=c.max_seq_len, partial_out=self.po,
-                                               partial_lse=self.pl)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
+        kp, vp = self.kv[self.i % len(self.kv)]
+        self.i += 1
+        self.pa.paged_attn_decode_partials(c.q, kp, vp, c.block_tables, c.seq_lens_k, c.scale,
+                                           num_splits=self.S, max_seq_len=c.max_seq_len,
+                                           partial_out=self.po, partial_lse=self.pl)
+
+    def partition_launches(self, launches):
+        """`launches` back-to-back partition-kernel launches over the rotated pool
+        copies (what the counter runs profile)."""
+        for _ in range(launches):
+            self.partials()
 
     def config(self):
         c = self.case
@@ -146,20 +141,8 @@ class Fp8DecodeStep(DecodeStep):
         self.i += 1
         self.pa.paged_attn_decode_fp8(c.q, kp, vp, c.block_tables, c.seq_lens_k, c.scale,
                                       self.K_SCALE, self.V_SCALE, max_seq_len=c.max_seq_len,
-                                      num_splits=self.S, out=self.out, workspace=self.ws)
-
-    def dominant_kernel_ms(self, launches):
-        """No partials-only entry point exists for FP8 pools: time whole calls
-        (partition kernel plus the few-microsecond merge)."""
-        import torch
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(launches):
-            self()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
+                                      num_splits=self.S, out=self.out, workspace=self.ws,
+                                      kernel_events=next_events(self))
 
     def config(self):
         return dict(super().config(), kv_format="fp8-e4m3")
@@ -167,8 +150,9 @@ class Fp8DecodeStep(DecodeStep):
 
 class PrefillStep:
     """kv_page_write is done once at setup; each step is one prefill_varlen call (with
-    `splitk`, one prefill_varlen_splitk call with the library's key-part count: the
-    prefill kernel, then the merge of the split tiles)."""
+    `splitk`, one prefill_varlen_splitk call with the key-part count that
+    paged_attn_prefill_plan_splits gives for the lengths: the prefill kernel, then the
+    merge of the split tiles)."""
 
     def __init__(self, name, splitk=False):
         import torch
@@ -181,7 +165,8 @@ class PrefillStep:
         self.out = torch.empty((c.T, c.Hq, c.D), dtype=torch.bfloat16, device="cuda")
         self.units = units.prefill_flops(c.seq_lens, c.q_lens, c.Hq, c.D, c.causal)
         self.unit_name = "TFLOP/s"
-        self.S = pa.prefill_num_splits(c.B, c.Hq, c.max_q_len) if splitk else 1
+        # key parts planned from the host lengths, as a scheduler would
+        self.S = pa.prefill_plan_splits(c.q_lens, c.seq_lens, c.Hq) if splitk else 1
         need = pa.prefill_workspace_bytes(c.B, c.T, c.max_q_len, c.Hq, c.D, self.S)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.splitk = splitk
@@ -192,23 +177,12 @@ class PrefillStep:
             self.pa.paged_attn_prefill_varlen_splitk(
                 c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
                 causal=True, max_q_len=c.max_q_len, num_splits=self.S, out=self.out,
-                workspace=self.ws)
+                workspace=self.ws, kernel_events=next_events(self))
             return
         self.pa.paged_attn_prefill_varlen(c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k,
                                           c.block_tables, c.scale, causal=True,
-                                          max_q_len=c.max_q_len, out=self.out)
-
-    def dominant_kernel_ms(self, launches):
-        """A step is one prefill launch: time `launches` of them back to back."""
-        import torch
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(launches):
-            self()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
+                                          max_q_len=c.max_q_len, out=self.out,
+                                          kernel_events=next_events(self))
 
     def config(self):
         c = self.case
@@ -219,12 +193,41 @@ class PrefillStep:
         return cfg
 
 
+class Fp8PrefillStep(PrefillStep):
+    """The same causal prefill over FP8 E4M3 pools: seeded random codes of the
+    pools' shape with per-pool scales (the queries stay bf16)."""
+
+    K_SCALE, V_SCALE = 0.02, 0.05
+
+    def __init__(self, name):
+        super().__init__(name)
+        from workloads import random_e4m3_codes
+        c = self.case
+        shape = tuple(c.k_pool.shape)
+        c.k_pool = c.v_pool = None
+        self.kc = random_e4m3_codes(shape, 8100, "cuda")
+        self.vc = random_e4m3_codes(shape, 8101, "cuda")
+
+    def __call__(self):
+        c = self.case
+        self.pa.paged_attn_prefill_varlen_fp8(
+            c.q, self.kc, self.vc, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
+            self.K_SCALE, self.V_SCALE, causal=True, max_q_len=c.max_q_len, out=self.out,
+            kernel_events=next_events(self))
+
+    def config(self):
+        return dict(super().config(), kv_format="fp8-e4m3")
+
+
 class MixedStep:
     """The mixed ragged step: write 2,578 new tokens, prefill the 5 chunks, decode 18 rows.
 
-    The prefill chunks and the decode rows read disjoint outputs and both only read
-    the pools after the write, so the decode runs on a second stream (default
-    priority) after the write and overlaps the prefill; the step ends when both
+    The prefill's key-part count comes from paged_attn_prefill_plan_splits over the
+    chunks' host lengths (as a scheduler would plan it), the decode's split count
+    from the library's rule.  The prefill chunks and the decode rows read disjoint
+    outputs and both only read the pools after the write, so the decode runs on a
+    second stream (default priority) after the write, issued behind the prefill so
+    that its work-groups fill the slots the prefill leaves; the step ends when both
     have finished (the launch stream waits for the second one)."""
 
     def __init__(self, name="mixed_ragged"):
@@ -243,6 +246,10 @@ class MixedStep:
         self.lens_d = c.seq_lens_k[n:].contiguous()
         self.bt_d = c.block_tables[n:].contiguous()
         self.max_d = max(c.seq_lens[n:])
+        self.max_q = max(c.q_lens[:n])
+        self.S_pf = pa.prefill_plan_splits(c.q_lens[:n], c.seq_lens[:n], c.Hq, causal=True)
+        need = pa.prefill_workspace_bytes(n, self.t_pf, self.max_q, c.Hq, c.D, self.S_pf)
+        self.ws_pf = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.S = pa.decode_num_splits(c.B - n, c.Hkv, self.max_d)
         need = pa.decode_workspace_bytes(c.B - n, c.Hq, c.Hkv, c.D, self.max_d, self.S)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
@@ -262,20 +269,22 @@ class MixedStep:
         pa.kv_page_write(c.k_pool, c.v_pool, c.k_new, c.v_new, c.cu_new, c.start_pos,
                          c.block_tables)
         self.side.wait_stream(main)
+        pa.paged_attn_prefill_varlen_splitk(self.q_pf, c.k_pool, c.v_pool, self.cu_pf,
+                                            self.lens_pf, self.bt_pf, c.scale, causal=True,
+                                            max_q_len=self.max_q, num_splits=self.S_pf,
+                                            out=self.out_pf, workspace=self.ws_pf)
         with torch.cuda.stream(self.side):
             pa.paged_attn_decode(self.q_d, c.k_pool, c.v_pool, self.bt_d, self.lens_d, c.scale,
                                  max_seq_len=self.max_d, num_splits=self.S, out=self.out_d,
                                  workspace=self.ws)
-        pa.paged_attn_prefill_varlen(self.q_pf, c.k_pool, c.v_pool, self.cu_pf, self.lens_pf,
-                                     self.bt_pf, c.scale, causal=True, max_q_len=512,
-                                     out=self.out_pf)
         main.wait_stream(self.side)
 
     def config(self):
         c = self.case
         return {"workload": c.name, "requests": c.B, "prefill_chunks": 5, "chunk_len": 512,
                 "decode_rows": c.B - 5, "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.D,
-                "page_size": c.page_size}
+                "page_size": c.page_size, "prefill_key_parts": self.S_pf,
+                "decode_splits": self.S}
 
 
 def make_step(name, num_splits=0):
@@ -290,16 +299,30 @@ def make_step(name, num_splits=0):
         return DecodeStep(name, copies=1, num_splits=num_splits)
     if name == "causal_prefill":
         return PrefillStep(name)
+    if name == "causal_prefill_fp8":
+        return Fp8PrefillStep("causal_prefill")
     if name == "long_history_chunk":
         return PrefillStep(name, splitk=True)
     return MixedStep(name)
 
 
-def time_step(step, steps, warmup):
+def next_events(step):
+    """The kernel-event pair for this call of a timed step, or None outside timing."""
+    it = getattr(step, "events", None)
+    return next(it) if it is not None else None
+
+
+def time_step(step, steps, warmup, kernel_events=True):
     """Warm up, then time exactly `steps` calls bracketed by synchronisations.
 
-    Returns (wall ms per step, event ms per step): HIP events are recorded on the
-    stream the kernels are launched on (torch's current stream)."""
+    Returns (wall ms per step, event ms per step, dominant-kernel ms or None).  The
+    step's time comes from HIP events recorded on the launch stream (torch's current
+    stream) before the first and after the last call, with nothing else in the
+    stream.  Then the same `steps` calls run once more, each handing its main
+    kernel's dispatch a pair of events that the dispatch itself stamps with that
+    kernel's start and end (the library's kernel_events option): their average is
+    the dominant kernel's duration.  Stamped dispatches lengthen a step by a few
+    microseconds on this runtime, which is why the timed pass carries none."""
     import torch
     for _ in range(warmup):
         step()
@@ -314,7 +337,20 @@ def time_step(step, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ev = start.elapsed_time(stop) / steps
-    return wall, ev
+    if not kernel_events or isinstance(step, MixedStep):
+        return wall, ev, None
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for a, b in pairs:                         # HIP events are created when first recorded
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    step.events = iter(pairs)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    step.events = None
+    return wall, ev, sum(a.elapsed_time(b) for a, b in pairs) / steps
 
 
 def rate(units, ms, unit_name):
@@ -360,7 +396,7 @@ def recorded_traffic():
 def traffic_pass(steps):
     """What the counter runs profile: a plain device copy of COPY_BYTES (the
     calibration), then `steps` launches of the decode partition kernel over the
-    rotated pool copies, exactly as dominant_kernel_ms launches them."""
+    rotated pool copies, as the timed steps launch them."""
     import torch
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
@@ -370,7 +406,7 @@ def traffic_pass(steps):
     del src, dst
     torch.cuda.empty_cache()
     step = make_step("qwen7b_decode", 0)
-    step.dominant_kernel_ms(steps)
+    step.partition_launches(steps)
     log(f"[bench] traffic pass: copy of {COPY_BYTES} bytes, {steps} partition launches; "
         f"sources {decode_source_digest()[:16]}")
 
@@ -486,10 +522,9 @@ def main():
 
     step = make_step(args.workload, args.num_splits)
     torch.cuda.synchronize()
-    wall, ev = time_step(step, args.steps, args.warmup)
+    wall, ev, kern_ms = time_step(step, args.steps, args.warmup)
     value = rate(step.units, ev, step.unit_name)
     launch = pa.describe_launch()
-    kern_ms = step.dominant_kernel_ms(args.steps)
     achieved = rate(step.units, kern_ms, step.unit_name)
     log(f"[bench] {args.workload}: {ev * 1e3:.1f} us/step (events), {wall * 1e3:.1f} us/step "
         f"(wall), {value:.1f} {step.unit_name}; dominant kernel {kern_ms * 1e3:.1f} us, "
@@ -515,6 +550,9 @@ def main():
                      "traffic": recorded_traffic() if args.workload == "qwen7b_decode" else None,
                      "kernel": "decode_partition_kernel" if bound == "hbm" else "prefill_kernel",
                      "kernel_us_per_launch": round(kern_ms * 1e3, 2),
+                     "kernel_timing": "start/end events stamped by that kernel's own "
+                                      "dispatch (hipExtLaunchKernel) in a second pass of "
+                                      "the same steps right after the timed pass",
                      "step_us": round(ev * 1e3, 2)},
     }
     del step
@@ -533,6 +571,7 @@ def main():
         extra = {}
         for label, name, splits in (("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
                                     ("causal_prefill", "causal_prefill", 0),
+                                    ("causal_prefill_fp8", "causal_prefill_fp8", 0),
                                     ("long_decode", "long_decode", 64),
                                     ("long_decode_auto_splits", "long_decode", -1),
                                     ("long_history_chunk", "long_history_chunk", 0),
@@ -543,12 +582,15 @@ def main():
                 splits = pa.decode_num_splits(c.B, c.Hkv, c.max_seq_len)
                 del c
             s = make_step(name, splits)
-            w2, e2 = time_step(s, max(5, args.steps // 3), 2)
+            w2, e2, k2 = time_step(s, max(5, args.steps // 3), 2)
             v2 = rate(s.units, e2, s.unit_name)
             pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
             extra[label] = {"value": round(v2, 2), "unit": s.unit_name,
                             "frac": round(v2 / pk, 4), "us_per_step": round(e2 * 1e3, 2),
                             "config": s.config()}
+            if k2:
+                extra[label]["main_kernel_us"] = round(k2 * 1e3, 2)
+                extra[label]["main_kernel_frac"] = round(rate(s.units, k2, s.unit_name) / pk, 4)
             log(f"[bench] {label}: {e2 * 1e3:.1f} us/step, {v2:.2f} {s.unit_name}")
             del s
             torch.cuda.empty_cache()

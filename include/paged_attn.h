@@ -304,6 +304,33 @@ int paged_attn_prefill_varlen_splitk(void* out, float* lse_out, const void* q,
 int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len);
 
 /*
+ * paged_attn_prefill_plan_splits -- a key-part count for
+ * paged_attn_prefill_varlen_splitk planned from host copies of the lengths (a
+ * scheduler knows them before it launches): q_lens[b] query rows over k_lens[b]
+ * keys, b < B, with the same causal flag and window_left as the launch.  Every
+ * query tile is counted in 64-key tiles and cut into parts as the kernel does.  A
+ * launch lasts at least its heaviest piece and at least the mean load per
+ * work-group slot of MI355X (256 CUs; one 256-row or two 128-row work-groups each),
+ * so the count starts at ceil(heaviest / mean - 0.05); each count from there to 8 is
+ * priced by placing its work-groups heaviest-first on the slots (as the grid is
+ * ordered), charging each work-group 2 tiles for its start and drain and the merge
+ * 3 tiles, and the cheapest count (the smallest within 3 % of it) is returned.  It is
+ * 1 when the heaviest tile is at most the mean or shorter than two 16-tile parts.
+ * Ragged batches of chunks over unequal histories ("The Stack Below the Stack
+ * (Part 2)", section 2.2; "Chapter 8: Attention Mechanisms", introduction: ragged
+ * batches) are the case it serves.  Host work grows with the work-group count
+ * (about 0.6 ms for 640 work-groups); beyond 16,384 (query tile, head) work-groups
+ * the starting bound is returned unpriced.
+ *
+ *   q_lens, k_lens : host arrays of B non-negative int32 (read only, not kept)
+ *
+ * Returns the count (>= 1), or 0 with pa_last_error() set when B < 0, Hq <= 0,
+ * window_left < 0, a length is negative, or an array is NULL with B > 0.
+ */
+int32_t paged_attn_prefill_plan_splits(int32_t B, const int32_t* q_lens, const int32_t* k_lens,
+                                       int32_t Hq, int32_t causal, int32_t window_left);
+
+/*
  * paged_attn_prefill_workspace_bytes -- workspace bytes of paged_attn_prefill_varlen_splitk
  * for this shape and num_splits (after resolving num_splits <= 0 as above): fp32
  * partial outputs [Tq * Hq, S, D] followed by fp32 partial lse [Tq * Hq, S], each
@@ -335,6 +362,14 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * The _ex entry points take every option of an operation in one struct; the
  * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
  * negative window PA_ERR_SHAPE.
+ *
+ * Kernel timing: kernel_start_event / kernel_stop_event, when not NULL, are HIP
+ * events (created beforehand, timing enabled, on the launch's device) that the
+ * dispatch of the operation's main kernel (decode: the partition kernel; prefill:
+ * the prefill kernel, not the merge) stamps with that kernel's own start and end
+ * (hipExtLaunchKernel).  hipEventElapsedTime on the pair then gives the kernel's
+ * duration inside a stream of work, with no event records added between launches.
+ * The library neither creates, records otherwise, nor destroys them.
  */
 typedef struct {
   int32_t num_splits;   /* as paged_attn_decode's (<= 0: the library's choice)            */
@@ -343,6 +378,9 @@ typedef struct {
   float k_scale;        /* kv_fp8 only                                                    */
   float v_scale;        /* kv_fp8 only                                                    */
   const float* alibi_slopes;  /* NULL, or device [Hq] float32 slopes (ALiBi above)        */
+  void* kernel_start_event;   /* NULL, or a created hipEvent_t (timing enabled) that the
+                                 partition kernel's dispatch stamps with its start       */
+  void* kernel_stop_event;    /* NULL, or a hipEvent_t stamped with that kernel's end     */
 } pa_decode_opts;
 
 typedef struct {
@@ -354,6 +392,9 @@ typedef struct {
   int32_t kv_fp8;       /* 0: bf16 pools; 1: E4M3 code pools (format above)               */
   float k_scale;        /* kv_fp8 only                                                    */
   float v_scale;        /* kv_fp8 only                                                    */
+  void* kernel_start_event;   /* NULL, or a created hipEvent_t (timing enabled) that the
+                                 prefill kernel's dispatch stamps with its start         */
+  void* kernel_stop_event;    /* NULL, or a hipEvent_t stamped with that kernel's end     */
 } pa_prefill_opts;
 
 /*

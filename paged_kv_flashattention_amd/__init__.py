@@ -52,8 +52,55 @@ class PagedAttnError(RuntimeError):
         super().__init__(f"{PA_STATUS.get(status, status)}: {detail}")
 
 
+_RECORDER = None
+
+
 def load_library():
-    return _lib.load()
+    return _RECORDER if _RECORDER is not None else _lib.load()
+
+
+class _Recorder:
+    """Stands in for the library while prepared() runs a call: forwards every C call
+    and keeps the launching ones with their marshalled arguments."""
+
+    _HOST_ONLY = ("_bytes", "_num_splits", "_plan_splits")
+
+    def __init__(self, lib):
+        self._lib = lib
+        self.launches = []
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name)
+        if name.startswith("pa_") or name.endswith(self._HOST_ONLY):
+            return fn
+
+        def call(*args):
+            self.launches.append((fn, args))
+            return fn(*args)
+        return call
+
+
+def prepared(call):
+    """Run ``call`` -- a function that makes calls of this module -- once, and return a
+    function that repeats exactly its C calls with the same marshalled arguments
+    (pointers, sizes, the stream current at preparation) without the Python-side
+    checks, for launch loops whose host cost matters.  The tensors ``call`` used must
+    stay alive, and keep their storage, while the returned function is used."""
+    global _RECORDER
+    rec = _Recorder(_lib.load())
+    _RECORDER = rec
+    try:
+        call()
+    finally:
+        _RECORDER = None
+    launches = list(rec.launches)
+
+    def run():
+        for fn, args in launches:
+            status = fn(*args)
+            if status != 0:
+                _check(status)
+    return run
 
 
 def library_path() -> str:
@@ -237,7 +284,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                       stream=None, validate: bool = False, window_left: int = 0,
-                      alibi_slopes: Optional[torch.Tensor] = None):
+                      alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
     """Decode attention: q [B, Hq, D] against each sequence's paged history.
 
     ``max_seq_len`` is a host-side bound of ``seq_lens``; if omitted it is read
@@ -245,10 +292,13 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
     natural-log lse [B, Hq] fp32 as well when ``return_lse``.  ``window_left`` = w > 0
     restricts each row to its last w keys (sliding window; see paged_attn_decode_ex);
     ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
+    ``kernel_events`` = (start, stop) torch.cuda.Event pair (timing enabled, recorded
+    once already) that the partition kernel's dispatch stamps with its own start and
+    end (see pa_decode_opts).
     """
     return _decode(None, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
                    num_splits, out, lse, workspace, return_lse, stream, validate, window_left,
-                   alibi_slopes)
+                   alibi_slopes, kernel_events)
 
 
 def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
@@ -257,13 +307,13 @@ def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_sca
                           lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                           stream=None, validate: bool = False, window_left: int = 0,
-                          alibi_slopes: Optional[torch.Tensor] = None):
+                          alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
     """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
     decode(code) * k_scale, values for decode(code) * v_scale.  Arguments and
     results are paged_attn_decode's."""
     return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
                    softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
-                   stream, validate, window_left, alibi_slopes)
+                   stream, validate, window_left, alibi_slopes, kernel_events)
 
 
 def _window(window_left) -> int:
@@ -284,9 +334,26 @@ def _alibi(slopes, Hq, dev):
     return slopes.data_ptr()
 
 
+def _events(kernel_events):
+    """(start, stop) raw hipEvent_t handles from a pair of torch.cuda.Event (created,
+    i.e. recorded at least once, with enable_timing=True) or of ints; (None, None)."""
+    if kernel_events is None:
+        return None, None
+    if len(kernel_events) != 2:
+        raise ValueError("kernel_events must be a (start, stop) pair")
+    out = []
+    for ev in kernel_events:
+        h = int(ev) if isinstance(ev, int) else int(ev.cuda_event)
+        if h == 0:
+            raise ValueError("kernel_events: a HIP event is created when first recorded; "
+                             "record each event once before passing it")
+        out.append(h)
+    return tuple(out)
+
+
 def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
             num_splits, out, lse, workspace, return_lse, stream, validate, window_left=0,
-            alibi_slopes=None):
+            alibi_slopes=None, kernel_events=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -328,8 +395,9 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
         _need(lse, "lse", torch.float32, 2, dev)
     lib = load_library()
     alibi_ptr = _alibi(alibi_slopes, Hq, dev)
+    ev0, ev1 = _events(kernel_events)
     opts = _lib.DecodeOpts(int(num_splits), window_left, 0 if scales is None else 1,
-                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr)
+                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr, ev0, ev1)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
     if need and workspace is None:
@@ -339,7 +407,7 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
-        if window_left or alibi_ptr is not None:
+        if window_left or alibi_ptr is not None or ev0 is not None:
             _check(lib.paged_attn_decode_ex(*head, int(max_seq_len), ctypes.byref(opts),
                                             *tail[2:]))
         elif scales is None:
@@ -387,8 +455,10 @@ def paged_attn_decode_partials(q, k_pool, v_pool, block_tables, seq_lens, softma
     return partial_out, partial_lse
 
 
-def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, stream=None):
-    """Merge partial_out [R, S, D] fp32 with partial_lse [R, S] fp32 -> (out bf16, lse fp32)."""
+def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, stream=None,
+                             want_lse: bool = True):
+    """Merge partial_out [R, S, D] fp32 with partial_lse [R, S] fp32 -> (out bf16, lse fp32).
+    With want_lse=False and no ``lse`` given, no lse is written (returned as None)."""
     _dtypes((partial_out, "partial_out", torch.float32), (partial_lse, "partial_lse", torch.float32),
             (out, "out", torch.bfloat16), (lse, "lse", torch.float32))
     dev = partial_out.device
@@ -400,9 +470,10 @@ def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, strea
     if out is None:
         out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, 2, dev)
-    if lse is None:
+    if lse is None and want_lse:
         lse = torch.empty((R,), dtype=torch.float32, device=dev)
-    _need(lse, "lse", torch.float32, 1, dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 1, dev)
     with torch.cuda.device(dev):
         _check(load_library().paged_attn_splitk_reduce(
             _ptr(out), _ptr(lse), _ptr(partial_out), _ptr(partial_lse), R, S, D,
@@ -416,17 +487,18 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                               out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                               stream=None, validate: bool = False, window_left: int = 0,
-                              alibi_slopes: Optional[torch.Tensor] = None):
+                              alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
     """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
 
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
     omitted it is read from the device (a synchronisation).  ``window_left`` = w > 0
     restricts the row at position p to keys j > p - w (sliding window);
     ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
+    ``kernel_events`` as paged_attn_decode's, for the prefill kernel.
     """
     return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
                     softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate,
-                    window_left, alibi_slopes)
+                    window_left, alibi_slopes, kernel_events=kernel_events)
 
 
 def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
@@ -437,17 +509,37 @@ def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, b
                                   workspace: Optional[torch.Tensor] = None,
                                   return_lse: bool = False, stream=None,
                                   validate: bool = False, window_left: int = 0,
-                                  alibi_slopes: Optional[torch.Tensor] = None):
+                                  alibi_slopes: Optional[torch.Tensor] = None,
+                                  kernel_events=None):
     """Ragged prefill over FP8 E4M3 pools (uint8 codes; keys stand for decode(code) *
     k_scale, values for decode(code) * v_scale), through paged_attn_prefill_ex.
     ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass)."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
-                    validate, window_left, alibi_slopes, _scales(k_scale, v_scale))
+                    validate, window_left, alibi_slopes, _scales(k_scale, v_scale),
+                    kernel_events)
 
 
 def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:
     return int(load_library().paged_attn_prefill_num_splits(B, Hq, max_q_len))
+
+
+def prefill_plan_splits(q_lens, k_lens, Hq: int, causal: bool = True,
+                        window_left: int = 0) -> int:
+    """Key parts for paged_attn_prefill_varlen_splitk planned from host lengths
+    (sequences of ints: query rows and keys per sequence); see
+    paged_attn_prefill_plan_splits in C."""
+    q = (ctypes.c_int32 * len(q_lens))(*[int(x) for x in q_lens])
+    k = (ctypes.c_int32 * len(k_lens))(*[int(x) for x in k_lens])
+    if len(q) != len(k):
+        raise ValueError("q_lens and k_lens must have one entry per sequence")
+    lib = load_library()
+    s = int(lib.paged_attn_prefill_plan_splits(len(q), ctypes.cast(q, ctypes.c_void_p),
+                                               ctypes.cast(k, ctypes.c_void_p), int(Hq),
+                                               1 if causal else 0, _window(window_left)))
+    if s <= 0:
+        raise PagedAttnError(2, lib.pa_last_error().decode())
+    return s
 
 
 def prefill_workspace_bytes(B, Tq, max_q_len, Hq, D, num_splits=0) -> int:
@@ -464,17 +556,18 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
                                      workspace: Optional[torch.Tensor] = None,
                                      return_lse: bool = False, stream=None,
                                      validate: bool = False, window_left: int = 0,
-                                     alibi_slopes: Optional[torch.Tensor] = None):
+                                     alibi_slopes: Optional[torch.Tensor] = None,
+                                     kernel_events=None):
     """Ragged prefill with long key ranges cut into at most ``num_splits`` parts
     (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
-                    validate, window_left, alibi_slopes)
+                    validate, window_left, alibi_slopes, None, kernel_events)
 
 
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
              causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
-             alibi_slopes=None, scales=None):
+             alibi_slopes=None, scales=None, kernel_events=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -524,7 +617,9 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
             P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0)
     alibi_ptr = _alibi(alibi_slopes, Hq, dev)
-    general = bool(window_left) or alibi_ptr is not None or scales is not None
+    ev0, ev1 = _events(kernel_events)
+    general = (bool(window_left) or alibi_ptr is not None or scales is not None
+               or ev0 is not None)
     if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
@@ -542,7 +637,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         elif general:
             ks, vs = scales if scales is not None else (1.0, 1.0)
             opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
-                                    0 if scales is None else 1, ks, vs)
+                                    0 if scales is None else 1, ks, vs, ev0, ev1)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

@@ -22,7 +22,8 @@ class DecodeOpts(ctypes.Structure):
     """pa_decode_opts"""
     _fields_ = [("num_splits", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+                ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
+                ("kernel_start_event", ctypes.c_void_p), ("kernel_stop_event", ctypes.c_void_p)]
 
 
 class PrefillOpts(ctypes.Structure):
@@ -30,7 +31,8 @@ class PrefillOpts(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("kernel_start_event", ctypes.c_void_p),
+                ("kernel_stop_event", ctypes.c_void_p)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)
@@ -64,6 +66,7 @@ SIGNATURES = {
                                                  c_i32, c_i32, c_i32, c_float, c_i32, c_i32,
                                                  c_vp, c_size, c_vp]),
     "paged_attn_prefill_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
+    "paged_attn_prefill_plan_splits": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, c_i32]),
     "paged_attn_prefill_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "paged_attn_decode_ex": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,

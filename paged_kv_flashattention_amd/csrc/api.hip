@@ -3,6 +3,11 @@
 // a failing call leaves outputs untouched; the only device work is the kernels'.
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
 #include <string.h>
 
 #include "../../include/paged_attn.h"
@@ -190,7 +195,7 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
                 float k_scale, float v_scale, void* stream, int32_t window = 0,
-                const float* alibi = nullptr) {
+                const float* alibi = nullptr, const pa::KernelEvents& ev = pa::KernelEvents()) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
@@ -220,7 +225,7 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char d1[256], d2[256];
-  hipError_t e = pa::launch_decode(a, s, d1, sizeof(d1));
+  hipError_t e = pa::launch_decode(a, s, d1, sizeof(d1), ev);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
   if (S > 1) {
     pa::ReduceArgs r{};
@@ -272,7 +277,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
                  const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
-                 float v_scale = 1.f) {
+                 float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents()) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -335,7 +340,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char d1[320], d2[256];
-  hipError_t e = pa::launch_prefill(a, hs, d1, sizeof(d1));
+  hipError_t e = pa::launch_prefill(a, hs, d1, sizeof(d1), ev);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
   if (S > 1) {
     e = pa::launch_prefill_merge(a, hs, d2, sizeof(d2));
@@ -349,6 +354,15 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
 }
 
 }  // namespace
+
+// The caller's optional kernel-timing events of an options struct.
+template <typename Opts>
+static pa::KernelEvents events_of(const Opts* o) {
+  pa::KernelEvents ev;
+  ev.start = static_cast<hipEvent_t>(o->kernel_start_event);
+  ev.stop = static_cast<hipEvent_t>(o->kernel_stop_event);
+  return ev;
+}
 
 extern "C" {
 
@@ -498,6 +512,116 @@ int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len) 
   return resolve_prefill_splits(B, Hq, max_q_len, 0);
 }
 
+// Host planning of the key-part count from the lengths themselves.  Each query tile
+// is counted in 64-key tiles exactly as the kernel bounds it (causal limit, window
+// start) and cut into parts exactly as the kernel cuts it.  A launch lasts at least
+// its heaviest piece and at least the mean load per work-group slot, so the count
+// starts at ceil(heaviest / mean) (less 5 % of slack for rounding); from there up to
+// 8 each count is priced by list-scheduling its work-groups heaviest-first onto the
+// slots (the grid's own order), each work-group charged kPlanWgTiles for its start
+// and drain and the launch kPlanMergeTiles for the merge when anything is cut.  The
+// cheapest count wins, the smallest within 3 % of it.
+constexpr long long kPlanWgTiles = 2;
+constexpr long long kPlanMergeTiles = 3;
+
+static long long plan_makespan(const std::vector<long long>& tiles, int32_t Hq, int s,
+                               long long slots, std::vector<long long>& jobs) {
+  jobs.clear();
+  bool cut = false;
+  for (const long long t : tiles) {
+    long long p = 1;
+    if (s > 1) {
+      p = t / kPrefillPartMinTiles;
+      if (p > s) p = s;
+      if (p < 1) p = 1;
+    }
+    cut |= p > 1;
+    for (long long k = 0; k < p; ++k) {
+      const long long len = (k + 1) * t / p - k * t / p + kPlanWgTiles;
+      for (int32_t h = 0; h < Hq; ++h) jobs.push_back(len);
+    }
+  }
+  std::sort(jobs.begin(), jobs.end(), std::greater<long long>());
+  std::priority_queue<long long, std::vector<long long>, std::greater<long long>> load;
+  for (long long i = 0; i < slots; ++i) load.push(0);
+  long long span = 0;
+  for (const long long j : jobs) {
+    const long long x = load.top() + j;
+    load.pop();
+    load.push(x);
+    if (x > span) span = x;
+  }
+  return span + (cut ? kPlanMergeTiles : 0);
+}
+
+int32_t paged_attn_prefill_plan_splits(int32_t B, const int32_t* q_lens, const int32_t* k_lens,
+                                       int32_t Hq, int32_t causal, int32_t window_left) {
+  g_last_error[0] = 0;
+  if (B < 0 || Hq <= 0 || window_left < 0) {
+    fail(PA_ERR_SHAPE, "prefill_plan_splits: B=%d Hq=%d window_left=%d", B, Hq, window_left);
+    return 0;
+  }
+  if (B == 0) return 1;
+  if (!q_lens || !k_lens) {
+    fail(PA_ERR_NULL, "prefill_plan_splits: q_lens or k_lens is NULL");
+    return 0;
+  }
+  int32_t max_q = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (q_lens[b] < 0 || k_lens[b] < 0) {
+      fail(PA_ERR_SHAPE, "prefill_plan_splits: sequence %d has q_len %d, k_len %d", b,
+           q_lens[b], k_lens[b]);
+      return 0;
+    }
+    if (q_lens[b] > max_q) max_q = q_lens[b];
+  }
+  if (max_q == 0) return 1;
+  const int W = pa::prefill_waves(max_q);
+  const int bm = 32 * W;
+  std::vector<long long> tiles;
+  long long total = 0, heavy = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const long long q = q_lens[b], L = k_lens[b];
+    for (long long r0 = 0; r0 < q; r0 += bm) {
+      const long long rows = q - r0 < bm ? q - r0 : bm;
+      long long k_lim = L;
+      if (causal) {
+        const long long lim = L - q + r0 + rows;
+        k_lim = lim < 0 ? 0 : (lim < L ? lim : L);
+      }
+      const long long n = (k_lim + 63) / 64;
+      long long first = 0;
+      if (window_left > 0) {
+        const long long lo = L - q + r0 - window_left + 1;
+        first = lo > 0 ? lo / 64 : 0;
+        if (first > n) first = n;
+      }
+      tiles.push_back(n - first);
+      total += n - first;
+      if (n - first > heavy) heavy = n - first;
+    }
+  }
+  const long long slots = 256ll * (8 / W);
+  // r = heaviest / mean = heavy * slots / work; the count starts at ceil(r - 0.05)
+  const long long work = total * Hq;
+  if (heavy < 2 * kPrefillPartMinTiles || heavy * slots <= work) return 1;
+  long long s_lo = (heavy * slots * 20 - work + work * 20 - 1) / (work * 20);
+  if (s_lo < 1) s_lo = 1;
+  if (s_lo > 8) return 8;
+  // a grid this large is priced by the bound alone
+  if ((long long)tiles.size() * Hq > (1ll << 14)) return (int32_t)s_lo;
+  std::vector<long long> jobs;
+  long long cost[9] = {0};
+  long long best = -1;
+  for (long long s = s_lo; s <= 8; ++s) {
+    cost[s] = plan_makespan(tiles, Hq, (int)s, slots, jobs);
+    if (best < 0 || cost[s] < best) best = cost[s];
+  }
+  for (long long s = s_lo; s <= 8; ++s)
+    if (cost[s] * 100 <= best * 103) return (int32_t)s;
+  return 8;
+}
+
 size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len, int32_t Hq,
                                           int32_t D, int32_t num_splits) {
   if (B <= 0 || Tq <= 0 || max_q_len <= 0 || Hq <= 0 || D <= 0) return 0;
@@ -534,7 +658,7 @@ int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k
                      max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
                      opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
                      opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
-                     stream, opts->window_left, opts->alibi_slopes);
+                     stream, opts->window_left, opts->alibi_slopes, events_of(opts));
 }
 
 size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -559,7 +683,7 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
                       workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
-                      opts->kv_fp8 == 1, opts->k_scale, opts->v_scale);
+                      opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts));
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

@@ -476,12 +476,13 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
 }
 
 template <int D, int W>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream,
+                                  const KernelEvents& ev) {
   dim3 grid(a.Hkv, a.S, a.B);
   if (a.kv_fp8)
-    hipLaunchKernelGGL((decode_partition_kernel<D, W, true>), grid, dim3(64 * W), 0, stream, a);
+    launch_kernel(decode_partition_kernel<D, W, true>, grid, dim3(64 * W), 0, stream, ev, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, W, false>), grid, dim3(64 * W), 0, stream, a);
+    launch_kernel(decode_partition_kernel<D, W, false>, grid, dim3(64 * W), 0, stream, ev, a);
   return hipGetLastError();
 }
 
@@ -498,15 +499,18 @@ static int decode_waves(const DecodeArgs& a) {
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream, int W) {
-  if (W == 4) return launch_decode_t<D, 4>(a, stream);
-  if (W == 2) return launch_decode_t<D, 2>(a, stream);
-  return launch_decode_t<D, 1>(a, stream);
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream, int W,
+                                  const KernelEvents& ev) {
+  if (W == 4) return launch_decode_t<D, 4>(a, stream, ev);
+  if (W == 2) return launch_decode_t<D, 2>(a, stream, ev);
+  return launch_decode_t<D, 1>(a, stream, ev);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len,
+                         const KernelEvents& ev) {
   const int W = decode_waves(a);
-  hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W) : launch_decode_d<64>(a, stream, W);
+  hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W, ev)
+                            : launch_decode_d<64>(a, stream, W, ev);
   snprintf(desc, desc_len,
            "decode_partition<D=%d,W=%d,%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
            W, a.kv_fp8 ? "fp8-e4m3" : "bf16", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);

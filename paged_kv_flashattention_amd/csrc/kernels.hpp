@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer (api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -74,14 +75,32 @@ struct PrefillArgs {
   float* part_lse;               // [Tq * Hq, S] partial natural-log lse   (S > 1)
 };
 
+// Optional events stamped with one kernel's own start and end: the dispatch
+// carries them (hipExtLaunchKernel), so measuring adds no work to the stream.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... Args>
+inline void launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds,
+                          hipStream_t stream, const KernelEvents& ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
+
 // Each launcher enqueues on `stream` and returns hipGetLastError() of the launch;
-// `desc` (>= 256 bytes) receives a one-line description of what was launched.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len);
+// `desc` (>= 256 bytes) receives a one-line description of what was launched.  The
+// decode and prefill launchers stamp `ev` around their main kernel.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len,
+                         const KernelEvents& ev = KernelEvents());
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, char* desc, size_t desc_len);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
                            size_t desc_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
-                          size_t desc_len);
+                          size_t desc_len, const KernelEvents& ev = KernelEvents());
 // with S > 1: merges the rows whose query tile was split (after launch_prefill)
 hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream, char* desc,
                                 size_t desc_len);

@@ -721,7 +721,8 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
 }
 
 template <int D, int W, bool GEN, bool F8, bool REV>
-static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
+static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
+                                   const KernelEvents& ev) {
   // more than 64 KiB of dynamic LDS must be requested once per process
   static const hipError_t attr = PfLds<D>::BYTES > 65536
       ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV>),
@@ -729,21 +730,22 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream) {
       : hipSuccess;
   if (attr != hipSuccess) return attr;
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
-  hipLaunchKernelGGL((prefill_kernel<D, W, GEN, F8, REV>), grid, dim3(64 * W), PfLds<D>::BYTES, stream,
-                     a);
+  launch_kernel(prefill_kernel<D, W, GEN, F8, REV>, grid, dim3(64 * W), (uint32_t)PfLds<D>::BYTES,
+                stream, ev, a);
   return hipGetLastError();
 }
 
 // the sliding-window bound and the ALiBi bias are compiled only into the general
 // variant
 template <int D, int W>
-static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
+                                   const KernelEvents& ev) {
   if (a.kv_fp8)
-    return a.alibi ? launch_prefill_w<D, W, true, true, true>(a, stream)
-                   : launch_prefill_w<D, W, true, true, false>(a, stream);
-  if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream);
-  return a.window > 0 ? launch_prefill_w<D, W, true, false, false>(a, stream)
-                      : launch_prefill_w<D, W, false, false, false>(a, stream);
+    return a.alibi ? launch_prefill_w<D, W, true, true, true>(a, stream, ev)
+                   : launch_prefill_w<D, W, true, true, false>(a, stream, ev);
+  if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
+  return a.window > 0 ? launch_prefill_w<D, W, true, false, false>(a, stream, ev)
+                      : launch_prefill_w<D, W, false, false, false>(a, stream, ev);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
@@ -777,14 +779,14 @@ hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, cha
 }
 
 hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
-                          size_t desc_len) {
+                          size_t desc_len, const KernelEvents& ev) {
   const int W = prefill_waves(a_in.max_q_len);
   const PrefillArgs a = prefill_shape(a_in, W);
   hipError_t e;
   if (a.D == 128)
-    e = W == 8 ? launch_prefill_t<128, 8>(a, stream) : launch_prefill_t<128, 4>(a, stream);
+    e = W == 8 ? launch_prefill_t<128, 8>(a, stream, ev) : launch_prefill_t<128, 4>(a, stream, ev);
   else
-    e = W == 8 ? launch_prefill_t<64, 8>(a, stream) : launch_prefill_t<64, 4>(a, stream);
+    e = W == 8 ? launch_prefill_t<64, 8>(a, stream, ev) : launch_prefill_t<64, 4>(a, stream, ev);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s) block=%d lds=%zu",

@@ -32,6 +32,7 @@ def test_header_declares_the_four_operations():
     for n in ["kv_page_write", "paged_attn_decode", "paged_attn_splitk_reduce",
               "paged_attn_prefill_varlen", "kv_page_write_fp8", "paged_attn_decode_fp8",
               "paged_attn_prefill_varlen_splitk", "paged_attn_prefill_num_splits",
+              "paged_attn_prefill_plan_splits",
               "paged_attn_prefill_workspace_bytes", "paged_attn_decode_ex",
               "paged_attn_decode_ex_workspace_bytes", "paged_attn_prefill_ex",
               "paged_attn_prefill_ex_workspace_bytes", "paged_attn_decode_workspace_bytes",
@@ -297,3 +298,103 @@ def test_failed_call_leaves_output_untouched(require_gpu):
     assert e.value.status == 5
     torch.cuda.synchronize()
     assert (out.float() == 7.0).all()
+
+
+def _tiles_model(q_lens, k_lens, causal, window):
+    """Per-query-tile 64-key counts, restated from the kernel's documented bounds:
+    a tile of R rows (R = 256 when the longest query run reaches 1,024, else 128)
+    whose last row sits at position p_last needs keys 0 .. p_last (all keys without
+    causal), and with a window w its first row's window starts at p_first - w + 1."""
+    R = 256 if max(q_lens) >= 1024 else 128
+    out = []
+    for q, L in zip(q_lens, k_lens):
+        for r0 in range(0, q, R):
+            r1 = min(q, r0 + R)                       # one past the tile's last row
+            last_key = L - q + r1 if causal else L    # keys [0, last_key)
+            last_key = max(0, min(L, last_key))
+            n = -(-last_key // 64)
+            first = 0
+            if window > 0:
+                first = min(max(0, L - q + r0 - window + 1) // 64, n)
+            out.append(n - first)
+    return out, 256 * (8 * 32 // R)
+
+
+def _makespan(tiles, Hq, s, slots):
+    """Heaviest-first list scheduling of the work-groups of part count s onto the
+    slots: each (tile, head) cut into p = min(s, tiles // 16) (at least 1) parts of
+    consecutive key tiles, each work-group charged 2 extra tiles, the merge 3."""
+    import heapq
+    jobs, cut = [], False
+    for t in tiles:
+        p = max(1, min(s, t // 16)) if s > 1 else 1
+        cut |= p > 1
+        jobs += [(k + 1) * t // p - k * t // p + 2 for k in range(p)] * Hq
+    loads = [0] * slots
+    for j in sorted(jobs, reverse=True):
+        heapq.heappush(loads, heapq.heappop(loads) + j)
+    return max(loads) + (3 if cut else 0)
+
+
+def _plan_model(q_lens, k_lens, Hq, causal, window):
+    if not q_lens or max(q_lens) == 0:
+        return 1
+    tiles, slots = _tiles_model(q_lens, k_lens, causal, window)
+    heavy, work = max(tiles), sum(tiles) * Hq
+    if heavy < 32 or heavy * slots <= work:
+        return 1
+    # ceil(heavy / mean - 0.05), mean = work / slots
+    s_lo = max(1, -(-(20 * heavy * slots - work) // (20 * work)))
+    if s_lo > 8:
+        return 8
+    if len(tiles) * Hq > 1 << 14:
+        return s_lo
+    cost = {s: _makespan(tiles, Hq, s, slots) for s in range(s_lo, 9)}
+    best = min(cost.values())
+    return min(s for s, c in cost.items() if c * 100 <= best * 103)
+
+
+def test_prefill_plan_splits_null_arrays(lib):
+    assert lib.paged_attn_prefill_plan_splits(2, None, None, 8, 1, 0) == 0
+    assert b"NULL" in lib.pa_last_error()
+    assert lib.paged_attn_prefill_plan_splits(0, None, None, 8, 1, 0) == 1
+
+
+def test_prefill_plan_splits_host_logic():
+    """The planner (host code, no GPU) against a restatement of its rule on fixed
+    and random batches, its documented special cases, and its rejections."""
+    import numpy as np
+    import paged_kv_flashattention_amd as pa
+    from paged_kv_flashattention_amd import PagedAttnError
+    # a full grid of equal causal rows needs no parts
+    assert pa.prefill_plan_splits([4096] * 4, [4096] * 4, 32) == 1
+    # 5 chunks of 512 over histories 214 .. 4,113: the heaviest tile (73 key tiles)
+    # is 2.1 times the mean load per slot; 3 parts leave the heavy chunk's pieces
+    # badly packed, 4 do not
+    assert pa.prefill_plan_splits([512] * 5, [1732, 726, 4625, 1703, 850], 32) == 4
+    # one chunk over a long history: 128 work-groups of ~520 tiles on 512 slots --
+    # 4 parts fill the slots once; 5 would need a second round for 128 of them
+    assert pa.prefill_plan_splits([512], [33280], 32) == 4
+    assert pa.prefill_plan_splits([512], [33280], 1) == 8           # capped at 8
+    assert pa.prefill_plan_splits([512], [600], 1) == 1             # too short to cut
+    assert pa.prefill_plan_splits([], [], 32) == 1
+    assert pa.prefill_plan_splits([0, 0], [100, 5], 32) == 1
+    rng = np.random.default_rng(7)
+    for _ in range(60):
+        B = int(rng.integers(1, 7))
+        q = [int(x) for x in rng.integers(0, 1500, B)]
+        h = [int(x) for x in rng.integers(0, 40000, B)]
+        k = [a + b for a, b in zip(q, h)]
+        Hq = int(rng.choice([1, 4, 8, 32]))
+        causal = bool(rng.integers(0, 2))
+        window = int(rng.choice([0, 0, 100, 3000]))
+        got = pa.prefill_plan_splits(q, k, Hq, causal=causal, window_left=window)
+        assert got == _plan_model(q, k, Hq, causal, window), (q, k, Hq, causal, window)
+        assert 1 <= got <= 8
+    for q, k in (([1], [-1]), ([-3], [10])):
+        with pytest.raises(PagedAttnError):
+            pa.prefill_plan_splits(q, k, 32)
+    with pytest.raises(PagedAttnError):
+        pa.prefill_plan_splits([1], [1], 0)
+    with pytest.raises(ValueError):
+        pa.prefill_plan_splits([1], [1], 8, window_left=-1)

@@ -186,19 +186,22 @@ def test_long_history_chunk_full_size_sampled(require_gpu):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("splitk", [False, True])
+@pytest.mark.parametrize("splitk", [0, 4, -1])
 def test_mixed_ragged_step_full_size(require_gpu, splitk):
     """The mixed step: write all 2,578 new tokens, prefill the five 512-token chunks over
-    their history (in one pass, or with long key ranges split and merged), decode the
-    18 single-token requests, all on the same pools."""
+    their history (in one pass, or with long key ranges split into 4 parts or into the
+    host planner's count, and merged), decode the 18 single-token requests, all on the
+    same pools."""
     case = make_config("mixed_ragged", "cuda")
+    n_pf = 5
+    if splitk < 0:
+        splitk = pa.prefill_plan_splits(case.q_lens[:n_pf], case.seq_lens[:n_pf], case.Hq)
     print(f"[mixed] mixed_ragged full size, splitk={splitk}", flush=True)
     kp, vp = pools_after_write(case)
     write(case)
-    n_pf = 5
     cu = case.cu_seqlens_q
     t_pf = int(cu[n_pf])
-    extra = dict(num_splits=4) if splitk else {}
+    extra = dict(num_splits=splitk) if splitk else {}
     prefill = pa.paged_attn_prefill_varlen_splitk if splitk else pa.paged_attn_prefill_varlen
     out_p, lse_p = prefill(
         case.q[:t_pf], case.k_pool, case.v_pool, cu[:n_pf + 1].contiguous(),
