@@ -525,6 +525,8 @@ def main():
     wall, ev, kern_ms = time_step(step, args.steps, args.warmup)
     value = rate(step.units, ev, step.unit_name)
     launch = pa.describe_launch()
+    if kern_ms is None:                      # the mixed step: no single main kernel
+        kern_ms = ev
     achieved = rate(step.units, kern_ms, step.unit_name)
     log(f"[bench] {args.workload}: {ev * 1e3:.1f} us/step (events), {wall * 1e3:.1f} us/step "
         f"(wall), {value:.1f} {step.unit_name}; dominant kernel {kern_ms * 1e3:.1f} us, "
@@ -548,7 +550,8 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": step.unit_name, "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic() if args.workload == "qwen7b_decode" else None,
-                     "kernel": "decode_partition_kernel" if bound == "hbm" else "prefill_kernel",
+                     "kernel": ("decode_partition_kernel" if bound == "hbm" else "prefill_kernel")
+                     if not isinstance(step, MixedStep) else "whole step",
                      "kernel_us_per_launch": round(kern_ms * 1e3, 2),
                      "kernel_timing": "start/end events stamped by that kernel's own "
                                       "dispatch (hipExtLaunchKernel) in a second pass of "
