@@ -590,6 +590,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   constexpr int B0 = REV ? 1 : 0, B1 = 1 - B0;
   auto tile_at = [&](int u) { return REV ? tile_hi - 1 - u : tile_lo + u; };
   const int nt = tile_hi - tile_lo;
+  // Walking upwards, the blocks from the first key past this wave's last valid row
+  // on are masked for all of its rows (causal), as are blocks past the sequence end:
+  // the wave computes only its first G blocks (finishing the last of them) and for
+  // the remaining tiles only moves its share and meets the barriers.  In the
+  // diagonal region of a 256-row tile that leaves 28 of the 64 (wave, block) steps
+  // to the other waves.  The steady loop below is the same for every wave; only
+  // where a wave's blocks end does it take the short tail.
+  const int w_last = min(r_w + 31, q_len - 1);              // last valid row of the wave
+  const int w_key_end = __builtin_amdgcn_readfirstlane(
+      !a.causal ? L : (w_last < r_w ? 0 : min(L, shift + w_last + 1)));
+  // finish the pending block (P from its scores, P V from V tile vp, block kbp)
+  auto finish = [&](f32x16& sp, const uint16_t* vp, int kbp) {
+    uint32_t pw[8];
+    float ps;
+    exps(sp, pw, ps);
+    settle(sp, pw, ps);
+    pv(vp, kbp, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
+  };
   if (nt > 0) {
     base_t = REV ? max(0, tile_hi - 64) : tile_lo;
     tab = load_tab(base_t);
@@ -597,11 +615,20 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     issue(tile_at(0), 0);
     publish(tile_at(0), 0);
     if (nt > 1) issue(tile_at(1), 1);
+    // G: blocks this wave computes, in walk order (wave-uniform)
+    const int G = REV ? 2 * nt
+                      : min(2 * nt, max(0, (w_key_end - tile_lo * kPfBN + 31) / 32));
     // first block: scores, mask, first reference
-    f32x16 s_pend = qk(kst(tile_at(0)), B0);
-    mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
-    decide(rowmax(s_pend));
-    for (int u = 0; u + 1 < nt; ++u) {
+    f32x16 s_pend;
+    if (G > 0) {
+      s_pend = qk(kst(tile_at(0)), B0);
+      mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
+      decide(rowmax(s_pend));
+    }
+    // iterations u whose two steps both score a computed block (2 u + 2 < G)
+    const int U1 = G > 0 ? min(nt - 1, (G - 1) / 2) : 0;
+    int u = 0;
+    for (; u < U1; ++u) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // first block of tile kt (pending) -> its second block
@@ -614,14 +641,39 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       mask(s_pend, kn * kPfBN + 32 * B0);
       vs_cur = vs_next;
     }
-    const int kl = tile_at(nt - 1);
-    step(s_pend, kst(kl), B1, vst(vs_cur), B0);
-    mask(s_pend, kl * kPfBN + 32 * B1);
-    uint32_t pw[8];
-    float ps;
-    exps(s_pend, pw, ps);
-    settle(s_pend, pw, ps);
-    pv(vst(vs_cur), B1, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    if (u == nt - 1) {
+      // the last tile: both of its blocks (G = 2 nt), only its first (G = 2 nt - 1),
+      // or none (G = 0, one tile)
+      const int kl = tile_at(u);
+      if (G == 2 * nt) {
+        step(s_pend, kst(kl), B1, vst(vs_cur), B0);
+        mask(s_pend, kl * kPfBN + 32 * B1);
+        finish(s_pend, vst(vs_cur), B1);
+      } else if (G == 2 * nt - 1) {
+        finish(s_pend, vst(vs_cur), B0);
+      }
+    } else {
+      // this wave's blocks end in tile u (G = 2 u + 1 or 2 u + 2) or there are none
+      const int kt = tile_at(u), kn = tile_at(u + 1);
+      const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
+      if (G == 2 * u + 2) {
+        step(s_pend, kst(kt), B1, vst(vs_cur), B0);
+        mask(s_pend, kt * kPfBN + 32 * B1);
+      } else if (G == 2 * u + 1) {
+        finish(s_pend, vst(vs_cur), B0);
+      }
+      publish(kn, vs_next);
+      if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
+      if (G == 2 * u + 2) finish(s_pend, vst(vs_cur), B1);
+      vs_cur = vs_next;
+      // the remaining tiles: this wave's share of each is moved, nothing computed
+      for (++u; u + 1 < nt; ++u) {
+        const int vs_n = vs_cur == 2 ? 0 : vs_cur + 1;
+        publish(tile_at(u + 1), vs_n);
+        if (u + 2 < nt) issue(tile_at(u + 2), vs_n == 2 ? 0 : vs_n + 1);
+        vs_cur = vs_n;
+      }
+    }
   }
 
   if (!row_ok) return;

@@ -225,3 +225,28 @@ def test_mixed_ragged_step_full_size(require_gpu, splitk):
     got_l = np.array([float(lse_p[t, h]) if t < t_pf else float(lse_d[t - t_pf, h])
                       for t, h in rows])
     assert_lse(got_l, l_ref, "mixed lse")
+
+
+@pytest.mark.parametrize("hist,ql", [
+    # 256-row tiles (a run of >= 1024): rows ending at every offset within a wave's 32
+    # and a block's 32 keys, waves with no valid row, with and without history
+    ([0, 0, 0, 0], [1024, 31, 33, 257]),
+    ([0, 5, 64], [1025, 63, 65]),
+    ([100, 0], [1100, 1]),
+    # 128-row tiles
+    ([0, 0, 0], [129, 32, 95]),
+    ([37, 0], [200, 64]),
+])
+def test_causal_prefill_rows_ending_mid_tile(require_gpu, hist, ql):
+    """Causal rows whose last key falls anywhere in a tile: each wave computes only
+    the blocks up to its last valid row (the rest of its tiles it only moves), so
+    every (tile size, row offset, history) combination is checked against the oracle."""
+    print(f"[prefill causal tail] hist={hist} q={ql}", flush=True)
+    case = make_case("pft", hist_lens=hist, q_lens=ql, write_new=True, causal=True, Hq=8,
+                     Hkv=2, D=128, page_size=16, seed=sum(ql) + 77, device="cuda")
+    kp, vp = pools_after_write(case)
+    write(case)
+    out, lse = run_prefill(case)
+    o_ref, l_ref = oracle_full(case, kp, vp)
+    assert_parity(as_f64(out), o_ref, "prefill causal tail")
+    assert_lse(as_f64(lse), l_ref, "prefill causal tail lse")
