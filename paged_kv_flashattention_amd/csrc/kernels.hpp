@@ -104,7 +104,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
 // with S > 1: merges the rows whose query tile was split (after launch_prefill)
 hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream, char* desc,
                                 size_t desc_len);
-// waves per prefill work-group (32 query rows each) for the longest query run
-int prefill_waves(int max_q_len);
+// waves per prefill work-group (32 query rows each) for the longest query run (and
+// whether the pools are FP8 with ALiBi slopes)
+int prefill_waves(int max_q_len, bool fp8_alibi = false);
 
 }  // namespace pa

@@ -197,10 +197,13 @@ __device__ __forceinline__ u32x2 pf_fp8x4_to_bf16(uint32_t w) {
 }
 
 // W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
-// variant (sliding window, ALiBi); F8: FP8 E4M3 pools and REV: key tiles walked
-// downwards (ALiBi), both in the general variant only.
+// variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
+// downwards, which is how the ALiBi variants (general only) walk, so REV also
+// compiles the bias in.
 template <int D, int W, bool GEN, bool F8, bool REV>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
+  static_assert(!REV || GEN, "the downward walk is a general-variant feature");
+  constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
   using M_ = PfDma<D, W>;
@@ -277,13 +280,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // (raw units; the scores are scaled later); the block start less the row's
   // position is one value per block and row, added with the softmax reference
   // (log2 units, `boff`, set when a block's scores are masked).
-  const float slope_log2 = GEN && a.alibi ? a.alibi[h] * kLog2e : 0.f;
+  const float slope_log2 = ALI ? a.alibi[h] * kLog2e : 0.f;
   f32x16 ebias;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ebias[4 * j + i] = GEN ? slope_log2 / a.scale_log2 * (float)(8 * j + 4 * hh + i) : 0.f;
+      ebias[4 * j + i] = ALI ? slope_log2 / a.scale_log2 * (float)(8 * j + 4 * hh + i) : 0.f;
   float boff = 0.f;
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
@@ -429,14 +432,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, sc[e]), sc[e + 1]);
     mt = fmaxf(mt, sc[15]);
     const float r = xor32_max(mt) * a.scale_log2;
-    return GEN ? r + boff : r;
+    return ALI ? r + boff : r;
   };
   // The block's ALiBi offset (general variant), then -inf for keys past the end,
   // (causal) above the diagonal and (window) below a row's window; only blocks that
   // touch one of these boundaries need the second part.  Called once per block,
   // right after its scores are formed and before they are used.
   auto mask = [&](f32x16& sc, int kb0) {
-    if (GEN) boff = slope_log2 * (float)(kb0 - my_pos);
+    if (ALI) boff = slope_log2 * (float)(kb0 - my_pos);
     const bool need =
         (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (GEN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // multiplies V
   auto exps = [&](const f32x16& sc, uint32_t* pw, float& ps) {
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
-    const float neg_m = GEN ? neg_m0 + boff : neg_m0;
+    const float neg_m = ALI ? neg_m0 + boff : neg_m0;
     ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
     constexpr int NV = 2 * (D / 32);           // PV MFMAs
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
-    const float neg_m = GEN ? neg_m0 + boff : neg_m0;
+    const float neg_m = ALI ? neg_m0 + boff : neg_m0;
     const uint16_t* kl = kq + k_lane + kbq * 32 * D;
     u32x4 kf[NK];
     kf[0] = *reinterpret_cast<const u32x4*>(kl);
@@ -792,17 +795,26 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
 template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
-  if (a.kv_fp8)
-    return a.alibi ? launch_prefill_w<D, W, true, true, true>(a, stream, ev)
-                   : launch_prefill_w<D, W, true, true, false>(a, stream, ev);
+  if (a.kv_fp8) {
+    if (a.alibi) return launch_prefill_w<D, W, true, true, true>(a, stream, ev);
+    return a.window > 0 ? launch_prefill_w<D, W, true, true, false>(a, stream, ev)
+                        : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
+  }
   if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
   return a.window > 0 ? launch_prefill_w<D, W, true, false, false>(a, stream, ev)
                       : launch_prefill_w<D, W, false, false, false>(a, stream, ev);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
-// longest query run fills them, else 4.
-int prefill_waves(int max_q_len) { return max_q_len >= PF_W8_MIN ? 8 : 4; }
+// longest query run fills them, else 4.  FP8 pools with ALiBi always take 8: the
+// 4-wave variant stages twice the codes per lane in registers, and with the bias
+// terms on top it would not fit the 256 registers of a two-wave-per-SIMD launch.
+int prefill_waves(int max_q_len, bool fp8_alibi) {
+  return max_q_len >= PF_W8_MIN || fp8_alibi ? 8 : 4;
+}
+static int prefill_waves(const PrefillArgs& a) {
+  return prefill_waves(a.max_q_len, a.kv_fp8 && a.alibi != nullptr);
+}
 
 static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
   PrefillArgs a = a_in;
@@ -815,7 +827,7 @@ static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
 
 hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, char* desc,
                                 size_t desc_len) {
-  const int W = prefill_waves(a_in.max_q_len);
+  const int W = prefill_waves(a_in);
   const PrefillArgs a = prefill_shape(a_in, W);
   const int rows_per_wg = kMergeThreads / (a.D / 4);
   dim3 grid(a.Hq * a.B * a.n_qt * (32 * W / rows_per_wg));
@@ -832,7 +844,7 @@ hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, cha
 
 hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
                           size_t desc_len, const KernelEvents& ev) {
-  const int W = prefill_waves(a_in.max_q_len);
+  const int W = prefill_waves(a_in);
   const PrefillArgs a = prefill_shape(a_in, W);
   hipError_t e;
   if (a.D == 128)

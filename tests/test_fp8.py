@@ -327,7 +327,7 @@ def test_fp8_prefill_parity(require_gpu, hist, ql, Hq, Hkv, D, ps, causal, split
 @pytest.mark.parametrize("q_lens", [[129, 300], [1100, 64]])
 def test_unit_scale_fp8_prefill_equals_bf16_prefill_bitwise(require_gpu, q_lens):
     """Unit scales: the widened codes are the bf16 values a bf16 pool would hold, and
-    both paths run the same general kernel from there."""
+    both paths run the same kernel body from there."""
     case = make_case("p8u", seq_lens=[300 + q_lens[0], q_lens[1]], q_lens=q_lens, causal=True,
                      Hq=8, Hkv=2, D=128, page_size=16, seed=19, device="cuda")
     shape = tuple(case.k_pool.shape)
@@ -339,10 +339,8 @@ def test_unit_scale_fp8_prefill_equals_bf16_prefill_bitwise(require_gpu, q_lens)
     rest = (case.cu_seqlens_q, case.seq_lens_k, case.block_tables, case.scale)
     o8, l8 = pa.paged_attn_prefill_varlen_fp8(*args, kc, vc, *rest, 1.0, 1.0, causal=True,
                                               max_q_len=max(q_lens), return_lse=True)
-    big = 1 << 30                      # a window longer than everything: the general kernel
     o16, l16 = pa.paged_attn_prefill_varlen(*args, as_bf16(kc), as_bf16(vc), *rest, causal=True,
-                                            max_q_len=max(q_lens), return_lse=True,
-                                            window_left=big)
+                                            max_q_len=max(q_lens), return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
     assert torch.equal(l8, l16)
