@@ -55,8 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--traffic-pass", action="store_true",
-                   help="run only a 1 GiB device copy and a few partition-kernel launches, "
-                        "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE collection")
+                   help="run only a 1 GiB device copy and a few launches of the workload's "
+                        "dominant kernel (qwen7b_decode or causal_prefill), for rocprofv3 "
+                        "--pmc FETCH_SIZE / WRITE_SIZE collection")
     return p.parse_args()
 
 
@@ -350,7 +351,10 @@ def time_step(step, steps, warmup, kernel_events=True):
         step()
     torch.cuda.synchronize()
     step.events = None
-    return wall, ev, sum(a.elapsed_time(b) for a, b in pairs) / steps
+    durs = sorted(a.elapsed_time(b) for a, b in pairs)
+    step.kernel_ms_median = durs[len(durs) // 2]
+    step.kernel_ms_min = durs[0]
+    return wall, ev, sum(durs) / steps
 
 
 def rate(units, ms, unit_name):
@@ -363,41 +367,53 @@ def rate(units, ms, unit_name):
 # HBM traffic of the dominant kernel, from rocprofv3 counters
 # ---------------------------------------------------------------------------
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_qwen7b_decode_traffic.json")
-DECODE_SOURCES = ["decode.hip", "common.hpp", "kernels.hpp"]
+# per workload: the recorded counter figures of its dominant kernel and the sources
+# that kernel is built from
+TRAFFIC = {
+    "qwen7b_decode": ("decode_partition_qwen7b_decode_traffic.json",
+                      ["decode.hip", "common.hpp", "kernels.hpp"]),
+    "causal_prefill": ("prefill_causal_prefill_traffic.json",
+                       ["prefill.hip", "common.hpp", "kernels.hpp"]),
+}
 COPY_BYTES = 1 << 30           # the calibration copy reads and writes this many bytes
 
 
-def decode_source_digest():
-    """sha256 over the sources the partition kernel is built from."""
+def source_digest(workload):
+    """sha256 over the sources the workload's dominant kernel is built from."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "paged_kv_flashattention_amd", "csrc")
-    for f in DECODE_SOURCES:
+    for f in TRAFFIC[workload][1]:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """Bytes per partition-kernel launch (FETCH_SIZE + WRITE_SIZE, each scaled by
-    the same counter's reading for a copy of known size), as recorded from the
-    counter runs -- or None when the kernel's sources changed since."""
+def recorded_traffic(workload):
+    """Bytes per launch of the workload's dominant kernel (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter's reading for a copy of known size), as recorded
+    from the counter runs -- or None when there is no record or the kernel's sources
+    changed since."""
+    if workload not in TRAFFIC:
+        return None
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", TRAFFIC[workload][0])) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != decode_source_digest():
+    if rec.get("source_sha256") != source_digest(workload):
         return None
     return rec.get("bytes_per_launch")
 
 
-def traffic_pass(steps):
+def traffic_pass(steps, workload):
     """What the counter runs profile: a plain device copy of COPY_BYTES (the
-    calibration), then `steps` launches of the decode partition kernel over the
-    rotated pool copies, as the timed steps launch them."""
+    calibration), then `steps` launches of the workload's dominant kernel as the
+    timed steps launch them (decode: the partition kernel over the rotated pool
+    copies; prefill: whole steps, whose only kernel is the prefill kernel)."""
     import torch
+    if workload not in TRAFFIC:
+        raise SystemExit(f"--traffic-pass covers {sorted(TRAFFIC)}, not {workload}")
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -405,10 +421,15 @@ def traffic_pass(steps):
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    step = make_step("qwen7b_decode", 0)
-    step.partition_launches(steps)
-    log(f"[bench] traffic pass: copy of {COPY_BYTES} bytes, {steps} partition launches; "
-        f"sources {decode_source_digest()[:16]}")
+    step = make_step(workload, 0)
+    if workload == "qwen7b_decode":
+        step.partition_launches(steps)
+    else:
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    log(f"[bench] traffic pass: copy of {COPY_BYTES} bytes, {steps} {workload} launches; "
+        f"sources {source_digest(workload)[:16]}")
 
 
 # ---------------------------------------------------------------------------
@@ -517,7 +538,7 @@ def main():
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
 
     if args.traffic_pass:
-        traffic_pass(args.steps)
+        traffic_pass(args.steps, args.workload)
         return
 
     step = make_step(args.workload, args.num_splits)
@@ -549,10 +570,12 @@ def main():
         "config": step.config(),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": step.unit_name, "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic() if args.workload == "qwen7b_decode" else None,
+                     "traffic": recorded_traffic(args.workload),
                      "kernel": ("decode_partition_kernel" if bound == "hbm" else "prefill_kernel")
                      if not isinstance(step, MixedStep) else "whole step",
                      "kernel_us_per_launch": round(kern_ms * 1e3, 2),
+                     "kernel_us_median": round(getattr(step, "kernel_ms_median", kern_ms) * 1e3, 2),
+                     "kernel_us_min": round(getattr(step, "kernel_ms_min", kern_ms) * 1e3, 2),
                      "kernel_timing": "start/end events stamped by that kernel's own "
                                       "dispatch (hipExtLaunchKernel) in a second pass of "
                                       "the same steps right after the timed pass",
