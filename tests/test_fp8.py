@@ -294,6 +294,10 @@ PREFILL = [
     ([500, 0], [1030, 260], 8, 2, 128, 64, True, 1, 0, False),      # D 128, 8 waves
     ([300, 0, 7], [40, 129, 1], 8, 2, 128, 16, False, 1, 0, False),
     ([1000, 0], [100, 257], 28, 4, 128, 16, True, 1, 200, True),    # window and ALiBi
+    ([1000, 0], [100, 257], 28, 4, 128, 16, True, 1, 200, False),   # window only, 4 waves
+    ([0, 300], [1100, 70], 8, 2, 128, 16, True, 1, 333, False),     # window only, 8 waves
+    ([600, 0], [90, 140], 8, 2, 64, 16, True, 1, 0, True),          # ALiBi only, D 64
+    ([2100, 37], [1030, 5], 8, 2, 128, 32, True, 2, 0, True),       # ALiBi, 8 waves, 2 parts
     ([4113, 214], [512, 40], 8, 2, 128, 16, True, 4, 0, False),     # key parts
 ]
 
