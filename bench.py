@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--workload", default="qwen7b_decode",
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
                             "long_decode", "causal_prefill", "causal_prefill_fp8",
-                            "mixed_ragged", "tiny_decode"])
+                            "mixed_ragged", "tiny_decode", "qwen7b_decode_warm"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
@@ -324,6 +324,10 @@ def make_step(name, num_splits=0):
         return Fp8DecodeStep("qwen7b_decode", copies=3, num_splits=num_splits)
     if name == "qwen7b_decode":
         return DecodeStep(name, copies=3, num_splits=num_splits)
+    if name == "qwen7b_decode_warm":
+        # one pool copy: the same 537 MB every step, so whatever of it the 256 MiB
+        # last-level cache keeps between steps is read from there (the warm figure)
+        return DecodeStep("qwen7b_decode", copies=1, num_splits=num_splits)
     if name == "long_decode":
         # the workload is stated with 64 partitions; --num-splits overrides
         return DecodeStep(name, copies=1, num_splits=num_splits or 64)
@@ -628,6 +632,8 @@ def main():
         # decode and the mixed step also replayed from a HIP graph (*_graph)
         extra = {}
         for label, name, splits in (("qwen7b_decode_graph", "qwen7b_decode", 0),
+                                    ("qwen7b_decode_warm", "qwen7b_decode_warm", 0),
+                                    ("tiny_decode", "tiny_decode", 0),
                                     ("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
                                     ("causal_prefill", "causal_prefill", 0),
                                     ("causal_prefill_fp8", "causal_prefill_fp8", 0),

@@ -252,7 +252,8 @@ int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out
  *   max_q_len  : host-side upper bound of the per-sequence q_len (sizes the grid;
  *                rows past it are not computed)
  * One launch covers Hq * B * ceil(max_q_len / R) work-groups of 2 R threads
- * (R = 128 query rows, or 256 when max_q_len >= 1024); when
+ * (R = 128 query rows, or 256 when max_q_len >= 512 or the pools are FP8 with ALiBi
+ * slopes); when
  * Hq * B * (ceil(max_q_len / 128) + 1) * 256 exceeds 2^32 - 1 the call is refused
  * with PA_ERR_SHAPE.
  */

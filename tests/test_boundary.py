@@ -302,10 +302,10 @@ def test_failed_call_leaves_output_untouched(require_gpu):
 
 def _tiles_model(q_lens, k_lens, causal, window):
     """Per-query-tile 64-key counts, restated from the kernel's documented bounds:
-    a tile of R rows (R = 256 when the longest query run reaches 1,024, else 128)
+    a tile of R rows (R = 256 when the longest query run reaches 512, else 128)
     whose last row sits at position p_last needs keys 0 .. p_last (all keys without
     causal), and with a window w its first row's window starts at p_first - w + 1."""
-    R = 256 if max(q_lens) >= 1024 else 128
+    R = 256 if max(q_lens) >= 512 else 128
     out = []
     for q, L in zip(q_lens, k_lens):
         for r0 in range(0, q, R):
@@ -368,12 +368,12 @@ def test_prefill_plan_splits_host_logic():
     from paged_kv_flashattention_amd import PagedAttnError
     # a full grid of equal causal rows needs no parts
     assert pa.prefill_plan_splits([4096] * 4, [4096] * 4, 32) == 1
-    # 5 chunks of 512 over histories 214 .. 4,113: the heaviest tile (73 key tiles)
-    # is 2.1 times the mean load per slot; 3 parts leave the heavy chunk's pieces
-    # badly packed, 4 do not
-    assert pa.prefill_plan_splits([512] * 5, [1732, 726, 4625, 1703, 850], 32) == 4
-    # one chunk over a long history: 128 work-groups of ~520 tiles on 512 slots --
-    # 4 parts fill the slots once; 5 would need a second round for 128 of them
+    # 5 chunks of 512 over histories 214 .. 4,113 (256-row tiles, two per chunk): the
+    # heaviest tile (73 key tiles) is 2.0 times the mean load per slot; 2 parts bring
+    # the modelled makespan from 75 to 44 tiles, more parts do not lower it (3: 53)
+    assert pa.prefill_plan_splits([512] * 5, [1732, 726, 4625, 1703, 850], 32) == 2
+    # one chunk over a long history: 64 work-groups of ~520 tiles on 256 slots --
+    # 4 parts fill the slots once; 5 would need a second round for 64 of them
     assert pa.prefill_plan_splits([512], [33280], 32) == 4
     assert pa.prefill_plan_splits([512], [33280], 1) == 8           # capped at 8
     assert pa.prefill_plan_splits([512], [600], 1) == 1             # too short to cut

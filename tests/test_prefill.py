@@ -37,7 +37,7 @@ CASES = [
     ([17, 0], [50, 130], 8, 8, 64, 32, True),              # MHA, D 64, page 32
     ([300, 0, 7], [40, 129, 1], 8, 2, 128, 16, False),     # non-causal
     ([0, 0], [1, 2], 4, 2, 64, 16, False),
-    # max_q_len >= 1024: 256-row work-groups (8 waves), ragged last tiles
+    # max_q_len >= 512: 256-row work-groups (8 waves), ragged last tiles
     ([0, 0], [1100, 300], 4, 2, 64, 16, True),
     ([500, 0], [1030, 260], 8, 2, 128, 32, True),
     ([0], [1024], 4, 4, 128, 64, False),
@@ -228,7 +228,7 @@ def test_mixed_ragged_step_full_size(require_gpu, splitk):
 
 
 @pytest.mark.parametrize("hist,ql", [
-    # 256-row tiles (a run of >= 1024): rows ending at every offset within a wave's 32
+    # 256-row tiles (a run of >= 512): rows ending at every offset within a wave's 32
     # and a block's 32 keys, waves with no valid row, with and without history
     ([0, 0, 0, 0], [1024, 31, 33, 257]),
     ([0, 5, 64], [1025, 63, 65]),
