@@ -650,7 +650,7 @@ def main():
             s = make_step(name, splits)
             if label.endswith("_graph"):
                 s = GraphStep(s, len(s.kv) if hasattr(s, "kv") else 1)
-            w2, e2, k2 = time_step(s, max(5, args.steps // 3), 2)
+            w2, e2, k2 = time_step(s, args.steps, args.warmup)
             v2 = rate(s.units, e2, s.unit_name)
             pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
             per = getattr(s, "calls", 1)
