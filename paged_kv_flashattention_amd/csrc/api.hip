@@ -248,6 +248,9 @@ constexpr int kPrefillPartMinTiles = 16;       // 64-key tiles per key-range par
 // 8-wave or two 4-wave work-groups per CU) -- measured on MI355X, splitting a
 // launch that already fills the chip gains less than the partial-result traffic
 // and the merge cost -- else enough parts for one work-group per slot, at most 8.
+// (The slot count takes the work-group size from max_q_len alone, as the workspace
+// query does, so both give the same S; FP8 pools with ALiBi launch 8-wave work-groups
+// whatever the length, for which the count is then only an estimate.)
 int32_t resolve_prefill_splits(int32_t B, int32_t Hq, int32_t max_q_len, int32_t num_splits) {
   if (num_splits > 0) return num_splits < kPrefillMaxSplits ? num_splits : kPrefillMaxSplits;
   if (B <= 0 || Hq <= 0 || max_q_len <= 0) return 1;

@@ -21,6 +21,8 @@
 #include <limits.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -778,12 +780,27 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
 template <int D, int W, bool GEN, bool F8, bool REV>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
-  // more than 64 KiB of dynamic LDS must be requested once per process
-  static const hipError_t attr = PfLds<D>::BYTES > 65536
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES)
-      : hipSuccess;
-  if (attr != hipSuccess) return attr;
+  // more than 64 KiB of dynamic LDS is requested for the kernel once per device (the
+  // first launch on each device sets it; concurrent first launches both set it, which
+  // is harmless).  state: 0 not yet, 1 set, 2 + error code otherwise.
+  if constexpr (PfLds<D>::BYTES > 65536) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> state[kMaxDevices];
+    int dev = 0;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return de;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    const int st = state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+      const hipError_t e =
+          hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES);
+      state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
+      if (e != hipSuccess) return e;
+    } else if (st != 1) {
+      return (hipError_t)(st - 2);
+    }
+  }
   dim3 grid(a.Hq * a.B * a.n_qt * a.S);
   launch_kernel(prefill_kernel<D, W, GEN, F8, REV>, grid, dim3(64 * W), (uint32_t)PfLds<D>::BYTES,
                 stream, ev, a);
