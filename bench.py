@@ -559,6 +559,25 @@ def cpu_baseline(step, min_s=10.0, budget_s=15.0):
 
 # ---------------------------------------------------------------------------
 
+def secondary_figure(label, name, splits, args):
+    """One secondary line: the workload `name` timed like the headline (a HIP graph
+    replay when the label ends in _graph)."""
+    s = make_step(name, splits)
+    if label.endswith("_graph"):
+        s = GraphStep(s, len(s.kv) if hasattr(s, "kv") else 1)
+    w2, e2, k2 = time_step(s, args.steps, args.warmup)
+    v2 = rate(s.units, e2, s.unit_name)
+    pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
+    per = getattr(s, "calls", 1)
+    fig = {"value": round(v2, 2), "unit": s.unit_name, "frac": round(v2 / pk, 4),
+           "us_per_step": round(e2 * 1e3 / per, 2), "config": s.config()}
+    if k2:
+        fig["main_kernel_us"] = round(k2 * 1e3, 2)
+        fig["main_kernel_frac"] = round(rate(s.units, k2, s.unit_name) / pk, 4)
+    log(f"[bench] {label}: {e2 * 1e3 / per:.1f} us/step, {v2:.2f} {s.unit_name}")
+    return fig
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -642,33 +661,29 @@ def main():
                                     ("long_history_chunk", "long_history_chunk", 0),
                                     ("mixed_ragged", "mixed_ragged", 0),
                                     ("mixed_ragged_graph", "mixed_ragged", 0)):
-            if splits < 0:
-                from workloads import make_config
-                c = make_config(name, "cuda")
-                splits = pa.decode_num_splits(c.B, c.Hkv, c.max_seq_len)
-                del c
-            s = make_step(name, splits)
-            if label.endswith("_graph"):
-                s = GraphStep(s, len(s.kv) if hasattr(s, "kv") else 1)
-            w2, e2, k2 = time_step(s, args.steps, args.warmup)
-            v2 = rate(s.units, e2, s.unit_name)
-            pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
-            per = getattr(s, "calls", 1)
-            extra[label] = {"value": round(v2, 2), "unit": s.unit_name,
-                            "frac": round(v2 / pk, 4), "us_per_step": round(e2 * 1e3 / per, 2),
-                            "config": s.config()}
-            if k2:
-                extra[label]["main_kernel_us"] = round(k2 * 1e3, 2)
-                extra[label]["main_kernel_frac"] = round(rate(s.units, k2, s.unit_name) / pk, 4)
-            log(f"[bench] {label}: {e2 * 1e3 / per:.1f} us/step, {v2:.2f} {s.unit_name}")
-            del s
+            # a secondary workload that fails is reported as such; the headline stands
+            try:
+                if splits < 0:
+                    from workloads import make_config
+                    c = make_config(name, "cuda")
+                    splits = pa.decode_num_splits(c.B, c.Hkv, c.max_seq_len)
+                    del c
+                extra[label] = secondary_figure(label, name, splits, args)
+            except Exception as exc:                      # noqa: BLE001
+                extra[label] = {"error": f"{type(exc).__name__}: {exc}"}
+                log(f"[bench] {label}: failed ({type(exc).__name__}: {exc})")
             torch.cuda.empty_cache()
         result["secondary"] = extra
 
     if not args.no_cpu_baseline:
-        s = make_step(args.workload, args.num_splits)
-        cb = cpu_baseline(s)
-        del s
+        try:
+            s = make_step(args.workload, args.num_splits)
+            cb = cpu_baseline(s)
+            del s
+        except Exception as exc:                          # noqa: BLE001
+            cb = None
+            result["cpu_baseline"] = {"error": f"{type(exc).__name__}: {exc}"}
+            log(f"[bench] cpu baseline failed ({type(exc).__name__}: {exc})")
         if cb is not None:
             result["cpu_baseline"] = cb
             log(f"[bench] cpu baseline: {cb['value']:.3f} {cb['unit']} ({cb['sample']})")
