@@ -41,6 +41,12 @@ CASES = [
     ([0, 0], [1100, 300], 4, 2, 64, 16, True),
     ([500, 0], [1030, 260], 8, 2, 128, 32, True),
     ([0], [1024], 4, 4, 128, 64, False),
+    # the 256-row threshold itself: 511 rows (4 waves) and 512 rows (8 waves)
+    ([40, 0], [511, 77], 8, 2, 128, 16, True),
+    ([0, 40], [512, 77], 8, 2, 128, 16, True),
+    # 8 waves with GQA 16 and D 64 (page 32), and without the causal mask
+    ([0, 300], [700, 40], 16, 1, 64, 32, True),
+    ([250, 0], [600, 513], 8, 4, 128, 16, False),
 ]
 
 
