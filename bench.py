@@ -476,7 +476,8 @@ STREAM_BYTES = 4 << 30
 
 def stream_read_gbs(iters=10):
     """Best GB/s of a plain streaming read of a 4 GiB buffer (libpa_stream.so, built
-    with the library), over a few grid sizes; HIP events on the launch stream."""
+    with the library: each work-group streams one contiguous chunk), over a few grid
+    sizes; HIP events on the launch stream."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "paged_kv_flashattention_amd", "libpa_stream.so")
@@ -487,7 +488,7 @@ def stream_read_gbs(iters=10):
                    ctypes.c_void_p]
     buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     best = (0.0, 0)
-    for blocks in (16384, 65536, 131072, 262144):
+    for blocks in (1024, 4096, 16384, 65536, 262144):
         sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
         s = torch.cuda.current_stream().cuda_stream
         for _ in range(2):
