@@ -217,22 +217,26 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int hh = lane >> 5;          // k-half of the MFMA operands
   const int g16 = lane & 15;
   // Work-group -> (query head h, sequence b, query tile qt, key part).  Work-groups
-  // are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2; with
-  // xcd_groups set, every (sequence, KV head) group lives on one XCD, so its K/V
-  // tiles are fetched into one L2 and shared there by the group's query heads and
-  // tiles.  Either way the heaviest query tiles (most keys) start first, all their
-  // key parts together, and every XCD keeps its share of the unsplit work.
+  // are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  With
+  // xcd_groups set, every (sequence, KV head) group lives on one XCD and each XCD
+  // runs its groups one after the other (group-major): all query heads, tiles and
+  // key parts of a group, heaviest tile first, then the next group, so a group's
+  // K/V stays in that XCD's L2 while its tiles are computed, and the next group's
+  // heavy tiles start while the previous group's light ones finish.  Without it the
+  // order is head-major, heaviest tiles first.  Either way all key parts of a tile
+  // start together and every XCD keeps its share of the unsplit work.
   int h, b, qt, part;
   {
     const int p = blockIdx.x;
     if (a.xcd_groups) {
-      const int k = p >> 3;
-      const int level = a.xcd_groups * a.G;      // work-groups per (tile level, part)
-      const int r2 = k / level;
-      const int rem = k - r2 * level;
+      const int k = p >> 3;                      // this work-group's place on its XCD
+      const int per_group = a.G * a.n_qt * a.S;  // work-groups of one group
+      const int gi = k / per_group;              // the XCD's gi-th group
+      const int rem = k - gi * per_group;
+      const int r2 = rem / a.G;                  // (tile rank, part), heaviest first
       const int rank = r2 / a.S;
       part = r2 - rank * a.S;
-      const int g = (p & 7) + 8 * (rem / a.G);
+      const int g = (p & 7) + 8 * gi;
       b = g / a.Hkv;
       h = (g - b * a.Hkv) * a.G + rem % a.G;
       qt = a.n_qt - 1 - rank;
@@ -874,7 +878,7 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
            "q-tiles x %d key parts, %s) block=%d lds=%zu",
            a.D, 32 * W, kPfBN, a.kv_fp8 ? "fp8-e4m3-widened" : "lds-dma",
            a.Hq * a.B * a.n_qt * a.S, a.Hq, a.B, a.n_qt, a.S,
-           a.xcd_groups ? "KV groups per XCD" : "head-major", 64 * W,
+           a.xcd_groups ? "KV groups per XCD, group-major" : "head-major", 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;
 }
