@@ -719,18 +719,22 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 
 // Merge of the query tiles that were cut into key-range parts ("The Stack Below
 // the Stack (Part 2)", section 2.2, step 3: with m the largest part lse, weights
-// exp(lse_c - m), lse = m + ln sum).  A work-group covers 256 / (D / 4) rows of one
-// (query head, sequence, query tile); each thread merges 4 output columns of one
-// row, with all of its loads issued before any is used, so the merge costs about
-// two memory round trips.  Work-groups of tiles with one part (written by the
-// prefill kernel) return at once.
+// exp(lse_c - m), lse = m + ln sum).  A work-group covers kMergePasses * 256 / (D / 4)
+// rows of one (query head, sequence, query tile); each thread merges 4 output columns
+// of one row per pass, with all of that row's loads issued before any is used, so a
+// pass costs about two memory round trips.  Work-groups of tiles with one part
+// (written by the prefill kernel) return at once.
 constexpr int kMergeThreads = 256;
+constexpr int kMergePasses = 4;     // rows per thread: most work-groups of a launch only
+                                    // find their tile unsplit and return, so fewer,
+                                    // larger work-groups finish the launch sooner
 constexpr int kMaxParts = 16;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs a, int bm) {
   constexpr int CH = D / 4;                  // 4-column chunks per row
-  constexpr int RPB = kMergeThreads / CH;    // rows per work-group
+  constexpr int RPP = kMergeThreads / CH;    // rows per pass
+  constexpr int RPB = RPP * kMergePasses;    // rows per work-group
   const int rblocks = bm / RPB;
   const int p = blockIdx.x / rblocks;
   const int rb = blockIdx.x - p * rblocks;
@@ -748,37 +752,39 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   const PfTiles tw = a.window > 0 ? pf_tiles<true>(a, L, q_len, r_wg, bm)
                                    : pf_tiles<false>(a, L, q_len, r_wg, bm);
   if (tw.parts <= 1) return;
-  const int row = r_wg + rb * RPB + threadIdx.x / CH;
   const int c = threadIdx.x % CH;
-  if (row >= q_len || t0 + row >= a.Tq) return;
-  const size_t orow = (size_t)(t0 + row) * a.Hq + h;
-  const size_t prow = orow * a.S;
-  float lse[kMaxParts];
+  for (int pass = 0; pass < kMergePasses; ++pass) {
+    const int row = r_wg + rb * RPB + pass * RPP + threadIdx.x / CH;
+    if (row >= q_len || t0 + row >= a.Tq) return;
+    const size_t orow = (size_t)(t0 + row) * a.Hq + h;
+    const size_t prow = orow * a.S;
+    float lse[kMaxParts];
 #pragma unroll
-  for (int k = 0; k < kMaxParts; ++k) lse[k] = k < tw.parts ? a.part_lse[prow + k] : kNegInf;
-  f32x4 o[kMaxParts];
-#pragma unroll
-  for (int k = 0; k < kMaxParts; ++k)
-    if (k < tw.parts) o[k] = *reinterpret_cast<const f32x4*>(a.part_o + (prow + k) * D + 4 * c);
-  float m = kNegInf;
-#pragma unroll
-  for (int k = 0; k < kMaxParts; ++k) m = fmaxf(m, lse[k]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (m != kNegInf) {
+    for (int k = 0; k < kMaxParts; ++k) lse[k] = k < tw.parts ? a.part_lse[prow + k] : kNegInf;
+    f32x4 o[kMaxParts];
 #pragma unroll
     for (int k = 0; k < kMaxParts; ++k)
-      if (k < tw.parts) {
-        const float w = __expf(lse[k] - m);
-        tot += w;
-        acc += w * o[k];
-      }
+      if (k < tw.parts) o[k] = *reinterpret_cast<const f32x4*>(a.part_o + (prow + k) * D + 4 * c);
+    float m = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) m = fmaxf(m, lse[k]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
+    if (m != kNegInf) {
+#pragma unroll
+      for (int k = 0; k < kMaxParts; ++k)
+        if (k < tw.parts) {
+          const float w = __expf(lse[k] - m);
+          tot += w;
+          acc += w * o[k];
+        }
+    }
+    const bool live = tot > 0.f;
+    const float inv = live ? 1.f / tot : 0.f;
+    *reinterpret_cast<u32x2*>(a.out + orow * D + 4 * c) =
+        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
   }
-  const bool live = tot > 0.f;
-  const float inv = live ? 1.f / tot : 0.f;
-  *reinterpret_cast<u32x2*>(a.out + orow * D + 4 * c) =
-      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  if (c == 0 && a.lse_out) a.lse_out[orow] = live ? m + __logf(tot) : kNegInf;
 }
 
 template <int D, int W, bool GEN, bool F8, bool REV>
@@ -851,7 +857,7 @@ hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, cha
                                 size_t desc_len) {
   const int W = prefill_waves(a_in);
   const PrefillArgs a = prefill_shape(a_in, W);
-  const int rows_per_wg = kMergeThreads / (a.D / 4);
+  const int rows_per_wg = kMergeThreads / (a.D / 4) * kMergePasses;
   dim3 grid(a.Hq * a.B * a.n_qt * (32 * W / rows_per_wg));
   if (a.D == 128)
     hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a,
