@@ -64,7 +64,9 @@ struct PrefillArgs {
   int causal;
   float scale_log2;
   int n_qt;                      // query tiles per sequence (of the longest)
-  int xcd_groups;                // (sequence, KV head) groups per XCD, or 0: plain order
+  int xcd_groups;                // XCD units per XCD, or 0: plain order
+  int xcd_split;                 // a (sequence, KV head) group's tile ranks are dealt over
+                                 // this many XCD units (1, 2, 4 or 8)
   int window;                    // sliding window: position p sees keys j > p - window (0: none)
   const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
   int kv_fp8;                    // pools hold FP8 E4M3 codes (uint8) instead of bf16

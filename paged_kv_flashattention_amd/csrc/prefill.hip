@@ -218,28 +218,38 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int g16 = lane & 15;
   // Work-group -> (query head h, sequence b, query tile qt, key part).  Work-groups
   // are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  With
-  // xcd_groups set, every (sequence, KV head) group lives on one XCD and each XCD
-  // runs its groups one after the other (group-major): all query heads, tiles and
-  // key parts of a group, heaviest tile first, then the next group, so a group's
-  // K/V stays in that XCD's L2 while its tiles are computed, and the next group's
-  // heavy tiles start while the previous group's light ones finish.  Without it the
-  // order is head-major, heaviest tiles first.  Either way all key parts of a tile
-  // start together and every XCD keeps its share of the unsplit work.
+  // xcd_groups set, the work is cut into units -- a (sequence, KV head) group or,
+  // when the group count is not a multiple of 8, one of xcd_split classes of its
+  // query-tile ranks, so that the units divide evenly among the XCDs (ranks are
+  // dealt to the classes zig-zag, so every class carries as much causal work) --
+  // and each XCD runs its units one after the other (unit-major): all query
+  // heads, tiles and key parts of a unit, heaviest tile first, then the next unit,
+  // so the group's K/V stays in that XCD's L2 while the unit's tiles use it, and the
+  // next unit's heavy tiles start while the previous one's light ones finish.
+  // Without it the order is head-major, heaviest tiles first.  Either way all key
+  // parts of a tile start together and every XCD keeps its share of the unsplit work.
   int h, b, qt, part;
   {
     const int p = blockIdx.x;
     if (a.xcd_groups) {
+      const int m = a.xcd_split;
+      const int tpu = (a.n_qt + m - 1) / m;      // tile ranks per unit
       const int k = p >> 3;                      // this work-group's place on its XCD
-      const int per_group = a.G * a.n_qt * a.S;  // work-groups of one group
-      const int gi = k / per_group;              // the XCD's gi-th group
-      const int rem = k - gi * per_group;
-      const int r2 = rem / a.G;                  // (tile rank, part), heaviest first
-      const int rank = r2 / a.S;
-      part = r2 - rank * a.S;
-      const int g = (p & 7) + 8 * gi;
+      const int per_unit = a.G * tpu * a.S;      // work-groups of one unit
+      const int ui = k / per_unit;               // the XCD's ui-th unit
+      const int rem = k - ui * per_unit;
+      const int r2 = rem / a.G;                  // (tile rank in unit, part), heaviest first
+      const int rl = r2 / a.S;
+      part = r2 - rl * a.S;
+      const int u = (p & 7) + 8 * ui;            // unit = group g, rank class j
+      const int g = u / m;
+      const int j = u - g * m;
+      // ranks dealt to the classes zig-zag (0 .. m-1, then m-1 .. 0, ...), so every
+      // class holds as much heavy as light causal work
+      const int rank = rl * m + ((rl & 1) ? m - 1 - j : j);
       b = g / a.Hkv;
       h = (g - b * a.Hkv) * a.G + rem % a.G;
-      qt = a.n_qt - 1 - rank;
+      qt = a.n_qt - 1 - rank;                    // below 0: past the unit's last tile
     } else {
       h = p % a.Hq;
       const int r = p / a.Hq;
@@ -251,6 +261,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     }
   }
 
+  if (qt < 0) return;
   const int t0 = a.cu_seqlens_q[b];
   const int q_len = a.cu_seqlens_q[b + 1] - t0;
   const int r_wg = qt * kPfBM;
@@ -787,6 +798,12 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   }
 }
 
+// query-tile slots per (head, sequence) in the grid: n_qt, rounded up to a multiple of
+// xcd_split in the unit-major order (the surplus work-groups return at once)
+static int prefill_grid_tiles(const PrefillArgs& a) {
+  return a.xcd_groups ? (a.n_qt + a.xcd_split - 1) / a.xcd_split * a.xcd_split : a.n_qt;
+}
+
 template <int D, int W, bool GEN, bool F8, bool REV>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
@@ -811,7 +828,7 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
       return (hipError_t)(st - 2);
     }
   }
-  dim3 grid(a.Hq * a.B * a.n_qt * a.S);
+  dim3 grid(a.Hq * a.B * prefill_grid_tiles(a) * a.S);
   launch_kernel(prefill_kernel<D, W, GEN, F8, REV>, grid, dim3(64 * W), (uint32_t)PfLds<D>::BYTES,
                 stream, ev, a);
   return hipGetLastError();
@@ -847,8 +864,18 @@ static int prefill_waves(const PrefillArgs& a) {
 static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
   PrefillArgs a = a_in;
   a.n_qt = (a.max_q_len + 32 * W - 1) / (32 * W);
+  // XCD units: groups, or m rank classes of each group with groups * m a multiple of
+  // 8.  Only for m <= 2 and when every unit gets a tile rank (n_qt >= m), else the
+  // plain order: with 4 or 8 classes most XCDs fetch most of a group's K/V anyway,
+  // while the unit order gives up the global heaviest-first packing (measured on
+  // MI355X: 5 x 2048 causal rows, Hq 16 / Hkv 2, 127 us in 4 classes against 112.5 us
+  // head-major; 1 x 8192 and 3 x 4096 at Hkv 4 in 2 classes 2-2.5 % faster than
+  // head-major).
   const int groups = a.B * a.Hkv;
-  a.xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
+  int m = 1;
+  while ((groups * m) % 8) m *= 2;
+  a.xcd_split = m;
+  a.xcd_groups = a.n_qt >= m && m <= 2 ? groups * m / 8 : 0;
   if (a.S < 1) a.S = 1;
   return a;
 }
@@ -879,12 +906,19 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
     e = W == 8 ? launch_prefill_t<128, 8>(a, stream, ev) : launch_prefill_t<128, 4>(a, stream, ev);
   else
     e = W == 8 ? launch_prefill_t<64, 8>(a, stream, ev) : launch_prefill_t<64, 4>(a, stream, ev);
+  char order[64];
+  if (!a.xcd_groups)
+    snprintf(order, sizeof(order), "head-major");
+  else if (a.xcd_split == 1)
+    snprintf(order, sizeof(order), "KV groups per XCD, group-major");
+  else
+    snprintf(order, sizeof(order), "KV groups in %d rank classes per XCD, unit-major",
+             a.xcd_split);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s) block=%d lds=%zu",
            a.D, 32 * W, kPfBN, a.kv_fp8 ? "fp8-e4m3-widened" : "lds-dma",
-           a.Hq * a.B * a.n_qt * a.S, a.Hq, a.B, a.n_qt, a.S,
-           a.xcd_groups ? "KV groups per XCD, group-major" : "head-major", 64 * W,
+           a.Hq * a.B * prefill_grid_tiles(a) * a.S, a.Hq, a.B, a.n_qt, a.S, order, 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;
 }
