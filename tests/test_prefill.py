@@ -256,3 +256,27 @@ def test_causal_prefill_rows_ending_mid_tile(require_gpu, hist, ql):
     o_ref, l_ref = oracle_full(case, kp, vp)
     assert_parity(as_f64(out), o_ref, "prefill causal tail")
     assert_lse(as_f64(lse), l_ref, "prefill causal tail lse")
+
+
+@pytest.mark.parametrize("hist,ql,Hq,Hkv,classes", [
+    ([0, 100], [1100, 300], 8, 2, 2),     # 4 groups: 2 rank classes, 5 tiles (one surplus)
+    ([0, 0, 7], [800, 5, 300], 12, 2, 4), # 6 groups: 4 classes would be needed -> head-major
+])
+def test_prefill_xcd_rank_classes(require_gpu, hist, ql, Hq, Hkv, classes):
+    """A group count that is not a multiple of 8: an even one deals each group's
+    query-tile ranks into 2 classes on 2 XCDs (every tile computed exactly once, the
+    surplus work-groups of an odd tile count return at once); otherwise head-major."""
+    print(f"[prefill xcd classes] hist={hist} q={ql} Hq={Hq} Hkv={Hkv}", flush=True)
+    case = make_case("pxc", hist_lens=hist, q_lens=ql, write_new=True, causal=True, Hq=Hq,
+                     Hkv=Hkv, D=128, page_size=16, seed=61, device="cuda")
+    kp, vp = pools_after_write(case)
+    write(case)
+    out, lse = run_prefill(case)
+    desc = pa.describe_launch()
+    if classes == 2:
+        assert "2 rank classes" in desc, desc
+    else:
+        assert "head-major" in desc, desc
+    o_ref, l_ref = oracle_full(case, kp, vp)
+    assert_parity(as_f64(out), o_ref, "prefill xcd classes")
+    assert_lse(as_f64(lse), l_ref, "prefill xcd classes lse")
