@@ -153,9 +153,11 @@ class PrefillStep:
     """kv_page_write is done once at setup; each step is one prefill_varlen call (with
     `splitk`, one prefill_varlen_splitk call with the key-part count that
     paged_attn_prefill_plan_splits gives for the lengths: the prefill kernel, then the
-    merge of the split tiles)."""
+    merge of the split tiles).  Steps rotate over `copies` copies of Q, the pools and
+    the output, so that a step does not find its inputs in the 256 MiB last-level
+    cache (two copies of the causal prefill's Q, K, V and O are 664 MB)."""
 
-    def __init__(self, name, splitk=False):
+    def __init__(self, name, splitk=False, copies=2):
         import torch
         import paged_kv_flashattention_amd as pa
         from workloads import make_config, units
@@ -171,24 +173,32 @@ class PrefillStep:
         need = pa.prefill_workspace_bytes(c.B, c.T, c.max_q_len, c.Hq, c.D, self.S)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.splitk = splitk
+        self.sets = [(c.q, c.k_pool, c.v_pool, self.out)]
+        for _ in range(1, copies):
+            self.sets.append((c.q.clone(), c.k_pool.clone(), c.v_pool.clone(),
+                              torch.empty_like(self.out)))
+        self.i = 0
 
     def __call__(self):
         c = self.case
+        q, kp, vp, out = self.sets[self.i % len(self.sets)]
+        self.i += 1
         if self.splitk:
             self.pa.paged_attn_prefill_varlen_splitk(
-                c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
-                causal=True, max_q_len=c.max_q_len, num_splits=self.S, out=self.out,
+                q, kp, vp, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
+                causal=True, max_q_len=c.max_q_len, num_splits=self.S, out=out,
                 workspace=self.ws, kernel_events=next_events(self))
             return
-        self.pa.paged_attn_prefill_varlen(c.q, c.k_pool, c.v_pool, c.cu_seqlens_q, c.seq_lens_k,
+        self.pa.paged_attn_prefill_varlen(q, kp, vp, c.cu_seqlens_q, c.seq_lens_k,
                                           c.block_tables, c.scale, causal=True,
-                                          max_q_len=c.max_q_len, out=self.out,
+                                          max_q_len=c.max_q_len, out=out,
                                           kernel_events=next_events(self))
 
     def config(self):
         c = self.case
         cfg = {"workload": c.name, "batch": c.B, "q_len": c.max_q_len, "Hq": c.Hq,
-               "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size, "causal": True}
+               "Hkv": c.Hkv, "head_dim": c.D, "page_size": c.page_size, "causal": True,
+               "input_copies_rotated": len(self.sets)}
         if self.splitk:
             cfg.update(history=max(c.seq_lens) - c.max_q_len, key_parts=self.S)
         return cfg
@@ -200,20 +210,26 @@ class Fp8PrefillStep(PrefillStep):
 
     K_SCALE, V_SCALE = 0.02, 0.05
 
-    def __init__(self, name):
-        super().__init__(name)
+    def __init__(self, name, copies=2):
+        super().__init__(name, copies=1)
+        import torch
         from workloads import random_e4m3_codes
         c = self.case
         shape = tuple(c.k_pool.shape)
         c.k_pool = c.v_pool = None
-        self.kc = random_e4m3_codes(shape, 8100, "cuda")
-        self.vc = random_e4m3_codes(shape, 8101, "cuda")
+        self.sets = [(c.q if i == 0 else c.q.clone(),
+                      random_e4m3_codes(shape, 8100 + 2 * i, "cuda"),
+                      random_e4m3_codes(shape, 8101 + 2 * i, "cuda"),
+                      self.out if i == 0 else torch.empty_like(self.out))
+                     for i in range(copies)]
 
     def __call__(self):
         c = self.case
+        q, kc, vc, out = self.sets[self.i % len(self.sets)]
+        self.i += 1
         self.pa.paged_attn_prefill_varlen_fp8(
-            c.q, self.kc, self.vc, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
-            self.K_SCALE, self.V_SCALE, causal=True, max_q_len=c.max_q_len, out=self.out,
+            q, kc, vc, c.cu_seqlens_q, c.seq_lens_k, c.block_tables, c.scale,
+            self.K_SCALE, self.V_SCALE, causal=True, max_q_len=c.max_q_len, out=out,
             kernel_events=next_events(self))
 
     def config(self):
