@@ -318,8 +318,8 @@ int32_t paged_attn_prefill_num_splits(int32_t B, int32_t Hq, int32_t max_q_len);
  * 3 tiles, and the cheapest count (the smallest within 3 % of it) is returned.  It is
  * 1 when the heaviest tile is at most the mean or shorter than two 16-tile parts.
  * Ragged batches of chunks over unequal histories ("The Stack Below the Stack
- * (Part 2)", section 2.2; "Chapter 8: Attention Mechanisms", introduction: ragged
- * batches) are the case it serves.  Host work grows with the work-group count
+ * (Part 2)", section 2.2; "8. Kernels and Attention Backends", chapter intro: a
+ * step holds ragged requests of very different lengths) are the case it serves.  Host work grows with the work-group count
  * (about 0.6 ms for 640 work-groups); beyond 16,384 (query tile, head) work-groups
  * the starting bound is returned unpriced.
  *

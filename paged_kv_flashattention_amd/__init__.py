@@ -68,6 +68,7 @@ class _Recorder:
     def __init__(self, lib):
         self._lib = lib
         self.launches = []
+        self.keep = []          # buffers the binding allocated during the recorded call
 
     def __getattr__(self, name):
         fn = getattr(self._lib, name)
@@ -84,8 +85,11 @@ def prepared(call):
     """Run ``call`` -- a function that makes calls of this module -- once, and return a
     function that repeats exactly its C calls with the same marshalled arguments
     (pointers, sizes, the stream current at preparation) without the Python-side
-    checks, for launch loops whose host cost matters.  The tensors ``call`` used must
-    stay alive, and keep their storage, while the returned function is used."""
+    checks, for launch loops whose host cost matters.  The tensors ``call`` passed in
+    must stay alive, and keep their storage, while the returned function is used;
+    buffers the binding allocated itself during ``call`` (outputs, workspaces) are
+    held by the returned function, so their memory is never handed out again while
+    it may still run."""
     global _RECORDER
     rec = _Recorder(_lib.load())
     _RECORDER = rec
@@ -94,8 +98,10 @@ def prepared(call):
     finally:
         _RECORDER = None
     launches = list(rec.launches)
+    keep = list(rec.keep)
 
     def run():
+        _ = keep
         for fn, args in launches:
             status = fn(*args)
             if status != 0:
@@ -126,6 +132,25 @@ def _stream(stream) -> int:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _internal(t: torch.Tensor, stream) -> torch.Tensor:
+    """Book-keeping for a buffer the binding allocated for one call (an output or a
+    workspace the caller did not pass).  torch's caching allocator ties a block to
+    the stream current at allocation; when the launch stream is another one, the
+    block is marked in use there too, so that it is not handed to the current
+    stream's next allocation while the launch stream's kernels still read or write
+    it.  While prepared() records a call, the buffer is also kept alive by the
+    recording, whose replays write into it."""
+    if _RECORDER is not None:
+        _RECORDER.keep.append(t)
+    if stream is not None:
+        handle = _stream(stream)
+        if handle != torch.cuda.current_stream(t.device).cuda_stream:
+            s = stream if isinstance(stream, torch.cuda.Stream) else \
+                torch.cuda.ExternalStream(handle, device=t.device)
+            t.record_stream(s)
+    return t
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device):
@@ -386,11 +411,11 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
         if B and int(seq_lens.max().item()) > max_seq_len:
             raise ValueError("max_seq_len is below a sequence length")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        out = _internal(torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev), stream)
     else:
         _need(out, "out", torch.bfloat16, 3, dev)
     if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        lse = _internal(torch.empty((B, Hq), dtype=torch.float32, device=dev), stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2, dev)
     lib = load_library()
@@ -400,9 +425,11 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
                            *(scales if scales is not None else (1.0, 1.0)), alibi_ptr, ev0, ev1)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    elif need:
+        workspace = _internal(torch.empty(need, dtype=torch.uint8, device=dev), stream)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     head = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
@@ -440,10 +467,12 @@ def paged_attn_decode_partials(q, k_pool, v_pool, block_tables, seq_lens, softma
         max_seq_len = int(seq_lens.max().item()) if B else 0
     S = int(num_splits)
     if partial_out is None:
-        partial_out = torch.empty((B * Hq, S, D), dtype=torch.float32, device=dev)
+        partial_out = _internal(torch.empty((B * Hq, S, D), dtype=torch.float32, device=dev),
+                                stream)
     _need(partial_out, "partial_out", torch.float32, 3, dev)
     if partial_lse is None:
-        partial_lse = torch.empty((B * Hq, S), dtype=torch.float32, device=dev)
+        partial_lse = _internal(torch.empty((B * Hq, S), dtype=torch.float32, device=dev),
+                                stream)
     _need(partial_lse, "partial_lse", torch.float32, 2, dev)
     if tuple(partial_out.shape) != (B * Hq, S, D) or tuple(partial_lse.shape) != (B * Hq, S):
         raise ValueError("partials must be [B*Hq, S, D] and [B*Hq, S]")
@@ -468,10 +497,10 @@ def paged_attn_splitk_reduce(partial_out, partial_lse, out=None, lse=None, strea
     if partial_lse.shape != (R, S):
         raise ValueError("partial_lse must be [R, S]")
     if out is None:
-        out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+        out = _internal(torch.empty((R, D), dtype=torch.bfloat16, device=dev), stream)
     _need(out, "out", torch.bfloat16, 2, dev)
     if lse is None and want_lse:
-        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+        lse = _internal(torch.empty((R,), dtype=torch.float32, device=dev), stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, 1, dev)
     with torch.cuda.device(dev):
@@ -605,11 +634,11 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             raise ValueError("max_q_len is below a sequence's query count")
         _validate_tables(block_tables, seq_lens_k, P, ps)
     if out is None:
-        out = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=dev)
+        out = _internal(torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=dev), stream)
     else:
         _need(out, "out", torch.bfloat16, 3, dev)
     if return_lse and lse is None:
-        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+        lse = _internal(torch.empty((Tq, Hq), dtype=torch.float32, device=dev), stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2, dev)
     lib = load_library()
@@ -629,7 +658,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         if workspace is not None:
             _need(workspace, "workspace", torch.uint8, 1, dev)
         elif need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = _internal(torch.empty(need, dtype=torch.uint8, device=dev), stream)
         ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
         if split is None:

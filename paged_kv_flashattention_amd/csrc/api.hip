@@ -55,7 +55,7 @@ int check_pool(int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_siz
 }
 
 constexpr int kChunk = 32;   // keys per decode chunk; partitions are multiples of it
-constexpr int32_t kMaxSplits = 65535;   // arrival counts are 16-bit
+constexpr int32_t kMaxSplits = 65535;   // the split index is the grid's y dimension
 
 int32_t resolve_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t num_splits) {
   const int32_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;

@@ -71,3 +71,45 @@ def assert_lse(got, ref, what=""):
     if fin.any():
         err = np.abs(got[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))
         assert err.max() <= LSE_ABS, f"{what}: lse error {err.max():.3e}"
+
+
+def oracle_by_sequence(case, kp, vp, split_kv_heads=False, alibi=None):
+    """The oracle's O [T, Hq, D] and lse [T, Hq] for every row of a large case, one
+    sequence at a time.
+
+    kp / vp are the host pools (bits).  For sequence b the pages its table row names
+    (its first ceil(L / page_size) entries) are taken out of the pools in table
+    order, and the oracle runs on that compact pool with the table 0 .. n-1: the
+    same keys at the same logical positions, without widening the whole pool to
+    float64 once per sequence.  With split_kv_heads each KV head's slice of the
+    compact pool goes to the oracle on its own (Hkv = 1) with the G query heads
+    that read it, so that every float64 operand is contiguous at long contexts."""
+    bt = case.block_tables.cpu().numpy()
+    lens = case.seq_lens_k.cpu().numpy()
+    cu = case.cu_seqlens_q.cpu().numpy()
+    q = bits(case.q)
+    T, Hq, D = q.shape
+    ps = case.page_size
+    Hkv = kp.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    for b in range(case.B):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        if t1 == t0:
+            continue
+        L = int(lens[b])
+        n = -(-L // ps)
+        pages = bt[b, :n].astype(np.int64)
+        kb, vb = kp[pages], vp[pages]
+        table = np.arange(max(n, 1), dtype=np.int32)[None]
+        groups = [(0, Hkv)] if not split_kv_heads else [(g, g + 1) for g in range(Hkv)]
+        for g0, g1 in groups:
+            h0, h1 = g0 * G, g1 * G
+            o, ls = oracle.attention_ref(
+                q[t0:t1, h0:h1], np.ascontiguousarray(kb[:, :, g0:g1]),
+                np.ascontiguousarray(vb[:, :, g0:g1]), table, [L], [0, t1 - t0], case.scale,
+                case.causal, ps, case.window, None if alibi is None else alibi[h0:h1])
+            out[t0:t1, h0:h1] = o
+            lse[t0:t1, h0:h1] = ls
+    return out, lse

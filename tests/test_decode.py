@@ -6,8 +6,8 @@ import torch
 
 import oracle
 import paged_kv_flashattention_amd as pa
-from tests.parity import (as_f64, assert_lse, assert_parity, oracle_full, oracle_rows,
-                          pools_after_write)
+from tests.parity import (as_f64, assert_lse, assert_parity, oracle_by_sequence, oracle_full,
+                          oracle_rows, pools_after_write)
 from workloads import bits, make_case, make_config, units
 
 pytestmark = pytest.mark.gpu
@@ -147,56 +147,31 @@ def test_splitk_reduce_standalone_matches_merge(require_gpu, S, D):
     assert ("_few" in pa.describe_launch()) == (S <= 8)
 
 
-def _sample_rows(case, n_seq, n_heads, seed):
-    rng = np.random.default_rng(seed)
-    seqs = rng.choice(case.B, size=min(n_seq, case.B), replace=False)
-    rows = []
-    for b in seqs:
-        for h in rng.choice(case.Hq, size=n_heads, replace=False):
-            rows.append((int(b), int(h)))
-    return rows
-
-
-def test_qwen7b_decode_full_size_sampled(require_gpu):
+def test_qwen7b_decode_full_size(require_gpu):
     """Qwen2.5-7B-shaped decode at its full size (32 x 8192, Hq 28, Hkv 4), in the
-    launch configuration the benchmark times; oracle on sampled (sequence, head) rows."""
+    launch configuration the benchmark times (the library's split count); every one
+    of the 896 (sequence, head) rows against the oracle."""
     case = make_config("qwen7b_decode", "cuda")
-    print("[decode] qwen7b full size", flush=True)
+    print("[decode] qwen7b full size, every row", flush=True)
     out, lse = run_decode(case, 0)
-    rows = _sample_rows(case, 6, 4, 1)
-    kp_rows = None
-    o_ref, l_ref = oracle_rows(case, rows)
-    got = np.stack([as_f64(out[b, h]) for b, h in rows])
-    assert_parity(got, o_ref, "qwen7b sampled")
-    assert_lse(np.array([float(lse[b, h]) for b, h in rows]), l_ref, "qwen7b lse")
-    # every output finite and every row a convex combination: |o| <= max |v|
-    assert torch.isfinite(out.float()).all()
+    o_ref, l_ref = oracle_by_sequence(case, bits(case.k_pool), bits(case.v_pool))
+    assert_parity(as_f64(out), o_ref, "qwen7b full")
+    assert_lse(as_f64(lse), l_ref, "qwen7b lse")
 
 
-def test_long_context_decode_full_size_sampled(require_gpu):
-    """Long-context decode at full size (8 x 131072, Hq 64, Hkv 8, page 64, S = 64)."""
+@pytest.mark.parametrize("splits", [64, 0])
+def test_long_context_decode_full_size(require_gpu, splits):
+    """Long-context decode at full size (8 x 131072, Hq 64, Hkv 8, page 64) with the 64
+    partitions it is stated with (4,096 one-wave work-groups) and with the library's
+    own split count; every one of the 512 (sequence, head) rows against the oracle,
+    which takes one sequence's pages and one KV head at a time."""
     case = make_config("long_decode", "cuda")
-    print("[decode] long_decode full size", flush=True)
-    out, lse = run_decode(case, 64)
-    rows = _sample_rows(case, 2, 3, 2)
-    # the oracle needs only the sampled sequences' pages: gather them on the host
-    bt = case.block_tables.cpu().numpy()
-    o_ref = np.zeros((len(rows), 128))
-    l_ref = np.zeros(len(rows))
-    q = bits(case.q)
-    for i, (b, h) in enumerate(rows):
-        pages = torch.as_tensor(bt[b].astype(np.int64), device="cuda")
-        kh = bits(case.k_pool[pages, :, h // 8])      # [pages, 64, D]
-        vh = bits(case.v_pool[pages, :, h // 8])
-        k = oracle.bf16_bits_to_f64(kh).reshape(-1, 128)
-        v = oracle.bf16_bits_to_f64(vh).reshape(-1, 128)
-        o, l = oracle.attend_rows(oracle.bf16_bits_to_f64(q[b, h])[None], k, v, case.scale,
-                                  [131072])
-        o_ref[i], l_ref[i] = o[0], l[0]
-    got = np.stack([as_f64(out[b, h]) for b, h in rows])
-    assert_parity(got, o_ref, "long_decode sampled")
-    assert_lse(np.array([float(lse[b, h]) for b, h in rows]), l_ref, "long lse")
-    assert torch.isfinite(out.float()).all()
+    print(f"[decode] long_decode full size, every row, splits={splits}", flush=True)
+    out, lse = run_decode(case, splits)
+    o_ref, l_ref = oracle_by_sequence(case, bits(case.k_pool), bits(case.v_pool),
+                                      split_kv_heads=True)
+    assert_parity(as_f64(out), o_ref, "long_decode full")
+    assert_lse(as_f64(lse), l_ref, "long lse")
 
 
 def test_workspace_is_scratch_and_reusable(require_gpu):

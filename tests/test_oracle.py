@@ -252,6 +252,63 @@ def test_softmax_rows_sum_to_one_and_masked_keys_are_zero():
             assert (p[i] == 0).all()
 
 
+def _brute_probs(q, k, scale, vis):
+    """Softmax probabilities by pure-Python loops: scaled dot products summed with
+    math.fsum, natural exponentials of the shifted scores, division by their sum."""
+    n, L = len(q), len(k)
+    p = [[0.0] * L for _ in range(n)]
+    for i in range(n):
+        s = [scale * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j]))
+             for j in range(vis[i])]
+        if not s:
+            continue
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = math.fsum(e)
+        for j in range(vis[i]):
+            p[i][j] = e[j] / tot
+    return np.array(p)
+
+
+def _probs_drop_scale(q, k, scale, vis):
+    return oa.softmax_probs_ref(q, k, 1.0, vis)
+
+
+def _probs_base_two(q, k, scale, vis):
+    # exp2 in place of exp: the scores scaled by ln 2 give the same as base 2
+    return oa.softmax_probs_ref(q, k, scale * math.log(2.0), vis)
+
+
+def _probs_no_mask(q, k, scale, vis):
+    return oa.softmax_probs_ref(q, k, scale, [len(k)] * len(q))
+
+
+@pytest.mark.parametrize("mutant", [None, _probs_drop_scale, _probs_base_two, _probs_no_mask])
+def test_softmax_probs_match_brute_force_and_weight_the_values(mutant):
+    """The probabilities equal a pure-Python softmax of the scaled scores, P V is
+    attend_rows' output and log sum exp of the scaled visible scores its lse; each
+    planted mistake (scale dropped, base 2, mask ignored) fails the brute force."""
+    rng = np.random.default_rng(61)
+    q, k, v = rng.standard_normal((5, 6)), rng.standard_normal((13, 6)), rng.standard_normal((13, 4))
+    vis, scale = [13, 1, 0, 7, 12], 0.37
+    fn = oa.softmax_probs_ref if mutant is None else mutant
+    p = fn(q, k, scale, vis)
+    ref = _brute_probs(q, k, scale, vis)
+    if mutant is not None:
+        assert np.abs(p - ref).max() > 1e-6
+        return
+    assert np.abs(p - ref).max() < 1e-14
+    o, lse = oracle.attend_rows(q, k, v, scale, vis)
+    assert np.abs(p @ v - o).max() < 1e-13
+    for i, n in enumerate(vis):
+        s = [scale * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j])) for j in range(n)]
+        if not s:
+            assert lse[i] == -np.inf and (p[i] == 0).all()
+            continue
+        m = max(s)
+        assert abs(lse[i] - (m + math.log(math.fsum(math.exp(x - m) for x in s)))) < 1e-13
+
+
 def test_page_permutation_leaves_output_unchanged():
     case = make_case("p", seq_lens=[40, 17, 64], Hq=4, Hkv=2, D=8, page_size=16, seed=8,
                      num_pages=12)
@@ -634,3 +691,22 @@ def test_planted_alibi_mistakes_are_caught(mutant):
     wrong = -SLOPES if mutant == "sign" else SLOPES * case.scale
     o, _ = run_oracle(case, alibi=wrong)
     assert np.abs(o - ob).max() > 1e-6
+
+
+@pytest.mark.parametrize("split_kv_heads", [False, True])
+@pytest.mark.parametrize("causal,window,alibi", [(True, 0, False), (False, 0, False),
+                                                 (True, 5, True), (True, 0, True)])
+def test_per_sequence_oracle_helper_equals_the_whole_pool_oracle(split_kv_heads, causal,
+                                                                 window, alibi):
+    """The full-size parity tests run the oracle one sequence (and KV head) at a time
+    on the sequence's own pages; that must be the oracle over the whole pool, bit for
+    bit, including empty sequences, chunks over history and rows before the first key."""
+    from tests.parity import oracle_by_sequence, oracle_full
+    case = make_case("bys", seq_lens=[40, 0, 17, 65], q_lens=[3, 2, 20, 65], Hq=6, Hkv=2, D=8,
+                     page_size=4, seed=71, causal=causal, window=window, num_pages=40)
+    slopes = np.array([0.3, -0.1, 0.05, 0.0, 0.2, 0.7]) if alibi else None
+    kp, vp = bits(case.k_pool), bits(case.v_pool)
+    o1, l1 = oracle_full(case, kp, vp, alibi=slopes)
+    o2, l2 = oracle_by_sequence(case, kp, vp, split_kv_heads=split_kv_heads, alibi=slopes)
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(l1, l2)

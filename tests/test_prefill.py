@@ -5,8 +5,9 @@ import pytest
 import torch
 
 import paged_kv_flashattention_amd as pa
-from tests.parity import (as_f64, assert_lse, assert_parity, oracle_full, oracle_rows,
-                          pools_after_write)
+import oracle
+from tests.parity import (as_f64, assert_lse, assert_parity, oracle_by_sequence, oracle_full,
+                          oracle_rows, pools_after_write)
 from workloads import bits, make_case, make_config
 
 pytestmark = pytest.mark.gpu
@@ -89,22 +90,62 @@ def test_prefill_decode_rows_match_decode_kernel(require_gpu):
     assert_parity(as_f64(out_d), o_ref, "decode")
 
 
-def test_causal_prefill_full_size_sampled(require_gpu):
+def _head_rows_oracle(case, kp, vp, b, h):
+    """Every row of query head h of sequence b from the oracle, run on that sequence's
+    pages and the KV head h reads (compact pool, table 0 .. n-1, Hq = Hkv = 1)."""
+    bt = case.block_tables.cpu().numpy()
+    cu = case.cu_seqlens_q.cpu().numpy()
+    L = case.seq_lens[b]
+    n = -(-L // case.page_size)
+    kvh = h // (case.Hq // case.Hkv)
+    pages = bt[b, :n].astype(np.int64)
+    t0, t1 = int(cu[b]), int(cu[b + 1])
+    o, ls = oracle.attention_ref(bits(case.q)[t0:t1, h:h + 1],
+                                 np.ascontiguousarray(kp[pages][:, :, kvh:kvh + 1]),
+                                 np.ascontiguousarray(vp[pages][:, :, kvh:kvh + 1]),
+                                 np.arange(n, dtype=np.int32)[None], [L], [0, t1 - t0],
+                                 case.scale, True, case.page_size)
+    return o[:, 0], ls[:, 0]
+
+
+def test_causal_prefill_full_size_every_work_group(require_gpu):
     """Dense causal prefill at full size: 4 x 4096 tokens, Hq 32, Hkv 8, written via
-    kv_page_write then attended; the oracle checks sampled (token, head) rows."""
+    kv_page_write then attended in the launch the benchmark times.  The oracle checks
+    one complete query head per (sequence, KV head) -- 32 heads of 4,096 rows, every
+    query tile and key tile of their groups -- and one row of every other (head,
+    sequence, 256-row query tile) work-group of the grid, 2,048 work-groups in all."""
     case = make_config("causal_prefill", "cuda")
-    print("[prefill] causal_prefill full size", flush=True)
+    print("[prefill] causal_prefill full size, every work-group", flush=True)
     kp, vp = pools_after_write(case)
     write(case)
     assert np.array_equal(bits(case.k_pool), kp)
     out, lse = run_prefill(case)
+    G = case.Hq // case.Hkv
+    got, ref, got_l, ref_l = [], [], [], []
+    whole = {(b, kvh * G + (b + 3 * kvh) % G) for b in range(case.B) for kvh in range(case.Hkv)}
+    for b, h in sorted(whole):
+        o, ls = _head_rows_oracle(case, kp, vp, b, h)
+        got.append(as_f64(out[4096 * b:4096 * (b + 1), h]))
+        got_l.append(as_f64(lse[4096 * b:4096 * (b + 1), h]))
+        ref.append(o)
+        ref_l.append(ls)
     rng = np.random.default_rng(5)
-    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, case.T, 48), rng.integers(0, 32, 48))]
-    rows += [(0, 0), (4095, 31), (4096, 5), (case.T - 1, 17)]     # first / last rows
+    rows = []
+    for b in range(case.B):
+        for h in range(case.Hq):
+            if (b, h) in whole:
+                continue
+            for qt in range(4096 // 256):
+                rows.append((4096 * b + 256 * qt + int(rng.integers(0, 256)), h))
     o_ref, l_ref = oracle_rows(case, rows, kp, vp)
-    got = np.stack([as_f64(out[t, h]) for t, h in rows])
-    assert_parity(got, o_ref, "causal_prefill sampled")
-    assert_lse(np.array([float(lse[t, h]) for t, h in rows]), l_ref, "causal_prefill lse")
+    idx_t = torch.as_tensor([t for t, _ in rows], device="cuda")
+    idx_h = torch.as_tensor([h for _, h in rows], device="cuda")
+    got.append(as_f64(out[idx_t, idx_h]))
+    got_l.append(as_f64(lse[idx_t, idx_h]))
+    ref.append(o_ref)
+    ref_l.append(l_ref)
+    assert_parity(np.concatenate(got), np.concatenate(ref), "causal_prefill")
+    assert_lse(np.concatenate(got_l), np.concatenate(ref_l), "causal_prefill lse")
     assert torch.isfinite(out.float()).all()
 
 
@@ -172,24 +213,19 @@ def test_prefill_splitk_workspace_is_scratch(require_gpu):
         assert_lse(as_f64(lse), l_ref, f"prefill splitk ws lse {i}")
 
 
-def test_long_history_chunk_full_size_sampled(require_gpu):
+def test_long_history_chunk_full_size(require_gpu):
     """A 512-token chunk over a 32,768-token history (Hq 32, Hkv 8), with the library's
-    own key-part count as the benchmark runs it; the oracle checks sampled rows."""
+    own key-part count as the benchmark runs it; every row against the oracle."""
     case = make_config("long_history_chunk", "cuda")
-    print("[prefill splitk] long_history_chunk full size", flush=True)
+    print("[prefill splitk] long_history_chunk full size, every row", flush=True)
     kp, vp = pools_after_write(case)
     write(case)
     assert pa.prefill_num_splits(1, 32, 512) > 1
     out, lse = run_prefill_splitk(case, 0)
     assert "prefill_merge" in pa.describe_launch()
-    rng = np.random.default_rng(8)
-    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, 512, 24), rng.integers(0, 32, 24))]
-    rows += [(0, 0), (511, 31), (255, 16), (256, 1)]
-    o_ref, l_ref = oracle_rows(case, rows, kp, vp)
-    got = np.stack([as_f64(out[t, h]) for t, h in rows])
-    assert_parity(got, o_ref, "long_history_chunk sampled")
-    assert_lse(np.array([float(lse[t, h]) for t, h in rows]), l_ref, "long_history_chunk lse")
-    assert torch.isfinite(out.float()).all()
+    o_ref, l_ref = oracle_by_sequence(case, kp, vp, split_kv_heads=True)
+    assert_parity(as_f64(out), o_ref, "long_history_chunk")
+    assert_lse(as_f64(lse), l_ref, "long_history_chunk lse")
 
 
 @pytest.mark.parametrize("splitk", [0, 4, -1])
@@ -220,16 +256,11 @@ def test_mixed_ragged_step_full_size(require_gpu, splitk):
         case.block_tables[n_pf:].contiguous(), case.seq_lens_k[n_pf:].contiguous(), case.scale,
         max_seq_len=max(case.seq_lens[n_pf:]), return_lse=True, validate=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(6)
-    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, t_pf, 40), rng.integers(0, 32, 40))]
-    rows += [(511, 0), (512, 31), (t_pf - 1, 3), (1024, 0), (1300, 7), (1535, 31)]
-    rows += [(t, h) for t in range(t_pf, case.T) for h in (0, 13, 31)]
-    o_ref, l_ref = oracle_rows(case, rows, kp, vp)
-    got = np.stack([as_f64(out_p[t, h]) if t < t_pf else as_f64(out_d[t - t_pf, h])
-                    for t, h in rows])
+    # every row of the step: the 2,560 prefill rows and the 18 decode rows, all heads
+    o_ref, l_ref = oracle_by_sequence(case, kp, vp)
+    got = np.concatenate([as_f64(out_p), as_f64(out_d)])
+    got_l = np.concatenate([as_f64(lse_p), as_f64(lse_d)])
     assert_parity(got, o_ref, "mixed step")
-    got_l = np.array([float(lse_p[t, h]) if t < t_pf else float(lse_d[t - t_pf, h])
-                      for t, h in rows])
     assert_lse(got_l, l_ref, "mixed lse")
 
 
@@ -280,3 +311,53 @@ def test_prefill_xcd_rank_classes(require_gpu, hist, ql, Hq, Hkv, classes):
     o_ref, l_ref = oracle_full(case, kp, vp)
     assert_parity(as_f64(out), o_ref, "prefill xcd classes")
     assert_lse(as_f64(lse), l_ref, "prefill xcd classes lse")
+
+
+NO_KEY_CASES = [
+    # seq_lens (keys), q_lens, causal, splits, window, alibi
+    ([0, 10, 300], [37, 50, 20], True, 1, 0, False),         # 4 waves: L = 0, L < q_len
+    ([0, 7], [5, 9], False, 1, 0, False),                    # non-causal, L = 0
+    ([100, 0], [600, 3], True, 1, 0, False),                 # 8 waves: 500 rows see nothing
+    ([0, 3000, 2500], [20, 3100, 300], True, 4, 0, False),   # key parts over L < q_len
+    ([0, 40], [30, 100], True, 1, 64, True),                 # window + ALiBi variant
+    ([0, 700], [10, 900], True, 1, 0, True),                 # ALiBi, 8 waves, walked down
+]
+
+
+@pytest.mark.parametrize("lens,ql,causal,splits,window,alibi", NO_KEY_CASES)
+def test_prefill_rows_that_see_no_key(require_gpu, lens, ql, causal, splits, window, alibi):
+    """Rows of a sequence with no keys, or causal rows placed before the sequence's
+    first key (q_len > keys, bottom-right alignment), give exactly O = 0 and lse = -inf
+    ("8. Kernels and Attention Backends", "Test the kernel at three levels": a fully
+    masked row needs a defined value); every other row matches the oracle."""
+    print(f"[prefill no-key] lens={lens} q={ql} causal={causal} S={splits} w={window} "
+          f"alibi={alibi}", flush=True)
+    case = make_case("pnk", seq_lens=lens, q_lens=ql, causal=causal, Hq=8, Hkv=2, D=128,
+                     page_size=16, seed=sum(lens) + sum(ql), device="cuda", window=window,
+                     num_pages=sum(-(-L // 16) for L in lens) + 3)
+    slopes = None
+    if alibi:
+        slopes = torch.tensor([2.0 ** (-(h + 1)) for h in range(8)], dtype=torch.float32,
+                              device="cuda")
+    if splits > 1:
+        out, lse = pa.paged_attn_prefill_varlen_splitk(
+            case.q, case.k_pool, case.v_pool, case.cu_seqlens_q, case.seq_lens_k,
+            case.block_tables, case.scale, causal=causal, max_q_len=case.max_q_len,
+            num_splits=splits, return_lse=True, validate=True, window_left=window,
+            alibi_slopes=slopes)
+        assert "prefill_merge" in pa.describe_launch()
+    else:
+        out, lse = pa.paged_attn_prefill_varlen(
+            case.q, case.k_pool, case.v_pool, case.cu_seqlens_q, case.seq_lens_k,
+            case.block_tables, case.scale, causal=causal, max_q_len=case.max_q_len,
+            return_lse=True, validate=True, window_left=window, alibi_slopes=slopes)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_full(case, bits(case.k_pool), bits(case.v_pool),
+                               alibi=None if slopes is None else slopes.cpu().numpy())
+    empty = np.isneginf(l_ref)
+    assert empty.any()
+    got_o, got_l = as_f64(out), as_f64(lse)
+    assert (got_o[empty] == 0).all(), "a row with no key has a nonzero output"
+    assert np.isneginf(got_l[empty]).all(), "a row with no key has a finite lse"
+    assert_parity(got_o, o_ref, "prefill no-key")
+    assert_lse(got_l, l_ref, "prefill no-key lse")
