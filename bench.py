@@ -49,15 +49,21 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen7b_decode",
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
-                            "long_decode", "causal_prefill", "causal_prefill_fp8",
-                            "mixed_ragged", "tiny_decode", "qwen7b_decode_warm"])
+                            "long_decode", "long_decode_auto", "causal_prefill",
+                            "causal_prefill_fp8", "mixed_ragged", "tiny_decode",
+                            "qwen7b_decode_warm"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--traffic-pass", action="store_true",
                    help="run only a 1 GiB device copy and a few launches of the workload's "
-                        "dominant kernel (qwen7b_decode or causal_prefill), for rocprofv3 "
-                        "--pmc FETCH_SIZE / WRITE_SIZE collection")
+                        "dominant kernel, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                        "collection (workloads: " + ", ".join(sorted(TRAFFIC)) + ")")
+    p.add_argument("--record-traffic", metavar="DIR",
+                   help="no GPU work: read the counter CSVs of the two --traffic-pass runs "
+                        "of --workload under DIR/pmc_<workload>_FETCH_SIZE and "
+                        "DIR/pmc_<workload>_WRITE_SIZE and write the workload's traffic "
+                        "record under profiles/")
     return p.parse_args()
 
 
@@ -347,6 +353,9 @@ def make_step(name, num_splits=0):
     if name == "long_decode":
         # the workload is stated with 64 partitions; --num-splits overrides
         return DecodeStep(name, copies=1, num_splits=num_splits or 64)
+    if name == "long_decode_auto":
+        # the same decode with the library's own split count
+        return DecodeStep("long_decode", copies=1, num_splits=num_splits)
     if name == "tiny_decode":
         return DecodeStep(name, copies=1, num_splits=num_splits)
     if name == "causal_prefill":
@@ -418,13 +427,21 @@ def rate(units, ms, unit_name):
 # HBM traffic of the dominant kernel, from rocprofv3 counters
 # ---------------------------------------------------------------------------
 
-# per workload: the recorded counter figures of its dominant kernel and the sources
-# that kernel is built from
+# per workload: the recorded counter figures of its dominant kernel, the sources that
+# kernel is built from, and the kernel's name as the profiler reports it (a prefix)
+_DECODE_SRC = ["decode.hip", "common.hpp", "kernels.hpp"]
+_PREFILL_SRC = ["prefill.hip", "common.hpp", "kernels.hpp"]
 TRAFFIC = {
-    "qwen7b_decode": ("decode_partition_qwen7b_decode_traffic.json",
-                      ["decode.hip", "common.hpp", "kernels.hpp"]),
-    "causal_prefill": ("prefill_causal_prefill_traffic.json",
-                       ["prefill.hip", "common.hpp", "kernels.hpp"]),
+    "qwen7b_decode": ("decode_partition_qwen7b_decode_traffic.json", _DECODE_SRC,
+                      "pa::decode_partition_kernel<"),
+    "long_decode": ("decode_partition_long_decode_traffic.json", _DECODE_SRC,
+                    "pa::decode_partition_kernel<"),
+    "long_decode_auto": ("decode_partition_long_decode_auto_traffic.json", _DECODE_SRC,
+                         "pa::decode_partition_kernel<"),
+    "causal_prefill": ("prefill_causal_prefill_traffic.json", _PREFILL_SRC,
+                       "pa::prefill_kernel<"),
+    "long_history_chunk": ("prefill_long_history_chunk_traffic.json", _PREFILL_SRC,
+                           "pa::prefill_kernel<"),
 }
 COPY_BYTES = 1 << 30           # the calibration copy reads and writes this many bytes
 
@@ -473,7 +490,7 @@ def traffic_pass(steps, workload):
     del src, dst
     torch.cuda.empty_cache()
     step = make_step(workload, 0)
-    if workload == "qwen7b_decode":
+    if isinstance(step, DecodeStep):
         step.partition_launches(steps)
     else:
         for _ in range(steps):
@@ -481,6 +498,65 @@ def traffic_pass(steps, workload):
     torch.cuda.synchronize()
     log(f"[bench] traffic pass: copy of {COPY_BYTES} bytes, {steps} {workload} launches; "
         f"sources {source_digest(workload)[:16]}")
+
+
+def record_traffic(workload, pmc_dir):
+    """The traffic record of `workload` from the counter CSVs of its two traffic-pass
+    runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each
+    counter is scaled by its own reading for the pass's calibration copy of
+    COPY_BYTES (read once, written once), and the dominant kernel's dispatches are
+    averaged: bytes per launch = (FETCH_SIZE x fetch scale + WRITE_SIZE x write
+    scale) x 1024.  Written to profiles/ with the digest of the kernel's sources."""
+    import csv
+    from workloads import config_shape, units
+    fname, _, kname = TRAFFIC[workload]
+
+    def per_dispatch(counter):
+        path = os.path.join(pmc_dir, f"pmc_{workload}_{counter}", "run_counter_collection.csv")
+        agg = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                k = (int(r["Dispatch_Id"]), name[5:] if name.startswith("void ") else name)
+                agg[k] = agg.get(k, 0.0) + float(r["Counter_Value"])
+        return agg
+
+    f, w = per_dispatch("FETCH_SIZE"), per_dispatch("WRITE_SIZE")
+    kib = COPY_BYTES / 1024
+    # the calibration copy: the one large copyBuffer dispatch
+    cf = max(v for (_, n), v in f.items() if "copyBuffer" in n)
+    cw = max(v for (_, n), v in w.items() if "copyBuffer" in n)
+    fs, ws = kib / cf, kib / cw
+    kf = [v for (_, n), v in sorted(f.items()) if n.startswith(kname)]
+    kw = [v for (_, n), v in sorted(w.items()) if n.startswith(kname)]
+    names = sorted({n for (_, n) in f if n.startswith(kname)})
+    fk, wk = sum(kf) / len(kf), sum(kw) / len(kw)
+    rec = {"kernel": names[0] if len(names) == 1 else names, "workload": workload,
+           "fetch_kib_per_launch": round(fk, 3), "fetch_kib_range": [min(kf), max(kf)],
+           "write_kib_per_launch": round(wk, 3), "write_kib_range": [min(kw), max(kw)],
+           "launches": len(kf),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_scale": round(fs, 6), "write_scale": round(ws, 6)},
+           "bytes_per_launch": int(round((fk * fs + wk * ws) * 1024))}
+    c = config_shape("long_decode" if workload == "long_decode_auto" else workload)
+    if workload in ("causal_prefill", "long_history_chunk"):
+        rec["minimum_bytes_per_launch"] = units.prefill_bytes(c["seq_lens"], c["q_lens"],
+                                                              c["Hq"], c["Hkv"], c["D"])
+        rec["minimum_bytes_note"] = ("Q and O once, K and V once per KV head; the kernel is "
+                                     "bound by its matrix work, not by these bytes")
+    else:
+        rec["algorithmic_bytes_per_launch"] = units.decode_bytes(
+            c["seq_lens"], c["Hq"], c["Hkv"], c["D"], c["page_size"])
+    rec["source_sha256"] = source_digest(workload)
+    rec["commands"] = [
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {k} "
+        f"--output-format csv -d $REPO/gpurun_out/pmc_{workload}_{k} -o run -- python3 "
+        f"$REPO/bench.py --traffic-pass --workload {workload} --steps 6"
+        for k in ("FETCH_SIZE", "WRITE_SIZE")] + [
+        f"python3 bench.py --workload {workload} --record-traffic gpurun_out"]
+    with open(os.path.join(ROOT, "profiles", fname), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    log(f"[bench] {workload}: {rec['bytes_per_launch']} bytes per launch -> profiles/{fname}")
 
 
 # ---------------------------------------------------------------------------
@@ -528,19 +604,34 @@ def stream_read_gbs(iters=10):
 # oracle baseline on the host cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(step, min_s=10.0, budget_s=15.0):
-    """The float64 oracle, as it stands, on a bounded sample of the same workload:
-    passes over the batch's sequences (each sequence's pages copied to the host once,
-    untimed) until at least min_s seconds of oracle time, stopping at budget_s."""
-    import numpy as np
-    import oracle
-    from workloads import bits, units
+def host_cores():
+    """(cores this process may run on, BLAS threads the oracle's NumPy uses)."""
+    cores = len(os.sched_getaffinity(0))
     try:
         # the oracle's NumPy runs single-threaded except inside BLAS calls
         from threadpoolctl import threadpool_info
-        cores = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+        blas = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
     except Exception:
-        cores = 1
+        blas = None
+    return cores, blas
+
+
+def cpu_baseline(step, min_s=10.0, budget_s=15.0):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload.
+
+    Decode: passes over the batch's sequences (each sequence's pages copied to the
+    host once, untimed) until at least min_s seconds of oracle time, stopping at
+    budget_s; algorithmic GB/s.  Causal prefill: whole (sequence, query head)
+    planes -- every row of one head over its sequence's keys, the oracle given that
+    sequence's pages and the KV head the query head reads -- until min_s; GFLOP/s
+    of algorithmic prefill work."""
+    if isinstance(step, PrefillStep) and not isinstance(step, Fp8PrefillStep) \
+            and not step.splitk:
+        return cpu_baseline_prefill(step, min_s, budget_s)
+    import numpy as np
+    import oracle
+    from workloads import bits, units
+    cores, blas = host_cores()
     c = step.case
     if not isinstance(step, DecodeStep) or isinstance(step, Fp8DecodeStep):
         return None
@@ -568,10 +659,48 @@ def cpu_baseline(step, min_s=10.0, budget_s=15.0):
                 break
         if t_used >= budget_s:
             break
-    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": cores,
+            "blas_threads": blas, "kind": "oracle",
             "sample": f"{c.name}: {done} sequence decodes ({done / c.B:.1f} passes over the "
                       f"{c.B} sequences), all {c.Hq} query heads, float64 NumPy, "
                       f"{t_used:.1f} s of oracle time"}
+
+
+def cpu_baseline_prefill(step, min_s=10.0, budget_s=15.0):
+    import numpy as np
+    import oracle
+    from workloads import bits, units
+    cores, blas = host_cores()
+    c = step.case
+    G = c.Hq // c.Hkv
+    bt = c.block_tables.cpu().numpy()
+    cu = c.cu_seqlens_q.cpu().numpy()
+    lens = c.seq_lens
+    q = bits(c.q)
+    kp, vp = bits(c.k_pool), bits(c.v_pool)          # the pools after the step's write
+    done, t_used, flops = 0, 0.0, 0
+    planes = [(b, h) for h in range(c.Hq) for b in range(c.B)]
+    for b, h in planes:
+        L = int(lens[b])
+        n = -(-L // c.page_size)
+        pages = bt[b, :n].astype(np.int64)
+        kvh = h // G
+        kb = np.ascontiguousarray(kp[pages][:, :, kvh:kvh + 1])
+        vb = np.ascontiguousarray(vp[pages][:, :, kvh:kvh + 1])
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        tic = time.perf_counter()
+        oracle.attention_ref(q[t0:t1, h:h + 1], kb, vb, np.arange(n, dtype=np.int32)[None],
+                             [L], [0, t1 - t0], c.scale, True, c.page_size)
+        t_used += time.perf_counter() - tic
+        flops += units.prefill_flops([L], [t1 - t0], 1, c.D, True)
+        done += 1
+        if t_used >= min_s:
+            break
+    return {"value": flops / t_used / 1e9, "unit": "GFLOP/s", "cores": cores,
+            "blas_threads": blas, "kind": "oracle",
+            "sample": f"{c.name}: {done} of the {len(planes)} (sequence, query head) planes "
+                      f"({t1 - t0} causal rows over {L} keys each), float64 NumPy with the "
+                      f"scores materialised, {t_used:.1f} s of oracle time"}
 
 
 # ---------------------------------------------------------------------------
@@ -595,8 +724,35 @@ def secondary_figure(label, name, splits, args):
     return fig
 
 
+def roofline_object(step, workload, kern_ms, ev_ms):
+    """The roofline of a step's dominant kernel: algorithmic units per launch over the
+    kernel's own (dispatch-stamped) duration against MI355X's published peak, with
+    the counter-measured HBM traffic recorded for the same sources (or null)."""
+    bound = "hbm" if step.unit_name == "GB/s" else "mfma"
+    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
+    if kern_ms is None:                      # the mixed step: no single main kernel
+        kern_ms = ev_ms
+    achieved = rate(step.units, kern_ms, step.unit_name)
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+            "unit": step.unit_name, "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(workload),
+            "algorithmic_units_per_launch": int(step.units),
+            "kernel": ("decode_partition_kernel" if bound == "hbm" else "prefill_kernel")
+            if not isinstance(step, MixedStep) else "whole step",
+            "kernel_us_per_launch": round(kern_ms * 1e3, 2),
+            "kernel_us_median": round(getattr(step, "kernel_ms_median", kern_ms) * 1e3, 2),
+            "kernel_us_min": round(getattr(step, "kernel_ms_min", kern_ms) * 1e3, 2),
+            "kernel_timing": "start/end events stamped by that kernel's own dispatch "
+                             "(hipExtLaunchKernel) in a second pass of the same steps "
+                             "right after the timed pass",
+            "step_us": round(ev_ms * 1e3, 2)}
+
+
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.workload, args.record_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU "
                                    "sharding of the path is described, not built",
@@ -623,8 +779,6 @@ def main():
     log(f"[bench] {args.workload}: {ev * 1e3:.1f} us/step (events), {wall * 1e3:.1f} us/step "
         f"(wall), {value:.1f} {step.unit_name}; dominant kernel {kern_ms * 1e3:.1f} us, "
         f"{achieved:.1f} {step.unit_name}; {launch}")
-    bound = "hbm" if step.unit_name == "GB/s" else "mfma"
-    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -639,19 +793,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": step.config(),
-        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": step.unit_name, "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(args.workload),
-                     "kernel": ("decode_partition_kernel" if bound == "hbm" else "prefill_kernel")
-                     if not isinstance(step, MixedStep) else "whole step",
-                     "kernel_us_per_launch": round(kern_ms * 1e3, 2),
-                     "kernel_us_median": round(getattr(step, "kernel_ms_median", kern_ms) * 1e3, 2),
-                     "kernel_us_min": round(getattr(step, "kernel_ms_min", kern_ms) * 1e3, 2),
-                     "kernel_timing": "start/end events stamped by that kernel's own "
-                                      "dispatch (hipExtLaunchKernel) in a second pass of "
-                                      "the same steps right after the timed pass",
-                     "step_us": round(ev * 1e3, 2)},
+        "roofline": roofline_object(step, args.workload, kern_ms, ev),
     }
+    bound = result["roofline"]["bound"]
     del step
     torch.cuda.empty_cache()
     if bound == "hbm":
@@ -663,6 +807,26 @@ def main():
             f"{achieved / read_gbs:.1%} of it")
 
     if not args.no_secondary and args.workload == "qwen7b_decode":
+        # the metric's second half: causal prefill (4 x 4096, Hq 32, Hkv 8) with a
+        # roofline object of its own and its own oracle baseline
+        try:
+            pf = make_step("causal_prefill", 0)
+            w2, e2, k2 = time_step(pf, args.steps, args.warmup)
+            result["roofline_prefill"] = dict(roofline_object(pf, "causal_prefill", k2, e2),
+                                              value=round(rate(pf.units, e2, pf.unit_name), 2),
+                                              config=pf.config())
+            log(f"[bench] causal_prefill: {e2 * 1e3:.1f} us/step, kernel {k2 * 1e3:.1f} us, "
+                f"{result['roofline_prefill']['achieved']:.1f} TFLOP/s in the kernel")
+            if not args.no_cpu_baseline:
+                cb = cpu_baseline(pf)
+                result["cpu_baseline_prefill"] = cb
+                log(f"[bench] prefill cpu baseline: {cb['value']:.3f} {cb['unit']} "
+                    f"({cb['sample']})")
+            del pf
+        except Exception as exc:                          # noqa: BLE001
+            result["roofline_prefill"] = {"error": f"{type(exc).__name__}: {exc}"}
+            log(f"[bench] causal_prefill: failed ({type(exc).__name__}: {exc})")
+        torch.cuda.empty_cache()
         # the other workloads, same timing; the long-context decode both with the 64
         # partitions it is stated with and with the library's own split choice; the C2
         # decode and the mixed step also replayed from a HIP graph (*_graph)
@@ -671,7 +835,6 @@ def main():
                                     ("qwen7b_decode_warm", "qwen7b_decode_warm", 0),
                                     ("tiny_decode", "tiny_decode", 0),
                                     ("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
-                                    ("causal_prefill", "causal_prefill", 0),
                                     ("causal_prefill_fp8", "causal_prefill_fp8", 0),
                                     ("long_decode", "long_decode", 64),
                                     ("long_decode_auto_splits", "long_decode", -1),

@@ -35,8 +35,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-__all__ = ["PagedCase", "make_case", "make_config", "CONFIGS", "CONFIG_ORDER",
-           "bits", "units", "random_e4m3_codes"]
+__all__ = ["PagedCase", "make_case", "make_config", "config_shape", "CONFIGS",
+           "CONFIG_ORDER", "bits", "units", "random_e4m3_codes"]
 
 BF16_NAN_BITS = 0x7FC0
 TAIL_POISON = 3.0e4
@@ -248,48 +248,44 @@ def _mixed_lengths(seed):
 CONFIG_ORDER = ["tiny_decode", "qwen7b_decode", "mixed_ragged", "causal_prefill", "long_decode"]
 
 
-def _cfg_tiny(device):
-    return make_case("tiny_decode", seq_lens=[17, 64, 100, 255], Hq=8, Hkv=2, D=64,
-                     page_size=16, num_pages=64, seed=1000, device=device, num_splits=1)
-
-
-def _cfg_qwen(device):
-    return make_case("qwen7b_decode", seq_lens=[8192] * 32, Hq=28, Hkv=4, D=128,
-                     page_size=16, num_pages=16384, seed=1001, device=device)
-
-
-def _cfg_mixed(device):
+def _shapes():
+    """make_case arguments of every named workload (structure and sizes only)."""
     hist, ql = _mixed_lengths(1002)
-    return make_case("mixed_ragged", hist_lens=hist, q_lens=ql, write_new=True, causal=True,
-                     Hq=32, Hkv=8, D=128, page_size=16, seed=1002, device=device)
+    return {
+        "tiny_decode": dict(seq_lens=[17, 64, 100, 255], Hq=8, Hkv=2, D=64, page_size=16,
+                            num_pages=64, seed=1000, num_splits=1),
+        "qwen7b_decode": dict(seq_lens=[8192] * 32, Hq=28, Hkv=4, D=128, page_size=16,
+                              num_pages=16384, seed=1001),
+        "mixed_ragged": dict(hist_lens=hist, q_lens=ql, write_new=True, causal=True, Hq=32,
+                             Hkv=8, D=128, page_size=16, seed=1002),
+        "causal_prefill": dict(hist_lens=[0] * 4, q_lens=[4096] * 4, write_new=True,
+                               causal=True, Hq=32, Hkv=8, D=128, page_size=16,
+                               num_pages=1024, seed=1003),
+        "long_decode": dict(seq_lens=[131072] * 8, Hq=64, Hkv=8, D=128, page_size=64,
+                            num_pages=16384, seed=1004, std_kv=0.5, num_splits=64),
+        # one 512-token prefill chunk over a 32,768-token history (chunked prefill of a
+        # long prompt): only 128 query tiles, the case key splitting is for
+        "long_history_chunk": dict(hist_lens=[32768], q_lens=[512], write_new=True,
+                                   causal=True, Hq=32, Hkv=8, D=128, page_size=16, seed=1005),
+    }
 
 
-def _cfg_prefill(device):
-    return make_case("causal_prefill", hist_lens=[0] * 4, q_lens=[4096] * 4, write_new=True,
-                     causal=True, Hq=32, Hkv=8, D=128, page_size=16, num_pages=1024,
-                     seed=1003, device=device)
+CONFIGS = {name: (lambda device, n=name: make_case(n, device=device, **_shapes()[n]))
+           for name in _shapes()}
 
 
-def _cfg_long(device):
-    return make_case("long_decode", seq_lens=[131072] * 8, Hq=64, Hkv=8, D=128, page_size=64,
-                     num_pages=16384, seed=1004, std_kv=0.5, device=device, num_splits=64)
-
-
-def _cfg_long_chunk(device):
-    # one 512-token prefill chunk over a 32,768-token history (chunked prefill of a
-    # long prompt): only 128 query tiles, the case key splitting is for
-    return make_case("long_history_chunk", hist_lens=[32768], q_lens=[512], write_new=True,
-                     causal=True, Hq=32, Hkv=8, D=128, page_size=16, seed=1005, device=device)
-
-
-CONFIGS = {
-    "tiny_decode": _cfg_tiny,
-    "qwen7b_decode": _cfg_qwen,
-    "mixed_ragged": _cfg_mixed,
-    "causal_prefill": _cfg_prefill,
-    "long_decode": _cfg_long,
-    "long_history_chunk": _cfg_long_chunk,
-}
+def config_shape(name: str) -> dict:
+    """The named workload's host-side structure without generating any values:
+    seq_lens (keys attended), q_lens, Hq, Hkv, D, page_size."""
+    a = _shapes()[name]
+    if a.get("write_new"):
+        ql = list(a["q_lens"])
+        lens = [h + n for h, n in zip(a["hist_lens"], ql)]
+    else:
+        lens = list(a["seq_lens"])
+        ql = [1] * len(lens) if a.get("q_lens") is None else list(a["q_lens"])
+    return dict(seq_lens=lens, q_lens=ql, Hq=a["Hq"], Hkv=a["Hkv"], D=a["D"],
+                page_size=a["page_size"])
 
 
 def make_config(name: str, device="cpu") -> PagedCase:
