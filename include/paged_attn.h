@@ -172,6 +172,35 @@ int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_po
                       void* stream);
 
 /*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The split-K partials go to a fixed scratch area inside the
+ * library instead of a caller workspace; the call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine) and records no memset.
+ *
+ *   - The scratch is PA_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB) of device memory in
+ *     the library's code object: each GPU the library runs on holds its own copy
+ *     until the process ends.  Its address on a device is looked up on the first
+ *     call on that device (make one call outside graph capture first).
+ *   - Arguments, split resolution, results and statuses are paged_attn_decode's
+ *     with no workspace.  When the resolved split count needs more partials than
+ *     the scratch holds (paged_attn_decode_workspace_bytes above 32 MiB), the call
+ *     returns PA_ERR_WORKSPACE and enqueues nothing.  The library's own split
+ *     choice (num_splits <= 0) always fits.
+ *   - Nothing in the scratch needs clearing: every call writes each partial it
+ *     reads.  Every call on a GPU shares that GPU's scratch, so calls that overlap
+ *     on one GPU (other streams, other threads) race and their results are
+ *     undefined; calls in one stream are ordered and safe.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paged_attn_decode_noalloc(void* out, float* lse_out, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_tables,
+                              const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                              int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                              int32_t D, float softmax_scale, int32_t max_seq_len,
+                              int32_t num_splits, void* stream);
+
+/*
  * paged_attn_decode_fp8 -- paged_attn_decode over FP8 E4M3 pools (format above):
  * the attention of q against keys decode(k_code) * k_scale and values
  * decode(v_code) * v_scale.  The codes are widened to bf16 exactly on their way to

@@ -50,6 +50,9 @@ SIGNATURES = {
     "paged_attn_decode": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                   c_float, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "paged_attn_decode_noalloc": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          c_float, c_i32, c_i32, c_vp]),
     "paged_attn_decode_fp8": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                       c_float, c_float, c_float, c_i32, c_i32, c_vp, c_size,

@@ -5,7 +5,9 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <vector>
 #include <string.h>
@@ -356,6 +358,43 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   return PA_OK;
 }
 
+// Scratch of paged_attn_decode_noalloc: the split-K partials of callers that cannot
+// allocate.  It lives in the library's code object, so every GPU the library runs
+// on holds its own copy from the library's first use there until the process ends.
+// In host code `scratch` only stands for the device array: its address on the
+// current device comes from hipGetSymbolAddress, taken once per device and kept.
+constexpr size_t kNoallocScratchBytes = PA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on the first call on each
+// device); PA_OK or a failure status with the reason recorded.
+int scratch_on_current_device(const char* what, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices with scratch", what, dev,
+                kMaxScratchDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(PA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", what, dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
+
 }  // namespace
 
 // The caller's optional kernel-timing events of an options struct.
@@ -463,6 +502,35 @@ int paged_attn_splitk_reduce(void* out, float* lse_out, const float* partial_out
                                    sizeof(g_last_launch));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "splitk_reduce launch: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+int paged_attn_decode_noalloc(void* out, float* lse_out, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_tables,
+                              const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                              int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv,
+                              int32_t D, float softmax_scale, int32_t max_seq_len,
+                              int32_t num_splits, void* stream) {
+  g_last_error[0] = 0;
+  // the same checks and split resolution as paged_attn_decode, then the size rule,
+  // all on the host before the device is touched
+  pa::DecodeArgs a;
+  int st = decode_args(a, "decode_noalloc", q, k_pool, v_pool, block_tables, seq_lens, B,
+                       max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                       num_splits);
+  if (st) return st;
+  const size_t need = workspace_for(B, Hq, D, a.S);
+  if (need > kNoallocScratchBytes)
+    return fail(PA_ERR_WORKSPACE, "decode_noalloc: %d splits need %zu bytes of partials, more "
+                "than the library's %zu-byte scratch (use fewer splits, or paged_attn_decode "
+                "with a workspace)", a.S, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (need && B > 0) {
+    st = scratch_on_current_device("decode_noalloc", &ws);
+    if (st) return st;
+  }
+  return decode_impl("decode_noalloc", out, lse_out, q, k_pool, v_pool, block_tables, seq_lens,
+                     B, max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
+                     num_splits, ws, ws ? kNoallocScratchBytes : 0, false, 1.f, 1.f, stream);
 }
 
 int paged_attn_decode_partials(float* partial_out, float* partial_lse, const void* q,
