@@ -124,13 +124,8 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // Keeps a value computed where it is written: later passes may not sink its
 // computation past this point (used to hold vector work between MFMAs).
 __device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void pin(uint32_t v) { asm volatile("" ::"v"(v)); }
 
-// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2_f32_bf16 against (1, 1))
-__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
-                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
-}
 
 // Transposing 8-byte LDS read: within each 16-lane group, lane j receives element
 // (j % 4) of the 8-byte rows that lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4 point at.
@@ -501,19 +496,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 
   // exp2(s * scale_log2 - m_run) of a block, packed to the P^T operand layout
   // (pw[0..3]: keys 16 u + 4 hh + 0..3 with u = 0, pw[4..7] with u = 1), and the
-  // lane's share of the block's row sum, taken on the same bf16-rounded P that
-  // multiplies V
+  // lane's share of the block's row sum, added in fp32 before P is rounded to bf16
+  // for P V.  (A row sum of the rounded pairs through v_dot2_f32_bf16 against
+  // (1, 1) forms a serial chain that does not issue under the matrix cores' work
+  // on gfx950: with one pipeline step's MFMAs in flight it held the matrix cores
+  // at 68 % of their peak against 82 % with plain fp32 adds, two waves per SIMD.)
   auto exps = [&](const f32x16& sc, uint32_t* pw, float& ps) {
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
     const float neg_m = ALI ? neg_m0 + boff : neg_m0;
-    ps = 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      pw[e / 2] =
-          pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m)),
-                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], a.scale_log2, neg_m)));
-      ps = sum_bf16x2(pw[e / 2], ps);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], a.scale_log2, neg_m));
+      pw[e / 2] = pack_bf16x2(p0, p1);
+      ps0 += p0;
+      ps1 += p1;
     }
+    ps = ps0 + ps1;
   };
   // The reference m_run is only checked after the fact: a block is exponentiated
   // against the current reference, and only when some lane's partial row sum
@@ -553,27 +553,38 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     kf[1] = *reinterpret_cast<const u32x4*>(kl + 256);
     f32x16 sn = ebias;
     uint32_t pw[8];
-    float ps = 0.f;
+    float pe[16];
+    float ps0 = 0.f, ps1 = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       if (i + 2 < NK) kf[i + 2] = *reinterpret_cast<const u32x4*>(kl + 256 * (i + 2));
       sn = mfma32x32x16(kf[i], qb[i], sn);
 #pragma unroll
-      for (int e = EPK * i; e < EPK * (i + 1); e += 2)
-        pw[e / 2] =
-            pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], a.scale_log2, neg_m)),
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], a.scale_log2, neg_m)));
-      // row sum of the pairs packed one chunk earlier
+      for (int e = EPK * i; e < EPK * (i + 1); e += 2) {
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], a.scale_log2, neg_m));
+        pe[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], a.scale_log2, neg_m));
+        pw[e / 2] = pack_bf16x2(pe[e], pe[e + 1]);
+        pin(pw[e / 2]);
+      }
+      // row sum (fp32, two chains) of the exponentials formed one chunk earlier
       if (i > 0) {
 #pragma unroll
-        for (int e = EPK * (i - 1); e < EPK * i; e += 2) ps = sum_bf16x2(pw[e / 2], ps);
+        for (int e = EPK * (i - 1); e < EPK * i; e += 2) {
+          ps0 = e == 0 ? pe[e] : ps0 + pe[e];
+          ps1 = e == 0 ? pe[e + 1] : ps1 + pe[e + 1];
+        }
       }
-      pin(ps);
+      pin(ps0);
+      pin(ps1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int e = EPK * (NK - 1); e < 16; e += 2) ps = sum_bf16x2(pw[e / 2], ps);
+    for (int e = EPK * (NK - 1); e < 16; e += 2) {
+      ps0 += pe[e];
+      ps1 += pe[e + 1];
+    }
+    float ps = ps0 + ps1;
     settle(s_pend, pw, ps);
     const u32x4 pb0 = {pw[0], pw[1], pw[2], pw[3]};
     const u32x4 pb1 = {pw[4], pw[5], pw[6], pw[7]};
