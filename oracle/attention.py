@@ -38,6 +38,14 @@ R5  ALiBi: "The Stack Below the Stack (Part 2)", section 5, names ALiBi among th
     query h at absolute position p against key j becomes
     scale * q . k + slope_h * (j - p), i.e. a linear penalty on the distance to
     earlier keys for positive slopes.  No slopes means no bias.
+R6  Document masks: the same section names document masking among the mask
+    functions (a query sees only keys of its own document; several documents
+    packed into one sequence) without fixing a representation.  Reading: the
+    documents of a sequence are contiguous runs of positions, and the caller
+    gives every query row the half-open range [key_lo, key_hi) of key
+    positions of its own document; the row sees key j only if
+    key_lo <= j < key_hi, on top of the causal bound and the window.  No
+    ranges means every row's range is the whole sequence.
 """
 
 from __future__ import annotations
@@ -163,9 +171,23 @@ def _first_visible(seq_len: int, q_len: int, window: int) -> np.ndarray:
     return np.maximum(0, pos - window + 1)
 
 
+def _document_bounds(vis, first, key_ranges, t0, t1):
+    """Per-row key bounds with the document ranges of R6 applied: a row sees keys
+    first_i <= j < vis_i, narrowed to its own [key_lo, key_hi)."""
+    if key_ranges is None:
+        return vis, first
+    lo = np.asarray(key_ranges[0], dtype=np.int64)[t0:t1]
+    hi = np.asarray(key_ranges[1], dtype=np.int64)[t0:t1]
+    return np.minimum(vis, hi), np.maximum(first, lo)
+
+
 def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
-                  scale: float, causal: bool, page_size: int, window: int = 0, alibi=None):
+                  scale: float, causal: bool, page_size: int, window: int = 0, alibi=None,
+                  key_ranges=None):
     """Exact attention of every query row; returns (O [T, Hq, D], lse [T, Hq]).
+
+    ``key_ranges`` = (key_lo [T], key_hi [T]) restricts each query row to the
+    keys of its own document (R6).
 
     Streams one (sequence, key head) at a time so that memory stays bounded
     by one sequence's score matrix per query head -- the N^2 b warning of
@@ -191,6 +213,7 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
         vb = gather_sequence_kv(v_pool, block_tables[b], L, page_size)
         vis = _visible_counts(L, t1 - t0, causal)
         first = _first_visible(L, t1 - t0, window)
+        vis, first = _document_bounds(vis, first, key_ranges, t0, t1)      # R6
         pos = L - (t1 - t0) + np.arange(t1 - t0)                        # R2
         for h in range(Hq):
             kvh = h // G                                                # R1
@@ -204,7 +227,7 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
 
 def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
                        scale: float, causal: bool, page_size: int, rows, window: int = 0,
-                       alibi=None):
+                       alibi=None, key_ranges=None):
     """Same as :func:`attention_ref` for selected (token, head) pairs only.
 
     Used at full workload sizes, where the oracle computes sampled outputs one
@@ -228,6 +251,8 @@ def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q
         q_len = int(cu[b + 1] - cu[b])
         vis_all = _visible_counts(L, q_len, causal)
         first_all = _first_visible(L, q_len, window)
+        vis_all, first_all = _document_bounds(vis_all, first_all, key_ranges, int(cu[b]),
+                                              int(cu[b + 1]))                   # R6
         kb = gather_sequence_kv(k_pool, block_tables[b], L, page_size)
         vb = gather_sequence_kv(v_pool, block_tables[b], L, page_size)
         for i, t, h in items:

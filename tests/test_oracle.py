@@ -24,7 +24,7 @@ from scipy.special import logsumexp
 
 import oracle
 from oracle import attention as oa
-from workloads import bits, make_case, units
+from workloads import bits, document_ranges, make_case, units
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -39,10 +39,12 @@ def _bf16(x):
             for v in x.ravel()]
 
 
-def brute_attention(case, window=None, alibi=None):
+def brute_attention(case, window=None, alibi=None, key_ranges=None):
     """Loops over sequences, rows, heads and keys; math.exp and math.fsum only.
     With a sliding window w > 0 the row at position p takes keys j > p - w only;
-    with ALiBi slopes the score of key j gets slope_h * (j - p) added."""
+    with ALiBi slopes the score of key j gets slope_h * (j - p) added; with
+    document ranges (key_lo, key_hi) per row, row t takes keys key_lo[t] <= j <
+    key_hi[t] only."""
     w = case.window if window is None else window
     q = bits(case.q)
     kp = bits(case.k_pool)
@@ -70,6 +72,8 @@ def brute_attention(case, window=None, alibi=None):
                 for j in range(max(0, min(limit, L))):
                     if j < start:
                         continue
+                    if key_ranges is not None and not (key_ranges[0][t] <= j < key_ranges[1][t]):
+                        continue
                     page, slot = int(bt[b][j // ps]), j % ps
                     kv = _bf16(kp[page, slot, kvh])
                     bias = 0.0 if alibi is None else float(alibi[h]) * (j - pos)
@@ -86,12 +90,12 @@ def brute_attention(case, window=None, alibi=None):
     return out, lse
 
 
-def run_oracle(case, window=None, alibi=None):
+def run_oracle(case, window=None, alibi=None, key_ranges=None):
     return oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
                                 case.block_tables.numpy(), case.seq_lens_k.numpy(),
                                 case.cu_seqlens_q.numpy(), case.scale, case.causal,
                                 case.page_size, case.window if window is None else window,
-                                alibi)
+                                alibi, key_ranges)
 
 
 def assert_close(a, b, tol=1e-12):
@@ -115,6 +119,7 @@ small_shapes = st.fixed_dictionaries(dict(
     lens=st.lists(st.integers(0, 40), min_size=3, max_size=3),
     qlens=st.lists(st.integers(1, 5), min_size=3, max_size=3),
     window=st.sampled_from([0, 0, 1, 2, 5, 17]),
+    docs=st.sampled_from([0, 0, 1, 3]),
 ))
 
 
@@ -133,8 +138,9 @@ def _small_case(p):
 @given(small_shapes)
 def test_oracle_matches_brute_force(p):
     case = _small_case(p)
-    o, lse = run_oracle(case)
-    ob, lseb = brute_attention(case)
+    kr = document_ranges(case.seq_lens, case.q_lens, p["docs"], p["seed"]) if p["docs"] else None
+    o, lse = run_oracle(case, key_ranges=kr)
+    ob, lseb = brute_attention(case, key_ranges=kr)
     assert_close(o, ob)
     assert_close(lse, lseb)
 
@@ -710,3 +716,98 @@ def test_per_sequence_oracle_helper_equals_the_whole_pool_oracle(split_kv_heads,
     o2, l2 = oracle_by_sequence(case, kp, vp, split_kv_heads=split_kv_heads, alibi=slopes)
     assert np.array_equal(o1, o2)
     assert np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# document masks (R6)
+# ----------------------------------------------------------------------------
+
+def _doc_case(causal=True, seed=91, window=0):
+    lens, ql = [40, 23, 0, 31], [7, 23, 3, 40]
+    case = make_case("doc", seq_lens=lens, q_lens=ql, Hq=4, Hkv=2, D=8, page_size=4,
+                     seed=seed, causal=causal, window=window,
+                     num_pages=sum(-(-L // 4) for L in lens) + 2)
+    return case, document_ranges(lens, ql, 4, seed)
+
+
+@pytest.mark.parametrize("causal,window,alibi", [(True, 0, False), (False, 0, False),
+                                                 (True, 6, False), (True, 0, True),
+                                                 (False, 5, True)])
+def test_document_ranges_match_brute_force(causal, window, alibi):
+    case, kr = _doc_case(causal, window=window)
+    slopes = np.array([0.25, -0.1, 0.5, 0.0]) if alibi else None
+    o, lse = run_oracle(case, alibi=slopes, key_ranges=kr)
+    ob, lb = brute_attention(case, alibi=slopes, key_ranges=kr)
+    assert_close(o, ob)
+    assert_close(lse, lb)
+    # some rows keep only part of their causal keys, some see nothing (before the
+    # first key of their sequence)
+    assert np.isneginf(lse).any() and np.isfinite(lse).any()
+
+
+def test_document_row_equals_attention_over_its_documents_keys():
+    """A row of document [s, e) equals unmasked attention over that document's keys
+    alone (the slice s .. min(e, p + 1) for a causal row at position p)."""
+    case, (lo, hi) = _doc_case(True, seed=92)
+    o, lse = run_oracle(case, key_ranges=(lo, hi))
+    q = oracle.bf16_bits_to_f64(bits(case.q))
+    cu = case.cu_seqlens_q.numpy()
+    for b, L in enumerate(case.seq_lens):
+        k = oracle.gather_sequence_kv(bits(case.k_pool), case.block_tables[b].numpy(), L, 4)
+        v = oracle.gather_sequence_kv(bits(case.v_pool), case.block_tables[b].numpy(), L, 4)
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t, p = int(cu[b]) + i, L - n + i
+            s0, s1 = int(lo[t]), min(int(hi[t]), p + 1)
+            for h in range(case.Hq):
+                if s1 <= s0:
+                    assert np.isneginf(lse[t, h]) and (o[t, h] == 0).all()
+                    continue
+                ks, vs = k[s0:s1, h // 2], v[s0:s1, h // 2]
+                s = case.scale * ks @ q[t, h]
+                w = np.exp(s - s.max())
+                assert np.abs(o[t, h] - w @ vs / w.sum()).max() < 1e-12
+                assert abs(lse[t, h] - (s.max() + np.log(w.sum()))) < 1e-12
+
+
+def test_one_document_per_sequence_changes_nothing():
+    case, _ = _doc_case(True, seed=93)
+    kr = document_ranges(case.seq_lens, case.q_lens, 1, 93)
+    o1, l1 = run_oracle(case)
+    o2, l2 = run_oracle(case, key_ranges=kr)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("mutant,causal", [("hi_inclusive", False), ("lo_ignored", True),
+                                           ("lo_off_by_one", True), ("lo_ignored", False)])
+def test_planted_document_mistakes_are_caught(mutant, causal):
+    """(A causal row's own position lies in its document, so key_hi binds only
+    without the causal mask.)"""
+    case, (lo, hi) = _doc_case(causal, seed=94)
+    ob, lb = brute_attention(case, key_ranges=(lo, hi))
+    if mutant == "hi_inclusive":
+        kr = (lo, hi + 1)
+    elif mutant == "lo_ignored":
+        kr = (np.zeros_like(lo), hi)
+    else:
+        kr = (lo + 1, hi)
+    o, l = run_oracle(case, key_ranges=kr)
+    with pytest.raises(AssertionError):
+        assert_close(o, ob)
+        assert_close(l, lb)
+
+
+def test_document_ranges_layout():
+    """The generator's ranges: each row's range holds its own position (rows at
+    negative positions get an empty range), ranges tile every sequence."""
+    lens, ql = [50, 9, 0, 300], [10, 9, 2, 1]
+    lo, hi = document_ranges(lens, ql, 5, 7)
+    t = 0
+    for L, n in zip(lens, ql):
+        for i in range(n):
+            p = L - n + i
+            if p < 0:
+                assert lo[t] == hi[t] == 0
+            else:
+                assert 0 <= lo[t] <= p < hi[t] <= L
+            t += 1

@@ -36,7 +36,7 @@ import numpy as np
 import torch
 
 __all__ = ["PagedCase", "make_case", "make_config", "config_shape", "CONFIGS",
-           "CONFIG_ORDER", "bits", "units", "random_e4m3_codes"]
+           "CONFIG_ORDER", "bits", "units", "random_e4m3_codes", "document_ranges"]
 
 BF16_NAN_BITS = 0x7FC0
 TAIL_POISON = 3.0e4
@@ -235,6 +235,34 @@ def make_case(name, seq_lens=None, Hq=8, Hkv=2, D=64, page_size=16, num_pages=No
         start_pos=start_pos, num_splits=num_splits, window=int(window),
         meta=dict(seed=seed, std_q=std_q, std_kv=std_kv), host_seq_lens=list(total),
     )
+
+
+def document_ranges(seq_lens, q_lens, docs_per_seq, seed: int):
+    """Seeded packed-document layout: every sequence's positions 0 .. L-1 are cut
+    into up to docs_per_seq contiguous documents at random boundaries, and each query
+    row (the last q_len positions of its sequence) gets the half-open key range
+    [key_lo, key_hi) of the document holding its position.  Returns host int32
+    arrays (key_lo, key_hi) of length sum(q_lens).  Structure only: no attention
+    arithmetic."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lo_all, hi_all = [], []
+    for L, n in zip(seq_lens, q_lens):
+        L, n = int(L), int(n)
+        k = max(1, min(int(docs_per_seq), L)) if L > 0 else 1
+        cuts = np.sort(rng.choice(np.arange(1, L), size=k - 1, replace=False)) if k > 1 \
+            else np.zeros(0, dtype=np.int64)
+        starts = np.concatenate([[0], cuts]).astype(np.int64)
+        ends = np.concatenate([cuts, [max(L, 0)]]).astype(np.int64)
+        for i in range(n):
+            p = L - n + i                       # the row's absolute position
+            d = int(np.searchsorted(starts, p, side="right") - 1) if p >= 0 else -1
+            if d < 0:                           # a row before the sequence's first key
+                lo_all.append(0)
+                hi_all.append(0)
+            else:
+                lo_all.append(int(starts[d]))
+                hi_all.append(int(ends[d]))
+    return np.asarray(lo_all, dtype=np.int32), np.asarray(hi_all, dtype=np.int32)
 
 
 def _mixed_lengths(seed):
