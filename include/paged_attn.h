@@ -389,6 +389,23 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * lse outputs include the bias.  The bias composes with the causal bound and the
  * window.
  *
+ * Document masks: the same section names document masking among the mask
+ * functions (several documents packed into one sequence, a query seeing only its
+ * own document's keys), again without a representation.  This library's: the
+ * documents of a sequence are contiguous runs of positions, and the caller gives
+ * every query row the half-open range [key_lo, key_hi) of key positions of its
+ * own document (absolute positions of its sequence, as seq_lens_k counts them);
+ * the row sees key j only if key_lo <= j < key_hi, on top of the causal bound and
+ * the window.  A decode row (the last position of its sequence) needs only key_lo.
+ * Ranges are data, not checked on the device: a range outside 0 .. seq_len masks
+ * accordingly.  Document masks select the prefill kernel's general variant; the
+ * host planner paged_attn_prefill_plan_splits does not see them.
+ *
+ * Together the causal bound, the window and the document range are one mask
+ * predicate per row, lo <= key <= lim, that the general variant applies to the
+ * blocks where some row's bound falls and uses to skip the key tiles outside every
+ * row's range.
+ *
  * The _ex entry points take every option of an operation in one struct; the
  * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
  * negative window PA_ERR_SHAPE.
@@ -411,6 +428,8 @@ typedef struct {
   void* kernel_start_event;   /* NULL, or a created hipEvent_t (timing enabled) that the
                                  partition kernel's dispatch stamps with its start       */
   void* kernel_stop_event;    /* NULL, or a hipEvent_t stamped with that kernel's end     */
+  const int32_t* key_lo;      /* NULL, or device [B] int32: first key of the document the
+                                 decode row belongs to (document masks above)            */
 } pa_decode_opts;
 
 typedef struct {
@@ -425,6 +444,9 @@ typedef struct {
   void* kernel_start_event;   /* NULL, or a created hipEvent_t (timing enabled) that the
                                  prefill kernel's dispatch stamps with its start         */
   void* kernel_stop_event;    /* NULL, or a hipEvent_t stamped with that kernel's end     */
+  const int32_t* key_lo;      /* NULL, or device [Tq] int32: key_lo of every query row    */
+  const int32_t* key_hi;      /* NULL, or device [Tq] int32: key_hi of every query row
+                                 (both or neither; document masks above)                 */
 } pa_prefill_opts;
 
 /*

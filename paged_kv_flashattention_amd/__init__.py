@@ -309,7 +309,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                       stream=None, validate: bool = False, window_left: int = 0,
-                      alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
+                      alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
+                      key_lo: Optional[torch.Tensor] = None):
     """Decode attention: q [B, Hq, D] against each sequence's paged history.
 
     ``max_seq_len`` is a host-side bound of ``seq_lens``; if omitted it is read
@@ -319,11 +320,12 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
     ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
     ``kernel_events`` = (start, stop) torch.cuda.Event pair (timing enabled, recorded
     once already) that the partition kernel's dispatch stamps with its own start and
-    end (see pa_decode_opts).
+    end (see pa_decode_opts).  ``key_lo`` (int32 [B] on the device): document masks,
+    the first key of the document each decode row belongs to.
     """
     return _decode(None, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
                    num_splits, out, lse, workspace, return_lse, stream, validate, window_left,
-                   alibi_slopes, kernel_events)
+                   alibi_slopes, kernel_events, key_lo)
 
 
 def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
@@ -332,13 +334,14 @@ def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_sca
                           lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                           stream=None, validate: bool = False, window_left: int = 0,
-                          alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
+                          alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
+                          key_lo: Optional[torch.Tensor] = None):
     """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
     decode(code) * k_scale, values for decode(code) * v_scale.  Arguments and
     results are paged_attn_decode's."""
     return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
                    softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
-                   stream, validate, window_left, alibi_slopes, kernel_events)
+                   stream, validate, window_left, alibi_slopes, kernel_events, key_lo)
 
 
 def _window(window_left) -> int:
@@ -378,7 +381,7 @@ def _events(kernel_events):
 
 def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
             num_splits, out, lse, workspace, return_lse, stream, validate, window_left=0,
-            alibi_slopes=None, kernel_events=None):
+            alibi_slopes=None, kernel_events=None, key_lo=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -420,9 +423,20 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
         _need(lse, "lse", torch.float32, 2, dev)
     lib = load_library()
     alibi_ptr = _alibi(alibi_slopes, Hq, dev)
+    lo_ptr = None
+    if key_lo is not None:
+        _need(key_lo, "key_lo", torch.int32, 1, dev)
+        if key_lo.shape[0] != B:
+            raise ValueError(f"key_lo must have B={B} entries")
+        if validate:
+            lo_h, lens_h = key_lo.cpu(), seq_lens.cpu()
+            if bool((lo_h < 0).any()) or bool((lo_h > lens_h).any()):
+                raise ValueError("key_lo must lie in [0, seq_lens]")
+        lo_ptr = key_lo.data_ptr()
     ev0, ev1 = _events(kernel_events)
     opts = _lib.DecodeOpts(int(num_splits), window_left, 0 if scales is None else 1,
-                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr, ev0, ev1)
+                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr, ev0, ev1,
+                           lo_ptr)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
     if workspace is not None:
@@ -434,7 +448,7 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
-        if window_left or alibi_ptr is not None or ev0 is not None:
+        if window_left or alibi_ptr is not None or ev0 is not None or lo_ptr is not None:
             _check(lib.paged_attn_decode_ex(*head, int(max_seq_len), ctypes.byref(opts),
                                             *tail[2:]))
         elif scales is None:
@@ -516,7 +530,8 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                               out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                               stream=None, validate: bool = False, window_left: int = 0,
-                              alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None):
+                              alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
+                              key_ranges=None):
     """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
 
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
@@ -524,10 +539,13 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
     restricts the row at position p to keys j > p - w (sliding window);
     ``alibi_slopes`` (float32 [Hq] on the device) adds slope_h * (j - p) to the scores.
     ``kernel_events`` as paged_attn_decode's, for the prefill kernel.
+    ``key_ranges`` = (key_lo, key_hi), int32 [Tq] each on the device: document masks,
+    row t sees keys key_lo[t] <= j < key_hi[t] of its sequence only.
     """
     return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
                     softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate,
-                    window_left, alibi_slopes, kernel_events=kernel_events)
+                    window_left, alibi_slopes, kernel_events=kernel_events,
+                    key_ranges=key_ranges)
 
 
 def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
@@ -539,14 +557,14 @@ def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, b
                                   return_lse: bool = False, stream=None,
                                   validate: bool = False, window_left: int = 0,
                                   alibi_slopes: Optional[torch.Tensor] = None,
-                                  kernel_events=None):
+                                  kernel_events=None, key_ranges=None):
     """Ragged prefill over FP8 E4M3 pools (uint8 codes; keys stand for decode(code) *
     k_scale, values for decode(code) * v_scale), through paged_attn_prefill_ex.
     ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass)."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
                     validate, window_left, alibi_slopes, _scales(k_scale, v_scale),
-                    kernel_events)
+                    kernel_events, key_ranges)
 
 
 def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:
@@ -586,17 +604,17 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
                                      return_lse: bool = False, stream=None,
                                      validate: bool = False, window_left: int = 0,
                                      alibi_slopes: Optional[torch.Tensor] = None,
-                                     kernel_events=None):
+                                     kernel_events=None, key_ranges=None):
     """Ragged prefill with long key ranges cut into at most ``num_splits`` parts
     (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
-                    validate, window_left, alibi_slopes, None, kernel_events)
+                    validate, window_left, alibi_slopes, None, kernel_events, key_ranges)
 
 
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
              causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
-             alibi_slopes=None, scales=None, kernel_events=None):
+             alibi_slopes=None, scales=None, kernel_events=None, key_ranges=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -646,9 +664,26 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             _ptr(seq_lens_k), _ptr(block_tables), B, Tq, int(max_q_len), block_tables.shape[1],
             P, ps, Hq, Hkv, D, float(softmax_scale), 1 if causal else 0)
     alibi_ptr = _alibi(alibi_slopes, Hq, dev)
+    lo_ptr = hi_ptr = None
+    if key_ranges is not None:
+        if len(key_ranges) != 2:
+            raise ValueError("key_ranges must be a (key_lo, key_hi) pair")
+        key_lo, key_hi = key_ranges
+        _need(key_lo, "key_lo", torch.int32, 1, dev)
+        _need(key_hi, "key_hi", torch.int32, 1, dev)
+        if key_lo.shape[0] != Tq or key_hi.shape[0] != Tq:
+            raise ValueError(f"key_lo and key_hi must have Tq={Tq} entries")
+        if validate:
+            cu = cu_seqlens_q.cpu()
+            lens = seq_lens_k.cpu()
+            row_len = torch.repeat_interleave(lens, (cu[1:] - cu[:-1]).long())
+            lo_h, hi_h = key_lo.cpu(), key_hi.cpu()
+            if bool((lo_h < 0).any()) or bool((hi_h > row_len).any()):
+                raise ValueError("key ranges must lie in [0, seq_lens_k] of their sequence")
+        lo_ptr, hi_ptr = key_lo.data_ptr(), key_hi.data_ptr()
     ev0, ev1 = _events(kernel_events)
     general = (bool(window_left) or alibi_ptr is not None or scales is not None
-               or ev0 is not None)
+               or ev0 is not None or lo_ptr is not None)
     if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
@@ -666,7 +701,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         elif general:
             ks, vs = scales if scales is not None else (1.0, 1.0)
             opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
-                                    0 if scales is None else 1, ks, vs, ev0, ev1)
+                                    0 if scales is None else 1, ks, vs, ev0, ev1, lo_ptr, hi_ptr)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

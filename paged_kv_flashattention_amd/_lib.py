@@ -23,7 +23,8 @@ class DecodeOpts(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
-                ("kernel_start_event", ctypes.c_void_p), ("kernel_stop_event", ctypes.c_void_p)]
+                ("kernel_start_event", ctypes.c_void_p), ("kernel_stop_event", ctypes.c_void_p),
+                ("key_lo", ctypes.c_void_p)]
 
 
 class PrefillOpts(ctypes.Structure):
@@ -32,7 +33,8 @@ class PrefillOpts(ctypes.Structure):
                 ("num_splits", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("kernel_start_event", ctypes.c_void_p),
-                ("kernel_stop_event", ctypes.c_void_p)]
+                ("kernel_stop_event", ctypes.c_void_p), ("key_lo", ctypes.c_void_p),
+                ("key_hi", ctypes.c_void_p)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)

@@ -105,7 +105,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 int32_t B, int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
-                float v_scale = 1.f, int32_t window = 0, const float* alibi = nullptr) {
+                float v_scale = 1.f, int32_t window = 0, const float* alibi = nullptr,
+                const int32_t* key_lo = nullptr) {
   if (B < 0 || max_seq_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
@@ -120,6 +121,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
   if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u))
     return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
+  if (key_lo && (reinterpret_cast<uintptr_t>(key_lo) & 3u))
+    return fail(PA_ERR_MISALIGNED, "%s: key_lo must be 4-byte aligned", what);
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   // with a window every row walks at most window + 31 keys (its lower bound rounded
@@ -145,6 +148,7 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.v_scale = fp8 ? v_scale : 1.f;
   a.window = window;
   a.alibi = alibi;
+  a.key_lo = key_lo;
   return PA_OK;
 }
 
@@ -197,12 +201,13 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
                 float k_scale, float v_scale, void* stream, int32_t window = 0,
-                const float* alibi = nullptr, const pa::KernelEvents& ev = pa::KernelEvents()) {
+                const float* alibi = nullptr, const pa::KernelEvents& ev = pa::KernelEvents(),
+                const int32_t* key_lo = nullptr) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
                        num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
-                       num_splits, fp8, k_scale, v_scale, window, alibi);
+                       num_splits, fp8, k_scale, v_scale, window, alibi, key_lo);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
@@ -282,7 +287,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
                  const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
-                 float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents()) {
+                 float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
+                 const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -301,6 +307,11 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     return fail(PA_ERR_SHAPE, "%s: softmax scale must be positive and finite", what);
   if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u))
     return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
+  if (!key_lo != !key_hi)
+    return fail(PA_ERR_NULL, "%s: key_lo and key_hi must both be given or both be NULL", what);
+  if ((key_lo && (reinterpret_cast<uintptr_t>(key_lo) & 3u)) ||
+      (key_hi && (reinterpret_cast<uintptr_t>(key_hi) & 3u)))
+    return fail(PA_ERR_MISALIGNED, "%s: key_lo and key_hi must be 4-byte aligned", what);
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   if (max_q_len > Tq) max_q_len = Tq;
@@ -336,6 +347,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.alibi = alibi;
   a.kv_fp8 = fp8 ? 1 : 0;
   a.v_scale = fp8 ? v_scale : 1.f;
+  a.key_lo = key_lo;
+  a.key_hi = key_hi;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -729,7 +742,8 @@ int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k
                      max_pages, num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
                      opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
                      opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
-                     stream, opts->window_left, opts->alibi_slopes, events_of(opts));
+                     stream, opts->window_left, opts->alibi_slopes, events_of(opts),
+                     opts->key_lo);
 }
 
 size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -754,7 +768,8 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       block_tables, B, Tq, max_q_len, max_pages, num_pages, page_size, Hq, Hkv,
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
                       workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
-                      opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts));
+                      opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts),
+                      opts->key_lo, opts->key_hi);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

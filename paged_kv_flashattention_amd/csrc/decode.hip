@@ -230,10 +230,12 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   int L = a.seq_lens[b];
   const int cap = a.max_pages * a.page_size;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  // sliding window: the row (position L - 1) sees keys lo .. L - 1; the walk starts
-  // at lo rounded down to a chunk, so chunks keep their page alignment, and the keys
-  // below lo are masked
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  // sliding window and document: the row (position L - 1) sees keys lo .. L - 1 (the
+  // window's start, or its document's start if later); the walk starts at lo rounded
+  // down to a chunk, so chunks keep their page alignment, and the keys below lo are
+  // masked
+  int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  if (a.key_lo) lo = max(lo, min(L, a.key_lo[b]));
   const int k_begin = (lo & ~31) + split * a.part_len;
   const int k_end = min(L, k_begin + a.part_len);
   const int n_chunks = k_end > k_begin ? (k_end - k_begin + 31) >> 5 : 0;

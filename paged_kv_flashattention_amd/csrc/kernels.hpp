@@ -27,6 +27,7 @@ struct DecodeArgs {
   float v_scale;                 // value of one V code unit (1 for bf16 pools)
   int window;                    // sliding window: keys j >= seq_len - window only (0: none)
   const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
+  const int32_t* key_lo;         // [B] first key of the row's document, or null (none)
 };
 
 struct ReduceArgs {
@@ -75,6 +76,8 @@ struct PrefillArgs {
   int part_min;                  // 64-key tiles per part at least
   float* part_o;                 // [Tq * Hq, S, D] partial outputs        (S > 1)
   float* part_lse;               // [Tq * Hq, S] partial natural-log lse   (S > 1)
+  const int32_t* key_lo;         // [Tq] document range [key_lo, key_hi) of each query
+  const int32_t* key_hi;         //   row, or both null (no document masks)
 };
 
 // Optional events stamped with one kernel's own start and end: the dispatch

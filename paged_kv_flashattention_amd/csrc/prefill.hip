@@ -35,13 +35,36 @@ constexpr float kSumLimit = 256.f;     // 2^kRescaleSlack: bound on a lane's blo
 #define PF_W8_MIN 512
 #endif
 
+// Document masks: the smallest key_lo and the largest key_hi over query rows
+// r0 .. r0 + rows - 1 of the sequence whose rows start at token t0, reduced over
+// one wave (each lane reads every 64th row).  The union of those rows' documents
+// lies in [lo, hi).
+struct DocSpan {
+  int lo, hi;
+};
+__device__ __forceinline__ DocSpan pf_doc_span(const PrefillArgs& a, int t0, int r0, int rows,
+                                               int lane) {
+  int lo = INT_MAX, hi = INT_MIN;
+  for (int r = lane; r < rows; r += 64) {
+    lo = min(lo, a.key_lo[t0 + r0 + r]);
+    hi = max(hi, a.key_hi[t0 + r0 + r]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  return DocSpan{__builtin_amdgcn_readfirstlane(lo), __builtin_amdgcn_readfirstlane(hi)};
+}
+
 // The key tiles a query tile needs and how many parts they are cut into.  A
 // query tile of rows r0 .. r0 + rows - 1 of a sequence with L keys and q_len query
 // rows needs keys up to k_lim - 1 (causal: up to its last row's position) and,
-// with a sliding window, from its first row's lower bound on: tiles first .. n - 1.
-// With key splitting on (S > 1) those tiles are cut into min(S, count / part_min)
-// parts of consecutive tiles (at least one), each computed by its own work-group;
-// the prefill merge recomputes the same count for every row.
+// with a sliding window, from its first row's lower bound on; with document masks
+// only keys inside the span of its rows' documents: tiles first .. n - 1.  With key
+// splitting on (S > 1) those tiles are cut into min(S, count / part_min) parts of
+// consecutive tiles (at least one), each computed by its own work-group; the prefill
+// merge recomputes the same count for every row.
 struct PfTiles {
   int first;   // first 64-key tile
   int n;       // one past the last tile
@@ -50,14 +73,19 @@ struct PfTiles {
 
 template <bool GEN>
 __device__ __forceinline__ PfTiles pf_tiles(const PrefillArgs& a, int L, int q_len, int r0,
-                                            int bm) {
+                                            int bm, int t0, int lane) {
   const int rows = min(bm, q_len - r0);
   int k_lim = L;
   if (a.causal) k_lim = min(L, max(0, L - q_len + r0 + rows));
+  // only the general variant (window, ALiBi, documents) sees a window or documents
+  int k_lo = GEN && a.window > 0 ? max(0, L - q_len + r0 - a.window + 1) : 0;
+  if (GEN && a.key_lo) {
+    const DocSpan d = pf_doc_span(a, t0, r0, min(rows, a.Tq - t0 - r0), lane);
+    k_lim = min(k_lim, max(0, d.hi));
+    k_lo = max(k_lo, min(d.lo, k_lim));
+  }
   PfTiles t;
   t.n = (k_lim + kPfBN - 1) / kPfBN;
-  // only the general variant (window, ALiBi) sees a window
-  const int k_lo = GEN && a.window > 0 ? max(0, L - q_len + r0 - a.window + 1) : 0;
   t.first = min(k_lo / kPfBN, t.n);
   t.parts = a.S > 1 ? max(1, min(a.S, (t.n - t.first) / a.part_min)) : 1;
   return t;
@@ -271,7 +299,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // keys past this work-group's last row are never needed; with key splitting this
   // work-group covers tiles tile_lo .. tile_hi - 1 of them
   const int shift = L - q_len;                 // position of row r is shift + r
-  const PfTiles tw = pf_tiles<GEN>(a, L, q_len, r_wg, kPfBM);
+  const PfTiles tw = pf_tiles<GEN>(a, L, q_len, r_wg, kPfBM, t0, lane);
   if (part >= tw.parts) return;
   const int tile_lo = tw.first + part * (tw.n - tw.first) / tw.parts;
   const int tile_hi = tw.first + (part + 1) * (tw.n - tw.first) / tw.parts;
@@ -281,11 +309,33 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int my_row = r_w + col;
   const bool row_ok = my_row < q_len && t0 + my_row < a.Tq;
   const int my_pos = shift + my_row;          // causal: keys <= my_pos are visible
-  const int w_pos_min = shift + r_w;
-  const int lim = a.causal ? min(L - 1, my_pos) : L - 1;   // last visible key
-  // sliding window: first visible key of this row, and the largest of the wave's
-  const int lo_row = GEN && a.window > 0 ? my_pos - a.window + 1 : INT_MIN;
-  const int w_lo_max = GEN && a.window > 0 ? shift + r_w + 31 - a.window + 1 : INT_MIN;
+  // Which keys this row sees (the mask, as one predicate): lo_row <= key <= lim.
+  // lim is the sequence end, the causal bound and (documents) its document's end;
+  // lo_row the window's start and (documents) its document's start.  w_lim_min and
+  // w_lo_max are the smallest lim and the largest lo_row among the wave's rows: a
+  // block needs the per-key mask only where one of them falls inside it.
+  int lim = a.causal ? min(L - 1, my_pos) : L - 1;         // last visible key
+  int lo_row = GEN && a.window > 0 ? my_pos - a.window + 1 : INT_MIN;
+  int w_lim_min = a.causal ? shift + r_w : L - 1;
+  int w_lo_max = GEN && a.window > 0 ? shift + r_w + 31 - a.window + 1 : INT_MIN;
+  int w_hi_max = L;                            // one past the wave's last visible key
+  if (GEN && a.key_lo) {
+    // rows past the query run take neutral bounds (their outputs are not written)
+    const int dlo = row_ok ? a.key_lo[t0 + my_row] : 0;
+    const int dhi = row_ok ? a.key_hi[t0 + my_row] : L;
+    lim = min(lim, dhi - 1);
+    lo_row = max(lo_row, dlo);
+    int mn = lim, mx = lo_row, hx = row_ok ? min(lim + 1, L) : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = min(mn, __shfl_xor(mn, off));
+      mx = max(mx, __shfl_xor(mx, off));
+      hx = max(hx, __shfl_xor(hx, off));
+    }
+    w_lim_min = __builtin_amdgcn_readfirstlane(mn);
+    w_lo_max = __builtin_amdgcn_readfirstlane(mx);
+    w_hi_max = __builtin_amdgcn_readfirstlane(hx);
+  }
   // ALiBi, slope_h * (key - row position), in two parts that cost nothing per score:
   // the key's offset within its block (8 j + 4 hh + i for element 4 j + i) is the
   // same for every block, so it is the initial value of the score accumulator
@@ -452,8 +502,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // right after its scores are formed and before they are used.
   auto mask = [&](f32x16& sc, int kb0) {
     if (ALI) boff = slope_log2 * (float)(kb0 - my_pos);
-    const bool need =
-        (kb0 + 32 > L) || (a.causal && kb0 + 31 > w_pos_min) || (GEN && kb0 < w_lo_max);
+    const bool need = (kb0 + 32 > L) || (kb0 + 31 > w_lim_min) || (GEN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -629,8 +678,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // to the other waves.  The steady loop below is the same for every wave; only
   // where a wave's blocks end does it take the short tail.
   const int w_last = min(r_w + 31, q_len - 1);              // last valid row of the wave
-  const int w_key_end = __builtin_amdgcn_readfirstlane(
-      !a.causal ? L : (w_last < r_w ? 0 : min(L, shift + w_last + 1)));
+  const int w_key_end = __builtin_amdgcn_readfirstlane(min(
+      w_hi_max, !a.causal ? L : (w_last < r_w ? 0 : min(L, shift + w_last + 1))));
   // finish the pending block (P from its scores, P V from V tile vp, block kbp)
   auto finish = [&](f32x16& sp, const uint16_t* vp, int kbp) {
     uint32_t pw[8];
@@ -771,8 +820,9 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   int L = a.seq_lens_k[b];
   const int cap = a.max_pages * a.page_size;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const PfTiles tw = a.window > 0 ? pf_tiles<true>(a, L, q_len, r_wg, bm)
-                                   : pf_tiles<false>(a, L, q_len, r_wg, bm);
+  const PfTiles tw = a.window > 0 || a.key_lo
+                        ? pf_tiles<true>(a, L, q_len, r_wg, bm, t0, threadIdx.x & 63)
+                        : pf_tiles<false>(a, L, q_len, r_wg, bm, t0, threadIdx.x & 63);
   if (tw.parts <= 1) return;
   const int c = threadIdx.x % CH;
   for (int pass = 0; pass < kMergePasses; ++pass) {
@@ -852,12 +902,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   if (a.kv_fp8) {
     if (a.alibi) return launch_prefill_w<D, W, true, true, true>(a, stream, ev);
-    return a.window > 0 ? launch_prefill_w<D, W, true, true, false>(a, stream, ev)
-                        : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
+    return a.window > 0 || a.key_lo ? launch_prefill_w<D, W, true, true, false>(a, stream, ev)
+                                    : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
   }
   if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
-  return a.window > 0 ? launch_prefill_w<D, W, true, false, false>(a, stream, ev)
-                      : launch_prefill_w<D, W, false, false, false>(a, stream, ev);
+  return a.window > 0 || a.key_lo ? launch_prefill_w<D, W, true, false, false>(a, stream, ev)
+                                  : launch_prefill_w<D, W, false, false, false>(a, stream, ev);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the

@@ -28,13 +28,13 @@ def pools_after_write(case):
                                case.block_tables.cpu().numpy(), case.page_size)
 
 
-def oracle_full(case, kp=None, vp=None, causal=None, alibi=None):
+def oracle_full(case, kp=None, vp=None, causal=None, alibi=None, key_ranges=None):
     if kp is None:
         kp, vp = pools_after_write(case)
     return oracle.attention_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
                                 case.seq_lens_k.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
                                 case.scale, case.causal if causal is None else causal,
-                                case.page_size, case.window, alibi)
+                                case.page_size, case.window, alibi, key_ranges)
 
 
 def oracle_rows(case, rows, kp=None, vp=None, alibi=None):
