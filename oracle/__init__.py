@@ -45,4 +45,5 @@ from .fp8 import (  # noqa: F401
     quantize_ref,
     dequantize_pool,
     kv_write_fp8_ref,
+    page_scales,
 )

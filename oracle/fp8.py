@@ -14,6 +14,10 @@ F1  Format: the OCP 8-bit E4M3 ("fn") encoding -- 1 sign bit, 4 exponent bits
     normal 2^-6, smallest subnormal 2^-9.
 F2  Scaling: one float32 scale per pool (k_scale for K, v_scale for V), given
     by the caller.  A stored code c stands for decode(c) * scale.
+F2' Finer scaling (an alternative to F2 the caller chooses): one float32 scale per
+    (page, KV head), arrays k_scales / v_scales of shape [pages, Hkv].  A code
+    in page p, head h stands for decode(c) * scales[p, h]; a new token's row is
+    quantised with the scale of the page and head it is written to.
 F3  Quantisation: y = float32(x) * float32(1 / scale) in float32 arithmetic,
     clamped to [-448, 448], then rounded to the nearest E4M3 value, ties to the
     even code (the IEEE default rounding).
@@ -29,7 +33,7 @@ import numpy as np
 from .attention import bf16_bits_to_f64
 
 __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_ref", "kv_write_fp8_ref",
-           "dequantize_pool"]
+           "dequantize_pool", "page_scales"]
 
 E4M3_MAX = 448.0
 
@@ -73,36 +77,53 @@ def e4m3_encode(x) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
-def quantize_ref(x, scale: float) -> np.ndarray:
+def page_scales(scales, ndim: int = 4) -> np.ndarray:
+    """Per-(page, KV head) scales [pages, Hkv] (F2') shaped to broadcast over a pool
+    [pages, page_size, Hkv, D]; a scalar (F2) is returned as a float32 scalar."""
+    s = np.asarray(scales, dtype=np.float32)
+    if s.ndim == 0:
+        return s
+    if s.ndim != 2:
+        raise ValueError("per-page scales must be [pages, Hkv]")
+    return s[:, None, :, None] if ndim == 4 else s
+
+
+def quantize_ref(x, scale) -> np.ndarray:
     """E4M3 codes of bf16 values x (uint16 bit patterns or floats) under a pool
-    scale (F2, F3)."""
+    scale (F2, F3), or under per-element scales broadcast against x (F2'): the
+    reciprocal of each scale is taken in float32, as for a pool scale."""
     xf = bf16_bits_to_f64(x).astype(np.float32)
-    inv = np.float32(1.0) / np.float32(scale)
+    inv = np.float32(1.0) / np.asarray(scale, dtype=np.float32)
     y = (xf * inv).astype(np.float32)
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return e4m3_encode(y.astype(np.float64))
 
 
-def dequantize_pool(codes, scale: float) -> np.ndarray:
-    """float64 values a code pool stands for: decode(c) * scale (F2)."""
-    return e4m3_decode(codes) * float(np.float32(scale))
+def dequantize_pool(codes, scale) -> np.ndarray:
+    """float64 values a code pool [pages, page_size, Hkv, D] stands for:
+    decode(c) * scale, with one scale per pool (F2) or per (page, KV head) (F2')."""
+    return e4m3_decode(codes) * page_scales(scale).astype(np.float64)
 
 
 def kv_write_fp8_ref(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
-                     page_size: int, k_scale: float, v_scale: float):
+                     page_size: int, k_scale, v_scale):
     """The page write of "Inside Ion", "IonAttention in One Paragraph" (token t of
     sequence b goes to page block_tables[b][pos // page_size], slot pos % page_size)
     with the quantisation fused in ("The Stack Below the Stack (Part 2)", 2.1).
-    Pools are uint8 code arrays [P, page_size, Hkv, D]; returns new arrays."""
+    Pools are uint8 code arrays [P, page_size, Hkv, D]; returns new arrays.  The
+    scales are one float per pool (F2), or [P, Hkv] arrays (F2'): token t's heads are
+    then quantised with the scales of the page it lands in."""
     kp = np.array(k_pool, dtype=np.uint8, copy=True)
     vp = np.array(v_pool, dtype=np.uint8, copy=True)
-    kq = quantize_ref(k_new, k_scale)
-    vq = quantize_ref(v_new, v_scale)
+    ks, vs = np.asarray(k_scale, np.float32), np.asarray(v_scale, np.float32)
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
     cu = np.asarray(cu_new)
     for b in range(len(cu) - 1):
         for t in range(int(cu[b]), int(cu[b + 1])):
             pos = int(start_pos[b]) + (t - int(cu[b]))
             page = int(block_tables[b][pos // page_size])
-            kp[page, pos % page_size] = kq[t]
-            vp[page, pos % page_size] = vq[t]
+            ksc = ks if ks.ndim == 0 else ks[page][:, None]        # [Hkv, 1] per head
+            vsc = vs if vs.ndim == 0 else vs[page][:, None]
+            kp[page, pos % page_size] = quantize_ref(k_new[t], ksc)
+            vp[page, pos % page_size] = quantize_ref(v_new[t], vsc)
     return kp, vp

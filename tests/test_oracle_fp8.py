@@ -117,3 +117,80 @@ def test_planted_fp8_mistakes_are_caught(monkeypatch, mutant):
         monkeypatch.setattr(of, "quantize_ref", lambda x, scale: real_q(x, 1.0 / scale))
         with pytest.raises(AssertionError):
             test_quantizer_clamps_and_scales()
+
+
+# ----------------------------------------------------------------------------
+# per-(page, KV head) scales (F2')
+# ----------------------------------------------------------------------------
+
+def _page_scales(P, Hkv, seed):
+    rng = np.random.default_rng(seed)
+    return (2.0 ** rng.uniform(-8, 2, size=(P, Hkv))).astype(np.float32)
+
+
+def test_page_scales_all_equal_are_the_pool_scale():
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 3, size=(6, 16, 2, 64)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    ks = np.full((6, 2), 0.0375, np.float32)
+    assert np.array_equal(of.quantize_ref(xb, of.page_scales(ks)), of.quantize_ref(xb, 0.0375))
+    c = of.quantize_ref(xb, 0.0375)
+    assert np.array_equal(of.dequantize_pool(c, ks), of.dequantize_pool(c, 0.0375))
+
+
+def test_page_scales_match_brute_force_per_element():
+    """Every element is encoded by the brute-force scan of y = x * fl32(1 / s) for
+    the scale of its own (page, head)."""
+    rng = np.random.default_rng(13)
+    x = rng.normal(0, 2, size=(3, 4, 2, 8)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xf = oa.bf16_bits_to_f64(xb)
+    ks = _page_scales(3, 2, 14)
+    codes = of.quantize_ref(xb, of.page_scales(ks))
+    for p in range(3):
+        for h in range(2):
+            inv = np.float32(1.0) / ks[p, h]
+            for r in range(4):
+                for d in range(8):
+                    y = float(np.clip(np.float32(xf[p, r, h, d]) * inv, -448.0, 448.0))
+                    assert codes[p, r, h, d] == _brute_encode(y), (p, h, r, d)
+    # dequantisation multiplies each code by its own page's scale
+    deq = of.dequantize_pool(codes, ks)
+    assert np.array_equal(deq[2, :, 1], of.e4m3_decode(codes[2, :, 1]) * float(ks[2, 1]))
+    # and stays within half an E4M3 step (relative 2^-4) of the value, away from clamping
+    ok = np.abs(xf) < 448.0 * ks[:, None, :, None] * 0.9
+    rel = np.abs(deq - xf) / np.maximum(np.abs(xf), 2.0 ** -6 * ks[:, None, :, None])
+    assert (rel[ok] <= 2.0 ** -4 + 1e-12).all()
+
+
+def test_page_scaled_write_uses_each_pages_scale():
+    case = make_case("w8p", hist_lens=[20, 0, 33], q_lens=[5, 40, 1], write_new=True, Hq=4,
+                     Hkv=2, D=64, page_size=16, seed=4)
+    P = case.k_pool.shape[0]
+    ks, vs = _page_scales(P, 2, 15), _page_scales(P, 2, 16)
+    kz = np.zeros(case.k_pool.shape, np.uint8)
+    kp8, vp8 = of.kv_write_fp8_ref(kz, kz, bits(case.k_new), bits(case.v_new), case.cu_new.numpy(),
+                                   case.start_pos.numpy(), case.block_tables.numpy(), 16, ks, vs)
+    bt, cu, sp = case.block_tables.numpy(), case.cu_new.numpy(), case.start_pos.numpy()
+    kn = bits(case.k_new)
+    for b in range(3):
+        for t in range(int(cu[b]), int(cu[b + 1])):
+            pos = int(sp[b]) + t - int(cu[b])
+            page = int(bt[b, pos // 16])
+            for h in range(2):
+                assert np.array_equal(kp8[page, pos % 16, h], of.quantize_ref(kn[t, h], ks[page, h]))
+    # equal per-page scales reproduce the per-pool write
+    k1, v1 = of.kv_write_fp8_ref(kz, kz, bits(case.k_new), bits(case.v_new), cu, sp, bt, 16,
+                                 np.full((P, 2), 0.05, np.float32), np.full((P, 2), 0.02, np.float32))
+    k2, v2 = of.kv_write_fp8_ref(kz, kz, bits(case.k_new), bits(case.v_new), cu, sp, bt, 16,
+                                 0.05, 0.02)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_planted_page_scale_mistake_is_caught(monkeypatch):
+    """A quantiser that takes the scale of the neighbouring page must fail the brute force."""
+    real = of.page_scales
+    monkeypatch.setattr(of, "page_scales",
+                        lambda s, ndim=4: real(np.roll(np.asarray(s), 1, axis=0), ndim))
+    with pytest.raises(AssertionError):
+        test_page_scales_match_brute_force_per_element()
