@@ -104,6 +104,15 @@ int kv_page_write(void* k_pool, void* v_pool, const void* k_new, const void* v_n
  *     value, ties to even.  NaN inputs give unspecified codes.
  * FP8 pools have the bf16 pools' shape [num_pages, page_size, Hkv, D], one byte
  * per element (uint8 storage), and the same 16-byte alignment rule.
+ *
+ * Finer scaling (the caller's choice): one float32 scale per (page, KV head),
+ * arrays k_scales / v_scales of shape [num_pages, Hkv] on the device, owned by the
+ * caller; a code of page p, head h stands for decode(c) * scales[p * Hkv + h], and a
+ * token row is quantised with the scale of the page and head it lands in.  Scales
+ * must be positive and finite (device data, not checked).  Decode and prefill fold
+ * each page's key scale into the score multiplier of that page's keys and apply
+ * each page's value scale to P before P V (the row sums stay unscaled), so the
+ * per-pool k_scale / v_scale arguments are then ignored.
  */
 
 /*
@@ -121,6 +130,21 @@ int kv_page_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void*
                       const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
                       int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D,
                       float k_scale, float v_scale, void* stream);
+
+/*
+ * kv_page_write_fp8_scales -- kv_page_write_fp8 with scales per (page, KV head):
+ * token t's head h is quantised under k_scales[page * Hkv + h] (keys) and
+ * v_scales[page * Hkv + h] (values) of the page it is written to.
+ *
+ *   k_scales, v_scales : device [num_pages, Hkv] float32 (4-byte aligned), required
+ * Every other argument, precondition and status is kv_page_write_fp8's.
+ */
+int kv_page_write_fp8_scales(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const int32_t* cu_new, const int32_t* start_pos,
+                             const int32_t* block_tables, int32_t B, int32_t T,
+                             int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hkv,
+                             int32_t D, const float* k_scales, const float* v_scales,
+                             void* stream);
 
 /*
  * paged_attn_decode_num_splits -- the split count paged_attn_decode uses when it is
@@ -430,6 +454,9 @@ typedef struct {
   void* kernel_stop_event;    /* NULL, or a hipEvent_t stamped with that kernel's end     */
   const int32_t* key_lo;      /* NULL, or device [B] int32: first key of the document the
                                  decode row belongs to (document masks above)            */
+  const float* k_scales;      /* kv_fp8 only: NULL (the pool scales above), or device
+                                 [num_pages, Hkv] float32 scales per (page, KV head)     */
+  const float* v_scales;      /* with k_scales (both or neither)                          */
 } pa_decode_opts;
 
 typedef struct {
@@ -447,6 +474,10 @@ typedef struct {
   const int32_t* key_lo;      /* NULL, or device [Tq] int32: key_lo of every query row    */
   const int32_t* key_hi;      /* NULL, or device [Tq] int32: key_hi of every query row
                                  (both or neither; document masks above)                 */
+  const float* k_scales;      /* kv_fp8 only: NULL (the pool scales above), or device
+                                 [num_pages, Hkv] float32 scales per (page, KV head); not
+                                 with ALiBi slopes (PA_ERR_UNSUPPORTED)                  */
+  const float* v_scales;      /* with k_scales (both or neither)                          */
 } pa_prefill_opts;
 
 /*

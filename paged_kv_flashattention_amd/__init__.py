@@ -9,7 +9,7 @@ Entry points (same names as the C ABI):
 * :func:`kv_page_write`      -- place new tokens' K/V into their pages;
 * :func:`kv_page_write_fp8`  -- the same, quantising into FP8 E4M3 pools;
 * :func:`paged_attn_decode`  -- one query row per sequence, split-K + merge;
-* :func:`paged_attn_decode_fp8` -- decode over FP8 E4M3 pools with per-pool scales;
+* :func:`paged_attn_decode_fp8` -- decode over FP8 E4M3 pools;
 * :func:`paged_attn_decode_partials` -- decode's per-partition results only;
 * :func:`paged_attn_splitk_reduce` -- the merge on its own;
 * :func:`paged_attn_prefill_varlen` -- ragged (causal) prefill on MFMA;
@@ -19,8 +19,9 @@ Entry points (same names as the C ABI):
 
 Data contract: bf16 Q / K / V / outputs, int32 indices (int64 is refused, not
 cast), fp32 lse, contiguous tensors on one GPU.  FP8 pools are uint8 (or
-torch.float8_e4m3fn) tensors of E4M3 codes with one float32 scale per pool.  An unsupported configuration
-raises; there is no fallback path.
+torch.float8_e4m3fn) tensors of E4M3 codes with one float32 scale per pool (floats)
+or one per (page, KV head) (float32 tensors [num_pages, Hkv] on the pools' GPU).
+An unsupported configuration raises; there is no fallback path.
 """
 
 from __future__ import annotations
@@ -194,11 +195,38 @@ def _need_fp8_pool(t, name: str, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+class _PageScales:
+    """FP8 scales per (page, KV head): device float32 tensors [num_pages, Hkv]."""
+
+    def __init__(self, k, v):
+        self.k, self.v = k, v
+
+    def check(self, pool_shape, dev):
+        P, _, Hkv, _ = pool_shape
+        for t, name in ((self.k, "k_scale"), (self.v, "v_scale")):
+            _need(t, name, torch.float32, 2, dev)
+            if tuple(t.shape) != (P, Hkv):
+                raise ValueError(f"{name} per page must be [num_pages={P}, Hkv={Hkv}], got "
+                                 f"{tuple(t.shape)}")
+        return self.k.data_ptr(), self.v.data_ptr()
+
+
 def _scales(k_scale, v_scale):
+    """One float32 scale per pool (floats), or per (page, KV head) (two tensors)."""
+    if isinstance(k_scale, torch.Tensor) or isinstance(v_scale, torch.Tensor):
+        if not (isinstance(k_scale, torch.Tensor) and isinstance(v_scale, torch.Tensor)):
+            raise TypeError("k_scale and v_scale must both be floats or both be tensors")
+        _dtypes((k_scale, "k_scale", torch.float32), (v_scale, "v_scale", torch.float32))
+        return _PageScales(k_scale, v_scale)
     ks, vs = float(k_scale), float(v_scale)
     if not (0.0 < ks < float("inf") and 0.0 < vs < float("inf")):
         raise ValueError(f"k_scale and v_scale must be positive and finite, got {ks}, {vs}")
     return ks, vs
+
+
+def _pool_scales(scales):
+    """(k_scale, v_scale) floats of the C call: 1 with scales per page (ignored)."""
+    return (1.0, 1.0) if isinstance(scales, _PageScales) else scales
 
 
 def _dtypes(*specs):
@@ -230,10 +258,11 @@ def kv_page_write(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
 
 
 def kv_page_write_fp8(k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tables,
-                      k_scale: float, v_scale: float, stream=None,
-                      validate: bool = False) -> None:
-    """Quantise k_new/v_new [T, Hkv, D] bf16 to E4M3 codes under the pool scales and
-    write them into the uint8 pools in place (see kv_page_write_fp8 in C)."""
+                      k_scale, v_scale, stream=None, validate: bool = False) -> None:
+    """Quantise k_new/v_new [T, Hkv, D] bf16 to E4M3 codes and write them into the
+    uint8 pools in place: under one scale per pool (floats; kv_page_write_fp8 in C)
+    or one per (page, KV head) (float32 tensors [num_pages, Hkv] on the device;
+    kv_page_write_fp8_scales in C)."""
     _kv_write(_scales(k_scale, v_scale), k_pool, v_pool, k_new, v_new, cu_new, start_pos,
               block_tables, stream, validate)
 
@@ -290,6 +319,9 @@ def _kv_write(scales, k_pool, v_pool, k_new, v_new, cu_new, start_pos, block_tab
     with torch.cuda.device(dev):
         if scales is None:
             _check(lib.kv_page_write(*args, _stream(stream)))
+        elif isinstance(scales, _PageScales):
+            kp_, vp_ = scales.check(k_pool.shape, dev)
+            _check(lib.kv_page_write_fp8_scales(*args, kp_, vp_, _stream(stream)))
         else:
             _check(lib.kv_page_write_fp8(*args, scales[0], scales[1], _stream(stream)))
 
@@ -329,7 +361,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
 
 
 def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
-                          k_scale: float, v_scale: float, max_seq_len: Optional[int] = None,
+                          k_scale, v_scale, max_seq_len: Optional[int] = None,
                           num_splits: int = 0, out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
@@ -337,8 +369,9 @@ def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_sca
                           alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
                           key_lo: Optional[torch.Tensor] = None):
     """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
-    decode(code) * k_scale, values for decode(code) * v_scale.  Arguments and
-    results are paged_attn_decode's."""
+    decode(code) * k_scale, values for decode(code) * v_scale, with one scale per pool
+    (floats) or per (page, KV head) (float32 tensors [num_pages, Hkv] on the device).
+    Arguments and results are paged_attn_decode's."""
     return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
                    softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
                    stream, validate, window_left, alibi_slopes, kernel_events, key_lo)
@@ -434,9 +467,12 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
                 raise ValueError("key_lo must lie in [0, seq_lens]")
         lo_ptr = key_lo.data_ptr()
     ev0, ev1 = _events(kernel_events)
+    ksp = vsp = None
+    if isinstance(scales, _PageScales):
+        ksp, vsp = scales.check(k_pool.shape, dev)
     opts = _lib.DecodeOpts(int(num_splits), window_left, 0 if scales is None else 1,
-                           *(scales if scales is not None else (1.0, 1.0)), alibi_ptr, ev0, ev1,
-                           lo_ptr)
+                           *(_pool_scales(scales) if scales is not None else (1.0, 1.0)),
+                           alibi_ptr, ev0, ev1, lo_ptr, ksp, vsp)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
     if workspace is not None:
@@ -448,7 +484,8 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
             _ptr(seq_lens), B, block_tables.shape[1], P, ps, Hq, Hkv, D, float(softmax_scale))
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
-        if window_left or alibi_ptr is not None or ev0 is not None or lo_ptr is not None:
+        if (window_left or alibi_ptr is not None or ev0 is not None or lo_ptr is not None
+                or ksp is not None):
             _check(lib.paged_attn_decode_ex(*head, int(max_seq_len), ctypes.byref(opts),
                                             *tail[2:]))
         elif scales is None:
@@ -549,7 +586,7 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
 
 
 def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
-                                  softmax_scale: float, k_scale: float, v_scale: float,
+                                  softmax_scale: float, k_scale, v_scale,
                                   causal: bool = True, max_q_len: Optional[int] = None,
                                   num_splits: int = 1, out: Optional[torch.Tensor] = None,
                                   lse: Optional[torch.Tensor] = None,
@@ -559,7 +596,8 @@ def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, b
                                   alibi_slopes: Optional[torch.Tensor] = None,
                                   kernel_events=None, key_ranges=None):
     """Ragged prefill over FP8 E4M3 pools (uint8 codes; keys stand for decode(code) *
-    k_scale, values for decode(code) * v_scale), through paged_attn_prefill_ex.
+    k_scale, values for decode(code) * v_scale; scales per pool as floats or per (page,
+    KV head) as float32 tensors [num_pages, Hkv]), through paged_attn_prefill_ex.
     ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass)."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
@@ -699,9 +737,13 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         if split is None:
             _check(lib.paged_attn_prefill_varlen(*args, _stream(stream)))
         elif general:
-            ks, vs = scales if scales is not None else (1.0, 1.0)
+            ks, vs = _pool_scales(scales) if scales is not None else (1.0, 1.0)
+            ksp = vsp = None
+            if isinstance(scales, _PageScales):
+                ksp, vsp = scales.check(k_pool.shape, dev)
             opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
-                                    0 if scales is None else 1, ks, vs, ev0, ev1, lo_ptr, hi_ptr)
+                                    0 if scales is None else 1, ks, vs, ev0, ev1, lo_ptr, hi_ptr,
+                                    ksp, vsp)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

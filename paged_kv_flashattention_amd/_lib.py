@@ -24,7 +24,8 @@ class DecodeOpts(ctypes.Structure):
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
                 ("kernel_start_event", ctypes.c_void_p), ("kernel_stop_event", ctypes.c_void_p),
-                ("key_lo", ctypes.c_void_p)]
+                ("key_lo", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p)]
 
 
 class PrefillOpts(ctypes.Structure):
@@ -34,7 +35,8 @@ class PrefillOpts(ctypes.Structure):
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("kernel_start_event", ctypes.c_void_p),
                 ("kernel_stop_event", ctypes.c_void_p), ("key_lo", ctypes.c_void_p),
-                ("key_hi", ctypes.c_void_p)]
+                ("key_hi", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)
@@ -47,6 +49,9 @@ SIGNATURES = {
     "kv_page_write_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                   c_float, c_float, c_vp]),
+    "kv_page_write_fp8_scales": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                         c_fp, c_fp, c_vp]),
     "paged_attn_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32]),
     "paged_attn_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "paged_attn_decode": (c_i32, [c_vp, c_fp, c_vp, c_vp, c_vp, c_vp, c_vp,

@@ -98,6 +98,20 @@ size_t workspace_for(int32_t B, int32_t Hq, int32_t D, int32_t S) {
   return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
 }
 
+// Scales per (page, KV head) of FP8 pools: both or neither, FP8 pools only, 4-byte
+// aligned.
+int page_scales_ok(const char* what, bool fp8, const float* k_scales, const float* v_scales) {
+  if (!k_scales && !v_scales) return PA_OK;
+  if (!k_scales || !v_scales)
+    return fail(PA_ERR_NULL, "%s: k_scales and v_scales must both be given or both be NULL",
+                what);
+  if (!fp8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: scales per page need FP8 pools (kv_fp8 = 1)", what);
+  if ((reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u))
+    return fail(PA_ERR_MISALIGNED, "%s: k_scales and v_scales must be 4-byte aligned", what);
+  return PA_OK;
+}
+
 // Checks and argument packing shared by paged_attn_decode and
 // paged_attn_decode_partials.  `what` names the entry point in messages.
 int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* k_pool,
@@ -106,7 +120,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 int32_t Hkv, int32_t D, float softmax_scale, int32_t max_seq_len,
                 int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
                 float v_scale = 1.f, int32_t window = 0, const float* alibi = nullptr,
-                const int32_t* key_lo = nullptr) {
+                const int32_t* key_lo = nullptr, const float* k_scales = nullptr,
+                const float* v_scales = nullptr) {
   if (B < 0 || max_seq_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
@@ -123,6 +138,10 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
     return fail(PA_ERR_MISALIGNED, "%s: alibi_slopes must be 4-byte aligned", what);
   if (key_lo && (reinterpret_cast<uintptr_t>(key_lo) & 3u))
     return fail(PA_ERR_MISALIGNED, "%s: key_lo must be 4-byte aligned", what);
+  st = page_scales_ok(what, fp8, k_scales, v_scales);
+  if (st) return st;
+  // with scales per page the pool scales are not used
+  if (k_scales) k_scale = v_scale = 1.f;
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   // with a window every row walks at most window + 31 keys (its lower bound rounded
@@ -149,6 +168,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.window = window;
   a.alibi = alibi;
   a.key_lo = key_lo;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   return PA_OK;
 }
 
@@ -158,9 +179,13 @@ int kv_write_impl(const char* what, void* k_pool, void* v_pool, const void* k_ne
                   const void* v_new, const int32_t* cu_new, const int32_t* start_pos,
                   const int32_t* block_tables, int32_t B, int32_t T, int32_t max_pages,
                   int32_t num_pages, int32_t page_size, int32_t Hkv, int32_t D, bool fp8,
-                  float k_scale, float v_scale, void* stream) {
+                  float k_scale, float v_scale, void* stream, const float* k_scales = nullptr,
+                  const float* v_scales = nullptr) {
   g_last_error[0] = 0;
   if (B < 0 || T < 0) return fail(PA_ERR_SHAPE, "%s: B=%d T=%d must be >= 0", what, B, T);
+  int st0 = page_scales_ok(what, fp8, k_scales, v_scales);
+  if (st0) return st0;
+  if (k_scales) k_scale = v_scale = 1.f;
   if (fp8 && !scales_ok(k_scale, v_scale))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   if (B == 0 || T == 0) {
@@ -187,6 +212,8 @@ int kv_write_impl(const char* what, void* k_pool, void* v_pool, const void* k_ne
   // the reciprocal is taken once, in float32, as the quantiser's definition does
   a.k_inv = fp8 ? 1.0f / k_scale : 1.f;
   a.v_inv = fp8 ? 1.0f / v_scale : 1.f;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   hipError_t e = pa::launch_kv_write(a, static_cast<hipStream_t>(stream), g_last_launch,
                                      sizeof(g_last_launch));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
@@ -202,12 +229,14 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 int32_t num_splits, void* workspace, size_t workspace_bytes, bool fp8,
                 float k_scale, float v_scale, void* stream, int32_t window = 0,
                 const float* alibi = nullptr, const pa::KernelEvents& ev = pa::KernelEvents(),
-                const int32_t* key_lo = nullptr) {
+                const int32_t* key_lo = nullptr, const float* k_scales = nullptr,
+                const float* v_scales = nullptr) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
                        num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
-                       num_splits, fp8, k_scale, v_scale, window, alibi, key_lo);
+                       num_splits, fp8, k_scale, v_scale, window, alibi, key_lo, k_scales,
+                       v_scales);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
@@ -288,7 +317,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
                  const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
                  float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
-                 const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr) {
+                 const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr,
+                 const float* k_scales = nullptr, const float* v_scales = nullptr) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -312,6 +342,12 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   if ((key_lo && (reinterpret_cast<uintptr_t>(key_lo) & 3u)) ||
       (key_hi && (reinterpret_cast<uintptr_t>(key_hi) & 3u)))
     return fail(PA_ERR_MISALIGNED, "%s: key_lo and key_hi must be 4-byte aligned", what);
+  st = page_scales_ok(what, fp8, k_scales, v_scales);
+  if (st) return st;
+  if (k_scales && alibi)
+    return fail(PA_ERR_UNSUPPORTED, "%s: FP8 scales per page with ALiBi slopes are not "
+                "supported in prefill", what);
+  if (k_scales) k_scale = v_scale = 1.f;
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
   if (max_q_len > Tq) max_q_len = Tq;
@@ -349,6 +385,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.v_scale = fp8 ? v_scale : 1.f;
   a.key_lo = key_lo;
   a.key_hi = key_hi;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -455,6 +493,19 @@ int kv_page_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void*
   return kv_write_impl("kv_page_write_fp8", k_pool, v_pool, k_new, v_new, cu_new, start_pos,
                        block_tables, B, T, max_pages, num_pages, page_size, Hkv, D, true,
                        k_scale, v_scale, stream);
+}
+
+int kv_page_write_fp8_scales(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const int32_t* cu_new, const int32_t* start_pos,
+                             const int32_t* block_tables, int32_t B, int32_t T,
+                             int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hkv,
+                             int32_t D, const float* k_scales, const float* v_scales,
+                             void* stream) {
+  if (!k_scales || !v_scales)
+    return fail(PA_ERR_NULL, "kv_page_write_fp8_scales: k_scales and v_scales are required");
+  return kv_write_impl("kv_page_write_fp8_scales", k_pool, v_pool, k_new, v_new, cu_new,
+                       start_pos, block_tables, B, T, max_pages, num_pages, page_size, Hkv, D,
+                       true, 1.f, 1.f, stream, k_scales, v_scales);
 }
 
 int paged_attn_decode(void* out, float* lse_out, const void* q, const void* k_pool,
@@ -743,7 +794,7 @@ int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k
                      opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
                      opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
                      stream, opts->window_left, opts->alibi_slopes, events_of(opts),
-                     opts->key_lo);
+                     opts->key_lo, opts->k_scales, opts->v_scales);
 }
 
 size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -769,7 +820,7 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
                       workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
                       opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts),
-                      opts->key_lo, opts->key_hi);
+                      opts->key_lo, opts->key_hi, opts->k_scales, opts->v_scales);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

@@ -30,6 +30,12 @@
 
 namespace pa {
 
+// Key and value scales of the two 16-key halves of a chunk (FP8 pools with scales
+// per (page, KV head)).
+struct ChunkScales {
+  float k0, k1, v0, v1;
+};
+
 template <int D>
 struct DecodeChunk {
   u32x4 ka[D / 32];          // K row (chunk key l%16), d in [D/4 * g, D/4 * (g+1))
@@ -300,9 +306,23 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     };
     DecodeChunk<D> ch;
     KRows<D> kr;
+    // FP8 pools with scales per (page, KV head): the scales of the two pages of the
+    // chunk in registers, read (scalar loads) one chunk ahead like its data
+    ChunkScales sc{1.f, 1.f, 1.f, 1.f};
+    auto scales_of = [&](int p0, int p1) {
+      ChunkScales r{1.f, 1.f, 1.f, 1.f};
+      if (F8 && a.k_scales) {
+        r.k0 = a.k_scales[(size_t)p0 * a.Hkv + kvh];
+        r.k1 = a.k_scales[(size_t)p1 * a.Hkv + kvh];
+        r.v0 = a.v_scales[(size_t)p0 * a.Hkv + kvh];
+        r.v1 = a.v_scales[(size_t)p1 * a.Hkv + kvh];
+      }
+      return r;
+    };
     {
       const int c0 = k_begin + 32 * c;
       const int p0 = page(c0), p1 = page(c0 + 16);
+      sc = scales_of(p0, p1);
       load_k(kr, p0, p1, c0);
       // K before V: the first scores then wait only for the K loads
       __builtin_amdgcn_sched_barrier(0);
@@ -313,6 +333,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       const int c0n = k_begin + 32 * min(c + 1, c_end - 1);
       const int pn0 = page(c0n);
       const int pn1 = page(c0n + 16);
+      const ChunkScales scn = scales_of(pn0, pn1);
 
       // this chunk's K rows -> LDS; the next chunk's K loads reuse the registers
       if constexpr (F8) decode_k8_to_lds<D>(kr, k_lds, lane);
@@ -329,11 +350,16 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
 
       if constexpr (F8) decode_widen_v8<D>(ch);
 
+      // FP8 pools with scales per (page, KV head): the keys of the chunk's first 16
+      // rows come from page p0, the next 16 from p1 (the same page when pages hold
+      // 32 or more keys), so each half has its own key scale in the score multiplier
+      const float sm0 = F8 && a.k_scales ? a.scale_log2 * sc.k0 : a.scale_log2;
+      const float sm1 = F8 && a.k_scales ? a.scale_log2 * sc.k1 : a.scale_log2;
       float s[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[i] = sa[i] * a.scale_log2;
-        s[4 + i] = sb[i] * a.scale_log2;
+        s[i] = sa[i] * sm0;
+        s[4 + i] = sb[i] * sm1;
       }
       if (a.alibi) {
         // score of key c0 + 4 g + o (o = j, or 12 + j for the second half) gets
@@ -374,6 +400,15 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       m_run = m_new;
 #pragma unroll
       for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
+      // the value scale of each half's page goes onto P (the row sum above stays
+      // unscaled): P V then sums p_j * v_scale(page of j) * decode(code_j)
+      if (F8 && a.v_scales) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] *= sc.v0;
+          p[4 + j] *= sc.v1;
+        }
+      }
       const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
 #pragma unroll
@@ -390,6 +425,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
         acc[t] = mfma16x16x32(va, pb, acc[t]);
       }
       load_v(ch, pn0, pn1, c0n);
+      sc = scn;
     }
   }
 
@@ -515,7 +551,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, si
                             : launch_decode_d<64>(a, stream, W, ev);
   snprintf(desc, desc_len,
            "decode_partition<D=%d,W=%d,%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
-           W, a.kv_fp8 ? "fp8-e4m3" : "bf16", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
+           W, a.kv_fp8 ? (a.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
   return e;
 }
 

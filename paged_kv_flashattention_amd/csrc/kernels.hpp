@@ -28,6 +28,8 @@ struct DecodeArgs {
   int window;                    // sliding window: keys j >= seq_len - window only (0: none)
   const float* alibi;            // [Hq] ALiBi slopes, or null: score += slope * (j - pos)
   const int32_t* key_lo;         // [B] first key of the row's document, or null (none)
+  const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
+  const float* v_scales;         //   or null: one scale per pool (folded as above)
 };
 
 struct ReduceArgs {
@@ -49,6 +51,8 @@ struct KvWriteArgs {
   int B, T, max_pages, num_pages, page_size, ps_shift, Hkv, D;
   int fp8;                       // quantise into FP8 E4M3 pools (uint8 codes)
   float k_inv, v_inv;            // 1 / k_scale, 1 / v_scale (float32)
+  const float* k_scales;         // [num_pages, Hkv] scales per (page, KV head), or null
+  const float* v_scales;
 };
 
 struct PrefillArgs {
@@ -78,6 +82,8 @@ struct PrefillArgs {
   float* part_lse;               // [Tq * Hq, S] partial natural-log lse   (S > 1)
   const int32_t* key_lo;         // [Tq] document range [key_lo, key_hi) of each query
   const int32_t* key_hi;         //   row, or both null (no document masks)
+  const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
+  const float* v_scales;         //   or null: one scale per pool
 };
 
 // Optional events stamped with one kernel's own start and end: the dispatch

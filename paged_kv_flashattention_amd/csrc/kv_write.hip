@@ -104,8 +104,16 @@ __global__ __launch_bounds__(kKvWriteBlock) void kv_page_write_fp8_kernel(KvWrit
   const u32x4 v1 = *reinterpret_cast<const u32x4*>(a.v_new + src + 8);
   uint8_t* kp = reinterpret_cast<uint8_t*>(a.k_pool);
   uint8_t* vp = reinterpret_cast<uint8_t*>(a.v_pool);
-  *reinterpret_cast<u32x4*>(kp + dst) = quantize16(k0, k1, a.k_inv);
-  *reinterpret_cast<u32x4*>(vp + dst) = quantize16(v0, v1, a.v_inv);
+  // scales per (page, KV head): the reciprocal of this page's scale, in float32 as
+  // for a pool scale
+  float k_inv = a.k_inv, v_inv = a.v_inv;
+  if (a.k_scales) {
+    const size_t s = (size_t)page * a.Hkv + rem / pieces_per_row;
+    k_inv = 1.0f / a.k_scales[s];
+    v_inv = 1.0f / a.v_scales[s];
+  }
+  *reinterpret_cast<u32x4*>(kp + dst) = quantize16(k0, k1, k_inv);
+  *reinterpret_cast<u32x4*>(vp + dst) = quantize16(v0, v1, v_inv);
 }
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
@@ -116,8 +124,9 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
     hipLaunchKernelGGL(kv_page_write_fp8_kernel, dim3(blocks), dim3(kKvWriteBlock), 0, stream, a);
   else
     hipLaunchKernelGGL(kv_page_write_kernel, dim3(blocks), dim3(kKvWriteBlock), 0, stream, a);
-  snprintf(desc, desc_len, "kv_page_write%s grid=%u block=%d tokens=%d", a.fp8 ? "_fp8" : "",
-           blocks, kKvWriteBlock, a.T);
+  snprintf(desc, desc_len, "kv_page_write%s grid=%u block=%d tokens=%d", a.fp8 ?
+           (a.k_scales ? "_fp8 (scales per page and KV head)" : "_fp8") : "", blocks,
+           kKvWriteBlock, a.T);
   return hipGetLastError();
 }
 

@@ -225,9 +225,10 @@ __device__ __forceinline__ u32x2 pf_fp8x4_to_bf16(uint32_t w) {
 // variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
 // downwards, which is how the ALiBi variants (general only) walk, so REV also
 // compiles the bias in.
-template <int D, int W, bool GEN, bool F8, bool REV>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   static_assert(!REV || GEN, "the downward walk is a general-variant feature");
+  static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   extern __shared__ __align__(16) uint16_t pf_lds[];
   using L_ = PfLds<D>;
@@ -414,6 +415,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const uint8_t* kbase8 = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * D;
   const uint8_t* vbase8 = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * D;
   u32x4 k8[F8_NP], v8[F8_NP];
+  // FP8 pools with scales per (page, KV head): each wave reads the key and value
+  // scales of its own 16-row region's page when it issues a tile and, when the tile
+  // is published, writes them to a small table kept per V stage: for each 32-key
+  // block of the tile (k of its first and second 16 keys, v of both).  After the
+  // barrier every wave finds there the scales of every block it computes.
+  __shared__ __align__(16) float pg_scales[PS ? 3 : 1][8];
+  float ks_next = 1.f, vs_next = 1.f;
   // DMA of tile n (tiles are issued in increasing order) into V stage vs
   auto issue = [&](int n, int vs) {
     if (REV ? n < base_t : n - base_t >= 64) {
@@ -422,6 +430,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     }
     int pg = __builtin_amdgcn_readlane(tab, n - base_t);
     pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+    if constexpr (PS) {
+      ks_next = a.k_scales[(size_t)pg * a.Hkv + kvh];
+      vs_next = a.v_scales[(size_t)pg * a.Hkv + kvh];
+    }
     if constexpr (F8) {
       const size_t base = ((size_t)pg * a.page_size + run0) * rs;
 #pragma unroll
@@ -442,6 +454,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
   auto publish = [&](int n, int vs) {
     vmcnt_wait<0>();
+    if constexpr (PS) {
+      // region r holds keys 16 r .. 16 r + 15 of the tile: half r % 2 of block r / 2
+      const int r = M_::region(wave);
+      if (lane == 0 && wave % (W / 4) == 0) {
+        pg_scales[vs][4 * (r >> 1) + (r & 1)] = ks_next;
+        pg_scales[vs][4 * (r >> 1) + 2 + (r & 1)] = vs_next;
+      }
+    }
     if constexpr (F8) {
       uint16_t* kr = kst(n) + M_::region(wave) * PfLds<D>::REGION;
       uint16_t* vr = vst(vs) + M_::region(wave) * PfLds<D>::REGION;
@@ -487,13 +507,34 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       sc = mfma32x32x16(*reinterpret_cast<const u32x4*>(kl + 256 * kk), qb[kk], sc);
     return sc;
   };
+  // Score multipliers of a block's two 16-key halves (elements 0..7 are keys 0..15
+  // of the block, elements 8..15 keys 16..31) and, with scales per page, the value
+  // scales that go onto P: the softmax scale (times the pool's k_scale for FP8
+  // pools) or, per (page, KV head), times each half's page scale.
+  struct BlkScale {
+    float ca, cb, va, vb;
+  };
+  auto blk_scale = [&](int vs, int kb) {
+    if constexpr (PS) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(&pg_scales[vs][4 * kb]);
+      return BlkScale{a.scale_log2 * t[0], a.scale_log2 * t[1], t[2], t[3]};
+    } else {
+      return BlkScale{a.scale_log2, a.scale_log2, 1.f, 1.f};
+    }
+  };
   // scaled row maximum of a block (log2 units)
-  auto rowmax = [&](const f32x16& sc) {
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+  auto rowmax = [&](const f32x16& sc, const BlkScale& bs) {
+    float ma = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-    for (int e = 3; e < 15; e += 2) mt = fmaxf(fmaxf(mt, sc[e]), sc[e + 1]);
-    mt = fmaxf(mt, sc[15]);
-    const float r = xor32_max(mt) * a.scale_log2;
+    for (int e = 3; e < 7; e += 2) ma = fmaxf(fmaxf(ma, sc[e]), sc[e + 1]);
+    ma = fmaxf(ma, sc[7]);
+    float mb = fmaxf(fmaxf(sc[8], sc[9]), sc[10]);
+#pragma unroll
+    for (int e = 11; e < 15; e += 2) mb = fmaxf(fmaxf(mb, sc[e]), sc[e + 1]);
+    mb = fmaxf(mb, sc[15]);
+    // both multipliers are positive, so scaling commutes with the maximum
+    const float r = PS ? xor32_max(fmaxf(ma * bs.ca, mb * bs.cb))
+                       : xor32_max(fmaxf(ma, mb)) * bs.ca;
     return ALI ? r + boff : r;
   };
   // The block's ALiBi offset (general variant), then -inf for keys past the end,
@@ -550,15 +591,21 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // (1, 1) forms a serial chain that does not issue under the matrix cores' work
   // on gfx950: with one pipeline step's MFMAs in flight it held the matrix cores
   // at 68 % of their peak against 82 % with plain fp32 adds, two waves per SIMD.)
-  auto exps = [&](const f32x16& sc, uint32_t* pw, float& ps) {
+  auto exps = [&](const f32x16& sc, const BlkScale& bs, uint32_t* pw, float& ps) {
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
     const float neg_m = ALI ? neg_m0 + boff : neg_m0;
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], a.scale_log2, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], a.scale_log2, neg_m));
-      pw[e / 2] = pack_bf16x2(p0, p1);
+      const float c = e < 8 ? bs.ca : bs.cb;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], c, neg_m));
+      if constexpr (PS) {
+        const float v = e < 8 ? bs.va : bs.vb;
+        pw[e / 2] = pack_bf16x2(p0 * v, p1 * v);
+      } else {
+        pw[e / 2] = pack_bf16x2(p0, p1);
+      }
       ps0 += p0;
       ps1 += p1;
     }
@@ -571,15 +618,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // the block.  The accepted P are therefore bounded by 2^kRescaleSlack and the
   // result is the same as with an exact running maximum ("The Stack Below the
   // Stack (Part 2)", 2.1 and 2.3: any common reference gives the same quotient).
-  auto settle = [&](const f32x16& sc, uint32_t* pw, float& ps) {
+  auto settle = [&](const f32x16& sc, const BlkScale& bs, uint32_t* pw, float& ps) {
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit) || m_run == kNegInf), 0)) {
-      const float m_new = fmaxf(m_run, rowmax(sc));
+      const float m_new = fmaxf(m_run, rowmax(sc, bs));
       const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
       m_run = m_new;
-      exps(sc, pw, ps);
+      exps(sc, bs, pw, ps);
     }
     l_run += ps;
   };
@@ -590,10 +637,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // depend on it, so the matrix cores and the vector ALU of one wave overlap;
   // operand reads run two MFMAs ahead.  sched_barrier keeps the compiler from
   // regrouping the chunks.
-  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, const uint16_t* vp, int kbp) {
+  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp) {
     constexpr int NK = D / 16;                 // QK MFMAs
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
     constexpr int NV = 2 * (D / 32);           // PV MFMAs
+    const uint16_t* vp = vst(vsi);
+    const BlkScale bs = blk_scale(vsi, kbp);
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
     const float neg_m = ALI ? neg_m0 + boff : neg_m0;
     const uint16_t* kl = kq + k_lane + kbq * 32 * D;
@@ -611,9 +660,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       sn = mfma32x32x16(kf[i], qb[i], sn);
 #pragma unroll
       for (int e = EPK * i; e < EPK * (i + 1); e += 2) {
-        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], a.scale_log2, neg_m));
-        pe[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], a.scale_log2, neg_m));
-        pw[e / 2] = pack_bf16x2(pe[e], pe[e + 1]);
+        const float c = e < 8 ? bs.ca : bs.cb;
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], c, neg_m));
+        pe[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], c, neg_m));
+        if constexpr (PS) {
+          const float v = e < 8 ? bs.va : bs.vb;
+          pw[e / 2] = pack_bf16x2(pe[e] * v, pe[e + 1] * v);
+        } else {
+          pw[e / 2] = pack_bf16x2(pe[e], pe[e + 1]);
+        }
         pin(pw[e / 2]);
       }
       // row sum (fp32, two chains) of the exponentials formed one chunk earlier
@@ -634,7 +689,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       ps1 += pe[e + 1];
     }
     float ps = ps0 + ps1;
-    settle(s_pend, pw, ps);
+    settle(s_pend, bs, pw, ps);
     const u32x4 pb0 = {pw[0], pw[1], pw[2], pw[3]};
     const u32x4 pb1 = {pw[4], pw[5], pw[6], pw[7]};
     // O^T += V^T P^T: MFMA i covers d-tile i % (D / 32) of 16-key half i / (D / 32)
@@ -681,12 +736,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int w_key_end = __builtin_amdgcn_readfirstlane(min(
       w_hi_max, !a.causal ? L : (w_last < r_w ? 0 : min(L, shift + w_last + 1))));
   // finish the pending block (P from its scores, P V from V tile vp, block kbp)
-  auto finish = [&](f32x16& sp, const uint16_t* vp, int kbp) {
+  auto finish = [&](f32x16& sp, int vsi, int kbp) {
+    const BlkScale bs = blk_scale(vsi, kbp);
     uint32_t pw[8];
     float ps;
-    exps(sp, pw, ps);
-    settle(sp, pw, ps);
-    pv(vp, kbp, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    exps(sp, bs, pw, ps);
+    settle(sp, bs, pw, ps);
+    pv(vst(vsi), kbp, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
   };
   if (nt > 0) {
     base_t = REV ? max(0, tile_hi - 64) : tile_lo;
@@ -703,7 +759,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     if (G > 0) {
       s_pend = qk(kst(tile_at(0)), B0);
       mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
-      decide(rowmax(s_pend));
+      decide(rowmax(s_pend, blk_scale(0, B0)));
     }
     // iterations u whose two steps both score a computed block (2 u + 2 < G)
     const int U1 = G > 0 ? min(nt - 1, (G - 1) / 2) : 0;
@@ -712,12 +768,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // first block of tile kt (pending) -> its second block
-      step(s_pend, kst(kt), B1, vst(vs_cur), B0);
+      step(s_pend, kst(kt), B1, vs_cur, B0);
       mask(s_pend, kt * kPfBN + 32 * B1);
       // second block of tile kt -> first block of tile kn
       publish(kn, vs_next);
       if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
-      step(s_pend, kst(kn), B0, vst(vs_cur), B1);
+      step(s_pend, kst(kn), B0, vs_cur, B1);
       mask(s_pend, kn * kPfBN + 32 * B0);
       vs_cur = vs_next;
     }
@@ -726,25 +782,25 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       // or none (G = 0, one tile)
       const int kl = tile_at(u);
       if (G == 2 * nt) {
-        step(s_pend, kst(kl), B1, vst(vs_cur), B0);
+        step(s_pend, kst(kl), B1, vs_cur, B0);
         mask(s_pend, kl * kPfBN + 32 * B1);
-        finish(s_pend, vst(vs_cur), B1);
+        finish(s_pend, vs_cur, B1);
       } else if (G == 2 * nt - 1) {
-        finish(s_pend, vst(vs_cur), B0);
+        finish(s_pend, vs_cur, B0);
       }
     } else {
       // this wave's blocks end in tile u (G = 2 u + 1 or 2 u + 2) or there are none
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       if (G == 2 * u + 2) {
-        step(s_pend, kst(kt), B1, vst(vs_cur), B0);
+        step(s_pend, kst(kt), B1, vs_cur, B0);
         mask(s_pend, kt * kPfBN + 32 * B1);
       } else if (G == 2 * u + 1) {
-        finish(s_pend, vst(vs_cur), B0);
+        finish(s_pend, vs_cur, B0);
       }
       publish(kn, vs_next);
       if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
-      if (G == 2 * u + 2) finish(s_pend, vst(vs_cur), B1);
+      if (G == 2 * u + 2) finish(s_pend, vs_cur, B1);
       vs_cur = vs_next;
       // the remaining tiles: this wave's share of each is moved, nothing computed
       for (++u; u + 1 < nt; ++u) {
@@ -865,7 +921,7 @@ static int prefill_grid_tiles(const PrefillArgs& a) {
   return a.xcd_groups ? (a.n_qt + a.xcd_split - 1) / a.xcd_split * a.xcd_split : a.n_qt;
 }
 
-template <int D, int W, bool GEN, bool F8, bool REV>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   // more than 64 KiB of dynamic LDS is requested for the kernel once per device (the
@@ -881,7 +937,7 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
     const int st = state[dev].load(std::memory_order_acquire);
     if (st == 0) {
       const hipError_t e =
-          hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV>),
+          hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES);
       state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
       if (e != hipSuccess) return e;
@@ -890,8 +946,8 @@ static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
     }
   }
   dim3 grid(a.Hq * a.B * prefill_grid_tiles(a) * a.S);
-  launch_kernel(prefill_kernel<D, W, GEN, F8, REV>, grid, dim3(64 * W), (uint32_t)PfLds<D>::BYTES,
-                stream, ev, a);
+  launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS>, grid, dim3(64 * W),
+                (uint32_t)PfLds<D>::BYTES, stream, ev, a);
   return hipGetLastError();
 }
 
@@ -901,6 +957,8 @@ template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   if (a.kv_fp8) {
+    // scales per (page, KV head) (the entry point refuses them with ALiBi slopes)
+    if (a.k_scales) return launch_prefill_w<D, W, true, true, false, true>(a, stream, ev);
     if (a.alibi) return launch_prefill_w<D, W, true, true, true>(a, stream, ev);
     return a.window > 0 || a.key_lo ? launch_prefill_w<D, W, true, true, false>(a, stream, ev)
                                     : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
@@ -978,7 +1036,9 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s) block=%d lds=%zu",
-           a.D, 32 * W, kPfBN, a.kv_fp8 ? "fp8-e4m3-widened" : "lds-dma",
+           a.D, 32 * W, kPfBN,
+           a.kv_fp8 ? (a.k_scales ? "fp8-e4m3-widened,scales per page" : "fp8-e4m3-widened")
+                    : "lds-dma",
            a.Hq * a.B * prefill_grid_tiles(a) * a.S, a.Hq, a.B, a.n_qt, a.S, order, 64 * W,
            a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;

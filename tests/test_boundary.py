@@ -232,6 +232,50 @@ def test_options_entry_points_check_their_options(lib):
         lib.paged_attn_prefill_workspace_bytes(1, 512, 512, 32, 128, 4)
 
 
+def test_page_scale_options_are_checked(lib):
+    """FP8 scales per (page, KV head): both arrays or neither, FP8 pools only, 4-byte
+    aligned; the page write's own entry point needs both; prefill does not combine
+    them with ALiBi slopes."""
+    from paged_kv_flashattention_amd import _lib
+    d = lib.paged_attn_decode_ex
+    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 16, 8, 2, 128, 0.1, 64]
+    ws = lib.paged_attn_decode_ex_workspace_bytes(2, 8, 2, 128, 64, None)
+    for fmt, ks, vs, st in [(1, FAKE, None, 1), (1, None, FAKE, 1), (0, FAKE, FAKE, 3),
+                            (1, FAKE + 2, FAKE, 4), (1, FAKE, FAKE + 1, 4)]:
+        o = _lib.DecodeOpts(1, 0, fmt, 1.0, 1.0)
+        o.k_scales, o.v_scales = ks, vs
+        assert d(*args, ctypes.byref(o), None, ws, None) == st, (fmt, ks, vs)
+        assert b"scales" in lib.pa_last_error()
+    p = lib.paged_attn_prefill_ex
+    pargs = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 4, 8, 16, 8, 2, 128, 0.1]
+    o = _lib.PrefillOpts(1, 0, 1)
+    o.kv_fp8, o.k_scale, o.v_scale, o.k_scales, o.v_scales = 1, 1.0, 1.0, FAKE, FAKE
+    o.alibi_slopes = FAKE
+    assert p(*pargs, ctypes.byref(o), None, 0, None) == 3
+    o.k_scales = None
+    assert p(*pargs, ctypes.byref(o), None, 0, None) == 1
+    w = lib.kv_page_write_fp8_scales
+    wb = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 8, 16, 2, 128, FAKE, FAKE, None]
+    for i, v, st in [(14, None, 1), (15, None, 1), (14, FAKE + 2, 4), (11, 8, 3), (4, None, 1)]:
+        bad = list(wb); bad[i] = v
+        assert w(*bad) == st, (i, v)
+    bad = list(wb); bad[8] = 0
+    assert w(*bad) == 0 and b"nothing" in lib.pa_describe_launch()
+
+
+def test_binding_takes_page_scales_as_tensor_pairs():
+    import paged_kv_flashattention_amd as pa
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    k8 = torch.zeros(4, 16, 2, 128, dtype=torch.uint8)
+    bt = torch.zeros(2, 2, dtype=torch.int32)
+    lens = torch.zeros(2, dtype=torch.int32)
+    sc = torch.ones(4, 2, dtype=torch.float32)
+    with pytest.raises(TypeError):       # a float and a tensor do not mix
+        pa.paged_attn_decode_fp8(q, k8, k8, bt, lens, 0.1, sc, 0.5)
+    with pytest.raises(TypeError):       # scales are float32
+        pa.paged_attn_decode_fp8(q, k8, k8, bt, lens, 0.1, sc.double(), sc.double())
+
+
 def test_binding_refuses_a_negative_window():
     import paged_kv_flashattention_amd as pa
     q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
