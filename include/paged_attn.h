@@ -478,6 +478,11 @@ typedef struct {
                                  [num_pages, Hkv] float32 scales per (page, KV head); not
                                  with ALiBi slopes (PA_ERR_UNSUPPORTED)                  */
   const float* v_scales;      /* with k_scales (both or neither)                          */
+  int32_t persistent;   /* 1: persistent work-groups (plain bf16 variant with 256-row query
+                           tiles only, else ignored): one per CU, each taking the grid's
+                           work items in turn and fetching the next item's Q rows and
+                           first K/V tile during the current item's last tile.  The
+                           results are the same bits as the plain grid's.  0: plain grid */
 } pa_prefill_opts;
 
 /*

@@ -568,7 +568,7 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                               lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                               stream=None, validate: bool = False, window_left: int = 0,
                               alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
-                              key_ranges=None):
+                              key_ranges=None, persistent: bool = False):
     """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
 
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
@@ -578,11 +578,13 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
     ``kernel_events`` as paged_attn_decode's, for the prefill kernel.
     ``key_ranges`` = (key_lo, key_hi), int32 [Tq] each on the device: document masks,
     row t sees keys key_lo[t] <= j < key_hi[t] of its sequence only.
+    ``persistent``: persistent work-groups with next-item prefetch (the ``persistent``
+    field of pa_prefill_opts; plain bf16 variant with 256-row tiles, else ignored).
     """
     return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
                     softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate,
                     window_left, alibi_slopes, kernel_events=kernel_events,
-                    key_ranges=key_ranges)
+                    key_ranges=key_ranges, persistent=persistent)
 
 
 def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
@@ -642,17 +644,21 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
                                      return_lse: bool = False, stream=None,
                                      validate: bool = False, window_left: int = 0,
                                      alibi_slopes: Optional[torch.Tensor] = None,
-                                     kernel_events=None, key_ranges=None):
+                                     kernel_events=None, key_ranges=None,
+                                     persistent: bool = False):
     """Ragged prefill with long key ranges cut into at most ``num_splits`` parts
-    (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C."""
+    (<= 0: the library's choice) and merged; see paged_attn_prefill_varlen_splitk in C.
+    ``persistent`` as paged_attn_prefill_varlen's."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
-                    validate, window_left, alibi_slopes, None, kernel_events, key_ranges)
+                    validate, window_left, alibi_slopes, None, kernel_events, key_ranges,
+                    persistent)
 
 
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
              causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
-             alibi_slopes=None, scales=None, kernel_events=None, key_ranges=None):
+             alibi_slopes=None, scales=None, kernel_events=None, key_ranges=None,
+             persistent=False):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -721,7 +727,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
         lo_ptr, hi_ptr = key_lo.data_ptr(), key_hi.data_ptr()
     ev0, ev1 = _events(kernel_events)
     general = (bool(window_left) or alibi_ptr is not None or scales is not None
-               or ev0 is not None or lo_ptr is not None)
+               or ev0 is not None or lo_ptr is not None or persistent)
     if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
@@ -743,7 +749,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
                 ksp, vsp = scales.check(k_pool.shape, dev)
             opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
                                     0 if scales is None else 1, ks, vs, ev0, ev1, lo_ptr, hi_ptr,
-                                    ksp, vsp)
+                                    ksp, vsp, 1 if persistent else 0)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

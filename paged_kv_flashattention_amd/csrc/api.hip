@@ -318,7 +318,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
                  float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
                  const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr,
-                 const float* k_scales = nullptr, const float* v_scales = nullptr) {
+                 const float* k_scales = nullptr, const float* v_scales = nullptr,
+                 int32_t persistent = 0) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -387,6 +388,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.key_hi = key_hi;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.persist = persistent ? 1 : 0;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -820,7 +822,8 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       D, softmax_scale, opts->causal, opts->num_splits, workspace,
                       workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
                       opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts),
-                      opts->key_lo, opts->key_hi, opts->k_scales, opts->v_scales);
+                      opts->key_lo, opts->key_hi, opts->k_scales, opts->v_scales,
+                      opts->persistent);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

@@ -84,6 +84,7 @@ struct PrefillArgs {
   const int32_t* key_hi;         //   row, or both null (no document masks)
   const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
   const float* v_scales;         //   or null: one scale per pool
+  int persist;                   // persistent work-groups (plain bf16 variant, 8 waves)
 };
 
 // Optional events stamped with one kernel's own start and end: the dispatch

@@ -21,6 +21,7 @@
 #include <limits.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -111,6 +112,9 @@ struct PfLds {
   static constexpr int V_STAGES = 3;              // V of tiles t - 1 .. t + 1
   static constexpr int V0 = K_STAGES * TILE;      // first V stage
   static constexpr size_t BYTES = (size_t)(K_STAGES + V_STAGES) * TILE * sizeof(uint16_t);
+  // persistent work-groups: the next item's Q rows (32 per wave) after the stages
+  static constexpr int Q0 = (K_STAGES + V_STAGES) * TILE;
+  static constexpr size_t q_bytes(int W) { return (size_t)32 * W * D * sizeof(uint16_t); }
 };
 
 // 16 bytes per lane from global memory straight into LDS: lane i reads
@@ -221,27 +225,15 @@ __device__ __forceinline__ u32x2 pf_fp8x4_to_bf16(uint32_t w) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
 }
 
-// W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
-// variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
-// downwards, which is how the ALiBi variants (general only) walk, so REV also
-// compiles the bias in.
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
-__global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
-  static_assert(!REV || GEN, "the downward walk is a general-variant feature");
-  static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
-  constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
-  extern __shared__ __align__(16) uint16_t pf_lds[];
-  using L_ = PfLds<D>;
-  using M_ = PfDma<D, W>;
-  constexpr int kPfBM = 32 * W;       // query rows per work-group
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31;         // query column of S^T / O^T
-  const int hh = lane >> 5;          // k-half of the MFMA operands
-  const int g16 = lane & 15;
-  // Work-group -> (query head h, sequence b, query tile qt, key part).  Work-groups
-  // are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  With
+// A work item: query rows 32 W qt .. 32 W qt + 32 W - 1 of query head h of sequence
+// b, over key part `part` of their key tiles.
+struct PfWork {
+  int h, b, qt, part;
+};
+
+__device__ __forceinline__ PfWork pf_work_of(const PrefillArgs& a, int p) {
+  // Item p -> (query head h, sequence b, query tile qt, key part).  Items (one per
+  // work-group of the plain grid, whose id is p) are handed to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  With
   // xcd_groups set, the work is cut into units -- a (sequence, KV head) group or,
   // when the group count is not a multiple of 8, one of xcd_split classes of its
   // query-tile ranks, so that the units divide evenly among the XCDs (ranks are
@@ -252,9 +244,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // next unit's heavy tiles start while the previous one's light ones finish.
   // Without it the order is head-major, heaviest tiles first.  Either way all key
   // parts of a tile start together and every XCD keeps its share of the unsplit work.
-  int h, b, qt, part;
+  PfWork w;
   {
-    const int p = blockIdx.x;
     if (a.xcd_groups) {
       const int m = a.xcd_split;
       const int tpu = (a.n_qt + m - 1) / m;      // tile ranks per unit
@@ -264,46 +255,106 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       const int rem = k - ui * per_unit;
       const int r2 = rem / a.G;                  // (tile rank in unit, part), heaviest first
       const int rl = r2 / a.S;
-      part = r2 - rl * a.S;
+      w.part = r2 - rl * a.S;
       const int u = (p & 7) + 8 * ui;            // unit = group g, rank class j
       const int g = u / m;
       const int j = u - g * m;
       // ranks dealt to the classes zig-zag (0 .. m-1, then m-1 .. 0, ...), so every
       // class holds as much heavy as light causal work
       const int rank = rl * m + ((rl & 1) ? m - 1 - j : j);
-      b = g / a.Hkv;
-      h = (g - b * a.Hkv) * a.G + rem % a.G;
-      qt = a.n_qt - 1 - rank;                    // below 0: past the unit's last tile
+      w.b = g / a.Hkv;
+      w.h = (g - w.b * a.Hkv) * a.G + rem % a.G;
+      w.qt = a.n_qt - 1 - rank;                    // below 0: past the unit's last tile
     } else {
-      h = p % a.Hq;
+      w.h = p % a.Hq;
       const int r = p / a.Hq;
-      b = r % a.B;
+      w.b = r % a.B;
       const int r2 = r / a.B;
       const int rank = r2 / a.S;
-      part = r2 - rank * a.S;
-      qt = a.n_qt - 1 - rank;
+      w.part = r2 - rank * a.S;
+      w.qt = a.n_qt - 1 - rank;
     }
   }
 
-  if (qt < 0) return;
-  const int t0 = a.cu_seqlens_q[b];
-  const int q_len = a.cu_seqlens_q[b + 1] - t0;
-  const int r_wg = qt * kPfBM;
-  if (r_wg >= q_len) return;
-  int L = a.seq_lens_k[b];
+  return w;
+}
+
+// What an item covers: its sequence's query rows start at token t0, q_len of them,
+// over L keys; its first row r_wg; its KV head; the key tiles tile_lo .. tile_hi - 1
+// (part `part` of `parts`).  ok = 0 for an item past its sequence's last query tile
+// or key part.
+struct PfSetup {
+  int ok, t0, q_len, L, r_wg, kvh, tile_lo, tile_hi, parts;
+};
+
+template <bool GEN>
+__device__ __forceinline__ PfSetup pf_setup(const PrefillArgs& a, const PfWork& w, int bm,
+                                            int lane) {
+  PfSetup s{};
+  if (w.qt < 0) return s;
+  s.t0 = a.cu_seqlens_q[w.b];
+  s.q_len = a.cu_seqlens_q[w.b + 1] - s.t0;
+  s.r_wg = w.qt * bm;
+  if (s.r_wg >= s.q_len) return s;
+  const int L = a.seq_lens_k[w.b];
   const int cap = a.max_pages * a.page_size;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int kvh = h / a.G;
+  s.L = L < 0 ? 0 : (L > cap ? cap : L);
+  s.kvh = w.h / a.G;
+  // keys past the item's last row are never needed; with key splitting the item
+  // covers tiles tile_lo .. tile_hi - 1 of them
+  const PfTiles tw = pf_tiles<GEN>(a, s.L, s.q_len, s.r_wg, bm, s.t0, lane);
+  if (w.part >= tw.parts) return s;
+  s.parts = tw.parts;
+  s.tile_lo = tw.first + w.part * (tw.n - tw.first) / tw.parts;
+  s.tile_hi = tw.first + (w.part + 1) * (tw.n - tw.first) / tw.parts;
+  s.ok = 1;
+  return s;
+}
+
+// Hand-over between consecutive items of a persistent work-group: during an item's
+// last tile the work-group already issues the next item's first K/V tile (into the
+// stages that follow the item's own), copies the next item's Q rows into the LDS Q
+// area and holds its block-table window, so that the next item starts on data in LDS
+// instead of waiting for its table, Q and first tile in turn.
+struct PfHand {
+  int has;        // this item's first tile was issued by the previous item
+  int q_lds;      //   and its Q rows sit in the LDS Q area
+  int kc, vc;     // K and V stage of this item's first tile
+  int tab;        // this item's block-table window (per lane), when has
+  int pn;         // the item after this one (its id), or -1
+};
+
+// W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
+// variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
+// downwards, which is how the ALiBi variants (general only) walk, so REV also
+// compiles the bias in.  PER: an item of a persistent work-group (hand-over in hd).
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER>
+__device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
+                                        const PfSetup& s, PfHand& hd, uint16_t* pf_lds) {
+  static_assert(!REV || GEN, "the downward walk is a general-variant feature");
+  static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
+  static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
+  constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
+  using L_ = PfLds<D>;
+  using M_ = PfDma<D, W>;
+  constexpr int kPfBM = 32 * W;       // query rows per work-group
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;         // query column of S^T / O^T
+  const int hh = lane >> 5;          // k-half of the MFMA operands
+  const int g16 = lane & 15;
+  const int h = w.h, b = w.b, part = w.part;
+  const int t0 = s.t0, q_len = s.q_len, r_wg = s.r_wg, L = s.L, kvh = s.kvh;
+  const int tile_lo = s.tile_lo, tile_hi = s.tile_hi;
   const uint16_t* kbase = a.k_pool + (size_t)kvh * D;
   const uint16_t* vbase = a.v_pool + (size_t)kvh * D;
-
-  // keys past this work-group's last row are never needed; with key splitting this
-  // work-group covers tiles tile_lo .. tile_hi - 1 of them
   const int shift = L - q_len;                 // position of row r is shift + r
-  const PfTiles tw = pf_tiles<GEN>(a, L, q_len, r_wg, kPfBM, t0, lane);
-  if (part >= tw.parts) return;
-  const int tile_lo = tw.first + part * (tw.n - tw.first) / tw.parts;
-  const int tile_hi = tw.first + (part + 1) * (tw.n - tw.first) / tw.parts;
+  // what the previous item of a persistent work-group prefetched for this one
+  const bool pre = PER && hd.has;
+  const bool q_pre = PER && hd.q_lds;
+  const int kc = PER ? hd.kc : 0, vc = PER ? hd.vc : 0;
+  if constexpr (PER) hd.has = hd.q_lds = 0;
 
   // this wave's rows and the position bound of its rows
   const int r_w = r_wg + 32 * wave;
@@ -354,7 +405,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 
   // Q^T operand: lane holds Q[row col][16 kk + 8 hh + j]
   u32x4 qb[D / 16];
-  {
+  if (!q_pre) {
     const uint16_t* qp = a.q + ((size_t)(t0 + (row_ok ? my_row : 0)) * a.Hq + h) * D + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qb[kk] = row_ok ? ld16(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
@@ -387,11 +438,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
   int base_t = 0;
   int tab = 0;
-  auto load_tab = [&](int first_tile) {
+  auto load_tab_of = [&](const int32_t* bt_, int first_tile) {
     int idx = ((first_tile + lane) * kPfBN + 16 * M_::region(wave)) >> a.ps_shift;
     idx = idx < a.max_pages ? idx : a.max_pages - 1;
-    return bt[idx];
+    return bt_[idx];
   };
+  auto load_tab = [&](int first_tile) { return load_tab_of(bt, first_tile); };
   const int run0 = (16 * M_::region(wave)) & (a.page_size - 1);
   const int rs = a.Hkv * D;
   // the global chunk each lane's DMA slot receives: slot 64 j + lane = line c,
@@ -423,16 +475,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) float pg_scales[PS ? 3 : 1][8];
   float ks_next = 1.f, vs_next = 1.f;
   // DMA of tile n (tiles are issued in increasing order) into V stage vs
-  auto issue = [&](int n, int vs) {
-    if (REV ? n < base_t : n - base_t >= 64) {
-      base_t = REV ? max(0, n - 63) : base_t + 64;
-      tab = load_tab(base_t);
-    }
-    int pg = __builtin_amdgcn_readlane(tab, n - base_t);
+  // DMA of the tile of page pg (KV head kvh_) into K stage ks and V stage vs
+  auto issue_page = [&](int pg, int kvh_, int ks, int vs) {
     pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
     if constexpr (PS) {
-      ks_next = a.k_scales[(size_t)pg * a.Hkv + kvh];
-      vs_next = a.v_scales[(size_t)pg * a.Hkv + kvh];
+      ks_next = a.k_scales[(size_t)pg * a.Hkv + kvh_];
+      vs_next = a.v_scales[(size_t)pg * a.Hkv + kvh_];
     }
     if constexpr (F8) {
       const size_t base = ((size_t)pg * a.page_size + run0) * rs;
@@ -444,15 +492,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
           const size_t off = base + (size_t)(piece / F8_PPR) * rs + 16 * (piece % F8_PPR);
           k8[k] = *reinterpret_cast<const u32x4*>(kbase8 + off);
           v8[k] = *reinterpret_cast<const u32x4*>(vbase8 + off);
+          (void)kvh_;
         }
       }
     } else {
-      pf_issue_tile<D, W>(kst(n), vst(vs), kbase, vbase, (size_t)pg * a.page_size + run0, rs,
+      pf_issue_tile<D, W>(kst(ks), vst(vs), a.k_pool + (size_t)kvh_ * D,
+                          a.v_pool + (size_t)kvh_ * D, (size_t)pg * a.page_size + run0, rs,
                           k_dma, v_dma, wave);
     }
   };
+  auto issue = [&](int n, int ks, int vs) {
+    if (REV ? n < base_t : n - base_t >= 64) {
+      base_t = REV ? max(0, n - 63) : base_t + 64;
+      tab = load_tab(base_t);
+    }
+    issue_page(__builtin_amdgcn_readlane(tab, n - base_t), kvh, ks, vs);
+  };
   // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
-  auto publish = [&](int n, int vs) {
+  auto publish = [&](int n, int ks, int vs) {
     vmcnt_wait<0>();
     if constexpr (PS) {
       // region r holds keys 16 r .. 16 r + 15 of the tile: half r % 2 of block r / 2
@@ -463,7 +520,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       }
     }
     if constexpr (F8) {
-      uint16_t* kr = kst(n) + M_::region(wave) * PfLds<D>::REGION;
+      uint16_t* kr = kst(ks) + M_::region(wave) * PfLds<D>::REGION;
       uint16_t* vr = vst(vs) + M_::region(wave) * PfLds<D>::REGION;
       const int row0 = n * kPfBN + 16 * M_::region(wave);
 #pragma unroll
@@ -744,20 +801,77 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     settle(sp, bs, pw, ps);
     pv(vst(vsi), kbp, u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]});
   };
+  // stages of the walk's k-th tile: K (kc + k) mod 2, V (vc + k) mod 3; the next
+  // item of a persistent work-group takes the stages after this item's last tile
+  if constexpr (PER) {
+    hd.kc = (kc + nt) & 1;
+    hd.vc = (vc + nt) % 3;
+  }
+  // The next item of a persistent work-group, as far as its prefetch needs it: its
+  // KV head, its block-table window and where this wave's share of its Q rows is.
+  int nx_do = 0, nx_kvh = 0, nx_qok = 0, tab_nx = 0;
+  const uint16_t* nx_q = a.q;
+  uint32_t nx_qoff = 0;
+  auto next_item = [&]() {
+    if (hd.pn < 0) return;
+    const PfWork nw = pf_work_of(a, hd.pn);
+    const PfSetup ns = pf_setup<GEN>(a, nw, kPfBM, lane);
+    if (!(ns.tile_hi > ns.tile_lo)) return;
+    nx_do = 1;
+    nx_kvh = ns.kvh;
+    tab_nx = load_tab_of(a.block_tables + (size_t)nw.b * a.max_pages, ns.tile_lo);
+    // Q rows r_wg + 32 wave .. of the next item, 16 bytes per lane and instruction:
+    // lane i takes row i % 32, columns 16 kk + 8 (i / 32) .. (the Q^T operand's
+    // layout), rows past the query run clamped to its last row (zeroed when read)
+    const int lim_row = min(ns.q_len, a.Tq - ns.t0) - 1;
+    nx_qok = lim_row >= 0;
+    const int row0 = max(0, min(ns.r_wg + 32 * wave, lim_row));
+    const int rel = max(0, min(ns.r_wg + 32 * wave + col, lim_row) - row0);
+    nx_q = a.q + ((size_t)(ns.t0 + row0) * a.Hq + nw.h) * D;
+    nx_qoff = (uint32_t)((rel * a.Hq * D + hh * 8) * 2);
+  };
+  // the next item's first tile and Q rows, issued as the tile after this item's last
+  auto prefetch = [&](int ks, int vs) {
+    issue_page(__builtin_amdgcn_readlane(tab_nx, 0), nx_kvh, ks, vs);
+    hd.has = 1;
+    hd.tab = tab_nx;
+    if (nx_qok) {
+      uint16_t* ql = pf_lds + L_::Q0 + wave * 32 * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) dma16(nx_q, nx_qoff + 32u * kk, ql + 512 * kk);
+      hd.q_lds = 1;
+    }
+  };
+  // DMA of the walk's k-th tile, or past the last one the next item's first
+  auto issue_walk = [&](int k) {
+    if (k < nt) {
+      issue(tile_at(k), (kc + k) & 1, (vc + k) % 3);
+    } else if constexpr (PER) {
+      if (k == nt && nx_do) prefetch((kc + k) & 1, (vc + k) % 3);
+    }
+  };
   if (nt > 0) {
     base_t = REV ? max(0, tile_hi - 64) : tile_lo;
-    tab = load_tab(base_t);
-    int vs_cur = 0;                       // V stage of the walk's current tile
-    issue(tile_at(0), 0);
-    publish(tile_at(0), 0);
-    if (nt > 1) issue(tile_at(1), 1);
+    tab = pre ? hd.tab : load_tab(base_t);
+    int vs_cur = vc;                      // V stage of the walk's current tile
+    int ks_cur = kc;                      // K stage of the walk's current tile
+    if (!pre) issue(tile_at(0), kc, vc);
+    publish(tile_at(0), kc, vc);
+    if (q_pre) {
+      const uint16_t* ql = pf_lds + L_::Q0 + wave * 32 * D + 8 * lane;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qb[kk] = row_ok ? *reinterpret_cast<const u32x4*>(ql + 512 * kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (PER) next_item();
+    issue_walk(1);
     // G: blocks this wave computes, in walk order (wave-uniform)
     const int G = REV ? 2 * nt
                       : min(2 * nt, max(0, (w_key_end - tile_lo * kPfBN + 31) / 32));
     // first block: scores, mask, first reference
     f32x16 s_pend;
     if (G > 0) {
-      s_pend = qk(kst(tile_at(0)), B0);
+      s_pend = qk(kst(ks_cur), B0);
       mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
       decide(rowmax(s_pend, blk_scale(0, B0)));
     }
@@ -768,21 +882,22 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // first block of tile kt (pending) -> its second block
-      step(s_pend, kst(kt), B1, vs_cur, B0);
+      step(s_pend, kst(ks_cur), B1, vs_cur, B0);
       mask(s_pend, kt * kPfBN + 32 * B1);
       // second block of tile kt -> first block of tile kn
-      publish(kn, vs_next);
-      if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
-      step(s_pend, kst(kn), B0, vs_cur, B1);
+      publish(kn, ks_cur ^ 1, vs_next);
+      issue_walk(u + 2);
+      step(s_pend, kst(ks_cur ^ 1), B0, vs_cur, B1);
       mask(s_pend, kn * kPfBN + 32 * B0);
       vs_cur = vs_next;
+      ks_cur ^= 1;
     }
     if (u == nt - 1) {
       // the last tile: both of its blocks (G = 2 nt), only its first (G = 2 nt - 1),
       // or none (G = 0, one tile)
       const int kl = tile_at(u);
       if (G == 2 * nt) {
-        step(s_pend, kst(kl), B1, vs_cur, B0);
+        step(s_pend, kst(ks_cur), B1, vs_cur, B0);
         mask(s_pend, kl * kPfBN + 32 * B1);
         finish(s_pend, vs_cur, B1);
       } else if (G == 2 * nt - 1) {
@@ -793,21 +908,23 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       if (G == 2 * u + 2) {
-        step(s_pend, kst(kt), B1, vs_cur, B0);
+        step(s_pend, kst(ks_cur), B1, vs_cur, B0);
         mask(s_pend, kt * kPfBN + 32 * B1);
       } else if (G == 2 * u + 1) {
         finish(s_pend, vs_cur, B0);
       }
-      publish(kn, vs_next);
-      if (u + 2 < nt) issue(tile_at(u + 2), vs_next == 2 ? 0 : vs_next + 1);
+      publish(kn, ks_cur ^ 1, vs_next);
+      issue_walk(u + 2);
       if (G == 2 * u + 2) finish(s_pend, vs_cur, B1);
       vs_cur = vs_next;
+      ks_cur ^= 1;
       // the remaining tiles: this wave's share of each is moved, nothing computed
       for (++u; u + 1 < nt; ++u) {
         const int vs_n = vs_cur == 2 ? 0 : vs_cur + 1;
-        publish(tile_at(u + 1), vs_n);
-        if (u + 2 < nt) issue(tile_at(u + 2), vs_n == 2 ? 0 : vs_n + 1);
+        publish(tile_at(u + 1), ks_cur ^ 1, vs_n);
+        issue_walk(u + 2);
         vs_cur = vs_n;
+        ks_cur ^= 1;
       }
     }
   }
@@ -817,7 +934,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const bool live = l_tot > 0.f;
   const float inv = live ? (F8 ? a.v_scale : 1.f) / l_tot : 0.f;
   const float lse = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
-  if (tw.parts > 1) {
+  if (s.parts > 1) {
     // this part's normalised output and lse, merged by the prefill merge kernel
     const size_t prow = ((size_t)(t0 + my_row) * a.Hq + h) * a.S + part;
     float* po = a.part_o + prow * D;
@@ -842,6 +959,54 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x2*>(op + 32 * t + 8 * j + 4 * hh) = w;
     }
   if (hh == 0 && a.lse_out) a.lse_out[(size_t)(t0 + my_row) * a.Hq + h] = lse;
+}
+
+// One work-group per item of the plain grid (item = blockIdx.x).
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
+__global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) uint16_t pf_lds[];
+  const PfWork w = pf_work_of(a, blockIdx.x);
+  const PfSetup s = pf_setup<GEN>(a, w, 32 * W, threadIdx.x & 63);
+  if (!s.ok) return;
+  PfHand hd{};
+  pf_item<D, W, GEN, F8, REV, PS, false>(a, w, s, hd, pf_lds);
+}
+
+// Persistent work-groups: one per CU, a multiple of 8 of them, each working through
+// items of the plain grid's order one after the other, with the hand-over above.  The
+// work-group j sits on XCD j mod 8 and takes only that XCD's items (ids p with
+// p mod 8 = j mod 8, the ids the plain grid sends there), in rounds over the XCD's
+// work-groups that alternate in direction (round r hands the XCD's items
+// r P8 .. r P8 + P8 - 1, P8 work-groups per XCD, to its work-groups in ascending, then
+// descending order), so that the heaviest-first order of the items pairs heavy with
+// light ones on every work-group.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 1) void prefill_persist_kernel(PrefillArgs a,
+                                                                    int n_items) {
+  extern __shared__ __align__(16) uint16_t pf_lds[];
+  const int x = blockIdx.x & 7, jx = blockIdx.x >> 3, p8 = gridDim.x >> 3;
+  const int lane = threadIdx.x & 63;
+  auto item_at = [&](int r) { return 8 * (r * p8 + ((r & 1) ? p8 - 1 - jx : jx)) + x; };
+  // the first item of round r or later that has work, or -1
+  auto find = [&](int r) {
+    for (;; ++r) {
+      const int p = item_at(r);
+      if (p >= n_items) return -1;
+      if (pf_setup<false>(a, pf_work_of(a, p), 32 * W, lane).ok) return r;
+    }
+  };
+  int r = find(0);
+  if (r < 0) return;
+  PfHand hd{};
+  for (;;) {
+    const PfWork w = pf_work_of(a, item_at(r));
+    const PfSetup s = pf_setup<false>(a, w, 32 * W, lane);
+    const int rn = find(r + 1);
+    hd.pn = rn < 0 ? -1 : item_at(rn);
+    pf_item<D, W, false, false, false, false, true>(a, w, s, hd, pf_lds);
+    if (rn < 0) return;
+    r = rn;
+  }
 }
 
 // Merge of the query tiles that were cut into key-range parts ("The Stack Below
@@ -921,31 +1086,84 @@ static int prefill_grid_tiles(const PrefillArgs& a) {
   return a.xcd_groups ? (a.n_qt + a.xcd_split - 1) / a.xcd_split * a.xcd_split : a.n_qt;
 }
 
+constexpr int kMaxDevices = 64;
+
+// More than 64 KiB of dynamic LDS is requested for a kernel once per device (the
+// first launch on each device sets it; concurrent first launches both set it, which
+// is harmless).  state (one per kernel and device): 0 not yet, 1 set, 2 + error code
+// otherwise.
+static hipError_t lds_attribute_once(std::atomic<int>* state, const void* kernel,
+                                     size_t bytes) {
+  int dev = 0;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return de;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int st = state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    const hipError_t e =
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
+    return e;
+  }
+  return st == 1 ? hipSuccess : (hipError_t)(st - 2);
+}
+
+// compute units of the current device (read once per device)
+static hipError_t device_cus(int* cus) {
+  static std::atomic<int> known[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int n = known[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    known[dev].store(n, std::memory_order_release);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
+// items of the plain grid (one per work-group there)
+static int prefill_items(const PrefillArgs& a) {
+  return a.Hq * a.B * prefill_grid_tiles(a) * a.S;
+}
+
+// persistent work-groups for a launch: one per CU, a multiple of 8, no more than
+// the items need
+static int prefill_persist_groups(const PrefillArgs& a, int cus) {
+  const int n = prefill_items(a);
+  return std::max(8, std::min(cus / 8 * 8, (n + 7) / 8 * 8));
+}
+
+template <int D>
+static hipError_t launch_prefill_persist(const PrefillArgs& a, hipStream_t stream,
+                                         const KernelEvents& ev) {
+  constexpr size_t lds = PfLds<D>::BYTES + PfLds<D>::q_bytes(8);
+  static std::atomic<int> state[kMaxDevices];
+  hipError_t e = lds_attribute_once(
+      state, reinterpret_cast<const void*>(prefill_persist_kernel<D, 8>), lds);
+  if (e != hipSuccess) return e;
+  int cus = 0;
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  launch_kernel(prefill_persist_kernel<D, 8>, dim3(prefill_persist_groups(a, cus)), dim3(512),
+                (uint32_t)lds, stream, ev, a, prefill_items(a));
+  return hipGetLastError();
+}
+
 template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
-  // more than 64 KiB of dynamic LDS is requested for the kernel once per device (the
-  // first launch on each device sets it; concurrent first launches both set it, which
-  // is harmless).  state: 0 not yet, 1 set, 2 + error code otherwise.
   if constexpr (PfLds<D>::BYTES > 65536) {
-    constexpr int kMaxDevices = 64;
     static std::atomic<int> state[kMaxDevices];
-    int dev = 0;
-    const hipError_t de = hipGetDevice(&dev);
-    if (de != hipSuccess) return de;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    const int st = state[dev].load(std::memory_order_acquire);
-    if (st == 0) {
-      const hipError_t e =
-          hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)PfLds<D>::BYTES);
-      state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
-      if (e != hipSuccess) return e;
-    } else if (st != 1) {
-      return (hipError_t)(st - 2);
-    }
+    const hipError_t e = lds_attribute_once(
+        state, reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS>),
+        PfLds<D>::BYTES);
+    if (e != hipSuccess) return e;
   }
-  dim3 grid(a.Hq * a.B * prefill_grid_tiles(a) * a.S);
+  dim3 grid(prefill_items(a));
   launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS>, grid, dim3(64 * W),
                 (uint32_t)PfLds<D>::BYTES, stream, ev, a);
   return hipGetLastError();
@@ -964,8 +1182,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                     : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
   }
   if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
-  return a.window > 0 || a.key_lo ? launch_prefill_w<D, W, true, false, false>(a, stream, ev)
-                                  : launch_prefill_w<D, W, false, false, false>(a, stream, ev);
+  if (a.window > 0 || a.key_lo) return launch_prefill_w<D, W, true, false, false>(a, stream, ev);
+  if (W == 8 && a.persist) return launch_prefill_persist<D>(a, stream, ev);
+  return launch_prefill_w<D, W, false, false, false>(a, stream, ev);
 }
 
 // Waves per work-group: 8 (256 query rows, half the K/V traffic per row) when the
@@ -1033,14 +1252,21 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
   else
     snprintf(order, sizeof(order), "KV groups in %d rank classes per XCD, unit-major",
              a.xcd_split);
+  const bool per = W == 8 && a.persist && !a.kv_fp8 && !a.alibi && a.window == 0 && !a.key_lo;
+  char pers[96] = "";
+  int cus = 0;
+  if (per && device_cus(&cus) == hipSuccess)
+    snprintf(pers, sizeof(pers), ", persistent: %d work-groups with next-item prefetch",
+             prefill_persist_groups(a, cus));
+  const size_t lds = (a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES) +
+                     (per ? (a.D == 128 ? PfLds<128>::q_bytes(8) : PfLds<64>::q_bytes(8)) : 0);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
-           "q-tiles x %d key parts, %s) block=%d lds=%zu",
+           "q-tiles x %d key parts, %s%s) block=%d lds=%zu",
            a.D, 32 * W, kPfBN,
            a.kv_fp8 ? (a.k_scales ? "fp8-e4m3-widened,scales per page" : "fp8-e4m3-widened")
                     : "lds-dma",
-           a.Hq * a.B * prefill_grid_tiles(a) * a.S, a.Hq, a.B, a.n_qt, a.S, order, 64 * W,
-           a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
+           prefill_items(a), a.Hq, a.B, a.n_qt, a.S, order, pers, 64 * W, lds);
   return e;
 }
 
