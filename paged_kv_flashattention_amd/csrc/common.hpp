@@ -144,4 +144,31 @@ struct PageWindow {
   }
 };
 
+// 16 bytes per lane from global memory straight into LDS: lane i reads
+// sbase + voff_i (a wave-uniform base address in SGPRs plus a 32-bit per-lane byte
+// offset) and its bytes land at lds_wave_base + 16 i (gfx950
+// global_load_lds_dwordx4, LDS base in M0).  Written as inline assembly so that
+// the compiler, which cannot tell which LDS reads such a load may feed, does not
+// wait for every outstanding one before each LDS read; completion is waited for
+// explicitly (vmcnt_wait) before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff,
+                                      uint16_t* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0", "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier that the compiler may not move memory operations across
+// (the hardware barrier alone; the waits it needs are issued explicitly).
+__device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace pa

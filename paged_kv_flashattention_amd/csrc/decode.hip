@@ -551,7 +551,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, si
                             : launch_decode_d<64>(a, stream, W, ev);
   snprintf(desc, desc_len,
            "decode_partition<D=%d,W=%d,%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
-           W, a.kv_fp8 ? (a.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
+           W, a.kv_fp8 ? (a.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16", a.Hkv,
+           a.S, a.B, 64 * W, a.part_len, a.S);
   return e;
 }
 

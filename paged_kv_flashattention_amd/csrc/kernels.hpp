@@ -3,6 +3,8 @@
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -93,6 +95,28 @@ struct KernelEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
+
+constexpr int kMaxDevices = 64;
+
+// More than 64 KiB of dynamic LDS is requested for a kernel once per device (the
+// first launch on each device sets it; concurrent first launches both set it, which
+// is harmless).  state (one per kernel and device): 0 not yet, 1 set, 2 + error code
+// otherwise.
+inline hipError_t lds_attribute_once(std::atomic<int>* state, const void* kernel,
+                                     size_t bytes) {
+  int dev = 0;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return de;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int st = state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    const hipError_t e =
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
+    return e;
+  }
+  return st == 1 ? hipSuccess : (hipError_t)(st - 2);
+}
 
 template <typename... Args>
 inline void launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds,

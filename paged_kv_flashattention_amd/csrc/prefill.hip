@@ -117,33 +117,6 @@ struct PfLds {
   static constexpr size_t q_bytes(int W) { return (size_t)32 * W * D * sizeof(uint16_t); }
 };
 
-// 16 bytes per lane from global memory straight into LDS: lane i reads
-// sbase + voff_i (a wave-uniform base address in SGPRs plus a 32-bit per-lane byte
-// offset) and its bytes land at lds_wave_base + 16 i (gfx950
-// global_load_lds_dwordx4, LDS base in M0).  Written as inline assembly so that
-// the compiler, which cannot tell which LDS reads such a load may feed, does not
-// wait for every outstanding one before each LDS read; completion is waited for
-// explicitly (vmcnt_wait) before the barrier that publishes a tile.
-__device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff,
-                                      uint16_t* lds_wave_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "m0", "memory");
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void vmcnt_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Work-group barrier that the compiler may not move memory operations across
-// (the hardware barrier alone; the waits it needs are issued explicitly).
-__device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
-
 // max(a, b, c) in one instruction.  The scores compared here come from MFMA
 // accumulators and cannot be signalling NaNs, so the quieting that fmaxf needs
 // before each comparison is not needed.
@@ -1084,28 +1057,6 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
 // xcd_split in the unit-major order (the surplus work-groups return at once)
 static int prefill_grid_tiles(const PrefillArgs& a) {
   return a.xcd_groups ? (a.n_qt + a.xcd_split - 1) / a.xcd_split * a.xcd_split : a.n_qt;
-}
-
-constexpr int kMaxDevices = 64;
-
-// More than 64 KiB of dynamic LDS is requested for a kernel once per device (the
-// first launch on each device sets it; concurrent first launches both set it, which
-// is harmless).  state (one per kernel and device): 0 not yet, 1 set, 2 + error code
-// otherwise.
-static hipError_t lds_attribute_once(std::atomic<int>* state, const void* kernel,
-                                     size_t bytes) {
-  int dev = 0;
-  const hipError_t de = hipGetDevice(&dev);
-  if (de != hipSuccess) return de;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  const int st = state[dev].load(std::memory_order_acquire);
-  if (st == 0) {
-    const hipError_t e =
-        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    state[dev].store(e == hipSuccess ? 1 : 2 + (int)e, std::memory_order_release);
-    return e;
-  }
-  return st == 1 ? hipSuccess : (hipError_t)(st - 2);
 }
 
 // compute units of the current device (read once per device)
