@@ -32,6 +32,7 @@ from .attention import (  # noqa: F401
     attend_rows,
     attention_ref,
     attention_rows_ref,
+    block_map_mask,
     softmax_probs_ref,
     tiled_attend_rows,
     split_partials_ref,

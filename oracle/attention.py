@@ -46,6 +46,16 @@ R6  Document masks: the same section names document masking among the mask
     positions of its own document; the row sees key j only if
     key_lo <= j < key_hi, on top of the causal bound and the window.  No
     ranges means every row's range is the whole sequence.
+R7  Mask functions: the same section shows a mask written as a predicate of
+    (sequence b, head h, query index, key index) and compiled with
+    create_block_mask, which records per (query block, key block) whether the
+    block needs the predicate at all.  Reading: a general mask is such a predicate
+    with the query index counted within the sequence's query run (row i of the
+    run, 0-based) and the key index within the sequence; the row sees key j only
+    if the predicate holds, on top of the causal bound, the window and the
+    document range.  A block map is the block form of a predicate that is
+    constant on blocks: entry [b][i // 64][j // 64] (nonzero: visible); entries
+    outside the map count as zero.
 """
 
 from __future__ import annotations
@@ -60,6 +70,7 @@ __all__ = [
     "attend_rows",
     "attention_ref",
     "attention_rows_ref",
+    "block_map_mask",
     "softmax_probs_ref",
     "tiled_attend_rows",
     "split_partials_ref",
@@ -103,14 +114,15 @@ def gather_sequence_kv(pool, table_row, seq_len: int, page_size: int) -> np.ndar
 
 
 def attend_rows(q_rows, k, v, scale: float, visible, first=None, slope: float = 0.0,
-                pos=None):
+                pos=None, allowed=None):
     """Plain softmax attention for a set of query rows against one key head.
 
     ``q_rows`` [n, D], ``k``/``v`` [L, D], ``visible`` [n] = number of leading
     keys each row may see; ``first`` [n] (optional) = index of the first key
     each row may see (R4; default 0); ``slope`` with ``pos`` [n] (the rows'
     absolute positions) adds slope * (j - pos_i) to every score (R5).  Returns
-    (O [n, D], lse [n]) in float64.
+    (O [n, D], lse [n]) in float64.  ``allowed`` [n, L] (optional, boolean): a
+    general mask on top of the others (R7); False hides the key.
 
     This is the definition the tiled method must reproduce exactly ("8.
     Kernels and Attention Backends", "Attention is an I/O problem": scores
@@ -136,6 +148,8 @@ def attend_rows(q_rows, k, v, scale: float, visible, first=None, slope: float = 
     if first is not None:
         first = np.asarray(first, dtype=np.int64).reshape(n)
         mask |= np.arange(L)[None, :] < first[:, None]
+    if allowed is not None:
+        mask |= ~np.broadcast_to(np.asarray(allowed, dtype=bool), (n, L))
     s = np.where(mask, -np.inf, s)
     m = s.max(axis=1)
     live = np.isfinite(m)
@@ -181,13 +195,43 @@ def _document_bounds(vis, first, key_ranges, t0, t1):
     return np.minimum(vis, hi), np.maximum(first, lo)
 
 
+def block_map_mask(block_map, block: int = 64):
+    """The predicate of a block map (R7): ``block_map`` [B, QB, KB], entry
+    [b][i // block][j // block] nonzero when query row i (of the sequence's query
+    run) may see key j; entries outside the map count as zero."""
+    bm = np.asarray(block_map)
+    if bm.ndim != 3:
+        raise ValueError("block_map must be [B, query blocks, key blocks]")
+
+    def pred(b, h, q_idx, kv_idx):
+        qb = np.asarray(q_idx) // block
+        kb = np.asarray(kv_idx) // block
+        qb, kb = np.broadcast_arrays(qb, kb)
+        inside = (qb < bm.shape[1]) & (kb < bm.shape[2])
+        out = np.zeros(qb.shape, dtype=bool)
+        out[inside] = bm[b][qb[inside], kb[inside]] != 0
+        return out
+    return pred
+
+
+def _allowed(mask_fn, b, h, n, L):
+    """[n, L] boolean of a predicate (R7) over the rows and keys of one sequence."""
+    if mask_fn is None:
+        return None
+    qi = np.arange(n)[:, None]
+    kj = np.arange(L)[None, :]
+    return np.broadcast_to(np.asarray(mask_fn(b, h, qi, kj), dtype=bool), (n, L))
+
+
 def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
                   scale: float, causal: bool, page_size: int, window: int = 0, alibi=None,
-                  key_ranges=None):
+                  key_ranges=None, mask_fn=None):
     """Exact attention of every query row; returns (O [T, Hq, D], lse [T, Hq]).
 
     ``key_ranges`` = (key_lo [T], key_hi [T]) restricts each query row to the
-    keys of its own document (R6).
+    keys of its own document (R6).  ``mask_fn(b, h, q_idx, kv_idx)`` (broadcasting
+    over index arrays) is a general mask on top (R7); :func:`block_map_mask` makes
+    one from a block map.
 
     Streams one (sequence, key head) at a time so that memory stays bounded
     by one sequence's score matrix per query head -- the N^2 b warning of
@@ -219,7 +263,7 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
             kvh = h // G                                                # R1
             slope = 0.0 if alibi is None else float(alibi[h])          # R5
             o, ls = attend_rows(q[t0:t1, h], kb[:, kvh], vb[:, kvh], scale, vis, first,
-                                slope, pos)
+                                slope, pos, _allowed(mask_fn, b, h, t1 - t0, L))   # R7
             out[t0:t1, h] = o
             lse[t0:t1, h] = ls
     return out, lse
@@ -227,7 +271,7 @@ def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
 
 def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
                        scale: float, causal: bool, page_size: int, rows, window: int = 0,
-                       alibi=None, key_ranges=None):
+                       alibi=None, key_ranges=None, mask_fn=None):
     """Same as :func:`attention_ref` for selected (token, head) pairs only.
 
     Used at full workload sizes, where the oracle computes sampled outputs one
@@ -259,9 +303,11 @@ def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q
             kvh = h // G
             i0 = t - int(cu[b])
             slope = 0.0 if alibi is None else float(alibi[h])
+            allowed = _allowed(mask_fn, b, h, q_len, L)
             o, ls = attend_rows(q[t:t + 1, h], kb[:, kvh], vb[:, kvh], scale,
                                 vis_all[i0:i0 + 1], first_all[i0:i0 + 1], slope,
-                                [L - q_len + i0])
+                                [L - q_len + i0],
+                                None if allowed is None else allowed[i0:i0 + 1])
             out[i], lse[i] = o[0], ls[0]
     return out, lse
 

@@ -39,12 +39,13 @@ def _bf16(x):
             for v in x.ravel()]
 
 
-def brute_attention(case, window=None, alibi=None, key_ranges=None):
+def brute_attention(case, window=None, alibi=None, key_ranges=None, pred=None):
     """Loops over sequences, rows, heads and keys; math.exp and math.fsum only.
     With a sliding window w > 0 the row at position p takes keys j > p - w only;
     with ALiBi slopes the score of key j gets slope_h * (j - p) added; with
     document ranges (key_lo, key_hi) per row, row t takes keys key_lo[t] <= j <
-    key_hi[t] only."""
+    key_hi[t] only; with a predicate, row i of sequence b (i counted within its
+    query run) and head h take key j only if pred(b, h, i, j) is true."""
     w = case.window if window is None else window
     q = bits(case.q)
     kp = bits(case.k_pool)
@@ -73,6 +74,8 @@ def brute_attention(case, window=None, alibi=None, key_ranges=None):
                     if j < start:
                         continue
                     if key_ranges is not None and not (key_ranges[0][t] <= j < key_ranges[1][t]):
+                        continue
+                    if pred is not None and not bool(pred(b, h, i, j)):
                         continue
                     page, slot = int(bt[b][j // ps]), j % ps
                     kv = _bf16(kp[page, slot, kvh])
@@ -811,3 +814,160 @@ def test_document_ranges_layout():
             else:
                 assert 0 <= lo[t] <= p < hi[t] <= L
             t += 1
+
+
+# ----------------------------------------------------------------------------
+# general masks (R7): a predicate of (sequence, head, query index, key index), and
+# its block form
+# ----------------------------------------------------------------------------
+
+def _mask_case(causal=False, seed=71):
+    return make_case("msk", seq_lens=[150, 70, 0, 131], q_lens=[130, 9, 0, 131], Hq=4, Hkv=2,
+                     D=8, page_size=16, seed=seed, causal=causal)
+
+
+def _run_mask(case, mask_fn, causal=None, window=0, key_ranges=None):
+    return oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
+                                case.block_tables.numpy(), case.seq_lens_k.numpy(),
+                                case.cu_seqlens_q.numpy(), case.scale,
+                                case.causal if causal is None else causal, case.page_size,
+                                window, None, key_ranges, mask_fn)
+
+
+def _lens(case):
+    cu = case.cu_seqlens_q.numpy()
+    return case.seq_lens_k.numpy(), cu[1:] - cu[:-1]
+
+
+def test_mask_fn_that_allows_everything_changes_nothing():
+    case = _mask_case(causal=True)
+    o0, l0 = _run_mask(case, None)
+    o1, l1 = _run_mask(case, lambda b, h, q, k: np.ones(np.broadcast(q, k).shape, bool))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_mask_fn_reproduces_causal_window_and_documents():
+    """The causal bound (R2), the window (R4) and document ranges (R6) written as
+    predicates give the same bits as the built-in forms."""
+    case = _mask_case()
+    L, n = _lens(case)
+    causal_fn = lambda b, h, q, k: k <= L[b] - n[b] + q
+    assert_close(_run_mask(case, causal_fn, causal=False)[0], _run_mask(case, None, True)[0], 0)
+    w = 20
+    win_fn = lambda b, h, q, k: (k <= L[b] - n[b] + q) & (k > L[b] - n[b] + q - w)
+    o_w, l_w = _run_mask(case, win_fn, causal=False)
+    o_r, l_r = _run_mask(case, None, causal=True, window=w)
+    assert_close(o_w, o_r, 0)
+    assert_close(l_w, l_r, 0)
+    kr = document_ranges(list(L), list(n), 3, 5)
+    cu = case.cu_seqlens_q.numpy()
+    doc_fn = lambda b, h, q, k: (k >= kr[0][cu[b] + q]) & (k < kr[1][cu[b] + q])
+    o_d, l_d = _run_mask(case, doc_fn, causal=True)
+    o_k, l_k = _run_mask(case, None, causal=True, key_ranges=kr)
+    assert_close(o_d, o_k, 0)
+    assert_close(l_d, l_k, 0)
+
+
+def _head_parity(b, h, q, k):
+    # even heads see even keys only, odd heads every key up to 3 q + 5: depends on
+    # every argument, so a predicate wired to the wrong one shows
+    return np.where(np.asarray(h) % 2 == 0, np.asarray(k) % 2 == 0,
+                    np.asarray(k) <= 3 * np.asarray(q) + 5 + np.asarray(b))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_fn_matches_brute_force(causal):
+    case = make_case("mbf", seq_lens=[23, 9, 0, 17], q_lens=[5, 9, 0, 3], Hq=4, Hkv=2, D=4,
+                     page_size=3, seed=3, causal=causal)
+    ob, lb = brute_attention(case, pred=_head_parity)
+    oo, lo = _run_mask(case, _head_parity)
+    assert_close(oo, ob, 1e-12)
+    assert_close(lo, lb, 1e-12)
+
+
+def _random_block_map(case, seed, density=0.5, block=64):
+    L, n = _lens(case)
+    rng = np.random.default_rng(seed)
+    qb = max(1, -(-int(n.max()) // block))
+    kb = max(1, -(-int(L.max()) // block))
+    return (rng.random((len(L), qb, kb)) < density).astype(np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_map_matches_brute_force(causal):
+    """A block map at 8 x 8 blocks on a small case against the brute force, whose
+    predicate looks the entries up one by one."""
+    case = make_case("mbm", seq_lens=[30, 19, 26], q_lens=[17, 19, 2], Hq=2, Hkv=1, D=4,
+                     page_size=16, seed=9, causal=causal)
+    bm = _random_block_map(case, 4, 0.6, block=8)
+    pred = lambda b, h, i, j: (i // 8 < bm.shape[1] and j // 8 < bm.shape[2]
+                               and bm[b][i // 8][j // 8] != 0)
+    ob, lb = brute_attention(case, pred=pred)
+    oo, lo = _run_mask(case, oracle.block_map_mask(bm, block=8))
+    assert_close(oo, ob, 1e-12)
+    assert_close(lo, lb, 1e-12)
+
+
+def test_block_map_edges():
+    """All blocks visible = no map; no block visible = every row sees nothing (O = 0,
+    lse = -inf); a map too small for the sequence hides the keys outside it."""
+    case = _mask_case(causal=True)
+    ones = np.ones_like(_random_block_map(case, 1))
+    o0, l0 = _run_mask(case, None)
+    o1, l1 = _run_mask(case, oracle.block_map_mask(ones))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    o2, l2 = _run_mask(case, oracle.block_map_mask(np.zeros_like(ones)))
+    assert not o2.any() and np.all(l2 == -np.inf)
+    small = ones[:, :1, :1]                 # rows 0..63, keys 0..63 only
+    o3, l3 = _run_mask(case, oracle.block_map_mask(small))
+    L, n = _lens(case)
+    cu = case.cu_seqlens_q.numpy()
+    ref = oracle.attention_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
+                               case.block_tables.numpy(), np.minimum(L, 64), cu, case.scale,
+                               False, case.page_size)
+    for b in range(len(L)):
+        for i in range(int(n[b])):
+            t = int(cu[b]) + i
+            if i >= 64 or L[b] == 0:
+                assert not o3[t].any() and np.all(l3[t] == -np.inf)
+            elif L[b] - n[b] + i >= 63:
+                # the causal bound lies past key 63: the row sees keys 0..63
+                assert_close(o3[t], ref[0][t], 1e-12)
+
+
+@pytest.mark.parametrize("mutant", ["transposed", "position"])
+def test_planted_mask_mistakes_are_caught(mutant):
+    """A block map read transposed, or indexed by absolute position instead of the
+    row's index in its query run, fails the brute force."""
+    case = make_case("mmu", seq_lens=[40, 33], q_lens=[12, 20], Hq=2, Hkv=1, D=4,
+                     page_size=16, seed=2, causal=False)
+    bm = _random_block_map(case, 8, 0.5, block=8)
+    bm = np.concatenate([bm, np.ones((bm.shape[0], max(0, bm.shape[2] - bm.shape[1]),
+                                      bm.shape[2]), np.uint8)], axis=1)
+    pred = lambda b, h, i, j: (i // 8 < bm.shape[1] and j // 8 < bm.shape[2]
+                               and bm[b][i // 8][j // 8] != 0)
+    ob, _ = brute_attention(case, pred=pred)
+    L, n = _lens(case)
+    if mutant == "transposed":
+        bad = np.ascontiguousarray(np.swapaxes(bm, 1, 2))
+        fn = oracle.block_map_mask(bad, block=8)
+    else:
+        good = oracle.block_map_mask(bm, block=8)
+        fn = lambda b, h, q, k: good(b, h, q + (L[b] - n[b]), k)
+    oo, _ = _run_mask(case, fn)
+    assert not np.allclose(oo, ob, atol=1e-6)
+
+
+def test_rows_ref_with_mask_fn_matches_full_ref():
+    case = _mask_case(causal=True)
+    bm = _random_block_map(case, 6, 0.5)
+    fn = oracle.block_map_mask(bm)
+    o, l = _run_mask(case, fn)
+    rows = [(0, 0), (64, 1), (129, 3), (130, 2), (138, 0), (139, 1), (200, 3), (269, 2)]
+    ro, rl = oracle.attention_rows_ref(bits(case.q), bits(case.k_pool), bits(case.v_pool),
+                                       case.block_tables.numpy(), case.seq_lens_k.numpy(),
+                                       case.cu_seqlens_q.numpy(), case.scale, True,
+                                       case.page_size, rows, mask_fn=fn)
+    for i, (t, h) in enumerate(rows):
+        assert_close(ro[i], o[t, h], 1e-12)
+        assert_close(rl[i], l[t, h], 1e-12)
