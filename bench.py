@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--workload", default="qwen7b_decode",
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
                             "long_decode", "long_decode_auto", "causal_prefill",
-                            "causal_prefill_fp8", "mixed_ragged", "tiny_decode",
+                            "causal_prefill_fp8", "causal_prefill_block_map",
+                            "mixed_ragged", "tiny_decode",
                             "qwen7b_decode_warm"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +211,37 @@ class PrefillStep:
         return cfg
 
 
+class BlockMapPrefillStep(PrefillStep):
+    """The causal prefill with a block map on top (64 x 64 blocks): every query block
+    sees the 4 key blocks up to its own and every 8th block before them (23 % of the
+    causal pairs).  The rate counts the pairs the map leaves visible."""
+
+    def __init__(self, name):
+        import numpy as np
+        import torch
+        from workloads import local_strided_block_map, units
+        super().__init__(name)
+        c = self.case
+        qb, kb = -(-c.max_q_len // 64), -(-max(c.seq_lens) // 64)
+        bm = np.stack([local_strided_block_map(qb, kb)] * c.B)
+        self.bm = torch.from_numpy(bm).cuda()
+        self.units = 4 * c.D * c.Hq * units.block_map_pairs(c.seq_lens, c.q_lens, True, bm)
+
+    def __call__(self):
+        c = self.case
+        q, kp, vp, out = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.pa.paged_attn_prefill_varlen(q, kp, vp, c.cu_seqlens_q, c.seq_lens_k,
+                                          c.block_tables, c.scale, causal=True,
+                                          max_q_len=c.max_q_len, out=out, block_map=self.bm,
+                                          kernel_events=next_events(self))
+
+    def config(self):
+        cfg = super().config()
+        cfg["block_map"] = "local 4 + every 8th of 64 x 64 blocks"
+        return cfg
+
+
 class Fp8PrefillStep(PrefillStep):
     """The same causal prefill over FP8 E4M3 pools: seeded random codes of the
     pools' shape with per-pool scales (the queries stay bf16)."""
@@ -362,6 +394,8 @@ def make_step(name, num_splits=0):
         return PrefillStep(name)
     if name == "causal_prefill_fp8":
         return Fp8PrefillStep("causal_prefill")
+    if name == "causal_prefill_block_map":
+        return BlockMapPrefillStep("causal_prefill")
     if name == "long_history_chunk":
         return PrefillStep(name, splitk=True)
     return MixedStep(name)
@@ -625,7 +659,8 @@ def cpu_baseline(step, min_s=10.0, budget_s=15.0):
     planes -- every row of one head over its sequence's keys, the oracle given that
     sequence's pages and the KV head the query head reads -- until min_s; GFLOP/s
     of algorithmic prefill work."""
-    if isinstance(step, PrefillStep) and not isinstance(step, Fp8PrefillStep) \
+    if isinstance(step, PrefillStep) and not isinstance(step, (Fp8PrefillStep,
+                                                               BlockMapPrefillStep)) \
             and not step.splitk:
         return cpu_baseline_prefill(step, min_s, budget_s)
     import numpy as np
@@ -836,6 +871,7 @@ def main():
                                     ("tiny_decode", "tiny_decode", 0),
                                     ("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
                                     ("causal_prefill_fp8", "causal_prefill_fp8", 0),
+                                    ("causal_prefill_block_map", "causal_prefill_block_map", 0),
                                     ("long_decode", "long_decode", 64),
                                     ("long_decode_auto_splits", "long_decode", -1),
                                     ("long_history_chunk", "long_history_chunk", 0),

@@ -404,7 +404,7 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * (its last w positions, itself included), on top of the causal bound when causal;
  * without causal only this lower bound applies.  A decode row sits at position
  * seq_len - 1, so it sees keys seq_len - w .. seq_len - 1.  w = 0: no window.
- * Document masks need no option: every sequence of a ragged batch is one document.
+ * Without document ranges (below) every sequence of a ragged batch is one document.
  *
  * ALiBi: the same section names ALiBi among the score modifications, again without
  * a formula.  This library's: with alibi_slopes (device float32 [Hq], one slope per
@@ -428,7 +428,23 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * Together the causal bound, the window and the document range are one mask
  * predicate per row, lo <= key <= lim, that the general variant applies to the
  * blocks where some row's bound falls and uses to skip the key tiles outside every
- * row's range.
+ * row's range.  Any mask that is an interval of keys per query row (prefix-LM
+ * masks, chunked local attention, ...) is such a predicate: give its bounds as
+ * key_lo / key_hi, with causal off where the interval reaches past the row.
+ *
+ * Block maps: the same section shows a mask written as a predicate of (sequence,
+ * head, query index, key index) and compiled by create_block_mask, which records
+ * per (query block, key block) whether the block is needed at all.  This
+ * library's: a block map is such a mask given in block form, block_map[b][i / 64]
+ * [j / 64] nonzero when row i of sequence b's query run (0-based within the run)
+ * may see key j; entries outside the map's block_map_q_blocks x block_map_k_blocks
+ * count as zero.  It combines (and) with the causal bound, the window, the
+ * document ranges and ALiBi.  The prefill walks only the 64-key tiles that one of
+ * its four 64-row query blocks lists (256-row work-groups) and masks a listed tile
+ * whole for the rows of a query block that does not list it.  Block maps take bf16
+ * pools, no key parts, and at most 262144 keys per sequence (max_pages x
+ * page_size); other requests are PA_ERR_UNSUPPORTED.  The map is data, read on the
+ * device.
  *
  * The _ex entry points take every option of an operation in one struct; the
  * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
@@ -483,6 +499,11 @@ typedef struct {
                            work items in turn and fetching the next item's Q rows and
                            first K/V tile during the current item's last tile.  The
                            results are the same bits as the plain grid's.  0: plain grid */
+  const uint8_t* block_map;   /* NULL, or device uint8 [B, block_map_q_blocks,
+                                 block_map_k_blocks]: a mask in block form (block maps
+                                 above); bf16 pools, no key parts                         */
+  int32_t block_map_q_blocks; /* query blocks of 64 rows per sequence in the map (>= 1)   */
+  int32_t block_map_k_blocks; /* key blocks of 64 keys per sequence in the map (>= 1)     */
 } pa_prefill_opts;
 
 /*

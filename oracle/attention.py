@@ -214,13 +214,14 @@ def block_map_mask(block_map, block: int = 64):
     return pred
 
 
-def _allowed(mask_fn, b, h, n, L):
-    """[n, L] boolean of a predicate (R7) over the rows and keys of one sequence."""
+def _allowed(mask_fn, b, h, rows, L):
+    """[len(rows), L] boolean of a predicate (R7) for the given query indices of one
+    sequence's query run (all n of them when ``rows`` is an int n) and its L keys."""
     if mask_fn is None:
         return None
-    qi = np.arange(n)[:, None]
+    qi = (np.arange(rows) if np.isscalar(rows) else np.asarray(rows))[:, None]
     kj = np.arange(L)[None, :]
-    return np.broadcast_to(np.asarray(mask_fn(b, h, qi, kj), dtype=bool), (n, L))
+    return np.broadcast_to(np.asarray(mask_fn(b, h, qi, kj), dtype=bool), (qi.shape[0], L))
 
 
 def attention_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q,
@@ -303,11 +304,9 @@ def attention_rows_ref(q, k_pool, v_pool, block_tables, seq_lens_k, cu_seqlens_q
             kvh = h // G
             i0 = t - int(cu[b])
             slope = 0.0 if alibi is None else float(alibi[h])
-            allowed = _allowed(mask_fn, b, h, q_len, L)
             o, ls = attend_rows(q[t:t + 1, h], kb[:, kvh], vb[:, kvh], scale,
                                 vis_all[i0:i0 + 1], first_all[i0:i0 + 1], slope,
-                                [L - q_len + i0],
-                                None if allowed is None else allowed[i0:i0 + 1])
+                                [L - q_len + i0], _allowed(mask_fn, b, h, [i0], L))
             out[i], lse[i] = o[0], ls[0]
     return out, lse
 

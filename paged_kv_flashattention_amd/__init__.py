@@ -568,7 +568,8 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
                               lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                               stream=None, validate: bool = False, window_left: int = 0,
                               alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
-                              key_ranges=None, persistent: bool = False):
+                              key_ranges=None, persistent: bool = False,
+                              block_map: Optional[torch.Tensor] = None):
     """Ragged prefill: q [Tq, Hq, D] rows of B sequences over their paged keys.
 
     ``max_q_len`` is a host-side bound of the per-sequence query counts; if
@@ -580,11 +581,15 @@ def paged_attn_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block
     row t sees keys key_lo[t] <= j < key_hi[t] of its sequence only.
     ``persistent``: persistent work-groups with next-item prefetch (the ``persistent``
     field of pa_prefill_opts; plain bf16 variant with 256-row tiles, else ignored).
+    ``block_map``: uint8 [B, query blocks, key blocks] on the device, a mask in block
+    form -- row i of sequence b's query run sees key j only if
+    block_map[b, i // 64, j // 64] is nonzero (entries outside the map count as zero),
+    on top of the other masks.
     """
     return _prefill(None, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
                     softmax_scale, causal, max_q_len, out, lse, return_lse, stream, validate,
                     window_left, alibi_slopes, kernel_events=kernel_events,
-                    key_ranges=key_ranges, persistent=persistent)
+                    key_ranges=key_ranges, persistent=persistent, block_map=block_map)
 
 
 def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables,
@@ -658,7 +663,7 @@ def paged_attn_prefill_varlen_splitk(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k
 def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, softmax_scale,
              causal, max_q_len, out, lse, return_lse, stream, validate, window_left=0,
              alibi_slopes=None, scales=None, kernel_events=None, key_ranges=None,
-             persistent=False):
+             persistent=False, block_map=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -725,9 +730,15 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             if bool((lo_h < 0).any()) or bool((hi_h > row_len).any()):
                 raise ValueError("key ranges must lie in [0, seq_lens_k] of their sequence")
         lo_ptr, hi_ptr = key_lo.data_ptr(), key_hi.data_ptr()
+    bm_ptr, bm_q, bm_k = None, 0, 0
+    if block_map is not None:
+        _need(block_map, "block_map", torch.uint8, 3, dev)
+        if block_map.shape[0] != B:
+            raise ValueError(f"block_map must be [B={B}, query blocks, key blocks]")
+        bm_ptr, bm_q, bm_k = block_map.data_ptr(), block_map.shape[1], block_map.shape[2]
     ev0, ev1 = _events(kernel_events)
     general = (bool(window_left) or alibi_ptr is not None or scales is not None
-               or ev0 is not None or lo_ptr is not None or persistent)
+               or ev0 is not None or lo_ptr is not None or persistent or bm_ptr is not None)
     if general and split is None:
         split = (1, None)                         # the plain launch, through prefill_ex
     if split is not None:
@@ -749,7 +760,7 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
                 ksp, vsp = scales.check(k_pool.shape, dev)
             opts = _lib.PrefillOpts(1 if causal else 0, window_left, num_splits, alibi_ptr,
                                     0 if scales is None else 1, ks, vs, ev0, ev1, lo_ptr, hi_ptr,
-                                    ksp, vsp, 1 if persistent else 0)
+                                    ksp, vsp, 1 if persistent else 0, bm_ptr, bm_q, bm_k)
             _check(lib.paged_attn_prefill_ex(*args[:-1], ctypes.byref(opts), _ptr(workspace),
                                              ws_bytes, _stream(stream)))
         else:

@@ -36,7 +36,9 @@ class PrefillOpts(ctypes.Structure):
                 ("v_scale", ctypes.c_float), ("kernel_start_event", ctypes.c_void_p),
                 ("kernel_stop_event", ctypes.c_void_p), ("key_lo", ctypes.c_void_p),
                 ("key_hi", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
-                ("v_scales", ctypes.c_void_p), ("persistent", ctypes.c_int32)]
+                ("v_scales", ctypes.c_void_p), ("persistent", ctypes.c_int32),
+                ("block_map", ctypes.c_void_p), ("block_map_q_blocks", ctypes.c_int32),
+                ("block_map_k_blocks", ctypes.c_int32)]
 
 
 c_dopts = ctypes.POINTER(DecodeOpts)

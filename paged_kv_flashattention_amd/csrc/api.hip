@@ -319,7 +319,8 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                  float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
                  const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr,
                  const float* k_scales = nullptr, const float* v_scales = nullptr,
-                 int32_t persistent = 0) {
+                 int32_t persistent = 0, const uint8_t* block_map = nullptr,
+                 int32_t bm_qb = 0, int32_t bm_kb = 0) {
   g_last_error[0] = 0;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
@@ -351,6 +352,20 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   if (k_scales) k_scale = v_scale = 1.f;
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
     return fail(PA_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite", what);
+  if (block_map) {
+    if (bm_qb < 1 || bm_kb < 1)
+      return fail(PA_ERR_SHAPE, "%s: block map of %d x %d blocks per sequence", what, bm_qb,
+                  bm_kb);
+    if (fp8)
+      return fail(PA_ERR_UNSUPPORTED, "%s: block maps need bf16 pools", what);
+    if (num_splits > 1)
+      return fail(PA_ERR_UNSUPPORTED, "%s: block maps take no key parts (num_splits %d)", what,
+                  num_splits);
+    if ((long long)max_pages * page_size > 262144)
+      return fail(PA_ERR_UNSUPPORTED, "%s: block maps cover at most 262144 keys per sequence "
+                  "(max_pages x page_size = %lld)", what, (long long)max_pages * page_size);
+    num_splits = 1;
+  }
   if (max_q_len > Tq) max_q_len = Tq;
   const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits);
   // one work-group per (query head, sequence, 128- or 256-row query tile, key
@@ -389,6 +404,9 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
   a.k_scales = k_scales;
   a.v_scales = v_scales;
   a.persist = persistent ? 1 : 0;
+  a.block_map = block_map;
+  a.bm_qb = bm_qb;
+  a.bm_kb = bm_kb;
   a.S = S;
   a.part_min = kPrefillPartMinTiles;
   if (S > 1) {
@@ -823,13 +841,14 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       workspace_bytes, stream, opts->window_left, opts->alibi_slopes,
                       opts->kv_fp8 == 1, opts->k_scale, opts->v_scale, events_of(opts),
                       opts->key_lo, opts->key_hi, opts->k_scales, opts->v_scales,
-                      opts->persistent);
+                      opts->persistent, opts->block_map, opts->block_map_q_blocks,
+                      opts->block_map_k_blocks);
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,
                                              int32_t Hq, int32_t D,
                                              const pa_prefill_opts* opts) {
-  if (!opts) return 0;
+  if (!opts || opts->block_map) return 0;     // block maps take no key parts
   return paged_attn_prefill_workspace_bytes(B, Tq, max_q_len, Hq, D, opts->num_splits);
 }
 

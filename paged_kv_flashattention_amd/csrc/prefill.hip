@@ -297,16 +297,26 @@ struct PfHand {
   int pn;         // the item after this one (its id), or -1
 };
 
+// Block maps (a mask given in block form, 64 query rows x 64 keys per block): the
+// listed key tiles of a work-group are gathered into a list in LDS, after the
+// K/V stages; entry 0 holds the count, entry 1 + i the i-th listed tile in
+// ascending order, with bit 16 + k set when the work-group's k-th 64-row query
+// block lists it.
+constexpr int kBsMaxTiles = 4096;           // 262,144 keys
+constexpr size_t kBsListBytes = (kBsMaxTiles + 16) * sizeof(int);
+
 // W waves (32 W query rows) per work-group; 8 W waves per CU.  GEN: the general
 // variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
 // downwards, which is how the ALiBi variants (general only) walk, so REV also
 // compiles the bias in.  PER: an item of a persistent work-group (hand-over in hd).
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER>
+// BS: a block map (general bf16 variant, 8 waves, no key parts).
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER, bool BS = false>
 __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
                                         const PfSetup& s, PfHand& hd, uint16_t* pf_lds) {
   static_assert(!REV || GEN, "the downward walk is a general-variant feature");
   static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
+  static_assert(!BS || (GEN && !F8 && !PER && W == 8), "block maps: general bf16, 8 waves");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   using L_ = PfLds<D>;
   using M_ = PfDma<D, W>;
@@ -476,7 +486,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   };
   auto issue = [&](int n, int ks, int vs) {
     if (REV ? n < base_t : n - base_t >= 64) {
-      base_t = REV ? max(0, n - 63) : base_t + 64;
+      base_t = REV ? max(0, n - 63) : (BS ? n : base_t + 64);
       tab = load_tab(base_t);
     }
     issue_page(__builtin_amdgcn_readlane(tab, n - base_t), kvh, ks, vs);
@@ -567,12 +577,25 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
                        : xor32_max(fmaxf(ma, mb)) * bs.ca;
     return ALI ? r + boff : r;
   };
+  // Block map: the walk's tiles come from the list (entry of walk index u), and a
+  // tile that this wave's query block does not list is masked whole.
+  int* const bs_list = reinterpret_cast<int*>(pf_lds + L_::Q0);
+  int bs_n = 0;
+  auto bs_entry = [&](int u) { return bs_list[1 + (REV ? bs_n - 1 - u : u)]; };
   // The block's ALiBi offset (general variant), then -inf for keys past the end,
   // (causal) above the diagonal and (window) below a row's window; only blocks that
-  // touch one of these boundaries need the second part.  Called once per block,
-  // right after its scores are formed and before they are used.
-  auto mask = [&](f32x16& sc, int kb0) {
+  // touch one of these boundaries need the second part.  Called once per block
+  // (walk index u of its tile), right after its scores are formed and before they
+  // are used.
+  auto mask = [&](f32x16& sc, int kb0, int u) {
     if (ALI) boff = slope_log2 * (float)(kb0 - my_pos);
+    if constexpr (BS) {
+      if (!((bs_entry(u) >> (16 + wave / 2)) & 1)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[e] = kNegInf;
+        return;
+      }
+    }
     const bool need = (kb0 + 32 > L) || (kb0 + 31 > w_lim_min) || (GEN && kb0 < w_lo_max);
     if (__builtin_expect(need, 0)) {
 #pragma unroll
@@ -753,8 +776,48 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   // reference at the first block instead of moving it at nearly every block.  B0, B1:
   // the first and second 32-key block of a tile in walk order.
   constexpr int B0 = REV ? 1 : 0, B1 = 1 - B0;
-  auto tile_at = [&](int u) { return REV ? tile_hi - 1 - u : tile_lo + u; };
-  const int nt = tile_hi - tile_lo;
+  if constexpr (BS) {
+    // the list: wave 0 reads the map entries of its query blocks for 1,024 tiles per
+    // pass (lane l: tiles t + 64 i + l) and compacts the listed ones in order
+    if (wave == 0) {
+      const uint8_t* mrow = a.block_map + (size_t)b * a.bm_qb * a.bm_kb;
+      const int qb0 = r_wg / 64;
+      int count = 0;
+      for (int tb = tile_lo; tb < tile_hi; tb += 64 * 16) {
+        int f[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = tb + 64 * i + lane;
+          const bool t_ok = t < tile_hi && t < a.bm_kb;
+          int fl = 0;
+#pragma unroll
+          for (int k = 0; k < W / 2; ++k) {
+            const int qb = qb0 + k;
+            const uint8_t v =
+                mrow[(size_t)min(qb, a.bm_qb - 1) * a.bm_kb + min(t, a.bm_kb - 1)];
+            fl |= (t_ok && qb < a.bm_qb && v != 0) ? 1 << k : 0;
+          }
+          f[i] = fl;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(f[i] != 0);
+          const int below = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (f[i]) bs_list[1 + count + below] = (tb + 64 * i + lane) | (f[i] << 16);
+          count += __builtin_popcountll(bal);
+        }
+      }
+      if (lane == 0) bs_list[0] = count;
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the list is in LDS
+    }
+    block_sync();
+    bs_n = __builtin_amdgcn_readfirstlane(bs_list[0]);
+  }
+  auto tile_at = [&](int u) {
+    return BS ? bs_entry(u) & 0xffff : (REV ? tile_hi - 1 - u : tile_lo + u);
+  };
+  const int nt = BS ? bs_n : tile_hi - tile_lo;
   // Walking upwards, the blocks from the first key past this wave's last valid row
   // on are masked for all of its rows (causal), as are blocks past the sequence end:
   // the wave computes only its first G blocks (finishing the last of them) and for
@@ -824,7 +887,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     }
   };
   if (nt > 0) {
-    base_t = REV ? max(0, tile_hi - 64) : tile_lo;
+    base_t = BS ? (REV ? max(0, tile_at(0) - 63) : tile_at(0))
+                : (REV ? max(0, tile_hi - 64) : tile_lo);
     tab = pre ? hd.tab : load_tab(base_t);
     int vs_cur = vc;                      // V stage of the walk's current tile
     int ks_cur = kc;                      // K stage of the walk's current tile
@@ -838,15 +902,25 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     }
     if constexpr (PER) next_item();
     issue_walk(1);
-    // G: blocks this wave computes, in walk order (wave-uniform)
-    const int G = REV ? 2 * nt
-                      : min(2 * nt, max(0, (w_key_end - tile_lo * kPfBN + 31) / 32));
+    // G: blocks this wave computes, in walk order (wave-uniform); with a block map,
+    // the listed tiles' blocks that start below the wave's key end
+    int G = REV ? 2 * nt : min(2 * nt, max(0, (w_key_end - tile_lo * kPfBN + 31) / 32));
+    if constexpr (BS && !REV) {
+      int c = 0;
+      for (int i = lane; i < nt; i += 64) {
+        const int k0 = (bs_list[1 + i] & 0xffff) * kPfBN;
+        c += (k0 < w_key_end ? 1 : 0) + (k0 + 32 < w_key_end ? 1 : 0);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+      G = __builtin_amdgcn_readfirstlane(c);
+    }
     // first block: scores, mask, first reference
     f32x16 s_pend;
     if (G > 0) {
       s_pend = qk(kst(ks_cur), B0);
-      mask(s_pend, tile_at(0) * kPfBN + 32 * B0);
-      decide(rowmax(s_pend, blk_scale(0, B0)));
+      mask(s_pend, tile_at(0) * kPfBN + 32 * B0, 0);
+      decide(rowmax(s_pend, blk_scale(vs_cur, B0)));
     }
     // iterations u whose two steps both score a computed block (2 u + 2 < G)
     const int U1 = G > 0 ? min(nt - 1, (G - 1) / 2) : 0;
@@ -856,12 +930,12 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       // first block of tile kt (pending) -> its second block
       step(s_pend, kst(ks_cur), B1, vs_cur, B0);
-      mask(s_pend, kt * kPfBN + 32 * B1);
+      mask(s_pend, kt * kPfBN + 32 * B1, u);
       // second block of tile kt -> first block of tile kn
       publish(kn, ks_cur ^ 1, vs_next);
       issue_walk(u + 2);
       step(s_pend, kst(ks_cur ^ 1), B0, vs_cur, B1);
-      mask(s_pend, kn * kPfBN + 32 * B0);
+      mask(s_pend, kn * kPfBN + 32 * B0, u + 1);
       vs_cur = vs_next;
       ks_cur ^= 1;
     }
@@ -871,7 +945,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       const int kl = tile_at(u);
       if (G == 2 * nt) {
         step(s_pend, kst(ks_cur), B1, vs_cur, B0);
-        mask(s_pend, kl * kPfBN + 32 * B1);
+        mask(s_pend, kl * kPfBN + 32 * B1, u);
         finish(s_pend, vs_cur, B1);
       } else if (G == 2 * nt - 1) {
         finish(s_pend, vs_cur, B0);
@@ -882,7 +956,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
       if (G == 2 * u + 2) {
         step(s_pend, kst(ks_cur), B1, vs_cur, B0);
-        mask(s_pend, kt * kPfBN + 32 * B1);
+        mask(s_pend, kt * kPfBN + 32 * B1, u);
       } else if (G == 2 * u + 1) {
         finish(s_pend, vs_cur, B0);
       }
@@ -935,14 +1009,14 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
 }
 
 // One work-group per item of the plain grid (item = blockIdx.x).
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   const PfWork w = pf_work_of(a, blockIdx.x);
   const PfSetup s = pf_setup<GEN>(a, w, 32 * W, threadIdx.x & 63);
   if (!s.ok) return;
   PfHand hd{};
-  pf_item<D, W, GEN, F8, REV, PS, false>(a, w, s, hd, pf_lds);
+  pf_item<D, W, GEN, F8, REV, PS, false, BS>(a, w, s, hd, pf_lds);
 }
 
 // Persistent work-groups: one per CU, a multiple of 8 of them, each working through
@@ -1104,19 +1178,19 @@ static hipError_t launch_prefill_persist(const PrefillArgs& a, hipStream_t strea
   return hipGetLastError();
 }
 
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
-  if constexpr (PfLds<D>::BYTES > 65536) {
+  constexpr size_t lds = PfLds<D>::BYTES + (BS ? kBsListBytes : 0);
+  if constexpr (lds > 65536) {
     static std::atomic<int> state[kMaxDevices];
     const hipError_t e = lds_attribute_once(
-        state, reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS>),
-        PfLds<D>::BYTES);
+        state, reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS, BS>), lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(prefill_items(a));
-  launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS>, grid, dim3(64 * W),
-                (uint32_t)PfLds<D>::BYTES, stream, ev, a);
+  launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS, BS>, grid, dim3(64 * W), (uint32_t)lds,
+                stream, ev, a);
   return hipGetLastError();
 }
 
@@ -1131,6 +1205,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
     if (a.alibi) return launch_prefill_w<D, W, true, true, true>(a, stream, ev);
     return a.window > 0 || a.key_lo ? launch_prefill_w<D, W, true, true, false>(a, stream, ev)
                                     : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
+  }
+  if (a.block_map) {
+    // block maps take 256-row work-groups (prefill_waves) and bf16 pools
+    if constexpr (W == 8) {
+      return a.alibi ? launch_prefill_w<D, 8, true, false, true, false, true>(a, stream, ev)
+                     : launch_prefill_w<D, 8, true, false, false, false, true>(a, stream, ev);
+    } else {
+      return hipErrorInvalidValue;
+    }
   }
   if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
   if (a.window > 0 || a.key_lo) return launch_prefill_w<D, W, true, false, false>(a, stream, ev);
@@ -1147,6 +1230,7 @@ int prefill_waves(int max_q_len, bool fp8_alibi) {
   return max_q_len >= PF_W8_MIN || fp8_alibi ? 8 : 4;
 }
 static int prefill_waves(const PrefillArgs& a) {
+  if (a.block_map) return 8;
   return prefill_waves(a.max_q_len, a.kv_fp8 && a.alibi != nullptr);
 }
 
@@ -1210,13 +1294,14 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
     snprintf(pers, sizeof(pers), ", persistent: %d work-groups with next-item prefetch",
              prefill_persist_groups(a, cus));
   const size_t lds = (a.D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES) +
-                     (per ? (a.D == 128 ? PfLds<128>::q_bytes(8) : PfLds<64>::q_bytes(8)) : 0);
+                     (per ? (a.D == 128 ? PfLds<128>::q_bytes(8) : PfLds<64>::q_bytes(8)) : 0) +
+                     (a.block_map ? kBsListBytes : 0);
   snprintf(desc, desc_len,
            "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s%s) block=%d lds=%zu",
            a.D, 32 * W, kPfBN,
            a.kv_fp8 ? (a.k_scales ? "fp8-e4m3-widened,scales per page" : "fp8-e4m3-widened")
-                    : "lds-dma",
+                    : (a.block_map ? "lds-dma,block map" : "lds-dma"),
            prefill_items(a), a.Hq, a.B, a.n_qt, a.S, order, pers, 64 * W, lds);
   return e;
 }

@@ -276,6 +276,32 @@ def test_binding_takes_page_scales_as_tensor_pairs():
         pa.paged_attn_decode_fp8(q, k8, k8, bt, lens, 0.1, sc.double(), sc.double())
 
 
+def test_block_map_options_are_checked(lib):
+    """Block maps: positive dimensions, bf16 pools, no key parts, at most 262144 keys
+    per sequence; no workspace."""
+    from paged_kv_flashattention_amd import _lib
+    p = lib.paged_attn_prefill_ex
+    pargs = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 4, 8, 16, 8, 2, 128, 0.1]
+
+    def opts(**kw):
+        o = _lib.PrefillOpts(1, 0, 1)
+        o.block_map, o.block_map_q_blocks, o.block_map_k_blocks = FAKE, 1, 2
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return o
+    for kw, st in [(dict(block_map_q_blocks=0), 2), (dict(block_map_k_blocks=-1), 2),
+                   (dict(kv_fp8=1, k_scale=1.0, v_scale=1.0), 3), (dict(num_splits=2), 3)]:
+        o = opts(**kw)
+        assert p(*pargs, ctypes.byref(o), None, 0, None) == st, kw
+        assert b"block map" in lib.pa_last_error()
+    big = list(pargs)
+    big[11] = 20000                                           # 20000 pages of 16 keys
+    o = opts()
+    assert p(*big, ctypes.byref(o), None, 0, None) == 3
+    o = opts(num_splits=0)
+    assert lib.paged_attn_prefill_ex_workspace_bytes(1, 512, 512, 32, 128, ctypes.byref(o)) == 0
+
+
 def test_binding_refuses_a_negative_window():
     import paged_kv_flashattention_amd as pa
     q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)

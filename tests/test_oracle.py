@@ -971,3 +971,18 @@ def test_rows_ref_with_mask_fn_matches_full_ref():
     for i, (t, h) in enumerate(rows):
         assert_close(ro[i], o[t, h], 1e-12)
         assert_close(rl[i], l[t, h], 1e-12)
+
+
+def test_block_map_pair_count_matches_a_loop():
+    """units.block_map_pairs (the flop count of a prefill with a block map) against
+    a loop over every (row, key) of small ragged cases, 16 x 16 blocks."""
+    rng = np.random.default_rng(0)
+    for _ in range(6):
+        lens = rng.integers(0, 120, 3).tolist()
+        ql = [int(min(L, rng.integers(1, 90))) if L else 0 for L in lens]
+        bm = (rng.random((3, 5, 7)) < 0.5).astype(np.uint8)
+        for causal in (False, True):
+            n_pairs = sum(1 for b in range(3) for i in range(ql[b]) for j in range(lens[b])
+                          if not (causal and j > lens[b] - ql[b] + i)
+                          and i // 16 < 5 and j // 16 < 7 and bm[b, i // 16, j // 16])
+            assert units.block_map_pairs(lens, ql, causal, bm, 16) == n_pairs

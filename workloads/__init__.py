@@ -265,6 +265,16 @@ def document_ranges(seq_lens, q_lens, docs_per_seq, seed: int):
     return np.asarray(lo_all, dtype=np.int32), np.asarray(hi_all, dtype=np.int32)
 
 
+def local_strided_block_map(q_blocks: int, k_blocks: int, local: int = 4, stride: int = 8,
+                            offset_blocks: int = 0):
+    """A structured sparse mask in block form (64 x 64 blocks): query block i sees the
+    key blocks within `local` blocks below its own position (i + offset_blocks) and
+    every `stride`-th block before that.  uint8 [q_blocks, k_blocks]."""
+    i = np.arange(q_blocks)[:, None] + offset_blocks
+    j = np.arange(k_blocks)[None, :]
+    return (((i - local < j) & (j <= i)) | (j % stride == 0)).astype(np.uint8)
+
+
 def _mixed_lengths(seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     hist = np.clip(np.rint(rng.lognormal(7.0, 1.0, size=23)), 16, 32768).astype(np.int64)

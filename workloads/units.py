@@ -71,6 +71,25 @@ def prefill_pairs(seq_lens: Sequence[int], q_lens: Sequence[int], causal: bool) 
     return total
 
 
+def block_map_pairs(seq_lens: Sequence[int], q_lens: Sequence[int], causal: bool,
+                    block_map, block: int = 64) -> int:
+    """Unmasked (query, key) pairs per query head with a block map on top: row i of
+    sequence b's query run sees key j only if block_map[b][i // block][j // block]
+    is nonzero (entries outside the map count as zero), and the causal bound."""
+    import numpy as np
+    bm = np.asarray(block_map)
+    total = 0
+    for b, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        for qb in range(min(bm.shape[1], -(-n // block))):
+            rows = np.arange(qb * block, min(n, qb * block + block))
+            # keys each row sees: [0, L) or, causal, [0, L - n + i]
+            lim = np.minimum(L, L - n + rows + 1) if causal else np.full(rows.shape, L)
+            for kb in np.nonzero(bm[b, qb, :min(bm.shape[2], -(-L // block))])[0]:
+                lo = kb * block
+                total += int(np.clip(lim - lo, 0, block).sum())
+    return total
+
+
 def prefill_flops(seq_lens: Sequence[int], q_lens: Sequence[int], Hq: int, D: int,
                   causal: bool) -> int:
     """Algorithmic flops: 4 * D * Hq per unmasked (query, key) pair."""
