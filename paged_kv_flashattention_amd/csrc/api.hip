@@ -3,7 +3,6 @@
 // a failing call leaves outputs untouched; the only device work is the kernels'.
 #include <stdarg.h>
 #include <stdio.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
@@ -171,13 +170,6 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.key_lo = key_lo;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
-  // whole-row variant (an experiment, selected by PA_DECODE_ROWS=1; split counts are
-  // not adapted to it: pass num_splits explicitly)
-  static const int rows_env = [] {
-    const char* v = getenv("PA_DECODE_ROWS");
-    return v ? atoi(v) : 0;
-  }();
-  a.heads_per_wg = rows_env && !fp8 && Hkv % (512 / D) == 0 ? 512 / D : 1;
   return PA_OK;
 }
 

@@ -160,17 +160,6 @@ __device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff,
                : "m0", "memory");
 }
 
-// The same for data read exactly once (decode's K/V): non-temporal, so the lines
-// do not displace reusable ones in the caches.
-__device__ __forceinline__ void dma16_nt(const uint16_t* sbase, uint32_t voff,
-                                         uint16_t* lds_wave_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "m0", "memory");
-}
-
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {

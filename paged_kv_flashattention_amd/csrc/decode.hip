@@ -25,8 +25,6 @@
 // must then bypass the per-XCD L2 caches.
 #include <stdio.h>
 
-#include <atomic>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -515,270 +513,6 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   if (g == 0) a.part_lse[row] = lse;
 }
 
-// Whole-row decode (bf16 pools, KV heads in groups of KH = 512 / D): one
-// work-group per (group of KH KV heads, sequence, partition), one wave per KV head.
-// A 32-key chunk's K and V rows are copied for all KH heads at once -- 1 KiB of
-// every key row, contiguous in the pool -- straight into LDS (global_load_lds, two
-// stages: the next chunk is in flight while the current one is computed), and each
-// wave reads its own head's slice from there.  Reading whole rows rather than one
-// head's 256-byte slice of each row keeps the HBM accesses long and contiguous
-// ("8. Kernels and Attention Backends", "Counting attention's traffic": decode is
-// bound by these reads).  The per-chunk arithmetic is decode_partition_kernel's.
-//
-// LDS image of one matrix of a chunk: row r (key c0 + r) holds the KH heads' D values
-// as 16-byte pieces; piece p of the row sits in slot p ^ (r & 15), so that the 16
-// lanes of a K operand read (rows n = 0..15, one piece) and of a V read (one row,
-// pieces n = 0..15) hit 16 distinct slots, i.e. all 64 banks.  The copy makes the
-// swizzle free: lane i of the instruction for row r fetches piece i ^ (r & 15).
-template <int D>
-struct DpLds {
-  static constexpr int KH = 512 / D;            // KV heads per work-group
-  static constexpr int ROW = KH * D;            // bf16 per row (1 KiB)
-  static constexpr int MAT = 32 * ROW;          // one matrix of a 32-key chunk
-  static constexpr int STAGE = 2 * MAT;         // K then V
-  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);   // two stages, 128 KiB
-};
-
-template <int D>
-__global__ __launch_bounds__(64 * DpLds<D>::KH) void decode_rows_kernel(DecodeArgs a) {
-  using P = DpLds<D>;
-  constexpr int W = P::KH;       // waves = KV heads of the group
-  constexpr int DPL = D / 16;    // d values per lane per V row = MFMA d-tiles
-  constexpr int RPW = 32 / W;    // rows of each matrix this wave copies per chunk
-  extern __shared__ __align__(16) uint16_t dp_lds[];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;       // head column (S^T, O^T) / K row within a tile
-  const int g = lane >> 4;       // k-group of the MFMA operands
-  const int kvh0 = blockIdx.x * W;
-  const int kvh = kvh0 + wave;
-  const int split = blockIdx.y;
-  const int b = blockIdx.z;
-
-  int L = a.seq_lens[b];
-  const int cap = a.max_pages * a.page_size;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  if (a.key_lo) lo = max(lo, min(L, a.key_lo[b]));
-  const int k_begin = (lo & ~31) + split * a.part_len;
-  const int k_end = min(L, k_begin + a.part_len);
-  const int n_chunks = k_end > k_begin ? (k_end - k_begin + 31) >> 5 : 0;
-
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_pages;
-  const int rs = a.Hkv * D;
-  const size_t page_elems = (size_t)a.page_size * rs;
-  const int psm = a.page_size - 1;
-  const uint16_t* kg = a.k_pool + (size_t)kvh0 * D;
-  const uint16_t* vg = a.v_pool + (size_t)kvh0 * D;
-
-  const bool head_ok = n < a.G;
-  const int h = kvh * a.G + n;
-  const float slope = a.alibi && head_ok ? a.alibi[h] * kLog2e : 0.f;
-  u32x4 qb[D / 32];
-  {
-    const uint16_t* qp = a.q + ((size_t)b * a.Hq + (head_ok ? h : 0)) * D + (D / 4) * g;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qb[kk] = head_ok ? ld16(qp + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // Block-table windows: lane j of tab holds page base + j, tab_n the next 64.  The
-  // window moves before a chunk whose first key lies past it is copied (chunks are
-  // 32-key aligned, so none straddles two windows), at the top of an iteration where
-  // no copy is in flight; tab_n was loaded 64 pages before, so the move waits for
-  // nothing.
-  int base = k_begin >> a.ps_shift;
-  int tab = bt[min(base + lane, a.max_pages - 1)];
-  int tab_n = bt[min(base + 64 + lane, a.max_pages - 1)];
-  auto window_for = [&](int c) {
-    if (((k_begin + 32 * c) >> a.ps_shift) - base >= 64) {
-      base += 64;
-      tab = tab_n;
-      tab_n = bt[min(base + 64 + lane, a.max_pages - 1)];
-    }
-  };
-  // copy of chunk c into stage st: this wave's RPW rows of K and of V
-  auto issue = [&](int c, int st) {
-    const int c0 = k_begin + 32 * c;
-    const int r0 = RPW * wave;
-    uint16_t* kst = dp_lds + st * P::STAGE;
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int r = r0 + j;
-      const int key = c0 + r;
-      int pg = __builtin_amdgcn_readlane(tab, (key >> a.ps_shift) - base);
-      pg = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
-      const size_t off = (size_t)pg * page_elems + (size_t)(key & psm) * rs;
-      const uint32_t vo = (uint32_t)(lane ^ (r & 15)) * 16u;
-      dma16_nt(kg + off, vo, kst + r * P::ROW);
-      dma16_nt(vg + off, vo, kst + P::MAT + r * P::ROW);
-    }
-  };
-
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  f32x4 acc[DPL];
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (n_chunks > 0) issue(0, 0);
-  for (int c = 0; c < n_chunks; ++c) {
-    const int st = c & 1;
-    // this wave's copy of chunk c has landed; after the barrier everyone's has, and
-    // every wave is done with chunk c - 1, whose stage the next copy refills
-    vmcnt_wait<0>();
-    block_sync();
-    if (c + 1 < n_chunks) {
-      window_for(c + 1);
-      issue(c + 1, st ^ 1);
-    }
-    const uint16_t* kl = dp_lds + st * P::STAGE;
-    const uint16_t* vl = kl + P::MAT;
-    const int c0 = k_begin + 32 * c;
-
-    // K operand: rows n and 16 + n, pieces of d = D/4 g + 8 kk of this wave's head
-    u32x4 ka[D / 32], kb[D / 32];
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int pc = (wave * (D / 8) + (D / 32) * g + kk) ^ n;
-      ka[kk] = *reinterpret_cast<const u32x4*>(kl + n * P::ROW + 8 * pc);
-      kb[kk] = *reinterpret_cast<const u32x4*>(kl + (16 + n) * P::ROW + 8 * pc);
-    }
-    // V: rows 4 g + i and 16 + 4 g + i, d = DPL n .. DPL n + DPL - 1 of this head
-    uint32_t v[8][D / 32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g + i;
-      if constexpr (D == 128) {
-        const int pc = (wave * 16 + n) ^ r;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vl + r * P::ROW + 8 * pc);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(vl + (16 + r) * P::ROW + 8 * pc);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v[i][w] = x[w];
-          v[4 + i][w] = y[w];
-        }
-      } else {
-        const int pc = (wave * 8 + (n >> 1)) ^ r;
-        const int e = 8 * pc + 4 * (n & 1);
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vl + r * P::ROW + e);
-        const u32x2 y = *reinterpret_cast<const u32x2*>(vl + (16 + r) * P::ROW + e);
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          v[i][w] = x[w];
-          v[4 + i][w] = y[w];
-        }
-      }
-    }
-
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-    f32x4 sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      sa = mfma16x16x32(ka[kk], qb[kk], sa);
-      sb = mfma16x16x32(kb[kk], qb[kk], sb);
-    }
-    float s[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sa[i] * a.scale_log2;
-      s[4 + i] = sb[i] * a.scale_log2;
-    }
-    if (a.alibi) {
-      const float fb = (float)(c0 + 4 * g - (L - 1));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = fmaf(slope, fb + (float)(j < 4 ? j : 12 + j), s[j]);
-    }
-    if (c0 + 32 > k_end || c0 < lo) {
-      // keys past the end: -inf and V rows 0 (the rows may hold anything); keys
-      // below the window or document: -inf
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = c0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-        if (key >= k_end) {
-          s[j] = kNegInf;
-#pragma unroll
-          for (int w = 0; w < D / 32; ++w) v[j][w] = 0u;
-        } else if (key < lo) {
-          s[j] = kNegInf;
-        }
-      }
-    }
-    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mt = wave_max_xor16_32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(s[j] - m_use);
-      psum += p[j];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
-    const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) {
-      const int w = t >> 1;
-      u32x4 va;
-      if ((t & 1) == 0) {
-        va = u32x4{pack_lo_halves(v[0][w], v[1][w]), pack_lo_halves(v[2][w], v[3][w]),
-                   pack_lo_halves(v[4][w], v[5][w]), pack_lo_halves(v[6][w], v[7][w])};
-      } else {
-        va = u32x4{pack_hi_halves(v[0][w], v[1][w]), pack_hi_halves(v[2][w], v[3][w]),
-                   pack_hi_halves(v[4][w], v[5][w]), pack_hi_halves(v[6][w], v[7][w])};
-      }
-      acc[t] = mfma16x16x32(va, pb, acc[t]);
-    }
-  }
-
-  const float l_tot = wave_sum_xor16_32(l_run);
-  const bool live = l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
-  const float lse = live ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
-  if (!head_ok) return;
-  if (a.S == 1 && !a.force_partials) {
-    uint16_t* op = a.out + ((size_t)b * a.Hq + h) * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = DPL * (4 * g + i);
-      if constexpr (DPL == 8) {
-        u32x4 w;
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2)
-          w[t2] = pack_bf16x2(acc[2 * t2][i] * inv, acc[2 * t2 + 1][i] * inv);
-        *reinterpret_cast<u32x4*>(op + d0) = w;
-      } else {
-        u32x2 w;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-          w[t2] = pack_bf16x2(acc[2 * t2][i] * inv, acc[2 * t2 + 1][i] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
-      }
-    }
-    if (g == 0 && a.lse_out) a.lse_out[(size_t)b * a.Hq + h] = lse;
-    return;
-  }
-  const size_t row = ((size_t)b * a.Hq + h) * a.S + split;
-  float* op = a.part_o + row * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d0 = DPL * (4 * g + i);
-#pragma unroll
-    for (int t4 = 0; t4 < DPL / 4; ++t4) {
-      const f32x4 w = {acc[4 * t4][i] * inv, acc[4 * t4 + 1][i] * inv, acc[4 * t4 + 2][i] * inv,
-                       acc[4 * t4 + 3][i] * inv};
-      *reinterpret_cast<f32x4*>(op + d0 + 4 * t4) = w;
-    }
-  }
-  if (g == 0) a.part_lse[row] = lse;
-}
-
 template <int D, int W>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream,
                                   const KernelEvents& ev) {
@@ -810,31 +544,8 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream, int W
   return launch_decode_t<D, 1>(a, stream, ev);
 }
 
-template <int D>
-static hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t stream,
-                                     const KernelEvents& ev) {
-  using P = DpLds<D>;
-  static std::atomic<int> state[kMaxDevices];
-  const hipError_t e = lds_attribute_once(
-      state, reinterpret_cast<const void*>(decode_rows_kernel<D>), P::BYTES);
-  if (e != hipSuccess) return e;
-  launch_kernel(decode_rows_kernel<D>, dim3(a.Hkv / P::KH, a.S, a.B), dim3(64 * P::KH),
-                (uint32_t)P::BYTES, stream, ev, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, size_t desc_len,
                          const KernelEvents& ev) {
-  if (a.heads_per_wg > 1) {
-    const hipError_t e = a.D == 128 ? launch_decode_rows<128>(a, stream, ev)
-                                    : launch_decode_rows<64>(a, stream, ev);
-    snprintf(desc, desc_len,
-             "decode_rows<D=%d,KV heads per work-group=%d,bf16,whole rows into LDS> "
-             "grid=(%d,%d,%d) block=%d part_len=%d splits=%d",
-             a.D, a.heads_per_wg, a.Hkv / a.heads_per_wg, a.S, a.B, 64 * a.heads_per_wg,
-             a.part_len, a.S);
-    return e;
-  }
   const int W = decode_waves(a);
   hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W, ev)
                             : launch_decode_d<64>(a, stream, W, ev);

@@ -32,7 +32,6 @@ struct DecodeArgs {
   const int32_t* key_lo;         // [B] first key of the row's document, or null (none)
   const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
   const float* v_scales;         //   or null: one scale per pool (folded as above)
-  int heads_per_wg;              // > 1: whole-row variant, that many KV heads per work-group
 };
 
 struct ReduceArgs {
