@@ -441,10 +441,12 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * count as zero.  It combines (and) with the causal bound, the window, the
  * document ranges and ALiBi.  The prefill walks only the 64-key tiles that one of
  * its four 64-row query blocks lists (256-row work-groups) and masks a listed tile
- * whole for the rows of a query block that does not list it.  Block maps take bf16
- * pools, no key parts, and at most 262144 keys per sequence (max_pages x
- * page_size); other requests are PA_ERR_UNSUPPORTED.  The map is data, read on the
- * device.
+ * whole for the rows of a query block that does not list it; there block maps take
+ * bf16 pools, no key parts, and at most 262144 keys per sequence (max_pages x
+ * page_size); other requests are PA_ERR_UNSUPPORTED.  The decode takes a map of one
+ * query block per sequence (its row is query index 0 of a one-row run),
+ * block_map[b][j / 64], and walks only the 32-key chunks of listed tiles, with bf16
+ * or FP8 pools and any split count.  The map is data, read on the device.
  *
  * The _ex entry points take every option of an operation in one struct; the
  * entry points above are these with fixed options.  A NULL opts is PA_ERR_NULL; a
@@ -473,6 +475,10 @@ typedef struct {
   const float* k_scales;      /* kv_fp8 only: NULL (the pool scales above), or device
                                  [num_pages, Hkv] float32 scales per (page, KV head)     */
   const float* v_scales;      /* with k_scales (both or neither)                          */
+  const uint8_t* block_map;   /* NULL, or device uint8 [B, block_map_k_blocks]: the 64-key
+                                 tiles each sequence's decode row sees (block maps above;
+                                 the row is query index 0 of its one-row run)             */
+  int32_t block_map_k_blocks; /* key blocks of 64 keys per sequence in the map (>= 1)     */
 } pa_decode_opts;
 
 typedef struct {

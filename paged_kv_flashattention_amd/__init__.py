@@ -342,7 +342,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                       stream=None, validate: bool = False, window_left: int = 0,
                       alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
-                      key_lo: Optional[torch.Tensor] = None):
+                      key_lo: Optional[torch.Tensor] = None,
+                      block_map: Optional[torch.Tensor] = None):
     """Decode attention: q [B, Hq, D] against each sequence's paged history.
 
     ``max_seq_len`` is a host-side bound of ``seq_lens``; if omitted it is read
@@ -353,11 +354,14 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: 
     ``kernel_events`` = (start, stop) torch.cuda.Event pair (timing enabled, recorded
     once already) that the partition kernel's dispatch stamps with its own start and
     end (see pa_decode_opts).  ``key_lo`` (int32 [B] on the device): document masks,
-    the first key of the document each decode row belongs to.
+    the first key of the document each decode row belongs to.  ``block_map`` (uint8
+    [B, key blocks] on the device): the row of sequence b sees key j only if
+    block_map[b, j // 64] is nonzero (a mask in block form; blocks outside the map
+    count as zero).
     """
     return _decode(None, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
                    num_splits, out, lse, workspace, return_lse, stream, validate, window_left,
-                   alibi_slopes, kernel_events, key_lo)
+                   alibi_slopes, kernel_events, key_lo, block_map)
 
 
 def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_scale: float,
@@ -367,14 +371,16 @@ def paged_attn_decode_fp8(q, k_pool, v_pool, block_tables, seq_lens, softmax_sca
                           workspace: Optional[torch.Tensor] = None, return_lse: bool = False,
                           stream=None, validate: bool = False, window_left: int = 0,
                           alibi_slopes: Optional[torch.Tensor] = None, kernel_events=None,
-                          key_lo: Optional[torch.Tensor] = None):
+                          key_lo: Optional[torch.Tensor] = None,
+                          block_map: Optional[torch.Tensor] = None):
     """Decode attention over FP8 E4M3 pools (uint8 codes): keys stand for
     decode(code) * k_scale, values for decode(code) * v_scale, with one scale per pool
     (floats) or per (page, KV head) (float32 tensors [num_pages, Hkv] on the device).
     Arguments and results are paged_attn_decode's."""
     return _decode(_scales(k_scale, v_scale), q, k_pool, v_pool, block_tables, seq_lens,
                    softmax_scale, max_seq_len, num_splits, out, lse, workspace, return_lse,
-                   stream, validate, window_left, alibi_slopes, kernel_events, key_lo)
+                   stream, validate, window_left, alibi_slopes, kernel_events, key_lo,
+                   block_map)
 
 
 def _window(window_left) -> int:
@@ -414,7 +420,7 @@ def _events(kernel_events):
 
 def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, max_seq_len,
             num_splits, out, lse, workspace, return_lse, stream, validate, window_left=0,
-            alibi_slopes=None, kernel_events=None, key_lo=None):
+            alibi_slopes=None, kernel_events=None, key_lo=None, block_map=None):
     window_left = _window(window_left)
     if scales is None:
         _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
@@ -466,13 +472,19 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
             if bool((lo_h < 0).any()) or bool((lo_h > lens_h).any()):
                 raise ValueError("key_lo must lie in [0, seq_lens]")
         lo_ptr = key_lo.data_ptr()
+    bm_ptr, bm_k = None, 0
+    if block_map is not None:
+        _need(block_map, "block_map", torch.uint8, 2, dev)
+        if block_map.shape[0] != B:
+            raise ValueError(f"block_map must be [B={B}, key blocks]")
+        bm_ptr, bm_k = block_map.data_ptr(), block_map.shape[1]
     ev0, ev1 = _events(kernel_events)
     ksp = vsp = None
     if isinstance(scales, _PageScales):
         ksp, vsp = scales.check(k_pool.shape, dev)
     opts = _lib.DecodeOpts(int(num_splits), window_left, 0 if scales is None else 1,
                            *(_pool_scales(scales) if scales is not None else (1.0, 1.0)),
-                           alibi_ptr, ev0, ev1, lo_ptr, ksp, vsp)
+                           alibi_ptr, ev0, ev1, lo_ptr, ksp, vsp, bm_ptr, bm_k)
     need = int(lib.paged_attn_decode_ex_workspace_bytes(B, Hq, Hkv, D, int(max_seq_len),
                                                         ctypes.byref(opts)))
     if workspace is not None:
@@ -485,7 +497,7 @@ def _decode(scales, q, k_pool, v_pool, block_tables, seq_lens, softmax_scale, ma
     tail = (int(max_seq_len), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
     with torch.cuda.device(dev):
         if (window_left or alibi_ptr is not None or ev0 is not None or lo_ptr is not None
-                or ksp is not None):
+                or ksp is not None or bm_ptr is not None):
             _check(lib.paged_attn_decode_ex(*head, int(max_seq_len), ctypes.byref(opts),
                                             *tail[2:]))
         elif scales is None:

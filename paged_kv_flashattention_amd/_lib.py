@@ -25,7 +25,8 @@ class DecodeOpts(ctypes.Structure):
                 ("v_scale", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
                 ("kernel_start_event", ctypes.c_void_p), ("kernel_stop_event", ctypes.c_void_p),
                 ("key_lo", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
-                ("v_scales", ctypes.c_void_p)]
+                ("v_scales", ctypes.c_void_p), ("block_map", ctypes.c_void_p),
+                ("block_map_k_blocks", ctypes.c_int32)]
 
 
 class PrefillOpts(ctypes.Structure):

@@ -121,7 +121,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
                 int32_t num_splits, bool fp8 = false, float k_scale = 1.f,
                 float v_scale = 1.f, int32_t window = 0, const float* alibi = nullptr,
                 const int32_t* key_lo = nullptr, const float* k_scales = nullptr,
-                const float* v_scales = nullptr) {
+                const float* v_scales = nullptr, const uint8_t* block_map = nullptr,
+                int32_t bm_kb = 0) {
   if (B < 0 || max_seq_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d max_seq_len=%d", what, B, max_seq_len);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
@@ -140,6 +141,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
     return fail(PA_ERR_MISALIGNED, "%s: key_lo must be 4-byte aligned", what);
   st = page_scales_ok(what, fp8, k_scales, v_scales);
   if (st) return st;
+  if (block_map && bm_kb < 1)
+    return fail(PA_ERR_SHAPE, "%s: block map of %d key blocks per sequence", what, bm_kb);
   // with scales per page the pool scales are not used
   if (k_scales) k_scale = v_scale = 1.f;
   if (fp8 && !(scales_ok(k_scale, v_scale) && softmax_scale * k_scale <= 3.0e38f))
@@ -170,6 +173,8 @@ int decode_args(pa::DecodeArgs& a, const char* what, const void* q, const void* 
   a.key_lo = key_lo;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.block_map = block_map;
+  a.bm_kb = bm_kb;
   return PA_OK;
 }
 
@@ -230,13 +235,14 @@ int decode_impl(const char* what, void* out, float* lse_out, const void* q, cons
                 float k_scale, float v_scale, void* stream, int32_t window = 0,
                 const float* alibi = nullptr, const pa::KernelEvents& ev = pa::KernelEvents(),
                 const int32_t* key_lo = nullptr, const float* k_scales = nullptr,
-                const float* v_scales = nullptr) {
+                const float* v_scales = nullptr, const uint8_t* block_map = nullptr,
+                int32_t bm_kb = 0) {
   g_last_error[0] = 0;
   pa::DecodeArgs a;
   int st = decode_args(a, what, q, k_pool, v_pool, block_tables, seq_lens, B, max_pages,
                        num_pages, page_size, Hq, Hkv, D, softmax_scale, max_seq_len,
                        num_splits, fp8, k_scale, v_scale, window, alibi, key_lo, k_scales,
-                       v_scales);
+                       v_scales, block_map, bm_kb);
   if (st) return st;
   if (B == 0) {
     snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
@@ -814,7 +820,8 @@ int paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k
                      opts->num_splits, workspace, workspace_bytes, opts->kv_fp8 == 1,
                      opts->kv_fp8 ? opts->k_scale : 1.f, opts->kv_fp8 ? opts->v_scale : 1.f,
                      stream, opts->window_left, opts->alibi_slopes, events_of(opts),
-                     opts->key_lo, opts->k_scales, opts->v_scales);
+                     opts->key_lo, opts->k_scales, opts->v_scales, opts->block_map,
+                     opts->block_map_k_blocks);
 }
 
 size_t paged_attn_decode_ex_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,

@@ -23,6 +23,7 @@
 // Stack (Part 2)", section 2.2: a second kernel combines the chunks).  Merging in
 // the last-arriving work-group instead was measured slower on MI355X: the partials
 // must then bypass the per-XCD L2 caches.
+#include <limits.h>
 #include <stdio.h>
 
 #include "common.hpp"
@@ -222,7 +223,8 @@ __device__ __forceinline__ void decode_widen_v8(DecodeChunk<D>& c) {
     }
 }
 
-template <int D, int W, bool F8>
+// BM: a block map is given (a.block_map), compiled in only then.
+template <int D, int W, bool F8, bool BM = false>
 __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) {
   constexpr int DPL = D / 16;   // d values per lane per V row = MFMA d-tiles
   const int lane = threadIdx.x & 63;
@@ -294,9 +296,36 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
   const int per = (n_chunks + W - 1) / W;
   int c = min(n_chunks, wave * per);
   const int c_hi = min(n_chunks, c + per);
+  // Block map (a mask in block form): the row, query index 0 of its one-row run, sees
+  // the keys of the 64-key tiles that entry [b][tile] lists.  A chunk lies in one tile
+  // (chunks are 32-key aligned), so the walk visits only the chunks of listed tiles:
+  // lm holds the listed bits of tiles tb .. tb + 63 (one ballot over a load per lane).
+  const uint8_t* bmap = BM ? a.block_map + (size_t)b * a.bm_kb : nullptr;
+  int tb = INT_MIN;
+  uint64_t lm = 0;
+  auto next_listed = [&](int cc, int lim) {
+    while (cc < lim) {
+      const int t = (k_begin + 32 * cc) >> 6;
+      if (t < tb || t >= tb + 64) {
+        tb = t;
+        const int tl = t + lane;
+        lm = __builtin_amdgcn_ballot_w64(tl < a.bm_kb && bmap[min(tl, a.bm_kb - 1)] != 0);
+      }
+      const uint64_t m = lm >> (t - tb);
+      if (m & 1) return cc;
+      // the first chunk of the next listed tile (of tile tb + 64 when none is left)
+      const int tn = m ? t + (int)__builtin_ctzll(m) : tb + 64;
+      cc = max(cc + 1, ((tn << 6) - k_begin) >> 5);
+    }
+    return lim;
+  };
   // Outer loop: one register window of 64 table entries per pass (lane j holds
   // entry base + j); the inner loop over the chunks it covers issues no other loads.
   while (c < c_hi) {
+    if constexpr (BM) {
+      c = next_listed(c, c_hi);
+      if (c >= c_hi) break;
+    }
     const int base = (k_begin + 32 * c) >> a.ps_shift;
     const int tab = bt[min(base + lane, a.max_pages - 1)];
     const int c_end = min(c_hi, (((base + 64) << a.ps_shift) - k_begin) >> 5);
@@ -328,9 +357,13 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       __builtin_amdgcn_sched_barrier(0);
       load_v(ch, p0, p1, c0);
     }
-    for (; c < c_end; ++c) {
+    for (; c < c_end;) {
+      // the next chunk to walk; its loads are issued during this one (the last chunk of
+      // a window repeats its own addresses, so the loads are unconditional)
+      int cn = c + 1;
+      if constexpr (BM) cn = next_listed(c + 1, c_end);
       const int c0 = k_begin + 32 * c;
-      const int c0n = k_begin + 32 * min(c + 1, c_end - 1);
+      const int c0n = k_begin + 32 * (cn < c_end ? cn : c);
       const int pn0 = page(c0n);
       const int pn1 = page(c0n + 16);
       const ChunkScales scn = scales_of(pn0, pn1);
@@ -426,6 +459,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       }
       load_v(ch, pn0, pn1, c0n);
       sc = scn;
+      c = cn;
     }
   }
 
@@ -517,10 +551,16 @@ template <int D, int W>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream,
                                   const KernelEvents& ev) {
   dim3 grid(a.Hkv, a.S, a.B);
-  if (a.kv_fp8)
+  if (a.block_map) {
+    if (a.kv_fp8)
+      launch_kernel(decode_partition_kernel<D, W, true, true>, grid, dim3(64 * W), 0, stream, ev, a);
+    else
+      launch_kernel(decode_partition_kernel<D, W, false, true>, grid, dim3(64 * W), 0, stream, ev, a);
+  } else if (a.kv_fp8) {
     launch_kernel(decode_partition_kernel<D, W, true>, grid, dim3(64 * W), 0, stream, ev, a);
-  else
+  } else {
     launch_kernel(decode_partition_kernel<D, W, false>, grid, dim3(64 * W), 0, stream, ev, a);
+  }
   return hipGetLastError();
 }
 
@@ -550,9 +590,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, char* desc, si
   hipError_t e = a.D == 128 ? launch_decode_d<128>(a, stream, W, ev)
                             : launch_decode_d<64>(a, stream, W, ev);
   snprintf(desc, desc_len,
-           "decode_partition<D=%d,W=%d,%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
-           W, a.kv_fp8 ? (a.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16", a.Hkv,
-           a.S, a.B, 64 * W, a.part_len, a.S);
+           "decode_partition<D=%d,W=%d,%s%s> grid=(%d,%d,%d) block=%d part_len=%d splits=%d", a.D,
+           W, a.kv_fp8 ? (a.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16",
+           a.block_map ? ",block map" : "", a.Hkv, a.S, a.B, 64 * W, a.part_len, a.S);
   return e;
 }
 

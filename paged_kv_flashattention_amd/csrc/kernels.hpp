@@ -32,6 +32,8 @@ struct DecodeArgs {
   const int32_t* key_lo;         // [B] first key of the row's document, or null (none)
   const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
   const float* v_scales;         //   or null: one scale per pool (folded as above)
+  const uint8_t* block_map;      // [B, bm_kb] listed 64-key tiles of each row, or null
+  int bm_kb;
 };
 
 struct ReduceArgs {

@@ -168,3 +168,90 @@ def test_block_map_at_full_size_every_work_group(require_gpu):
     gl = as_f64(lse)[[t for t, _ in rows], [h for _, h in rows]]
     assert_parity(got, ro, "full-size block map")
     assert_lse(gl, rl, "full-size block map lse")
+
+
+# ---- decode: the row is query index 0 of its one-row run, so the map is [B, key blocks]
+
+def _decode_oracle(case, bm, kp=None, vp=None, window=0):
+    if kp is None:
+        kp, vp = bits(case.k_pool), bits(case.v_pool)
+    return oracle.attention_ref(bits(case.q), kp, vp, case.block_tables.cpu().numpy(),
+                                case.seq_lens_k.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
+                                case.scale, False, case.page_size, window, None, None,
+                                oracle.block_map_mask(bm[:, None, :]))
+
+
+DECODE_CASES = [
+    # lens, Hq, Hkv, D, ps, splits, density
+    ([0, 1, 17, 500, 4096, 63, 64, 65], 8, 2, 128, 16, 0, 0.5),
+    ([3000, 1000, 129], 28, 4, 128, 32, 3, 0.3),
+    ([777, 2048], 16, 8, 64, 64, 1, 0.6),
+    ([8192] * 4, 28, 4, 128, 16, 2, 0.1),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,ps,splits,density", DECODE_CASES)
+def test_decode_block_map(require_gpu, lens, Hq, Hkv, D, ps, splits, density):
+    print(f"[block map decode] lens={lens} Hq={Hq} Hkv={Hkv} D={D} ps={ps} S={splits} "
+          f"density={density}", flush=True)
+    case = make_case("bmd", seq_lens=lens, Hq=Hq, Hkv=Hkv, D=D, page_size=ps, seed=sum(lens) + D,
+                     device="cuda")
+    rng = np.random.default_rng(len(lens))
+    bm = (rng.random((len(lens), max(1, -(-max(lens) // 64)))) < density).astype(np.uint8)
+    out, lse = pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                    case.seq_lens_k, case.scale, max_seq_len=max(lens),
+                                    num_splits=splits, return_lse=True, validate=True,
+                                    block_map=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = _decode_oracle(case, bm)
+    assert_parity(as_f64(out), o_ref, "decode block map")
+    assert_lse(as_f64(lse), l_ref, "decode block map lse")
+
+
+def _sink_window_map(B, L, sink_blocks=1, window_blocks=4):
+    """Attention sinks plus a recent window, in block form: the first sink_blocks and
+    the last window_blocks 64-key blocks of each sequence."""
+    kb = -(-L // 64)
+    m = np.zeros((B, kb), np.uint8)
+    m[:, :sink_blocks] = 1
+    m[:, max(0, kb - window_blocks):] = 1
+    return m
+
+
+def test_decode_block_map_sinks_and_window_full_size(require_gpu):
+    """The C2 decode (32 x 8192, Hq 28 / Hkv 4) with sinks + a recent window as a block
+    map: every (sequence, head) row against the oracle."""
+    from workloads import make_config
+    case = make_config("qwen7b_decode", device="cuda")
+    bm = _sink_window_map(32, 8192)
+    out, lse = pa.paged_attn_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                    case.seq_lens_k, case.scale, max_seq_len=8192,
+                                    return_lse=True, block_map=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = _decode_oracle(case, bm)
+    assert_parity(as_f64(out), o_ref, "C2 sinks + window")
+    assert_lse(as_f64(lse), l_ref, "C2 sinks + window lse")
+
+
+def test_decode_block_map_fp8_and_window(require_gpu):
+    """FP8 pools (scales per page) with a map and a sliding window together."""
+    from oracle import fp8 as of
+    from workloads import random_e4m3_codes
+    case = make_case("bmf", seq_lens=[3000, 700, 1500], Hq=16, Hkv=4, D=128, page_size=16,
+                     seed=12, device="cuda")
+    shape = tuple(case.k_pool.shape)
+    kc, vc = random_e4m3_codes(shape, 1, "cuda"), random_e4m3_codes(shape, 2, "cuda")
+    rng = np.random.default_rng(3)
+    ks = (2.0 ** rng.uniform(-8, -4, (shape[0], shape[2]))).astype(np.float32)
+    vs = (2.0 ** rng.uniform(-6, -3, (shape[0], shape[2]))).astype(np.float32)
+    bm = (rng.random((3, 47)) < 0.5).astype(np.uint8)
+    out, lse = pa.paged_attn_decode_fp8(case.q, kc, vc, case.block_tables, case.seq_lens_k,
+                                        case.scale, torch.from_numpy(ks).cuda(),
+                                        torch.from_numpy(vs).cuda(), max_seq_len=3000,
+                                        return_lse=True, window_left=1200,
+                                        block_map=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = _decode_oracle(case, bm, of.dequantize_pool(kc.cpu().numpy(), ks),
+                                  of.dequantize_pool(vc.cpu().numpy(), vs), window=1200)
+    assert_parity(as_f64(out), o_ref, "fp8 decode block map + window")
+    assert_lse(as_f64(lse), l_ref, "fp8 decode block map + window lse")
