@@ -223,8 +223,9 @@ __device__ __forceinline__ void decode_widen_v8(DecodeChunk<D>& c) {
     }
 }
 
-// BM: a block map is given (a.block_map), compiled in only then.
-template <int D, int W, bool F8, bool BM = false>
+// BM: a block map is given (a.block_map); PS: FP8 pools with scales per (page, KV
+// head) (a.k_scales).  Each is compiled in only when used.
+template <int D, int W, bool F8, bool BM = false, bool PS = false>
 __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) {
   constexpr int DPL = D / 16;   // d values per lane per V row = MFMA d-tiles
   const int lane = threadIdx.x & 63;
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
     ChunkScales sc{1.f, 1.f, 1.f, 1.f};
     auto scales_of = [&](int p0, int p1) {
       ChunkScales r{1.f, 1.f, 1.f, 1.f};
-      if (F8 && a.k_scales) {
+      if constexpr (PS) {
         r.k0 = a.k_scales[(size_t)p0 * a.Hkv + kvh];
         r.k1 = a.k_scales[(size_t)p1 * a.Hkv + kvh];
         r.v0 = a.v_scales[(size_t)p0 * a.Hkv + kvh];
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       int cn = c + 1;
       if constexpr (BM) cn = next_listed(c + 1, c_end);
       const int c0 = k_begin + 32 * c;
-      const int c0n = k_begin + 32 * (cn < c_end ? cn : c);
+      const int c0n = k_begin + 32 * (BM ? (cn < c_end ? cn : c) : min(c + 1, c_end - 1));
       const int pn0 = page(c0n);
       const int pn1 = page(c0n + 16);
       const ChunkScales scn = scales_of(pn0, pn1);
@@ -386,8 +387,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       // FP8 pools with scales per (page, KV head): the keys of the chunk's first 16
       // rows come from page p0, the next 16 from p1 (the same page when pages hold
       // 32 or more keys), so each half has its own key scale in the score multiplier
-      const float sm0 = F8 && a.k_scales ? a.scale_log2 * sc.k0 : a.scale_log2;
-      const float sm1 = F8 && a.k_scales ? a.scale_log2 * sc.k1 : a.scale_log2;
+      const float sm0 = PS ? a.scale_log2 * sc.k0 : a.scale_log2;
+      const float sm1 = PS ? a.scale_log2 * sc.k1 : a.scale_log2;
       float s[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(DecodeArgs a) 
       for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
       // the value scale of each half's page goes onto P (the row sum above stays
       // unscaled): P V then sums p_j * v_scale(page of j) * decode(code_j)
-      if (F8 && a.v_scales) {
+      if constexpr (PS) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           p[j] *= sc.v0;
@@ -551,15 +552,21 @@ template <int D, int W>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream,
                                   const KernelEvents& ev) {
   dim3 grid(a.Hkv, a.S, a.B);
-  if (a.block_map) {
-    if (a.kv_fp8)
-      launch_kernel(decode_partition_kernel<D, W, true, true>, grid, dim3(64 * W), 0, stream, ev, a);
+  const dim3 block(64 * W);
+  if (a.kv_fp8 && a.k_scales) {
+    if (a.block_map)
+      launch_kernel(decode_partition_kernel<D, W, true, true, true>, grid, block, 0, stream, ev, a);
     else
-      launch_kernel(decode_partition_kernel<D, W, false, true>, grid, dim3(64 * W), 0, stream, ev, a);
+      launch_kernel(decode_partition_kernel<D, W, true, false, true>, grid, block, 0, stream, ev, a);
   } else if (a.kv_fp8) {
-    launch_kernel(decode_partition_kernel<D, W, true>, grid, dim3(64 * W), 0, stream, ev, a);
+    if (a.block_map)
+      launch_kernel(decode_partition_kernel<D, W, true, true>, grid, block, 0, stream, ev, a);
+    else
+      launch_kernel(decode_partition_kernel<D, W, true>, grid, block, 0, stream, ev, a);
+  } else if (a.block_map) {
+    launch_kernel(decode_partition_kernel<D, W, false, true>, grid, block, 0, stream, ev, a);
   } else {
-    launch_kernel(decode_partition_kernel<D, W, false>, grid, dim3(64 * W), 0, stream, ev, a);
+    launch_kernel(decode_partition_kernel<D, W, false>, grid, block, 0, stream, ev, a);
   }
   return hipGetLastError();
 }
