@@ -432,7 +432,7 @@ def time_step(step, steps, warmup, kernel_events=True):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ev = start.elapsed_time(stop) / steps
-    if not kernel_events or isinstance(step, (MixedStep, GraphStep)):
+    if not kernel_events or isinstance(step, (MixedStep, GraphStep, PreparedStep)):
         return wall, ev, None
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
@@ -740,12 +740,33 @@ def cpu_baseline_prefill(step, min_s=10.0, budget_s=15.0):
 
 # ---------------------------------------------------------------------------
 
+class PreparedStep:
+    """A step's C calls replayed through pa.prepared(): the arguments are marshalled
+    once and no Python-side checks run per call, as in a launch loop whose host cost
+    matters (the tiny decode is bound by it)."""
+
+    def __init__(self, step):
+        self.step = step
+        self.units, self.unit_name = step.units, step.unit_name
+        self.run = step.pa.prepared(step)
+
+    def __call__(self):
+        self.run()
+
+    def config(self):
+        cfg = dict(self.step.config())
+        cfg["launch"] = "pa.prepared: C calls replayed with marshalled arguments"
+        return cfg
+
+
 def secondary_figure(label, name, splits, args):
     """One secondary line: the workload `name` timed like the headline (a HIP graph
     replay when the label ends in _graph)."""
     s = make_step(name, splits)
     if label.endswith("_graph"):
         s = GraphStep(s, len(s.kv) if hasattr(s, "kv") else 1)
+    elif label.endswith("_prepared"):
+        s = PreparedStep(s)
     w2, e2, k2 = time_step(s, args.steps, args.warmup)
     v2 = rate(s.units, e2, s.unit_name)
     pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
@@ -869,6 +890,7 @@ def main():
         for label, name, splits in (("qwen7b_decode_graph", "qwen7b_decode", 0),
                                     ("qwen7b_decode_warm", "qwen7b_decode_warm", 0),
                                     ("tiny_decode", "tiny_decode", 0),
+                                    ("tiny_decode_prepared", "tiny_decode", 0),
                                     ("qwen7b_decode_fp8", "qwen7b_decode_fp8", 0),
                                     ("causal_prefill_fp8", "causal_prefill_fp8", 0),
                                     ("causal_prefill_block_map", "causal_prefill_block_map", 0),
