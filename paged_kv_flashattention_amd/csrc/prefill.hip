@@ -126,23 +126,6 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-// Exponential split (an experiment): PF_POLY_EXP2_PAIRS of the 8 exponential pairs
-// per block computed on the FMA units: 2^floor(x) (exponent) times a degree-3
-// polynomial for 2^f on [0, 1) fitted here for relative error (7.5e-5); x below
-// -126 gives 0.
-#ifndef PF_POLY_EXP2_PAIRS
-#define PF_POLY_EXP2_PAIRS 0
-#endif
-__device__ __forceinline__ float poly_exp2(float x) {
-  const float xc = fmaxf(x, -126.f);
-  const float fl = __builtin_floorf(xc);
-  const float f = xc - fl;
-  float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(0.07802428305149078f, f, 0.22606727480888367f),
-                                          f, 0.6958336234092712f), f, 0.9999251961708069f);
-  p = __builtin_amdgcn_ldexpf(p, (int)fl);
-  return x < -126.f ? 0.f : p;
-}
-
 // Keeps a value computed where it is written: later passes may not sink its
 // computation past this point (used to hold vector work between MFMAs).
 __device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
@@ -731,13 +714,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
 #pragma unroll
       for (int e = EPK * i; e < EPK * (i + 1); e += 2) {
         const float c = e < 8 ? bs.ca : bs.cb;
-        if (PF_POLY_EXP2_PAIRS > 0 && (e / 2) % (8 / (PF_POLY_EXP2_PAIRS > 0 ? PF_POLY_EXP2_PAIRS : 1)) == 0) {
-          pe[e] = poly_exp2(__builtin_fmaf(s_pend[e], c, neg_m));
-          pe[e + 1] = poly_exp2(__builtin_fmaf(s_pend[e + 1], c, neg_m));
-        } else {
-          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], c, neg_m));
-          pe[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], c, neg_m));
-        }
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e], c, neg_m));
+        pe[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_pend[e + 1], c, neg_m));
         if constexpr (PS) {
           const float v = e < 8 ? bs.va : bs.vb;
           pw[e / 2] = pack_bf16x2(pe[e] * v, pe[e + 1] * v);
