@@ -35,9 +35,6 @@ constexpr float kSumLimit = 256.f;     // 2^kRescaleSlack: bound on a lane's blo
 #ifndef PF_W8_MIN
 #define PF_W8_MIN 512
 #endif
-#ifndef PF_PINGPONG
-#define PF_PINGPONG 1
-#endif
 
 // Document masks: the smallest key_lo and the largest key_hi over query rows
 // r0 .. r0 + rows - 1 of the sequence whose rows start at token t0, reduced over
@@ -693,14 +690,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   // depend on it, so the matrix cores and the vector ALU of one wave overlap;
   // operand reads run two MFMAs ahead.  sched_barrier keeps the compiler from
   // regrouping the chunks.
-  // (the step in two halves: the scores of the next block with the pending block's
-  // exponentials, which returns the packed P, then that block's P V)
-  struct PendP {
-    u32x4 b0, b1;
-  };
-  auto step_qk = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp) {
+  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp) {
     constexpr int NK = D / 16;                 // QK MFMAs
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
+    constexpr int NV = 2 * (D / 32);           // PV MFMAs
+    const uint16_t* vp = vst(vsi);
     const BlkScale bs = blk_scale(vsi, kbp);
     const float neg_m0 = m_run == kNegInf ? 0.f : -m_run;
     const float neg_m = ALI ? neg_m0 + boff : neg_m0;
@@ -749,13 +743,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     }
     float ps = ps0 + ps1;
     settle(s_pend, bs, pw, ps);
-    s_pend = sn;
-    return PendP{u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]}};
-  };
-  auto step_pv = [&](const PendP& pp, int vsi, int kbp) {
-    constexpr int NV = 2 * (D / 32);           // PV MFMAs
-    const uint16_t* vp = vst(vsi);
-    const u32x4 pb0 = pp.b0, pb1 = pp.b1;
+    const u32x4 pb0 = {pw[0], pw[1], pw[2], pw[3]};
+    const u32x4 pb1 = {pw[4], pw[5], pw[6], pw[7]};
     // O^T += V^T P^T: MFMA i covers d-tile i % (D / 32) of 16-key half i / (D / 32)
     auto vfrag = [&](int i) {
       const uint16_t* vl =
@@ -775,10 +764,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       acc[t] = mfma32x32x16(vf[i], i < D / 32 ? pb0 : pb1, acc[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp) {
-    const PendP pp = step_qk(s_pend, kq, kbq, vsi, kbp);
-    step_pv(pp, vsi, kbp);
+    s_pend = sn;
   };
 
   // Software pipeline over 32-key blocks: while the matrix cores compute S of
@@ -942,24 +928,12 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     for (; u < U1; ++u) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
-      // first block of tile kt (pending) -> its second block.  Ping-pong: the second
-      // wave on each SIMD (waves W/2 ..) meets the tile's barrier between the two
-      // halves of this step, the first wave after it, so after every barrier one
-      // wave computes scores and exponentials while the other runs P V MFMAs (it has
-      // read tile kt's K, which the barrier lets be refilled, and its pending V stays
-      // resident: three V stages)
-      const PendP pp = step_qk(s_pend, kst(ks_cur), B1, vs_cur, B0);
-      if (PF_PINGPONG && wave >= W / 2) {
-        publish(kn, ks_cur ^ 1, vs_next);
-        issue_walk(u + 2);
-      }
-      step_pv(pp, vs_cur, B0);
+      // first block of tile kt (pending) -> its second block
+      step(s_pend, kst(ks_cur), B1, vs_cur, B0);
       mask(s_pend, kt * kPfBN + 32 * B1, u);
       // second block of tile kt -> first block of tile kn
-      if (!(PF_PINGPONG && wave >= W / 2)) {
-        publish(kn, ks_cur ^ 1, vs_next);
-        issue_walk(u + 2);
-      }
+      publish(kn, ks_cur ^ 1, vs_next);
+      issue_walk(u + 2);
       step(s_pend, kst(ks_cur ^ 1), B0, vs_cur, B1);
       mask(s_pend, kn * kPfBN + 32 * B0, u + 1);
       vs_cur = vs_next;
