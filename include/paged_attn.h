@@ -442,8 +442,9 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  * document ranges and ALiBi.  The prefill walks only the 64-key tiles that one of
  * its four 64-row query blocks lists (256-row work-groups) and masks a listed tile
  * whole for the rows of a query block that does not list it; there block maps take
- * bf16 pools, no key parts, and at most 262144 keys per sequence (max_pages x
- * page_size); other requests are PA_ERR_UNSUPPORTED.  The decode takes a map of one
+ * bf16 or FP8 pools (scales per pool or per page), no key parts, and at most 262144
+ * keys per sequence (max_pages x page_size); other requests are PA_ERR_UNSUPPORTED.
+ * The decode takes a map of one
  * query block per sequence (its row is query index 0 of a one-row run),
  * block_map[b][j / 64], and walks only the 32-key chunks of listed tiles, with bf16
  * or FP8 pools and any split count.  The map is data, read on the device.
@@ -507,7 +508,7 @@ typedef struct {
                            results are the same bits as the plain grid's.  0: plain grid */
   const uint8_t* block_map;   /* NULL, or device uint8 [B, block_map_q_blocks,
                                  block_map_k_blocks]: a mask in block form (block maps
-                                 above); bf16 pools, no key parts                         */
+                                 above); no key parts                                     */
   int32_t block_map_q_blocks; /* query blocks of 64 rows per sequence in the map (>= 1)   */
   int32_t block_map_k_blocks; /* key blocks of 64 keys per sequence in the map (>= 1)     */
 } pa_prefill_opts;

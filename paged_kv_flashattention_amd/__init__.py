@@ -613,15 +613,17 @@ def paged_attn_prefill_varlen_fp8(q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, b
                                   return_lse: bool = False, stream=None,
                                   validate: bool = False, window_left: int = 0,
                                   alibi_slopes: Optional[torch.Tensor] = None,
-                                  kernel_events=None, key_ranges=None):
+                                  kernel_events=None, key_ranges=None,
+                                  block_map: Optional[torch.Tensor] = None):
     """Ragged prefill over FP8 E4M3 pools (uint8 codes; keys stand for decode(code) *
     k_scale, values for decode(code) * v_scale; scales per pool as floats or per (page,
     KV head) as float32 tensors [num_pages, Hkv]), through paged_attn_prefill_ex.
-    ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass)."""
+    ``num_splits`` as paged_attn_prefill_varlen_splitk's (1: one pass); ``block_map``
+    as paged_attn_prefill_varlen's (one pass only)."""
     return _prefill((int(num_splits), workspace), q, k_pool, v_pool, cu_seqlens_q, seq_lens_k,
                     block_tables, softmax_scale, causal, max_q_len, out, lse, return_lse, stream,
                     validate, window_left, alibi_slopes, _scales(k_scale, v_scale),
-                    kernel_events, key_ranges)
+                    kernel_events, key_ranges, block_map=block_map)
 
 
 def prefill_num_splits(B: int, Hq: int, max_q_len: int) -> int:

@@ -362,8 +362,6 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     if (bm_qb < 1 || bm_kb < 1)
       return fail(PA_ERR_SHAPE, "%s: block map of %d x %d blocks per sequence", what, bm_qb,
                   bm_kb);
-    if (fp8)
-      return fail(PA_ERR_UNSUPPORTED, "%s: block maps need bf16 pools", what);
     if (num_splits > 1)
       return fail(PA_ERR_UNSUPPORTED, "%s: block maps take no key parts (num_splits %d)", what,
                   num_splits);

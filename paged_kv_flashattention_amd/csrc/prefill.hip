@@ -309,14 +309,14 @@ constexpr size_t kBsListBytes = (kBsMaxTiles + 16) * sizeof(int);
 // variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
 // downwards, which is how the ALiBi variants (general only) walk, so REV also
 // compiles the bias in.  PER: an item of a persistent work-group (hand-over in hd).
-// BS: a block map (general bf16 variant, 8 waves, no key parts).
+// BS: a block map (general variant, 8 waves, no key parts).
 template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER, bool BS = false>
 __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
                                         const PfSetup& s, PfHand& hd, uint16_t* pf_lds) {
   static_assert(!REV || GEN, "the downward walk is a general-variant feature");
   static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
-  static_assert(!BS || (GEN && !F8 && !PER && W == 8), "block maps: general bf16, 8 waves");
+  static_assert(!BS || (GEN && !PER && W == 8), "block maps: general variant, 8 waves");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   using L_ = PfLds<D>;
   using M_ = PfDma<D, W>;
@@ -1200,6 +1200,16 @@ template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   if (a.kv_fp8) {
+    if (a.block_map) {
+      // block maps take 256-row work-groups (prefill_waves)
+      if constexpr (W == 8) {
+        if (a.k_scales) return launch_prefill_w<D, 8, true, true, false, true, true>(a, stream, ev);
+        return a.alibi ? launch_prefill_w<D, 8, true, true, true, false, true>(a, stream, ev)
+                       : launch_prefill_w<D, 8, true, true, false, false, true>(a, stream, ev);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
     // scales per (page, KV head) (the entry point refuses them with ALiBi slopes)
     if (a.k_scales) return launch_prefill_w<D, W, true, true, false, true>(a, stream, ev);
     if (a.alibi) return launch_prefill_w<D, W, true, true, true>(a, stream, ev);
@@ -1207,7 +1217,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                     : launch_prefill_w<D, W, false, true, false>(a, stream, ev);
   }
   if (a.block_map) {
-    // block maps take 256-row work-groups (prefill_waves) and bf16 pools
+    // block maps take 256-row work-groups (prefill_waves)
     if constexpr (W == 8) {
       return a.alibi ? launch_prefill_w<D, 8, true, false, true, false, true>(a, stream, ev)
                      : launch_prefill_w<D, 8, true, false, false, false, true>(a, stream, ev);
@@ -1287,7 +1297,8 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
   else
     snprintf(order, sizeof(order), "KV groups in %d rank classes per XCD, unit-major",
              a.xcd_split);
-  const bool per = W == 8 && a.persist && !a.kv_fp8 && !a.alibi && a.window == 0 && !a.key_lo;
+  const bool per = W == 8 && a.persist && !a.kv_fp8 && !a.alibi && a.window == 0 && !a.key_lo &&
+                   !a.block_map;
   char pers[96] = "";
   int cus = 0;
   if (per && device_cus(&cus) == hipSuccess)
@@ -1297,11 +1308,12 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
                      (per ? (a.D == 128 ? PfLds<128>::q_bytes(8) : PfLds<64>::q_bytes(8)) : 0) +
                      (a.block_map ? kBsListBytes : 0);
   snprintf(desc, desc_len,
-           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s> grid=%d (%d heads x %d seqs x %d "
+           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s%s) block=%d lds=%zu",
            a.D, 32 * W, kPfBN,
            a.kv_fp8 ? (a.k_scales ? "fp8-e4m3-widened,scales per page" : "fp8-e4m3-widened")
-                    : (a.block_map ? "lds-dma,block map" : "lds-dma"),
+                    : "lds-dma",
+           a.block_map ? ",block map" : "",
            prefill_items(a), a.Hq, a.B, a.n_qt, a.S, order, pers, 64 * W, lds);
   return e;
 }

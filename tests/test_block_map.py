@@ -170,6 +170,56 @@ def test_block_map_at_full_size_every_work_group(require_gpu):
     assert_lse(gl, rl, "full-size block map lse")
 
 
+FP8_CASES = [
+    # hist, q_lens, Hq, Hkv, D, ps, causal, density, scales, alibi
+    ([0, 300, 40], [700, 260, 100], 8, 2, 128, 16, True, 0.5, "pool", False),
+    ([500, 0], [300, 513], 8, 4, 128, 32, False, 0.3, "page", False),
+    ([100, 40], [600, 90], 8, 2, 64, 64, True, 0.7, "page", False),
+    ([0, 200], [900, 400], 8, 2, 128, 16, True, 0.6, "pool", True),
+]
+
+
+@pytest.mark.parametrize("hist,ql,Hq,Hkv,D,ps,causal,density,scales,alibi", FP8_CASES)
+def test_block_map_fp8_pools(require_gpu, hist, ql, Hq, Hkv, D, ps, causal, density, scales,
+                             alibi):
+    """FP8 E4M3 pools (one scale per pool, or per (page, KV head)) with a block map: the
+    oracle attends over the same codes dequantised with the same scales."""
+    from oracle import fp8 as of
+    from workloads import random_e4m3_codes
+    print(f"[block map fp8] hist={hist} q={ql} Hq={Hq} Hkv={Hkv} D={D} ps={ps} "
+          f"causal={causal} density={density} scales={scales} alibi={alibi}", flush=True)
+    case = make_case("bm8", hist_lens=hist, q_lens=ql, write_new=True, causal=causal, Hq=Hq,
+                     Hkv=Hkv, D=D, page_size=ps, seed=sum(hist) + sum(ql) + ps, device="cuda")
+    shape = tuple(case.k_pool.shape)
+    P = shape[0]
+    kc = random_e4m3_codes(shape, sum(ql), "cuda")
+    vc = random_e4m3_codes(shape, sum(ql) + 1, "cuda")
+    rng = np.random.default_rng(sum(hist))
+    if scales == "page":
+        ks = (2.0 ** rng.uniform(-8, -4, (P, Hkv))).astype(np.float32)
+        vs = (2.0 ** rng.uniform(-6, -3, (P, Hkv))).astype(np.float32)
+        k_arg, v_arg = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+        kd, vd = of.dequantize_pool(kc.cpu().numpy(), ks), of.dequantize_pool(vc.cpu().numpy(), vs)
+    else:
+        k_arg, v_arg = 2.0 ** -6, 2.0 ** -4
+        kd, vd = of.dequantize_pool(kc.cpu().numpy(), k_arg), of.dequantize_pool(vc.cpu().numpy(), v_arg)
+    slopes = None
+    if alibi:
+        slopes = torch.tensor([2.0 ** (-(h + 1) / 2) for h in range(Hq)], dtype=torch.float32,
+                              device="cuda")
+    bm = random_map(case, density, sum(ql) + 7)
+    out, lse = pa.paged_attn_prefill_varlen_fp8(
+        case.q, kc, vc, case.cu_seqlens_q, case.seq_lens_k, case.block_tables, case.scale,
+        k_arg, v_arg, causal=causal, max_q_len=case.max_q_len, return_lse=True, validate=True,
+        alibi_slopes=slopes, block_map=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    desc = pa.describe_launch()
+    assert "block map" in desc and "fp8" in desc.lower(), desc
+    o_ref, l_ref = reference(case, bm, causal, alibi=slopes, kp=kd, vp=vd)
+    assert_parity(as_f64(out), o_ref, "fp8 block map")
+    assert_lse(as_f64(lse), l_ref, "fp8 block map lse")
+
+
 # ---- decode: the row is query index 0 of its one-row run, so the map is [B, key blocks]
 
 def _decode_oracle(case, bm, kp=None, vp=None, window=0):

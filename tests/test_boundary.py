@@ -277,8 +277,8 @@ def test_binding_takes_page_scales_as_tensor_pairs():
 
 
 def test_block_map_options_are_checked(lib):
-    """Block maps: positive dimensions, bf16 pools, no key parts, at most 262144 keys
-    per sequence; no workspace."""
+    """Block maps: positive dimensions, no key parts, at most 262144 keys per sequence;
+    no workspace."""
     from paged_kv_flashattention_amd import _lib
     p = lib.paged_attn_prefill_ex
     pargs = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 4, 8, 16, 8, 2, 128, 0.1]
@@ -290,7 +290,8 @@ def test_block_map_options_are_checked(lib):
             setattr(o, k, v)
         return o
     for kw, st in [(dict(block_map_q_blocks=0), 2), (dict(block_map_k_blocks=-1), 2),
-                   (dict(kv_fp8=1, k_scale=1.0, v_scale=1.0), 3), (dict(num_splits=2), 3)]:
+                   (dict(num_splits=2), 3), (dict(kv_fp8=1, k_scale=1.0, v_scale=1.0,
+                                                  num_splits=2), 3)]:
         o = opts(**kw)
         assert p(*pargs, ctypes.byref(o), None, 0, None) == st, kw
         assert b"block map" in lib.pa_last_error()
