@@ -51,7 +51,7 @@ def parse():
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
                             "long_decode", "long_decode_auto", "causal_prefill",
                             "causal_prefill_fp8", "causal_prefill_block_map",
-                            "mixed_ragged", "tiny_decode",
+                            "mixed_ragged", "mixed_ragged_two_streams", "tiny_decode",
                             "qwen7b_decode_warm"])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,17 +279,21 @@ class MixedStep:
 
     The prefill's key-part count comes from paged_attn_prefill_plan_splits over the
     chunks' host lengths (as a scheduler would plan it), the decode's split count
-    from the library's rule.  The prefill chunks and the decode rows read disjoint
-    outputs and both only read the pools after the write, so the decode runs on a
-    second stream (default priority) after the write, issued behind the prefill so
-    that its work-groups fill the slots the prefill leaves; the step ends when both
-    have finished (the launch stream waits for the second one)."""
+    from the library's rule.  With one_launch (the workload's figure) the prefill and
+    the decode run in one kernel (paged_attn_mixed) after the write, then the two
+    merges, all on the launch stream.  Without it the prefill chunks and the decode
+    rows, which read disjoint outputs and only read the pools after the write, run as
+    separate kernels: the decode on a second stream (default priority) after the
+    write, issued behind the prefill so that its work-groups fill the slots the
+    prefill leaves; the step ends when both have finished (the launch stream waits for
+    the second one)."""
 
-    def __init__(self, name="mixed_ragged"):
+    def __init__(self, name="mixed_ragged", one_launch=True):
         import torch
         import paged_kv_flashattention_amd as pa
         from workloads import make_config, units
         self.pa = pa
+        self.one_launch = one_launch
         self.case = c = make_config(name, "cuda")
         n = 5
         self.t_pf = int(c.cu_seqlens_q[n])
@@ -315,6 +319,14 @@ class MixedStep:
         self.units = self.flops
         self.unit_name = "TFLOP/s"
         self.side = torch.cuda.Stream()
+        if one_launch:
+            # one kernel for both parts (paged_attn_mixed) with the same key parts and
+            # the library's decode split count for that launch, then the two merges,
+            # all on the launch stream
+            need = pa.mixed_workspace_bytes(c.Hq, c.Hkv, c.D, (n, self.t_pf, self.max_q, self.S_pf),
+                                            (c.B - n, self.max_d, 0))
+            self.ws_mixed = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            self.launch = None
 
     def __call__(self):
         import torch
@@ -323,6 +335,17 @@ class MixedStep:
         main = torch.cuda.current_stream()
         pa.kv_page_write(c.k_pool, c.v_pool, c.k_new, c.v_new, c.cu_new, c.start_pos,
                          c.block_tables)
+        if self.one_launch:
+            pa.paged_attn_mixed(c.k_pool, c.v_pool, c.scale,
+                                prefill=(self.q_pf, self.cu_pf, self.lens_pf, self.bt_pf),
+                                decode=(self.q_d, self.bt_d, self.lens_d),
+                                prefill_max_q_len=self.max_q, prefill_num_splits=self.S_pf,
+                                decode_max_seq_len=self.max_d, decode_num_splits=0,
+                                prefill_out=self.out_pf, decode_out=self.out_d,
+                                workspace=self.ws_mixed)
+            if self.launch is None:
+                self.launch = pa.describe_launch()
+            return
         self.side.wait_stream(main)
         pa.paged_attn_prefill_varlen_splitk(self.q_pf, c.k_pool, c.v_pool, self.cu_pf,
                                             self.lens_pf, self.bt_pf, c.scale, causal=True,
@@ -336,10 +359,16 @@ class MixedStep:
 
     def config(self):
         c = self.case
-        return {"workload": c.name, "requests": c.B, "prefill_chunks": 5, "chunk_len": 512,
-                "decode_rows": c.B - 5, "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.D,
-                "page_size": c.page_size, "prefill_key_parts": self.S_pf,
-                "decode_splits": self.S}
+        cfg = {"workload": c.name, "requests": c.B, "prefill_chunks": 5, "chunk_len": 512,
+               "decode_rows": c.B - 5, "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.D,
+               "page_size": c.page_size, "prefill_key_parts": self.S_pf,
+               "decode_splits": self.S, "launch": "prefill and decode kernels on two streams"}
+        if self.one_launch:
+            import re
+            m = re.search(r"x (\d+) splits", self.launch or "")
+            cfg.update(decode_splits=int(m.group(1)) if m else None,
+                       launch="one kernel for both parts (paged_attn_mixed)")
+        return cfg
 
 
 class GraphStep:
@@ -398,7 +427,9 @@ def make_step(name, num_splits=0):
         return BlockMapPrefillStep("causal_prefill")
     if name == "long_history_chunk":
         return PrefillStep(name, splitk=True)
-    return MixedStep(name)
+    if name == "mixed_ragged_two_streams":
+        return MixedStep("mixed_ragged", one_launch=False)
+    return MixedStep(name, one_launch=True)
 
 
 def next_events(step):
@@ -463,8 +494,9 @@ def rate(units, ms, unit_name):
 
 # per workload: the recorded counter figures of its dominant kernel, the sources that
 # kernel is built from, and the kernel's name as the profiler reports it (a prefix)
-_DECODE_SRC = ["decode.hip", "common.hpp", "kernels.hpp"]
-_PREFILL_SRC = ["prefill.hip", "common.hpp", "kernels.hpp"]
+_DECODE_SRC = ["decode.hip", "decode_item.hpp", "decode_walk.inc", "common.hpp", "kernels.hpp"]
+_PREFILL_SRC = ["prefill.hip", "decode_item.hpp", "decode_walk.inc", "common.hpp",
+                "kernels.hpp"]
 TRAFFIC = {
     "qwen7b_decode": ("decode_partition_qwen7b_decode_traffic.json", _DECODE_SRC,
                       "pa::decode_partition_kernel<"),
@@ -898,7 +930,8 @@ def main():
                                     ("long_decode_auto_splits", "long_decode", -1),
                                     ("long_history_chunk", "long_history_chunk", 0),
                                     ("mixed_ragged", "mixed_ragged", 0),
-                                    ("mixed_ragged_graph", "mixed_ragged", 0)):
+                                    ("mixed_ragged_graph", "mixed_ragged", 0),
+                                    ("mixed_ragged_two_streams", "mixed_ragged_two_streams", 0)):
             # a secondary workload that fails is reported as such; the headline stands
             try:
                 if splits < 0:

@@ -555,6 +555,81 @@ size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_
                                              int32_t Hq, int32_t D,
                                              const pa_prefill_opts* opts);
 
+/*
+ * The mixed step: one step of a serving engine holds prefill chunks and decode rows
+ * side by side ("8. Kernels and Attention Backends", chapter intro: one step of 23
+ * ragged requests), and one kernel can serve both kinds ("Inside Ion: Custom
+ * Attention Kernels for NVIDIA Grace", "IonAttention in One Paragraph").
+ * paged_attn_mixed computes a prefill batch (as paged_attn_prefill_varlen_splitk) and
+ * a decode batch (as paged_attn_decode) over the same bf16 pools in one kernel
+ * launch: its first work-groups each run eight decode items (a (sequence, KV head,
+ * partition) item per wave, as the decode with one-wave work-groups runs it), and
+ * the work-groups after them run the prefill's items (256-row query tiles,
+ * whatever max_q_len) in the prefill grid's order, so the decode's short items
+ * take CUs while the prefill's heaviest tiles start and free them for the rest.
+ * Where the prefill has key parts or the decode has partitions, their merge kernels
+ * follow on the same stream (the prefill merge, then the split-K reduce).  The
+ * prefill rows are bit for bit those of paged_attn_prefill_varlen_splitk with the same
+ * key-part count when that launch takes 256-row tiles too (max_q_len >= 512); the
+ * decode rows those of paged_attn_decode with the same split count when that launch
+ * takes one-wave work-groups (Hkv x splits x B >= 512), and otherwise equal up to
+ * rounding (its waves then split a partition's chunks and merge them).
+ * Options (windows, ALiBi, FP8 pools, document ranges, block maps) are not taken:
+ * use the separate entry points for them.
+ */
+typedef struct {
+  void* out;                    /* bf16 [Tq, Hq, D]                                     */
+  float* lse_out;               /* fp32 [Tq, Hq] or NULL                                */
+  const void* q;                /* bf16 [Tq, Hq, D]                                     */
+  const int32_t* cu_seqlens_q;  /* [B + 1] int32, cu[B] == Tq                           */
+  const int32_t* seq_lens_k;    /* [B] int32                                            */
+  const int32_t* block_tables;  /* [B, max_pages] int32                                 */
+  int32_t B, Tq, max_q_len, max_pages;   /* B == 0: no prefill part                     */
+  int32_t causal;               /* as paged_attn_prefill_varlen's                       */
+  int32_t num_splits;           /* key parts as paged_attn_prefill_varlen_splitk's (<= 0:
+                                   the library's count for 256-row work-groups)         */
+} pa_mixed_prefill;
+
+typedef struct {
+  void* out;                    /* bf16 [B, Hq, D]                                      */
+  float* lse_out;               /* fp32 [B, Hq] or NULL                                 */
+  const void* q;                /* bf16 [B, Hq, D], one query row per sequence          */
+  const int32_t* block_tables;  /* [B, max_pages] int32                                 */
+  const int32_t* seq_lens;      /* [B] int32                                            */
+  int32_t B, max_pages;         /* B == 0: no decode part                               */
+  int32_t max_seq_len;          /* host-side bound of seq_lens, as paged_attn_decode's  */
+  int32_t num_splits;           /* > 0: as paged_attn_decode's; <= 0: paged_attn_decode's
+                                   own count times the waves per work-group its launch
+                                   would give each item (1, 2 or 4), so that each
+                                   one-wave item here walks as many keys as a wave does
+                                   there                                                */
+} pa_mixed_decode;
+
+/*
+ * Workspace bytes of paged_attn_mixed: the prefill's key-part partials (as
+ * paged_attn_prefill_workspace_bytes with 256-row tiles) followed by the decode's
+ * split-K partials (as paged_attn_decode_workspace_bytes), each region 256-byte
+ * aligned, with the split counts paged_attn_mixed resolves; 0 when neither part
+ * needs one or an argument is NULL or not positive.
+ */
+size_t paged_attn_mixed_workspace_bytes(const pa_mixed_prefill* prefill,
+                                        const pa_mixed_decode* decode, int32_t Hq,
+                                        int32_t Hkv, int32_t D);
+
+/*
+ * paged_attn_mixed -- the prefill and decode batches above in one launch (plus their
+ * merges).  Both parts share the pools (num_pages, page_size, Hkv, D), Hq and the
+ * softmax scale.  prefill or decode NULL: PA_ERR_NULL.  Each part is checked as its
+ * own entry point checks it (the same statuses; the message names the part); a part
+ * with B == 0 is skipped, and with both skipped nothing is launched.  The workspace
+ * is scratch (calls that share one must not run concurrently).
+ */
+int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* decode,
+                     const void* k_pool, const void* v_pool, int32_t num_pages,
+                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                     float softmax_scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Human-readable name of a pa_status value (static string). */
 const char* pa_status_string(int status);
 

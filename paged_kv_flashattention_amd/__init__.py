@@ -40,7 +40,8 @@ __all__ = [
     "paged_attn_prefill_varlen", "paged_attn_prefill_varlen_splitk",
     "paged_attn_prefill_varlen_fp8", "prefill_num_splits",
     "prefill_workspace_bytes", "decode_num_splits", "decode_workspace_bytes",
-    "describe_launch", "library_path", "load_library",
+    "describe_launch", "library_path", "load_library", "paged_attn_mixed",
+    "mixed_workspace_bytes",
 ]
 
 PA_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
@@ -781,3 +782,151 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
             _check(lib.paged_attn_prefill_varlen_splitk(*args, num_splits, _ptr(workspace),
                                                         ws_bytes, _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def mixed_workspace_bytes(Hq: int, Hkv: int, D: int, prefill=None, decode=None) -> int:
+    """Workspace bytes of paged_attn_mixed for the host-side sizes of its parts:
+    prefill = (B, Tq, max_q_len, num_splits), decode = (B, max_seq_len, num_splits),
+    either None for no such part."""
+    p = _lib.MixedPrefill()
+    d = _lib.MixedDecode()
+    if prefill is not None:
+        p.B, p.Tq, p.max_q_len, p.num_splits = (int(x) for x in prefill)
+    if decode is not None:
+        d.B, d.max_seq_len, d.num_splits = (int(x) for x in decode)
+    return int(load_library().paged_attn_mixed_workspace_bytes(ctypes.byref(p), ctypes.byref(d),
+                                                               int(Hq), int(Hkv), int(D)))
+
+
+def paged_attn_mixed(k_pool, v_pool, softmax_scale: float, prefill=None, decode=None,
+                     causal: bool = True, prefill_max_q_len: Optional[int] = None,
+                     prefill_num_splits: int = 0, decode_max_seq_len: Optional[int] = None,
+                     decode_num_splits: int = 0, prefill_out: Optional[torch.Tensor] = None,
+                     decode_out: Optional[torch.Tensor] = None,
+                     prefill_lse: Optional[torch.Tensor] = None,
+                     decode_lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                     workspace: Optional[torch.Tensor] = None, stream=None,
+                     validate: bool = False):
+    """A step's prefill chunks and decode rows over the same bf16 pools in one kernel
+    launch (then the merges of their key parts and partitions): see paged_attn_mixed
+    in C.
+
+    ``prefill`` = (q [Tq, Hq, D], cu_seqlens_q [B+1], seq_lens_k [B], block_tables), as
+    paged_attn_prefill_varlen_splitk takes them; ``decode`` = (q [B, Hq, D],
+    block_tables, seq_lens), as paged_attn_decode takes them; either may be None.
+    ``prefill_num_splits`` <= 0 takes the library's key-part count for 256-row tiles;
+    ``decode_num_splits`` <= 0 the decode's split rule.  Host-side bounds read from
+    the device when omitted (a synchronisation).  Returns (prefill_out, decode_out),
+    with (prefill_lse, decode_lse) after them when ``return_lse``; a missing part's
+    entries are None.  Outputs and lse buffers may be passed in (``*_out``,
+    ``*_lse``), as for graph capture."""
+    _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16),
+            (prefill_out, "prefill_out", torch.bfloat16),
+            (decode_out, "decode_out", torch.bfloat16),
+            (prefill_lse, "prefill_lse", torch.float32), (decode_lse, "decode_lse", torch.float32))
+    if prefill is None and decode is None:
+        raise ValueError("paged_attn_mixed needs a prefill part, a decode part or both")
+    dev = (prefill or decode)[0].device
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    P, ps, Hkv, D = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    Hq = None
+    mp = _lib.MixedPrefill()
+    md = _lib.MixedDecode()
+    pf_out = pf_lse = dec_out = dec_lse = None
+    if prefill is not None:
+        q, cu, lens, bt = prefill
+        _dtypes((q, "prefill q", torch.bfloat16), (cu, "cu_seqlens_q", torch.int32),
+                (lens, "seq_lens_k", torch.int32), (bt, "prefill block_tables", torch.int32))
+        _need(q, "prefill q", torch.bfloat16, 3, dev)
+        _need(cu, "cu_seqlens_q", torch.int32, 1, dev)
+        _need(lens, "seq_lens_k", torch.int32, 1, dev)
+        _need(bt, "prefill block_tables", torch.int32, 2, dev)
+        Tq, Hq, Dq = q.shape
+        B = lens.shape[0]
+        if Dq != D:
+            raise ValueError("prefill q does not match the pools' head dim")
+        if cu.shape[0] != B + 1 or bt.shape[0] != B:
+            raise ValueError("cu_seqlens_q must be [B+1] and block_tables [B, max_pages]")
+        if prefill_max_q_len is None:
+            prefill_max_q_len = int((cu[1:] - cu[:-1]).max().item()) if B else 0
+        if validate:
+            cu_h = cu.cpu()
+            if int(cu_h[0]) != 0 or int(cu_h[-1]) != Tq or bool((cu_h[1:] < cu_h[:-1]).any()):
+                raise ValueError("cu_seqlens_q must be non-decreasing from 0 to Tq")
+            if B and int((cu_h[1:] - cu_h[:-1]).max()) > prefill_max_q_len:
+                raise ValueError("prefill_max_q_len is below a sequence's query count")
+            _validate_tables(bt, lens, P, ps)
+        pf_out = prefill_out
+        if pf_out is None:
+            pf_out = _internal(torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=dev), stream)
+        else:
+            _need(pf_out, "prefill_out", torch.bfloat16, 3, dev)
+            if tuple(pf_out.shape) != (Tq, Hq, D):
+                raise ValueError("prefill_out must be [Tq, Hq, D]")
+        pf_lse = prefill_lse
+        if pf_lse is not None:
+            _need(pf_lse, "prefill_lse", torch.float32, 2, dev)
+            if tuple(pf_lse.shape) != (Tq, Hq):
+                raise ValueError("prefill_lse must be [Tq, Hq]")
+        elif return_lse:
+            pf_lse = _internal(torch.empty((Tq, Hq), dtype=torch.float32, device=dev), stream)
+        mp.out, mp.lse_out, mp.q = _ptr(pf_out), _ptr(pf_lse), _ptr(q)
+        mp.cu_seqlens_q, mp.seq_lens_k, mp.block_tables = _ptr(cu), _ptr(lens), _ptr(bt)
+        mp.B, mp.Tq, mp.max_q_len, mp.max_pages = B, Tq, int(prefill_max_q_len), bt.shape[1]
+        mp.causal, mp.num_splits = 1 if causal else 0, int(prefill_num_splits)
+    if decode is not None:
+        q, bt, lens = decode
+        _dtypes((q, "decode q", torch.bfloat16), (bt, "decode block_tables", torch.int32),
+                (lens, "seq_lens", torch.int32))
+        _need(q, "decode q", torch.bfloat16, 3, dev)
+        _need(bt, "decode block_tables", torch.int32, 2, dev)
+        _need(lens, "seq_lens", torch.int32, 1, dev)
+        B, Hq_d, Dq = q.shape
+        if Hq is not None and Hq_d != Hq:
+            raise ValueError("the prefill and decode parts must have the same Hq")
+        Hq = Hq_d
+        if Dq != D:
+            raise ValueError("decode q does not match the pools' head dim")
+        if lens.shape[0] != B or bt.shape[0] != B:
+            raise ValueError("seq_lens must be [B] and block_tables [B, max_pages]")
+        if decode_max_seq_len is None:
+            decode_max_seq_len = int(lens.max().item()) if B else 0
+        if validate:
+            _validate_tables(bt, lens, P, ps)
+            if B and int(lens.max().item()) > decode_max_seq_len:
+                raise ValueError("decode_max_seq_len is below a sequence length")
+        dec_out = decode_out
+        if dec_out is None:
+            dec_out = _internal(torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev), stream)
+        else:
+            _need(dec_out, "decode_out", torch.bfloat16, 3, dev)
+            if tuple(dec_out.shape) != (B, Hq, D):
+                raise ValueError("decode_out must be [B, Hq, D]")
+        dec_lse = decode_lse
+        if dec_lse is not None:
+            _need(dec_lse, "decode_lse", torch.float32, 2, dev)
+            if tuple(dec_lse.shape) != (B, Hq):
+                raise ValueError("decode_lse must be [B, Hq]")
+        elif return_lse:
+            dec_lse = _internal(torch.empty((B, Hq), dtype=torch.float32, device=dev), stream)
+        md.out, md.lse_out, md.q = _ptr(dec_out), _ptr(dec_lse), _ptr(q)
+        md.block_tables, md.seq_lens = _ptr(bt), _ptr(lens)
+        md.B, md.max_pages, md.max_seq_len = B, bt.shape[1], int(decode_max_seq_len)
+        md.num_splits = int(decode_num_splits)
+    lib = load_library()
+    need = int(lib.paged_attn_mixed_workspace_bytes(ctypes.byref(mp), ctypes.byref(md), Hq, Hkv, D))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    elif need:
+        workspace = _internal(torch.empty(need, dtype=torch.uint8, device=dev), stream)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    with torch.cuda.device(dev):
+        _check(lib.paged_attn_mixed(ctypes.byref(mp), ctypes.byref(md), _ptr(k_pool),
+                                    _ptr(v_pool), P, ps, Hq, Hkv, D, float(softmax_scale),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+    if return_lse:
+        return pf_out, dec_out, pf_lse, dec_lse
+    return pf_out, dec_out

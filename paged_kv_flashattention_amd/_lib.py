@@ -42,8 +42,27 @@ class PrefillOpts(ctypes.Structure):
                 ("block_map_k_blocks", ctypes.c_int32)]
 
 
+class MixedPrefill(ctypes.Structure):
+    """pa_mixed_prefill"""
+    _fields_ = [("out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("cu_seqlens_q", ctypes.c_void_p), ("seq_lens_k", ctypes.c_void_p),
+                ("block_tables", ctypes.c_void_p), ("B", ctypes.c_int32), ("Tq", ctypes.c_int32),
+                ("max_q_len", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("num_splits", ctypes.c_int32)]
+
+
+class MixedDecode(ctypes.Structure):
+    """pa_mixed_decode"""
+    _fields_ = [("out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("block_tables", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("num_splits", ctypes.c_int32)]
+
+
 c_dopts = ctypes.POINTER(DecodeOpts)
 c_popts = ctypes.POINTER(PrefillOpts)
+c_mpf = ctypes.POINTER(MixedPrefill)
+c_mdec = ctypes.POINTER(MixedDecode)
 
 # name -> (restype, argtypes); mirrors include/paged_attn.h
 SIGNATURES = {
@@ -91,6 +110,9 @@ SIGNATURES = {
                                       c_i32, c_float, c_popts, c_vp, c_size, c_vp]),
     "paged_attn_prefill_ex_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32,
                                                        c_popts]),
+    "paged_attn_mixed_workspace_bytes": (c_size, [c_mpf, c_mdec, c_i32, c_i32, c_i32]),
+    "paged_attn_mixed": (c_i32, [c_mpf, c_mdec, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                 c_float, c_vp, c_size, c_vp]),
     "pa_status_string": (ctypes.c_char_p, [c_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_describe_launch": (ctypes.c_char_p, []),

@@ -293,10 +293,12 @@ constexpr int kPrefillPartMinTiles = 16;       // 64-key tiles per key-range par
 // (The slot count takes the work-group size from max_q_len alone, as the workspace
 // query does, so both give the same S; FP8 pools with ALiBi launch 8-wave work-groups
 // whatever the length, for which the count is then only an estimate.)
-int32_t resolve_prefill_splits(int32_t B, int32_t Hq, int32_t max_q_len, int32_t num_splits) {
+// (waves > 0: work-groups of that many waves, as the mixed step's 8.)
+int32_t resolve_prefill_splits(int32_t B, int32_t Hq, int32_t max_q_len, int32_t num_splits,
+                               int waves = 0) {
   if (num_splits > 0) return num_splits < kPrefillMaxSplits ? num_splits : kPrefillMaxSplits;
   if (B <= 0 || Hq <= 0 || max_q_len <= 0) return 1;
-  const int W = pa::prefill_waves(max_q_len);
+  const int W = waves > 0 ? waves : pa::prefill_waves(max_q_len);
   const long long n_qt = (max_q_len + 32 * W - 1) / (32 * W);
   const long long wgs = (long long)Hq * B * n_qt;
   const long long slots = 256ll * (8 / W);
@@ -313,28 +315,32 @@ size_t prefill_workspace_for(int32_t Tq, int32_t Hq, int32_t D, int32_t S) {
   return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
 }
 
-// Checks and launches shared by the prefill entry points; S == 1 is the plain
-// one-pass prefill.
-int prefill_impl(const char* what, void* out, float* lse_out, const void* q, const void* k_pool,
-                 const void* v_pool, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+// Checks and argument packing shared by the prefill entry points and the mixed step
+// (waves > 0: work-groups of that many waves, for the key-part count); the key parts
+// S are resolved (1: the plain one-pass prefill) and their workspace checked.  With no
+// query row to compute, *nothing is set and a is left empty.
+int prefill_args(pa::PrefillArgs& a, bool* nothing, const char* what, void* out,
+                 float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
                  const int32_t* block_tables, int32_t B, int32_t Tq, int32_t max_q_len,
                  int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
-                 void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
+                 void* workspace, size_t workspace_bytes, int32_t window = 0,
                  const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
-                 float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
-                 const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr,
-                 const float* k_scales = nullptr, const float* v_scales = nullptr,
-                 int32_t persistent = 0, const uint8_t* block_map = nullptr,
-                 int32_t bm_qb = 0, int32_t bm_kb = 0) {
-  g_last_error[0] = 0;
+                 float v_scale = 1.f, const int32_t* key_lo = nullptr,
+                 const int32_t* key_hi = nullptr, const float* k_scales = nullptr,
+                 const float* v_scales = nullptr, int32_t persistent = 0,
+                 const uint8_t* block_map = nullptr, int32_t bm_qb = 0, int32_t bm_kb = 0,
+                 int waves = 0) {
+  a = pa::PrefillArgs{};
+  *nothing = false;
   if (B < 0 || Tq < 0 || max_q_len < 0 || window < 0)
     return fail(PA_ERR_SHAPE, "%s: B=%d Tq=%d max_q_len=%d window=%d", what, B, Tq, max_q_len,
                 window);
   int st = check_pool(B, max_pages, num_pages, page_size, Hq, Hkv, D);
   if (st) return st;
   if (B == 0 || Tq == 0 || max_q_len == 0) {
-    snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
+    *nothing = true;
     return PA_OK;
   }
   if (!out || !q || !k_pool || !v_pool || !cu_seqlens_q || !seq_lens_k || !block_tables)
@@ -371,7 +377,7 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     num_splits = 1;
   }
   if (max_q_len > Tq) max_q_len = Tq;
-  const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits);
+  const int32_t S = resolve_prefill_splits(B, Hq, max_q_len, num_splits, waves);
   // one work-group per (query head, sequence, 128- or 256-row query tile, key
   // part); the launch holds at most 2^32 - 1 work-items
   if ((long long)Hq * B * ((max_q_len + 127) / 128 + 1) * 256 * S > 0xffffffffll)
@@ -383,7 +389,6 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
                 what, need, S, workspace ? workspace_bytes : (size_t)0);
   if (need && !aligned16(workspace))
     return fail(PA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", what);
-  pa::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_pool = static_cast<const uint16_t*>(k_pool);
   a.v_pool = static_cast<const uint16_t*>(v_pool);
@@ -418,6 +423,38 @@ int prefill_impl(const char* what, void* out, float* lse_out, const void* q, con
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_lse = reinterpret_cast<float*>(ws + align256((size_t)Tq * Hq * S * D * sizeof(float)));
   }
+  return PA_OK;
+}
+
+// Checks and launches shared by the prefill entry points; S == 1 is the plain
+// one-pass prefill.
+int prefill_impl(const char* what, void* out, float* lse_out, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                 const int32_t* block_tables, int32_t B, int32_t Tq, int32_t max_q_len,
+                 int32_t max_pages, int32_t num_pages, int32_t page_size, int32_t Hq,
+                 int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, int32_t num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
+                 const float* alibi = nullptr, bool fp8 = false, float k_scale = 1.f,
+                 float v_scale = 1.f, const pa::KernelEvents& ev = pa::KernelEvents(),
+                 const int32_t* key_lo = nullptr, const int32_t* key_hi = nullptr,
+                 const float* k_scales = nullptr, const float* v_scales = nullptr,
+                 int32_t persistent = 0, const uint8_t* block_map = nullptr,
+                 int32_t bm_qb = 0, int32_t bm_kb = 0) {
+  g_last_error[0] = 0;
+  pa::PrefillArgs a;
+  bool nothing = false;
+  const int st = prefill_args(a, &nothing, what, out, lse_out, q, k_pool, v_pool, cu_seqlens_q,
+                              seq_lens_k, block_tables, B, Tq, max_q_len, max_pages, num_pages,
+                              page_size, Hq, Hkv, D, softmax_scale, causal, num_splits,
+                              workspace, workspace_bytes, window, alibi, fp8, k_scale, v_scale,
+                              key_lo, key_hi, k_scales, v_scales, persistent, block_map, bm_qb,
+                              bm_kb);
+  if (st) return st;
+  if (nothing) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "%s: nothing to do", what);
+    return PA_OK;
+  }
+  const int32_t S = a.S;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char d1[320], d2[256];
   hipError_t e = pa::launch_prefill(a, hs, d1, sizeof(d1), ev);
@@ -848,6 +885,119 @@ int paged_attn_prefill_ex(void* out, float* lse_out, const void* q, const void* 
                       opts->key_lo, opts->key_hi, opts->k_scales, opts->v_scales,
                       opts->persistent, opts->block_map, opts->block_map_q_blocks,
                       opts->block_map_k_blocks);
+}
+
+// The mixed step's parts: the prefill's key-part count for 256-row work-groups, and
+// the workspace regions of both parts.
+static int32_t mixed_prefill_splits(const pa_mixed_prefill& p, int32_t Hq) {
+  const int32_t mq = p.max_q_len < p.Tq ? p.max_q_len : p.Tq;
+  return resolve_prefill_splits(p.B, Hq, mq, p.num_splits, 8);
+}
+
+// The decode part's split count: the caller's, or (num_splits <= 0) the decode's own
+// count times the waves per work-group its own launch would give each item -- every
+// item of the mixed launch is walked by one wave, so each wave keeps the run of keys
+// it would stream in paged_attn_decode (measured on MI355X, the mixed ragged step:
+// 116.5-120.7 us with 4 splits, 152.5-154.5 us with the decode's own 2, whose
+// one-wave items of 1,760 keys then outlast the prefill).
+static int32_t mixed_decode_splits(const pa_mixed_decode& d, int32_t Hkv) {
+  if (d.num_splits > 0) return d.num_splits;
+  const int32_t s0 = resolve_splits(d.B, Hkv, d.max_seq_len, 0);
+  const int w = pa::decode_waves((long long)Hkv * s0 * (d.B > 0 ? d.B : 1), false);
+  return resolve_splits(d.B, Hkv, d.max_seq_len, s0 * w);
+}
+
+static size_t mixed_prefill_bytes(const pa_mixed_prefill& p, int32_t Hq, int32_t D) {
+  if (p.B <= 0 || p.Tq <= 0 || p.max_q_len <= 0) return 0;
+  return prefill_workspace_for(p.Tq, Hq, D, mixed_prefill_splits(p, Hq));
+}
+
+size_t paged_attn_mixed_workspace_bytes(const pa_mixed_prefill* prefill,
+                                        const pa_mixed_decode* decode, int32_t Hq,
+                                        int32_t Hkv, int32_t D) {
+  if (!prefill || !decode || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  const size_t pf = mixed_prefill_bytes(*prefill, Hq, D);
+  const size_t dec = decode->B > 0 && decode->max_seq_len >= 0
+                         ? workspace_for(decode->B, Hq, D, mixed_decode_splits(*decode, Hkv))
+                         : 0;
+  return pf + dec;
+}
+
+int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* decode,
+                     const void* k_pool, const void* v_pool, int32_t num_pages,
+                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                     float softmax_scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_last_error[0] = 0;
+  if (!prefill || !decode) return fail(PA_ERR_NULL, "mixed: prefill or decode is NULL");
+  const pa_mixed_prefill& p = *prefill;
+  const pa_mixed_decode& dc = *decode;
+  // the prefill's partials come first in the workspace, the decode's after them; a
+  // part with B == 0 is not checked
+  const size_t pf_need = Hq > 0 && D > 0 ? mixed_prefill_bytes(p, Hq, D) : 0;
+  pa::PrefillArgs a{};
+  if (p.B != 0) {
+    bool no_prefill = false;
+    const int st = prefill_args(a, &no_prefill, "mixed (prefill part)", p.out, p.lse_out, p.q,
+                                k_pool, v_pool, p.cu_seqlens_q, p.seq_lens_k, p.block_tables,
+                                p.B, p.Tq, p.max_q_len, p.max_pages, num_pages, page_size, Hq,
+                                Hkv, D, softmax_scale, p.causal, p.num_splits, workspace,
+                                workspace_bytes < pf_need ? workspace_bytes : pf_need, 0,
+                                nullptr, false, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, 0,
+                                nullptr, 0, 0, 8);
+    if (st) return st;
+    if (no_prefill) a = pa::PrefillArgs{};
+  }
+  pa::DecodeArgs d{};
+  if (dc.B != 0) {
+    const int st = decode_args(d, "mixed (decode part)", dc.q, k_pool, v_pool, dc.block_tables,
+                               dc.seq_lens, dc.B, dc.max_pages, num_pages, page_size, Hq, Hkv,
+                               D, softmax_scale, dc.max_seq_len,
+                               dc.max_seq_len >= 0 ? mixed_decode_splits(dc, Hkv) : 0);
+    if (st) return st;
+    if (!dc.out) return fail(PA_ERR_NULL, "mixed (decode part): out is NULL");
+    if (!aligned16(dc.out))
+      return fail(PA_ERR_MISALIGNED, "mixed (decode part): out must be 16-byte aligned");
+    const size_t need = workspace_for(dc.B, Hq, D, d.S);
+    char* ws = workspace ? static_cast<char*>(workspace) + pf_need : nullptr;
+    const size_t have = workspace_bytes > pf_need ? workspace_bytes - pf_need : 0;
+    if (need && (!workspace || have < need))
+      return fail(PA_ERR_WORKSPACE, "mixed: workspace of %zu bytes needed (%zu prefill, %zu "
+                  "decode for %d splits), got %zu", pf_need + need, pf_need, need, d.S,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (need && !aligned16(workspace))
+      return fail(PA_ERR_MISALIGNED, "mixed: workspace must be 16-byte aligned");
+    d.out = static_cast<uint16_t*>(dc.out);
+    d.lse_out = dc.lse_out;
+    if (d.S > 1) {
+      d.part_o = reinterpret_cast<float*>(ws);
+      d.part_lse = reinterpret_cast<float*>(
+          ws + align256((size_t)dc.B * Hq * d.S * D * sizeof(float)));
+    }
+  }
+  if (a.B == 0 && d.B == 0) {
+    snprintf(g_last_launch, sizeof(g_last_launch), "mixed: nothing to do");
+    return PA_OK;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char d1[400], d2[256] = "", d3[256] = "";
+  hipError_t e = pa::launch_mixed(a, d, hs, d1, sizeof(d1));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "mixed launch: %s", hipGetErrorString(e));
+  if (a.B > 0 && a.S > 1) {
+    e = pa::launch_prefill_merge(a, hs, d2, sizeof(d2), 8);
+    if (e != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "mixed prefill merge launch: %s", hipGetErrorString(e));
+  }
+  if (d.B > 0 && d.S > 1) {
+    pa::ReduceArgs r{};
+    r.out = d.out; r.lse_out = d.lse_out; r.part_o = d.part_o; r.part_lse = d.part_lse;
+    r.R = d.B * Hq; r.S = d.S; r.D = D;
+    e = pa::launch_reduce(r, hs, d3, sizeof(d3));
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "mixed reduce launch: %s", hipGetErrorString(e));
+  }
+  snprintf(g_last_launch, sizeof(g_last_launch), "%s%s%s%s%s", d1, d2[0] ? "; " : "", d2,
+           d3[0] ? "; " : "", d3);
+  return PA_OK;
 }
 
 size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_len,

@@ -141,11 +141,21 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream, char* desc,
                            size_t desc_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, char* desc,
                           size_t desc_len, const KernelEvents& ev = KernelEvents());
-// with S > 1: merges the rows whose query tile was split (after launch_prefill)
+// with S > 1: merges the rows whose query tile was split (after launch_prefill; waves
+// > 0: after a launch of work-groups of that many waves, as launch_mixed's 8)
 hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream, char* desc,
-                                size_t desc_len);
+                                size_t desc_len, int waves = 0);
+// One kernel for a prefill batch (plain bf16 variant, 256-row query tiles; p.B = 0:
+// none) and a decode batch (bf16, d.B = 0: none) over the same pools; the merges of
+// their key parts and partitions are the caller's (launch_prefill_merge with 8 waves,
+// launch_reduce).  `ev` is stamped around the kernel.
+hipError_t launch_mixed(const PrefillArgs& p, const DecodeArgs& d, hipStream_t stream,
+                        char* desc, size_t desc_len, const KernelEvents& ev = KernelEvents());
 // waves per prefill work-group (32 query rows each) for the longest query run (and
 // whether the pools are FP8 with ALiBi slopes)
 int prefill_waves(int max_q_len, bool fp8_alibi = false);
+// waves per decode work-group for a grid of `groups` (KV head, partition, sequence)
+// items
+int decode_waves(long long groups, bool fp8);
 
 }  // namespace pa

@@ -25,6 +25,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "decode_item.hpp"
 #include "kernels.hpp"
 
 namespace pa {
@@ -1056,6 +1057,38 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_persist_kernel(PrefillArgs 
   }
 }
 
+// One launch for a step's prefill query runs and decode rows over the same pools (a
+// kernel that serves both kinds of request of a step: "Inside Ion: Custom Attention
+// Kernels for NVIDIA Grace", "IonAttention in One Paragraph").  Work-groups 0 ..
+// n_dg - 1 each run eight decode items, one per wave, as the one-wave decode
+// partition kernel runs them (item 8 x work-group + wave; KV head fastest, then
+// partition, then sequence), staging their K rows in the start of the dynamic LDS; the
+// work-groups after them run the plain prefill grid's items (256-row query tiles,
+// plain bf16 variant) in its order.  The decode items come first so that they run
+// while the prefill's heaviest tiles start, and the CUs they free take prefill
+// items; n_dg is a multiple of 8, so prefill item p runs on XCD p mod 8 as in the
+// plain grid.
+template <int D>
+__global__ __launch_bounds__(512, 1) void mixed_kernel(PrefillArgs a, DecodeArgs d, int n_dg) {
+  extern __shared__ __align__(16) uint16_t pf_lds[];
+  static_assert(8 * 32 * KRows<D>::LROW <= PfLds<D>::TILE * 5, "decode staging fits the LDS");
+  if ((int)blockIdx.x < n_dg) {
+    const int i = 8 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per_b = d.Hkv * d.S;
+    if (i >= per_b * d.B) return;
+    const int b = i / per_b;
+    const int r = i - b * per_b;
+    const int split = r / d.Hkv;
+    decode_item<D, 1, false, false, false, true>(d, r - split * d.Hkv, split, b);
+    return;
+  }
+  const PfWork w = pf_work_of(a, blockIdx.x - n_dg);
+  const PfSetup s = pf_setup<false>(a, w, 256, threadIdx.x & 63);
+  if (!s.ok) return;
+  PfHand hd{};
+  pf_item<D, 8, false, false, false, false, false>(a, w, s, hd, pf_lds);
+}
+
 // Merge of the query tiles that were cut into key-range parts ("The Stack Below
 // the Stack (Part 2)", section 2.2, step 3: with m the largest part lse, weights
 // exp(lse_c - m), lse = m + ln sum).  A work-group covers kMergePasses * 256 / (D / 4)
@@ -1264,8 +1297,8 @@ static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
 }
 
 hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, char* desc,
-                                size_t desc_len) {
-  const int W = prefill_waves(a_in);
+                                size_t desc_len, int waves) {
+  const int W = waves > 0 ? waves : prefill_waves(a_in);
   const PrefillArgs a = prefill_shape(a_in, W);
   const int rows_per_wg = kMergeThreads / (a.D / 4) * kMergePasses;
   dim3 grid(a.Hq * a.B * a.n_qt * (32 * W / rows_per_wg));
@@ -1278,6 +1311,47 @@ hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, cha
   snprintf(desc, desc_len, "prefill_merge<D=%d> grid=%u (query tiles x heads x %d-row blocks) "
            "parts<=%d", a.D, grid.x, rows_per_wg, a.S);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_mixed_d(const PrefillArgs& a, const DecodeArgs& d, int n_dg, int n_pf,
+                                 hipStream_t stream, const KernelEvents& ev) {
+  constexpr size_t lds = PfLds<D>::BYTES;
+  static std::atomic<int> state[kMaxDevices];
+  const hipError_t e =
+      lds_attribute_once(state, reinterpret_cast<const void*>(mixed_kernel<D>), lds);
+  if (e != hipSuccess) return e;
+  launch_kernel(mixed_kernel<D>, dim3(n_dg + n_pf), dim3(512), (uint32_t)lds, stream, ev, a, d,
+                n_dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_mixed(const PrefillArgs& p_in, const DecodeArgs& d, hipStream_t stream,
+                        char* desc, size_t desc_len, const KernelEvents& ev) {
+  const int D = p_in.B > 0 ? p_in.D : d.D;
+  PrefillArgs a = p_in;
+  int n_pf = 0;
+  if (a.B > 0) {
+    a = prefill_shape(p_in, 8);
+    n_pf = prefill_items(a);
+  }
+  const long long n_dec = d.B > 0 ? (long long)d.Hkv * d.S * d.B : 0;
+  const int n_dg = (int)(((n_dec + 7) / 8 + 7) / 8 * 8);
+  if (n_dg + (long long)n_pf > 0x7fffffffll) return hipErrorInvalidValue;
+  if (n_dg + n_pf == 0) {
+    snprintf(desc, desc_len, "mixed: nothing to do");
+    return hipSuccess;
+  }
+  const hipError_t e = D == 128 ? launch_mixed_d<128>(a, d, n_dg, n_pf, stream, ev)
+                                : launch_mixed_d<64>(a, d, n_dg, n_pf, stream, ev);
+  snprintf(desc, desc_len,
+           "mixed<D=%d> grid=%d: %d decode work-groups (%lld one-wave items: %d KV heads x %d "
+           "splits x %d rows) then %d prefill items (256-row tiles, %d key parts, %s) "
+           "block=512 lds=%zu",
+           D, n_dg + n_pf, n_dg, n_dec, d.Hkv, d.S, d.B, n_pf, a.S,
+           a.xcd_groups ? "KV groups per XCD" : "head-major",
+           D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
+  return e;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,

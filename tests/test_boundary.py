@@ -469,3 +469,71 @@ def test_prefill_plan_splits_host_logic():
         pa.prefill_plan_splits([1], [1], 0)
     with pytest.raises(ValueError):
         pa.prefill_plan_splits([1], [1], 8, window_left=-1)
+
+
+def test_mixed_step_arguments_are_checked(lib):
+    """paged_attn_mixed: NULL parts, each part checked as its own entry point checks it
+    (the message names the part), empty parts skipped, and the workspace sized as the
+    prefill's key parts (256-row tiles) plus the decode's partials; nothing here
+    reaches a launch."""
+    from paged_kv_flashattention_amd import _lib
+    m = lib.paged_attn_mixed
+    w = lib.paged_attn_mixed_workspace_bytes
+    P, ps, Hq, Hkv, D = 64, 16, 8, 2, 128
+
+    def pf(**kw):
+        p = _lib.MixedPrefill(FAKE, None, FAKE, FAKE, FAKE, FAKE, 2, 1200, 600, 8, 1, 3)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+
+    def dec(**kw):
+        d = _lib.MixedDecode(FAKE, None, FAKE, FAKE, FAKE, 3, 8, 120, 2)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+    args = (FAKE, FAKE, P, ps, Hq, Hkv, D, 0.1)
+    assert m(None, ctypes.byref(dec()), *args, None, 0, None) == 1
+    assert m(ctypes.byref(pf()), None, *args, None, 0, None) == 1
+    # both parts empty: nothing to do, nothing checked
+    assert m(ctypes.byref(pf(B=0, cu_seqlens_q=None)), ctypes.byref(dec(B=0, q=None)), *args,
+             None, 0, None) == 0
+    assert b"nothing to do" in lib.pa_describe_launch()
+    # a missing pointer or a bad size in one part is that part's error
+    assert m(ctypes.byref(pf(cu_seqlens_q=None)), ctypes.byref(dec(B=0)), *args, None, 0,
+             None) == 1
+    assert b"prefill part" in lib.pa_last_error()
+    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(out=None)), *args, None, 0, None) == 1
+    assert b"decode part" in lib.pa_last_error()
+    assert m(ctypes.byref(pf(B=-1)), ctypes.byref(dec()), *args, None, 0, None) == 2
+    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(max_seq_len=-5)), *args, None, 0,
+             None) == 2
+    assert m(ctypes.byref(pf()), ctypes.byref(dec()), FAKE, FAKE, P, ps, Hq, Hkv, 96, 0.1,
+             None, 0, None) == 3
+    # workspace: the prefill's parts for 256-row tiles, then the decode's partials
+    need_pf = lib.paged_attn_prefill_workspace_bytes(2, 1200, 600, Hq, D, 3)
+    need_dec = lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 120, 2)
+    assert need_pf > 0 and need_dec > 0
+    assert w(ctypes.byref(pf()), ctypes.byref(dec()), Hq, Hkv, D) == need_pf + need_dec
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec()), Hq, Hkv, D) == need_dec
+    assert w(ctypes.byref(pf()), ctypes.byref(dec(B=0)), Hq, Hkv, D) == need_pf
+    assert w(ctypes.byref(pf(num_splits=1)), ctypes.byref(dec(num_splits=1)), Hq, Hkv, D) == 0
+    # the decode part's own count (num_splits <= 0): the decode's count (1 for 3 rows of
+    # 120 keys) times the waves its launch would give each item (4 for 6 items), at most
+    # one 32-key chunk per split
+    assert lib.paged_attn_decode_num_splits(3, Hkv, 120) == 1
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0)), Hq, Hkv, D) == \
+        lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 120, 4)
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0, max_seq_len=70)), Hq, Hkv,
+             D) == lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 70, 3)
+    assert w(None, ctypes.byref(dec()), Hq, Hkv, D) == 0
+    # short prefill runs still take 256-row tiles, and the library's part count is
+    # resolved for them: 4 x 32 x 2 tiles fill the 256 slots (one part), where the
+    # prefill alone would take 128-row tiles, 384 of 512 slots, and two parts
+    short = pf(B=4, max_q_len=300, num_splits=0)
+    assert w(ctypes.byref(short), ctypes.byref(dec(B=0)), 32, Hkv, D) == 0
+    assert lib.paged_attn_prefill_workspace_bytes(4, 1200, 300, 32, D, 0) > 0
+    for ws_bytes in (0, need_pf, need_pf + need_dec - 1):
+        assert m(ctypes.byref(pf()), ctypes.byref(dec()), *args,
+                 FAKE if ws_bytes else None, ws_bytes, None) == 5
+        assert b"workspace" in lib.pa_last_error()

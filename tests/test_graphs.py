@@ -268,3 +268,71 @@ def test_kernel_events_time_the_main_kernel(require_gpu):
                              dc.scale, max_seq_len=8192,
                              kernel_events=(torch.cuda.Event(enable_timing=True),
                                             torch.cuda.Event(enable_timing=True)))
+
+
+def test_mixed_step_in_one_launch_graph_replays_match_eager(require_gpu):
+    """The page write and the one-launch mixed step (paged_attn_mixed: key-split prefill
+    chunks and decode rows in one kernel, then both merges) captured in a graph:
+    every replay, with eager mixed calls of other shapes on the same workspace in
+    between, gives the eager results bit for bit, and those match the oracle."""
+    print("[graph] one-launch mixed step", flush=True)
+    case = make_case("gmx", hist_lens=[2000, 0, 300, 4000, 17], q_lens=[512, 700, 1, 1, 1],
+                     write_new=True, causal=True, Hq=8, Hkv=2, D=128, page_size=16, seed=80,
+                     device="cuda")
+    kp, vp = pools_after_write(case)
+    t_pf = int(case.cu_seqlens_q[2])
+    pf = (case.q[:t_pf].contiguous(), case.cu_seqlens_q[:3].contiguous(),
+          case.seq_lens_k[:2].contiguous(), case.block_tables[:2].contiguous())
+    dc = (case.q[t_pf:].contiguous(), case.block_tables[2:].contiguous(),
+          case.seq_lens_k[2:].contiguous())
+    need = pa.mixed_workspace_bytes(8, 2, 128, (2, t_pf, 700, 3), (3, 4001, 0))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    bufs = {"pf_o": torch.empty((t_pf, 8, 128), dtype=torch.bfloat16, device="cuda"),
+            "pf_l": torch.empty((t_pf, 8), dtype=torch.float32, device="cuda"),
+            "dc_o": torch.empty((3, 8, 128), dtype=torch.bfloat16, device="cuda"),
+            "dc_l": torch.empty((3, 8), dtype=torch.float32, device="cuda")}
+
+    def run():
+        pa.kv_page_write(case.k_pool, case.v_pool, case.k_new, case.v_new, case.cu_new,
+                         case.start_pos, case.block_tables)
+        pa.paged_attn_mixed(case.k_pool, case.v_pool, case.scale, prefill=pf, decode=dc,
+                            prefill_max_q_len=700, prefill_num_splits=3,
+                            decode_max_seq_len=4001, decode_num_splits=0,
+                            prefill_out=bufs["pf_o"], decode_out=bufs["dc_o"],
+                            prefill_lse=bufs["pf_l"], decode_lse=bufs["dc_l"], workspace=ws)
+
+    def snapshot():
+        return {k: (bits(t).copy() if t.dtype == torch.bfloat16 else t.cpu().numpy().copy())
+                for k, t in bufs.items()}
+
+    run()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    o_ref, l_ref = oracle_full(case, kp, vp)
+    assert_parity(as_f64(bufs["pf_o"]), o_ref[:t_pf], "graph mixed prefill")
+    assert_parity(as_f64(bufs["dc_o"]), o_ref[t_pf:], "graph mixed decode")
+    assert_lse(as_f64(bufs["dc_l"]), l_ref[t_pf:], "graph mixed decode lse")
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in bufs.values():
+            t.fill_(-7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+        # other shapes on the same workspace: the first prefill chunk alone with 2 parts,
+        # two decode rows with 7 splits
+        pa.paged_attn_mixed(case.k_pool, case.v_pool, case.scale,
+                            prefill=(pf[0][:512], pf[1][:2], pf[2][:1], pf[3][:1]),
+                            decode=(dc[0][:2], dc[1][:2], dc[2][:2]), prefill_num_splits=2,
+                            decode_num_splits=7, workspace=ws)
+        torch.cuda.synchronize()
