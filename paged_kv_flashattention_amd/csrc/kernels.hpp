@@ -89,6 +89,8 @@ struct PrefillArgs {
   const float* k_scales;         // FP8 pools: [num_pages, Hkv] scales per (page, KV head),
   const float* v_scales;         //   or null: one scale per pool
   int persist;                   // persistent work-groups (plain bf16 variant, 8 waves)
+  int hp;                        // paired heads: a work-group of 8 waves takes two query
+                                 //   heads of one KV group x 128 rows (set by the launcher)
   const uint8_t* block_map;      // [B, bm_qb, bm_kb] visible 64 x 64 blocks, or null
   int bm_qb, bm_kb;
 };

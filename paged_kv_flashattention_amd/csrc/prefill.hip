@@ -218,16 +218,20 @@ __device__ __forceinline__ PfWork pf_work_of(const PrefillArgs& a, int p) {
   // next unit's heavy tiles start while the previous one's light ones finish.
   // Without it the order is head-major, heaviest tiles first.  Either way all key
   // parts of a tile start together and every XCD keeps its share of the unsplit work.
+  // With paired heads (a.hp) an item takes query heads h and h + 1 (h even within its
+  // KV group), so the head dimension of the grid has half the entries.
   PfWork w;
   {
+    const int hs = a.hp ? 2 : 1;
     if (a.xcd_groups) {
       const int m = a.xcd_split;
+      const int gh = a.G / hs;                   // head slots of a group
       const int tpu = (a.n_qt + m - 1) / m;      // tile ranks per unit
       const int k = p >> 3;                      // this work-group's place on its XCD
-      const int per_unit = a.G * tpu * a.S;      // work-groups of one unit
+      const int per_unit = gh * tpu * a.S;       // work-groups of one unit
       const int ui = k / per_unit;               // the XCD's ui-th unit
       const int rem = k - ui * per_unit;
-      const int r2 = rem / a.G;                  // (tile rank in unit, part), heaviest first
+      const int r2 = rem / gh;                   // (tile rank in unit, part), heaviest first
       const int rl = r2 / a.S;
       w.part = r2 - rl * a.S;
       const int u = (p & 7) + 8 * ui;            // unit = group g, rank class j
@@ -237,11 +241,12 @@ __device__ __forceinline__ PfWork pf_work_of(const PrefillArgs& a, int p) {
       // class holds as much heavy as light causal work
       const int rank = rl * m + ((rl & 1) ? m - 1 - j : j);
       w.b = g / a.Hkv;
-      w.h = (g - w.b * a.Hkv) * a.G + rem % a.G;
+      w.h = (g - w.b * a.Hkv) * a.G + hs * (rem % gh);
       w.qt = a.n_qt - 1 - rank;                    // below 0: past the unit's last tile
     } else {
-      w.h = p % a.Hq;
-      const int r = p / a.Hq;
+      const int hq = a.Hq / hs;
+      w.h = hs * (p % hq);
+      const int r = p / hq;
       w.b = r % a.B;
       const int r2 = r / a.B;
       const int rank = r2 / a.S;
@@ -310,25 +315,30 @@ constexpr size_t kBsListBytes = (kBsMaxTiles + 16) * sizeof(int);
 // variant (sliding window, ALiBi); F8: FP8 E4M3 pools; REV: key tiles walked
 // downwards, which is how the ALiBi variants (general only) walk, so REV also
 // compiles the bias in.  PER: an item of a persistent work-group (hand-over in hd).
-// BS: a block map (general variant, 8 waves, no key parts).
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER, bool BS = false>
+// BS: a block map (general variant, 8 waves, no key parts).  HP: paired heads (plain
+// bf16 variant, 8 waves): waves 0-3 take query head w.h and waves 4-7 head w.h + 1,
+// both over the same 128 rows, so each K/V tile in LDS serves two heads.
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS, bool PER, bool BS = false,
+          bool HP = false>
 __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
                                         const PfSetup& s, PfHand& hd, uint16_t* pf_lds) {
   static_assert(!REV || GEN, "the downward walk is a general-variant feature");
   static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
   static_assert(!BS || (GEN && !PER && W == 8), "block maps: general variant, 8 waves");
+  static_assert(!HP || (!GEN && !F8 && !PER && !BS && W == 8),
+                "paired heads: plain bf16 variant, 8 waves");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   using L_ = PfLds<D>;
   using M_ = PfDma<D, W>;
-  constexpr int kPfBM = 32 * W;       // query rows per work-group
+  constexpr int kPfBM = HP ? 128 : 32 * W;   // query rows per work-group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;         // query column of S^T / O^T
   const int hh = lane >> 5;          // k-half of the MFMA operands
   const int g16 = lane & 15;
-  const int h = w.h, b = w.b, part = w.part;
+  const int h = w.h + (HP ? wave / 4 : 0), b = w.b, part = w.part;
   const int t0 = s.t0, q_len = s.q_len, r_wg = s.r_wg, L = s.L, kvh = s.kvh;
   const int tile_lo = s.tile_lo, tile_hi = s.tile_hi;
   const uint16_t* kbase = a.k_pool + (size_t)kvh * D;
@@ -341,7 +351,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   if constexpr (PER) hd.has = hd.q_lds = 0;
 
   // this wave's rows and the position bound of its rows
-  const int r_w = r_wg + 32 * wave;
+  const int r_w = r_wg + 32 * (HP ? wave % 4 : wave);
   const int my_row = r_w + col;
   const bool row_ok = my_row < q_len && t0 + my_row < a.Tq;
   const int my_pos = shift + my_row;          // causal: keys <= my_pos are visible
@@ -1010,14 +1020,15 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
 }
 
 // One work-group per item of the plain grid (item = blockIdx.x).
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false,
+          bool HP = false>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   const PfWork w = pf_work_of(a, blockIdx.x);
-  const PfSetup s = pf_setup<GEN>(a, w, 32 * W, threadIdx.x & 63);
+  const PfSetup s = pf_setup<GEN>(a, w, HP ? 128 : 32 * W, threadIdx.x & 63);
   if (!s.ok) return;
   PfHand hd{};
-  pf_item<D, W, GEN, F8, REV, PS, false, BS>(a, w, s, hd, pf_lds);
+  pf_item<D, W, GEN, F8, REV, PS, false, BS, HP>(a, w, s, hd, pf_lds);
 }
 
 // Persistent work-groups: one per CU, a multiple of 8 of them, each working through
@@ -1185,7 +1196,7 @@ static hipError_t device_cus(int* cus) {
 
 // items of the plain grid (one per work-group there)
 static int prefill_items(const PrefillArgs& a) {
-  return a.Hq * a.B * prefill_grid_tiles(a) * a.S;
+  return a.Hq / (a.hp ? 2 : 1) * a.B * prefill_grid_tiles(a) * a.S;
 }
 
 // persistent work-groups for a launch: one per CU, a multiple of 8, no more than
@@ -1211,19 +1222,21 @@ static hipError_t launch_prefill_persist(const PrefillArgs& a, hipStream_t strea
   return hipGetLastError();
 }
 
-template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false>
+template <int D, int W, bool GEN, bool F8, bool REV, bool PS = false, bool BS = false,
+          bool HP = false>
 static hipError_t launch_prefill_w(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   constexpr size_t lds = PfLds<D>::BYTES + (BS ? kBsListBytes : 0);
   if constexpr (lds > 65536) {
     static std::atomic<int> state[kMaxDevices];
     const hipError_t e = lds_attribute_once(
-        state, reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS, BS>), lds);
+        state, reinterpret_cast<const void*>(prefill_kernel<D, W, GEN, F8, REV, PS, BS, HP>),
+        lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(prefill_items(a));
-  launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS, BS>, grid, dim3(64 * W), (uint32_t)lds,
-                stream, ev, a);
+  launch_kernel(prefill_kernel<D, W, GEN, F8, REV, PS, BS, HP>, grid, dim3(64 * W),
+                (uint32_t)lds, stream, ev, a);
   return hipGetLastError();
 }
 
@@ -1261,6 +1274,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
   if (a.alibi) return launch_prefill_w<D, W, true, false, true>(a, stream, ev);
   if (a.window > 0 || a.key_lo) return launch_prefill_w<D, W, true, false, false>(a, stream, ev);
   if (W == 8 && a.persist) return launch_prefill_persist<D>(a, stream, ev);
+  if constexpr (W == 8) {
+    if (a.hp) return launch_prefill_w<D, 8, false, false, false, false, false, true>(a, stream, ev);
+  }
   return launch_prefill_w<D, W, false, false, false>(a, stream, ev);
 }
 
@@ -1277,9 +1293,25 @@ static int prefill_waves(const PrefillArgs& a) {
   return prefill_waves(a.max_q_len, a.kv_fp8 && a.alibi != nullptr);
 }
 
-static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W) {
+// Paired heads (a work-group of 8 waves takes two query heads of one KV group over 128
+// rows instead of one head over 256): for the plain bf16 variant of an unsplit
+// 8-wave launch with an even GQA group.  Each K/V tile copied into LDS then serves
+// two heads' rows, the work-groups are as many as with 256-row tiles, and a causal
+// work-group's diagonal spans 128 keys instead of 256, so fewer of its (wave, block)
+// steps are masked whole.  A row's result does not depend on the tile height when
+// the keys are not split, so the output bits are those of the 256-row launch; with
+// key parts the parts follow the tile height, and the planner and the merge count
+// 256-row tiles, so split launches keep them.
+static bool prefill_pairs(const PrefillArgs& a, int W) {
+  return W == 8 && a.S <= 1 && !a.kv_fp8 && !a.alibi && a.window == 0 && !a.key_lo &&
+         !a.block_map && !a.persist && a.G % 2 == 0;
+}
+
+static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W, bool pairs = false) {
   PrefillArgs a = a_in;
-  a.n_qt = (a.max_q_len + 32 * W - 1) / (32 * W);
+  a.hp = pairs ? 1 : 0;
+  const int rows = pairs ? 128 : 32 * W;       // query rows per tile
+  a.n_qt = (a.max_q_len + rows - 1) / rows;
   // XCD units: groups, or m rank classes of each group with groups * m a multiple of
   // 8.  Only for m <= 2 and when every unit gets a tile rank (n_qt >= m), else the
   // plain order: with 4 or 8 classes most XCDs fetch most of a group's K/V anyway,
@@ -1357,7 +1389,7 @@ hipError_t launch_mixed(const PrefillArgs& p_in, const DecodeArgs& d, hipStream_
 hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* desc,
                           size_t desc_len, const KernelEvents& ev) {
   const int W = prefill_waves(a_in);
-  const PrefillArgs a = prefill_shape(a_in, W);
+  const PrefillArgs a = prefill_shape(a_in, W, prefill_pairs(a_in, W));
   hipError_t e;
   if (a.D == 128)
     e = W == 8 ? launch_prefill_t<128, 8>(a, stream, ev) : launch_prefill_t<128, 4>(a, stream, ev);
@@ -1382,12 +1414,12 @@ hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t stream, char* des
                      (per ? (a.D == 128 ? PfLds<128>::q_bytes(8) : PfLds<64>::q_bytes(8)) : 0) +
                      (a.block_map ? kBsListBytes : 0);
   snprintf(desc, desc_len,
-           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s%s> grid=%d (%d heads x %d seqs x %d "
+           "prefill<D=%d,BM=%d,BN=%d,mfma32x32x16,%s%s%s> grid=%d (%d heads x %d seqs x %d "
            "q-tiles x %d key parts, %s%s) block=%d lds=%zu",
-           a.D, 32 * W, kPfBN,
+           a.D, a.hp ? 128 : 32 * W, kPfBN,
            a.kv_fp8 ? (a.k_scales ? "fp8-e4m3-widened,scales per page" : "fp8-e4m3-widened")
                     : "lds-dma",
-           a.block_map ? ",block map" : "",
+           a.block_map ? ",block map" : "", a.hp ? ",paired heads" : "",
            prefill_items(a), a.Hq, a.B, a.n_qt, a.S, order, pers, 64 * W, lds);
   return e;
 }

@@ -361,3 +361,40 @@ def test_prefill_rows_that_see_no_key(require_gpu, lens, ql, causal, splits, win
     assert np.isneginf(got_l[empty]).all(), "a row with no key has a finite lse"
     assert_parity(got_o, o_ref, "prefill no-key")
     assert_lse(got_l, l_ref, "prefill no-key lse")
+
+
+PAIR_CASES = [
+    # hist, q_lens, Hq, Hkv, D, causal
+    ([0, 0, 0], [1024, 129, 600], 8, 4, 128, True),        # GQA 2
+    ([300, 0], [700, 512], 16, 1, 128, True),              # GQA 16
+    ([0, 64], [513, 900], 32, 4, 64, True),                # GQA 8, D 64
+    ([1000, 0], [530, 1100], 8, 2, 128, False),            # non-causal
+    ([0, 0], [1030, 520], 28, 4, 128, True),               # GQA 7: one head per work-group
+]
+
+
+@pytest.mark.parametrize("hist,ql,Hq,Hkv,D,causal", PAIR_CASES)
+def test_paired_heads_give_the_256_row_bits(require_gpu, hist, ql, Hq, Hkv, D, causal):
+    """An unsplit 8-wave launch with an even GQA group pairs two query heads over 128 rows
+    per work-group; the output bits equal the 256-row layout's (taken from the
+    persistent grid, which keeps it) and match the oracle; an odd group keeps one head
+    per work-group."""
+    print(f"[paired heads] hist={hist} q={ql} Hq={Hq} Hkv={Hkv} D={D} causal={causal}",
+          flush=True)
+    case = make_case("php", hist_lens=hist, q_lens=ql, write_new=True, causal=causal, Hq=Hq,
+                     Hkv=Hkv, D=D, page_size=16, seed=sum(ql) + Hq, device="cuda")
+    kp, vp = pools_after_write(case)
+    write(case)
+    o0, l0 = run_prefill(case)
+    desc = pa.describe_launch()
+    assert ("paired heads" in desc) == ((Hq // Hkv) % 2 == 0), desc
+    o1, l1 = pa.paged_attn_prefill_varlen(
+        case.q, case.k_pool, case.v_pool, case.cu_seqlens_q, case.seq_lens_k, case.block_tables,
+        case.scale, causal=causal, max_q_len=case.max_q_len, return_lse=True, persistent=True)
+    torch.cuda.synchronize()
+    assert "BM=256" in pa.describe_launch()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+    o_ref, l_ref = oracle_full(case, kp, vp)
+    assert_parity(as_f64(o0), o_ref, "paired heads")
+    assert_lse(as_f64(l0), l_ref, "paired heads lse")
