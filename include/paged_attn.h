@@ -574,8 +574,8 @@ size_t paged_attn_prefill_ex_workspace_bytes(int32_t B, int32_t Tq, int32_t max_
  * decode rows those of paged_attn_decode with the same split count when that launch
  * takes one-wave work-groups (Hkv x splits x B >= 512), and otherwise equal up to
  * rounding (its waves then split a partition's chunks and merge them).
- * Options (windows, ALiBi, FP8 pools, document ranges, block maps) are not taken:
- * use the separate entry points for them.
+ * FP8 pools are taken (pa_mixed_fp8 below); the other options (windows, ALiBi,
+ * document ranges, block maps) are not: use the separate entry points for them.
  */
 typedef struct {
   void* out;                    /* bf16 [Tq, Hq, D]                                     */
@@ -599,11 +599,20 @@ typedef struct {
   int32_t B, max_pages;         /* B == 0: no decode part                               */
   int32_t max_seq_len;          /* host-side bound of seq_lens, as paged_attn_decode's  */
   int32_t num_splits;           /* > 0: as paged_attn_decode's; <= 0: paged_attn_decode's
-                                   own count times the waves per work-group its launch
-                                   would give each item (1, 2 or 4), so that each
-                                   one-wave item here walks as many keys as a wave does
-                                   there                                                */
+                                   (or paged_attn_decode_fp8's) own count times the waves
+                                   per work-group its launch would give each item (1, 2
+                                   or 4), so that each one-wave item here walks as many
+                                   keys as a wave does there                            */
 } pa_mixed_decode;
+
+/* FP8 E4M3 pools for paged_attn_mixed (a NULL pointer there: bf16 pools), with the
+ * scales paged_attn_decode_ex and paged_attn_prefill_ex take: one per pool, or per
+ * (page, KV head) when k_scales / v_scales are given (both or neither). */
+typedef struct {
+  float k_scale, v_scale;       /* one scale per pool (with k_scales NULL)              */
+  const float* k_scales;        /* NULL, or device [num_pages, Hkv] float32             */
+  const float* v_scales;        /* with k_scales                                        */
+} pa_mixed_fp8;
 
 /*
  * Workspace bytes of paged_attn_mixed: the prefill's key-part partials (as
@@ -613,20 +622,21 @@ typedef struct {
  * needs one or an argument is NULL or not positive.
  */
 size_t paged_attn_mixed_workspace_bytes(const pa_mixed_prefill* prefill,
-                                        const pa_mixed_decode* decode, int32_t Hq,
-                                        int32_t Hkv, int32_t D);
+                                        const pa_mixed_decode* decode, const pa_mixed_fp8* fp8,
+                                        int32_t Hq, int32_t Hkv, int32_t D);
 
 /*
  * paged_attn_mixed -- the prefill and decode batches above in one launch (plus their
- * merges).  Both parts share the pools (num_pages, page_size, Hkv, D), Hq and the
- * softmax scale.  prefill or decode NULL: PA_ERR_NULL.  Each part is checked as its
- * own entry point checks it (the same statuses; the message names the part); a part
- * with B == 0 is skipped, and with both skipped nothing is launched.  The workspace
- * is scratch (calls that share one must not run concurrently).
+ * merges).  Both parts share the pools (num_pages, page_size, Hkv, D; bf16, or with
+ * fp8 non-NULL E4M3 codes under fp8's scales), Hq and the softmax scale.  prefill or
+ * decode NULL: PA_ERR_NULL.  Each part is checked as its own entry point checks it (the
+ * same statuses; the message names the part); a part with B == 0 is skipped, and with
+ * both skipped nothing is launched.  The workspace is scratch (calls that share one
+ * must not run concurrently).
  */
 int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* decode,
-                     const void* k_pool, const void* v_pool, int32_t num_pages,
-                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                     const pa_mixed_fp8* fp8, const void* k_pool, const void* v_pool,
+                     int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
                      float softmax_scale, void* workspace, size_t workspace_bytes,
                      void* stream);
 

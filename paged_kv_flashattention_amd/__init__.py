@@ -784,18 +784,20 @@ def _prefill(split, q, k_pool, v_pool, cu_seqlens_q, seq_lens_k, block_tables, s
     return (out, lse) if return_lse else out
 
 
-def mixed_workspace_bytes(Hq: int, Hkv: int, D: int, prefill=None, decode=None) -> int:
+def mixed_workspace_bytes(Hq: int, Hkv: int, D: int, prefill=None, decode=None,
+                          fp8: bool = False) -> int:
     """Workspace bytes of paged_attn_mixed for the host-side sizes of its parts:
     prefill = (B, Tq, max_q_len, num_splits), decode = (B, max_seq_len, num_splits),
-    either None for no such part."""
+    either None for no such part; fp8 for FP8 pools (the decode's split rule differs)."""
     p = _lib.MixedPrefill()
     d = _lib.MixedDecode()
     if prefill is not None:
         p.B, p.Tq, p.max_q_len, p.num_splits = (int(x) for x in prefill)
     if decode is not None:
         d.B, d.max_seq_len, d.num_splits = (int(x) for x in decode)
+    f = ctypes.byref(_lib.MixedFp8(1.0, 1.0, None, None)) if fp8 else None
     return int(load_library().paged_attn_mixed_workspace_bytes(ctypes.byref(p), ctypes.byref(d),
-                                                               int(Hq), int(Hkv), int(D)))
+                                                               f, int(Hq), int(Hkv), int(D)))
 
 
 def paged_attn_mixed(k_pool, v_pool, softmax_scale: float, prefill=None, decode=None,
@@ -806,7 +808,7 @@ def paged_attn_mixed(k_pool, v_pool, softmax_scale: float, prefill=None, decode=
                      prefill_lse: Optional[torch.Tensor] = None,
                      decode_lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                      workspace: Optional[torch.Tensor] = None, stream=None,
-                     validate: bool = False):
+                     validate: bool = False, k_scale=None, v_scale=None):
     """A step's prefill chunks and decode rows over the same bf16 pools in one kernel
     launch (then the merges of their key parts and partitions): see paged_attn_mixed
     in C.
@@ -819,16 +821,30 @@ def paged_attn_mixed(k_pool, v_pool, softmax_scale: float, prefill=None, decode=
     the device when omitted (a synchronisation).  Returns (prefill_out, decode_out),
     with (prefill_lse, decode_lse) after them when ``return_lse``; a missing part's
     entries are None.  Outputs and lse buffers may be passed in (``*_out``,
-    ``*_lse``), as for graph capture."""
-    _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16),
-            (prefill_out, "prefill_out", torch.bfloat16),
+    ``*_lse``), as for graph capture.  With ``k_scale`` and ``v_scale`` the pools hold
+    FP8 E4M3 codes under those scales (floats: one per pool; float32 tensors
+    [num_pages, Hkv]: per page and KV head), as paged_attn_decode_fp8 takes them."""
+    scales = None
+    if k_scale is not None or v_scale is not None:
+        if k_scale is None or v_scale is None:
+            raise TypeError("k_scale and v_scale must both be given for FP8 pools")
+        scales = _scales(k_scale, v_scale)
+        _need_fp8_dtype(k_pool, "k_pool")
+        _need_fp8_dtype(v_pool, "v_pool")
+    else:
+        _dtypes((k_pool, "k_pool", torch.bfloat16), (v_pool, "v_pool", torch.bfloat16))
+    _dtypes((prefill_out, "prefill_out", torch.bfloat16),
             (decode_out, "decode_out", torch.bfloat16),
             (prefill_lse, "prefill_lse", torch.float32), (decode_lse, "decode_lse", torch.float32))
     if prefill is None and decode is None:
         raise ValueError("paged_attn_mixed needs a prefill part, a decode part or both")
     dev = (prefill or decode)[0].device
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    if scales is None:
+        _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+        _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    else:
+        _need_fp8_pool(k_pool, "k_pool", dev)
+        _need_fp8_pool(v_pool, "v_pool", dev)
     P, ps, Hkv, D = k_pool.shape
     if v_pool.shape != k_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
@@ -917,14 +933,21 @@ def paged_attn_mixed(k_pool, v_pool, softmax_scale: float, prefill=None, decode=
         md.B, md.max_pages, md.max_seq_len = B, bt.shape[1], int(decode_max_seq_len)
         md.num_splits = int(decode_num_splits)
     lib = load_library()
-    need = int(lib.paged_attn_mixed_workspace_bytes(ctypes.byref(mp), ctypes.byref(md), Hq, Hkv, D))
+    f8 = None
+    if scales is not None:
+        ksp = vsp = None
+        if isinstance(scales, _PageScales):
+            ksp, vsp = scales.check(k_pool.shape, dev)
+        f8 = ctypes.byref(_lib.MixedFp8(*_pool_scales(scales), ksp, vsp))
+    need = int(lib.paged_attn_mixed_workspace_bytes(ctypes.byref(mp), ctypes.byref(md), f8, Hq,
+                                                    Hkv, D))
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1, dev)
     elif need:
         workspace = _internal(torch.empty(need, dtype=torch.uint8, device=dev), stream)
     ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
-        _check(lib.paged_attn_mixed(ctypes.byref(mp), ctypes.byref(md), _ptr(k_pool),
+        _check(lib.paged_attn_mixed(ctypes.byref(mp), ctypes.byref(md), f8, _ptr(k_pool),
                                     _ptr(v_pool), P, ps, Hq, Hkv, D, float(softmax_scale),
                                     _ptr(workspace), ws_bytes, _stream(stream)))
     if return_lse:

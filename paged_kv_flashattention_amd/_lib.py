@@ -59,10 +59,17 @@ class MixedDecode(ctypes.Structure):
                 ("max_seq_len", ctypes.c_int32), ("num_splits", ctypes.c_int32)]
 
 
+class MixedFp8(ctypes.Structure):
+    """pa_mixed_fp8"""
+    _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
+
+
 c_dopts = ctypes.POINTER(DecodeOpts)
 c_popts = ctypes.POINTER(PrefillOpts)
 c_mpf = ctypes.POINTER(MixedPrefill)
 c_mdec = ctypes.POINTER(MixedDecode)
+c_mfp8 = ctypes.POINTER(MixedFp8)
 
 # name -> (restype, argtypes); mirrors include/paged_attn.h
 SIGNATURES = {
@@ -110,9 +117,9 @@ SIGNATURES = {
                                       c_i32, c_float, c_popts, c_vp, c_size, c_vp]),
     "paged_attn_prefill_ex_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32,
                                                        c_popts]),
-    "paged_attn_mixed_workspace_bytes": (c_size, [c_mpf, c_mdec, c_i32, c_i32, c_i32]),
-    "paged_attn_mixed": (c_i32, [c_mpf, c_mdec, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                 c_float, c_vp, c_size, c_vp]),
+    "paged_attn_mixed_workspace_bytes": (c_size, [c_mpf, c_mdec, c_mfp8, c_i32, c_i32, c_i32]),
+    "paged_attn_mixed": (c_i32, [c_mpf, c_mdec, c_mfp8, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                 c_i32, c_float, c_vp, c_size, c_vp]),
     "pa_status_string": (ctypes.c_char_p, [c_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_describe_launch": (ctypes.c_char_p, []),

@@ -900,10 +900,10 @@ static int32_t mixed_prefill_splits(const pa_mixed_prefill& p, int32_t Hq) {
 // it would stream in paged_attn_decode (measured on MI355X, the mixed ragged step:
 // 116.5-120.7 us with 4 splits, 152.5-154.5 us with the decode's own 2, whose
 // one-wave items of 1,760 keys then outlast the prefill).
-static int32_t mixed_decode_splits(const pa_mixed_decode& d, int32_t Hkv) {
+static int32_t mixed_decode_splits(const pa_mixed_decode& d, int32_t Hkv, bool fp8) {
   if (d.num_splits > 0) return d.num_splits;
   const int32_t s0 = resolve_splits(d.B, Hkv, d.max_seq_len, 0);
-  const int w = pa::decode_waves((long long)Hkv * s0 * (d.B > 0 ? d.B : 1), false);
+  const int w = pa::decode_waves((long long)Hkv * s0 * (d.B > 0 ? d.B : 1), fp8);
   return resolve_splits(d.B, Hkv, d.max_seq_len, s0 * w);
 }
 
@@ -913,25 +913,31 @@ static size_t mixed_prefill_bytes(const pa_mixed_prefill& p, int32_t Hq, int32_t
 }
 
 size_t paged_attn_mixed_workspace_bytes(const pa_mixed_prefill* prefill,
-                                        const pa_mixed_decode* decode, int32_t Hq,
-                                        int32_t Hkv, int32_t D) {
+                                        const pa_mixed_decode* decode, const pa_mixed_fp8* fp8,
+                                        int32_t Hq, int32_t Hkv, int32_t D) {
   if (!prefill || !decode || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
   const size_t pf = mixed_prefill_bytes(*prefill, Hq, D);
-  const size_t dec = decode->B > 0 && decode->max_seq_len >= 0
-                         ? workspace_for(decode->B, Hq, D, mixed_decode_splits(*decode, Hkv))
-                         : 0;
+  const size_t dec =
+      decode->B > 0 && decode->max_seq_len >= 0
+          ? workspace_for(decode->B, Hq, D, mixed_decode_splits(*decode, Hkv, fp8 != nullptr))
+          : 0;
   return pf + dec;
 }
 
 int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* decode,
-                     const void* k_pool, const void* v_pool, int32_t num_pages,
-                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
+                     const pa_mixed_fp8* fp8, const void* k_pool, const void* v_pool,
+                     int32_t num_pages, int32_t page_size, int32_t Hq, int32_t Hkv, int32_t D,
                      float softmax_scale, void* workspace, size_t workspace_bytes,
                      void* stream) {
   g_last_error[0] = 0;
   if (!prefill || !decode) return fail(PA_ERR_NULL, "mixed: prefill or decode is NULL");
   const pa_mixed_prefill& p = *prefill;
   const pa_mixed_decode& dc = *decode;
+  // FP8 pools: the scales of both parts (checked by each part's own checks below)
+  const bool f8 = fp8 != nullptr;
+  const float ks = f8 ? fp8->k_scale : 1.f, vs = f8 ? fp8->v_scale : 1.f;
+  const float* kss = f8 ? fp8->k_scales : nullptr;
+  const float* vss = f8 ? fp8->v_scales : nullptr;
   // the prefill's partials come first in the workspace, the decode's after them; a
   // part with B == 0 is not checked
   const size_t pf_need = Hq > 0 && D > 0 ? mixed_prefill_bytes(p, Hq, D) : 0;
@@ -943,8 +949,8 @@ int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* dec
                                 p.B, p.Tq, p.max_q_len, p.max_pages, num_pages, page_size, Hq,
                                 Hkv, D, softmax_scale, p.causal, p.num_splits, workspace,
                                 workspace_bytes < pf_need ? workspace_bytes : pf_need, 0,
-                                nullptr, false, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, 0,
-                                nullptr, 0, 0, 8);
+                                nullptr, f8, ks, vs, nullptr, nullptr, kss, vss, 0, nullptr, 0,
+                                0, 8);
     if (st) return st;
     if (no_prefill) a = pa::PrefillArgs{};
   }
@@ -953,7 +959,8 @@ int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* dec
     const int st = decode_args(d, "mixed (decode part)", dc.q, k_pool, v_pool, dc.block_tables,
                                dc.seq_lens, dc.B, dc.max_pages, num_pages, page_size, Hq, Hkv,
                                D, softmax_scale, dc.max_seq_len,
-                               dc.max_seq_len >= 0 ? mixed_decode_splits(dc, Hkv) : 0);
+                               dc.max_seq_len >= 0 ? mixed_decode_splits(dc, Hkv, f8) : 0, f8,
+                               ks, vs, 0, nullptr, nullptr, kss, vss);
     if (st) return st;
     if (!dc.out) return fail(PA_ERR_NULL, "mixed (decode part): out is NULL");
     if (!aligned16(dc.out))

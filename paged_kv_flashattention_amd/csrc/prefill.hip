@@ -1079,7 +1079,9 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_persist_kernel(PrefillArgs 
 // while the prefill's heaviest tiles start, and the CUs they free take prefill
 // items; n_dg is a multiple of 8, so prefill item p runs on XCD p mod 8 as in the
 // plain grid.
-template <int D>
+// F8: FP8 E4M3 pools (the plain FP8 prefill variant, or with PS, scales per (page, KV
+// head), the general one, which reads them).
+template <int D, bool F8 = false, bool PS = false>
 __global__ __launch_bounds__(512, 1) void mixed_kernel(PrefillArgs a, DecodeArgs d, int n_dg) {
   extern __shared__ __align__(16) uint16_t pf_lds[];
   static_assert(8 * 32 * KRows<D>::LROW <= PfLds<D>::TILE * 5, "decode staging fits the LDS");
@@ -1090,14 +1092,14 @@ __global__ __launch_bounds__(512, 1) void mixed_kernel(PrefillArgs a, DecodeArgs
     const int b = i / per_b;
     const int r = i - b * per_b;
     const int split = r / d.Hkv;
-    decode_item<D, 1, false, false, false, true>(d, r - split * d.Hkv, split, b);
+    decode_item<D, 1, F8, false, PS, true>(d, r - split * d.Hkv, split, b);
     return;
   }
   const PfWork w = pf_work_of(a, blockIdx.x - n_dg);
-  const PfSetup s = pf_setup<false>(a, w, 256, threadIdx.x & 63);
+  const PfSetup s = pf_setup<PS>(a, w, 256, threadIdx.x & 63);
   if (!s.ok) return;
   PfHand hd{};
-  pf_item<D, 8, false, false, false, false, false>(a, w, s, hd, pf_lds);
+  pf_item<D, 8, PS, F8, false, PS, false>(a, w, s, hd, pf_lds);
 }
 
 // Merge of the query tiles that were cut into key-range parts ("The Stack Below
@@ -1345,17 +1347,27 @@ hipError_t launch_prefill_merge(const PrefillArgs& a_in, hipStream_t stream, cha
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_mixed_d(const PrefillArgs& a, const DecodeArgs& d, int n_dg, int n_pf,
+template <int D, bool F8, bool PS>
+static hipError_t launch_mixed_v(const PrefillArgs& a, const DecodeArgs& d, int n_dg, int n_pf,
                                  hipStream_t stream, const KernelEvents& ev) {
   constexpr size_t lds = PfLds<D>::BYTES;
   static std::atomic<int> state[kMaxDevices];
   const hipError_t e =
-      lds_attribute_once(state, reinterpret_cast<const void*>(mixed_kernel<D>), lds);
+      lds_attribute_once(state, reinterpret_cast<const void*>(mixed_kernel<D, F8, PS>), lds);
   if (e != hipSuccess) return e;
-  launch_kernel(mixed_kernel<D>, dim3(n_dg + n_pf), dim3(512), (uint32_t)lds, stream, ev, a, d,
-                n_dg);
+  launch_kernel(mixed_kernel<D, F8, PS>, dim3(n_dg + n_pf), dim3(512), (uint32_t)lds, stream,
+                ev, a, d, n_dg);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_mixed_d(const PrefillArgs& a, const DecodeArgs& d, int n_dg, int n_pf,
+                                 hipStream_t stream, const KernelEvents& ev) {
+  const bool fp8 = a.kv_fp8 || d.kv_fp8;
+  const bool ps = a.k_scales || d.k_scales;
+  if (fp8 && ps) return launch_mixed_v<D, true, true>(a, d, n_dg, n_pf, stream, ev);
+  if (fp8) return launch_mixed_v<D, true, false>(a, d, n_dg, n_pf, stream, ev);
+  return launch_mixed_v<D, false, false>(a, d, n_dg, n_pf, stream, ev);
 }
 
 hipError_t launch_mixed(const PrefillArgs& p_in, const DecodeArgs& d, hipStream_t stream,
@@ -1376,11 +1388,14 @@ hipError_t launch_mixed(const PrefillArgs& p_in, const DecodeArgs& d, hipStream_
   }
   const hipError_t e = D == 128 ? launch_mixed_d<128>(a, d, n_dg, n_pf, stream, ev)
                                 : launch_mixed_d<64>(a, d, n_dg, n_pf, stream, ev);
+  const bool fp8 = a.kv_fp8 || d.kv_fp8;
   snprintf(desc, desc_len,
-           "mixed<D=%d> grid=%d: %d decode work-groups (%lld one-wave items: %d KV heads x %d "
+           "mixed<D=%d,%s> grid=%d: %d decode work-groups (%lld one-wave items: %d KV heads x %d "
            "splits x %d rows) then %d prefill items (256-row tiles, %d key parts, %s) "
            "block=512 lds=%zu",
-           D, n_dg + n_pf, n_dg, n_dec, d.Hkv, d.S, d.B, n_pf, a.S,
+           D,
+           fp8 ? (a.k_scales || d.k_scales ? "fp8-e4m3 scales per page" : "fp8-e4m3") : "bf16",
+           n_dg + n_pf, n_dg, n_dec, d.Hkv, d.S, d.B, n_pf, a.S,
            a.xcd_groups ? "KV groups per XCD" : "head-major",
            D == 128 ? PfLds<128>::BYTES : PfLds<64>::BYTES);
   return e;

@@ -493,47 +493,59 @@ def test_mixed_step_arguments_are_checked(lib):
             setattr(d, k, v)
         return d
     args = (FAKE, FAKE, P, ps, Hq, Hkv, D, 0.1)
-    assert m(None, ctypes.byref(dec()), *args, None, 0, None) == 1
-    assert m(ctypes.byref(pf()), None, *args, None, 0, None) == 1
+    assert m(None, ctypes.byref(dec()), None, *args, None, 0, None) == 1
+    assert m(ctypes.byref(pf()), None, None, *args, None, 0, None) == 1
     # both parts empty: nothing to do, nothing checked
-    assert m(ctypes.byref(pf(B=0, cu_seqlens_q=None)), ctypes.byref(dec(B=0, q=None)), *args,
-             None, 0, None) == 0
+    assert m(ctypes.byref(pf(B=0, cu_seqlens_q=None)), ctypes.byref(dec(B=0, q=None)), None,
+             *args, None, 0, None) == 0
     assert b"nothing to do" in lib.pa_describe_launch()
     # a missing pointer or a bad size in one part is that part's error
-    assert m(ctypes.byref(pf(cu_seqlens_q=None)), ctypes.byref(dec(B=0)), *args, None, 0,
+    assert m(ctypes.byref(pf(cu_seqlens_q=None)), ctypes.byref(dec(B=0)), None, *args, None, 0,
              None) == 1
     assert b"prefill part" in lib.pa_last_error()
-    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(out=None)), *args, None, 0, None) == 1
+    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(out=None)), None, *args, None, 0, None) == 1
     assert b"decode part" in lib.pa_last_error()
-    assert m(ctypes.byref(pf(B=-1)), ctypes.byref(dec()), *args, None, 0, None) == 2
-    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(max_seq_len=-5)), *args, None, 0,
+    assert m(ctypes.byref(pf(B=-1)), ctypes.byref(dec()), None, *args, None, 0, None) == 2
+    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec(max_seq_len=-5)), None, *args, None, 0,
              None) == 2
-    assert m(ctypes.byref(pf()), ctypes.byref(dec()), FAKE, FAKE, P, ps, Hq, Hkv, 96, 0.1,
+    assert m(ctypes.byref(pf()), ctypes.byref(dec()), None, FAKE, FAKE, P, ps, Hq, Hkv, 96, 0.1,
              None, 0, None) == 3
     # workspace: the prefill's parts for 256-row tiles, then the decode's partials
     need_pf = lib.paged_attn_prefill_workspace_bytes(2, 1200, 600, Hq, D, 3)
     need_dec = lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 120, 2)
     assert need_pf > 0 and need_dec > 0
-    assert w(ctypes.byref(pf()), ctypes.byref(dec()), Hq, Hkv, D) == need_pf + need_dec
-    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec()), Hq, Hkv, D) == need_dec
-    assert w(ctypes.byref(pf()), ctypes.byref(dec(B=0)), Hq, Hkv, D) == need_pf
-    assert w(ctypes.byref(pf(num_splits=1)), ctypes.byref(dec(num_splits=1)), Hq, Hkv, D) == 0
+    assert w(ctypes.byref(pf()), ctypes.byref(dec()), None, Hq, Hkv, D) == need_pf + need_dec
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec()), None, Hq, Hkv, D) == need_dec
+    assert w(ctypes.byref(pf()), ctypes.byref(dec(B=0)), None, Hq, Hkv, D) == need_pf
+    assert w(ctypes.byref(pf(num_splits=1)), ctypes.byref(dec(num_splits=1)), None, Hq, Hkv,
+             D) == 0
     # the decode part's own count (num_splits <= 0): the decode's count (1 for 3 rows of
     # 120 keys) times the waves its launch would give each item (4 for 6 items), at most
     # one 32-key chunk per split
     assert lib.paged_attn_decode_num_splits(3, Hkv, 120) == 1
-    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0)), Hq, Hkv, D) == \
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0)), None, Hq, Hkv, D) == \
         lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 120, 4)
-    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0, max_seq_len=70)), Hq, Hkv,
-             D) == lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 70, 3)
-    assert w(None, ctypes.byref(dec()), Hq, Hkv, D) == 0
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0, max_seq_len=70)), None, Hq,
+             Hkv, D) == lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 70, 3)
+    assert w(None, ctypes.byref(dec()), None, Hq, Hkv, D) == 0
     # short prefill runs still take 256-row tiles, and the library's part count is
     # resolved for them: 4 x 32 x 2 tiles fill the 256 slots (one part), where the
     # prefill alone would take 128-row tiles, 384 of 512 slots, and two parts
     short = pf(B=4, max_q_len=300, num_splits=0)
-    assert w(ctypes.byref(short), ctypes.byref(dec(B=0)), 32, Hkv, D) == 0
+    assert w(ctypes.byref(short), ctypes.byref(dec(B=0)), None, 32, Hkv, D) == 0
     assert lib.paged_attn_prefill_workspace_bytes(4, 1200, 300, 32, D, 0) > 0
+    # FP8 pools: the decode's own count for FP8 (1) times the waves the FP8 decode would
+    # take (4), and the scales are checked as the separate entry points check them
+    f8 = _lib.MixedFp8(0.5, 0.25, None, None)
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(dec(num_splits=0)), ctypes.byref(f8), Hq,
+             Hkv, D) == lib.paged_attn_decode_workspace_bytes(3, Hq, Hkv, D, 120, 4)
+    bad = _lib.MixedFp8(-1.0, 0.25, None, None)
+    assert m(ctypes.byref(pf(B=0)), ctypes.byref(dec()), ctypes.byref(bad), *args, None, 0,
+             None) == 2
+    half = _lib.MixedFp8(1.0, 1.0, FAKE, None)
+    assert m(ctypes.byref(pf()), ctypes.byref(dec(B=0)), ctypes.byref(half), *args, None, 0,
+             None) == 1
     for ws_bytes in (0, need_pf, need_pf + need_dec - 1):
-        assert m(ctypes.byref(pf()), ctypes.byref(dec()), *args,
+        assert m(ctypes.byref(pf()), ctypes.byref(dec()), None, *args,
                  FAKE if ws_bytes else None, ws_bytes, None) == 5
         assert b"workspace" in lib.pa_last_error()

@@ -182,3 +182,48 @@ def test_mixed_workspace_reuse_and_refusals(require_gpu):
     with pytest.raises(pa.PagedAttnError, match="WORKSPACE"):
         pa.paged_attn_mixed(case.k_pool, case.v_pool, case.scale, prefill=pf, decode=dec,
                             prefill_num_splits=4, decode_num_splits=3, workspace=ws[:need - 1])
+
+
+@pytest.mark.parametrize("scales,D", [("pool", 128), ("page", 128), ("page", 64)])
+def test_mixed_fp8_pools(require_gpu, scales, D):
+    """The one-launch step over FP8 E4M3 pools (one scale per pool, or per page and KV
+    head): every row against the oracle on the dequantised pools; the prefill rows
+    bit-identical to paged_attn_prefill_varlen_fp8 with the same key parts."""
+    from oracle import fp8 as of
+    from workloads import random_e4m3_codes
+    print(f"[mixed fp8] scales={scales} D={D}", flush=True)
+    lens = [2500, 700, 3000, 1, 64, 1500]
+    ql = [600, 512, 1, 1, 1, 1]
+    case = make_case("mx8", seq_lens=lens, q_lens=ql, Hq=16, Hkv=4, D=D, page_size=16,
+                     seed=D + len(scales), device="cuda", causal=True)
+    shape = tuple(case.k_pool.shape)
+    P = shape[0]
+    kc, vc = random_e4m3_codes(shape, 31, "cuda"), random_e4m3_codes(shape, 32, "cuda")
+    rng = np.random.default_rng(33)
+    if scales == "page":
+        ks = (2.0 ** rng.uniform(-8, -4, (P, 4))).astype(np.float32)
+        vs = (2.0 ** rng.uniform(-6, -3, (P, 4))).astype(np.float32)
+        k_arg, v_arg = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    else:
+        ks, vs = 2.0 ** -6, 2.0 ** -4
+        k_arg, v_arg = ks, vs
+    pf, dec, t_pf = parts(case, 2)
+    o_p, o_d, l_p, l_d = pa.paged_attn_mixed(
+        kc, vc, case.scale, prefill=pf, decode=dec, prefill_max_q_len=600,
+        prefill_num_splits=3, decode_max_seq_len=3000, decode_num_splits=0, return_lse=True,
+        validate=True, k_scale=k_arg, v_scale=v_arg)
+    torch.cuda.synchronize()
+    desc = pa.describe_launch()
+    assert "fp8-e4m3" in desc and (("scales per page" in desc) == (scales == "page")), desc
+    s_p, s_pl = pa.paged_attn_prefill_varlen_fp8(pf[0], kc, vc, *pf[1:], case.scale, k_arg,
+                                                 v_arg, causal=True, max_q_len=600,
+                                                 num_splits=3, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, s_p) and torch.equal(l_p, s_pl)
+    kd = of.dequantize_pool(kc.cpu().numpy(), ks)
+    vd = of.dequantize_pool(vc.cpu().numpy(), vs)
+    o_ref, l_ref = oracle_full(case, kd, vd)
+    assert_parity(as_f64(o_p), o_ref[:t_pf], "mixed fp8 prefill rows")
+    assert_lse(as_f64(l_p), l_ref[:t_pf], "mixed fp8 prefill lse")
+    assert_parity(as_f64(o_d), o_ref[t_pf:], "mixed fp8 decode rows")
+    assert_lse(as_f64(l_d), l_ref[t_pf:], "mixed fp8 decode lse")
