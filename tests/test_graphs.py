@@ -336,3 +336,46 @@ def test_mixed_step_in_one_launch_graph_replays_match_eager(require_gpu):
                             decode=(dc[0][:2], dc[1][:2], dc[2][:2]), prefill_num_splits=2,
                             decode_num_splits=7, workspace=ws)
         torch.cuda.synchronize()
+
+
+def test_prepared_mixed_step_repeats_the_launch(require_gpu):
+    """pa.prepared() around the one-launch mixed step (its structs marshalled once, the
+    workspace the binding allocated held by the returned function): replays after new
+    queries are written in place match direct calls bit for bit."""
+    print("[prepared] one-launch mixed step", flush=True)
+    case = make_case("pmx", hist_lens=[1500, 0, 200, 3000], q_lens=[512, 600, 1, 1],
+                     write_new=True, causal=True, Hq=8, Hkv=2, D=128, page_size=16, seed=90,
+                     device="cuda")
+    pa.kv_page_write(case.k_pool, case.v_pool, case.k_new, case.v_new, case.cu_new,
+                     case.start_pos, case.block_tables)
+    t_pf = int(case.cu_seqlens_q[2])
+    q_pf = case.q[:t_pf].contiguous()
+    q_d = case.q[t_pf:].contiguous()
+    pf = (q_pf, case.cu_seqlens_q[:3].contiguous(), case.seq_lens_k[:2].contiguous(),
+          case.block_tables[:2].contiguous())
+    dc = (q_d, case.block_tables[2:].contiguous(), case.seq_lens_k[2:].contiguous())
+    o_p = torch.empty((t_pf, 8, 128), dtype=torch.bfloat16, device="cuda")
+    o_d = torch.empty((2, 8, 128), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        pa.paged_attn_mixed(case.k_pool, case.v_pool, case.scale, prefill=pf, decode=dc,
+                            prefill_max_q_len=600, prefill_num_splits=2,
+                            decode_max_seq_len=3001, prefill_out=o_p, decode_out=o_d)
+
+    run = pa.prepared(step)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    for rep in range(3):
+        if rep:
+            gen.manual_seed(200 + rep)
+            q_pf.copy_(torch.randn(q_pf.shape, generator=gen, device="cuda").to(torch.bfloat16))
+            q_d.copy_(torch.randn(q_d.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        step()
+        torch.cuda.synchronize()
+        ref = (bits(o_p).copy(), bits(o_d).copy())
+        o_p.zero_()
+        o_d.zero_()
+        run()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o_p), ref[0]), rep
+        assert np.array_equal(bits(o_d), ref[1]), rep
