@@ -616,10 +616,10 @@ def record_traffic(workload, pmc_dir):
     rec["source_sha256"] = source_digest(workload)
     rec["commands"] = [
         f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {k} "
-        f"--output-format csv -d $REPO/gpurun_out/pmc_{workload}_{k} -o run -- python3 "
+        f"--output-format csv -d $OUT/pmc_{workload}_{k} -o run -- python3 "
         f"$REPO/bench.py --traffic-pass --workload {workload} --steps 6"
         for k in ("FETCH_SIZE", "WRITE_SIZE")] + [
-        f"python3 bench.py --workload {workload} --record-traffic gpurun_out"]
+        f"python3 bench.py --workload {workload} --record-traffic $OUT"]
     with open(os.path.join(ROOT, "profiles", fname), "w") as fh:
         json.dump(rec, fh, indent=1)
     log(f"[bench] {workload}: {rec['bytes_per_launch']} bytes per launch -> profiles/{fname}")
