@@ -113,7 +113,8 @@ def test_causal_prefill_full_size_every_work_group(require_gpu):
     kv_page_write then attended in the launch the benchmark times.  The oracle checks
     one complete query head per (sequence, KV head) -- 32 heads of 4,096 rows, every
     query tile and key tile of their groups -- and one row of every other (head,
-    sequence, 256-row query tile) work-group of the grid, 2,048 work-groups in all."""
+    sequence, 128-row query block), so every work-group of the grid (2,048 of them,
+    each two heads' 128 rows with paired heads, or one head's 256) has rows checked."""
     case = make_config("causal_prefill", "cuda")
     print("[prefill] causal_prefill full size, every work-group", flush=True)
     kp, vp = pools_after_write(case)
@@ -135,8 +136,8 @@ def test_causal_prefill_full_size_every_work_group(require_gpu):
         for h in range(case.Hq):
             if (b, h) in whole:
                 continue
-            for qt in range(4096 // 256):
-                rows.append((4096 * b + 256 * qt + int(rng.integers(0, 256)), h))
+            for qt in range(4096 // 128):
+                rows.append((4096 * b + 128 * qt + int(rng.integers(0, 128)), h))
     o_ref, l_ref = oracle_rows(case, rows, kp, vp)
     idx_t = torch.as_tensor([t for t, _ in rows], device="cuda")
     idx_h = torch.as_tensor([h for _, h in rows], device="cuda")
