@@ -598,11 +598,14 @@ typedef struct {
   const int32_t* seq_lens;      /* [B] int32                                            */
   int32_t B, max_pages;         /* B == 0: no decode part                               */
   int32_t max_seq_len;          /* host-side bound of seq_lens, as paged_attn_decode's  */
-  int32_t num_splits;           /* > 0: as paged_attn_decode's; <= 0: paged_attn_decode's
-                                   (or paged_attn_decode_fp8's) own count times the waves
-                                   per work-group its launch would give each item (1, 2
-                                   or 4), so that each one-wave item here walks as many
-                                   keys as a wave does there                            */
+  int32_t num_splits;           /* > 0: as paged_attn_decode's; <= 0: the larger of
+                                   paged_attn_decode's (or paged_attn_decode_fp8's) own
+                                   count times the waves per work-group its launch would
+                                   give each item (1, 2 or 4), so that each one-wave item
+                                   here walks as many keys as a wave does there, and the
+                                   count that gives the CUs the prefill's work-groups
+                                   leave free (of 256) eight items each, partitions kept
+                                   at 8 chunks of 32 keys or more                       */
 } pa_mixed_decode;
 
 /* FP8 E4M3 pools for paged_attn_mixed (a NULL pointer there: bf16 pools), with the

@@ -894,17 +894,45 @@ static int32_t mixed_prefill_splits(const pa_mixed_prefill& p, int32_t Hq) {
   return resolve_prefill_splits(p.B, Hq, mq, p.num_splits, 8);
 }
 
-// The decode part's split count: the caller's, or (num_splits <= 0) the decode's own
-// count times the waves per work-group its own launch would give each item -- every
-// item of the mixed launch is walked by one wave, so each wave keeps the run of keys
-// it would stream in paged_attn_decode (measured on MI355X, the mixed ragged step:
-// 116.5-120.7 us with 4 splits, 152.5-154.5 us with the decode's own 2, whose
-// one-wave items of 1,760 keys then outlast the prefill).
-static int32_t mixed_decode_splits(const pa_mixed_decode& d, int32_t Hkv, bool fp8) {
+// The decode part's split count: the caller's, or (num_splits <= 0) the larger of two
+// counts.  (1) The decode's own count times the waves per work-group its own launch
+// would give each item: every item of the mixed launch is walked by one wave, so each
+// wave keeps the run of keys it would stream in paged_attn_decode (measured on MI355X,
+// the mixed ragged step: 116.5-120.7 us with 4 splits, 152.5-154.5 us with the
+// decode's own 2, whose one-wave items of 1,760 keys then outlast the prefill).
+// (2) Enough items for the CUs the prefill's work-groups leave: eight items (one
+// work-group) per CU of MI355X's 256 beyond the prefill's work-group count, partitions
+// kept at 8 chunks or more -- a work-group holds eight items on one CU, so a decode
+// alone with (1)'s count read its KV through a quarter of the CUs (32 x 8192 keys, Hq 28
+// / Hkv 4: 166.5 us with 64 work-groups, 93.4 us with 256, against 85.4 us for
+// paged_attn_decode).  prefill_wgs: the prefill part's work-groups.
+static int32_t mixed_decode_splits(const pa_mixed_decode& d, int32_t Hkv, bool fp8,
+                                   long long prefill_wgs) {
   if (d.num_splits > 0) return d.num_splits;
   const int32_t s0 = resolve_splits(d.B, Hkv, d.max_seq_len, 0);
   const int w = pa::decode_waves((long long)Hkv * s0 * (d.B > 0 ? d.B : 1), fp8);
-  return resolve_splits(d.B, Hkv, d.max_seq_len, s0 * w);
+  long long s = (long long)s0 * w;
+  const long long free_cus = 256 - prefill_wgs;
+  if (free_cus > 0 && d.B > 0) {
+    const long long groups = (long long)d.B * Hkv;
+    const int32_t chunks = d.max_seq_len > 0 ? (d.max_seq_len + kChunk - 1) / kChunk : 1;
+    long long spread = (8 * free_cus + groups - 1) / groups;
+    const long long cap = chunks / 8 > 0 ? chunks / 8 : 1;
+    if (spread > cap) spread = cap;
+    if (spread > s) s = spread;
+  }
+  return resolve_splits(d.B, Hkv, d.max_seq_len, (int32_t)(s < kMaxSplits ? s : kMaxSplits));
+}
+
+// Work-groups of the mixed launch's prefill part, from the host scalars the split
+// count and the grid depend on.
+static long long mixed_prefill_wgs(const pa_mixed_prefill& p, int32_t Hq, int32_t Hkv) {
+  if (p.B <= 0 || p.Tq <= 0 || p.max_q_len <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  pa::PrefillArgs a{};
+  a.B = p.B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.max_q_len = p.max_q_len < p.Tq ? p.max_q_len : p.Tq;
+  a.S = mixed_prefill_splits(p, Hq);
+  return pa::mixed_prefill_items(a);
 }
 
 static size_t mixed_prefill_bytes(const pa_mixed_prefill& p, int32_t Hq, int32_t D) {
@@ -919,7 +947,9 @@ size_t paged_attn_mixed_workspace_bytes(const pa_mixed_prefill* prefill,
   const size_t pf = mixed_prefill_bytes(*prefill, Hq, D);
   const size_t dec =
       decode->B > 0 && decode->max_seq_len >= 0
-          ? workspace_for(decode->B, Hq, D, mixed_decode_splits(*decode, Hkv, fp8 != nullptr))
+          ? workspace_for(decode->B, Hq, D,
+                          mixed_decode_splits(*decode, Hkv, fp8 != nullptr,
+                                              mixed_prefill_wgs(*prefill, Hq, Hkv)))
           : 0;
   return pf + dec;
 }
@@ -959,7 +989,11 @@ int paged_attn_mixed(const pa_mixed_prefill* prefill, const pa_mixed_decode* dec
     const int st = decode_args(d, "mixed (decode part)", dc.q, k_pool, v_pool, dc.block_tables,
                                dc.seq_lens, dc.B, dc.max_pages, num_pages, page_size, Hq, Hkv,
                                D, softmax_scale, dc.max_seq_len,
-                               dc.max_seq_len >= 0 ? mixed_decode_splits(dc, Hkv, f8) : 0, f8,
+                               dc.max_seq_len >= 0
+                                   ? mixed_decode_splits(dc, Hkv, f8,
+                                                         a.B > 0 ? pa::mixed_prefill_items(a) : 0)
+                                   : 0,
+                               f8,
                                ks, vs, 0, nullptr, nullptr, kss, vss);
     if (st) return st;
     if (!dc.out) return fail(PA_ERR_NULL, "mixed (decode part): out is NULL");

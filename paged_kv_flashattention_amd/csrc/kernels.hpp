@@ -153,6 +153,9 @@ hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream, char* 
 // launch_reduce).  `ev` is stamped around the kernel.
 hipError_t launch_mixed(const PrefillArgs& p, const DecodeArgs& d, hipStream_t stream,
                         char* desc, size_t desc_len, const KernelEvents& ev = KernelEvents());
+// work-groups of the prefill part of launch_mixed (from p's B, Hq, Hkv, max_q_len and S;
+// 0 for no prefill part)
+long long mixed_prefill_items(const PrefillArgs& p);
 // waves per prefill work-group (32 query rows each) for the longest query run (and
 // whether the pools are FP8 with ALiBi slopes)
 int prefill_waves(int max_q_len, bool fp8_alibi = false);

@@ -1370,6 +1370,11 @@ static hipError_t launch_mixed_d(const PrefillArgs& a, const DecodeArgs& d, int 
   return launch_mixed_v<D, false, false>(a, d, n_dg, n_pf, stream, ev);
 }
 
+long long mixed_prefill_items(const PrefillArgs& p) {
+  if (p.B <= 0 || p.max_q_len <= 0) return 0;
+  return prefill_items(prefill_shape(p, 8));
+}
+
 hipError_t launch_mixed(const PrefillArgs& p_in, const DecodeArgs& d, hipStream_t stream,
                         char* desc, size_t desc_len, const KernelEvents& ev) {
   const int D = p_in.B > 0 ? p_in.D : d.D;

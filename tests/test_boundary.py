@@ -534,6 +534,18 @@ def test_mixed_step_arguments_are_checked(lib):
     short = pf(B=4, max_q_len=300, num_splits=0)
     assert w(ctypes.byref(short), ctypes.byref(dec(B=0)), None, 32, Hkv, D) == 0
     assert lib.paged_attn_prefill_workspace_bytes(4, 1200, 300, 32, D, 0) > 0
+    # a decode alone spreads over every CU: 32 rows of 8,192 keys at Hkv 4 take the
+    # decode's 2 splits x 2 waves = 4 beside a prefill whose work-groups fill the chip
+    # (4 x 4096 causal rows, Hq 28: 28 x 4 x 16 work-groups), but 16 alone (8 items per
+    # work-group, 256 work-groups)
+    big = dec(B=32, max_seq_len=8192, num_splits=0)
+    c2 = lambda s: lib.paged_attn_decode_workspace_bytes(32, 28, 4, D, 8192, s)
+    assert w(ctypes.byref(pf(B=0)), ctypes.byref(big), None, 28, 4, D) == c2(16)
+    full = pf(B=4, Tq=16384, max_q_len=4096, num_splits=1)
+    assert w(ctypes.byref(full), ctypes.byref(big), None, 28, 4, D) == c2(4)
+    # a small prefill (2 x 300 rows, Hq 28: 112 work-groups) leaves 144 CUs: 9 splits
+    small = pf(B=2, Tq=600, max_q_len=300, num_splits=1)
+    assert w(ctypes.byref(small), ctypes.byref(big), None, 28, 4, D) == c2(9)
     # FP8 pools: the decode's own count for FP8 (1) times the waves the FP8 decode would
     # take (4), and the scales are checked as the separate entry points check them
     f8 = _lib.MixedFp8(0.5, 0.25, None, None)
