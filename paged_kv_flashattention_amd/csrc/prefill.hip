@@ -502,8 +502,37 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     }
     issue_page(__builtin_amdgcn_readlane(tab, n - base_t), kvh, ks, vs);
   };
-  // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's
-  auto publish = [&](int n, int ks, int vs) {
+  // FP8 pools: quarter q (0, 1: K; 2, 3: V) of this wave's share of tile n, widened
+  // from the codes in registers into K stage ks and V stage vs
+  auto widen = [&](int n, int ks, int vs, int q) {
+    uint16_t* kr = kst(ks) + M_::region(wave) * PfLds<D>::REGION;
+    uint16_t* vr = vst(vs) + M_::region(wave) * PfLds<D>::REGION;
+    const int row0 = n * kPfBN + 16 * M_::region(wave);
+#pragma unroll
+    for (int k = 0; k < F8_NP; ++k) {
+      const int i = lane + 64 * k;
+      if (F8_IPW % 64 == 0 || i < F8_IPW) {
+        const int piece = (wave % (W / 4)) * F8_IPW + i;
+        const int sl = piece / F8_PPR, c = 2 * (piece % F8_PPR) + (q & 1);
+        const int h2 = 2 * (q & 1);              // the piece's first or second 8 codes
+        if (q < 2) {
+          const u32x2 k0 = pf_fp8x4_to_bf16(k8[k][h2]), k1 = pf_fp8x4_to_bf16(k8[k][h2 + 1]);
+          *reinterpret_cast<u32x4*>(kr + 128 * c + 8 * sl) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+        } else {
+          // V rows at or past the sequence end are zeroed (P = 0 times NaN is not 0)
+          u32x4 va = {0u, 0u, 0u, 0u};
+          if (row0 + sl < L) {
+            const u32x2 v0 = pf_fp8x4_to_bf16(v8[k][h2]), v1 = pf_fp8x4_to_bf16(v8[k][h2 + 1]);
+            va = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          }
+          *reinterpret_cast<u32x4*>(vr + 128 * c + 8 * ((sl + 4 * c) & 15)) = va;
+        }
+      }
+    }
+  };
+  // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's.
+  // widened: (FP8) this wave's share of tile n was widened during the step before.
+  auto publish = [&](int n, int ks, int vs, bool widened = false) {
     vmcnt_wait<0>();
     if constexpr (PS) {
       // region r holds keys 16 r .. 16 r + 15 of the tile: half r % 2 of block r / 2
@@ -514,31 +543,9 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       }
     }
     if constexpr (F8) {
-      uint16_t* kr = kst(ks) + M_::region(wave) * PfLds<D>::REGION;
-      uint16_t* vr = vst(vs) + M_::region(wave) * PfLds<D>::REGION;
-      const int row0 = n * kPfBN + 16 * M_::region(wave);
+      if (!widened) {
 #pragma unroll
-      for (int k = 0; k < F8_NP; ++k) {
-        const int i = lane + 64 * k;
-        if (F8_IPW % 64 == 0 || i < F8_IPW) {
-          const int piece = (wave % (W / 4)) * F8_IPW + i;
-          const int sl = piece / F8_PPR, c = 2 * (piece % F8_PPR);
-          const u32x2 k0 = pf_fp8x4_to_bf16(k8[k][0]), k1 = pf_fp8x4_to_bf16(k8[k][1]);
-          const u32x2 k2 = pf_fp8x4_to_bf16(k8[k][2]), k3 = pf_fp8x4_to_bf16(k8[k][3]);
-          *reinterpret_cast<u32x4*>(kr + 128 * c + 8 * sl) = u32x4{k0[0], k0[1], k1[0], k1[1]};
-          *reinterpret_cast<u32x4*>(kr + 128 * (c + 1) + 8 * sl) =
-              u32x4{k2[0], k2[1], k3[0], k3[1]};
-          // V rows at or past the sequence end are zeroed (P = 0 times NaN is not 0)
-          u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-          if (row0 + sl < L) {
-            const u32x2 v0 = pf_fp8x4_to_bf16(v8[k][0]), v1 = pf_fp8x4_to_bf16(v8[k][1]);
-            const u32x2 v2 = pf_fp8x4_to_bf16(v8[k][2]), v3 = pf_fp8x4_to_bf16(v8[k][3]);
-            va = u32x4{v0[0], v0[1], v1[0], v1[1]};
-            vb = u32x4{v2[0], v2[1], v3[0], v3[1]};
-          }
-          *reinterpret_cast<u32x4*>(vr + 128 * c + 8 * ((sl + 4 * c) & 15)) = va;
-          *reinterpret_cast<u32x4*>(vr + 128 * (c + 1) + 8 * ((sl + 4 * (c + 1)) & 15)) = vb;
-        }
+        for (int q = 0; q < 4; ++q) widen(n, ks, vs, q);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the tile is in LDS
     } else if (n * kPfBN + kPfBN > L) {
@@ -701,7 +708,13 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   // depend on it, so the matrix cores and the vector ALU of one wave overlap;
   // operand reads run two MFMAs ahead.  sched_barrier keeps the compiler from
   // regrouping the chunks.
-  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp) {
+  //
+  // FP8 pools: with wn >= 0 the step also widens this wave's share of tile wn (codes in
+  // registers) into K stage wks and V stage wvs, a quarter after every other P V MFMA,
+  // where the vector ALU has nothing else to do; the tile's publish then only waits.
+  // The stages of the tile published next are not read during the step before it.
+  auto step = [&](f32x16& s_pend, const uint16_t* kq, int kbq, int vsi, int kbp, int wn = -1,
+                  int wks = 0, int wvs = 0) {
     constexpr int NK = D / 16;                 // QK MFMAs
     constexpr int EPK = 16 / NK;               // exponentials per QK MFMA
     constexpr int NV = 2 * (D / 32);           // PV MFMAs
@@ -773,6 +786,10 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       if (i + 2 < NV) vf[i + 2] = vfrag(i + 2);
       const int t = i % (D / 32);
       acc[t] = mfma32x32x16(vf[i], i < D / 32 ? pb0 : pb1, acc[t]);
+      if constexpr (F8) {
+        // NV / 4 MFMAs per quarter (NV is 4 or 8)
+        if (wn >= 0 && (i + 1) % (NV / 4) == 0) widen(wn, wks, wvs, i / (NV / 4));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     s_pend = sn;
@@ -939,11 +956,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     for (; u < U1; ++u) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
-      // first block of tile kt (pending) -> its second block
-      step(s_pend, kst(ks_cur), B1, vs_cur, B0);
+      // first block of tile kt (pending) -> its second block (FP8: widening tile kn)
+      step(s_pend, kst(ks_cur), B1, vs_cur, B0, F8 ? kn : -1, ks_cur ^ 1, vs_next);
       mask(s_pend, kt * kPfBN + 32 * B1, u);
       // second block of tile kt -> first block of tile kn
-      publish(kn, ks_cur ^ 1, vs_next);
+      publish(kn, ks_cur ^ 1, vs_next, F8);
       issue_walk(u + 2);
       step(s_pend, kst(ks_cur ^ 1), B0, vs_cur, B1);
       mask(s_pend, kn * kPfBN + 32 * B0, u + 1);
