@@ -533,7 +533,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   // tile n's loads (this wave's) have landed; tail rows zeroed; then everyone's.
   // widened: (FP8) this wave's share of tile n was widened during the step before.
   auto publish = [&](int n, int ks, int vs, bool widened = false) {
-    vmcnt_wait<0>();
+    // widened tiles went through registers, whose loads the compiler waits for
+    if (!widened) vmcnt_wait<0>();
     if constexpr (PS) {
       // region r holds keys 16 r .. 16 r + 15 of the tile: half r % 2 of block r / 2
       const int r = M_::region(wave);
@@ -959,9 +960,16 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       // first block of tile kt (pending) -> its second block (FP8: widening tile kn)
       step(s_pend, kst(ks_cur), B1, vs_cur, B0, F8 ? kn : -1, ks_cur ^ 1, vs_next);
       mask(s_pend, kt * kPfBN + 32 * B1, u);
-      // second block of tile kt -> first block of tile kn
-      publish(kn, ks_cur ^ 1, vs_next, F8);
-      issue_walk(u + 2);
+      // second block of tile kt -> first block of tile kn.  FP8 pools: tile kn's codes
+      // are in LDS already, so the registers take tile u + 2's codes before the barrier
+      // (with scales per page the scale registers of tile kn are still to be published)
+      if constexpr (F8 && !PS) {
+        issue_walk(u + 2);
+        publish(kn, ks_cur ^ 1, vs_next, true);
+      } else {
+        publish(kn, ks_cur ^ 1, vs_next, F8);
+        issue_walk(u + 2);
+      }
       step(s_pend, kst(ks_cur ^ 1), B0, vs_cur, B1);
       mask(s_pend, kn * kPfBN + 32 * B0, u + 1);
       vs_cur = vs_next;
