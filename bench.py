@@ -500,8 +500,8 @@ _PREFILL_SRC = ["prefill.hip", "decode_item.hpp", "decode_walk.inc", "common.hpp
 TRAFFIC = {
     "qwen7b_decode": ("decode_partition_qwen7b_decode_traffic.json", _DECODE_SRC,
                       "pa::decode_partition_kernel<"),
-    "long_decode": ("decode_partition_long_decode_traffic.json", _DECODE_SRC,
-                    "pa::decode_partition_kernel<"),
+    "long_decode": ("decode_group_long_decode_traffic.json", _DECODE_SRC,
+                    "pa::decode_group_kernel<"),
     "long_decode_auto": ("decode_partition_long_decode_auto_traffic.json", _DECODE_SRC,
                          "pa::decode_partition_kernel<"),
     "causal_prefill": ("prefill_causal_prefill_traffic.json", _PREFILL_SRC,
@@ -812,6 +812,14 @@ def secondary_figure(label, name, splits, args):
     return fig
 
 
+def dominant_kernel_name(workload, bound):
+    """The dominant kernel's name: the profiler name recorded for the workload, else the
+    decode partition kernel (HBM-bound steps) or the prefill kernel."""
+    if workload in TRAFFIC:
+        return TRAFFIC[workload][2].split("::")[-1].rstrip("<")
+    return "decode_partition_kernel" if bound == "hbm" else "prefill_kernel"
+
+
 def roofline_object(step, workload, kern_ms, ev_ms):
     """The roofline of a step's dominant kernel: algorithmic units per launch over the
     kernel's own (dispatch-stamped) duration against MI355X's published peak, with
@@ -825,7 +833,7 @@ def roofline_object(step, workload, kern_ms, ev_ms):
             "unit": step.unit_name, "frac": round(achieved / peak, 4),
             "traffic": recorded_traffic(workload),
             "algorithmic_units_per_launch": int(step.units),
-            "kernel": ("decode_partition_kernel" if bound == "hbm" else "prefill_kernel")
+            "kernel": dominant_kernel_name(workload, bound)
             if not isinstance(step, MixedStep) else "whole step",
             "kernel_us_per_launch": round(kern_ms * 1e3, 2),
             "kernel_us_median": round(getattr(step, "kernel_ms_median", kern_ms) * 1e3, 2),

@@ -175,6 +175,10 @@ size_t paged_attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int
  * partition's partial output and log-sum-exp go to the workspace and a second
  * kernel merges them exactly ("The Stack Below the Stack (Part 2)", section 2.2).
  * With S == 1 the first kernel writes out/lse_out directly and no workspace is used.
+ * How partitions map to work-groups is the library's choice and does not change a
+ * bit of the results: when B * Hkv * S is several times the number of one-wave
+ * work-groups that stream HBM best on MI355X, each work-group walks up to 8
+ * consecutive partitions of one (sequence, KV head) as one run of keys.
  *
  *   out       : [B, Hq, D] bf16                 lse_out : [B, Hq] fp32 or NULL
  *   q         : [B, Hq, D] bf16
@@ -455,7 +459,8 @@ size_t paged_attn_prefill_workspace_bytes(int32_t B, int32_t Tq, int32_t max_q_l
  *
  * Kernel timing: kernel_start_event / kernel_stop_event, when not NULL, are HIP
  * events (created beforehand, timing enabled, on the launch's device) that the
- * dispatch of the operation's main kernel (decode: the partition kernel; prefill:
+ * dispatch of the operation's main kernel (decode: the partition kernel, or the
+ * kernel of grouped partitions; prefill:
  * the prefill kernel, not the merge) stamps with that kernel's own start and end
  * (hipExtLaunchKernel).  hipEventElapsedTime on the pair then gives the kernel's
  * duration inside a stream of work, with no event records added between launches.

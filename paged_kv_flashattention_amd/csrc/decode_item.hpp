@@ -225,6 +225,15 @@ __device__ __forceinline__ void decode_widen_v8(DecodeChunk<D>& c) {
     }
 }
 
+// Grouped partitions: the LDS stage of a one-wave work-group's finished partials, at
+// most kGpMaxParts partitions x 16 heads x (D + 4) floats, then their lse values.
+constexpr int kGpMaxParts = 8;
+template <int D>
+__device__ __forceinline__ float* gp_stage() {
+  __shared__ __align__(16) float buf[kGpMaxParts * 16 * (D + 4) + kGpMaxParts * 16];
+  return buf;
+}
+
 // BM: a block map is given (a.block_map); PS: FP8 pools with scales per (page, KV
 // head) (a.k_scales).  Each is compiled in only when used.
 //
@@ -233,8 +242,10 @@ __device__ __forceinline__ void decode_widen_v8(DecodeChunk<D>& c) {
 // its row of a static array, or (DYN) a slice at the start of the kernel's dynamic
 // LDS chosen by its wave index in the work-group.  DYN takes W = 1: each wave's item
 // is its own and meets no barrier, so the waves of one work-group may run different
-// items.
-template <int D, int W, bool F8, bool BM = false, bool PS = false, bool DYN = false>
+// items.  GP: the item is a group of a.group partitions from `split` on, walked as one
+// run of chunks, each partition's partial written as the walk leaves it.
+template <int D, int W, bool F8, bool BM = false, bool PS = false, bool DYN = false,
+          bool GP = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int split, int b) {
 #include "decode_walk.inc"
 }

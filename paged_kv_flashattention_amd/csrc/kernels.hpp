@@ -34,6 +34,7 @@ struct DecodeArgs {
   const float* v_scales;         //   or null: one scale per pool (folded as above)
   const uint8_t* block_map;      // [B, bm_kb] listed 64-key tiles of each row, or null
   int bm_kb;
+  int group;                     // partitions per one-wave work-group (0 or 1: one)
 };
 
 struct ReduceArgs {

@@ -454,7 +454,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   // FP8 pools: each wave covers the pieces (16 consecutive codes of one row) of its
   // region, row-major so that a row's pieces are neighbouring lanes; they are
   // loaded into registers one tile ahead, like the DMA, and widened to bf16 into the
-  // tile's slots when the tile is published.
+  // tile's slots during the step before the tile is published (in the steady loop)
+  // or at the publish (the walk's first tile and the tiles after a wave's last block).
   constexpr int F8_PPR = D / 16;                  // pieces per row
   constexpr int F8_IPW = 4 * D / W;               // pieces per wave per matrix
   constexpr int F8_NP = F8 ? (F8_IPW + 63) / 64 : 1;
