@@ -40,9 +40,9 @@ def _slice(case, b0, b1):
             case.seq_lens_k[b0:b1].contiguous())
 
 
-def _decode(case, q, bt, sl, S, fp8=None, block_map=None):
+def _decode(case, q, bt, sl, S, fp8=None, block_map=None, **extra):
     kw = dict(max_seq_len=case.max_seq_len, num_splits=S, return_lse=True, validate=True,
-              block_map=block_map)
+              block_map=block_map, **extra)
     if fp8 is None:
         out, lse = pa.paged_attn_decode(q, case.k_pool, case.v_pool, bt, sl, case.scale, **kw)
     else:
@@ -52,19 +52,21 @@ def _decode(case, q, bt, sl, S, fp8=None, block_map=None):
     return out, lse, pa.describe_launch()
 
 
-def _check_against_sub_batches(case, S, fp8=None, block_map=None):
+def _check_against_sub_batches(case, S, fp8=None, block_map=None, key_lo=None, **extra):
     """The grouped launch over the whole batch, then each sub-batch launched one
     partition per one-wave work-group: equal bits, row by row."""
     B, Hkv = case.q.shape[0], case.k_pool.shape[2]
     g = _group(B, Hkv, S, fp8 is not None)
     assert g >= 2
-    out, lse, desc = _decode(case, case.q, case.block_tables, case.seq_lens_k, S, fp8, block_map)
+    out, lse, desc = _decode(case, case.q, case.block_tables, case.seq_lens_k, S, fp8, block_map,
+                             key_lo=key_lo, **extra)
     assert "decode_group" in desc and f"partitions per work-group={g}" in desc, desc
     n = _sub_batch(Hkv, S, fp8 is not None)
     assert B % n == 0
     for b0 in range(0, B, n):
         bm = None if block_map is None else block_map[b0:b0 + n].contiguous()
-        o, l, d = _decode(case, *_slice(case, b0, b0 + n), S, fp8, bm)
+        lo = None if key_lo is None else key_lo[b0:b0 + n].contiguous()
+        o, l, d = _decode(case, *_slice(case, b0, b0 + n), S, fp8, bm, key_lo=lo, **extra)
         assert "decode_partition" in d and "W=1" in d, d
         assert torch.equal(out[b0:b0 + n].view(torch.int16), o.view(torch.int16)), (b0, desc)
         assert torch.equal(lse[b0:b0 + n], l), (b0, desc)
@@ -199,3 +201,22 @@ def test_grouped_partitions_block_map(require_gpu):
                                         oracle.block_map_mask(bm[:, None, :]))
     assert_parity(as_f64(out), o_ref, "grouped decode block map")
     assert_lse(as_f64(lse), l_ref, "grouped decode block map lse")
+
+
+def test_grouped_partitions_window_alibi_documents(require_gpu):
+    """Grouped partitions with a sliding window, ALiBi slopes and document starts, which
+    move where each row's walk begins (partitions sized for the window)."""
+    B, Hq, Hkv, D, ps, S, w = 16, 16, 8, 128, 16, 16, 3000
+    lens = _lens(B, 9000, 1571)
+    case = make_case("grpw", seq_lens=lens, Hq=Hq, Hkv=Hkv, D=D, page_size=ps, seed=93,
+                     device="cuda", window=w)
+    rng = np.random.default_rng(94)
+    lo = np.array([int(rng.integers(0, L)) if L else 0 for L in lens], dtype=np.int32)
+    slopes = torch.from_numpy((2.0 ** -rng.uniform(1, 8, Hq)).astype(np.float32)).cuda()
+    print("[decode group] window + alibi + documents", flush=True)
+    out, lse = _check_against_sub_batches(case, S, key_lo=torch.from_numpy(lo).cuda(),
+                                          window_left=w, alibi_slopes=slopes)
+    o_ref, l_ref = oracle_full(case, alibi=slopes.cpu().numpy(),
+                               key_ranges=(lo, np.asarray(lens, dtype=np.int32)))
+    assert_parity(as_f64(out), o_ref, "grouped decode window alibi documents")
+    assert_lse(as_f64(lse), l_ref, "grouped decode window alibi documents lse")
