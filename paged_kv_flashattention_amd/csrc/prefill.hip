@@ -958,6 +958,16 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
     for (; u < U1; ++u) {
       const int kt = tile_at(u), kn = tile_at(u + 1);
       const int vs_next = vs_cur == 2 ? 0 : vs_cur + 1;
+      // Waves w and w + 4 share a SIMD, and the older one wins its issue slots: left
+      // alone it finishes each barrier interval first and waits while the younger one
+      // runs by itself.  Issue priority instead goes to one wave group from here to
+      // the next such point and to the other group after it, alternating per tile, so
+      // each barrier interval's two steps are led by different waves (bf16: with FP8
+      // pools, whose widening shares the P V phase, this measured slower).
+      if constexpr (W == 8 && !F8) {
+        if ((wave >= 4) == (u & 1)) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       // first block of tile kt (pending) -> its second block (FP8: widening tile kn)
       step(s_pend, kst(ks_cur), B1, vs_cur, B0, F8 ? kn : -1, ks_cur ^ 1, vs_next);
       mask(s_pend, kt * kPfBN + 32 * B1, u);
@@ -976,6 +986,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
       vs_cur = vs_next;
       ks_cur ^= 1;
     }
+    if constexpr (W == 8 && !F8) __builtin_amdgcn_s_setprio(0);
     if (u == nt - 1) {
       // the last tile: both of its blocks (G = 2 nt), only its first (G = 2 nt - 1),
       // or none (G = 0, one tile)
