@@ -326,7 +326,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
   static_assert(!BS || (GEN && !PER && W == 8), "block maps: general variant, 8 waves");
-  static_assert(!HP || (!GEN && !F8 && !PER && !BS && W == 8),
+  static_assert(!HP || ((!GEN || BS) && !F8 && !PER && W == 8),
                 "paired heads: plain bf16 variant, 8 waves");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   using L_ = PfLds<D>;
@@ -610,7 +610,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   auto mask = [&](f32x16& sc, int kb0, int u) {
     if (ALI) boff = slope_log2 * (float)(kb0 - my_pos);
     if constexpr (BS) {
-      if (!((bs_entry(u) >> (16 + wave / 2)) & 1)) {
+      // the wave's query block: bit 16 + (its first row - r_wg) / 64 of the entry
+      if (!((bs_entry(u) >> (16 + (HP ? wave & 3 : wave) / 2)) & 1)) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[e] = kNegInf;
         return;
@@ -821,7 +822,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
           const bool t_ok = t < tile_hi && t < a.bm_kb;
           int fl = 0;
 #pragma unroll
-          for (int k = 0; k < W / 2; ++k) {
+          for (int k = 0; k < kPfBM / 64; ++k) {
             const int qb = qb0 + k;
             const uint8_t v =
                 mrow[(size_t)min(qb, a.bm_qb - 1) * a.bm_kb + min(t, a.bm_kb - 1)];
@@ -1304,6 +1305,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
   if (a.block_map) {
     // block maps take 256-row work-groups (prefill_waves)
     if constexpr (W == 8) {
+      if (a.hp) return launch_prefill_w<D, 8, true, false, false, false, true, true>(a, stream, ev);
       return a.alibi ? launch_prefill_w<D, 8, true, false, true, false, true>(a, stream, ev)
                      : launch_prefill_w<D, 8, true, false, false, false, true>(a, stream, ev);
     } else {
@@ -1334,7 +1336,9 @@ static int prefill_waves(const PrefillArgs& a) {
 
 // Paired heads (a work-group of 8 waves takes two query heads of one KV group over 128
 // rows instead of one head over 256): for the plain bf16 variant of an unsplit
-// 8-wave launch with an even GQA group.  Each K/V tile copied into LDS then serves
+// 8-wave launch with an even GQA group, and for its block-map variant (bf16, no
+// window, ALiBi or document masks), whose work-groups then walk the union of two
+// query blocks' listed tiles instead of four.  Each K/V tile copied into LDS then serves
 // two heads' rows, the work-groups are as many as with 256-row tiles, and a causal
 // work-group's diagonal spans 128 keys instead of 256, so fewer of its (wave, block)
 // steps are masked whole.  A row's result does not depend on the tile height when
@@ -1343,7 +1347,7 @@ static int prefill_waves(const PrefillArgs& a) {
 // 256-row tiles, so split launches keep them.
 static bool prefill_pairs(const PrefillArgs& a, int W) {
   return W == 8 && a.S <= 1 && !a.kv_fp8 && !a.alibi && a.window == 0 && !a.key_lo &&
-         !a.block_map && !a.persist && a.G % 2 == 0;
+         !a.persist && a.G % 2 == 0;
 }
 
 static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W, bool pairs = false) {
