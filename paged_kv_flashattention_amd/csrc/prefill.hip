@@ -326,7 +326,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, const PfWork& w,
   static_assert(!PS || (F8 && GEN && !REV), "scales per page: FP8 general variant, no ALiBi");
   static_assert(!PER || (!GEN && !F8), "persistent work-groups: plain bf16 variant");
   static_assert(!BS || (GEN && !PER && W == 8), "block maps: general variant, 8 waves");
-  static_assert(!HP || (!F8 && !PER && W == 8),
+  static_assert(!HP || (!PER && W == 8),
                 "paired heads: plain bf16 variant, 8 waves");
   constexpr bool ALI = REV;          // ALiBi slopes present (a.alibi != nullptr)
   using L_ = PfLds<D>;
@@ -1286,6 +1286,22 @@ template <int D, int W>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream,
                                    const KernelEvents& ev) {
   if (a.kv_fp8) {
+    if constexpr (W == 8) {
+      if (a.hp) {
+        if (a.block_map) {
+          if (a.k_scales)
+            return launch_prefill_w<D, 8, true, true, false, true, true, true>(a, stream, ev);
+          return a.alibi ? launch_prefill_w<D, 8, true, true, true, false, true, true>(a, stream, ev)
+                         : launch_prefill_w<D, 8, true, true, false, false, true, true>(a, stream, ev);
+        }
+        if (a.k_scales)
+          return launch_prefill_w<D, 8, true, true, false, true, false, true>(a, stream, ev);
+        if (a.alibi) return launch_prefill_w<D, 8, true, true, true, false, false, true>(a, stream, ev);
+        return a.window > 0 || a.key_lo
+                   ? launch_prefill_w<D, 8, true, true, false, false, false, true>(a, stream, ev)
+                   : launch_prefill_w<D, 8, false, true, false, false, false, true>(a, stream, ev);
+      }
+    }
     if (a.block_map) {
       // block maps take 256-row work-groups (prefill_waves)
       if constexpr (W == 8) {
@@ -1343,19 +1359,19 @@ static int prefill_waves(const PrefillArgs& a) {
 }
 
 // Paired heads (a work-group of 8 waves takes two query heads of one KV group over 128
-// rows instead of one head over 256): for the plain bf16 variant of an unsplit
-// 8-wave bf16 launch with an even GQA group, with or without a window, ALiBi, document
-// masks or a block map: a work-group then walks the union of 128 rows' key ranges
-// (windows, documents) or of two query blocks' listed tiles instead of 256 rows' or
-// four blocks'.  Each K/V tile copied into LDS then serves
-// two heads' rows, the work-groups are as many as with 256-row tiles, and a causal
+// rows instead of one head over 256): for every unsplit 8-wave launch with an even
+// GQA group, bf16 or FP8 pools, with or without a window, ALiBi, document masks or a
+// block map: a work-group then walks the union of 128 rows' key ranges (windows,
+// documents) or of two query blocks' listed tiles instead of 256 rows' or four
+// blocks'.  Each K/V tile copied into LDS then serves two heads' rows, the
+// work-groups are as many as with 256-row tiles, and a causal
 // work-group's diagonal spans 128 keys instead of 256, so fewer of its (wave, block)
 // steps are masked whole.  A row's result does not depend on the tile height when
 // the keys are not split, so the output bits are those of the 256-row launch; with
 // key parts the parts follow the tile height, and the planner and the merge count
 // 256-row tiles, so split launches keep them.
 static bool prefill_pairs(const PrefillArgs& a, int W) {
-  return W == 8 && a.S <= 1 && !a.kv_fp8 && !a.persist && a.G % 2 == 0;
+  return W == 8 && a.S <= 1 && !a.persist && a.G % 2 == 0;
 }
 
 static PrefillArgs prefill_shape(const PrefillArgs& a_in, int W, bool pairs = false) {
