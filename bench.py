@@ -47,6 +47,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle-ms", type=float, default=0.0,
+                   help="after the warm-up steps, run untimed steps for this many more "
+                        "milliseconds before timing the headline workload (the secondary "
+                        "figures always take %g ms)" % SECONDARY_SETTLE_MS)
     p.add_argument("--workload", default="qwen7b_decode",
                    choices=["qwen7b_decode", "qwen7b_decode_fp8", "long_history_chunk",
                             "long_decode", "long_decode_auto", "causal_prefill",
@@ -438,8 +442,21 @@ def next_events(step):
     return next(it) if it is not None else None
 
 
-def time_step(step, steps, warmup, kernel_events=True):
+# Untimed running before the secondary figures are timed.  A GPU that has been idle
+# runs a heavy kernel at full speed for its first 1-2 ms of sustained load, then
+# 15-25 % slower for several milliseconds, and only after 10-30 ms back at a steady
+# rate (kernel traces of the causal prefill: 580 us, then 730 us, then 575 us per
+# launch).  Five warm-up steps of a 0.6 ms kernel end inside that dip, so the
+# secondary figures first run their own steps untimed for this long.
+SECONDARY_SETTLE_MS = 50.0
+
+
+def time_step(step, steps, warmup, kernel_events=True, settle_ms=0.0):
     """Warm up, then time exactly `steps` calls bracketed by synchronisations.
+
+    After the `warmup` calls, more untimed calls run until `settle_ms` milliseconds
+    of wall time have passed (0: none), so that the timed calls find the engine at
+    its sustained clock.
 
     Returns (wall ms per step, event ms per step, dominant-kernel ms or None).  The
     step's time comes from HIP events recorded on the launch stream (torch's current
@@ -453,6 +470,14 @@ def time_step(step, steps, warmup, kernel_events=True):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    step.settle_calls = 0
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            step.settle_calls += 8
+            torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -799,12 +824,13 @@ def secondary_figure(label, name, splits, args):
         s = GraphStep(s, len(s.kv) if hasattr(s, "kv") else 1)
     elif label.endswith("_prepared"):
         s = PreparedStep(s)
-    w2, e2, k2 = time_step(s, args.steps, args.warmup)
+    w2, e2, k2 = time_step(s, args.steps, args.warmup, settle_ms=SECONDARY_SETTLE_MS)
     v2 = rate(s.units, e2, s.unit_name)
     pk = HBM_PEAK_GBS if s.unit_name == "GB/s" else BF16_PEAK_TFLOPS
     per = getattr(s, "calls", 1)
     fig = {"value": round(v2, 2), "unit": s.unit_name, "frac": round(v2 / pk, 4),
-           "us_per_step": round(e2 * 1e3 / per, 2), "config": s.config()}
+           "us_per_step": round(e2 * 1e3 / per, 2), "settle_ms": SECONDARY_SETTLE_MS,
+           "config": s.config()}
     if k2:
         fig["main_kernel_us"] = round(k2 * 1e3, 2)
         fig["main_kernel_frac"] = round(rate(s.units, k2, s.unit_name) / pk, 4)
@@ -866,7 +892,7 @@ def main():
 
     step = make_step(args.workload, args.num_splits)
     torch.cuda.synchronize()
-    wall, ev, kern_ms = time_step(step, args.steps, args.warmup)
+    wall, ev, kern_ms = time_step(step, args.steps, args.warmup, settle_ms=args.settle_ms)
     value = rate(step.units, ev, step.unit_name)
     launch = pa.describe_launch()
     if kern_ms is None:                      # the mixed step: no single main kernel
@@ -883,6 +909,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall, 5),
+        **({"settle_ms": args.settle_ms} if args.settle_ms > 0 else {}),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -907,9 +934,11 @@ def main():
         # roofline object of its own and its own oracle baseline
         try:
             pf = make_step("causal_prefill", 0)
-            w2, e2, k2 = time_step(pf, args.steps, args.warmup)
+            w2, e2, k2 = time_step(pf, args.steps, args.warmup,
+                                   settle_ms=SECONDARY_SETTLE_MS)
             result["roofline_prefill"] = dict(roofline_object(pf, "causal_prefill", k2, e2),
                                               value=round(rate(pf.units, e2, pf.unit_name), 2),
+                                              settle_ms=SECONDARY_SETTLE_MS,
                                               config=pf.config())
             log(f"[bench] causal_prefill: {e2 * 1e3:.1f} us/step, kernel {k2 * 1e3:.1f} us, "
                 f"{result['roofline_prefill']['achieved']:.1f} TFLOP/s in the kernel")
